@@ -1,0 +1,130 @@
+/*
+ * moe_oracle.h -- plain CPU oracle for the batched routed-MoE FFN.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the HIP library; the only thing the two sides
+ * share is the seeded input generator.
+ *
+ * Sources (SharpInference GitHub issues):
+ *   #406 "batched int8-MMQ trunk prefill gated off for MoE", section "The
+ *        work" item 2: batch the router over N tokens, bucket tokens per
+ *        expert, grouped expert GEMM, scatter; int8 MMQ with an argmax-stable
+ *        contract.
+ *   #408 "full-offload MoE decode ~3.4x behind llama.cpp", "Hypothesis":
+ *        64 experts / 8 active, norm_topk_prob=false; Q8_1 (int8 block)
+ *        activations for the expert matvec; router on the GPU.
+ *   #388 "Carnice prefill toward llama.cpp 676 t/s", "Remaining levers" 1:
+ *        router matvec norm[N x embDim] x routerW[numExperts x embDim] +
+ *        softmax + top-k + shared-expert gate, bucketed into the CSR
+ *        expStart / expTokI / expTokK.
+ *   #129 (batched weighted scatter-reduce), "Scope": per token, sum the na
+ *        unweighted down-partials in top-k slot order with the per-(token,
+ *        slot) weights, then add the shared-expert row, in that order.
+ *
+ * Precision: decisions that pick an integer (router top-k, int8 codes) are
+ * taken in fp32 exactly as the GPU takes them; every value that is not a
+ * decision (softmax weights, the int8 dot products after their exact int32
+ * block sums, SwiGLU, the combine) is carried in fp64.  The one exception is
+ * ora_combine_f32, which reproduces the fp32 host reduce of #129 bit for bit.
+ *
+ * Q8_0 weight rows: in/32 blocks of {binary16 scale, int8 q[32]} = 34 bytes,
+ * little-endian, unpadded.  Activation blocks: int8 codes plus one binary16
+ * scale per 32 values (the Q8_1-style block of #408).
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ora_dims {
+  int32_t d;              /* hidden size, multiple of 32 */
+  int32_t n_experts;      /* E */
+  int32_t top_k;          /* k = na */
+  int32_t ffn;            /* routed expert intermediate size, multiple of 32 */
+  int32_t shared_ffn;     /* shared expert intermediate size, 0 = none */
+  int32_t norm_topk_prob; /* 1: renormalise the k selected weights */
+} ora_dims;
+
+/* IEEE binary16 <-> binary32, round to nearest even (n values). */
+void ora_half_to_float(const uint16_t* h, float* f, int64_t n);
+void ora_float_to_half(const float* f, uint16_t* h, int64_t n);
+
+/* Router logits l[t][e] = fp32 fmaf chain over ascending j of x[t][j]*W[e][j],
+ * starting from +0, then + bias[e] (fp32 add) when bias != NULL. */
+void ora_router_logits(const float* x, int32_t n, int32_t d, const float* w,
+                       const float* bias, int32_t n_experts, float* logits);
+
+/* Top-k by (logit descending, expert id ascending); slot s = rank s. */
+void ora_topk(const float* logits, int32_t n, int32_t n_experts, int32_t k, int32_t* ids);
+
+/* Softmax over all E logits (fp64), picked at the top-k ids; renormalised
+ * over the k picks when norm != 0. */
+void ora_route_weights(const float* logits, const int32_t* ids, int32_t n, int32_t n_experts,
+                       int32_t k, int32_t norm, double* w);
+
+/* Shared-expert gate: sigmoid(x[t] . g) in fp64. */
+void ora_shared_gate(const float* x, int32_t n, int32_t d, const float* g, double* gs);
+
+/* CSR buckets: counts per expert, exclusive scan into exp_start[E+1(+1)],
+ * then (token asc, slot asc) placement.  has_shared appends group E holding
+ * every token once with slot index k.  exp_start has E+1+has_shared entries;
+ * tok_i/tok_k have n*k (+n) entries. */
+void ora_csr(const int32_t* ids, int32_t n, int32_t n_experts, int32_t k, int32_t has_shared,
+             int32_t* exp_start, int32_t* tok_i, int32_t* tok_k);
+
+/* Per-32-block int8 quantiser (fp32 decisions): amax, code =
+ * clamp(rint(v * (127/amax)), -127, 127), scale = binary16(amax/127);
+ * an all-zero block gives scale 0 and zero codes. */
+void ora_quantize_q8(const float* v, int64_t n_values, int8_t* q, uint16_t* scale16);
+
+/* Q8 dot of an activation row (codes + fp16 scales) with one Q8_0 weight row:
+ * sum over blocks of exact int32 block sums times sa*sw, in fp64. */
+double ora_q8_dot(const int8_t* qa, const uint16_t* sa16, const uint8_t* w_row, int32_t n_blocks);
+
+/* One SwiGLU expert on one quantised token row: g,u = Q8 dots; h = silu(g)*u
+ * (fp64), requantised per 32 in fp32; y = Q8 dot with the down rows.
+ * gate/up: [ffn][d/32*34] bytes, down: [d][ffn/32*34] bytes.  hq/hs/h may be
+ * NULL. */
+void ora_expert_ffn(int32_t d, int32_t ffn, const int8_t* xq, const uint16_t* xs,
+                    const uint8_t* gate, const uint8_t* up, const uint8_t* down, double* y,
+                    int8_t* hq, uint16_t* hs, double* h);
+
+/* The per-token loop over the listed tokens (OpenMP over the list):
+ * router, top-k, weights, quantiser, k experts (+ shared), combine in fp64.
+ * out: [n_list][d].  partial (may be NULL): [n_list][k+has_shared][d]
+ * unweighted expert outputs.  ids/w/gs (may be NULL): [n_list][k], [n_list][k],
+ * [n_list].  Returns 0, or -1 on a bad argument. */
+int32_t ora_moe_tokens(const ora_dims* dm, const float* x, int32_t n_tokens,
+                       const float* router_w, const float* router_bias,
+                       const uint8_t* gate_q8, const uint8_t* up_q8, const uint8_t* down_q8,
+                       const uint8_t* sh_gate_q8, const uint8_t* sh_up_q8, const uint8_t* sh_down_q8,
+                       const float* sh_gate_vec, const int32_t* token_list, int32_t n_list,
+                       double* out, double* partial, int32_t* ids, double* w, double* gs);
+
+/* The same layer evaluated grouped by expert: router for all tokens, CSR,
+ * then every expert group's rows in CSR order, then the combine.  Must agree
+ * bit for bit with ora_moe_tokens.  out: [n_tokens][d]. */
+int32_t ora_moe_grouped(const ora_dims* dm, const float* x, int32_t n_tokens,
+                        const float* router_w, const float* router_bias,
+                        const uint8_t* gate_q8, const uint8_t* up_q8, const uint8_t* down_q8,
+                        const uint8_t* sh_gate_q8, const uint8_t* sh_up_q8, const uint8_t* sh_down_q8,
+                        const float* sh_gate_vec, double* out);
+
+/* The fp32 host reduce of #129: o = +0; o = fmaf(w[t][s], P[t][s][j], o) for
+ * s = 0..k-1; then o = fmaf(gs[t], P[t][k][j], o) when gs != NULL.
+ * partial: [n][kk][d] with kk = k (+1 with a shared row). */
+void ora_combine_f32(const float* partial, const float* w, const float* gs, int32_t n, int32_t k,
+                     int32_t kk, int32_t d, float* out);
+
+/* RMSNorm with unit gain in fp64: x / sqrt(mean(x^2) + eps). */
+void ora_rmsnorm(const float* x, int32_t n, int32_t d, double eps, double* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
