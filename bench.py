@@ -1,0 +1,232 @@
+"""Benchmark: batched routed-MoE FFN prefill on one MI355X.
+
+One step = one full pass of the layer (router logits, routing + int8
+quantiser, CSR bucketing, grouped gate/up + SwiGLU GEMM, grouped down GEMM,
+ordered combine) over one batch of synthetic tokens, inputs resident in HBM.
+
+Prints ONE JSON line with tokens/s, the roofline fraction of the dominant
+kernel (timed live with HIP events on the launch stream) and the CPU oracle's
+rate on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE FFN prefill tokens/sec (OLMoE-shape N=2048) + % int8 MFMA peak"
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime (recorded by the library on
+    the stream it launches on)."""
+
+    def __init__(self):
+        self.h = C.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.h.hipEventDestroy.argtypes = [C.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = C.c_void_p()
+            if self.h.hipEventCreate(C.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = C.c_float()
+        if self.h.hipEventElapsedTime(C.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.h.hipEventDestroy(e)
+
+
+def gemm_ops(shape, n_tokens):
+    """Useful int8 ops (2 per multiply-add, no padding) of the two grouped GEMMs."""
+    P = n_tokens * shape.top_k
+    gu = 2 * P * (2 * shape.ffn) * shape.d
+    dn = 2 * P * shape.d * shape.ffn
+    if shape.shared_ffn:
+        gu += 2 * n_tokens * (2 * shape.shared_ffn) * shape.d
+        dn += 2 * n_tokens * shape.d * shape.shared_ffn
+    return gu, dn
+
+
+def stage_bytes(shape, n_tokens, counts):
+    """Algorithmic HBM bytes per stage: what the method must read or write
+    once (weights of the experts the batch touches, activations, partials)."""
+    d, F, k, E = shape.d, shape.ffn, shape.top_k, shape.n_experts
+    kk = k + (1 if shape.shared_ffn else 0)
+    touched = sum(1 for c in counts[:E] if c > 0)
+    q8 = 34.0 / 32.0
+    gu_w = touched * 2 * F * d * q8 + (2 * shape.shared_ffn * d * q8 if shape.shared_ffn else 0)
+    dn_w = touched * d * F * q8 + (d * shape.shared_ffn * q8 if shape.shared_ffn else 0)
+    P = n_tokens * k + (n_tokens if shape.shared_ffn else 0)
+    x_q = n_tokens * d * (1 + 2 / 32)
+    h_q = n_tokens * k * F * (1 + 2 / 32) + (n_tokens * shape.shared_ffn * (1 + 2 / 32) if shape.shared_ffn else 0)
+    part = n_tokens * kk * d * 4
+    return {
+        "router_logits": n_tokens * d * 4 + E * d * 4 + n_tokens * E * 4,
+        "gateup_swiglu": gu_w + x_q + h_q,
+        "down": dn_w + h_q + part,
+        "combine": part + n_tokens * k * 4 + n_tokens * d * 4,
+        "P": P,
+    }
+
+
+def read_traffic(kernel_tag):
+    """Measured HBM bytes per launch of a kernel from the committed rocprofv3
+    PMC summary, valid only while the kernel source is unchanged."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "mixture_experts_ffn_gemm_amd", "csrc", rec["source"])
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if sha != rec.get("source_sha256"):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(lw, x, target_s):
+    from oracle import oracle as O
+    n = x.shape[0]
+    t0 = time.perf_counter()
+    O.moe_tokens(lw, x, tokens=list(range(min(8, n))))
+    per = (time.perf_counter() - t0) / min(8, n)
+    m = int(max(8, min(n, target_s / max(per, 1e-9))))
+    toks = list(range(m))
+    t0 = time.perf_counter()
+    O.moe_tokens(lw, x, tokens=toks)
+    dt = time.perf_counter() - t0
+    return {"value": m / dt, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"first {m} of the {n} tokens of the same layer (per-token oracle loop, "
+                      f"router + top-k + quantiser + k experts + combine), {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="olmoe_n2048")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall-time budget of the CPU oracle sample (0 disables it)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_workloads as mw
+    from mixture_experts_ffn_gemm_amd import binding as B
+    from mixture_experts_ffn_gemm_amd.layer import MoeLayer
+
+    B.lib()
+    wl = mw.WORKLOADS[args.workload]
+    s = wl.shape
+    t0 = time.perf_counter()
+    lw = mw.workload_layer(args.workload)
+    x_np = mw.workload_tokens(args.workload)
+    log(f"[bench] {args.workload}: inputs generated in {time.perf_counter() - t0:.1f} s")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layer = MoeLayer.from_workload(lw, device=dev)
+    n = x_np.shape[0]
+    x = torch.from_numpy(x_np).to(dev)
+    out = torch.empty((n, s.d), dtype=torch.float32, device=dev)
+    ws = layer.workspace(n)
+    stream = torch.cuda.current_stream(dev)
+    exp_start = torch.empty(s.n_experts + 1 + (1 if s.shared_ffn else 0), dtype=torch.int32, device=dev)
+    B.moe_ffn_prefill(layer.handle, x, n, out, ws, ws.numel(), B.make_routing(exp_start=exp_start), stream)
+    for _ in range(args.warmup):
+        B.moe_ffn_prefill(layer.handle, x, n, out, ws, ws.numel(), None, stream)
+    torch.cuda.synchronize()
+    counts = np.diff(exp_start.cpu().numpy())
+
+    hip = HipEvents()
+    evs = [hip.create(B.N_STAGE_EVENTS) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        B.moe_ffn_prefill_profiled(layer.handle, x, n, out, ws, ws.numel(), evs[i], None, stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    stage_ms = {name: 0.0 for name in B.STAGES}
+    for i in range(args.steps):
+        for j, name in enumerate(B.STAGES):
+            stage_ms[name] += hip.elapsed_ms(evs[i][j], evs[i][j + 1]) / args.steps
+    for e in evs:
+        hip.destroy(e)
+
+    gu_ops, dn_ops = gemm_ops(s, n)
+    sb = stage_bytes(s, n, counts)
+    gu_us = stage_ms["gateup_swiglu"] * 1e3
+    dn_us = stage_ms["down"] * 1e3
+    gu_tops = gu_ops / (gu_us * 1e-6) / 1e12
+    roofline = {"bound": "mfma", "kernel": "gateup_kernel (grouped gate/up + SwiGLU + requant)",
+                "achieved": round(gu_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                "frac": round(gu_tops / INT8_PEAK_TOPS, 4),
+                "traffic": read_traffic("gateup_olmoe_n2048") if args.workload == "olmoe_n2048" else None,
+                "algorithmic_ops_per_launch": gu_ops, "avg_launch_us": round(gu_us, 2)}
+    stages = {}
+    for name in B.STAGES:
+        us = stage_ms[name] * 1e3
+        ent = {"avg_us": round(us, 2)}
+        if name in sb:
+            ent["hbm_GBps_algorithmic"] = round(sb[name] / (us * 1e-6) / 1e9, 1)
+            ent["hbm_frac"] = round(sb[name] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        stages[name] = ent
+    stages["gateup_swiglu"]["int8_TOPs"] = round(gu_tops, 1)
+    stages["down"]["int8_TOPs"] = round(dn_ops / (dn_us * 1e-6) / 1e12, 1)
+    gemm_frac = (gu_ops + dn_ops) / ((gu_us + dn_us) * 1e-6) / 1e12 / INT8_PEAK_TOPS
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("[bench] timing the CPU oracle sample")
+        cpu = cpu_baseline(lw, x_np, args.cpu_seconds)
+
+    res = {
+        "metric": METRIC, "value": round(n / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights packed as Q8_0)",
+        "config": {"workload": args.workload, **{k: v for k, v in mw.describe(args.workload).items()
+                                                 if k != "workload"}},
+        "grouped_gemm_int8_frac": round(gemm_frac, 4),
+        "experts_touched": int((counts[:s.n_experts] > 0).sum()),
+        "stages": stages, "roofline": roofline, "cpu_baseline": cpu,
+    }
+    layer.close()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

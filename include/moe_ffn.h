@@ -1,0 +1,206 @@
+/*
+ * moe_ffn.h -- C ABI of the MI355X (gfx950) batched routed-MoE FFN library
+ * (libmoe_ffn.so).
+ *
+ * The operation is the batched MoE FFN over N prompt tokens described in the
+ * SharpInference issue pages:
+ *   #406 "batched int8-MMQ trunk prefill gated off for MoE", "The work" item 2:
+ *        batch the router over N tokens, group tokens per expert, run a
+ *        grouped/segmented expert GEMM, scatter the results back;
+ *        "argmax-stable (int8 MMQ)" is the accepted numeric contract;
+ *   #388 "Carnice prefill toward llama.cpp 676 t/s", "Remaining levers" 1:
+ *        router matvec + softmax + top-k + shared-expert gate on the GPU, with
+ *        the expert bucketing (expStart / expTokI / expTokK CSR) built on the
+ *        GPU so that the selection never round-trips to the host;
+ *   #408 "full-offload MoE decode", "Hypothesis": 64 experts / 8 active,
+ *        norm_topk_prob=false; one fused gathered-expert launch instead of
+ *        per-expert matvecs; int8 (Q8_1-style) activations;
+ *   #129 (batched weighted scatter-reduce), "Scope": per token, the na
+ *        unweighted down-partials are summed in top-k slot order with their
+ *        weights, then the shared-expert row is added, in one launch over
+ *        N x embDim.
+ *
+ * Numerics (what every entry point computes):
+ *   logit[t][e]  = fp32 fused multiply-add chain over ascending j of
+ *                  x[t][j] * router_w[e][j], from +0, then + bias[e];
+ *   top-k        = experts by (logit descending, id ascending); slot s = rank s;
+ *   w[t][s]      = softmax over all E logits at ids[t][s]; divided by the sum
+ *                  of the k picks when norm_topk_prob;
+ *   gs[t]        = sigmoid(x[t] . shared_gate_vec) when a shared expert exists;
+ *   activations  = per-32-block int8 codes rint(x * 127/amax) (half to even)
+ *                  with a binary16 scale amax/127; zero block -> zeros;
+ *   expert FFN   = g, u = int8 block dot products (exact int32 per block,
+ *                  times activation-scale * weight-scale, summed in fp32);
+ *                  h = silu(g) * u, requantised per 32 like the activations;
+ *                  y = int8 dot of h with the down rows (unweighted partial);
+ *   out[t][j]    = fp32 fused multiply-add chain from +0 over s = 0..k-1 of
+ *                  w[t][s] * y_s[j], then gs[t] * shared_y[j] when present.
+ *
+ * Conventions:
+ *   - Every pointer argument is a DEVICE pointer unless stated otherwise.
+ *     Struct arguments (dims, routing) are host memory.
+ *   - Every call returns a moe_ffn_status.  Arguments are validated on the
+ *     host before anything is enqueued; on an error nothing is enqueued.  The
+ *     library never aborts and never throws.
+ *   - Work is enqueued on the caller's stream and the call returns without a
+ *     host synchronisation, except moe_ffn_weights_create, which synchronises
+ *     its stream before returning.  Device faults surface at the caller's next
+ *     synchronisation.
+ *   - A weights handle is immutable after creation and may be shared by
+ *     concurrent calls; concurrent calls need their own workspaces.
+ *   - Supported shapes: d, ffn, shared_ffn multiples of 32 (internally
+ *     zero-padded to multiples of 128); 1 <= n_experts <= 256;
+ *     1 <= top_k <= min(n_experts, 16); 0 <= n_tokens <= the max_tokens the
+ *     workspace was sized for.  n_tokens == 0 is a no-op.
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_ffn_status {
+  MOE_FFN_OK = 0,
+  MOE_FFN_INVALID_ARG = -1,        /* NULL pointer, bad shape, aliasing, N out of range */
+  MOE_FFN_UNSUPPORTED = -2,        /* a shape outside the supported set */
+  MOE_FFN_WORKSPACE_TOO_SMALL = -3,/* ws_bytes below moe_ffn_workspace_size(n_tokens) */
+  MOE_FFN_OUT_OF_MEMORY = -4,      /* device allocation failed (weights create) */
+  MOE_FFN_HIP_ERROR = -5           /* a HIP runtime call or launch failed */
+} moe_ffn_status;
+
+/* Layer shape.  norm_topk_prob: #408 "Hypothesis" names it; OLMoE uses 0. */
+typedef struct moe_ffn_dims {
+  int32_t d_model;        /* hidden size d */
+  int32_t n_experts;      /* routed experts E */
+  int32_t top_k;          /* active experts per token (na) */
+  int32_t d_ffn;          /* routed expert intermediate size F */
+  int32_t d_shared_ffn;   /* shared expert intermediate size, 0 = no shared expert */
+  int32_t norm_topk_prob; /* 1: renormalise the k selected softmax weights */
+} moe_ffn_dims;
+
+/* Opaque, library-owned device copy of one layer's weights in the layout the
+ * kernels read (int8 code planes in MFMA operand order plus binary16 scale
+ * planes; the router matrix transposed). */
+typedef struct moe_ffn_weights moe_ffn_weights;
+
+/* Optional caller-owned device buffers that receive the routing decisions and
+ * intermediate products of a call (for parity checks).  Any member may be
+ * NULL.  Shapes: topk_ids / topk_w [N][k]; shared_gate [N]; exp_start
+ * [E+1(+1 with a shared expert)]; exp_tok_i / exp_tok_k [N*k (+N)]; xq [N][d]
+ * int8; xs [N][d/32] binary16 bits; partial [N][k(+1)][d] fp32 unweighted
+ * expert outputs, slot k holding the shared expert. */
+typedef struct moe_ffn_routing {
+  int32_t* topk_ids;
+  float* topk_w;
+  float* shared_gate;
+  int32_t* exp_start;
+  int32_t* exp_tok_i;
+  int32_t* exp_tok_k;
+  int8_t* xq;
+  uint16_t* xs;
+  float* partial;
+} moe_ffn_routing;
+
+/* Build a weights handle (load time; #388 "Measurement discipline": one-time
+ * setup belongs at load, not in the timed path).
+ *   router_w     fp32 [E][d] row-major.
+ *   router_bias  fp32 [E], or NULL for no bias (added to the logits before
+ *                both the top-k and the softmax).
+ *   gate_q8, up_q8   Q8_0 [E][F][d/32] blocks of 34 bytes {binary16 scale,
+ *                int8 q[32]}, rows contiguous, unpadded (#406 "References":
+ *                Q8_0 MMQ).
+ *   down_q8      Q8_0 [E][d][F/32] blocks.
+ *   sh_gate_q8, sh_up_q8 [Fs][d/32], sh_down_q8 [d][Fs/32], sh_gate_vec fp32
+ *                [d]: the shared expert and its gate; all NULL when
+ *                d_shared_ffn == 0, all non-NULL otherwise.
+ * The inputs are read on `stream`; the call synchronises `stream` before it
+ * returns, after which the caller may free them.  On success *out owns
+ * device memory released by moe_ffn_weights_destroy. */
+int moe_ffn_weights_create(const moe_ffn_dims* dims, const float* router_w,
+                           const float* router_bias, const void* gate_q8, const void* up_q8,
+                           const void* down_q8, const void* sh_gate_q8, const void* sh_up_q8,
+                           const void* sh_down_q8, const float* sh_gate_vec, hipStream_t stream,
+                           moe_ffn_weights** out);
+
+/* Release a handle (NULL is accepted).  The caller must ensure no enqueued
+ * work still reads it. */
+int moe_ffn_weights_destroy(moe_ffn_weights* w);
+
+/* Host-side query: the dims a handle was built with. */
+int moe_ffn_weights_dims(const moe_ffn_weights* w, moe_ffn_dims* dims_out);
+
+/* Workspace bytes needed by a prefill or decode call over up to max_tokens
+ * tokens (host-side query, nothing enqueued). */
+int moe_ffn_workspace_size(const moe_ffn_weights* w, int32_t max_tokens, size_t* bytes);
+
+/* The batched MoE FFN over n_tokens tokens (#406 "The work" item 2):
+ * router + top-k + weights (+ shared gate), per-32 int8 quantiser, CSR
+ * bucketing, one grouped gate/up + SwiGLU int8 GEMM launch over all experts
+ * (and the shared expert), one grouped down GEMM launch, and the ordered
+ * combine (#129 "Scope").
+ *   x        fp32 [n_tokens][d], not modified.
+ *   out      fp32 [n_tokens][d]; must not overlap x or the workspace.
+ *   ws       device workspace of ws_bytes >= moe_ffn_workspace_size(n_tokens),
+ *            256-byte aligned; contents on entry are ignored.
+ *   routing  NULL, or optional outputs (see moe_ffn_routing).
+ * Returns without a host synchronisation. */
+int moe_ffn_prefill(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* out,
+                    void* ws, size_t ws_bytes, const moe_ffn_routing* routing,
+                    hipStream_t stream);
+
+/* moe_ffn_prefill with stage timing (#388 "Measurement discipline": per-phase
+ * timing buckets measured warm, with setup excluded).  stage_events points to
+ * MOE_FFN_N_STAGE_EVENTS caller-created hipEvent_t handles (host array); event
+ * i is recorded on `stream` before stage i and the last one after the final
+ * stage, so hipEventElapsedTime(ev[i], ev[i+1]) is the device time of stage i:
+ * 0 router logits, 1 routing + quantiser, 2 bucketing, 3 grouped gate/up +
+ * SwiGLU, 4 grouped down, 5 combine.  Same arguments and results as
+ * moe_ffn_prefill otherwise. */
+#define MOE_FFN_N_STAGE_EVENTS 7
+int moe_ffn_prefill_profiled(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* out,
+                             void* ws, size_t ws_bytes, const moe_ffn_routing* routing,
+                             hipStream_t stream, hipEvent_t* stage_events);
+
+/* Decode / small batch (#408 "Hypothesis" lever 1): the same computation for
+ * 1 <= n_tokens <= 8, with the expert FFN run by one gathered launch per
+ * stage in which each selected expert's weights are read once for all the
+ * tokens that picked it.  Returns MOE_FFN_INVALID_ARG for n_tokens outside
+ * [1, 8]. */
+int moe_ffn_decode(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* out,
+                   void* ws, size_t ws_bytes, const moe_ffn_routing* routing,
+                   hipStream_t stream);
+
+/* Stage entry point: the ordered weighted combine on its own (#129 "Scope").
+ * partial fp32 [n][kk][d] (kk = k, or k+1 when shared_gate != NULL, slot k
+ * being the shared row), topk_w fp32 [n][k], shared_gate fp32 [n] or NULL,
+ * out fp32 [n][d] (must not overlap the inputs).  1 <= k <= 16. */
+int moe_ffn_combine(const float* partial, const float* topk_w, const float* shared_gate,
+                    int32_t n, int32_t k, int32_t d, float* out, hipStream_t stream);
+
+/* Stage entry point: the per-32-block int8 activation quantiser on its own.
+ * v fp32 [n_values] (n_values % 32 == 0), q int8 [n_values], scales
+ * binary16 bits [n_values/32]. */
+int moe_ffn_quantize(const float* v, int64_t n_values, int8_t* q, uint16_t* scales,
+                     hipStream_t stream);
+
+/* Layer-stack helper (residual + RMSNorm between MoE layers; #388 "Why 676
+ * needs a per-layer rewrite": the residual stream is sequential across
+ * layers).  h fp32 [n][d] is updated in place to h + y when y != NULL (y
+ * fp32 [n][d]); then xn fp32 [n][d] receives h / sqrt(mean(h^2) + eps)
+ * (unit gain).  xn must not overlap h or y. */
+int moe_ffn_residual_rmsnorm(float* h, const float* y, float* xn, int32_t n, int32_t d,
+                             float eps, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* moe_ffn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_FFN_H */

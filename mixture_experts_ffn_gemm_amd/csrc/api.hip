@@ -1,0 +1,414 @@
+// api.hip -- host side of libmoe_ffn: argument validation, the weights handle,
+// workspace carving and the launch sequence of one MoE FFN layer.
+//
+// One prefill call enqueues, on the caller's stream and without any host
+// synchronisation or device-to-host transfer (SharpInference #388 "Remaining
+// levers" 1: the selection must not round-trip to the host):
+//   1. router logits            (fp32 fused-chain matvec, all experts)
+//   2. routing                  (top-k, softmax weights, shared gate, int8 x,
+//                                per-tile expert histograms and ranks)
+//   3. bucketing                (CSR expStart/expTokI/expTokK + 32-row tile table)
+//   4. grouped gate/up + SwiGLU (one launch over all experts + shared expert)
+//   5. grouped down             (one launch; unweighted partials per slot)
+//   6. ordered combine          (#129 "Scope")
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "internal.h"
+
+using namespace moe;
+
+namespace moe {
+
+WsLayout ws_layout(const Dims& dm, int max_tokens) {
+  WsLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return o;
+  };
+  const size_t Nn = (size_t)std::max(max_tokens, 1);
+  const size_t kk = (size_t)dm.k + dm.has_shared;
+  const size_t P_total = Nn * dm.k + (dm.has_shared ? Nn : 0);
+  L.n_route_tiles = (int)((Nn + ROUTE_TILE - 1) / ROUTE_TILE);
+  L.tile_bound = (int)((P_total + (size_t)(MT - 1) * dm.G) / MT + 1);
+  const size_t kbmax = (size_t)dm.kmax_pad / QB;
+  L.logits = take(Nn * dm.E * 4);
+  L.ids = take(Nn * dm.k * 4);
+  L.rank = take(Nn * dm.k * 4);
+  L.w = take(Nn * dm.k * 4);
+  L.gs = take(Nn * 4);
+  L.xq = take(Nn * dm.d_pad);
+  L.xs = take(Nn * (dm.d_pad / QB) * 2);
+  L.hist = take((size_t)L.n_route_tiles * dm.E * 4);
+  L.exp_start = take((size_t)(dm.E + 2) * 4);
+  L.tok_i = take(P_total * 4);
+  L.tok_k = take(P_total * 4);
+  L.tiles = take((4 + 3 * (size_t)L.tile_bound) * 4);
+  L.hq = take((size_t)L.tile_bound * kbmax * 1024);
+  L.hs = take((size_t)L.tile_bound * 32 * kbmax * 2);
+  L.partial = take(Nn * kk * dm.d * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace moe
+
+namespace {
+
+constexpr int MAX_TOKENS = 1 << 20;
+
+int check_dims(const moe_ffn_dims* u) {
+  if (!u) return MOE_FFN_INVALID_ARG;
+  if (u->d_model <= 0 || u->d_ffn <= 0 || u->d_shared_ffn < 0 || u->n_experts <= 0 || u->top_k <= 0)
+    return MOE_FFN_INVALID_ARG;
+  if (u->norm_topk_prob != 0 && u->norm_topk_prob != 1) return MOE_FFN_INVALID_ARG;
+  if (u->top_k > u->n_experts) return MOE_FFN_INVALID_ARG;
+  if (u->d_model % QB || u->d_ffn % QB || u->d_shared_ffn % QB) return MOE_FFN_UNSUPPORTED;
+  if (u->n_experts > MAX_EXPERTS || u->top_k > MAX_TOPK) return MOE_FFN_UNSUPPORTED;
+  if (u->d_model > (1 << 16) || u->d_ffn > (1 << 16) || u->d_shared_ffn > (1 << 16))
+    return MOE_FFN_UNSUPPORTED;
+  return MOE_FFN_OK;
+}
+
+Dims make_dims(const moe_ffn_dims* u) {
+  Dims dm{};
+  dm.d = u->d_model;
+  dm.E = u->n_experts;
+  dm.k = u->top_k;
+  dm.F = u->d_ffn;
+  dm.Fs = u->d_shared_ffn;
+  dm.norm = u->norm_topk_prob;
+  dm.has_shared = u->d_shared_ffn > 0 ? 1 : 0;
+  dm.d_pad = round_up(dm.d, KPAD);
+  dm.F_pad = round_up(dm.F, KPAD);
+  dm.Fs_pad = dm.has_shared ? round_up(dm.Fs, KPAD) : 0;
+  dm.kmax_pad = std::max(dm.F_pad, dm.Fs_pad);
+  dm.E64 = round_up(dm.E, 64);
+  dm.G = dm.E + dm.has_shared;
+  return dm;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+  return na && nb && pa < pb + nb && pb < pa + na;
+}
+
+#define HIP_TRY(expr)                                   \
+  do {                                                  \
+    if ((expr) != hipSuccess) return MOE_FFN_HIP_ERROR; \
+  } while (0)
+
+int current_device_matches(const moe_ffn_weights* w) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_FFN_HIP_ERROR;
+  return dev == w->device ? MOE_FFN_OK : MOE_FFN_INVALID_ARG;
+}
+
+int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, void* ws,
+              size_t ws_bytes, const moe_ffn_routing* r, hipStream_t s, hipEvent_t* ev = nullptr) {
+  if (!W || n < 0 || n > MAX_TOKENS) return MOE_FFN_INVALID_ARG;
+  if (n == 0) return current_device_matches(W);  // no-op; buffers may be NULL
+  if (!x || !out || !ws) return MOE_FFN_INVALID_ARG;
+  const Dims& dm = W->dm;
+  const WsLayout L = ws_layout(dm, n);
+  if (ws_bytes < L.total) return MOE_FFN_WORKSPACE_TOO_SMALL;
+  if (((uintptr_t)ws & 255u) || ((uintptr_t)x & 15u) || ((uintptr_t)out & 15u))
+    return MOE_FFN_INVALID_ARG;
+  const size_t xb = (size_t)n * dm.d * sizeof(float);
+  if (overlaps(x, xb, out, xb) || overlaps(out, xb, ws, ws_bytes)) return MOE_FFN_INVALID_ARG;
+  const int dev_ok = current_device_matches(W);
+  if (dev_ok != MOE_FFN_OK) return dev_ok;
+
+  char* base = (char*)ws;
+  float* logits = (float*)(base + L.logits);
+  int32_t* ids = (int32_t*)(base + L.ids);
+  int32_t* rank = (int32_t*)(base + L.rank);
+  float* w = (float*)(base + L.w);
+  float* gs = (float*)(base + L.gs);
+  int8_t* xq = (int8_t*)(base + L.xq);
+  uint16_t* xs = (uint16_t*)(base + L.xs);
+  int32_t* hist = (int32_t*)(base + L.hist);
+  int32_t* exp_start = (int32_t*)(base + L.exp_start);
+  int32_t* tok_i = (int32_t*)(base + L.tok_i);
+  int32_t* tok_k = (int32_t*)(base + L.tok_k);
+  int32_t* tiles = (int32_t*)(base + L.tiles);
+  int8_t* hq = (int8_t*)(base + L.hq);
+  uint16_t* hs = (uint16_t*)(base + L.hs);
+  float* partial = (float*)(base + L.partial);
+  const int kk = dm.k + dm.has_shared;
+  auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
+
+  HIP_TRY(mark(0));
+  HIP_TRY(launch_router_logits(x, n, dm.d, W->router_wt, W->has_bias ? W->router_bias : nullptr,
+                               dm.E, dm.E64, logits, s));
+  HIP_TRY(mark(1));
+  HIP_TRY(launch_route(logits, x, n, dm.d, dm.d_pad, dm.E, dm.k, dm.norm,
+                       dm.has_shared ? W->sh_gate_vec : nullptr, ids, w, gs, rank, xq, xs, hist, s));
+  HIP_TRY(mark(2));
+  HIP_TRY(launch_bucket(ids, rank, hist, n, dm.E, dm.k, dm.has_shared, exp_start, tok_i, tok_k,
+                        tiles, L.tile_bound, s));
+  GemmArgs a{};
+  a.tiles = tiles;
+  a.tok_i = tok_i;
+  a.tok_k = tok_k;
+  a.E = dm.E;
+  a.G = dm.G;
+  a.n_tokens = n;
+  a.p_total = n * dm.k + (dm.has_shared ? n : 0);
+  a.tile_bound = L.tile_bound;
+  a.kbmax = dm.kmax_pad / QB;
+  a.hq = hq;
+  a.hs = hs;
+  a.xq = xq;
+  a.xs = xs;
+  a.d_pad = dm.d_pad;
+  a.gu_q = W->gu_q;
+  a.gu_s = W->gu_s;
+  a.gu_q_group = W->gu_q_per_expert;
+  a.gu_s_group = W->gu_s_per_expert;
+  a.sh_gu_q = W->sh_gu_q;
+  a.sh_gu_s = W->sh_gu_s;
+  a.F_pad = dm.F_pad;
+  a.Fs_pad = dm.Fs_pad;
+  a.dn_q = W->dn_q;
+  a.dn_s = W->dn_s;
+  a.dn_q_group = W->dn_q_per_expert;
+  a.dn_s_group = W->dn_s_per_expert;
+  a.sh_dn_q = W->sh_dn_q;
+  a.sh_dn_s = W->sh_dn_s;
+  a.partial = partial;
+  a.d = dm.d;
+  a.kk = kk;
+  HIP_TRY(mark(3));
+  HIP_TRY(launch_gateup(a, s));
+  HIP_TRY(mark(4));
+  HIP_TRY(launch_down(a, s));
+  HIP_TRY(mark(5));
+  HIP_TRY(launch_combine(partial, w, dm.has_shared ? gs : nullptr, n, dm.k, kk, dm.d, out, s));
+  HIP_TRY(mark(6));
+
+  if (r) {
+    const size_t nk = (size_t)n * dm.k;
+    const size_t ptot = nk + (dm.has_shared ? (size_t)n : 0);
+    if (r->topk_ids) HIP_TRY(hipMemcpyAsync(r->topk_ids, ids, nk * 4, hipMemcpyDeviceToDevice, s));
+    if (r->topk_w) HIP_TRY(hipMemcpyAsync(r->topk_w, w, nk * 4, hipMemcpyDeviceToDevice, s));
+    if (r->shared_gate && dm.has_shared)
+      HIP_TRY(hipMemcpyAsync(r->shared_gate, gs, (size_t)n * 4, hipMemcpyDeviceToDevice, s));
+    if (r->exp_start)
+      HIP_TRY(hipMemcpyAsync(r->exp_start, exp_start, (size_t)(dm.E + 1 + dm.has_shared) * 4,
+                             hipMemcpyDeviceToDevice, s));
+    if (r->exp_tok_i) HIP_TRY(hipMemcpyAsync(r->exp_tok_i, tok_i, ptot * 4, hipMemcpyDeviceToDevice, s));
+    if (r->exp_tok_k) HIP_TRY(hipMemcpyAsync(r->exp_tok_k, tok_k, ptot * 4, hipMemcpyDeviceToDevice, s));
+    if (r->xq)
+      HIP_TRY(hipMemcpy2DAsync(r->xq, (size_t)dm.d, xq, (size_t)dm.d_pad, (size_t)dm.d, (size_t)n,
+                               hipMemcpyDeviceToDevice, s));
+    if (r->xs)
+      HIP_TRY(hipMemcpy2DAsync(r->xs, (size_t)(dm.d / QB) * 2, xs, (size_t)(dm.d_pad / QB) * 2,
+                               (size_t)(dm.d / QB) * 2, (size_t)n, hipMemcpyDeviceToDevice, s));
+    if (r->partial)
+      HIP_TRY(hipMemcpyAsync(r->partial, partial, (size_t)n * kk * dm.d * 4, hipMemcpyDeviceToDevice, s));
+  }
+  return MOE_FFN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_ffn_weights_create(const moe_ffn_dims* dims, const float* router_w,
+                           const float* router_bias, const void* gate_q8, const void* up_q8,
+                           const void* down_q8, const void* sh_gate_q8, const void* sh_up_q8,
+                           const void* sh_down_q8, const float* sh_gate_vec, hipStream_t stream,
+                           moe_ffn_weights** out) {
+  if (!out) return MOE_FFN_INVALID_ARG;
+  *out = nullptr;
+  const int rc = check_dims(dims);
+  if (rc != MOE_FFN_OK) return rc;
+  if (!router_w || !gate_q8 || !up_q8 || !down_q8) return MOE_FFN_INVALID_ARG;
+  const bool has_sh = dims->d_shared_ffn > 0;
+  const bool any_sh = sh_gate_q8 || sh_up_q8 || sh_down_q8 || sh_gate_vec;
+  const bool all_sh = sh_gate_q8 && sh_up_q8 && sh_down_q8 && sh_gate_vec;
+  if (has_sh ? !all_sh : any_sh) return MOE_FFN_INVALID_ARG;
+
+  moe_ffn_weights* W = new (std::nothrow) moe_ffn_weights();
+  if (!W) return MOE_FFN_OUT_OF_MEMORY;
+  W->user = *dims;
+  W->dm = make_dims(dims);
+  const Dims& dm = W->dm;
+  if (hipGetDevice(&W->device) != hipSuccess) {
+    delete W;
+    return MOE_FFN_HIP_ERROR;
+  }
+  W->has_bias = router_bias ? 1 : 0;
+  W->gu_q_per_expert = (size_t)dm.F_pad * dm.d_pad * 2;
+  W->gu_s_per_expert = (size_t)dm.F_pad * 2 * (dm.d_pad / QB);
+  W->dn_q_per_expert = (size_t)dm.d_pad * dm.F_pad;
+  W->dn_s_per_expert = (size_t)dm.d_pad * (dm.F_pad / QB);
+  const size_t sh_gu_q = (size_t)dm.Fs_pad * dm.d_pad * 2, sh_gu_s = (size_t)dm.Fs_pad * 2 * (dm.d_pad / QB);
+  const size_t sh_dn_q = (size_t)dm.d_pad * dm.Fs_pad, sh_dn_s = (size_t)dm.d_pad * (dm.Fs_pad / QB);
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return o;
+  };
+  const size_t o_rw = take((size_t)dm.d * dm.E64 * 4);
+  const size_t o_rb = take((size_t)dm.E * 4);
+  const size_t o_sg = take((size_t)dm.d * 4);
+  const size_t o_guq = take(W->gu_q_per_expert * dm.E);
+  const size_t o_gus = take(W->gu_s_per_expert * 2 * dm.E);
+  const size_t o_dnq = take(W->dn_q_per_expert * dm.E);
+  const size_t o_dns = take(W->dn_s_per_expert * 2 * dm.E);
+  const size_t o_sguq = take(sh_gu_q), o_sgus = take(sh_gu_s * 2);
+  const size_t o_sdnq = take(sh_dn_q), o_sdns = take(sh_dn_s * 2);
+  if (hipMalloc(&W->base, off) != hipSuccess) {
+    (void)hipGetLastError();
+    delete W;
+    return MOE_FFN_OUT_OF_MEMORY;
+  }
+  char* b = (char*)W->base;
+  W->router_wt = (float*)(b + o_rw);
+  W->router_bias = (float*)(b + o_rb);
+  W->sh_gate_vec = (float*)(b + o_sg);
+  W->gu_q = (int8_t*)(b + o_guq);
+  W->gu_s = (uint16_t*)(b + o_gus);
+  W->dn_q = (int8_t*)(b + o_dnq);
+  W->dn_s = (uint16_t*)(b + o_dns);
+  W->sh_gu_q = has_sh ? (int8_t*)(b + o_sguq) : nullptr;
+  W->sh_gu_s = has_sh ? (uint16_t*)(b + o_sgus) : nullptr;
+  W->sh_dn_q = has_sh ? (int8_t*)(b + o_sdnq) : nullptr;
+  W->sh_dn_s = has_sh ? (uint16_t*)(b + o_sdns) : nullptr;
+
+  const int nbd = dm.d / QB, nbf = dm.F / QB;
+  hipError_t e = hipSuccess;
+  if (e == hipSuccess) e = launch_transpose_router(router_w, dm.E, dm.d, dm.E64, W->router_wt, stream);
+  if (e == hipSuccess)
+    e = router_bias ? hipMemcpyAsync(W->router_bias, router_bias, (size_t)dm.E * 4, hipMemcpyDeviceToDevice, stream)
+                    : hipMemsetAsync(W->router_bias, 0, (size_t)dm.E * 4, stream);
+  if (e == hipSuccess)
+    e = has_sh ? hipMemcpyAsync(W->sh_gate_vec, sh_gate_vec, (size_t)dm.d * 4, hipMemcpyDeviceToDevice, stream)
+               : hipMemsetAsync(W->sh_gate_vec, 0, (size_t)dm.d * 4, stream);
+  if (e == hipSuccess)
+    e = launch_repack_q8((const uint8_t*)gate_q8, (const uint8_t*)up_q8, dm.E,
+                         (size_t)dm.F * nbd * Q8_BYTES, dm.F, nbd, 2, dm.F_pad / GU_COLS, dm.d_pad / QB,
+                         W->gu_q, W->gu_s, W->gu_q_per_expert, W->gu_s_per_expert, stream);
+  if (e == hipSuccess)
+    e = launch_repack_q8((const uint8_t*)down_q8, (const uint8_t*)down_q8, dm.E,
+                         (size_t)dm.d * nbf * Q8_BYTES, dm.d, nbf, 4, dm.d_pad / DN_COLS, dm.F_pad / QB,
+                         W->dn_q, W->dn_s, W->dn_q_per_expert, W->dn_s_per_expert, stream);
+  if (e == hipSuccess && has_sh) {
+    const int nbs = dm.Fs / QB;
+    e = launch_repack_q8((const uint8_t*)sh_gate_q8, (const uint8_t*)sh_up_q8, 1,
+                         (size_t)dm.Fs * nbd * Q8_BYTES, dm.Fs, nbd, 2, dm.Fs_pad / GU_COLS,
+                         dm.d_pad / QB, W->sh_gu_q, W->sh_gu_s, sh_gu_q, sh_gu_s, stream);
+    if (e == hipSuccess)
+      e = launch_repack_q8((const uint8_t*)sh_down_q8, (const uint8_t*)sh_down_q8, 1,
+                           (size_t)dm.d * nbs * Q8_BYTES, dm.d, nbs, 4, dm.d_pad / DN_COLS,
+                           dm.Fs_pad / QB, W->sh_dn_q, W->sh_dn_s, sh_dn_q, sh_dn_s, stream);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipFree(W->base);
+    delete W;
+    return MOE_FFN_HIP_ERROR;
+  }
+  *out = W;
+  return MOE_FFN_OK;
+}
+
+int moe_ffn_weights_destroy(moe_ffn_weights* w) {
+  if (!w) return MOE_FFN_OK;
+  const hipError_t e = hipFree(w->base);
+  delete w;
+  return e == hipSuccess ? MOE_FFN_OK : MOE_FFN_HIP_ERROR;
+}
+
+int moe_ffn_weights_dims(const moe_ffn_weights* w, moe_ffn_dims* dims_out) {
+  if (!w || !dims_out) return MOE_FFN_INVALID_ARG;
+  *dims_out = w->user;
+  return MOE_FFN_OK;
+}
+
+int moe_ffn_workspace_size(const moe_ffn_weights* w, int32_t max_tokens, size_t* bytes) {
+  if (!w || !bytes || max_tokens < 0 || max_tokens > MAX_TOKENS) return MOE_FFN_INVALID_ARG;
+  *bytes = ws_layout(w->dm, max_tokens).total;
+  return MOE_FFN_OK;
+}
+
+int moe_ffn_prefill(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* out,
+                    void* ws, size_t ws_bytes, const moe_ffn_routing* routing, hipStream_t stream) {
+  return run_layer(w, x, n_tokens, out, ws, ws_bytes, routing, stream);
+}
+
+int moe_ffn_prefill_profiled(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* out,
+                             void* ws, size_t ws_bytes, const moe_ffn_routing* routing,
+                             hipStream_t stream, hipEvent_t* stage_events) {
+  if (!stage_events) return MOE_FFN_INVALID_ARG;
+  for (int i = 0; i < MOE_FFN_N_STAGE_EVENTS; ++i)
+    if (!stage_events[i]) return MOE_FFN_INVALID_ARG;
+  return run_layer(w, x, n_tokens, out, ws, ws_bytes, routing, stream, stage_events);
+}
+
+int moe_ffn_decode(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* out, void* ws,
+                   size_t ws_bytes, const moe_ffn_routing* routing, hipStream_t stream) {
+  if (n_tokens < 1 || n_tokens > DECODE_MAX_TOKENS) return MOE_FFN_INVALID_ARG;
+  return run_layer(w, x, n_tokens, out, ws, ws_bytes, routing, stream);
+}
+
+int moe_ffn_combine(const float* partial, const float* topk_w, const float* shared_gate, int32_t n,
+                    int32_t k, int32_t d, float* out, hipStream_t stream) {
+  if (n < 0 || k < 1 || k > MAX_TOPK || d <= 0) return MOE_FFN_INVALID_ARG;
+  if (d % 4) return MOE_FFN_UNSUPPORTED;
+  if (n == 0) return MOE_FFN_OK;
+  if (!partial || !topk_w || !out) return MOE_FFN_INVALID_ARG;
+  if (((uintptr_t)partial & 15u) || ((uintptr_t)out & 15u)) return MOE_FFN_UNSUPPORTED;
+  const int kk = k + (shared_gate ? 1 : 0);
+  const size_t pb = (size_t)n * kk * d * 4, ob = (size_t)n * d * 4;
+  if (overlaps(out, ob, partial, pb) || overlaps(out, ob, topk_w, (size_t)n * k * 4) ||
+      (shared_gate && overlaps(out, ob, shared_gate, (size_t)n * 4)))
+    return MOE_FFN_INVALID_ARG;
+  HIP_TRY(launch_combine(partial, topk_w, shared_gate, n, k, kk, d, out, stream));
+  return MOE_FFN_OK;
+}
+
+int moe_ffn_quantize(const float* v, int64_t n_values, int8_t* q, uint16_t* scales,
+                     hipStream_t stream) {
+  if (n_values < 0) return MOE_FFN_INVALID_ARG;
+  if (n_values % QB) return MOE_FFN_UNSUPPORTED;
+  if (n_values == 0) return MOE_FFN_OK;
+  if (!v || !q || !scales) return MOE_FFN_INVALID_ARG;
+  HIP_TRY(launch_quantize(v, n_values, q, scales, stream));
+  return MOE_FFN_OK;
+}
+
+int moe_ffn_residual_rmsnorm(float* h, const float* y, float* xn, int32_t n, int32_t d, float eps,
+                             hipStream_t stream) {
+  if (n < 0 || d <= 0 || !(eps >= 0.0f)) return MOE_FFN_INVALID_ARG;
+  if (n == 0) return MOE_FFN_OK;
+  if (!h || !xn) return MOE_FFN_INVALID_ARG;
+  const size_t b = (size_t)n * d * 4;
+  if (overlaps(xn, b, h, b) || (y && overlaps(xn, b, y, b))) return MOE_FFN_INVALID_ARG;
+  HIP_TRY(launch_residual_rmsnorm(h, y, xn, n, d, eps, stream));
+  return MOE_FFN_OK;
+}
+
+const char* moe_ffn_status_str(int status) {
+  switch (status) {
+    case MOE_FFN_OK: return "ok";
+    case MOE_FFN_INVALID_ARG: return "invalid argument";
+    case MOE_FFN_UNSUPPORTED: return "unsupported shape";
+    case MOE_FFN_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_FFN_OUT_OF_MEMORY: return "out of device memory";
+    case MOE_FFN_HIP_ERROR: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

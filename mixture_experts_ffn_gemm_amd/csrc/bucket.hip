@@ -1,0 +1,121 @@
+// bucket.hip -- expert bucketing on the GPU (SharpInference #388 "Remaining
+// levers" 1: the expStart / expTokI / expTokK CSR must be built on the GPU or the
+// selection round-trips to the host).
+//
+// The routing kernel left, per 16-token tile, a histogram of expert counts and
+// each (token, slot) pair's rank among the tile's pairs of the same expert.  A
+// pair's CSR position is then
+//     expStart[e] + (pairs of e in earlier tiles) + rank,
+// which keeps every expert's rows in (token, slot) order -- a stable counting
+// sort with no atomics, so the result is deterministic.  Workgroup 0 also
+// writes expStart and the table of 32-row tiles that drives the grouped GEMMs.
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+// Exclusive prefix sum of up to 512 ints held in s[0..n) (in place), 256 threads.
+__device__ void block_exclusive_scan_512(int* s, int n, int* s_tmp /* 256 */) {
+  const int t = threadIdx.x;
+  const int a = (2 * t < n) ? s[2 * t] : 0;
+  const int b = (2 * t + 1 < n) ? s[2 * t + 1] : 0;
+  s_tmp[t] = a + b;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int v = (t >= off) ? s_tmp[t - off] : 0;
+    __syncthreads();
+    s_tmp[t] += v;
+    __syncthreads();
+  }
+  const int excl = s_tmp[t] - (a + b);
+  __syncthreads();
+  if (2 * t < n) s[2 * t] = excl;
+  if (2 * t + 1 < n) s[2 * t + 1] = excl + a;
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void bucket_kernel(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ rank,
+    const int32_t* __restrict__ hist, int n, int E, int k, int has_shared, int n_tiles,
+    int32_t* __restrict__ exp_start, int32_t* __restrict__ tok_i, int32_t* __restrict__ tok_k,
+    int32_t* __restrict__ tiles, int tile_bound) {
+  __shared__ int s_start[2 * 256 + 2];
+  __shared__ int s_pre[MAX_EXPERTS];
+  __shared__ int s_cnt[MAX_EXPERTS + 1];
+  __shared__ int s_tmp[256];
+  const int tile = blockIdx.x;
+  const int P = n * k;
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int tot = 0, pre = 0;
+    for (int tt = 0; tt < n_tiles; ++tt) {
+      const int h = hist[(size_t)tt * E + e];
+      tot += h;
+      pre += (tt < tile) ? h : 0;
+    }
+    s_start[e] = tot;
+    s_cnt[e] = tot;
+    s_pre[e] = pre;
+  }
+  __syncthreads();
+  block_exclusive_scan_512(s_start, E, s_tmp);
+
+  const int t0 = tile * ROUTE_TILE;
+  const int nt = min(ROUTE_TILE, n - t0);
+  for (int q = threadIdx.x; q < nt * k; q += 256) {
+    const int t = t0 + q / k, s = q % k;
+    const int e = ids[(size_t)t * k + s];
+    const int pos = s_start[e] + s_pre[e] + rank[(size_t)t * k + s];
+    if ((unsigned)pos < (unsigned)P) {
+      tok_i[pos] = t;
+      tok_k[pos] = s;
+    }
+  }
+  if (has_shared)
+    for (int q = threadIdx.x; q < nt; q += 256) {
+      tok_i[P + t0 + q] = t0 + q;
+      tok_k[P + t0 + q] = k;
+    }
+
+  if (tile != 0) return;
+  // expStart, then the 32-row tile table over the E (+1) groups
+  for (int e = threadIdx.x; e <= E; e += 256) exp_start[e] = (e < E) ? s_start[e] : P;
+  if (has_shared && threadIdx.x == 0) exp_start[E + 1] = P + n;
+  const int G = E + has_shared;
+  if (threadIdx.x == 0 && has_shared) s_cnt[E] = n;
+  __syncthreads();
+  __shared__ int s_nt[2 * 256 + 2];
+  for (int g = threadIdx.x; g < G; g += 256) s_nt[g] = (s_cnt[g] + MT - 1) / MT;
+  __syncthreads();
+  const int last_nt = s_nt[G - 1];
+  block_exclusive_scan_512(s_nt, G, s_tmp);
+  for (int g = threadIdx.x; g < G; g += 256) {
+    const int c = s_cnt[g];
+    const int first = (g < E) ? s_start[g] : P;
+    const int ntg = (c + MT - 1) / MT;
+    for (int i = 0; i < ntg && s_nt[g] + i < tile_bound; ++i) {
+      int32_t* ent = tiles + 4 + 3 * (size_t)(s_nt[g] + i);
+      ent[0] = g;
+      ent[1] = first + i * MT;
+      ent[2] = first + c;
+    }
+  }
+  if (threadIdx.x == 0) {
+    tiles[0] = min(s_nt[G - 1] + last_nt, tile_bound);
+    tiles[1] = 0;
+    tiles[2] = 0;
+    tiles[3] = 0;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bucket(const int32_t* ids, const int32_t* rank, const int32_t* hist, int n, int E,
+                         int k, int has_shared, int32_t* exp_start, int32_t* tok_i, int32_t* tok_k,
+                         int32_t* tiles, int tile_bound, hipStream_t s) {
+  const int n_tiles = (n + ROUTE_TILE - 1) / ROUTE_TILE;
+  bucket_kernel<<<n_tiles, 256, 0, s>>>(ids, rank, hist, n, E, k, has_shared, n_tiles, exp_start,
+                                        tok_i, tok_k, tiles, tile_bound);
+  return hipGetLastError();
+}
+
+}  // namespace moe

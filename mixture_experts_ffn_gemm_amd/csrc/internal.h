@@ -1,0 +1,153 @@
+// internal.h -- private declarations of libmoe_ffn (HIP, gfx950 only).
+//
+// Data layout in HBM (all planes are library-owned, built at load time):
+//
+//   router_wt   fp32 [d/4][E64][4]   the router matrix transposed so that lane e
+//                                    of a wavefront reads expert e's 4 weights
+//                                    for 4 consecutive j in one 16-byte load;
+//                                    E64 = E rounded up to 64, zero rows past E.
+//   gate/up     int8 codes [F_pad/64][KB][4][2][32][16] per expert, KB = d_pad/32.
+//               One 1 KiB chunk is one 32x32 MFMA B operand: tile tt (0,1 = gate
+//               rows 64c + 32tt + r, 2,3 = up rows 64c + 32(tt-2) + r), half h of
+//               the 32-byte block, row r, 16 bytes.  Lane l of a wavefront reads
+//               bytes [16 l, 16 l + 16) of the chunk.
+//               binary16 scales [F_pad/64][4][32][KB].
+//   down        int8 codes [d_pad/128][KBF][4][2][32][16] per expert, KBF = F_pad/32,
+//               tile tt = down rows 128c + 32tt + r; scales [d_pad/128][4][32][KBF].
+//   The shared expert has its own planes of the same form (F replaced by Fs).
+//   Padding rows/blocks hold zero codes and zero scales.
+//
+// Workspace (per call, caller-allocated, carved by ws_layout()):
+//   logits fp32 [N][E]; ids, rank i32 [N][k]; w fp32 [N][k]; gs fp32 [N];
+//   xq int8 [N][d_pad]; xs fp16 [N][d_pad/32]; hist i32 [ceil(N/16)][E];
+//   exp_start i32 [E+2]; tok_i, tok_k i32 [N*k + N];
+//   tiles i32 [4 + 3*T_bound]  (tiles[0] = number of 32-row tiles, then
+//                               {group, first CSR row, end CSR row} per tile);
+//   hq int8 [T_bound][KBMAX][2][32][16]  (the down GEMM's A operand chunks);
+//   hs fp16 [T_bound][32][KBMAX];
+//   partial fp32 [N][k + has_shared][d].
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_ffn.h"
+
+namespace moe {
+
+constexpr int QB = 32;            // int8 block length (Q8_0 / activation blocks)
+constexpr int Q8_BYTES = 34;      // Q8_0 block: binary16 scale + 32 codes
+constexpr int KPAD = 128;         // K-dimension padding granule (4 blocks)
+constexpr int ROUTE_TILE = 16;    // tokens per routing workgroup
+constexpr int MT = 32;            // rows per GEMM row tile
+constexpr int GU_COLS = 64;       // SwiGLU output columns per gate/up work item
+constexpr int DN_COLS = 128;      // output columns per down work item
+constexpr int MAX_TOPK = 16;
+constexpr int MAX_EXPERTS = 256;
+constexpr int DECODE_MAX_TOKENS = 8;
+
+struct Dims {
+  int d, E, k, F, Fs, norm;
+  int has_shared;
+  int d_pad, F_pad, Fs_pad, kmax_pad;  // kmax_pad = max(F_pad, Fs_pad)
+  int E64;
+  int G;  // expert groups = E + has_shared
+};
+
+inline int round_up(int v, int m) { return (v + m - 1) / m * m; }
+
+struct WsLayout {
+  size_t logits, ids, rank, w, gs, xq, xs, hist, exp_start, tok_i, tok_k, tiles, hq, hs, partial;
+  size_t total;
+  int n_route_tiles;
+  int tile_bound;
+};
+
+WsLayout ws_layout(const Dims& dm, int max_tokens);
+
+}  // namespace moe
+
+struct moe_ffn_weights {
+  moe_ffn_dims user;
+  moe::Dims dm;
+  int device;
+  int has_bias;
+  void* base;  // one allocation holding every plane below
+  float* router_wt;
+  float* router_bias;
+  float* sh_gate_vec;
+  int8_t* gu_q;
+  uint16_t* gu_s;
+  int8_t* dn_q;
+  uint16_t* dn_s;
+  int8_t* sh_gu_q;
+  uint16_t* sh_gu_s;
+  int8_t* sh_dn_q;
+  uint16_t* sh_dn_s;
+  size_t gu_q_per_expert, gu_s_per_expert, dn_q_per_expert, dn_s_per_expert;  // elements
+};
+
+namespace moe {
+
+// ---- launchers (each returns hipGetLastError() of its launch) ----
+hipError_t launch_repack_q8(const uint8_t* src0, const uint8_t* src1, int n_groups,
+                            size_t src_group_bytes, int src_rows, int src_blocks, int tiles_per_src,
+                            int n_col_tiles, int kb_pad, int8_t* dst_q, uint16_t* dst_s,
+                            size_t dst_q_group, size_t dst_s_group, hipStream_t s);
+hipError_t launch_transpose_router(const float* w, int E, int d, int E64, float* wt, hipStream_t s);
+
+hipError_t launch_router_logits(const float* x, int n, int d, const float* wt, const float* bias,
+                                int E, int E64, float* logits, hipStream_t s);
+hipError_t launch_route(const float* logits, const float* x, int n, int d, int d_pad, int E, int k,
+                        int norm, const float* sh_gate_vec, int32_t* ids, float* w, float* gs,
+                        int32_t* rank, int8_t* xq, uint16_t* xs, int32_t* hist, hipStream_t s);
+hipError_t launch_quantize(const float* v, int64_t n_values, int8_t* q, uint16_t* scales,
+                           hipStream_t s);
+hipError_t launch_bucket(const int32_t* ids, const int32_t* rank, const int32_t* hist, int n,
+                         int E, int k, int has_shared, int32_t* exp_start, int32_t* tok_i,
+                         int32_t* tok_k, int32_t* tiles, int tile_bound, hipStream_t s);
+
+struct GemmArgs {
+  // common
+  const int32_t* tiles;
+  const int32_t* tok_i;
+  const int32_t* tok_k;
+  int E;
+  int G;          // groups: E routed (+1 shared)
+  int n_tokens;
+  int p_total;    // CSR rows: N*k (+N)
+  int tile_bound;
+  int kbmax;  // kmax_pad / 32
+  int8_t* hq;
+  uint16_t* hs;
+  // gate/up
+  const int8_t* xq;
+  const uint16_t* xs;
+  int d_pad;
+  const int8_t* gu_q;
+  const uint16_t* gu_s;
+  size_t gu_q_group, gu_s_group;
+  const int8_t* sh_gu_q;
+  const uint16_t* sh_gu_s;
+  int F_pad, Fs_pad;
+  // down
+  const int8_t* dn_q;
+  const uint16_t* dn_s;
+  size_t dn_q_group, dn_s_group;
+  const int8_t* sh_dn_q;
+  const uint16_t* sh_dn_s;
+  float* partial;
+  int d;
+  int kk;
+};
+
+hipError_t launch_gateup(const GemmArgs& a, hipStream_t s);
+hipError_t launch_down(const GemmArgs& a, hipStream_t s);
+
+hipError_t launch_combine(const float* partial, const float* w, const float* gs, int n, int k,
+                          int kk, int d, float* out, hipStream_t s);
+hipError_t launch_residual_rmsnorm(float* h, const float* y, float* xn, int n, int d, float eps,
+                                   hipStream_t s);
+
+}  // namespace moe

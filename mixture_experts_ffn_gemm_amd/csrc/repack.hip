@@ -1,0 +1,80 @@
+// repack.hip -- load-time repacking of the layer weights (not on the timed path).
+//
+// Q8_0 rows arrive as 34-byte blocks {binary16 scale, int8 q[32]} (the format of
+// the Q8_0 MMQ path in SharpInference #406 "References").  34-byte blocks are not
+// 16-byte aligned, so the int8 codes are split out into 1 KiB chunks that are
+// exactly one 32x32x32 MFMA operand in lane order, and the scales into their own
+// binary16 plane.  The repack is lossless.
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(256) void repack_q8_kernel(
+    const uint8_t* __restrict__ src0, const uint8_t* __restrict__ src1, size_t src_group_bytes,
+    int src_rows, int src_blocks, int tiles_per_src, int n_col_tiles, int kb_pad,
+    int8_t* __restrict__ dst_q, uint16_t* __restrict__ dst_s, size_t dst_q_group,
+    size_t dst_s_group) {
+  const int g = blockIdx.y;
+  const long piece = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long n_pieces = (long)n_col_tiles * kb_pad * 4 * 64;
+  if (piece >= n_pieces) return;
+  const int lane = (int)(piece % 64);
+  const int tt = (int)((piece / 64) % 4);
+  const int kb = (int)((piece / 256) % kb_pad);
+  const int c = (int)(piece / (256L * kb_pad));
+  const int half = lane / 32, r = lane % 32;
+  const int row = c * 32 * tiles_per_src + 32 * (tt % tiles_per_src) + r;
+  const uint8_t* src = (tt / tiles_per_src) ? src1 : src0;
+  const bool valid = row < src_rows && kb < src_blocks;
+  uint32_t words[4] = {0u, 0u, 0u, 0u};
+  uint16_t scale = 0;
+  if (valid) {
+    const uint8_t* blk = src + (size_t)g * src_group_bytes + ((size_t)row * src_blocks + kb) * Q8_BYTES;
+    const uint8_t* q = blk + 2 + half * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      words[i] = (uint32_t)q[4 * i] | ((uint32_t)q[4 * i + 1] << 8) | ((uint32_t)q[4 * i + 2] << 16) |
+                 ((uint32_t)q[4 * i + 3] << 24);
+    scale = (uint16_t)(blk[0] | (blk[1] << 8));
+  }
+  uint4* dq = reinterpret_cast<uint4*>(dst_q + (size_t)g * dst_q_group);
+  dq[piece] = make_uint4(words[0], words[1], words[2], words[3]);
+  if (half == 0)
+    dst_s[(size_t)g * dst_s_group + ((size_t)(c * 4 + tt) * 32 + r) * kb_pad + kb] = scale;
+}
+
+__global__ __launch_bounds__(256) void transpose_router_kernel(const float* __restrict__ w, int E,
+                                                               int d, int E64,
+                                                               float* __restrict__ wt) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;  // over (j/4, e, j%4)
+  if (i >= (long)d * E64) return;
+  const int j4 = (int)(i % 4);
+  const int e = (int)((i / 4) % E64);
+  const int jq = (int)(i / (4L * E64));
+  const int j = jq * 4 + j4;
+  wt[i] = (e < E) ? w[(size_t)e * d + j] : 0.0f;
+}
+
+}  // namespace
+
+hipError_t launch_repack_q8(const uint8_t* src0, const uint8_t* src1, int n_groups,
+                            size_t src_group_bytes, int src_rows, int src_blocks,
+                            int tiles_per_src, int n_col_tiles, int kb_pad, int8_t* dst_q,
+                            uint16_t* dst_s, size_t dst_q_group, size_t dst_s_group,
+                            hipStream_t s) {
+  const long n_pieces = (long)n_col_tiles * kb_pad * 4 * 64;
+  dim3 grid((unsigned)((n_pieces + 255) / 256), (unsigned)n_groups);
+  repack_q8_kernel<<<grid, 256, 0, s>>>(src0, src1, src_group_bytes, src_rows, src_blocks,
+                                        tiles_per_src, n_col_tiles, kb_pad, dst_q, dst_s,
+                                        dst_q_group, dst_s_group);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_router(const float* w, int E, int d, int E64, float* wt, hipStream_t s) {
+  const long n = (long)d * E64;
+  transpose_router_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(w, E, d, E64, wt);
+  return hipGetLastError();
+}
+
+}  // namespace moe

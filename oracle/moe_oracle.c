@@ -20,6 +20,7 @@
 #include "moe_oracle.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -422,3 +423,5 @@ void ora_rmsnorm(const float* x, int32_t n, int32_t d, double eps, double* out) 
     for (int32_t j = 0; j < d; ++j) out[(int64_t)t * d + j] = (double)x[(int64_t)t * d + j] * r;
   }
 }
+
+int32_t ora_num_threads(void) { return (int32_t)omp_get_max_threads(); }

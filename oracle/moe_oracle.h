@@ -121,6 +121,9 @@ int32_t ora_moe_grouped(const ora_dims* dm, const float* x, int32_t n_tokens,
 void ora_combine_f32(const float* partial, const float* w, const float* gs, int32_t n, int32_t k,
                      int32_t kk, int32_t d, float* out);
 
+/* Number of OpenMP threads the parallel loops above use. */
+int32_t ora_num_threads(void);
+
 /* RMSNorm with unit gain in fp64: x / sqrt(mean(x^2) + eps). */
 void ora_rmsnorm(const float* x, int32_t n, int32_t d, double eps, double* out);
 

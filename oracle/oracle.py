@@ -49,6 +49,7 @@ def lib():
                                       vp, vp]),
             "ora_combine_f32": (None, [vp, vp, vp, i32, i32, i32, i32, vp]),
             "ora_rmsnorm": (None, [vp, i32, i32, dbl, vp]),
+            "ora_num_threads": (i32, []),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -240,3 +241,7 @@ def routing(lw, x):
     start, ti, tk = csr(ids, s.n_experts, bool(s.shared_ffn))
     return {"logits": logits, "ids": ids, "w": w, "gs": gs, "xq": xq, "xs": xs,
             "exp_start": start, "tok_i": ti, "tok_k": tk}
+
+
+def num_threads() -> int:
+    return int(lib().ora_num_threads())

@@ -1,0 +1,93 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point include/moe_ffn.h declares, and rejects bad arguments before
+touching the device."""
+import ctypes as C
+import os
+
+import pytest
+
+from helpers import public_header_symbols
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_ffn.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from mixture_experts_ffn_gemm_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from mixture_experts_ffn_gemm_amd import build
+        build.build()
+    return binding
+
+
+def test_header_declares_the_expected_entry_points(B):
+    syms = public_header_symbols(HEADER)
+    assert set(syms) == set(B.EXPORTED)
+
+
+def test_library_exports_every_header_symbol(B):
+    L = B.lib()
+    for s in public_header_symbols(HEADER):
+        assert hasattr(L, s), s
+
+
+def test_status_strings(B):
+    assert B.status_str(0) == "ok"
+    assert B.status_str(-3) == "workspace too small"
+    assert B.status_str(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("dims,rc", [
+    ((0, 8, 2, 256, 0, 0), -1),          # d = 0
+    ((100, 8, 2, 256, 0, 0), -2),        # d not a multiple of 32
+    ((128, 8, 9, 256, 0, 0), -1),        # top_k > E
+    ((128, 300, 2, 256, 0, 0), -2),      # E > 256
+    ((128, 64, 17, 256, 0, 0), -2),      # top_k > 16
+    ((128, 8, 2, 250, 0, 0), -2),        # ffn not a multiple of 32
+    ((128, 8, 2, 256, 0, 2), -1),        # norm flag not 0/1
+])
+def test_weights_create_rejects_bad_dims_before_any_device_call(B, dims, rc):
+    h = C.c_void_p(1234)
+    dm = B.moe_ffn_dims(*dims)
+    got = B.lib().moe_ffn_weights_create(C.byref(dm), 8, None, 16, 16, 16, None, None, None, None,
+                                         None, C.byref(h))
+    assert got == rc
+    assert h.value is None
+
+
+def test_weights_create_rejects_null_and_partial_shared(B):
+    h = C.c_void_p()
+    dm = B.moe_ffn_dims(128, 8, 2, 256, 0, 0)
+    assert B.lib().moe_ffn_weights_create(C.byref(dm), None, None, 16, 16, 16, None, None, None, None,
+                                          None, C.byref(h)) == -1
+    # shared pointers without a shared expert
+    assert B.lib().moe_ffn_weights_create(C.byref(dm), 8, None, 16, 16, 16, 16, None, None, None,
+                                          None, C.byref(h)) == -1
+    dm2 = B.moe_ffn_dims(128, 8, 2, 256, 64, 0)
+    assert B.lib().moe_ffn_weights_create(C.byref(dm2), 8, None, 16, 16, 16, 16, 16, None, 16,
+                                          None, C.byref(h)) == -1
+    assert B.lib().moe_ffn_weights_create(C.byref(dm), 8, None, 16, 16, 16, None, None, None, None,
+                                          None, None) == -1
+
+
+def test_stage_entry_points_validate_on_the_host(B):
+    L = B.lib()
+    assert L.moe_ffn_combine(None, 16, None, 4, 2, 128, 32, None) == -1
+    assert L.moe_ffn_combine(16, 16, None, 4, 0, 128, 4096, None) == -1      # k = 0
+    assert L.moe_ffn_combine(16, 16, None, 4, 17, 128, 4096, None) == -1     # k > 16
+    assert L.moe_ffn_combine(16, 16, None, 4, 2, 130, 4096, None) == -2      # d % 4
+    assert L.moe_ffn_combine(16, 16, None, 4, 2, 128, 16, None) == -1        # out overlaps partial
+    assert L.moe_ffn_quantize(16, 33, 64, 128, None) == -2
+    assert L.moe_ffn_quantize(None, 32, 64, 128, None) == -1
+    assert L.moe_ffn_quantize(16, -32, 64, 128, None) == -1
+    assert L.moe_ffn_residual_rmsnorm(16, None, 16, 4, 8, 1e-5, None) == -1   # xn overlaps h
+    assert L.moe_ffn_residual_rmsnorm(16, None, 4096, 4, 8, -1.0, None) == -1
+    n = C.c_size_t()
+    assert L.moe_ffn_workspace_size(None, 16, C.byref(n)) == -1
+    dm = B.moe_ffn_dims()
+    assert L.moe_ffn_weights_dims(None, C.byref(dm)) == -1
+    assert L.moe_ffn_prefill(None, 16, 4, 32, 64, 1 << 20, None, None) == -1
+    assert L.moe_ffn_decode(None, 16, 9, 32, 64, 1 << 20, None, None) == -1
+    assert L.moe_ffn_decode(None, 16, 0, 32, 64, 1 << 20, None, None) == -1
+    assert L.moe_ffn_weights_destroy(None) == 0

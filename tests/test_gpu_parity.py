@@ -1,0 +1,261 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on
+the same seeded inputs.
+
+Bar: routing top-k ids, CSR arrays and the int8 activation codes/scales are
+bit-exact; the ordered combine is bit-exact given identical inputs; the fp32
+outputs are within relative L2 2e-3 and per-element 1e-2 * rms(out) of the
+oracle (int8 MMQ, argmax-stable contract of SharpInference #406).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import moe_workloads as mw
+from helpers import moe_close
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def say(*a):
+    print("[gpu-parity]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib_loaded():
+    from mixture_experts_ffn_gemm_amd import binding
+    binding.lib()   # raises when the library is missing: no fallback
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    yield
+
+
+def run_gpu(lw, x, api="prefill", layer=None, keep=False):
+    from mixture_experts_ffn_gemm_amd import binding as B
+    from mixture_experts_ffn_gemm_amd.layer import MoeLayer
+    s = lw.shape
+    n = x.shape[0]
+    own = layer is None
+    if own:
+        layer = MoeLayer.from_workload(lw)
+    dev = torch.device("cuda")
+    kk = s.top_k + (1 if s.shared_ffn else 0)
+    P = n * s.top_k + (n if s.shared_ffn else 0)
+    bufs = dict(
+        topk_ids=torch.full((n, s.top_k), -7, dtype=torch.int32, device=dev),
+        topk_w=torch.full((n, s.top_k), -7.0, dtype=torch.float32, device=dev),
+        shared_gate=torch.zeros(n, dtype=torch.float32, device=dev),
+        exp_start=torch.full((s.n_experts + 1 + (1 if s.shared_ffn else 0),), -7, dtype=torch.int32, device=dev),
+        exp_tok_i=torch.full((P,), -7, dtype=torch.int32, device=dev),
+        exp_tok_k=torch.full((P,), -7, dtype=torch.int32, device=dev),
+        xq=torch.zeros((n, s.d), dtype=torch.int8, device=dev),
+        xs=torch.zeros((n, s.d // 32), dtype=torch.int16, device=dev),
+        partial=torch.zeros((n, kk, s.d), dtype=torch.float32, device=dev),
+    )
+    r = B.make_routing(**bufs)
+    xt = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    out = torch.full((n, s.d), float("nan"), dtype=torch.float32, device=dev)
+    if api == "prefill":
+        layer.prefill(xt, out=out, routing=r)
+    else:
+        layer.decode(xt, out=out, routing=r)
+    torch.cuda.synchronize()
+    res = {k: v.cpu().numpy() for k, v in bufs.items()}
+    res["xs"] = res["xs"].view(np.uint16)
+    res["out"] = out.cpu().numpy()
+    if own and not keep:
+        layer.close()
+    if keep:
+        res["layer"] = layer
+    return res
+
+
+def check_routing(lw, x, g):
+    s = lw.shape
+    o = O.routing(lw, x)
+    assert np.array_equal(g["topk_ids"], o["ids"]), "top-k ids differ"
+    assert np.array_equal(g["exp_start"], o["exp_start"]), "expStart differs"
+    assert np.array_equal(g["exp_tok_i"], o["tok_i"]), "expTokI differs"
+    assert np.array_equal(g["exp_tok_k"], o["tok_k"]), "expTokK differs"
+    assert np.array_equal(g["xq"], o["xq"]), "int8 activation codes differ"
+    assert np.array_equal(g["xs"], o["xs"]), "activation scales differ"
+    np.testing.assert_allclose(g["topk_w"], o["w"], rtol=2e-6, atol=1e-7)
+    if s.shared_ffn:
+        np.testing.assert_allclose(g["shared_gate"], o["gs"], rtol=1e-5, atol=1e-6)
+    return o
+
+
+def check_outputs(lw, x, g, tokens=None):
+    n = x.shape[0]
+    toks = np.arange(n) if tokens is None else np.asarray(tokens)
+    ref = O.moe_tokens(lw, x, tokens=toks, want_partial=True)
+    r, e = moe_close(g["out"][toks], ref["out"])
+    # Unweighted partials: same L2 bar; per element, one int8 code of h landing
+    # on the other side of a rounding boundary (fp32 on the GPU, fp64 in the
+    # oracle) moves a partial by |W_down| * (h step) ~ 3/(127 sqrt(F)) of its
+    # rms times amax/rms of the h block, i.e. a few percent when F is 32 wide.
+    rp, ep = moe_close(g["partial"][toks], ref["partial"], elem=6e-2)
+    # the GPU's combine reproduces the fp32 ordered reduce bit for bit
+    gs = g["shared_gate"][toks] if lw.shape.shared_ffn else None
+    comb = O.combine_f32(g["partial"][toks], g["topk_w"][toks], gs)
+    assert np.array_equal(comb, g["out"][toks]), "combine is not the ordered fp32 reduce"
+    return r, e
+
+
+# ------------------------------------------------------------- stage kernels
+def test_quantize_stage_bitexact():
+    from mixture_experts_ffn_gemm_amd import binding as B
+    rng = np.random.default_rng(20)
+    v = (rng.standard_normal((37, 256)) * np.exp(rng.standard_normal((37, 1)) * 4)).astype(np.float32)
+    v[5, 64:96] = 0.0
+    v[6, :32] = np.float32(1e-30)
+    v[7, 32:64] = np.array([127.0, 2.5, 3.5, -2.5] + [0.0] * 28, np.float32)
+    vt = torch.from_numpy(v).cuda()
+    q = torch.empty(v.shape, dtype=torch.int8, device="cuda")
+    s = torch.empty((37, 8), dtype=torch.int16, device="cuda")
+    B.moe_ffn_quantize(vt, v.size, q, s)
+    torch.cuda.synchronize()
+    oq, os_ = O.quantize_q8(v)
+    assert np.array_equal(q.cpu().numpy(), oq)
+    assert np.array_equal(s.cpu().numpy().view(np.uint16), os_)
+
+
+@pytest.mark.parametrize("k,shared,n,d", [(1, False, 3, 64), (8, False, 37, 2048), (8, True, 21, 256),
+                                          (16, True, 5, 128), (3, False, 0, 32)])
+def test_combine_stage_bitexact(k, shared, n, d):
+    from mixture_experts_ffn_gemm_amd import binding as B
+    rng = np.random.default_rng(21 + k)
+    kk = k + (1 if shared else 0)
+    P = rng.standard_normal((n, kk, d)).astype(np.float32)
+    w = rng.random((n, k)).astype(np.float32)
+    gs = rng.random(n).astype(np.float32) if shared else None
+    out = torch.empty((n, d), dtype=torch.float32, device="cuda")
+    B.moe_ffn_combine(torch.from_numpy(P).cuda(), torch.from_numpy(w).cuda(),
+                      torch.from_numpy(gs).cuda() if shared else None, n, k, d, out)
+    torch.cuda.synchronize()
+    ref = O.combine_f32(P, w, gs)
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
+def test_combine_stage_golden_order():
+    import json
+    from mixture_experts_ffn_gemm_amd import binding as B
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "combine_slot_order.json")))
+    for c in g["cases"]:
+        k = len(c["weights"])
+        # pad d to 4 so the float4 path is exercised with the same value in every column
+        P = np.repeat(np.array(c["partials"], np.float32)[None], 1, 0)
+        P = np.repeat(P, 4, axis=2)
+        w = np.array([c["weights"]], np.float32)
+        gs = np.array([c["shared_gate"]], np.float32) if "shared_gate" in c else None
+        out = torch.empty((1, 4), dtype=torch.float32, device="cuda")
+        B.moe_ffn_combine(torch.from_numpy(P).cuda(), torch.from_numpy(w).cuda(),
+                          torch.from_numpy(gs).cuda() if gs is not None else None, 1, k, 4, out)
+        torch.cuda.synchronize()
+        assert np.all(out.cpu().numpy() == np.float32(c["expected"][0])), c["name"]
+
+
+# ------------------------------------------------------------- whole layer
+def test_tiny_layer_parity():
+    lw = mw.workload_layer("tiny")
+    x = mw.workload_tokens("tiny")
+    g = run_gpu(lw, x)
+    check_routing(lw, x, g)
+    r, e = check_outputs(lw, x, g)
+    say(f"tiny: rel_l2={r:.2e} max_elem={e:.2e}")
+
+
+SHAPES = [
+    dict(d=96, E=5, k=5, F=64, norm=True),             # k = E, paddings everywhere
+    dict(d=128, E=8, k=1, F=32),                        # k = 1
+    dict(d=160, E=16, k=3, F=96, Fs=64, zipf=1.1),      # shared expert, Fs != F, skew
+    dict(d=256, E=70, k=4, F=128, norm=True),           # E not a multiple of 64
+    dict(d=64, E=1, k=1, F=64, norm=True),              # a single expert (dense FFN)
+    dict(d=128, E=256, k=16, F=64, Fs=32),              # E = 256, k = 16, shared
+]
+
+
+@pytest.mark.parametrize("case", range(len(SHAPES)))
+@pytest.mark.parametrize("n", [1, 7, 53])
+def test_shape_edge_cases(case, n):
+    shape, lw = mw.random_shape_case(case, **SHAPES[case])
+    x = mw.make_tokens(200 + case, n, shape.d)
+    g = run_gpu(lw, x)
+    check_routing(lw, x, g)
+    check_outputs(lw, x, g)
+
+
+def test_empty_batch_is_a_noop():
+    from mixture_experts_ffn_gemm_amd.layer import MoeLayer
+    lw = mw.workload_layer("tiny")
+    layer = MoeLayer.from_workload(lw)
+    out = torch.full((1, 128), 3.0, device="cuda")
+    x = torch.zeros((0, 128), device="cuda")
+    layer.prefill(x, out=out[:0])
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0)
+    layer.close()
+
+
+def test_repeat_runs_are_bitwise_identical():
+    lw = mw.workload_layer("tiny")
+    x = mw.make_tokens(1, 300, 128)
+    a = run_gpu(lw, x)
+    b = run_gpu(lw, x)
+    for key in ("out", "partial", "topk_w", "exp_tok_i"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.slow
+def test_olmoe_layer_full_size():
+    """OLMoE-shaped layer at N=2048: routing for every token bit-exact, outputs
+    on sampled tokens (incl. the first and last)."""
+    lw = mw.workload_layer("olmoe_n2048")
+    x = mw.workload_tokens("olmoe_n2048")
+    say("olmoe_n2048: weights generated")
+    g = run_gpu(lw, x)
+    check_routing(lw, x, g)
+    say("olmoe_n2048: routing bit-exact")
+    toks = np.unique(np.concatenate([[0, 1, 2047], np.random.default_rng(5).integers(0, 2048, 21)]))
+    r, e = check_outputs(lw, x, g, toks)
+    say(f"olmoe_n2048: rel_l2={r:.2e} max_elem={e:.2e} on {len(toks)} tokens")
+    counts = np.diff(g["exp_start"])
+    assert counts.sum() == 2048 * 8 and counts.min() > 0
+
+
+@pytest.mark.slow
+def test_a3b_layer_full_size():
+    """35B-A3B-shaped layer: E=256, shared expert + gate, Zipf-skewed routing."""
+    lw = mw.workload_layer("a3b_n512")
+    x = mw.workload_tokens("a3b_n512")
+    g = run_gpu(lw, x)
+    check_routing(lw, x, g)
+    counts = np.diff(g["exp_start"][:257])
+    say(f"a3b_n512: experts touched {int((counts > 0).sum())}, max load {int(counts.max())}")
+    toks = np.unique(np.concatenate([[0, 511], np.random.default_rng(6).integers(0, 512, 14)]))
+    r, e = check_outputs(lw, x, g, toks)
+    say(f"a3b_n512: rel_l2={r:.2e} max_elem={e:.2e}")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("n", [1, 8])
+def test_decode(n):
+    lw = mw.workload_layer("olmoe_decode1")
+    x = mw.make_tokens(5, n, 2048)
+    g = run_gpu(lw, x, api="decode")
+    check_routing(lw, x, g)
+    check_outputs(lw, x, g)
+
+
+@pytest.mark.slow
+def test_n4096_prefill_sampled():
+    lw = mw.workload_layer("olmoe_n4096")
+    x = mw.workload_tokens("olmoe_n4096")
+    g = run_gpu(lw, x)
+    check_routing(lw, x, g)
+    toks = np.unique(np.concatenate([[0, 4095], np.random.default_rng(7).integers(0, 4096, 10)]))
+    check_outputs(lw, x, g, toks)
