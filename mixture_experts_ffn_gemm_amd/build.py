@@ -18,6 +18,7 @@ ARCH = "gfx950"
 
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", f"--offload-arch={ARCH}", "-fno-gpu-rdc",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-mllvm", "-amdgpu-mfma-vgpr-form",
                "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
                "-I", INCLUDE, "-I", CSRC]
 

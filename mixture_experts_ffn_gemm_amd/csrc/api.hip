@@ -4,9 +4,10 @@
 // One prefill call enqueues, on the caller's stream and without any host
 // synchronisation or device-to-host transfer (SharpInference #388 "Remaining
 // levers" 1: the selection must not round-trip to the host):
-//   1. router logits            (fp32 fused-chain matvec, all experts)
-//   2. routing                  (top-k, softmax weights, shared gate, int8 x,
-//                                per-tile expert histograms and ranks)
+//   1. router                   (fp32 fused-chain logits for all experts, the
+//                                int8 quantiser of x, the shared-expert gate)
+//   2. routing                  (top-k, softmax weights, per-tile expert
+//                                histograms and ranks)
 //   3. bucketing                (CSR expStart/expTokI/expTokK + 32-row tile table)
 //   4. grouped gate/up + SwiGLU (one launch over all experts + shared expert)
 //   5. grouped down             (one launch; unweighted partials per slot)
@@ -35,7 +36,7 @@ WsLayout ws_layout(const Dims& dm, int max_tokens) {
   const size_t kk = (size_t)dm.k + dm.has_shared;
   const size_t P_total = Nn * dm.k + (dm.has_shared ? Nn : 0);
   L.n_route_tiles = (int)((Nn + ROUTE_TILE - 1) / ROUTE_TILE);
-  L.tile_bound = (int)((P_total + (size_t)(MT - 1) * dm.G) / MT + 1);
+  L.tile_bound = (int)((P_total + (size_t)(MT_WG - 1) * dm.G) / MT_WG + 1);
   const size_t kbmax = (size_t)dm.kmax_pad / QB;
   L.logits = take(Nn * dm.E * 4);
   L.ids = take(Nn * dm.k * 4);
@@ -49,8 +50,9 @@ WsLayout ws_layout(const Dims& dm, int max_tokens) {
   L.tok_i = take(P_total * 4);
   L.tok_k = take(P_total * 4);
   L.tiles = take((4 + 3 * (size_t)L.tile_bound) * 4);
-  L.hq = take((size_t)L.tile_bound * kbmax * 1024);
-  L.hs = take((size_t)L.tile_bound * 32 * kbmax * 2);
+  const size_t t32 = (size_t)L.tile_bound * (MT_WG / MT_WAVE);
+  L.hq = take(t32 * kbmax * 1024);
+  L.hs = take(t32 * 32 * kbmax * 2);
   L.partial = take(Nn * kk * dm.d * 4);
   L.total = off;
   return L;
@@ -144,11 +146,10 @@ int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, v
   auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
 
   HIP_TRY(mark(0));
-  HIP_TRY(launch_router_logits(x, n, dm.d, W->router_wt, W->has_bias ? W->router_bias : nullptr,
-                               dm.E, dm.E64, logits, s));
+  HIP_TRY(launch_router(x, n, dm.d, dm.d_pad, W->router_wt, W->has_bias ? W->router_bias : nullptr,
+                        dm.E, dm.E64, logits, dm.has_shared ? W->sh_gate_vec : nullptr, gs, xq, xs, s));
   HIP_TRY(mark(1));
-  HIP_TRY(launch_route(logits, x, n, dm.d, dm.d_pad, dm.E, dm.k, dm.norm,
-                       dm.has_shared ? W->sh_gate_vec : nullptr, ids, w, gs, rank, xq, xs, hist, s));
+  HIP_TRY(launch_route(logits, n, dm.E, dm.k, dm.norm, ids, w, rank, hist, s));
   HIP_TRY(mark(2));
   HIP_TRY(launch_bucket(ids, rank, hist, n, dm.E, dm.k, dm.has_shared, exp_start, tok_i, tok_k,
                         tiles, L.tile_bound, s));
@@ -167,20 +168,14 @@ int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, v
   a.xq = xq;
   a.xs = xs;
   a.d_pad = dm.d_pad;
-  a.gu_q = W->gu_q;
-  a.gu_s = W->gu_s;
-  a.gu_q_group = W->gu_q_per_expert;
-  a.gu_s_group = W->gu_s_per_expert;
-  a.sh_gu_q = W->sh_gu_q;
-  a.sh_gu_s = W->sh_gu_s;
+  a.gu = W->gu;
+  a.gu_group = W->gu_per_expert;
+  a.sh_gu = W->sh_gu;
   a.F_pad = dm.F_pad;
   a.Fs_pad = dm.Fs_pad;
-  a.dn_q = W->dn_q;
-  a.dn_s = W->dn_s;
-  a.dn_q_group = W->dn_q_per_expert;
-  a.dn_s_group = W->dn_s_per_expert;
-  a.sh_dn_q = W->sh_dn_q;
-  a.sh_dn_s = W->sh_dn_s;
+  a.dn = W->dn;
+  a.dn_group = W->dn_per_expert;
+  a.sh_dn = W->sh_dn;
   a.partial = partial;
   a.d = dm.d;
   a.kk = kk;
@@ -245,12 +240,11 @@ int moe_ffn_weights_create(const moe_ffn_dims* dims, const float* router_w,
     return MOE_FFN_HIP_ERROR;
   }
   W->has_bias = router_bias ? 1 : 0;
-  W->gu_q_per_expert = (size_t)dm.F_pad * dm.d_pad * 2;
-  W->gu_s_per_expert = (size_t)dm.F_pad * 2 * (dm.d_pad / QB);
-  W->dn_q_per_expert = (size_t)dm.d_pad * dm.F_pad;
-  W->dn_s_per_expert = (size_t)dm.d_pad * (dm.F_pad / QB);
-  const size_t sh_gu_q = (size_t)dm.Fs_pad * dm.d_pad * 2, sh_gu_s = (size_t)dm.Fs_pad * 2 * (dm.d_pad / QB);
-  const size_t sh_dn_q = (size_t)dm.d_pad * dm.Fs_pad, sh_dn_s = (size_t)dm.d_pad * (dm.Fs_pad / QB);
+  // [strips][k-steps][17 KiB] per expert (see internal.h)
+  W->gu_per_expert = (size_t)(dm.F_pad / GU_COLS) * (dm.d_pad / QB / KSTEP) * KSTEP_BYTES;
+  W->dn_per_expert = (size_t)(dm.d_pad / DN_COLS) * (dm.F_pad / QB / KSTEP) * KSTEP_BYTES;
+  const size_t sh_gu = (size_t)(dm.Fs_pad / GU_COLS) * (dm.d_pad / QB / KSTEP) * KSTEP_BYTES;
+  const size_t sh_dn = (size_t)(dm.d_pad / DN_COLS) * (dm.Fs_pad / QB / KSTEP) * KSTEP_BYTES;
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -261,12 +255,9 @@ int moe_ffn_weights_create(const moe_ffn_dims* dims, const float* router_w,
   const size_t o_rw = take((size_t)dm.d * dm.E64 * 4);
   const size_t o_rb = take((size_t)dm.E * 4);
   const size_t o_sg = take((size_t)dm.d * 4);
-  const size_t o_guq = take(W->gu_q_per_expert * dm.E);
-  const size_t o_gus = take(W->gu_s_per_expert * 2 * dm.E);
-  const size_t o_dnq = take(W->dn_q_per_expert * dm.E);
-  const size_t o_dns = take(W->dn_s_per_expert * 2 * dm.E);
-  const size_t o_sguq = take(sh_gu_q), o_sgus = take(sh_gu_s * 2);
-  const size_t o_sdnq = take(sh_dn_q), o_sdns = take(sh_dn_s * 2);
+  const size_t o_gu = take(W->gu_per_expert * dm.E);
+  const size_t o_dn = take(W->dn_per_expert * dm.E);
+  const size_t o_sgu = take(sh_gu), o_sdn = take(sh_dn);
   if (hipMalloc(&W->base, off) != hipSuccess) {
     (void)hipGetLastError();
     delete W;
@@ -276,14 +267,10 @@ int moe_ffn_weights_create(const moe_ffn_dims* dims, const float* router_w,
   W->router_wt = (float*)(b + o_rw);
   W->router_bias = (float*)(b + o_rb);
   W->sh_gate_vec = (float*)(b + o_sg);
-  W->gu_q = (int8_t*)(b + o_guq);
-  W->gu_s = (uint16_t*)(b + o_gus);
-  W->dn_q = (int8_t*)(b + o_dnq);
-  W->dn_s = (uint16_t*)(b + o_dns);
-  W->sh_gu_q = has_sh ? (int8_t*)(b + o_sguq) : nullptr;
-  W->sh_gu_s = has_sh ? (uint16_t*)(b + o_sgus) : nullptr;
-  W->sh_dn_q = has_sh ? (int8_t*)(b + o_sdnq) : nullptr;
-  W->sh_dn_s = has_sh ? (uint16_t*)(b + o_sdns) : nullptr;
+  W->gu = (uint8_t*)(b + o_gu);
+  W->dn = (uint8_t*)(b + o_dn);
+  W->sh_gu = has_sh ? (uint8_t*)(b + o_sgu) : nullptr;
+  W->sh_dn = has_sh ? (uint8_t*)(b + o_sdn) : nullptr;
 
   const int nbd = dm.d / QB, nbf = dm.F / QB;
   hipError_t e = hipSuccess;
@@ -297,20 +284,20 @@ int moe_ffn_weights_create(const moe_ffn_dims* dims, const float* router_w,
   if (e == hipSuccess)
     e = launch_repack_q8((const uint8_t*)gate_q8, (const uint8_t*)up_q8, dm.E,
                          (size_t)dm.F * nbd * Q8_BYTES, dm.F, nbd, 2, dm.F_pad / GU_COLS, dm.d_pad / QB,
-                         W->gu_q, W->gu_s, W->gu_q_per_expert, W->gu_s_per_expert, stream);
+                         W->gu, W->gu_per_expert, stream);
   if (e == hipSuccess)
     e = launch_repack_q8((const uint8_t*)down_q8, (const uint8_t*)down_q8, dm.E,
                          (size_t)dm.d * nbf * Q8_BYTES, dm.d, nbf, 4, dm.d_pad / DN_COLS, dm.F_pad / QB,
-                         W->dn_q, W->dn_s, W->dn_q_per_expert, W->dn_s_per_expert, stream);
+                         W->dn, W->dn_per_expert, stream);
   if (e == hipSuccess && has_sh) {
     const int nbs = dm.Fs / QB;
     e = launch_repack_q8((const uint8_t*)sh_gate_q8, (const uint8_t*)sh_up_q8, 1,
                          (size_t)dm.Fs * nbd * Q8_BYTES, dm.Fs, nbd, 2, dm.Fs_pad / GU_COLS,
-                         dm.d_pad / QB, W->sh_gu_q, W->sh_gu_s, sh_gu_q, sh_gu_s, stream);
+                         dm.d_pad / QB, W->sh_gu, sh_gu, stream);
     if (e == hipSuccess)
       e = launch_repack_q8((const uint8_t*)sh_down_q8, (const uint8_t*)sh_down_q8, 1,
                            (size_t)dm.d * nbs * Q8_BYTES, dm.d, nbs, 4, dm.d_pad / DN_COLS,
-                           dm.Fs_pad / QB, W->sh_dn_q, W->sh_dn_s, sh_dn_q, sh_dn_s, stream);
+                           dm.Fs_pad / QB, W->sh_dn, sh_dn, stream);
   }
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   if (e != hipSuccess) {

@@ -8,7 +8,7 @@
 //     expStart[e] + (pairs of e in earlier tiles) + rank,
 // which keeps every expert's rows in (token, slot) order -- a stable counting
 // sort with no atomics, so the result is deterministic.  Workgroup 0 also
-// writes expStart and the table of 32-row tiles that drives the grouped GEMMs.
+// writes expStart and the table of 128-row tiles that drives the grouped GEMMs.
 #include "internal.h"
 
 namespace moe {
@@ -45,12 +45,27 @@ __global__ __launch_bounds__(256) void bucket_kernel(
   __shared__ int s_tmp[256];
   const int tile = blockIdx.x;
   const int P = n * k;
-  for (int e = threadIdx.x; e < E; e += 256) {
+  // Per-expert totals over all tiles and over the tiles before this one; for
+  // small E several threads share an expert's column and their sums meet in LDS.
+  __shared__ int s_part_tot[256], s_part_pre[256];
+  const int nparts = max(1, 256 / E);
+  if (threadIdx.x < E * nparts) {
+    const int e = threadIdx.x % E, part = threadIdx.x / E;
     int tot = 0, pre = 0;
-    for (int tt = 0; tt < n_tiles; ++tt) {
+    for (int tt = part; tt < n_tiles; tt += nparts) {
       const int h = hist[(size_t)tt * E + e];
       tot += h;
       pre += (tt < tile) ? h : 0;
+    }
+    s_part_tot[threadIdx.x] = tot;
+    s_part_pre[threadIdx.x] = pre;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int tot = 0, pre = 0;
+    for (int part = 0; part < nparts; ++part) {
+      tot += s_part_tot[part * E + e];
+      pre += s_part_pre[part * E + e];
     }
     s_start[e] = tot;
     s_cnt[e] = tot;
@@ -77,25 +92,25 @@ __global__ __launch_bounds__(256) void bucket_kernel(
     }
 
   if (tile != 0) return;
-  // expStart, then the 32-row tile table over the E (+1) groups
+  // expStart, then the 128-row tile table over the E (+1) groups
   for (int e = threadIdx.x; e <= E; e += 256) exp_start[e] = (e < E) ? s_start[e] : P;
   if (has_shared && threadIdx.x == 0) exp_start[E + 1] = P + n;
   const int G = E + has_shared;
   if (threadIdx.x == 0 && has_shared) s_cnt[E] = n;
   __syncthreads();
   __shared__ int s_nt[2 * 256 + 2];
-  for (int g = threadIdx.x; g < G; g += 256) s_nt[g] = (s_cnt[g] + MT - 1) / MT;
+  for (int g = threadIdx.x; g < G; g += 256) s_nt[g] = (s_cnt[g] + MT_WG - 1) / MT_WG;
   __syncthreads();
   const int last_nt = s_nt[G - 1];
   block_exclusive_scan_512(s_nt, G, s_tmp);
   for (int g = threadIdx.x; g < G; g += 256) {
     const int c = s_cnt[g];
     const int first = (g < E) ? s_start[g] : P;
-    const int ntg = (c + MT - 1) / MT;
+    const int ntg = (c + MT_WG - 1) / MT_WG;
     for (int i = 0; i < ntg && s_nt[g] + i < tile_bound; ++i) {
       int32_t* ent = tiles + 4 + 3 * (size_t)(s_nt[g] + i);
       ent[0] = g;
-      ent[1] = first + i * MT;
+      ent[1] = first + i * MT_WG;
       ent[2] = first + c;
     }
   }

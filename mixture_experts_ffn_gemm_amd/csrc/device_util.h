@@ -29,9 +29,13 @@ __device__ inline void quant_block32(float v, int8_t& q, uint16_t& s16) {
   s16 = __half_as_ushort(__float2half_rn(dd));
 }
 
-// Logical workgroup index that keeps consecutive logical indices on one XCD:
-// the hardware deals workgroups round-robin over the 8 XCDs, so workgroup b
-// runs on XCD b % 8.  nb must be a multiple of 8.
-__device__ inline int xcd_major(int b, int nb) { return (b & 7) * (nb >> 3) + (b >> 3); }
+
+// Workgroup barrier that orders LDS accesses only: global loads still in flight
+// (a register prefetch ring) are not drained, unlike __syncthreads().
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 }  // namespace moe

@@ -6,14 +6,15 @@
 //                                    of a wavefront reads expert e's 4 weights
 //                                    for 4 consecutive j in one 16-byte load;
 //                                    E64 = E rounded up to 64, zero rows past E.
-//   gate/up     int8 codes [F_pad/64][KB][4][2][32][16] per expert, KB = d_pad/32.
-//               One 1 KiB chunk is one 32x32 MFMA B operand: tile tt (0,1 = gate
-//               rows 64c + 32tt + r, 2,3 = up rows 64c + 32(tt-2) + r), half h of
-//               the 32-byte block, row r, 16 bytes.  Lane l of a wavefront reads
-//               bytes [16 l, 16 l + 16) of the chunk.
-//               binary16 scales [F_pad/64][4][32][KB].
-//   down        int8 codes [d_pad/128][KBF][4][2][32][16] per expert, KBF = F_pad/32,
-//               tile tt = down rows 128c + 32tt + r; scales [d_pad/128][4][32][KBF].
+//   gate/up     per expert [F_pad/64 strips][d_pad/128 k-steps][17 KiB]; a k-step
+//               block is 16 chunks of 1 KiB [block i (4)][tile tt (4)] followed by
+//               1 KiB of binary16 scales [tt][32 rows][4 blocks].  A chunk is one
+//               32x32x32 MFMA B operand: [half of the 32-byte block][32 rows][16 B],
+//               so lane l of a wavefront reads bytes [16 l, 16 l + 16).  Strip c
+//               holds tiles tt = 0,1: gate rows 64c + 32tt + r; tt = 2,3: the up
+//               rows 64c + 32(tt-2) + r (so gate and up of one column meet in one lane).
+//   down        per expert [d_pad/128 strips][F_pad/128 k-steps][17 KiB], tile tt =
+//               down rows 128c + 32tt + r.
 //   The shared expert has its own planes of the same form (F replaced by Fs).
 //   Padding rows/blocks hold zero codes and zero scales.
 //
@@ -21,10 +22,11 @@
 //   logits fp32 [N][E]; ids, rank i32 [N][k]; w fp32 [N][k]; gs fp32 [N];
 //   xq int8 [N][d_pad]; xs fp16 [N][d_pad/32]; hist i32 [ceil(N/16)][E];
 //   exp_start i32 [E+2]; tok_i, tok_k i32 [N*k + N];
-//   tiles i32 [4 + 3*T_bound]  (tiles[0] = number of 32-row tiles, then
+//   tiles i32 [4 + 3*T_bound]  (tiles[0] = number of 128-row tiles, then
 //                               {group, first CSR row, end CSR row} per tile);
-//   hq int8 [T_bound][KBMAX][2][32][16]  (the down GEMM's A operand chunks);
-//   hs fp16 [T_bound][32][KBMAX];
+//   hq int8 [4*T_bound][KBMAX][2][32][16]  (the down GEMM's A operand chunks,
+//                               one run per 32-row quarter of a tile);
+//   hs fp16 [4*T_bound][32][KBMAX];
 //   partial fp32 [N][k + has_shared][d].
 #pragma once
 
@@ -40,9 +42,12 @@ constexpr int QB = 32;            // int8 block length (Q8_0 / activation blocks
 constexpr int Q8_BYTES = 34;      // Q8_0 block: binary16 scale + 32 codes
 constexpr int KPAD = 128;         // K-dimension padding granule (4 blocks)
 constexpr int ROUTE_TILE = 16;    // tokens per routing workgroup
-constexpr int MT = 32;            // rows per GEMM row tile
-constexpr int GU_COLS = 64;       // SwiGLU output columns per gate/up work item
-constexpr int DN_COLS = 128;      // output columns per down work item
+constexpr int MT_WG = 128;        // rows per grouped-GEMM workgroup tile
+constexpr int MT_WAVE = 32;       // rows per wavefront
+constexpr int GU_COLS = 64;       // SwiGLU output columns per gate/up strip
+constexpr int DN_COLS = 128;      // output columns per down strip
+constexpr int KSTEP = 4;          // 32-blocks per GEMM k-step
+constexpr int KSTEP_BYTES = 17 * 1024;  // codes (16 KiB) + scales (1 KiB) of a k-step
 constexpr int MAX_TOPK = 16;
 constexpr int MAX_EXPERTS = 256;
 constexpr int DECODE_MAX_TOKENS = 8;
@@ -77,15 +82,11 @@ struct moe_ffn_weights {
   float* router_wt;
   float* router_bias;
   float* sh_gate_vec;
-  int8_t* gu_q;
-  uint16_t* gu_s;
-  int8_t* dn_q;
-  uint16_t* dn_s;
-  int8_t* sh_gu_q;
-  uint16_t* sh_gu_s;
-  int8_t* sh_dn_q;
-  uint16_t* sh_dn_s;
-  size_t gu_q_per_expert, gu_s_per_expert, dn_q_per_expert, dn_s_per_expert;  // elements
+  uint8_t* gu;
+  uint8_t* dn;
+  uint8_t* sh_gu;
+  uint8_t* sh_dn;
+  size_t gu_per_expert, dn_per_expert;  // bytes
 };
 
 namespace moe {
@@ -93,15 +94,15 @@ namespace moe {
 // ---- launchers (each returns hipGetLastError() of its launch) ----
 hipError_t launch_repack_q8(const uint8_t* src0, const uint8_t* src1, int n_groups,
                             size_t src_group_bytes, int src_rows, int src_blocks, int tiles_per_src,
-                            int n_col_tiles, int kb_pad, int8_t* dst_q, uint16_t* dst_s,
-                            size_t dst_q_group, size_t dst_s_group, hipStream_t s);
+                            int n_strips, int kb_pad, uint8_t* dst, size_t dst_group_bytes,
+                            hipStream_t s);
 hipError_t launch_transpose_router(const float* w, int E, int d, int E64, float* wt, hipStream_t s);
 
-hipError_t launch_router_logits(const float* x, int n, int d, const float* wt, const float* bias,
-                                int E, int E64, float* logits, hipStream_t s);
-hipError_t launch_route(const float* logits, const float* x, int n, int d, int d_pad, int E, int k,
-                        int norm, const float* sh_gate_vec, int32_t* ids, float* w, float* gs,
-                        int32_t* rank, int8_t* xq, uint16_t* xs, int32_t* hist, hipStream_t s);
+hipError_t launch_router(const float* x, int n, int d, int d_pad, const float* wt, const float* bias,
+                         int E, int E64, float* logits, const float* sh_gate_vec, float* gs,
+                         int8_t* xq, uint16_t* xs, hipStream_t s);
+hipError_t launch_route(const float* logits, int n, int E, int k, int norm, int32_t* ids, float* w,
+                        int32_t* rank, int32_t* hist, hipStream_t s);
 hipError_t launch_quantize(const float* v, int64_t n_values, int8_t* q, uint16_t* scales,
                            hipStream_t s);
 hipError_t launch_bucket(const int32_t* ids, const int32_t* rank, const int32_t* hist, int n,
@@ -125,18 +126,14 @@ struct GemmArgs {
   const int8_t* xq;
   const uint16_t* xs;
   int d_pad;
-  const int8_t* gu_q;
-  const uint16_t* gu_s;
-  size_t gu_q_group, gu_s_group;
-  const int8_t* sh_gu_q;
-  const uint16_t* sh_gu_s;
+  const uint8_t* gu;
+  size_t gu_group;
+  const uint8_t* sh_gu;
   int F_pad, Fs_pad;
   // down
-  const int8_t* dn_q;
-  const uint16_t* dn_s;
-  size_t dn_q_group, dn_s_group;
-  const int8_t* sh_dn_q;
-  const uint16_t* sh_dn_s;
+  const uint8_t* dn;
+  size_t dn_group;
+  const uint8_t* sh_dn;
   float* partial;
   int d;
   int kk;

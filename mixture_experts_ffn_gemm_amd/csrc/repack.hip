@@ -10,14 +10,16 @@
 namespace moe {
 namespace {
 
+// One thread per 16-byte piece of a chunk (strip c, block kb, tile tt, lane);
+// the half-0 lanes also move the block scale.  Destination per group:
+// [strip][k-step][16 chunks of codes + 1 KiB of scales].
 __global__ __launch_bounds__(256) void repack_q8_kernel(
     const uint8_t* __restrict__ src0, const uint8_t* __restrict__ src1, size_t src_group_bytes,
-    int src_rows, int src_blocks, int tiles_per_src, int n_col_tiles, int kb_pad,
-    int8_t* __restrict__ dst_q, uint16_t* __restrict__ dst_s, size_t dst_q_group,
-    size_t dst_s_group) {
+    int src_rows, int src_blocks, int tiles_per_src, int n_strips, int kb_pad,
+    uint8_t* __restrict__ dst, size_t dst_group_bytes) {
   const int g = blockIdx.y;
   const long piece = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long n_pieces = (long)n_col_tiles * kb_pad * 4 * 64;
+  const long n_pieces = (long)n_strips * kb_pad * 4 * 64;
   if (piece >= n_pieces) return;
   const int lane = (int)(piece % 64);
   const int tt = (int)((piece / 64) % 4);
@@ -38,10 +40,12 @@ __global__ __launch_bounds__(256) void repack_q8_kernel(
                  ((uint32_t)q[4 * i + 3] << 24);
     scale = (uint16_t)(blk[0] | (blk[1] << 8));
   }
-  uint4* dq = reinterpret_cast<uint4*>(dst_q + (size_t)g * dst_q_group);
-  dq[piece] = make_uint4(words[0], words[1], words[2], words[3]);
+  const int n_ks = kb_pad / KSTEP, ks = kb / KSTEP, kbi = kb % KSTEP;
+  uint8_t* step = dst + (size_t)g * dst_group_bytes + ((size_t)c * n_ks + ks) * KSTEP_BYTES;
+  *reinterpret_cast<uint4*>(step + (size_t)(kbi * 4 + tt) * 1024 + lane * 16) =
+      make_uint4(words[0], words[1], words[2], words[3]);
   if (half == 0)
-    dst_s[(size_t)g * dst_s_group + ((size_t)(c * 4 + tt) * 32 + r) * kb_pad + kb] = scale;
+    *reinterpret_cast<uint16_t*>(step + 16 * 1024 + ((tt * 32 + r) * KSTEP + kbi) * 2) = scale;
 }
 
 __global__ __launch_bounds__(256) void transpose_router_kernel(const float* __restrict__ w, int E,
@@ -60,14 +64,12 @@ __global__ __launch_bounds__(256) void transpose_router_kernel(const float* __re
 
 hipError_t launch_repack_q8(const uint8_t* src0, const uint8_t* src1, int n_groups,
                             size_t src_group_bytes, int src_rows, int src_blocks,
-                            int tiles_per_src, int n_col_tiles, int kb_pad, int8_t* dst_q,
-                            uint16_t* dst_s, size_t dst_q_group, size_t dst_s_group,
-                            hipStream_t s) {
-  const long n_pieces = (long)n_col_tiles * kb_pad * 4 * 64;
+                            int tiles_per_src, int n_strips, int kb_pad, uint8_t* dst,
+                            size_t dst_group_bytes, hipStream_t s) {
+  const long n_pieces = (long)n_strips * kb_pad * 4 * 64;
   dim3 grid((unsigned)((n_pieces + 255) / 256), (unsigned)n_groups);
   repack_q8_kernel<<<grid, 256, 0, s>>>(src0, src1, src_group_bytes, src_rows, src_blocks,
-                                        tiles_per_src, n_col_tiles, kb_pad, dst_q, dst_s,
-                                        dst_q_group, dst_s_group);
+                                        tiles_per_src, n_strips, kb_pad, dst, dst_group_bytes);
   return hipGetLastError();
 }
 

@@ -12,75 +12,186 @@
 namespace moe {
 namespace {
 
-constexpr int RL_JC = 32;  // router: j values per LDS chunk (8 float4 rows)
+constexpr int RL_JC = 64;  // router: j values per LDS chunk (two 32-blocks)
 
-// Logits for RT tokens per wavefront x 64 experts per workgroup column; lane =
-// expert.  Each logit is one fp32 fused multiply-add chain over ascending j,
-// from +0, then + bias (a separate fp32 add).  The chain order is the contract
-// that makes top-k ids reproducible bit for bit.  The 64 x 32 slab of the
-// transposed router matrix is staged in LDS once per workgroup and read by its
-// four wavefronts; x comes in through wave-uniform (scalar) loads.
+// Router logits for 4*RT tokens x 64 experts per workgroup (lane = expert, RT
+// tokens per wavefront).  Each logit is one fp32 fused multiply-add chain over
+// ascending j, from +0, then + bias (a separate fp32 add); the chain order is
+// the contract that makes top-k ids reproducible bit for bit.  Per chunk of 64
+// j the workgroup stages the transposed router slab (64 experts x 64 j) and the
+// 4*RT token rows in LDS.  With one workgroup per CU the chunk loads are
+// latency-bound, so they run PF chunks ahead through a ring of registers
+// (the chunk loop is unrolled by PF so every ring slot is a fixed register).
+// Zero padding past d leaves every chain unchanged (fma(0, 0, acc) = acc for
+// acc != -0, and a chain from +0 never reaches -0).
+//
+// The workgroups of expert column 0 also run, on the staged x chunk, the
+// per-32-block int8 quantiser (each 32-block is one half-wavefront) and the
+// shared-expert gate dot product, so x is read from HBM once.
+typedef float f4v __attribute__((ext_vector_type(4)));
+
 template <int RT>
-__global__ __launch_bounds__(256) void router_logits_kernel(
-    const float* __restrict__ x, int n, int d, const float* __restrict__ wt,
-    const float* __restrict__ bias, int E, int E64, float* __restrict__ logits) {
-  __shared__ float4 wl[2][RL_JC / 4][64];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int eg = blockIdx.y;
-  const int t0 = blockIdx.x * 4 * RT + wave * RT;
-  const int e = eg * 64 + lane;
-  const float4* wsrc = reinterpret_cast<const float4*>(wt) + eg * 64;
-  const float4* xr[RT];
+struct RouterChunk {
+  f4v w[4];  // W rows jq = tid/64 + 4i of the chunk, expert = lane
+  float x[RT];  // x[token tid/64 + 4r][chunk column lane]
+};
+
+struct RouterCtx {
+  const f4v* wsrc;
+  const float* xbase;
+  int n, d, d4, d_pad, E64, t0, tid, lane, wave;
+  bool quant;
+  const float* shg;
+  int8_t* xq;
+  uint16_t* xs;
+};
+
+template <int RT>
+__device__ __forceinline__ void router_fetch(RouterChunk<RT>& c, const RouterCtx& k, int ch) {
+  const f4v z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int jq = ch * (RL_JC / 4) + (k.tid >> 6) + 4 * i;
+    c.w[i] = (jq < k.d4) ? k.wsrc[(size_t)jq * k.E64 + k.lane] : z4;
+  }
+  const int j = ch * RL_JC + k.lane;
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
-    const int t = min(t0 + r, n - 1);
-    xr[r] = reinterpret_cast<const float4*>(x + (size_t)t * d);
+    const int t = min(k.t0 + (k.tid >> 6) + 4 * r, k.n - 1);
+    c.x[r] = (j < k.d) ? k.xbase[(size_t)t * k.d + j] : 0.0f;
   }
-  float acc[RT];
-#pragma unroll
-  for (int r = 0; r < RT; ++r) acc[r] = 0.0f;
+}
 
-  const int nchunks = d / RL_JC;
-  // cooperative load: 512 float4 per chunk, 2 per thread
-  const int i0 = threadIdx.x, i1 = threadIdx.x + 256;
-  float4 p0 = wsrc[(size_t)(i0 >> 6) * E64 + (i0 & 63)];
-  float4 p1 = wsrc[(size_t)(i1 >> 6) * E64 + (i1 & 63)];
-  wl[0][i0 >> 6][i0 & 63] = p0;
-  wl[0][i1 >> 6][i1 & 63] = p1;
-  __syncthreads();
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int buf = ch & 1;
-    const bool more = ch + 1 < nchunks;
-    if (more) {
-      const size_t jq = (size_t)(ch + 1) * (RL_JC / 4);
-      p0 = wsrc[(jq + (i0 >> 6)) * E64 + (i0 & 63)];
-      p1 = wsrc[(jq + (i1 >> 6)) * E64 + (i1 & 63)];
-    }
+// One chunk: stash the fetched slot into LDS buffer ch&1, refill the slot with
+// chunk ch + PF, quantise (column-0 workgroups), run the fused chains.
+template <int RT, int PF>
+__device__ __forceinline__ void router_step(RouterChunk<RT>& slot, const RouterCtx& k, int ch, int nchunks,
+                                            f4v (&wl)[2][RL_JC / 4][64], f4v (&xl)[2][4 * RT][RL_JC / 4],
+                                            float (&acc)[RT], float (&gacc)[RT]) {
+  constexpr int JQ = RL_JC / 4;
+  const int buf = ch & 1;
 #pragma unroll
-    for (int jl = 0; jl < RL_JC / 4; ++jl) {
-      const float4 wv = wl[buf][jl][lane];
+  for (int i = 0; i < 4; ++i) wl[buf][(k.tid >> 6) + 4 * i][k.lane] = slot.w[i];
 #pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        const float4 xv = xr[r][ch * (RL_JC / 4) + jl];
-        acc[r] = __builtin_fmaf(xv.x, wv.x, acc[r]);
-        acc[r] = __builtin_fmaf(xv.y, wv.y, acc[r]);
-        acc[r] = __builtin_fmaf(xv.z, wv.z, acc[r]);
-        acc[r] = __builtin_fmaf(xv.w, wv.w, acc[r]);
+  for (int r = 0; r < RT; ++r)
+    reinterpret_cast<float*>(&xl[buf][(k.tid >> 6) + 4 * r][0])[k.lane] = slot.x[r];
+  lds_barrier();
+  if (ch + PF < nchunks) router_fetch<RT>(slot, k, ch + PF);
+  if (k.quant) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int tl = (k.tid >> 6) + 4 * r;
+      const float val = reinterpret_cast<const float*>(&xl[buf][tl][0])[k.lane];
+      const int j = ch * RL_JC + k.lane;
+      int8_t q;
+      uint16_t s16;
+      quant_block32(val, q, s16);
+      const int t = k.t0 + tl;
+      if (t < k.n) {
+        k.xq[(size_t)t * k.d_pad + j] = q;
+        if ((k.lane & 31) == 0) k.xs[(size_t)t * (k.d_pad / QB) + (j >> 5)] = s16;
+        if (k.shg && j < k.d) gacc[r] = __builtin_fmaf(val, k.shg[j], gacc[r]);
       }
     }
-    if (more) {
-      wl[buf ^ 1][i0 >> 6][i0 & 63] = p0;
-      wl[buf ^ 1][i1 >> 6][i1 & 63] = p1;
-    }
-    __syncthreads();
+  }
+  // LDS operands in batches of 4 f4v rows, then the fused chains
+#pragma unroll
+  for (int jb = 0; jb < JQ; jb += 4) {
+    f4v wv[4], xv[RT][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wv[q] = wl[buf][jb + q][k.lane];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xv[r][q] = xl[buf][k.wave * RT + r][jb + q];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        acc[r] = __builtin_fmaf(xv[r][q].x, wv[q].x, acc[r]);
+        acc[r] = __builtin_fmaf(xv[r][q].y, wv[q].y, acc[r]);
+        acc[r] = __builtin_fmaf(xv[r][q].z, wv[q].z, acc[r]);
+        acc[r] = __builtin_fmaf(xv[r][q].w, wv[q].w, acc[r]);
+      }
+  }
+}
+
+template <int RT>
+__global__ __launch_bounds__(256, 1) void router_kernel(
+    const float* __restrict__ x, int n, int d, int d_pad, const float* __restrict__ wt,
+    const float* __restrict__ bias, int E, int E64, float* __restrict__ logits,
+    const float* __restrict__ shg, float* __restrict__ gs, int8_t* __restrict__ xq,
+    uint16_t* __restrict__ xs) {
+  constexpr int TPW = 4 * RT;       // tokens per workgroup
+  constexpr int JQ = RL_JC / 4;     // f4v rows per chunk
+  constexpr int PF = 4;             // chunks in flight (one named register slot each)
+  __shared__ f4v wl[2][JQ][64];
+  __shared__ f4v xl[2][TPW][JQ];
+  RouterCtx k;
+  k.tid = threadIdx.x;
+  k.lane = k.tid & 63;
+  k.wave = __builtin_amdgcn_readfirstlane(k.tid >> 6);
+  const int eg = blockIdx.y;
+  k.quant = (eg == 0);
+  k.t0 = blockIdx.x * TPW;
+  k.n = n;
+  k.d = d;
+  k.d4 = d >> 2;
+  k.d_pad = d_pad;
+  k.E64 = E64;
+  k.wsrc = reinterpret_cast<const f4v*>(wt) + eg * 64;
+  k.xbase = x;
+  k.shg = shg;
+  k.xq = xq;
+  k.xs = xs;
+  const int e = eg * 64 + k.lane;
+
+  float acc[RT], gacc[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    acc[r] = 0.0f;
+    gacc[r] = 0.0f;
+  }
+  const int nchunks = (d + RL_JC - 1) / RL_JC;
+  RouterChunk<RT> s0, s1, s2, s3;
+  router_fetch<RT>(s0, k, 0);
+  if (1 < nchunks) router_fetch<RT>(s1, k, 1);
+  if (2 < nchunks) router_fetch<RT>(s2, k, 2);
+  if (3 < nchunks) router_fetch<RT>(s3, k, 3);
+  for (int ch0 = 0; ch0 < nchunks; ch0 += PF) {
+    router_step<RT, PF>(s0, k, ch0, nchunks, wl, xl, acc, gacc);
+    if (ch0 + 1 < nchunks) router_step<RT, PF>(s1, k, ch0 + 1, nchunks, wl, xl, acc, gacc);
+    if (ch0 + 2 < nchunks) router_step<RT, PF>(s2, k, ch0 + 2, nchunks, wl, xl, acc, gacc);
+    if (ch0 + 3 < nchunks) router_step<RT, PF>(s3, k, ch0 + 3, nchunks, wl, xl, acc, gacc);
   }
   if (e < E) {
     const float b = bias ? bias[e] : 0.0f;
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-      const int t = t0 + r;
+      const int t = k.t0 + k.wave * RT + r;
       if (t < n) logits[(size_t)t * E + e] = bias ? acc[r] + b : acc[r];
+    }
+  }
+  if (k.quant) {
+    // zero blocks of the K padding not covered by the chunks
+    const int jpad0 = nchunks * RL_JC;
+    for (int v = k.tid; v < TPW * (d_pad - jpad0); v += 256) {
+      const int tl = v / (d_pad - jpad0), j = jpad0 + v % (d_pad - jpad0);
+      const int t = k.t0 + tl;
+      if (t < n) {
+        xq[(size_t)t * d_pad + j] = 0;
+        if ((j & 31) == 0) xs[(size_t)t * (d_pad / QB) + (j >> 5)] = 0;
+      }
+    }
+    if (shg) {
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        float a = gacc[r];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) a += __shfl_xor(a, off, 64);
+        const int t = k.t0 + (k.tid >> 6) + 4 * r;
+        if (k.lane == 0 && t < n) gs[t] = 1.0f / (1.0f + expf(-a));
+      }
     }
   }
 }
@@ -99,15 +210,13 @@ __device__ inline bool outranks(float av, int ai, float bv, int bi) {
 }
 
 // One workgroup per 16 tokens, one wavefront per 4 of them: top-k by repeated
-// wave-wide best-of-the-rest, softmax over all E, optional renormalisation,
-// shared gate, int8 quantisation of x; then wavefront 0 ranks the tile's
-// (token, slot) pairs per expert in (token, slot) order and the tile's
-// histogram is written for the bucketing kernel.
+// wave-wide best-of-the-rest, softmax over all E, optional renormalisation;
+// then wavefront 0 ranks the tile's (token, slot) pairs per expert in
+// (token, slot) order and the tile's histogram is written for the bucketing
+// kernel.
 __global__ __launch_bounds__(256) void route_kernel(
-    const float* __restrict__ logits, const float* __restrict__ x, int n, int d, int d_pad, int E,
-    int k, int norm, const float* __restrict__ shg, int32_t* __restrict__ ids,
-    float* __restrict__ wout, float* __restrict__ gs, int32_t* __restrict__ rank,
-    int8_t* __restrict__ xq, uint16_t* __restrict__ xs, int32_t* __restrict__ hist) {
+    const float* __restrict__ logits, int n, int E, int k, int norm, int32_t* __restrict__ ids,
+    float* __restrict__ wout, int32_t* __restrict__ rank, int32_t* __restrict__ hist) {
   __shared__ int s_ids[ROUTE_TILE * MAX_TOPK];
   __shared__ int s_cnt[MAX_EXPERTS];
   const int lane = threadIdx.x & 63;
@@ -171,22 +280,6 @@ __global__ __launch_bounds__(256) void route_kernel(
       wout[(size_t)t * k + lane] = p;
       s_ids[tl * MAX_TOPK + lane] = myid;
     }
-    const float* xt = x + (size_t)t * d;
-    if (shg) {
-      float a = 0.0f;
-      for (int j = lane; j < d; j += 64) a = __builtin_fmaf(xt[j], shg[j], a);
-      a = wave_sum(a);
-      if (lane == 0) gs[t] = 1.0f / (1.0f + expf(-a));
-    }
-    for (int b2 = 0; b2 < d_pad / 64; ++b2) {
-      const int j = b2 * 64 + lane;
-      const float val = (j < d) ? xt[j] : 0.0f;
-      int8_t q;
-      uint16_t s16;
-      quant_block32(val, q, s16);
-      xq[(size_t)t * d_pad + j] = q;
-      if ((lane & 31) == 0) xs[(size_t)t * (d_pad / QB) + 2 * b2 + (lane >> 5)] = s16;
-    }
   }
   __syncthreads();
   if (wave == 0) {
@@ -231,27 +324,32 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
 
 }  // namespace
 
-hipError_t launch_router_logits(const float* x, int n, int d, const float* wt, const float* bias,
-                                int E, int E64, float* logits, hipStream_t s) {
+hipError_t launch_router(const float* x, int n, int d, int d_pad, const float* wt, const float* bias,
+                         int E, int E64, float* logits, const float* sh_gate_vec, float* gs,
+                         int8_t* xq, uint16_t* xs, hipStream_t s) {
   const int eg = E64 / 64;
   // tokens per wavefront: as many as keep >= 1024 wavefronts in flight
   int rt = 4;
   while (rt > 1 && (long)((n + rt - 1) / rt) * eg < 1024) rt >>= 1;
   dim3 grid((unsigned)((n + 4 * rt - 1) / (4 * rt)), (unsigned)eg);
   switch (rt) {
-    case 4: router_logits_kernel<4><<<grid, 256, 0, s>>>(x, n, d, wt, bias, E, E64, logits); break;
-    case 2: router_logits_kernel<2><<<grid, 256, 0, s>>>(x, n, d, wt, bias, E, E64, logits); break;
-    default: router_logits_kernel<1><<<grid, 256, 0, s>>>(x, n, d, wt, bias, E, E64, logits); break;
+    case 4:
+      router_kernel<4><<<grid, 256, 0, s>>>(x, n, d, d_pad, wt, bias, E, E64, logits, sh_gate_vec, gs, xq, xs);
+      break;
+    case 2:
+      router_kernel<2><<<grid, 256, 0, s>>>(x, n, d, d_pad, wt, bias, E, E64, logits, sh_gate_vec, gs, xq, xs);
+      break;
+    default:
+      router_kernel<1><<<grid, 256, 0, s>>>(x, n, d, d_pad, wt, bias, E, E64, logits, sh_gate_vec, gs, xq, xs);
+      break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_route(const float* logits, const float* x, int n, int d, int d_pad, int E, int k,
-                        int norm, const float* sh_gate_vec, int32_t* ids, float* w, float* gs,
-                        int32_t* rank, int8_t* xq, uint16_t* xs, int32_t* hist, hipStream_t s) {
+hipError_t launch_route(const float* logits, int n, int E, int k, int norm, int32_t* ids, float* w,
+                        int32_t* rank, int32_t* hist, hipStream_t s) {
   const int tiles = (n + ROUTE_TILE - 1) / ROUTE_TILE;
-  route_kernel<<<tiles, 256, 0, s>>>(logits, x, n, d, d_pad, E, k, norm, sh_gate_vec, ids, w, gs,
-                                     rank, xq, xs, hist);
+  route_kernel<<<tiles, 256, 0, s>>>(logits, n, E, k, norm, ids, w, rank, hist);
   return hipGetLastError();
 }
 
