@@ -14,24 +14,31 @@
 namespace moe {
 namespace {
 
-// Exclusive prefix sum of up to 512 ints held in s[0..n) (in place), 256 threads.
-__device__ void block_exclusive_scan_512(int* s, int n, int* s_tmp /* 256 */) {
-  const int t = threadIdx.x;
-  const int a = (2 * t < n) ? s[2 * t] : 0;
-  const int b = (2 * t + 1 < n) ? s[2 * t + 1] : 0;
-  s_tmp[t] = a + b;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int v = (t >= off) ? s_tmp[t - off] : 0;
-    __syncthreads();
-    s_tmp[t] += v;
-    __syncthreads();
+// Exclusive prefix sum of up to 512 ints held in s[0..n), in place, by one
+// wavefront (call from all 64 lanes of one wavefront): 8 values per lane, then a
+// shuffle scan of the 64 lane totals.
+__device__ void wave_exclusive_scan_512(int* s, int n, int lane) {
+  int v[8];
+  int tot = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int i = lane * 8 + j;
+    v[j] = (i < n) ? s[i] : 0;
+    tot += v[j];
   }
-  const int excl = s_tmp[t] - (a + b);
-  __syncthreads();
-  if (2 * t < n) s[2 * t] = excl;
-  if (2 * t + 1 < n) s[2 * t + 1] = excl + a;
-  __syncthreads();
+  int inc = tot;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int up = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += up;
+  }
+  int run = inc - tot;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int i = lane * 8 + j;
+    if (i < n) s[i] = run;
+    run += v[j];
+  }
 }
 
 __global__ __launch_bounds__(256) void bucket_kernel(
@@ -42,7 +49,6 @@ __global__ __launch_bounds__(256) void bucket_kernel(
   __shared__ int s_start[2 * 256 + 2];
   __shared__ int s_pre[MAX_EXPERTS];
   __shared__ int s_cnt[MAX_EXPERTS + 1];
-  __shared__ int s_tmp[256];
   const int tile = blockIdx.x;
   const int P = n * k;
   // Per-expert totals over all tiles and over the tiles before this one; for
@@ -52,7 +58,18 @@ __global__ __launch_bounds__(256) void bucket_kernel(
   if (threadIdx.x < E * nparts) {
     const int e = threadIdx.x % E, part = threadIdx.x / E;
     int tot = 0, pre = 0;
-    for (int tt = part; tt < n_tiles; tt += nparts) {
+    int tt = part;
+    for (; tt + 3 * nparts < n_tiles; tt += 4 * nparts) {
+      int h[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) h[u] = hist[(size_t)(tt + u * nparts) * E + e];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        tot += h[u];
+        pre += (tt + u * nparts < tile) ? h[u] : 0;
+      }
+    }
+    for (; tt < n_tiles; tt += nparts) {
       const int h = hist[(size_t)tt * E + e];
       tot += h;
       pre += (tt < tile) ? h : 0;
@@ -72,7 +89,8 @@ __global__ __launch_bounds__(256) void bucket_kernel(
     s_pre[e] = pre;
   }
   __syncthreads();
-  block_exclusive_scan_512(s_start, E, s_tmp);
+  if (threadIdx.x < 64) wave_exclusive_scan_512(s_start, E, threadIdx.x);
+  __syncthreads();
 
   const int t0 = tile * ROUTE_TILE;
   const int nt = min(ROUTE_TILE, n - t0);
@@ -102,7 +120,9 @@ __global__ __launch_bounds__(256) void bucket_kernel(
   for (int g = threadIdx.x; g < G; g += 256) s_nt[g] = (s_cnt[g] + MT_WG - 1) / MT_WG;
   __syncthreads();
   const int last_nt = s_nt[G - 1];
-  block_exclusive_scan_512(s_nt, G, s_tmp);
+  __syncthreads();
+  if (threadIdx.x < 64) wave_exclusive_scan_512(s_nt, G, threadIdx.x);
+  __syncthreads();
   for (int g = threadIdx.x; g < G; g += 256) {
     const int c = s_cnt[g];
     const int first = (g < E) ? s_start[g] : P;

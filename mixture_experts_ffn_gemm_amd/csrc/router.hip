@@ -39,11 +39,7 @@ struct RouterChunk {
 struct RouterCtx {
   const f4v* wsrc;
   const float* xbase;
-  int n, d, d4, d_pad, E64, t0, tid, lane, wave;
-  bool quant;
-  const float* shg;
-  int8_t* xq;
-  uint16_t* xs;
+  int n, d, d4, E64, t0, tid, lane, wave;
 };
 
 template <int RT>
@@ -67,7 +63,7 @@ __device__ __forceinline__ void router_fetch(RouterChunk<RT>& c, const RouterCtx
 template <int RT, int PF>
 __device__ __forceinline__ void router_step(RouterChunk<RT>& slot, const RouterCtx& k, int ch, int nchunks,
                                             f4v (&wl)[2][RL_JC / 4][64], f4v (&xl)[2][4 * RT][RL_JC / 4],
-                                            float (&acc)[RT], float (&gacc)[RT]) {
+                                            float (&acc)[RT]) {
   constexpr int JQ = RL_JC / 4;
   const int buf = ch & 1;
 #pragma unroll
@@ -77,23 +73,6 @@ __device__ __forceinline__ void router_step(RouterChunk<RT>& slot, const RouterC
     reinterpret_cast<float*>(&xl[buf][(k.tid >> 6) + 4 * r][0])[k.lane] = slot.x[r];
   lds_barrier();
   if (ch + PF < nchunks) router_fetch<RT>(slot, k, ch + PF);
-  if (k.quant) {
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      const int tl = (k.tid >> 6) + 4 * r;
-      const float val = reinterpret_cast<const float*>(&xl[buf][tl][0])[k.lane];
-      const int j = ch * RL_JC + k.lane;
-      int8_t q;
-      uint16_t s16;
-      quant_block32(val, q, s16);
-      const int t = k.t0 + tl;
-      if (t < k.n) {
-        k.xq[(size_t)t * k.d_pad + j] = q;
-        if ((k.lane & 31) == 0) k.xs[(size_t)t * (k.d_pad / QB) + (j >> 5)] = s16;
-        if (k.shg && j < k.d) gacc[r] = __builtin_fmaf(val, k.shg[j], gacc[r]);
-      }
-    }
-  }
   // LDS operands in batches of 4 f4v rows, then the fused chains
 #pragma unroll
   for (int jb = 0; jb < JQ; jb += 4) {
@@ -118,10 +97,8 @@ __device__ __forceinline__ void router_step(RouterChunk<RT>& slot, const RouterC
 
 template <int RT>
 __global__ __launch_bounds__(256, 1) void router_kernel(
-    const float* __restrict__ x, int n, int d, int d_pad, const float* __restrict__ wt,
-    const float* __restrict__ bias, int E, int E64, float* __restrict__ logits,
-    const float* __restrict__ shg, float* __restrict__ gs, int8_t* __restrict__ xq,
-    uint16_t* __restrict__ xs) {
+    const float* __restrict__ x, int n, int d, const float* __restrict__ wt,
+    const float* __restrict__ bias, int E, int E64, float* __restrict__ logits) {
   constexpr int TPW = 4 * RT;       // tokens per workgroup
   constexpr int JQ = RL_JC / 4;     // f4v rows per chunk
   constexpr int PF = 4;             // chunks in flight (one named register slot each)
@@ -132,26 +109,18 @@ __global__ __launch_bounds__(256, 1) void router_kernel(
   k.lane = k.tid & 63;
   k.wave = __builtin_amdgcn_readfirstlane(k.tid >> 6);
   const int eg = blockIdx.y;
-  k.quant = (eg == 0);
   k.t0 = blockIdx.x * TPW;
   k.n = n;
   k.d = d;
   k.d4 = d >> 2;
-  k.d_pad = d_pad;
   k.E64 = E64;
   k.wsrc = reinterpret_cast<const f4v*>(wt) + eg * 64;
   k.xbase = x;
-  k.shg = shg;
-  k.xq = xq;
-  k.xs = xs;
   const int e = eg * 64 + k.lane;
 
-  float acc[RT], gacc[RT];
+  float acc[RT];
 #pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    acc[r] = 0.0f;
-    gacc[r] = 0.0f;
-  }
+  for (int r = 0; r < RT; ++r) acc[r] = 0.0f;
   const int nchunks = (d + RL_JC - 1) / RL_JC;
   RouterChunk<RT> s0, s1, s2, s3;
   router_fetch<RT>(s0, k, 0);
@@ -159,10 +128,10 @@ __global__ __launch_bounds__(256, 1) void router_kernel(
   if (2 < nchunks) router_fetch<RT>(s2, k, 2);
   if (3 < nchunks) router_fetch<RT>(s3, k, 3);
   for (int ch0 = 0; ch0 < nchunks; ch0 += PF) {
-    router_step<RT, PF>(s0, k, ch0, nchunks, wl, xl, acc, gacc);
-    if (ch0 + 1 < nchunks) router_step<RT, PF>(s1, k, ch0 + 1, nchunks, wl, xl, acc, gacc);
-    if (ch0 + 2 < nchunks) router_step<RT, PF>(s2, k, ch0 + 2, nchunks, wl, xl, acc, gacc);
-    if (ch0 + 3 < nchunks) router_step<RT, PF>(s3, k, ch0 + 3, nchunks, wl, xl, acc, gacc);
+    router_step<RT, PF>(s0, k, ch0, nchunks, wl, xl, acc);
+    if (ch0 + 1 < nchunks) router_step<RT, PF>(s1, k, ch0 + 1, nchunks, wl, xl, acc);
+    if (ch0 + 2 < nchunks) router_step<RT, PF>(s2, k, ch0 + 2, nchunks, wl, xl, acc);
+    if (ch0 + 3 < nchunks) router_step<RT, PF>(s3, k, ch0 + 3, nchunks, wl, xl, acc);
   }
   if (e < E) {
     const float b = bias ? bias[e] : 0.0f;
@@ -172,26 +141,40 @@ __global__ __launch_bounds__(256, 1) void router_kernel(
       if (t < n) logits[(size_t)t * E + e] = bias ? acc[r] + b : acc[r];
     }
   }
-  if (k.quant) {
-    // zero blocks of the K padding not covered by the chunks
-    const int jpad0 = nchunks * RL_JC;
-    for (int v = k.tid; v < TPW * (d_pad - jpad0); v += 256) {
-      const int tl = v / (d_pad - jpad0), j = jpad0 + v % (d_pad - jpad0);
-      const int t = k.t0 + tl;
-      if (t < n) {
-        xq[(size_t)t * d_pad + j] = 0;
-        if ((j & 31) == 0) xs[(size_t)t * (d_pad / QB) + (j >> 5)] = 0;
-      }
+}
+
+// One workgroup per token row: the per-32-block int8 quantiser over the
+// K-padded row (each 32-block is one half-wavefront; padding blocks get zero
+// codes and scales) and, with a shared expert, its gate sigmoid(x . g) reduced
+// in a fixed order.  It runs before the router so that the router's reads of x
+// find it in the cache.
+__global__ __launch_bounds__(256) void quantize_rows_kernel(
+    const float* __restrict__ x, int d, int d_pad, const float* __restrict__ shg,
+    float* __restrict__ gs, int8_t* __restrict__ xq, uint16_t* __restrict__ xs) {
+  __shared__ float s_part[4];
+  const int t = blockIdx.x;
+  const float* xr = x + (size_t)t * d;
+  float gacc = 0.0f;
+  for (int j0 = 0; j0 < d_pad; j0 += 256) {
+    const int j = j0 + threadIdx.x;
+    const float v = (j < d) ? xr[j] : 0.0f;
+    int8_t q;
+    uint16_t s16;
+    quant_block32(v, q, s16);  // every lane takes part in the block's shuffles
+    if (j < d_pad) {
+      xq[(size_t)t * d_pad + j] = q;
+      if ((threadIdx.x & 31) == 0) xs[(size_t)t * (d_pad / QB) + (j >> 5)] = s16;
     }
-    if (shg) {
+    if (shg && j < d) gacc = __builtin_fmaf(v, shg[j], gacc);
+  }
+  if (shg) {
 #pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        float a = gacc[r];
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) a += __shfl_xor(a, off, 64);
-        const int t = k.t0 + (k.tid >> 6) + 4 * r;
-        if (k.lane == 0 && t < n) gs[t] = 1.0f / (1.0f + expf(-a));
-      }
+    for (int off = 32; off > 0; off >>= 1) gacc += __shfl_xor(gacc, off, 64);
+    if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = gacc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const float a = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+      gs[t] = 1.0f / (1.0f + expf(-a));
     }
   }
 }
@@ -202,109 +185,106 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
-// a outranks b: higher logit, then lower id; id INT_MAX marks "no candidate".
-__device__ inline bool outranks(float av, int ai, float bv, int bi) {
-  if (ai == 0x7fffffff) return false;
-  if (bi == 0x7fffffff) return true;
-  return av > bv || (av == bv && ai < bi);
-}
-
-// One workgroup per 16 tokens, one wavefront per 4 of them: top-k by repeated
-// wave-wide best-of-the-rest, softmax over all E, optional renormalisation;
-// then wavefront 0 ranks the tile's (token, slot) pairs per expert in
-// (token, slot) order and the tile's histogram is written for the bucketing
-// kernel.
+// One workgroup per 16 tokens.  The tile's logits are staged in LDS; each
+// (token, expert) finds its rank among the token's experts -- the number of
+// experts with a larger logit, or an equal logit and a lower id -- and the
+// experts of rank < k take slot = rank.  This is the top-k of the contract
+// (logit descending, id ascending) computed without any serial reduction.
+// Then softmax over all E, optional renormalisation, and the per-expert rank
+// of each (token, slot) pair among the tile's pairs in (token, slot) order,
+// with the tile's histogram, for the bucketing kernel.
 __global__ __launch_bounds__(256) void route_kernel(
     const float* __restrict__ logits, int n, int E, int k, int norm, int32_t* __restrict__ ids,
     float* __restrict__ wout, int32_t* __restrict__ rank, int32_t* __restrict__ hist) {
-  __shared__ int s_ids[ROUTE_TILE * MAX_TOPK];
+  __shared__ __attribute__((aligned(16))) float s_l[ROUTE_TILE][MAX_EXPERTS + 4];
+  __shared__ __attribute__((aligned(16))) int s_ids[ROUTE_TILE * MAX_TOPK];
+  __shared__ float s_val[ROUTE_TILE][MAX_TOPK];
   __shared__ int s_cnt[MAX_EXPERTS];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
   const int t0 = blockIdx.x * ROUTE_TILE;
-  for (int e = threadIdx.x; e < E; e += 256) s_cnt[e] = 0;
+  const int nt = min(ROUTE_TILE, n - t0);
+  for (int i = tid; i < ROUTE_TILE * E; i += 256) {
+    const int tl = i / E, e = i - tl * E;
+    s_l[tl][e] = (tl < nt) ? logits[(size_t)(t0 + tl) * E + e] : 0.0f;
+  }
+  if (E & 3)  // pad each row to a multiple of 4 with -inf
+    for (int i = tid; i < ROUTE_TILE * 4; i += 256) {
+      const int tl = i >> 2, e = E + (i & 3);
+      if (e < ((E + 3) & ~3)) s_l[tl][e] = -__builtin_huge_valf();
+    }
+  for (int e = tid; e < E; e += 256) s_cnt[e] = 0;
+  __syncthreads();
 
-  for (int i = 0; i < ROUTE_TILE / 4; ++i) {
-    const int tl = wave * (ROUTE_TILE / 4) + i;
-    const int t = t0 + tl;
-    if (t >= n) break;
-    float v[MAX_EXPERTS / 64];
-    bool live[MAX_EXPERTS / 64];
-#pragma unroll
-    for (int c = 0; c < MAX_EXPERTS / 64; ++c) {
-      const int e = lane + 64 * c;
-      live[c] = e < E;
-      v[c] = live[c] ? logits[(size_t)t * E + e] : 0.0f;
+  // ranks: thread (token tl = tid/16, expert group g = tid%16) owns experts g + 16c
+  const int tl = tid >> 4, g = tid & 15;
+  const int E4 = (E + 3) & ~3;  // logits row padded to 4 with -inf (never outranks)
+  for (int e = g; e < E; e += 16) {
+    const float le = s_l[tl][e];
+    int r = 0;
+#pragma unroll 4
+    for (int e2 = 0; e2 < E4; e2 += 4) {
+      const float4 l4 = *reinterpret_cast<const float4*>(&s_l[tl][e2]);
+      r += (l4.x > le || (l4.x == le && e2 + 0 < e)) ? 1 : 0;
+      r += (l4.y > le || (l4.y == le && e2 + 1 < e)) ? 1 : 0;
+      r += (l4.z > le || (l4.z == le && e2 + 2 < e)) ? 1 : 0;
+      r += (l4.w > le || (l4.w == le && e2 + 3 < e)) ? 1 : 0;
     }
-    float m = 0.0f, myv = 0.0f;
-    int myid = -1;
-    for (int s = 0; s < k; ++s) {
-      float bv = 0.0f;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int c = 0; c < MAX_EXPERTS / 64; ++c)
-        if (live[c] && outranks(v[c], lane + 64 * c, bv, bi)) {
-          bv = v[c];
-          bi = lane + 64 * c;
-        }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, 64);
-        const int oi = __shfl_xor(bi, off, 64);
-        if (outranks(ov, oi, bv, bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if (s == 0) m = bv;
-      if (lane == s) {
-        myid = bi;
-        myv = bv;
-      }
-#pragma unroll
-      for (int c = 0; c < MAX_EXPERTS / 64; ++c)
-        if (lane + 64 * c == bi) live[c] = false;
-    }
-    float part = 0.0f;
-#pragma unroll
-    for (int c = 0; c < MAX_EXPERTS / 64; ++c)
-      if (lane + 64 * c < E) part += expf(v[c] - m);
-    const float den = wave_sum(part);
-    float p = (lane < k) ? expf(myv - m) / den : 0.0f;
-    if (norm) {
-      const float sum = wave_sum(p);
-      p = p / sum;
-    }
-    if (lane < k) {
-      ids[(size_t)t * k + lane] = myid;
-      wout[(size_t)t * k + lane] = p;
-      s_ids[tl * MAX_TOPK + lane] = myid;
+    if (r < k) {
+      s_ids[tl * MAX_TOPK + r] = e;
+      s_val[tl][r] = le;
     }
   }
   __syncthreads();
-  if (wave == 0) {
-    const int nt = min(ROUTE_TILE, n - t0);
-    const int np = nt * k;
-    for (int base = 0; base < np; base += 64) {
-      const int q = base + lane;
-      const bool valid = q < np;
-      const int e = valid ? s_ids[(q / k) * MAX_TOPK + q % k] : -1;
-      int r = 0;
-      bool last = true;
-      for (int i2 = 0; i2 < 64; ++i2) {
-        const int ei = __builtin_amdgcn_readlane(e, i2);
-        if (ei == e) {
-          if (i2 < lane) ++r;
-          if (i2 > lane) last = false;
+
+  // softmax over all E (the 16 threads of a token share the sum), weights of the k slots
+  const float m = s_val[tl][0];
+  float part = 0.0f;
+  for (int e = g; e < E; e += 16) part += expf(s_l[tl][e] - m);
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) part += __shfl_xor(part, off, 16);
+  float p = (g < k) ? expf(s_val[tl][min(g, k - 1)] - m) / part : 0.0f;
+  if (norm) {
+    float sum = p;
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 16);
+    p = p / sum;
+  }
+  if (tl < nt && g < k) {
+    ids[(size_t)(t0 + tl) * k + g] = s_ids[tl * MAX_TOPK + g];
+    wout[(size_t)(t0 + tl) * k + g] = p;
+  }
+
+  // rank of pair q = (token, slot) among the tile's earlier pairs of the same expert
+  const int np = nt * k;
+  if (tid < np) {
+    const int q = tid;
+    const int e = s_ids[(q / k) * MAX_TOPK + q % k];
+    int r = 0;
+    bool last = true;
+    // pairs of earlier tokens (all their k slots), then this token's earlier slots
+    for (int t2 = 0; t2 < nt; ++t2) {
+      const int4* row = reinterpret_cast<const int4*>(&s_ids[t2 * MAX_TOPK]);
+#pragma unroll
+      for (int c4 = 0; c4 < MAX_TOPK / 4; ++c4) {
+        if (4 * c4 >= k) break;
+        const int4 v = row[c4];
+        const int ev[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int s2 = 4 * c4 + u;
+          if (s2 < k && ev[u] == e) {
+            const int q2 = t2 * k + s2;
+            r += (q2 < q) ? 1 : 0;
+            if (q2 > q) last = false;
+          }
         }
       }
-      const int cbase = valid ? s_cnt[e] : 0;
-      if (valid) rank[(size_t)(t0 + q / k) * k + q % k] = cbase + r;
-      if (valid && last) s_cnt[e] = cbase + r + 1;
     }
+    rank[(size_t)(t0 + q / k) * k + q % k] = r;
+    if (last) s_cnt[e] = r + 1;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) hist[(size_t)blockIdx.x * E + e] = s_cnt[e];
+  for (int e = tid; e < E; e += 256) hist[(size_t)blockIdx.x * E + e] = s_cnt[e];
 }
 
 __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ v, int64_t n_values,
@@ -327,21 +307,18 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
 hipError_t launch_router(const float* x, int n, int d, int d_pad, const float* wt, const float* bias,
                          int E, int E64, float* logits, const float* sh_gate_vec, float* gs,
                          int8_t* xq, uint16_t* xs, hipStream_t s) {
+  quantize_rows_kernel<<<n, 256, 0, s>>>(x, d, d_pad, sh_gate_vec, gs, xq, xs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int eg = E64 / 64;
   // tokens per wavefront: as many as keep >= 1024 wavefronts in flight
   int rt = 4;
   while (rt > 1 && (long)((n + rt - 1) / rt) * eg < 1024) rt >>= 1;
   dim3 grid((unsigned)((n + 4 * rt - 1) / (4 * rt)), (unsigned)eg);
   switch (rt) {
-    case 4:
-      router_kernel<4><<<grid, 256, 0, s>>>(x, n, d, d_pad, wt, bias, E, E64, logits, sh_gate_vec, gs, xq, xs);
-      break;
-    case 2:
-      router_kernel<2><<<grid, 256, 0, s>>>(x, n, d, d_pad, wt, bias, E, E64, logits, sh_gate_vec, gs, xq, xs);
-      break;
-    default:
-      router_kernel<1><<<grid, 256, 0, s>>>(x, n, d, d_pad, wt, bias, E, E64, logits, sh_gate_vec, gs, xq, xs);
-      break;
+    case 4: router_kernel<4><<<grid, 256, 0, s>>>(x, n, d, wt, bias, E, E64, logits); break;
+    case 2: router_kernel<2><<<grid, 256, 0, s>>>(x, n, d, wt, bias, E, E64, logits); break;
+    default: router_kernel<1><<<grid, 256, 0, s>>>(x, n, d, wt, bias, E, E64, logits); break;
   }
   return hipGetLastError();
 }
