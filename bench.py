@@ -25,6 +25,9 @@ if ROOT not in sys.path:
 METRIC = "MoE FFN prefill tokens/sec (OLMoE-shape N=2048) + % int8 MFMA peak"
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+# Exact per-32-block rescale: cvt + fma (2 unpacked fp32 lane-ops) per output
+# element per block of 64 int8 ops; 256 CU x 4 SIMD x 16 lanes x 2.4 GHz.
+RESCALE_ROOF_TOPS = 256 * 4 * 16 * 2.4e9 / 2 * 64 / 1e12
 
 
 def log(*a):
@@ -94,18 +97,51 @@ def stage_bytes(shape, n_tokens, counts):
     }
 
 
+KERNEL_SOURCES = ("gemm.hip", "internal.h", "device_util.h")
+
+
+def kernel_source_sha256():
+    """Digest of the sources the grouped GEMM kernels are compiled from."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mixture_experts_ffn_gemm_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def read_traffic(kernel_tag):
-    """Measured HBM bytes per launch of a kernel from the committed rocprofv3
-    PMC summary, valid only while the kernel source is unchanged."""
-    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_pmc.json")
+    """HBM bytes per launch of a kernel from the committed rocprofv3 PMC
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy kernel's
+    reading), valid only while the kernel's sources are unchanged."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_traffic.txt")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path))
-    src = os.path.join(ROOT, "mixture_experts_ffn_gemm_amd", "csrc", rec["source"])
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if sha != rec.get("source_sha256"):
+    rec = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            rec[key.strip()] = val.strip()
+    if rec.get("sources_sha256") != kernel_source_sha256():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    try:
+        return int(float(rec["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib, reps):
+    """Launch a plain streaming kernel (read N bytes, write N bytes) so that
+    rocprofv3's FETCH_SIZE / WRITE_SIZE readings can be scaled to bytes."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.randn(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"kernel": "torch neg (float32, contiguous)",
+                                           "bytes_read": n * 4, "bytes_written": n * 4,
+                                           "launches": reps}}), flush=True)
 
 
 def cpu_baseline(lw, x, target_s):
@@ -132,12 +168,18 @@ def main():
     ap.add_argument("--workload", default="olmoe_n2048")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-time budget of the CPU oracle sample (0 disables it)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain MIB-MiB streaming kernel (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, max(1, args.steps))
+        return
 
     import numpy as np
     import torch
@@ -191,11 +233,13 @@ def main():
     gu_us = stage_ms["gateup_swiglu"] * 1e3
     dn_us = stage_ms["down"] * 1e3
     gu_tops = gu_ops / (gu_us * 1e-6) / 1e12
-    roofline = {"bound": "mfma", "kernel": "gateup_kernel (grouped gate/up + SwiGLU + requant)",
+    roofline = {"bound": "mfma", "kernel": "grouped_gemm_kernel<true> (grouped gate/up + SwiGLU + requantise)",
                 "achieved": round(gu_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
                 "frac": round(gu_tops / INT8_PEAK_TOPS, 4),
                 "traffic": read_traffic("gateup_olmoe_n2048") if args.workload == "olmoe_n2048" else None,
-                "algorithmic_ops_per_launch": gu_ops, "avg_launch_us": round(gu_us, 2)}
+                "algorithmic_ops_per_launch": gu_ops, "avg_launch_us": round(gu_us, 2),
+                "rescale_roof": {"peak": RESCALE_ROOF_TOPS, "unit": "TOP/s",
+                                 "frac": round(gu_tops / RESCALE_ROOF_TOPS, 4)}}
     stages = {}
     for name in B.STAGES:
         us = stage_ms[name] * 1e3
