@@ -10,11 +10,13 @@
 //
 // Work decomposition: the bucketing kernel writes a table of 128-row tiles (a
 // tile never straddles two groups).  A workgroup (4 wavefronts, 32 rows each)
-// computes one tile against one column strip; workgroups are numbered
-// strip-major and dealt XCD-major, so the tiles of one expert that use the same
-// weight strip run back to back on one XCD and share it through its L2.  The
-// grid is the static upper bound on the number of workgroups; surplus
-// workgroups exit after reading the tile count.
+// computes one tile against one column strip.  Workgroups are numbered
+// tile-major (strips inner) and dealt to the 8 XCDs in contiguous ranges, so
+// one XCD runs every strip of a tile back to back (the tile's activation rows
+// stay in its L2) and the few tiles of one expert mostly share an XCD (each
+// weight strip is fetched about once).  The grid is the static upper bound on
+// the number of workgroups; surplus workgroups exit after reading the tile
+// count.
 //
 // K loop: per k-step of 4 blocks the workgroup stages the strip's weight codes
 // (4 blocks x 4 tiles of 32x32 bytes) and their binary16 scales (17 KiB) in LDS
@@ -74,39 +76,47 @@ __device__ inline void stage_kstep(const uint8_t* strip, int ks, const int8_t* a
     __builtin_amdgcn_global_load_lds((glb_void*)(as + i * a_blk), (lds_void*)(ad + i * 1024), 16, 0, 0);
 }
 
-// One k-step (4 blocks) of 4 output tiles for this wavefront.
-//   buf : staged k-step (weights, their scales, this wavefront's A chunks)
-//   sa  : the 4 binary16 activation scales of this lane's A row (zero in lanes 32..63)
-// All operands of the k-step are read from LDS first (A: 4 chunks, B: 16
-// chunks, scales).  The 16 (block, tile) steps are then software-pipelined one
-// step deep with the issue order pinned so that every MFMA is followed by 16
-// independent VALU operations of the previous step: the MFMA pipe (about half
-// as busy as the VALU) then never blocks instruction issue.
-__device__ inline void compute_kstep(const char* buf, int wave, uint2 sa, int lane, v16f (&acc)[4]) {
-  const v16i zi = {0};
-  const v16f zf = {0};
+// Operands of one k-step (4 blocks x 4 output tiles) for this wavefront, read
+// from the staged LDS buffer into registers: the A chunks of its 32 rows, the
+// 16 B chunks and the weight scales of the 4 tiles.
+struct KOps {
+  v4i av[KSTEP];
+  v4i bv[4 * KSTEP];
   v4h sw[4];
+};
+
+__device__ inline void load_kstep(const char* buf, int wave, int lane, KOps& o) {
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
     const uint2 p = *reinterpret_cast<const uint2*>(buf + 16 * 1024 + (tt * 32 + (lane & 31)) * 8);
-    sw[tt] = as_v4h(p.x, p.y);
+    o.sw[tt] = as_v4h(p.x, p.y);
   }
+  const char* bp = buf + lane * 16;
+  const char* apl = buf + A_OFF + wave * (KSTEP * 1024) + lane * 16;
+#pragma unroll
+  for (int i = 0; i < KSTEP; ++i) o.av[i] = *reinterpret_cast<const v4i*>(apl + i * 1024);
+#pragma unroll
+  for (int j = 0; j < 4 * KSTEP; ++j) o.bv[j] = *reinterpret_cast<const v4i*>(bp + j * 1024);
+}
+
+// One k-step from registers.  sa holds the 4 binary16 activation scales of
+// this lane's A row; lanes 32..63 contribute zero K slots to the scale MFMA.
+// The 16 (block, tile) steps are software-pipelined one step deep with the
+// issue order pinned so that every MFMA is followed by 16 independent VALU
+// operations of the previous step: the MFMA pipe (about half as busy as the
+// VALU) then never blocks instruction issue.
+__device__ inline void compute_kstep(const KOps& o, uint2 sa, int lane, v16f (&acc)[4]) {
+  const v16i zi = {0};
+  const v16f zf = {0};
+  if (lane >= 32) sa = make_uint2(0u, 0u);
   v4h sav[KSTEP];
 #pragma unroll
   for (int i = 0; i < KSTEP; ++i) {
     const uint32_t m = (i & 1) ? 0xffff0000u : 0x0000ffffu;
     sav[i] = (i < 2) ? as_v4h(sa.x & m, 0u) : as_v4h(0u, sa.y & m);
   }
-  const char* bp = buf + lane * 16;
-  const char* apl = buf + A_OFF + wave * (KSTEP * 1024) + lane * 16;
-  v4i av[KSTEP], bv[4 * KSTEP];
-#pragma unroll
-  for (int i = 0; i < KSTEP; ++i) av[i] = *reinterpret_cast<const v4i*>(apl + i * 1024);
-#pragma unroll
-  for (int j = 0; j < 4 * KSTEP; ++j) bv[j] = *reinterpret_cast<const v4i*>(bp + j * 1024);
-
-  v16i c_cur = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[0], bv[0], zi, 0, 0, 0);
-  v16f s_cur = __builtin_amdgcn_mfma_f32_32x32x8f16(sav[0], sw[0], zf, 0, 0, 0);
+  v16i c_cur = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.av[0], o.bv[0], zi, 0, 0, 0);
+  v16f s_cur = __builtin_amdgcn_mfma_f32_32x32x8f16(sav[0], o.sw[0], zf, 0, 0, 0);
 #pragma unroll
   for (int j = 0; j < 4 * KSTEP; ++j) {
     const int t0 = j & 3;
@@ -117,12 +127,12 @@ __device__ inline void compute_kstep(const char* buf, int wave, uint2 sa, int la
     float cf[16];
     // sched_barrier(0) fences pin this exact order: MFMA(j+1), convert(j),
     // scale MFMA(j+1), accumulate(j).
-    if (more) c_nxt = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[i1], bv[j + 1], zi, 0, 0, 0);
+    if (more) c_nxt = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.av[i1], o.bv[j + 1], zi, 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int v = 0; v < 16; ++v) cf[v] = (float)c_cur[v];
     __builtin_amdgcn_sched_barrier(0);
-    if (more) s_nxt = __builtin_amdgcn_mfma_f32_32x32x8f16(sav[i1], sw[t1], zf, 0, 0, 0);
+    if (more) s_nxt = __builtin_amdgcn_mfma_f32_32x32x8f16(sav[i1], o.sw[t1], zf, 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[t0][v] = __builtin_fmaf(cf[v], s_cur[v], acc[t0][v]);
@@ -132,6 +142,27 @@ __device__ inline void compute_kstep(const char* buf, int wave, uint2 sa, int la
       s_cur = s_nxt;
     }
   }
+}
+
+// One iteration of the double-buffered k loop on buffer `cur` (the other
+// buffer, `nxt`, receives k-step ks+1).  Order matters: the barrier makes
+// k-step ks visible and frees `nxt` (every wavefront has read its operands of
+// ks-1); the operands of ks are read into registers before the loads into
+// `nxt` are issued, so no LDS read waits behind those loads; the prefetched
+// activation scales are first used one iteration later, so nothing waits for
+// them either.  The loads of ks+1 then overlap the whole compute of ks.
+__device__ inline void kloop_step(const uint8_t* strip, int ks, int KS, const int8_t* ap, size_t a_blk,
+                                  const uint16_t* asp, bool active, int wave, int lane,
+                                  const char* cur, char* nxt, uint2 sa_cur, uint2& sa_nxt,
+                                  v16f (&acc)[4]) {
+  __syncthreads();
+  KOps o;
+  if (active) load_kstep(cur, wave, lane, o);
+  if (ks + 1 < KS) {
+    stage_kstep(strip, ks + 1, ap, a_blk, nxt, wave, lane);
+    if (active) sa_nxt = *reinterpret_cast<const uint2*>(asp + (size_t)(ks + 1) * KSTEP);
+  }
+  if (active) compute_kstep(o, sa_cur, lane, acc);
 }
 
 // Grouped GEMM.  GATEUP: A = gathered int8 token rows (xq via expTokI), B = the
@@ -155,7 +186,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
   if (slot >= per_xcd) return;
   const int blk = ((int)blockIdx.x & 7) * per_xcd + slot;
   if (blk >= n_valid) return;
-  const int c = blk / n_tiles, T = blk - (blk / n_tiles) * n_tiles;
+  const int T = blk / nstrips, c = blk - (blk / nstrips) * nstrips;
   const int32_t* ent = a.tiles + 4 + 3 * T;
   const int g = ent[0], row0 = ent[1], row_end = ent[2];
   if (g < 0 || g >= a.G || row0 < 0 || row_end <= row0 || row_end > a.p_total) return;
@@ -187,25 +218,15 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
   v16f acc[4];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) acc[tt] = (v16f){0};
-  uint2 sacur = make_uint2(0u, 0u), sanext = make_uint2(0u, 0u);
 
   stage_kstep(strip, 0, ap, a_blk, lds[0], wave, lane);
-  if (active) {
-    sacur = *reinterpret_cast<const uint2*>(asp);
-    if (lane >= 32) sacur = make_uint2(0u, 0u);
-  }
-  for (int ks = 0; ks < KS; ++ks) {
-    __syncthreads();  // k-step ks is in LDS; every wavefront is done with k-step ks-1
-    const bool more = ks + 1 < KS;
-    if (more) {
-      stage_kstep(strip, ks + 1, ap, a_blk, lds[(ks + 1) & 1], wave, lane);
-      if (active) {
-        sanext = *reinterpret_cast<const uint2*>(asp + (size_t)(ks + 1) * KSTEP);
-        if (lane >= 32) sanext = make_uint2(0u, 0u);
-      }
-    }
-    if (active) compute_kstep(lds[ks & 1], wave, sacur, lane, acc);
-    sacur = sanext;
+  uint2 sa0 = make_uint2(0u, 0u), sa1 = make_uint2(0u, 0u);
+  if (active) sa0 = *reinterpret_cast<const uint2*>(asp);
+  // Unrolled by two so that each buffer and scale register is fixed.
+  for (int ks = 0; ks < KS; ks += 2) {
+    kloop_step(strip, ks, KS, ap, a_blk, asp, active, wave, lane, lds[0], lds[1], sa0, sa1, acc);
+    if (ks + 1 < KS)
+      kloop_step(strip, ks + 1, KS, ap, a_blk, asp, active, wave, lane, lds[1], lds[0], sa1, sa0, acc);
   }
   __syncthreads();  // every wavefront is out of the k loop: LDS is free for the epilogue
   if (!active) return;
