@@ -93,8 +93,10 @@ typedef struct moe_ffn_weights moe_ffn_weights;
  * intermediate products of a call (for parity checks).  Any member may be
  * NULL.  Shapes: topk_ids / topk_w [N][k]; shared_gate [N]; exp_start
  * [E+1(+1 with a shared expert)]; exp_tok_i / exp_tok_k [N*k (+N)]; xq [N][d]
- * int8; xs [N][d/32] binary16 bits; partial [N][k(+1)][d] fp32 unweighted
- * expert outputs, slot k holding the shared expert. */
+ * int8 (16-byte aligned, else MOE_FFN_INVALID_ARG); xs [N][d/32] binary16
+ * bits; partial [N][k(+1)][d] fp32 unweighted expert outputs, slot k holding
+ * the shared expert.  They must not overlap the inputs, `out` or the
+ * workspace. */
 typedef struct moe_ffn_routing {
   int32_t* topk_ids;
   float* topk_w;
@@ -159,8 +161,8 @@ int moe_ffn_prefill(const moe_ffn_weights* w, const float* x, int32_t n_tokens, 
  * MOE_FFN_N_STAGE_EVENTS caller-created hipEvent_t handles (host array); event
  * i is recorded on `stream` before stage i and the last one after the final
  * stage, so hipEventElapsedTime(ev[i], ev[i+1]) is the device time of stage i:
- * 0 router logits, 1 routing + quantiser, 2 bucketing, 3 grouped gate/up +
- * SwiGLU, 4 grouped down, 5 combine.  Same arguments and results as
+ * 0 router logits, 1 top-k routing, 2 bucketing + activation quantiser,
+ * 3 grouped gate/up + SwiGLU, 4 grouped down, 5 combine.  Same arguments and results as
  * moe_ffn_prefill otherwise. */
 #define MOE_FFN_N_STAGE_EVENTS 7
 int moe_ffn_prefill_profiled(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* out,

@@ -154,7 +154,7 @@ def moe_ffn_prefill(handle: int, x, n_tokens: int, out, ws, ws_bytes: int,
 
 
 N_STAGE_EVENTS = 7
-STAGES = ("router_logits", "route_quantise", "bucket", "gateup_swiglu", "down", "combine")
+STAGES = ("router_logits", "route", "bucket_quantise", "gateup_swiglu", "down", "combine")
 
 
 def moe_ffn_prefill_profiled(handle: int, x, n_tokens: int, out, ws, ws_bytes: int, stage_events,

@@ -4,11 +4,14 @@
 // One prefill call enqueues, on the caller's stream and without any host
 // synchronisation or device-to-host transfer (SharpInference #388 "Remaining
 // levers" 1: the selection must not round-trip to the host):
-//   1. router                   (fp32 fused-chain logits for all experts, the
-//                                int8 quantiser of x, the shared-expert gate)
+//   1. router                   (fp32 fused-chain logits for all experts)
 //   2. routing                  (top-k, softmax weights, per-tile expert
 //                                histograms and ranks)
-//   3. bucketing                (CSR expStart/expTokI/expTokK + 32-row tile table)
+//   3. bucketing                (CSR expStart/expTokI/expTokK, the 128-row tile
+//                                table, each pair's padded GEMM row), then the
+//                                int8 quantiser of x (and the shared-expert
+//                                gate), which writes each token's codes to its
+//                                expert slots' rows in GEMM operand form
 //   4. grouped gate/up + SwiGLU (one launch over all experts + shared expert)
 //   5. grouped down             (one launch; unweighted partials per slot)
 //   6. ordered combine          (#129 "Scope")
@@ -43,14 +46,16 @@ WsLayout ws_layout(const Dims& dm, int max_tokens) {
   L.rank = take(Nn * dm.k * 4);
   L.w = take(Nn * dm.k * 4);
   L.gs = take(Nn * 4);
-  L.xq = take(Nn * dm.d_pad);
-  L.xs = take(Nn * (dm.d_pad / QB) * 2);
   L.hist = take((size_t)L.n_route_tiles * dm.E * 4);
   L.exp_start = take((size_t)(dm.E + 2) * 4);
   L.tok_i = take(P_total * 4);
   L.tok_k = take(P_total * 4);
+  L.pos = take(Nn * kk * 4);
   L.tiles = take((4 + 3 * (size_t)L.tile_bound) * 4);
   const size_t t32 = (size_t)L.tile_bound * (MT_WG / MT_WAVE);
+  const size_t kbd = (size_t)dm.d_pad / QB;
+  L.gq = take(t32 * kbd * 1024);
+  L.gqs = take(t32 * 32 * kbd * 2);
   L.hq = take(t32 * kbmax * 1024);
   L.hs = take(t32 * 32 * kbmax * 2);
   L.partial = take(Nn * kk * dm.d * 4);
@@ -123,6 +128,7 @@ int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, v
     return MOE_FFN_INVALID_ARG;
   const size_t xb = (size_t)n * dm.d * sizeof(float);
   if (overlaps(x, xb, out, xb) || overlaps(out, xb, ws, ws_bytes)) return MOE_FFN_INVALID_ARG;
+  if (r && r->xq && ((uintptr_t)r->xq & 15u)) return MOE_FFN_INVALID_ARG;
   const int dev_ok = current_device_matches(W);
   if (dev_ok != MOE_FFN_OK) return dev_ok;
 
@@ -132,13 +138,14 @@ int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, v
   int32_t* rank = (int32_t*)(base + L.rank);
   float* w = (float*)(base + L.w);
   float* gs = (float*)(base + L.gs);
-  int8_t* xq = (int8_t*)(base + L.xq);
-  uint16_t* xs = (uint16_t*)(base + L.xs);
   int32_t* hist = (int32_t*)(base + L.hist);
   int32_t* exp_start = (int32_t*)(base + L.exp_start);
   int32_t* tok_i = (int32_t*)(base + L.tok_i);
   int32_t* tok_k = (int32_t*)(base + L.tok_k);
+  int32_t* pos = (int32_t*)(base + L.pos);
   int32_t* tiles = (int32_t*)(base + L.tiles);
+  int8_t* gq = (int8_t*)(base + L.gq);
+  uint16_t* gqs = (uint16_t*)(base + L.gqs);
   int8_t* hq = (int8_t*)(base + L.hq);
   uint16_t* hs = (uint16_t*)(base + L.hs);
   float* partial = (float*)(base + L.partial);
@@ -146,13 +153,16 @@ int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, v
   auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
 
   HIP_TRY(mark(0));
-  HIP_TRY(launch_router(x, n, dm.d, dm.d_pad, W->router_wt, W->has_bias ? W->router_bias : nullptr,
-                        dm.E, dm.E64, logits, dm.has_shared ? W->sh_gate_vec : nullptr, gs, xq, xs, s));
+  HIP_TRY(launch_router(x, n, dm.d, W->router_wt, W->has_bias ? W->router_bias : nullptr, dm.E,
+                        dm.E64, logits, s));
   HIP_TRY(mark(1));
   HIP_TRY(launch_route(logits, n, dm.E, dm.k, dm.norm, ids, w, rank, hist, s));
   HIP_TRY(mark(2));
-  HIP_TRY(launch_bucket(ids, rank, hist, n, dm.E, dm.k, dm.has_shared, exp_start, tok_i, tok_k,
+  HIP_TRY(launch_bucket(ids, rank, hist, n, dm.E, dm.k, dm.has_shared, exp_start, tok_i, tok_k, pos,
                         tiles, L.tile_bound, s));
+  HIP_TRY(launch_quantize_scatter(x, n, dm.d, dm.d_pad, pos, kk, L.tile_bound * MT_WG, gq, gqs,
+                                  dm.has_shared ? W->sh_gate_vec : nullptr, gs,
+                                  r ? r->xq : nullptr, r ? r->xs : nullptr, s));
   GemmArgs a{};
   a.tiles = tiles;
   a.tok_i = tok_i;
@@ -165,8 +175,8 @@ int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, v
   a.kbmax = dm.kmax_pad / QB;
   a.hq = hq;
   a.hs = hs;
-  a.xq = xq;
-  a.xs = xs;
+  a.gq = gq;
+  a.gqs = gqs;
   a.d_pad = dm.d_pad;
   a.gu = W->gu;
   a.gu_group = W->gu_per_expert;
@@ -199,12 +209,6 @@ int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, v
                              hipMemcpyDeviceToDevice, s));
     if (r->exp_tok_i) HIP_TRY(hipMemcpyAsync(r->exp_tok_i, tok_i, ptot * 4, hipMemcpyDeviceToDevice, s));
     if (r->exp_tok_k) HIP_TRY(hipMemcpyAsync(r->exp_tok_k, tok_k, ptot * 4, hipMemcpyDeviceToDevice, s));
-    if (r->xq)
-      HIP_TRY(hipMemcpy2DAsync(r->xq, (size_t)dm.d, xq, (size_t)dm.d_pad, (size_t)dm.d, (size_t)n,
-                               hipMemcpyDeviceToDevice, s));
-    if (r->xs)
-      HIP_TRY(hipMemcpy2DAsync(r->xs, (size_t)(dm.d / QB) * 2, xs, (size_t)(dm.d_pad / QB) * 2,
-                               (size_t)(dm.d / QB) * 2, (size_t)n, hipMemcpyDeviceToDevice, s));
     if (r->partial)
       HIP_TRY(hipMemcpyAsync(r->partial, partial, (size_t)n * kk * dm.d * 4, hipMemcpyDeviceToDevice, s));
   }

@@ -7,8 +7,12 @@
 // pair's CSR position is then
 //     expStart[e] + (pairs of e in earlier tiles) + rank,
 // which keeps every expert's rows in (token, slot) order -- a stable counting
-// sort with no atomics, so the result is deterministic.  Workgroup 0 also
-// writes expStart and the table of 128-row tiles that drives the grouped GEMMs.
+// sort with no atomics, so the result is deterministic.  Each group's rows are
+// cut into 128-row GEMM tiles; a pair's padded row (its group's first tile *
+// 128 + its index within the group) is written per (token, slot), so the
+// quantiser can place the token's codes where the GEMM's tile reads them.
+// Workgroup 0 also writes expStart and the tile table that drives the grouped
+// GEMMs.
 #include "internal.h"
 
 namespace moe {
@@ -45,12 +49,15 @@ __global__ __launch_bounds__(256) void bucket_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ rank,
     const int32_t* __restrict__ hist, int n, int E, int k, int has_shared, int n_tiles,
     int32_t* __restrict__ exp_start, int32_t* __restrict__ tok_i, int32_t* __restrict__ tok_k,
-    int32_t* __restrict__ tiles, int tile_bound) {
+    int32_t* __restrict__ pos_out, int32_t* __restrict__ tiles, int tile_bound) {
   __shared__ int s_start[2 * 256 + 2];
   __shared__ int s_pre[MAX_EXPERTS];
   __shared__ int s_cnt[MAX_EXPERTS + 1];
+  __shared__ int s_nt[2 * 256 + 2];
   const int tile = blockIdx.x;
   const int P = n * k;
+  const int G = E + has_shared;
+  const int kk = k + has_shared;
   // Per-expert totals over all tiles and over the tiles before this one; for
   // small E several threads share an expert's column and their sums meet in LDS.
   __shared__ int s_part_tot[256], s_part_pre[256];
@@ -88,41 +95,44 @@ __global__ __launch_bounds__(256) void bucket_kernel(
     s_cnt[e] = tot;
     s_pre[e] = pre;
   }
+  if (threadIdx.x == 0 && has_shared) s_cnt[E] = n;
+  __syncthreads();
+  // group tile counts (every workgroup needs the first tile of each group)
+  for (int g = threadIdx.x; g < G; g += 256) s_nt[g] = (s_cnt[g] + MT_WG - 1) / MT_WG;
+  __syncthreads();
+  const int last_nt = s_nt[G - 1];
   __syncthreads();
   if (threadIdx.x < 64) wave_exclusive_scan_512(s_start, E, threadIdx.x);
+  else if (threadIdx.x < 128) wave_exclusive_scan_512(s_nt, G, threadIdx.x - 64);
   __syncthreads();
 
+  const int pad_rows = tile_bound * MT_WG;
   const int t0 = tile * ROUTE_TILE;
   const int nt = min(ROUTE_TILE, n - t0);
   for (int q = threadIdx.x; q < nt * k; q += 256) {
     const int t = t0 + q / k, s = q % k;
     const int e = ids[(size_t)t * k + s];
-    const int pos = s_start[e] + s_pre[e] + rank[(size_t)t * k + s];
+    const int local = s_pre[e] + rank[(size_t)t * k + s];
+    const int pos = s_start[e] + local;
     if ((unsigned)pos < (unsigned)P) {
       tok_i[pos] = t;
       tok_k[pos] = s;
     }
+    const int prow = s_nt[e] * MT_WG + local;
+    pos_out[(size_t)t * kk + s] = prow < pad_rows ? prow : -1;
   }
   if (has_shared)
     for (int q = threadIdx.x; q < nt; q += 256) {
       tok_i[P + t0 + q] = t0 + q;
       tok_k[P + t0 + q] = k;
+      const int prow = s_nt[E] * MT_WG + t0 + q;
+      pos_out[(size_t)(t0 + q) * kk + k] = prow < pad_rows ? prow : -1;
     }
 
   if (tile != 0) return;
   // expStart, then the 128-row tile table over the E (+1) groups
   for (int e = threadIdx.x; e <= E; e += 256) exp_start[e] = (e < E) ? s_start[e] : P;
   if (has_shared && threadIdx.x == 0) exp_start[E + 1] = P + n;
-  const int G = E + has_shared;
-  if (threadIdx.x == 0 && has_shared) s_cnt[E] = n;
-  __syncthreads();
-  __shared__ int s_nt[2 * 256 + 2];
-  for (int g = threadIdx.x; g < G; g += 256) s_nt[g] = (s_cnt[g] + MT_WG - 1) / MT_WG;
-  __syncthreads();
-  const int last_nt = s_nt[G - 1];
-  __syncthreads();
-  if (threadIdx.x < 64) wave_exclusive_scan_512(s_nt, G, threadIdx.x);
-  __syncthreads();
   for (int g = threadIdx.x; g < G; g += 256) {
     const int c = s_cnt[g];
     const int first = (g < E) ? s_start[g] : P;
@@ -146,10 +156,10 @@ __global__ __launch_bounds__(256) void bucket_kernel(
 
 hipError_t launch_bucket(const int32_t* ids, const int32_t* rank, const int32_t* hist, int n, int E,
                          int k, int has_shared, int32_t* exp_start, int32_t* tok_i, int32_t* tok_k,
-                         int32_t* tiles, int tile_bound, hipStream_t s) {
+                         int32_t* pos, int32_t* tiles, int tile_bound, hipStream_t s) {
   const int n_tiles = (n + ROUTE_TILE - 1) / ROUTE_TILE;
   bucket_kernel<<<n_tiles, 256, 0, s>>>(ids, rank, hist, n, E, k, has_shared, n_tiles, exp_start,
-                                        tok_i, tok_k, tiles, tile_bound);
+                                        tok_i, tok_k, pos, tiles, tile_bound);
   return hipGetLastError();
 }
 

@@ -29,6 +29,37 @@ __device__ inline void quant_block32(float v, int8_t& q, uint16_t& s16) {
   s16 = __half_as_ushort(__float2half_rn(dd));
 }
 
+// The same quantiser with each lane holding half a block (16 values; lanes
+// 2i and 2i+1 hold block i): amax over the lane pair, then the codes of this
+// lane's 16 values packed little-endian into 4 words.  Decisions identical to
+// quant_block32.
+__device__ inline void quant_half_block16(const float (&v)[16], uint32_t (&packed)[4],
+                                          uint16_t& s16) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(v[i]));
+  a = fmaxf(a, __shfl_xor(a, 1, 64));
+  if (a == 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) packed[i] = 0u;
+    s16 = 0;
+    return;
+  }
+  const float dd = a / 127.0f;
+  const float id = 127.0f / a;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t w = 0u;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      float r = rintf(v[4 * i + b] * id);
+      r = fminf(fmaxf(r, -127.0f), 127.0f);
+      w |= ((uint32_t)(int)r & 0xffu) << (8 * b);
+    }
+    packed[i] = w;
+  }
+  s16 = __half_as_ushort(__float2half_rn(dd));
+}
 
 // Workgroup barrier that orders LDS accesses only: global loads still in flight
 // (a register prefetch ring) are not drained, unlike __syncthreads().

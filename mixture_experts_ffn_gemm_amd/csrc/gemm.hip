@@ -18,17 +18,40 @@
 // the number of workgroups; surplus workgroups exit after reading the tile
 // count.
 //
-// K loop: per k-step of 4 blocks the workgroup stages the strip's weight codes
-// (4 blocks x 4 tiles of 32x32 bytes) and their binary16 scales (17 KiB) in LDS
-// with direct global->LDS loads, double-buffered.  Per 32-block each wavefront
-// issues, per 32x32 output tile,
+// Arithmetic per 32-block, per 32x32 output tile of a wavefront:
 //   v_mfma_i32_32x32x32_i8  -> exact int32 block sums C[m][n]
 //   v_mfma_f32_32x32x8_f16  -> S[m][n] = sa[m] * sw[n]: an outer product of the
 //                              two binary16 block scales, exact in fp32 (only
 //                              one of the 8 K slots is non-zero in A),
-// and the VALU does acc = fma(float(C), S, acc): two VALU operations per
-// output element per block, which is the bound of this kernel (the MFMA pipe
-// is about 35% busy).
+// then the VALU does acc = fma(float(C), S, acc): two VALU operations per
+// output element per block, which bounds the kernel.  Everything else is
+// arranged so that it hides under that VALU stream:
+//
+// * Memory: per k-step (4 blocks) a workgroup stages the strip's weight codes
+//   (16 chunks of 1 KiB: [block][tile]) and scales (1 KiB), and each
+//   wavefront its 32 activation rows (a 4 KiB slab [row][128 B], the 16-byte
+//   pieces of row r XOR-swizzled by r%8 so that the MFMA operand reads are
+//   free of LDS bank conflicts) and their scales (256 B), with direct
+//   global->LDS copies into one of two LDS buffers.  Every copy reads whole
+//   cache lines: the quantiser and the gate/up epilogue store the activations
+//   already in slab form (a gather of 32 scattered rows per copy would hold
+//   one vector-L1 miss slot per row and stall the copies behind the L1's miss
+//   limit).  Every wavefront issues
+//   exactly DMA_PER_KSTEP copies per k-step, in two halves (weights right after
+//   the barrier, activations one block later) so that the copies of all
+//   wavefronts never queue at once.  The copies are inline assembly, so the
+//   compiler never inserts its own (conservative) waits for them, and they are
+//   waited for with explicit vmcnt counts (the loop issues no other
+//   vector-memory instructions).
+// * One barrier per k-step, before the last block of k-step j: it publishes
+//   k-step j+1 (copied four blocks earlier) and proves that every wavefront
+//   has read all of k-step j, whose buffer then receives k-step j+2.
+// * LDS operands are read one block ahead: the A chunk and the 4 B chunks of
+//   block b+1 are requested before block b is computed, so LDS latency and
+//   bandwidth overlap the MFMA/VALU work instead of stalling after a barrier.
+// * Within a block the 4 tiles are software-pipelined one step deep with the
+//   issue order pinned: MFMA(t+1), convert(t), scale MFMA(t+1), accumulate(t),
+//   and the pipeline runs on across blocks and k-steps.
 // Operand layouts (gfx950): A lane l = row l%32, bytes/halves k = 16*(l/32)+j
 // (i8) or 4*(l/32)+j (f16x8); B likewise by column; D lane l = column l%32,
 // register v = row 8*(v/4) + 4*(l/32) + v%4.
@@ -42,11 +65,18 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
+typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr int A_OFF = KSTEP_BYTES;                   // A chunks follow the weight k-step
-constexpr int STAGE_BYTES = KSTEP_BYTES + 4 * KSTEP * 1024;  // + 4 wavefronts x 4 A chunks
+constexpr int NWAVE = MT_WG / MT_WAVE;                   // 4 wavefronts x 32 rows
+constexpr int B_OFF = 0;                                 // weight codes [block][tile] x 1 KiB
+constexpr int BS_OFF = 16 * 1024;                        // weight scales [tile][32 rows][4 blocks]
+constexpr int A_OFF = KSTEP_BYTES;                       // activation chunks [wave][block] x 1 KiB
+constexpr int AS_OFF = A_OFF + NWAVE * KSTEP * 1024;     // activation scales [wave][32 rows][4 blocks]
+constexpr int STAGE = AS_OFF + NWAVE * 32 * KSTEP * 2;   // 34 KiB per k-step buffer
+constexpr int DMA_PER_KSTEP = 10;                        // copies per wavefront per k-step
+constexpr int EPI_STRIDE = 65;                           // gate/up epilogue scratch row (floats)
+static_assert(NWAVE * 32 * EPI_STRIDE * 4 <= STAGE, "epilogue scratch must fit in one buffer");
+static_assert(2 * 2 * STAGE <= 160 * 1024, "two workgroups per CU must fit in the LDS");
 
 __device__ inline int out_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
 
@@ -55,124 +85,196 @@ __device__ inline v4h as_v4h(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(v4h, u);
 }
 
-// Stage k-step `ks`: the weight strip's 17 chunks of 1 KiB (codes + scales)
-// into `dst`, and this wavefront's 4 A-operand chunks (one per block) into
-// dst + A_OFF + wave * 4 KiB.  All loads go straight from global memory to LDS;
-// A rows are gathered per lane (lane l supplies row l%32, half l/32).
-__device__ inline void stage_kstep(const uint8_t* strip, int ks, const int8_t* ap, size_t a_blk,
-                                   char* dst, int wave, int lane) {
-  const uint8_t* src = strip + (size_t)ks * KSTEP_BYTES + lane * 16;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int chunk = wave + 4 * i;
-    __builtin_amdgcn_global_load_lds((glb_void*)(src + chunk * 1024), (lds_void*)(dst + chunk * 1024), 16, 0, 0);
-  }
-  if (wave == 0)
-    __builtin_amdgcn_global_load_lds((glb_void*)(src + 16 * 1024), (lds_void*)(dst + 16 * 1024), 16, 0, 0);
-  const int8_t* as = ap + (size_t)ks * KSTEP * a_blk;
-  char* ad = dst + A_OFF + wave * (KSTEP * 1024);
-#pragma unroll
-  for (int i = 0; i < KSTEP; ++i)
-    __builtin_amdgcn_global_load_lds((glb_void*)(as + i * a_blk), (lds_void*)(ad + i * 1024), 16, 0, 0);
+// global -> LDS copies: lane l moves `size` bytes from base + voff (base is
+// wavefront-uniform, voff this lane's 32-bit offset) to LDS address
+// m0 + size * l (m0 is wavefront-uniform).
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
 }
 
-// Operands of one k-step (4 blocks x 4 output tiles) for this wavefront, read
-// from the staged LDS buffer into registers: the A chunks of its 32 rows, the
-// 16 B chunks and the weight scales of the 4 tiles.
-struct KOps {
-  v4i av[KSTEP];
-  v4i bv[4 * KSTEP];
-  v4h sw[4];
+// Wait until at most n of this wavefront's copies are in flight (vector loads
+// complete in order), then meet the other wavefronts.
+__device__ __forceinline__ void wait_copies_barrier_0() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void wait_copies_barrier_1kstep() {
+  static_assert(DMA_PER_KSTEP == 10, "the vmcnt immediate below is DMA_PER_KSTEP");
+  asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Copy sources of k-step 0: wavefront-uniform bases and per-lane 32-bit
+// offsets.  K-step j adds j * KSTEP_BYTES to the weight base, KSTEP chunks to
+// the activation base and one k-step of scales (32 rows x KSTEP) to the scale
+// base.
+struct Src {
+  const uint8_t* w;    // the strip's first k-step
+  const int8_t* a;     // this wavefront's activation chunks (gq or hq)
+  const uint16_t* as;  // their scales (gqs or hs)
+  uint32_t o_w;        // 16 * lane: code chunk piece
+  uint32_t o_ws;       // 16 KiB + 256 * wave + 4 * lane: a quarter of the weight scales
 };
 
-__device__ inline void load_kstep(const char* buf, int wave, int lane, KOps& o) {
+// This wavefront's copies of k-step j into the buffer at LDS address L, in
+// two halves issued at different points of the k loop, so that the copies of
+// all wavefronts never queue at once: the weight half (code chunks wave + 4i
+// and a quarter of the weight scales) and the activation half (its 4
+// activation chunks and its 32 rows' activation scales).
+__device__ __forceinline__ void issue_weights(const Src& s, int j, uint32_t L, int wave) {
+  const uint8_t* w = s.w + (size_t)j * KSTEP_BYTES;
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    const uint2 p = *reinterpret_cast<const uint2*>(buf + 16 * 1024 + (tt * 32 + (lane & 31)) * 8);
-    o.sw[tt] = as_v4h(p.x, p.y);
+  for (int i = 0; i < 4; ++i) {
+    const int c = wave + 4 * i;
+    dma16(w + c * 1024, s.o_w, L + B_OFF + c * 1024);
   }
-  const char* bp = buf + lane * 16;
-  const char* apl = buf + A_OFF + wave * (KSTEP * 1024) + lane * 16;
+  dma4(w, s.o_ws, L + BS_OFF + wave * 256);
+}
+__device__ __forceinline__ void issue_acts(const Src& s, int j, uint32_t L, int wave, int lane) {
+  const int8_t* a = s.a + (size_t)j * KSTEP * 1024;
 #pragma unroll
-  for (int i = 0; i < KSTEP; ++i) o.av[i] = *reinterpret_cast<const v4i*>(apl + i * 1024);
-#pragma unroll
-  for (int j = 0; j < 4 * KSTEP; ++j) o.bv[j] = *reinterpret_cast<const v4i*>(bp + j * 1024);
+  for (int i = 0; i < KSTEP; ++i) dma16(a + i * 1024, lane * 16, L + A_OFF + (wave * KSTEP + i) * 1024);
+  dma4(s.as + (size_t)j * 32 * KSTEP, lane * 4, L + AS_OFF + wave * 256);
 }
 
-// One k-step from registers.  sa holds the 4 binary16 activation scales of
-// this lane's A row; lanes 32..63 contribute zero K slots to the scale MFMA.
-// The 16 (block, tile) steps are software-pipelined one step deep with the
-// issue order pinned so that every MFMA is followed by 16 independent VALU
-// operations of the previous step: the MFMA pipe (about half as busy as the
-// VALU) then never blocks instruction issue.
-__device__ inline void compute_kstep(const KOps& o, uint2 sa, int lane, v16f (&acc)[4]) {
+// Register operands of one block: this wavefront's A chunk and the 4 B chunks.
+struct Ops {
+  v4i a;
+  v4i b[4];
+};
+
+__device__ __forceinline__ void read_block(const char* buf, int b, int wave, int lane, Ops& o) {
+  // A: row lane%32, piece 2b + lane/32 of the k-step, stored at its row's
+  // 128-byte line position (piece ^ row%8)
+  const int r = lane & 31, p = 2 * b + (lane >> 5);
+  o.a = *reinterpret_cast<const v4i*>(buf + A_OFF + wave * (KSTEP * 1024) + r * 128 + ((p ^ (r & 7)) << 4));
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    o.b[t] = *reinterpret_cast<const v4i*>(buf + B_OFF + (b * 4 + t) * 1024 + lane * 16);
+}
+
+// The k-step's scales: weight scales of the 4 tiles (column lane%32, blocks
+// 0-3: the B operands of the scale MFMA) and the activation scales of this
+// lane's row (lanes 32-63 supply the zero K slots 4-7).
+struct Scales {
+  v4h sw[4];
+  uint2 sa;
+};
+
+__device__ __forceinline__ void read_scales(const char* buf, int wave, int lane, Scales& s) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint2 p = *reinterpret_cast<const uint2*>(buf + BS_OFF + (t * 32 + (lane & 31)) * 8);
+    s.sw[t] = as_v4h(p.x, p.y);
+  }
+  const uint2 p = *reinterpret_cast<const uint2*>(buf + AS_OFF + wave * 256 + (lane & 31) * 8);
+  const uint32_t m = lane < 32 ? 0xffffffffu : 0u;
+  s.sa = make_uint2(p.x & m, p.y & m);
+}
+
+// A operand of the scale MFMA for block b: K slot b holds this row's scale.
+__device__ __forceinline__ v4h sa_slot(const uint2 sa, int b) {
+  const uint32_t m = (b & 1) ? 0xffff0000u : 0x0000ffffu;
+  return b < 2 ? as_v4h(sa.x & m, 0u) : as_v4h(0u, sa.y & m);
+}
+
+// Empty asm statements that take values "in and out" without emitting an
+// instruction.  Volatile asm statements keep their order, so threading the
+// pipeline's values through them pins the issue order of the MFMAs and the
+// VALU groups (instruction selection would otherwise hoist all of a k-step's
+// scale MFMAs, whose operands are known at its start, and run out of registers).
+template <typename T>
+__device__ __forceinline__ void anchor(T& v) {
+  asm volatile("" : "+v"(v));
+}
+template <typename T, typename U>
+__device__ __forceinline__ void anchor(T& v, U& u) {
+  asm volatile("" : "+v"(v), "+v"(u));
+}
+
+// One block (4 tiles) of the pipeline.  On entry c and s hold the in-flight
+// MFMAs of tile 0 of this block; on exit they hold those of tile 0 of the
+// next block (operands `on`, scales `sn`, block bn).  Per tile t the order is
+// MFMA(t+1), convert(t), scale MFMA(t+1), accumulate(t).
+__device__ __forceinline__ void compute_block(const Ops& o, const Scales& sc, int b, const Ops& on,
+                                              const Scales& sn, int bn, v16i& c, v16f& s,
+                                              v16f (&acc)[4]) {
   const v16i zi = {0};
   const v16f zf = {0};
-  if (lane >= 32) sa = make_uint2(0u, 0u);
-  v4h sav[KSTEP];
+  v4h sav = sa_slot(sc.sa, b);
+  v4h savn = sa_slot(sn.sa, bn);
 #pragma unroll
-  for (int i = 0; i < KSTEP; ++i) {
-    const uint32_t m = (i & 1) ? 0xffff0000u : 0x0000ffffu;
-    sav[i] = (i < 2) ? as_v4h(sa.x & m, 0u) : as_v4h(0u, sa.y & m);
-  }
-  v16i c_cur = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.av[0], o.bv[0], zi, 0, 0, 0);
-  v16f s_cur = __builtin_amdgcn_mfma_f32_32x32x8f16(sav[0], o.sw[0], zf, 0, 0, 0);
+  for (int t = 0; t < 4; ++t) {
+    v16i cn = t < 3 ? __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a, o.b[t + 1], zi, 0, 0, 0)
+                    : __builtin_amdgcn_mfma_i32_32x32x32_i8(on.a, on.b[0], zi, 0, 0, 0);
+    anchor(cn, c);
+    v16f cf;
 #pragma unroll
-  for (int j = 0; j < 4 * KSTEP; ++j) {
-    const int t0 = j & 3;
-    const bool more = j + 1 < 4 * KSTEP;
-    const int i1 = (j + 1) >> 2, t1 = (j + 1) & 3;
-    v16i c_nxt;
-    v16f s_nxt;
-    float cf[16];
-    // sched_barrier(0) fences pin this exact order: MFMA(j+1), convert(j),
-    // scale MFMA(j+1), accumulate(j).
-    if (more) c_nxt = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.av[i1], o.bv[j + 1], zi, 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int v = 0; v < 16; ++v) cf[v] = (float)c[v];
+    if (t < 3)
+      anchor(cf, sav);
+    else
+      anchor(cf, savn);
+    v16f sx = t < 3 ? __builtin_amdgcn_mfma_f32_32x32x8f16(sav, sc.sw[t + 1], zf, 0, 0, 0)
+                    : __builtin_amdgcn_mfma_f32_32x32x8f16(savn, sn.sw[0], zf, 0, 0, 0);
+    anchor(sx, acc[t]);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) cf[v] = (float)c_cur[v];
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) s_nxt = __builtin_amdgcn_mfma_f32_32x32x8f16(sav[i1], o.sw[t1], zf, 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[t0][v] = __builtin_fmaf(cf[v], s_cur[v], acc[t0][v]);
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) {
-      c_cur = c_nxt;
-      s_cur = s_nxt;
-    }
+    for (int v = 0; v < 16; ++v) acc[t][v] = __builtin_fmaf(cf[v], s[v], acc[t][v]);
+    anchor(acc[t]);
+    c = cn;
+    s = sx;
   }
 }
 
-// One iteration of the double-buffered k loop on buffer `cur` (the other
-// buffer, `nxt`, receives k-step ks+1).  Order matters: the barrier makes
-// k-step ks visible and frees `nxt` (every wavefront has read its operands of
-// ks-1); the operands of ks are read into registers before the loads into
-// `nxt` are issued, so no LDS read waits behind those loads; the prefetched
-// activation scales are first used one iteration later, so nothing waits for
-// them either.  The loads of ks+1 then overlap the whole compute of ks.
-__device__ inline void kloop_step(const uint8_t* strip, int ks, int KS, const int8_t* ap, size_t a_blk,
-                                  const uint16_t* asp, bool active, int wave, int lane,
-                                  const char* cur, char* nxt, uint2 sa_cur, uint2& sa_nxt,
-                                  v16f (&acc)[4]) {
-  __syncthreads();
-  KOps o;
-  if (active) load_kstep(cur, wave, lane, o);
-  if (ks + 1 < KS) {
-    stage_kstep(strip, ks + 1, ap, a_blk, nxt, wave, lane);
-    if (active) sa_nxt = *reinterpret_cast<const uint2*>(asp + (size_t)(ks + 1) * KSTEP);
+// K-step j of an active wavefront, from buffer `cur`; k-step j+1 is (or, for
+// the last k-step, stale data standing in for it is) in `nxt`.  On entry X
+// holds block 0's operands, sc the k-step's scales and c/s the MFMAs of
+// (block 0, tile 0); on exit X, sn and c/s are those of k-step j+1 (after the
+// last k-step they belong to no k-step and are discarded).
+__device__ __forceinline__ void kstep(const Src& src, int j, int KS, int wave, int lane, const char* cur,
+                                      const char* nxt, uint32_t cur_lds, uint32_t nxt_lds, Ops& X,
+                                      Ops& Y, const Scales& sc, Scales& sn, v16i& c, v16f& s,
+                                      v16f (&acc)[4]) {
+  // The activation half of k-step j+1 (its weight half went out at the
+  // barrier of k-step j-1; k-steps 0 and 1 are copied whole by the prologue).
+  if (j >= 1 && j + 1 < KS) issue_acts(src, j + 1, nxt_lds, wave, lane);
+  read_block(cur, 1, wave, lane, Y);
+  compute_block(X, sc, 0, Y, sc, 1, c, s, acc);
+  read_block(cur, 2, wave, lane, X);
+  compute_block(Y, sc, 1, X, sc, 2, c, s, acc);
+  read_block(cur, 3, wave, lane, Y);
+  compute_block(X, sc, 2, Y, sc, 3, c, s, acc);
+  if (j + 1 < KS) {
+    // k-step j+1 has landed for every wavefront, and every wavefront has read
+    // all of k-step j: its buffer takes k-step j+2.
+    wait_copies_barrier_0();
+    if (j + 2 < KS) issue_weights(src, j + 2, cur_lds, wave);
   }
-  if (active) compute_kstep(o, sa_cur, lane, acc);
+  read_block(nxt, 0, wave, lane, X);
+  read_scales(nxt, wave, lane, sn);
+  compute_block(Y, sc, 3, X, sn, 0, c, s, acc);
 }
 
-// Grouped GEMM.  GATEUP: A = gathered int8 token rows (xq via expTokI), B = the
+// Grouped GEMM.  GATEUP: A = the int8 token rows of the tile's (token, slot)
+// pairs, which the quantiser wrote in chunk form at their padded rows; B = the
 // [gate;up] strip of 64 SwiGLU columns; epilogue h = silu(gate) * up,
 // requantised per 32 into the down GEMM's A-operand chunks.  !GATEUP: A = those
 // chunks, B = a 128-column strip of the down matrix; epilogue scatters the fp32
 // rows to partial[token][slot] (the unweighted down-partials of #129 "Scope").
 template <bool GATEUP>
 __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[2][STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[2][STAGE];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_tiles = min(a.tiles[0], a.tile_bound);
@@ -186,47 +288,70 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
   if (slot >= per_xcd) return;
   const int blk = ((int)blockIdx.x & 7) * per_xcd + slot;
   if (blk >= n_valid) return;
-  const int T = blk / nstrips, c = blk - (blk / nstrips) * nstrips;
+  const int T = blk / nstrips, cs = blk - (blk / nstrips) * nstrips;
   const int32_t* ent = a.tiles + 4 + 3 * T;
   const int g = ent[0], row0 = ent[1], row_end = ent[2];
   if (g < 0 || g >= a.G || row0 < 0 || row_end <= row0 || row_end > a.p_total) return;
   const bool shared = g >= a.E;
   const int Fg_pad = shared ? a.Fs_pad : a.F_pad;
-  if (GATEUP && c >= Fg_pad / GU_COLS) return;
+  if (GATEUP && cs >= Fg_pad / GU_COLS) return;
   const int KB = GATEUP ? a.d_pad / QB : Fg_pad / QB;
   const int KS = KB / KSTEP;
   const uint8_t* strip = GATEUP ? (shared ? a.sh_gu : a.gu + (size_t)g * a.gu_group)
                                 : (shared ? a.sh_dn : a.dn + (size_t)g * a.dn_group);
-  strip += (size_t)c * KS * KSTEP_BYTES;
+  strip += (size_t)cs * KS * KSTEP_BYTES;
 
   const int wrow0 = row0 + MT_WAVE * wave;  // first CSR row of this wavefront
-  const bool active = wrow0 < row_end;
-  const int t32 = T * (MT_WG / MT_WAVE) + wave;  // 32-row tile index of the h chunks
-  const int8_t* ap;
-  const uint16_t* asp;
-  if (GATEUP) {
-    const int p_lane = min(wrow0 + (lane & 31), row_end - 1);
-    const int tok = min(max(a.tok_i[p_lane], 0), a.n_tokens - 1);
-    ap = a.xq + (size_t)tok * a.d_pad + (lane >> 5) * 16;
-    asp = a.xs + (size_t)tok * KB;
+  const bool active = wrow0 < row_end;      // wavefront-uniform
+  const int t32 = T * NWAVE + wave;         // 32-row tile index of the h chunks
+  // A operand: this wavefront's run of 1 KiB chunks (one per 32-block) and
+  // their scales, per 32-row quarter t32 of the tile.
+  const int a_kb = GATEUP ? a.d_pad / QB : a.kbmax;
+  Src src;
+  src.w = strip;
+  src.o_w = lane * 16;
+  src.o_ws = 16 * 1024 + wave * 256 + lane * 4;
+  src.a = (GATEUP ? a.gq : a.hq) + (size_t)t32 * a_kb * 1024;
+  src.as = (GATEUP ? a.gqs : a.hs) + (size_t)t32 * a_kb * 32;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)&lds[0][0];
+  const uint32_t lds1 = (uint32_t)(uintptr_t)(lds_char*)&lds[1][0];
+
+  // Prologue: k-steps 0 and 1 in flight; wait for k-step 0.
+  issue_weights(src, 0, lds0, wave);
+  issue_acts(src, 0, lds0, wave, lane);
+  if (KS > 1) {
+    issue_weights(src, 1, lds1, wave);
+    issue_acts(src, 1, lds1, wave, lane);
+    wait_copies_barrier_1kstep();
   } else {
-    ap = a.hq + (size_t)t32 * a.kbmax * 1024 + lane * 16;
-    asp = a.hs + ((size_t)t32 * 32 + (lane & 31)) * a.kbmax;
+    wait_copies_barrier_0();
   }
-  const size_t a_blk = GATEUP ? QB : 1024;  // bytes between consecutive blocks of one A row
-
   v16f acc[4];
+  if (active) {
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt) acc[tt] = (v16f){0};
-
-  stage_kstep(strip, 0, ap, a_blk, lds[0], wave, lane);
-  uint2 sa0 = make_uint2(0u, 0u), sa1 = make_uint2(0u, 0u);
-  if (active) sa0 = *reinterpret_cast<const uint2*>(asp);
-  // Unrolled by two so that each buffer and scale register is fixed.
-  for (int ks = 0; ks < KS; ks += 2) {
-    kloop_step(strip, ks, KS, ap, a_blk, asp, active, wave, lane, lds[0], lds[1], sa0, sa1, acc);
-    if (ks + 1 < KS)
-      kloop_step(strip, ks + 1, KS, ap, a_blk, asp, active, wave, lane, lds[1], lds[0], sa1, sa0, acc);
+    for (int t = 0; t < 4; ++t) acc[t] = (v16f){0};
+    Ops X, Y;
+    Scales s0, s1;
+    read_block(lds[0], 0, wave, lane, X);
+    read_scales(lds[0], wave, lane, s0);
+    const v16i zi = {0};
+    const v16f zf = {0};
+    v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(X.a, X.b[0], zi, 0, 0, 0);
+    v16f s = __builtin_amdgcn_mfma_f32_32x32x8f16(sa_slot(s0.sa, 0), s0.sw[0], zf, 0, 0, 0);
+    // Unrolled by two so that each buffer and scale set has a fixed role.
+    for (int j = 0; j < KS; j += 2) {
+      kstep(src, j, KS, wave, lane, lds[0], lds[1], lds0, lds1, X, Y, s0, s1, c, s, acc);
+      if (j + 1 < KS)
+        kstep(src, j + 1, KS, wave, lane, lds[1], lds[0], lds1, lds0, X, Y, s1, s0, c, s, acc);
+    }
+  } else {
+    // A wavefront past the tile's rows computes nothing but still does its
+    // share of the copies and meets every barrier.
+    for (int j = 0; j + 1 < KS; ++j) {
+      if (j >= 1) issue_acts(src, j + 1, (j & 1) ? lds0 : lds1, wave, lane);
+      wait_copies_barrier_0();
+      if (j + 2 < KS) issue_weights(src, j + 2, (j & 1) ? lds1 : lds0, wave);
+    }
   }
   __syncthreads();  // every wavefront is out of the k loop: LDS is free for the epilogue
   if (!active) return;
@@ -236,14 +361,14 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
     // through LDS ([32][65] floats, conflict-free) so that lane l then owns the
     // whole 32-block (row l%32, sub-strip l/32): amax, the two divisions and 32
     // codes per lane, written as two 16-byte pieces of the down GEMM's A chunk.
-    float* hl = reinterpret_cast<float*>(&lds[0][0]) + wave * (32 * 65);
+    float* hl = reinterpret_cast<float*>(&lds[0][0]) + wave * (32 * EPI_STRIDE);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float gv = acc[sub][v], uv = acc[2 + sub][v];
         const float h = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
-        hl[out_row(v, lane) * 65 + sub * 32 + (lane & 31)] = h;
+        hl[out_row(v, lane) * EPI_STRIDE + sub * 32 + (lane & 31)] = h;
       }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -252,7 +377,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
-      hv[j] = hl[r * 65 + sub * 32 + j];
+      hv[j] = hl[r * EPI_STRIDE + sub * 32 + j];
       amax = fmaxf(amax, fabsf(hv[j]));
     }
     uint32_t packed[8];
@@ -275,11 +400,15 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
         packed[i] = w;
       }
     }
-    const int kbf = 2 * c + sub;
-    char* chunk = reinterpret_cast<char*>(a.hq) + ((size_t)t32 * a.kbmax + kbf) * 1024 + r * 16;
-    *reinterpret_cast<uint4*>(chunk) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    *reinterpret_cast<uint4*>(chunk + 512) = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-    a.hs[((size_t)t32 * 32 + r) * a.kbmax + kbf] = s16;
+    // block kbf of h = pieces 2(kbf%4), +1 of k-step kbf/4 in row r's line
+    const int kbf = 2 * cs + sub, p0 = 2 * (kbf & 3);
+    char* line = reinterpret_cast<char*>(a.hq) +
+                 (((size_t)t32 * (a.kbmax / KSTEP) + (kbf >> 2)) * 32 + r) * 128;
+    *reinterpret_cast<uint4*>(line + ((p0 ^ (r & 7)) << 4)) =
+        make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    *reinterpret_cast<uint4*>(line + (((p0 + 1) ^ (r & 7)) << 4)) =
+        make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    a.hs[(((size_t)t32 * (a.kbmax / KSTEP) + (kbf >> 2)) * 32 + r) * KSTEP + (kbf & 3)] = s16;
   } else {
     const int p_lane = min(wrow0 + (lane & 31), row_end - 1);
     const int tok_l = a.tok_i[p_lane];
@@ -288,12 +417,12 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
     for (int v = 0; v < 16; ++v) {
       const int m = out_row(v, lane);
       const int tok = __shfl(tok_l, m, 64);
-      const int slot = __shfl(slot_l, m, 64);
-      if (wrow0 + m < row_end && (unsigned)tok < (unsigned)a.n_tokens && (unsigned)slot < (unsigned)a.kk) {
-        float* dst = a.partial + ((size_t)tok * a.kk + slot) * a.d;
+      const int slt = __shfl(slot_l, m, 64);
+      if (wrow0 + m < row_end && (unsigned)tok < (unsigned)a.n_tokens && (unsigned)slt < (unsigned)a.kk) {
+        float* dst = a.partial + ((size_t)tok * a.kk + slt) * a.d;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-          const int col = c * DN_COLS + tt * 32 + (lane & 31);
+          const int col = cs * DN_COLS + tt * 32 + (lane & 31);
           if (col < a.d) dst[col] = acc[tt][v];
         }
       }

@@ -20,13 +20,21 @@
 //
 // Workspace (per call, caller-allocated, carved by ws_layout()):
 //   logits fp32 [N][E]; ids, rank i32 [N][k]; w fp32 [N][k]; gs fp32 [N];
-//   xq int8 [N][d_pad]; xs fp16 [N][d_pad/32]; hist i32 [ceil(N/16)][E];
-//   exp_start i32 [E+2]; tok_i, tok_k i32 [N*k + N];
+//   hist i32 [ceil(N/16)][E]; exp_start i32 [E+2]; tok_i, tok_k i32 [N*k + N];
+//   pos i32 [N][k + has_shared]  (padded GEMM row of each (token, slot) pair:
+//                               first tile of its group * 128 + its index in
+//                               the group; -1 if beyond the tile bound);
 //   tiles i32 [4 + 3*T_bound]  (tiles[0] = number of 128-row tiles, then
 //                               {group, first CSR row, end CSR row} per tile);
-//   hq int8 [4*T_bound][KBMAX][2][32][16]  (the down GEMM's A operand chunks,
-//                               one run per 32-row quarter of a tile);
-//   hs fp16 [4*T_bound][32][KBMAX];
+//   The GEMM A operands, per 32-row quarter t32 of a tile (padded row / 32)
+//   and k-step j (4 blocks = 128 codes):
+//   gq int8 [4*T_bound][d_pad/128][32 rows][128]  (gate/up activations: a 4 KiB
+//                               slab per (t32, j); the 16-code piece p of row r
+//                               (block p/2 of the k-step, half p%2) sits at byte
+//                               16 * (p ^ (r % 8)) of the row's 128-byte line);
+//   gqs fp16 [4*T_bound][d_pad/128][32][4]    (their scales);
+//   hq int8 [4*T_bound][KBMAX/4][32][128], hs fp16 [4*T_bound][KBMAX/4][32][4]
+//                               (the same for h, the down GEMM's A operand);
 //   partial fp32 [N][k + has_shared][d].
 #pragma once
 
@@ -63,7 +71,7 @@ struct Dims {
 inline int round_up(int v, int m) { return (v + m - 1) / m * m; }
 
 struct WsLayout {
-  size_t logits, ids, rank, w, gs, xq, xs, hist, exp_start, tok_i, tok_k, tiles, hq, hs, partial;
+  size_t logits, ids, rank, w, gs, hist, exp_start, tok_i, tok_k, pos, tiles, gq, gqs, hq, hs, partial;
   size_t total;
   int n_route_tiles;
   int tile_bound;
@@ -98,16 +106,23 @@ hipError_t launch_repack_q8(const uint8_t* src0, const uint8_t* src1, int n_grou
                             hipStream_t s);
 hipError_t launch_transpose_router(const float* w, int E, int d, int E64, float* wt, hipStream_t s);
 
-hipError_t launch_router(const float* x, int n, int d, int d_pad, const float* wt, const float* bias,
-                         int E, int E64, float* logits, const float* sh_gate_vec, float* gs,
-                         int8_t* xq, uint16_t* xs, hipStream_t s);
+hipError_t launch_router(const float* x, int n, int d, const float* wt, const float* bias, int E,
+                         int E64, float* logits, hipStream_t s);
+// Quantise every token row per 32-block and write its codes and scales to the
+// padded GEMM rows pos[t][0..kk) in the gq/gqs layout (rows past pad_rows or
+// -1 are skipped); with sh_gate_vec != NULL also gs[t] = sigmoid(x[t] . g);
+// xq_out [N][d] / xs_out [N][d/32] (each optional) receive token-major copies.
+hipError_t launch_quantize_scatter(const float* x, int n, int d, int d_pad, const int32_t* pos,
+                                  int kk, int pad_rows, int8_t* gq, uint16_t* gqs,
+                                  const float* sh_gate_vec, float* gs, int8_t* xq_out,
+                                  uint16_t* xs_out, hipStream_t s);
 hipError_t launch_route(const float* logits, int n, int E, int k, int norm, int32_t* ids, float* w,
                         int32_t* rank, int32_t* hist, hipStream_t s);
 hipError_t launch_quantize(const float* v, int64_t n_values, int8_t* q, uint16_t* scales,
                            hipStream_t s);
 hipError_t launch_bucket(const int32_t* ids, const int32_t* rank, const int32_t* hist, int n,
                          int E, int k, int has_shared, int32_t* exp_start, int32_t* tok_i,
-                         int32_t* tok_k, int32_t* tiles, int tile_bound, hipStream_t s);
+                         int32_t* tok_k, int32_t* pos, int32_t* tiles, int tile_bound, hipStream_t s);
 
 struct GemmArgs {
   // common
@@ -123,8 +138,8 @@ struct GemmArgs {
   int8_t* hq;
   uint16_t* hs;
   // gate/up
-  const int8_t* xq;
-  const uint16_t* xs;
+  const int8_t* gq;
+  const uint16_t* gqs;
   int d_pad;
   const uint8_t* gu;
   size_t gu_group;

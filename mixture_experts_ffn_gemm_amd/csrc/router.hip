@@ -1,5 +1,7 @@
-// router.hip -- router logits, top-k / softmax / shared gate, per-32 int8
-// activation quantiser and the per-tile expert histograms.
+// router.hip -- router logits, top-k / softmax, the per-tile expert
+// histograms, and the per-32 int8 activation quantiser (with the shared gate),
+// which runs after the bucketing and scatters each token's codes to its
+// expert slots.
 //
 // SharpInference #388 "Remaining levers" 1 moves the router matvec
 // norm[N x embDim] x routerW[numExperts x embDim] + softmax + top-k + shexp-gate
@@ -24,10 +26,6 @@ constexpr int RL_JC = 64;  // router: j values per LDS chunk (two 32-blocks)
 // (the chunk loop is unrolled by PF so every ring slot is a fixed register).
 // Zero padding past d leaves every chain unchanged (fma(0, 0, acc) = acc for
 // acc != -0, and a chain from +0 never reaches -0).
-//
-// The workgroups of expert column 0 also run, on the staged x chunk, the
-// per-32-block int8 quantiser (each 32-block is one half-wavefront) and the
-// shared-expert gate dot product, so x is read from HBM once.
 typedef float f4v __attribute__((ext_vector_type(4)));
 
 template <int RT>
@@ -59,7 +57,7 @@ __device__ __forceinline__ void router_fetch(RouterChunk<RT>& c, const RouterCtx
 }
 
 // One chunk: stash the fetched slot into LDS buffer ch&1, refill the slot with
-// chunk ch + PF, quantise (column-0 workgroups), run the fused chains.
+// chunk ch + PF, run the fused chains.
 template <int RT, int PF>
 __device__ __forceinline__ void router_step(RouterChunk<RT>& slot, const RouterCtx& k, int ch, int nchunks,
                                             f4v (&wl)[2][RL_JC / 4][64], f4v (&xl)[2][4 * RT][RL_JC / 4],
@@ -143,39 +141,79 @@ __global__ __launch_bounds__(256, 1) void router_kernel(
   }
 }
 
-// One workgroup per token row: the per-32-block int8 quantiser over the
-// K-padded row (each 32-block is one half-wavefront; padding blocks get zero
-// codes and scales) and, with a shared expert, its gate sigmoid(x . g) reduced
-// in a fixed order.  It runs before the router so that the router's reads of x
-// find it in the cache.
-__global__ __launch_bounds__(256) void quantize_rows_kernel(
-    const float* __restrict__ x, int d, int d_pad, const float* __restrict__ shg,
-    float* __restrict__ gs, int8_t* __restrict__ xq, uint16_t* __restrict__ xs) {
-  __shared__ float s_part[4];
-  const int t = blockIdx.x;
+// Activation quantiser and scatter, after the bucketing: one wavefront per
+// token row.  Lane pairs quantise 32-blocks (each lane 16 values), and each
+// block's codes and scale are written once per expert slot of the token,
+// straight into the GEMM operand layout at the slot's padded row
+// (t32 = row / 32, r = row % 32): one 4 KiB slab per (t32, k-step) holding
+// [32 rows][128 B], piece p (16 codes: block p/2 of the k-step, half p%2)
+// of row r at 16 * (p ^ (r % 8)), and the scales at [t32][k-step][r][block].
+// The 8 lanes of one k-step therefore write one whole 128-byte line per slot.
+// The K-padding blocks past d get zero codes and scales.  With a shared
+// expert the wavefront also computes the gate sigmoid(x . g) (a fixed-order
+// reduction).  Optionally the token-major codes and scales are written out.
+__global__ __launch_bounds__(256) void quantize_scatter_kernel(
+    const float* __restrict__ x, int n, int d, int d_pad, const int32_t* __restrict__ pos, int kk,
+    int pad_rows, int8_t* __restrict__ gq, uint16_t* __restrict__ gqs,
+    const float* __restrict__ shg, float* __restrict__ gs, int8_t* __restrict__ xq_out,
+    uint16_t* __restrict__ xs_out) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= n) return;
   const float* xr = x + (size_t)t * d;
+  const int KS = d_pad / (QB * KSTEP);
+  int prow[MAX_TOPK + 1];
+#pragma unroll
+  for (int s = 0; s < MAX_TOPK + 1; ++s) {
+    const int v = s < kk ? pos[(size_t)t * kk + s] : -1;
+    prow[s] = (v >= 0 && v < pad_rows) ? v : -1;
+  }
   float gacc = 0.0f;
-  for (int j0 = 0; j0 < d_pad; j0 += 256) {
-    const int j = j0 + threadIdx.x;
-    const float v = (j < d) ? xr[j] : 0.0f;
-    int8_t q;
-    uint16_t s16;
-    quant_block32(v, q, s16);  // every lane takes part in the block's shuffles
-    if (j < d_pad) {
-      xq[(size_t)t * d_pad + j] = q;
-      if ((threadIdx.x & 31) == 0) xs[(size_t)t * (d_pad / QB) + (j >> 5)] = s16;
+  for (int j0 = 0; j0 < KS; j0 += 8) {
+    const int j = j0 + (lane >> 3), p = lane & 7;  // k-step, piece
+    const int kb = KSTEP * j + (p >> 1), half = p & 1;
+    const int c0 = kb * QB + half * 16;  // first column of the piece
+    float v[16];
+    if (c0 < d) {  // d % 32 == 0: a piece is all valid or all padding
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 q = *reinterpret_cast<const float4*>(xr + c0 + 4 * i);
+        v[4 * i] = q.x;
+        v[4 * i + 1] = q.y;
+        v[4 * i + 2] = q.z;
+        v[4 * i + 3] = q.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = 0.0f;
     }
-    if (shg && j < d) gacc = __builtin_fmaf(v, shg[j], gacc);
+    uint32_t pk[4];
+    uint16_t s16;
+    quant_half_block16(v, pk, s16);  // lanes 2i, 2i+1 share a block; all take part
+    if (j < KS) {
+      const uint4 codes = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+#pragma unroll
+      for (int s = 0; s < MAX_TOPK + 1; ++s) {
+        const int row = prow[s];
+        if (s < kk && row >= 0) {
+          const int t32 = row >> 5, r = row & 31;
+          const size_t slab = (size_t)t32 * KS + j;
+          *reinterpret_cast<uint4*>(gq + (slab * 32 + r) * 128 + ((p ^ (r & 7)) << 4)) = codes;
+          if (half == 0) gqs[(slab * 32 + r) * KSTEP + (p >> 1)] = s16;
+        }
+      }
+      if (xq_out && c0 < d) *reinterpret_cast<uint4*>(xq_out + (size_t)t * d + c0) = codes;
+      if (xs_out && half == 0 && c0 < d) xs_out[(size_t)t * (d / QB) + kb] = s16;
+    }
+    if (shg && c0 < d) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) gacc = __builtin_fmaf(v[i], shg[c0 + i], gacc);
+    }
   }
   if (shg) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) gacc += __shfl_xor(gacc, off, 64);
-    if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = gacc;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const float a = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
-      gs[t] = 1.0f / (1.0f + expf(-a));
-    }
+    if (lane == 0) gs[t] = 1.0f / (1.0f + expf(-gacc));
   }
 }
 
@@ -304,12 +342,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
 
 }  // namespace
 
-hipError_t launch_router(const float* x, int n, int d, int d_pad, const float* wt, const float* bias,
-                         int E, int E64, float* logits, const float* sh_gate_vec, float* gs,
-                         int8_t* xq, uint16_t* xs, hipStream_t s) {
-  quantize_rows_kernel<<<n, 256, 0, s>>>(x, d, d_pad, sh_gate_vec, gs, xq, xs);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+hipError_t launch_router(const float* x, int n, int d, const float* wt, const float* bias, int E,
+                         int E64, float* logits, hipStream_t s) {
   const int eg = E64 / 64;
   // tokens per wavefront: as many as keep >= 1024 wavefronts in flight
   int rt = 4;
@@ -320,6 +354,15 @@ hipError_t launch_router(const float* x, int n, int d, int d_pad, const float* w
     case 2: router_kernel<2><<<grid, 256, 0, s>>>(x, n, d, wt, bias, E, E64, logits); break;
     default: router_kernel<1><<<grid, 256, 0, s>>>(x, n, d, wt, bias, E, E64, logits); break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_scatter(const float* x, int n, int d, int d_pad, const int32_t* pos,
+                                  int kk, int pad_rows, int8_t* gq, uint16_t* gqs,
+                                  const float* sh_gate_vec, float* gs, int8_t* xq_out,
+                                  uint16_t* xs_out, hipStream_t s) {
+  quantize_scatter_kernel<<<(n + 3) / 4, 256, 0, s>>>(x, n, d, d_pad, pos, kk, pad_rows, gq, gqs,
+                                                      sh_gate_vec, gs, xq_out, xs_out);
   return hipGetLastError();
 }
 
