@@ -410,21 +410,26 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
         make_uint4(packed[4], packed[5], packed[6], packed[7]);
     a.hs[(((size_t)t32 * (a.kbmax / KSTEP) + (kbf >> 2)) * 32 + r) * KSTEP + (kbf & 3)] = s16;
   } else {
-    const int p_lane = min(wrow0 + (lane & 31), row_end - 1);
-    const int tok_l = a.tok_i[p_lane];
-    const int slot_l = a.tok_k[p_lane];
+    // Destination row of each of the lane's 16 output rows: lane r looks up
+    // CSR row wrow0 + r once; all 16 exchanges are issued before any store.
+    const int p_lane = wrow0 + (lane & 31);
+    int ri = -1;
+    if (p_lane < row_end) {
+      const int tok = a.tok_i[p_lane], slt = a.tok_k[p_lane];
+      if ((unsigned)tok < (unsigned)a.n_tokens && (unsigned)slt < (unsigned)a.kk) ri = tok * a.kk + slt;
+    }
+    int rows[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) rows[v] = __shfl(ri, out_row(v, lane), 64);
+    const bool full = (cs + 1) * DN_COLS <= a.d;  // the strip has no padding columns
+    const int col0 = cs * DN_COLS + (lane & 31);
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int m = out_row(v, lane);
-      const int tok = __shfl(tok_l, m, 64);
-      const int slt = __shfl(slot_l, m, 64);
-      if (wrow0 + m < row_end && (unsigned)tok < (unsigned)a.n_tokens && (unsigned)slt < (unsigned)a.kk) {
-        float* dst = a.partial + ((size_t)tok * a.kk + slt) * a.d;
+      if (rows[v] >= 0) {
+        float* dst = a.partial + (size_t)rows[v] * a.d + col0;
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          const int col = cs * DN_COLS + tt * 32 + (lane & 31);
-          if (col < a.d) dst[col] = acc[tt][v];
-        }
+        for (int tt = 0; tt < 4; ++tt)
+          if (full || col0 + tt * 32 < a.d) dst[tt * 32] = acc[tt][v];
       }
     }
   }
