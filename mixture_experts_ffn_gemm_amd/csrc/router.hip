@@ -14,130 +14,163 @@
 namespace moe {
 namespace {
 
-constexpr int RL_JC = 64;  // router: j values per LDS chunk (two 32-blocks)
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr int RJC = 64;          // router: j values per LDS chunk
+constexpr int RJQ = RJC / 4;     // 4-j quads per chunk
+constexpr int RNB = 4;           // chunk buffers in the LDS ring
+constexpr int RPF = RNB - 1;     // chunks copied ahead
+constexpr int RDMA = 6;          // copies per wavefront per chunk
+constexpr int RT = 2;            // tokens per wavefront
+constexpr int R_WB = RJQ * 64 * 16;       // transposed router slab per chunk (16 KiB)
+constexpr int R_XB = 4 * RT * RJC * 4;    // the workgroup's token rows per chunk (2 KiB)
+constexpr int R_BUF = R_WB + R_XB;
+
+// global -> LDS copies: lane l writes LDS address m0 + size * l
+__device__ __forceinline__ void rdma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void rdma4(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void rwait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 16 steps of two fp32 fused multiply-add chains: for i = 0..15,
+//   acc0 = fma(xa[i], w[i], acc0); acc1 = fma(xb[i], w[i], acc1),
+// where xa/xb[i] is lane i of each 16-lane row of xa/xb, broadcast to the
+// row by DPP row_newbcast (every row holds the same 16 values), and w[i] is
+// this lane's weight (quads w0..w3).  v_fmac_f32 is fused (one rounding), as
+// the chain's definition requires; the leading s_nop covers the wait states
+// a DPP read needs after a VALU write of its source.
+#define RFMA2(I, W)                                                                          \
+  "v_fmac_f32_dpp %0, %2, " W " row_newbcast:" #I " row_mask:0xf bank_mask:0xf\n\t"         \
+  "v_fmac_f32_dpp %1, %3, " W " row_newbcast:" #I " row_mask:0xf bank_mask:0xf\n\t"
+__device__ __forceinline__ void router_fma16(float& acc0, float& acc1, float xa, float xb,
+                                             const f4v& w0, const f4v& w1, const f4v& w2,
+                                             const f4v& w3) {
+  asm volatile("s_nop 1\n\t"
+      RFMA2(0, "%4") RFMA2(1, "%5") RFMA2(2, "%6") RFMA2(3, "%7")
+      RFMA2(4, "%8") RFMA2(5, "%9") RFMA2(6, "%10") RFMA2(7, "%11")
+      RFMA2(8, "%12") RFMA2(9, "%13") RFMA2(10, "%14") RFMA2(11, "%15")
+      RFMA2(12, "%16") RFMA2(13, "%17") RFMA2(14, "%18") RFMA2(15, "%19")
+      : "+v"(acc0), "+v"(acc1)
+      : "v"(xa), "v"(xb), "v"(w0.x), "v"(w0.y), "v"(w0.z), "v"(w0.w), "v"(w1.x), "v"(w1.y),
+        "v"(w1.z), "v"(w1.w), "v"(w2.x), "v"(w2.y), "v"(w2.z), "v"(w2.w), "v"(w3.x), "v"(w3.y),
+        "v"(w3.z), "v"(w3.w));
+}
+#undef RFMA2
 
 // Router logits for 4*RT tokens x 64 experts per workgroup (lane = expert, RT
 // tokens per wavefront).  Each logit is one fp32 fused multiply-add chain over
 // ascending j, from +0, then + bias (a separate fp32 add); the chain order is
-// the contract that makes top-k ids reproducible bit for bit.  Per chunk of 64
-// j the workgroup stages the transposed router slab (64 experts x 64 j) and the
-// 4*RT token rows in LDS.  With one workgroup per CU the chunk loads are
-// latency-bound, so they run PF chunks ahead through a ring of registers
-// (the chunk loop is unrolled by PF so every ring slot is a fixed register).
-// Zero padding past d leaves every chain unchanged (fma(0, 0, acc) = acc for
-// acc != -0, and a chain from +0 never reaches -0).
-typedef float f4v __attribute__((ext_vector_type(4)));
-
-template <int RT>
-struct RouterChunk {
-  f4v w[4];  // W rows jq = tid/64 + 4i of the chunk, expert = lane
-  float x[RT];  // x[token tid/64 + 4r][chunk column lane]
-};
-
-struct RouterCtx {
-  const f4v* wsrc;
-  const float* xbase;
-  int n, d, d4, E64, t0, tid, lane, wave;
-};
-
-template <int RT>
-__device__ __forceinline__ void router_fetch(RouterChunk<RT>& c, const RouterCtx& k, int ch) {
-  const f4v z4 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int jq = ch * (RL_JC / 4) + (k.tid >> 6) + 4 * i;
-    c.w[i] = (jq < k.d4) ? k.wsrc[(size_t)jq * k.E64 + k.lane] : z4;
-  }
-  const int j = ch * RL_JC + k.lane;
-#pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    const int t = min(k.t0 + (k.tid >> 6) + 4 * r, k.n - 1);
-    c.x[r] = (j < k.d) ? k.xbase[(size_t)t * k.d + j] : 0.0f;
-  }
-}
-
-// One chunk: stash the fetched slot into LDS buffer ch&1, refill the slot with
-// chunk ch + PF, run the fused chains.
-template <int RT, int PF>
-__device__ __forceinline__ void router_step(RouterChunk<RT>& slot, const RouterCtx& k, int ch, int nchunks,
-                                            f4v (&wl)[2][RL_JC / 4][64], f4v (&xl)[2][4 * RT][RL_JC / 4],
-                                            float (&acc)[RT]) {
-  constexpr int JQ = RL_JC / 4;
-  const int buf = ch & 1;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) wl[buf][(k.tid >> 6) + 4 * i][k.lane] = slot.w[i];
-#pragma unroll
-  for (int r = 0; r < RT; ++r)
-    reinterpret_cast<float*>(&xl[buf][(k.tid >> 6) + 4 * r][0])[k.lane] = slot.x[r];
-  lds_barrier();
-  if (ch + PF < nchunks) router_fetch<RT>(slot, k, ch + PF);
-  // LDS operands in batches of 4 f4v rows, then the fused chains
-#pragma unroll
-  for (int jb = 0; jb < JQ; jb += 4) {
-    f4v wv[4], xv[RT][4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) wv[q] = wl[buf][jb + q][k.lane];
-#pragma unroll
-    for (int r = 0; r < RT; ++r)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) xv[r][q] = xl[buf][k.wave * RT + r][jb + q];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        acc[r] = __builtin_fmaf(xv[r][q].x, wv[q].x, acc[r]);
-        acc[r] = __builtin_fmaf(xv[r][q].y, wv[q].y, acc[r]);
-        acc[r] = __builtin_fmaf(xv[r][q].z, wv[q].z, acc[r]);
-        acc[r] = __builtin_fmaf(xv[r][q].w, wv[q].w, acc[r]);
-      }
-  }
-}
-
-template <int RT>
+// the contract that makes top-k ids reproducible bit for bit.
+//
+// The chains are latency- and operand-bound (two per lane across the whole
+// chip at OLMoE sizes), so every operand takes the cheapest path.  Per chunk of
+// 64 j the transposed router slab (64 experts x 64 j, 16 KiB) and the
+// workgroup's 8 token rows (2 KiB) are copied into a ring of LDS buffers RPF
+// chunks ahead.  Per 16 j a lane reads its expert's 16 weights (4 x 16 B) and
+// one value of each of its wavefront's two token rows (lane i of every
+// 16-lane row reads column i), and the token value of each step reaches all
+// lanes through a DPP row broadcast inside the FMA: 6 LDS reads per 32 FMAs.
+// The reads of the next 16 j are issued before the current 16 j are
+// computed.  Only the d/16 sub-chunks inside d are visited (d % 32 == 0), so
+// no padding term enters a chain.
 __global__ __launch_bounds__(256, 1) void router_kernel(
     const float* __restrict__ x, int n, int d, const float* __restrict__ wt,
     const float* __restrict__ bias, int E, int E64, float* __restrict__ logits) {
-  constexpr int TPW = 4 * RT;       // tokens per workgroup
-  constexpr int JQ = RL_JC / 4;     // f4v rows per chunk
-  constexpr int PF = 4;             // chunks in flight (one named register slot each)
-  __shared__ f4v wl[2][JQ][64];
-  __shared__ f4v xl[2][TPW][JQ];
-  RouterCtx k;
-  k.tid = threadIdx.x;
-  k.lane = k.tid & 63;
-  k.wave = __builtin_amdgcn_readfirstlane(k.tid >> 6);
+  __shared__ __attribute__((aligned(1024))) char ring[RNB * R_BUF];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int eg = blockIdx.y;
-  k.t0 = blockIdx.x * TPW;
-  k.n = n;
-  k.d = d;
-  k.d4 = d >> 2;
-  k.E64 = E64;
-  k.wsrc = reinterpret_cast<const f4v*>(wt) + eg * 64;
-  k.xbase = x;
-  const int e = eg * 64 + k.lane;
+  const int tw = blockIdx.x * 4 * RT + wave * RT;  // this wavefront's first token
+  const int C = (d + RJC - 1) / RJC, NQ = d / 4;
+  const uint32_t lbase = (uint32_t)(uintptr_t)(lds_char*)ring;
+  const float* xr0 = x + (size_t)min(tw, n - 1) * d;
+  const float* xr1 = x + (size_t)min(tw + 1, n - 1) * d;
 
-  float acc[RT];
+  // Wavefront w copies quads 4w..4w+3 of the slab (1 KiB each: the 64
+  // experts' 4 j; quads past d re-read the last one) and its own two token
+  // rows (columns past d re-read column d-1).
+  auto issue = [&](int c) {
+    const uint32_t buf = lbase + (uint32_t)((c % RNB) * R_BUF);
 #pragma unroll
-  for (int r = 0; r < RT; ++r) acc[r] = 0.0f;
-  const int nchunks = (d + RL_JC - 1) / RL_JC;
-  RouterChunk<RT> s0, s1, s2, s3;
-  router_fetch<RT>(s0, k, 0);
-  if (1 < nchunks) router_fetch<RT>(s1, k, 1);
-  if (2 < nchunks) router_fetch<RT>(s2, k, 2);
-  if (3 < nchunks) router_fetch<RT>(s3, k, 3);
-  for (int ch0 = 0; ch0 < nchunks; ch0 += PF) {
-    router_step<RT, PF>(s0, k, ch0, nchunks, wl, xl, acc);
-    if (ch0 + 1 < nchunks) router_step<RT, PF>(s1, k, ch0 + 1, nchunks, wl, xl, acc);
-    if (ch0 + 2 < nchunks) router_step<RT, PF>(s2, k, ch0 + 2, nchunks, wl, xl, acc);
-    if (ch0 + 3 < nchunks) router_step<RT, PF>(s3, k, ch0 + 3, nchunks, wl, xl, acc);
-  }
-  if (e < E) {
-    const float b = bias ? bias[e] : 0.0f;
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      const int t = k.t0 + k.wave * RT + r;
-      if (t < n) logits[(size_t)t * E + e] = bias ? acc[r] + b : acc[r];
+    for (int i = 0; i < 4; ++i) {
+      const int jq = min(c * RJQ + 4 * wave + i, NQ - 1);
+      rdma16(wt + ((size_t)jq * E64 + eg * 64) * 4, lane * 16, buf + (4 * wave + i) * 1024);
     }
+    const uint32_t xo = (uint32_t)min(c * RJC + lane, d - 1) * 4;
+    rdma4(xr0, xo, buf + R_WB + (RT * wave) * (RJC * 4));
+    rdma4(xr1, xo, buf + R_WB + (RT * wave + 1) * (RJC * 4));
+  };
+  const int np = min(RPF, C);
+  for (int c = 0; c < np; ++c) issue(c);
+
+  auto wait_chunk = [&](int c) {  // chunk c copied for every wavefront
+    const int newer = min(RPF - 1, C - 1 - c);
+    if (newer >= 2)
+      rwait_vm<2 * RDMA>();
+    else if (newer == 1)
+      rwait_vm<RDMA>();
+    else
+      rwait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // operands of one 16-j sub-chunk
+  f4v w[2][4];
+  float xa[2], xb[2];
+  auto load_sub = [&](int sub, int b) {
+    const int c = sub >> 2, q0 = (sub & 3) * 4;
+    const char* buf = ring + (c % RNB) * R_BUF;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[b][q] = *reinterpret_cast<const f4v*>(buf + (q0 + q) * 1024 + lane * 16);
+    const float* xrow = reinterpret_cast<const float*>(buf + R_WB) + (RT * wave) * RJC + q0 * 4 + (lane & 15);
+    xa[b] = xrow[0];
+    xb[b] = xrow[RJC];
+  };
+  float acc0 = 0.0f, acc1 = 0.0f;
+  // One full chunk (4 sub-chunks of 16 j) per iteration, then the trailing
+  // half chunk when d % 64 == 32.  The reads of sub-chunk s+1 are issued
+  // before sub-chunk s is computed, unconditionally (after the last sub-chunk
+  // they read stale LDS and are discarded).  Before the first sub-chunk of
+  // chunk c+1 is read, chunk c+1 is waited for and published; every wavefront
+  // has then read all of chunk c-1, whose buffer takes chunk c+RPF.
+  const int CF = d / RJC;
+  wait_chunk(0);
+  load_sub(0, 0);
+  for (int c = 0; c < CF; ++c) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int b = q & 1;
+      if (q == 3 && c + 1 < C) {
+        wait_chunk(c + 1);
+        if (c + RPF < C) issue(c + RPF);
+      }
+      load_sub(4 * c + q + 1, b ^ 1);
+      router_fma16(acc0, acc1, xa[b], xb[b], w[b][0], w[b][1], w[b][2], w[b][3]);
+    }
+  }
+  if (CF < C) {  // 32 trailing j: sub-chunks 4 CF (already requested) and 4 CF + 1
+    load_sub(4 * CF + 1, 1);
+    router_fma16(acc0, acc1, xa[0], xb[0], w[0][0], w[0][1], w[0][2], w[0][3]);
+    router_fma16(acc0, acc1, xa[1], xb[1], w[1][0], w[1][1], w[1][2], w[1][3]);
+  }
+  const int e = eg * 64 + lane;
+  if (e < E) {
+    const float bb = bias ? bias[e] : 0.0f;
+    if (tw < n) logits[(size_t)tw * E + e] = bias ? acc0 + bb : acc0;
+    if (tw + 1 < n) logits[(size_t)(tw + 1) * E + e] = bias ? acc1 + bb : acc1;
   }
 }
 
@@ -344,16 +377,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
 
 hipError_t launch_router(const float* x, int n, int d, const float* wt, const float* bias, int E,
                          int E64, float* logits, hipStream_t s) {
-  const int eg = E64 / 64;
-  // tokens per wavefront: as many as keep >= 1024 wavefronts in flight
-  int rt = 4;
-  while (rt > 1 && (long)((n + rt - 1) / rt) * eg < 1024) rt >>= 1;
-  dim3 grid((unsigned)((n + 4 * rt - 1) / (4 * rt)), (unsigned)eg);
-  switch (rt) {
-    case 4: router_kernel<4><<<grid, 256, 0, s>>>(x, n, d, wt, bias, E, E64, logits); break;
-    case 2: router_kernel<2><<<grid, 256, 0, s>>>(x, n, d, wt, bias, E, E64, logits); break;
-    default: router_kernel<1><<<grid, 256, 0, s>>>(x, n, d, wt, bias, E, E64, logits); break;
-  }
+  dim3 grid((unsigned)((n + 4 * RT - 1) / (4 * RT)), (unsigned)(E64 / 64));
+  router_kernel<<<grid, 256, 0, s>>>(x, n, d, wt, bias, E, E64, logits);
   return hipGetLastError();
 }
 
