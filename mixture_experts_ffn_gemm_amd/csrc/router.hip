@@ -116,8 +116,9 @@ __global__ __launch_bounds__(256, 1) void router_kernel(
   const int np = min(RPF, C);
   for (int c = 0; c < np; ++c) issue(c);
 
-  auto wait_chunk = [&](int c) {  // chunk c copied for every wavefront
-    const int newer = min(RPF - 1, C - 1 - c);
+  // Wait until chunk c is copied for every wavefront, given how many chunks
+  // this wavefront has issued after it (vector loads complete in order).
+  auto wait_chunk = [&](int newer) {
     if (newer >= 2)
       rwait_vm<2 * RDMA>();
     else if (newer == 1)
@@ -147,14 +148,16 @@ __global__ __launch_bounds__(256, 1) void router_kernel(
   // chunk c+1 is read, chunk c+1 is waited for and published; every wavefront
   // has then read all of chunk c-1, whose buffer takes chunk c+RPF.
   const int CF = d / RJC;
-  wait_chunk(0);
+  static_assert(RPF == 3, "the in-loop wait below assumes chunks c+1 and c+2 in flight");
+  wait_chunk(np - 1);  // chunks 1..np-1 were issued after chunk 0
   load_sub(0, 0);
   for (int c = 0; c < CF; ++c) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int b = q & 1;
       if (q == 3 && c + 1 < C) {
-        wait_chunk(c + 1);
+        // issued so far: chunks 0 .. min(c+2, C-1); newer than c+1: c+2 if it exists
+        wait_chunk(c + 2 < C ? 1 : 0);
         if (c + RPF < C) issue(c + RPF);
       }
       load_sub(4 * c + q + 1, b ^ 1);
@@ -202,23 +205,31 @@ __global__ __launch_bounds__(256) void quantize_scatter_kernel(
     prow[s] = (v >= 0 && v < pad_rows) ? v : -1;
   }
   float gacc = 0.0f;
+  // Each pass covers 8 k-steps; the next pass's row values are loaded before
+  // this pass is quantised and scattered (padding columns load column 0 and
+  // are zeroed).
+  auto load = [&](int j0, f4v (&v)[4]) {
+    const int j = j0 + (lane >> 3), p = lane & 7;
+    const int c0 = (KSTEP * j + (p >> 1)) * QB + (p & 1) * 16;
+    const float* src = xr + (c0 < d ? c0 : 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const f4v*>(src + 4 * i);
+  };
+  f4v cur[4], nxt[4];
+  load(0, cur);
   for (int j0 = 0; j0 < KS; j0 += 8) {
+    if (j0 + 8 < KS) load(j0 + 8, nxt);
     const int j = j0 + (lane >> 3), p = lane & 7;  // k-step, piece
     const int kb = KSTEP * j + (p >> 1), half = p & 1;
     const int c0 = kb * QB + half * 16;  // first column of the piece
+    const bool valid = c0 < d;           // d % 32 == 0: a piece is all valid or all padding
     float v[16];
-    if (c0 < d) {  // d % 32 == 0: a piece is all valid or all padding
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 q = *reinterpret_cast<const float4*>(xr + c0 + 4 * i);
-        v[4 * i] = q.x;
-        v[4 * i + 1] = q.y;
-        v[4 * i + 2] = q.z;
-        v[4 * i + 3] = q.w;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+    for (int i = 0; i < 4; ++i) {
+      v[4 * i] = valid ? cur[i].x : 0.0f;
+      v[4 * i + 1] = valid ? cur[i].y : 0.0f;
+      v[4 * i + 2] = valid ? cur[i].z : 0.0f;
+      v[4 * i + 3] = valid ? cur[i].w : 0.0f;
     }
     uint32_t pk[4];
     uint16_t s16;
@@ -235,13 +246,15 @@ __global__ __launch_bounds__(256) void quantize_scatter_kernel(
           if (half == 0) gqs[(slab * 32 + r) * KSTEP + (p >> 1)] = s16;
         }
       }
-      if (xq_out && c0 < d) *reinterpret_cast<uint4*>(xq_out + (size_t)t * d + c0) = codes;
-      if (xs_out && half == 0 && c0 < d) xs_out[(size_t)t * (d / QB) + kb] = s16;
+      if (xq_out && valid) *reinterpret_cast<uint4*>(xq_out + (size_t)t * d + c0) = codes;
+      if (xs_out && half == 0 && valid) xs_out[(size_t)t * (d / QB) + kb] = s16;
     }
-    if (shg && c0 < d) {
+    if (shg && valid) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) gacc = __builtin_fmaf(v[i], shg[c0 + i], gacc);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
   }
   if (shg) {
 #pragma unroll
@@ -256,7 +269,7 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
-// One workgroup per 16 tokens.  The tile's logits are staged in LDS; each
+// One workgroup per ROUTE_TILE tokens, 16 threads per token.  The tile's logits are staged in LDS; each
 // (token, expert) finds its rank among the token's experts -- the number of
 // experts with a larger logit, or an equal logit and a lower id -- and the
 // experts of rank < k take slot = rank.  This is the top-k of the contract
@@ -264,7 +277,7 @@ __device__ inline float wave_sum(float v) {
 // Then softmax over all E, optional renormalisation, and the per-expert rank
 // of each (token, slot) pair among the tile's pairs in (token, slot) order,
 // with the tile's histogram, for the bucketing kernel.
-__global__ __launch_bounds__(256) void route_kernel(
+__global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(
     const float* __restrict__ logits, int n, int E, int k, int norm, int32_t* __restrict__ ids,
     float* __restrict__ wout, int32_t* __restrict__ rank, int32_t* __restrict__ hist) {
   __shared__ __attribute__((aligned(16))) float s_l[ROUTE_TILE][MAX_EXPERTS + 4];
@@ -274,16 +287,16 @@ __global__ __launch_bounds__(256) void route_kernel(
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * ROUTE_TILE;
   const int nt = min(ROUTE_TILE, n - t0);
-  for (int i = tid; i < ROUTE_TILE * E; i += 256) {
+  for (int i = tid; i < ROUTE_TILE * E; i += ROUTE_THREADS) {
     const int tl = i / E, e = i - tl * E;
     s_l[tl][e] = (tl < nt) ? logits[(size_t)(t0 + tl) * E + e] : 0.0f;
   }
   if (E & 3)  // pad each row to a multiple of 4 with -inf
-    for (int i = tid; i < ROUTE_TILE * 4; i += 256) {
+    for (int i = tid; i < ROUTE_TILE * 4; i += ROUTE_THREADS) {
       const int tl = i >> 2, e = E + (i & 3);
       if (e < ((E + 3) & ~3)) s_l[tl][e] = -__builtin_huge_valf();
     }
-  for (int e = tid; e < E; e += 256) s_cnt[e] = 0;
+  for (int e = tid; e < E; e += ROUTE_THREADS) s_cnt[e] = 0;
   __syncthreads();
 
   // ranks: thread (token tl = tid/16, expert group g = tid%16) owns experts g + 16c
@@ -355,7 +368,7 @@ __global__ __launch_bounds__(256) void route_kernel(
     if (last) s_cnt[e] = r + 1;
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 256) hist[(size_t)blockIdx.x * E + e] = s_cnt[e];
+  for (int e = tid; e < E; e += ROUTE_THREADS) hist[(size_t)blockIdx.x * E + e] = s_cnt[e];
 }
 
 __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ v, int64_t n_values,
@@ -394,7 +407,7 @@ hipError_t launch_quantize_scatter(const float* x, int n, int d, int d_pad, cons
 hipError_t launch_route(const float* logits, int n, int E, int k, int norm, int32_t* ids, float* w,
                         int32_t* rank, int32_t* hist, hipStream_t s) {
   const int tiles = (n + ROUTE_TILE - 1) / ROUTE_TILE;
-  route_kernel<<<tiles, 256, 0, s>>>(logits, n, E, k, norm, ids, w, rank, hist);
+  route_kernel<<<tiles, ROUTE_THREADS, 0, s>>>(logits, n, E, k, norm, ids, w, rank, hist);
   return hipGetLastError();
 }
 

@@ -228,6 +228,27 @@ def test_olmoe_layer_full_size():
 
 
 @pytest.mark.slow
+def test_repeated_calls_are_bitwise_identical():
+    """Four prefill calls on one OLMoE-shaped N=2048 batch give bitwise
+    identical routing weights, CSR and outputs.  Every stage is deterministic
+    by construction, so any difference is a synchronisation bug (a read of an
+    LDS buffer before its copy landed): the softmax weights of an affected
+    token change even where its top-k ids do not."""
+    lw = mw.workload_layer("olmoe_n2048")
+    x = mw.workload_tokens("olmoe_n2048")
+    first = run_gpu(lw, x, keep=True)
+    layer = first.pop("layer")
+    try:
+        for i in range(3):
+            g = run_gpu(lw, x, layer=layer)
+            for key in ("topk_ids", "topk_w", "exp_start", "exp_tok_i", "xq", "xs", "out"):
+                assert np.array_equal(g[key].view(np.uint8), first[key].view(np.uint8)), f"call {i + 2}: {key} differs"
+    finally:
+        layer.close()
+    say("olmoe_n2048: 4 calls bitwise identical")
+
+
+@pytest.mark.slow
 def test_a3b_layer_full_size():
     """35B-A3B-shaped layer: E=256, shared expert + gate, Zipf-skewed routing."""
     lw = mw.workload_layer("a3b_n512")
