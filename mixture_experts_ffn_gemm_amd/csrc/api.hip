@@ -186,6 +186,7 @@ int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, v
   a.dn = W->dn;
   a.dn_group = W->dn_per_expert;
   a.sh_dn = W->sh_dn;
+  a.dn_exp = W->dn_exp;
   a.partial = partial;
   a.d = dm.d;
   a.kk = kk;
@@ -244,11 +245,11 @@ int moe_ffn_weights_create(const moe_ffn_dims* dims, const float* router_w,
     return MOE_FFN_HIP_ERROR;
   }
   W->has_bias = router_bias ? 1 : 0;
-  // [strips][k-steps][17 KiB] per expert (see internal.h)
+  // [strips][k-steps][17 KiB (gate/up) or 18 KiB (down)] per expert (see internal.h)
   W->gu_per_expert = (size_t)(dm.F_pad / GU_COLS) * (dm.d_pad / QB / KSTEP) * KSTEP_BYTES;
-  W->dn_per_expert = (size_t)(dm.d_pad / DN_COLS) * (dm.F_pad / QB / KSTEP) * KSTEP_BYTES;
+  W->dn_per_expert = (size_t)(dm.d_pad / DN_COLS) * (dm.F_pad / QB / KSTEP) * DN_KSTEP_BYTES;
   const size_t sh_gu = (size_t)(dm.Fs_pad / GU_COLS) * (dm.d_pad / QB / KSTEP) * KSTEP_BYTES;
-  const size_t sh_dn = (size_t)(dm.d_pad / DN_COLS) * (dm.Fs_pad / QB / KSTEP) * KSTEP_BYTES;
+  const size_t sh_dn = (size_t)(dm.d_pad / DN_COLS) * (dm.Fs_pad / QB / KSTEP) * DN_KSTEP_BYTES;
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -259,6 +260,7 @@ int moe_ffn_weights_create(const moe_ffn_dims* dims, const float* router_w,
   const size_t o_rw = take((size_t)dm.d * dm.E64 * 4);
   const size_t o_rb = take((size_t)dm.E * 4);
   const size_t o_sg = take((size_t)dm.d * 4);
+  const size_t o_ex = take((size_t)dm.G * 4);
   const size_t o_gu = take(W->gu_per_expert * dm.E);
   const size_t o_dn = take(W->dn_per_expert * dm.E);
   const size_t o_sgu = take(sh_gu), o_sdn = take(sh_dn);
@@ -271,6 +273,7 @@ int moe_ffn_weights_create(const moe_ffn_dims* dims, const float* router_w,
   W->router_wt = (float*)(b + o_rw);
   W->router_bias = (float*)(b + o_rb);
   W->sh_gate_vec = (float*)(b + o_sg);
+  W->dn_exp = (int32_t*)(b + o_ex);
   W->gu = (uint8_t*)(b + o_gu);
   W->dn = (uint8_t*)(b + o_dn);
   W->sh_gu = has_sh ? (uint8_t*)(b + o_sgu) : nullptr;
@@ -288,20 +291,26 @@ int moe_ffn_weights_create(const moe_ffn_dims* dims, const float* router_w,
   if (e == hipSuccess)
     e = launch_repack_q8((const uint8_t*)gate_q8, (const uint8_t*)up_q8, dm.E,
                          (size_t)dm.F * nbd * Q8_BYTES, dm.F, nbd, 2, dm.F_pad / GU_COLS, dm.d_pad / QB,
-                         W->gu, W->gu_per_expert, stream);
+                         W->gu, W->gu_per_expert, nullptr, stream);
+  if (e == hipSuccess)
+    e = launch_scale_exponent((const uint8_t*)down_q8, dm.E, (size_t)dm.d * nbf * Q8_BYTES,
+                              (long)dm.d * nbf, W->dn_exp, stream);
   if (e == hipSuccess)
     e = launch_repack_q8((const uint8_t*)down_q8, (const uint8_t*)down_q8, dm.E,
                          (size_t)dm.d * nbf * Q8_BYTES, dm.d, nbf, 4, dm.d_pad / DN_COLS, dm.F_pad / QB,
-                         W->dn, W->dn_per_expert, stream);
+                         W->dn, W->dn_per_expert, W->dn_exp, stream);
   if (e == hipSuccess && has_sh) {
     const int nbs = dm.Fs / QB;
     e = launch_repack_q8((const uint8_t*)sh_gate_q8, (const uint8_t*)sh_up_q8, 1,
                          (size_t)dm.Fs * nbd * Q8_BYTES, dm.Fs, nbd, 2, dm.Fs_pad / GU_COLS,
-                         dm.d_pad / QB, W->sh_gu, sh_gu, stream);
+                         dm.d_pad / QB, W->sh_gu, sh_gu, nullptr, stream);
+    if (e == hipSuccess)
+      e = launch_scale_exponent((const uint8_t*)sh_down_q8, 1, (size_t)dm.d * nbs * Q8_BYTES,
+                                (long)dm.d * nbs, W->dn_exp + dm.E, stream);
     if (e == hipSuccess)
       e = launch_repack_q8((const uint8_t*)sh_down_q8, (const uint8_t*)sh_down_q8, 1,
                            (size_t)dm.d * nbs * Q8_BYTES, dm.d, nbs, 4, dm.d_pad / DN_COLS,
-                           dm.Fs_pad / QB, W->sh_dn, sh_dn, stream);
+                           dm.Fs_pad / QB, W->sh_dn, sh_dn, W->dn_exp + dm.E, stream);
   }
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   if (e != hipSuccess) {

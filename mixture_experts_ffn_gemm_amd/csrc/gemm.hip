@@ -18,17 +18,31 @@
 // the number of workgroups; surplus workgroups exit after reading the tile
 // count.
 //
-// Arithmetic per 32-block, per 32x32 output tile of a wavefront:
+// Arithmetic per 32-block, per 32x32 output tile of a wavefront, gate/up:
 //   v_mfma_i32_32x32x32_i8  -> exact int32 block sums C[m][n]
 //   v_mfma_f32_32x32x8_f16  -> S[m][n] = sa[m] * sw[n]: an outer product of the
 //                              two binary16 block scales, exact in fp32 (only
 //                              one of the 8 K slots is non-zero in A),
 // then the VALU does acc = fma(float(C), S, acc): two VALU operations per
-// output element per block, which bounds the kernel.  Everything else is
-// arranged so that it hides under that VALU stream:
+// output element per block, which bounds the kernel.  Gate/up keeps this exact
+// form because its output is requantised (a value moved across a rounding
+// boundary of the h quantiser changes a code).
+//
+// Down (its fp32 output is final): the int8 MFMA's accumulator input is the
+// bit pattern of 1.5f, so its int32 result, read as a float, is exactly
+// D = 1.5 + C * 2^-23 (|C| < 2^19 leaves the exponent field alone).  With the
+// weight scales stored as W = sw * 2^(23-e) the scale MFMA gives
+// S = sa * W = 2^(23-e) * sa * sw, and one VALU fma per element and block,
+// acc = fma(D, S, acc), adds 2^-e * C * sa * sw + 1.5 * S.  Once per k-step
+// a third MFMA takes the accumulator as its input and subtracts the 4 blocks'
+// 1.5 * S (A = -sa twice, B = {W, W/2} per block).  The epilogue multiplies
+// by 2^e.  The only rounding beyond the exact form is that of the corrected
+// accumulator, whose magnitude is that of the 1.5 * S terms: about 1e-4
+// relative to the output, well inside the output tolerance.
 //
 // * Memory: per k-step (4 blocks) a workgroup stages the strip's weight codes
-//   (16 chunks of 1 KiB: [block][tile]) and scales (1 KiB), and each
+//   (16 chunks of 1 KiB: [block][tile]) and scales (1 KiB; 2 KiB of pairs for
+//   down), and each
 //   wavefront its 32 activation rows (a 4 KiB slab [row][128 B], the 16-byte
 //   pieces of row r XOR-swizzled by r%8 so that the MFMA operand reads are
 //   free of LDS bank conflicts) and their scales (256 B), with direct
@@ -37,7 +51,7 @@
 //   already in slab form (a gather of 32 scattered rows per copy would hold
 //   one vector-L1 miss slot per row and stall the copies behind the L1's miss
 //   limit).  Every wavefront issues
-//   exactly DMA_PER_KSTEP copies per k-step, in two halves (weights right after
+//   exactly Lay::DMA copies per k-step, in two halves (weights right after
 //   the barrier, activations one block later) so that the copies of all
 //   wavefronts never queue at once.  The copies are inline assembly, so the
 //   compiler never inserts its own (conservative) waits for them, and they are
@@ -50,11 +64,15 @@
 //   block b+1 are requested before block b is computed, so LDS latency and
 //   bandwidth overlap the MFMA/VALU work instead of stalling after a barrier.
 // * Within a block the 4 tiles are software-pipelined one step deep with the
-//   issue order pinned: MFMA(t+1), convert(t), scale MFMA(t+1), accumulate(t),
-//   and the pipeline runs on across blocks and k-steps.
+//   issue order pinned (gate/up: MFMA(t+1), convert(t), scale MFMA(t+1),
+//   accumulate(t); down: MFMA(t+1), accumulate(t) half 1, scale MFMA(t+1),
+//   accumulate(t) half 2), and the
+//   pipeline runs on across blocks and k-steps.
 // Operand layouts (gfx950): A lane l = row l%32, bytes/halves k = 16*(l/32)+j
 // (i8) or 4*(l/32)+j (f16x8); B likewise by column; D lane l = column l%32,
 // register v = row 8*(v/4) + 4*(l/32) + v%4.
+#include <type_traits>
+
 #include "device_util.h"
 #include "internal.h"
 
@@ -69,14 +87,22 @@ typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int NWAVE = MT_WG / MT_WAVE;                   // 4 wavefronts x 32 rows
 constexpr int B_OFF = 0;                                 // weight codes [block][tile] x 1 KiB
-constexpr int BS_OFF = 16 * 1024;                        // weight scales [tile][32 rows][4 blocks]
-constexpr int A_OFF = KSTEP_BYTES;                       // activation chunks [wave][block] x 1 KiB
-constexpr int AS_OFF = A_OFF + NWAVE * KSTEP * 1024;     // activation scales [wave][32 rows][4 blocks]
-constexpr int STAGE = AS_OFF + NWAVE * 32 * KSTEP * 2;   // 34 KiB per k-step buffer
-constexpr int DMA_PER_KSTEP = 10;                        // copies per wavefront per k-step
+constexpr int BS_OFF = 16 * 1024;                        // weight scales (gate/up: [tile][32 rows][4
+                                                         // blocks]; down: [tile][half][32 rows][4])
 constexpr int EPI_STRIDE = 65;                           // gate/up epilogue scratch row (floats)
-static_assert(NWAVE * 32 * EPI_STRIDE * 4 <= STAGE, "epilogue scratch must fit in one buffer");
-static_assert(2 * 2 * STAGE <= 160 * 1024, "two workgroups per CU must fit in the LDS");
+
+// Stage layout of one k-step buffer: the weight k-step (17 or 18 KiB), then
+// the activation chunks [wave][block] x 1 KiB and their scales [wave][32 rows][4 blocks].
+template <bool GATEUP>
+struct Lay {
+  static constexpr int W_BYTES = GATEUP ? KSTEP_BYTES : DN_KSTEP_BYTES;
+  static constexpr int A_OFF = W_BYTES;
+  static constexpr int AS_OFF = A_OFF + NWAVE * KSTEP * 1024;
+  static constexpr int STAGE = AS_OFF + NWAVE * 32 * KSTEP * 2;  // 34 / 35 KiB
+  static constexpr int DMA = GATEUP ? 10 : 11;                   // copies per wavefront per k-step
+};
+static_assert(NWAVE * 32 * EPI_STRIDE * 4 <= Lay<true>::STAGE, "epilogue scratch must fit in one buffer");
+static_assert(2 * 2 * Lay<false>::STAGE <= 160 * 1024, "two workgroups per CU must fit in the LDS");
 
 __device__ inline int out_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
 
@@ -84,6 +110,7 @@ __device__ inline v4h as_v4h(uint32_t lo, uint32_t hi) {
   const uint2 u = make_uint2(lo, hi);
   return __builtin_bit_cast(v4h, u);
 }
+__device__ inline v4h as_v4h(uint2 u) { return __builtin_bit_cast(v4h, u); }
 
 // global -> LDS copies: lane l moves `size` bytes from base + voff (base is
 // wavefront-uniform, voff this lane's 32-bit offset) to LDS address
@@ -108,9 +135,9 @@ __device__ __forceinline__ void wait_copies_barrier_0() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
-__device__ __forceinline__ void wait_copies_barrier_1kstep() {
-  static_assert(DMA_PER_KSTEP == 10, "the vmcnt immediate below is DMA_PER_KSTEP");
-  asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+template <int N>
+__device__ __forceinline__ void wait_copies_barrier_n() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -124,7 +151,7 @@ struct Src {
   const int8_t* a;     // this wavefront's activation chunks (gq or hq)
   const uint16_t* as;  // their scales (gqs or hs)
   uint32_t o_w;        // 16 * lane: code chunk piece
-  uint32_t o_ws;       // 16 KiB + 256 * wave + 4 * lane: a quarter of the weight scales
+  uint32_t o_ws;       // 16 KiB + 4 * lane + this wavefront's share of the weight scales
 };
 
 // This wavefront's copies of k-step j into the buffer at LDS address L, in
@@ -132,20 +159,28 @@ struct Src {
 // all wavefronts never queue at once: the weight half (code chunks wave + 4i
 // and a quarter of the weight scales) and the activation half (its 4
 // activation chunks and its 32 rows' activation scales).
+template <bool GATEUP>
 __device__ __forceinline__ void issue_weights(const Src& s, int j, uint32_t L, int wave) {
-  const uint8_t* w = s.w + (size_t)j * KSTEP_BYTES;
+  const uint8_t* w = s.w + (size_t)j * Lay<GATEUP>::W_BYTES;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = wave + 4 * i;
     dma16(w + c * 1024, s.o_w, L + B_OFF + c * 1024);
   }
-  dma4(w, s.o_ws, L + BS_OFF + wave * 256);
+  if (GATEUP) {
+    dma4(w, s.o_ws, L + BS_OFF + wave * 256);
+  } else {
+    dma4(w, s.o_ws, L + BS_OFF + wave * 512);
+    dma4(w, s.o_ws + 256, L + BS_OFF + wave * 512 + 256);
+  }
 }
+template <bool GATEUP>
 __device__ __forceinline__ void issue_acts(const Src& s, int j, uint32_t L, int wave, int lane) {
   const int8_t* a = s.a + (size_t)j * KSTEP * 1024;
 #pragma unroll
-  for (int i = 0; i < KSTEP; ++i) dma16(a + i * 1024, lane * 16, L + A_OFF + (wave * KSTEP + i) * 1024);
-  dma4(s.as + (size_t)j * 32 * KSTEP, lane * 4, L + AS_OFF + wave * 256);
+  for (int i = 0; i < KSTEP; ++i)
+    dma16(a + i * 1024, lane * 16, L + Lay<GATEUP>::A_OFF + (wave * KSTEP + i) * 1024);
+  dma4(s.as + (size_t)j * 32 * KSTEP, lane * 4, L + Lay<GATEUP>::AS_OFF + wave * 256);
 }
 
 // Register operands of one block: this wavefront's A chunk and the 4 B chunks.
@@ -154,31 +189,33 @@ struct Ops {
   v4i b[4];
 };
 
+template <bool GATEUP>
 __device__ __forceinline__ void read_block(const char* buf, int b, int wave, int lane, Ops& o) {
   // A: row lane%32, piece 2b + lane/32 of the k-step, stored at its row's
   // 128-byte line position (piece ^ row%8)
   const int r = lane & 31, p = 2 * b + (lane >> 5);
-  o.a = *reinterpret_cast<const v4i*>(buf + A_OFF + wave * (KSTEP * 1024) + r * 128 + ((p ^ (r & 7)) << 4));
+  o.a = *reinterpret_cast<const v4i*>(buf + Lay<GATEUP>::A_OFF + wave * (KSTEP * 1024) + r * 128 +
+                                      ((p ^ (r & 7)) << 4));
 #pragma unroll
   for (int t = 0; t < 4; ++t)
     o.b[t] = *reinterpret_cast<const v4i*>(buf + B_OFF + (b * 4 + t) * 1024 + lane * 16);
 }
 
-// The k-step's scales: weight scales of the 4 tiles (column lane%32, blocks
+// Gate/up: the k-step's weight scales of the 4 tiles (column lane%32, blocks
 // 0-3: the B operands of the scale MFMA) and the activation scales of this
 // lane's row (lanes 32-63 supply the zero K slots 4-7).
-struct Scales {
+struct GuScales {
   v4h sw[4];
   uint2 sa;
 };
 
-__device__ __forceinline__ void read_scales(const char* buf, int wave, int lane, Scales& s) {
+__device__ __forceinline__ void read_scales(const char* buf, int wave, int lane, GuScales& s) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const uint2 p = *reinterpret_cast<const uint2*>(buf + BS_OFF + (t * 32 + (lane & 31)) * 8);
     s.sw[t] = as_v4h(p.x, p.y);
   }
-  const uint2 p = *reinterpret_cast<const uint2*>(buf + AS_OFF + wave * 256 + (lane & 31) * 8);
+  const uint2 p = *reinterpret_cast<const uint2*>(buf + Lay<true>::AS_OFF + wave * 256 + (lane & 31) * 8);
   const uint32_t m = lane < 32 ? 0xffffffffu : 0u;
   s.sa = make_uint2(p.x & m, p.y & m);
 }
@@ -187,6 +224,36 @@ __device__ __forceinline__ void read_scales(const char* buf, int wave, int lane,
 __device__ __forceinline__ v4h sa_slot(const uint2 sa, int b) {
   const uint32_t m = (b & 1) ? 0xffff0000u : 0x0000ffffu;
   return b < 2 ? as_v4h(sa.x & m, 0u) : as_v4h(0u, sa.y & m);
+}
+
+// Down: per tile the B operand shared by the scale and correction MFMAs (lane
+// l: column l%32, K slots 4(l/32)..4(l/32)+3 = {W, W/2} of blocks 2(l/32) and
+// 2(l/32)+1), and this lane's pair of activation scales q (row l%32, the same
+// two blocks).
+struct DnScales {
+  uint2 wb[4];
+  uint32_t q;
+};
+
+__device__ __forceinline__ void read_scales(const char* buf, int wave, int lane, DnScales& s) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) s.wb[t] = *reinterpret_cast<const uint2*>(buf + BS_OFF + t * 512 + lane * 8);
+  const uint2 p = *reinterpret_cast<const uint2*>(buf + Lay<false>::AS_OFF + wave * 256 + (lane & 31) * 8);
+  s.q = lane < 32 ? p.x : p.y;
+}
+
+// A operand of the down scale MFMA for block b: K slot 2b (the slot whose B
+// entry is W of block b) holds this row's activation scale.
+__device__ __forceinline__ v4h dn_sa_slot(uint32_t q, int b, int lane) {
+  const uint32_t v = ((lane >> 5) == (b >> 1)) ? q : 0u;
+  return (b & 1) ? as_v4h(0u, v >> 16) : as_v4h(v & 0xffffu, 0u);
+}
+
+// A operand of the correction MFMA: -sa in both slots of each block, so that
+// A.B = -(sa W + sa W/2) = -1.5 S summed over the k-step's 4 blocks.
+__device__ __forceinline__ v4h dn_corr_a(uint32_t q) {
+  const uint32_t lo = q & 0xffffu, hi = q >> 16;
+  return as_v4h((lo | (lo << 16)) ^ 0x80008000u, (hi | (hi << 16)) ^ 0x80008000u);
 }
 
 // Empty asm statements that take values "in and out" without emitting an
@@ -203,67 +270,131 @@ __device__ __forceinline__ void anchor(T& v, U& u) {
   asm volatile("" : "+v"(v), "+v"(u));
 }
 
-// One block (4 tiles) of the pipeline.  On entry c and s hold the in-flight
-// MFMAs of tile 0 of this block; on exit they hold those of tile 0 of the
-// next block (operands `on`, scales `sn`, block bn).  Per tile t the order is
-// MFMA(t+1), convert(t), scale MFMA(t+1), accumulate(t).
-__device__ __forceinline__ void compute_block(const Ops& o, const Scales& sc, int b, const Ops& on,
-                                              const Scales& sn, int bn, v16i& c, v16f& s,
-                                              v16f (&acc)[4]) {
-  const v16i zi = {0};
+// Per-wavefront constants of the pipelines: the accumulator input of every
+// int8 MFMA (gate/up: the bits of 1.5 * 2^23; down: the bits of 1.5f), the
+// constant A and B operands of the gate/up conversion MFMA (one non-zero K
+// slot: -3072 * 4096 = -1.5 * 2^23) and, for down, the k-step's correction A
+// operand.
+struct Ctx {
+  v16i magic;
+  v4h sub_a, sub_b;
+  v4h corr;
+};
+
+// One block (4 tiles) of the gate/up pipeline, which runs two tiles ahead.
+// On entry dn holds the int8 MFMA of tile 1 of this block (as the float
+// 1.5 * 2^23 + C), cf = float(C) and s the scale product of tile 0; on exit
+// the same for the next block (operands `on`, scales `sn`, block bn).  Per
+// tile t: int8 MFMA(t+2), a third of acc(t) = fma(cf(t), s(t), acc(t)), the
+// conversion MFMA(t+1) (C input dn, minus 1.5 * 2^23: exactly float(C)), a
+// third, scale MFMA(t+1), the last third.  The VALU does one fma per element
+// and block; the conversion runs on the matrix pipe, and the result is the
+// same as fma(float(C), S, acc).
+__device__ __forceinline__ void compute_block(const Ops& o, const GuScales& sc, int b, const Ops& on,
+                                              const GuScales& sn, int bn, const Ctx& cx, int,
+                                              v16i& dn, v16f& cf, v16f& s, v16f (&acc)[4]) {
   const v16f zf = {0};
   v4h sav = sa_slot(sc.sa, b);
   v4h savn = sa_slot(sn.sa, bn);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    v16i cn = t < 3 ? __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a, o.b[t + 1], zi, 0, 0, 0)
-                    : __builtin_amdgcn_mfma_i32_32x32x32_i8(on.a, on.b[0], zi, 0, 0, 0);
-    anchor(cn, c);
-    v16f cf;
+    v16i dnn = t < 2 ? __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a, o.b[t + 2], cx.magic, 0, 0, 0)
+                     : __builtin_amdgcn_mfma_i32_32x32x32_i8(on.a, on.b[t - 2], cx.magic, 0, 0, 0);
+    anchor(dnn, dn);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) cf[v] = (float)c[v];
+    for (int v = 0; v < 5; ++v) acc[t][v] = __builtin_fmaf(cf[v], s[v], acc[t][v]);
+    anchor(acc[t]);
+    v16f cfn = __builtin_amdgcn_mfma_f32_32x32x8f16(cx.sub_a, cx.sub_b, __builtin_bit_cast(v16f, dn), 0, 0, 0);
+    anchor(cfn, acc[t]);
+#pragma unroll
+    for (int v = 5; v < 10; ++v) acc[t][v] = __builtin_fmaf(cf[v], s[v], acc[t][v]);
     if (t < 3)
-      anchor(cf, sav);
+      anchor(acc[t], sav);
     else
-      anchor(cf, savn);
+      anchor(acc[t], savn);
     v16f sx = t < 3 ? __builtin_amdgcn_mfma_f32_32x32x8f16(sav, sc.sw[t + 1], zf, 0, 0, 0)
                     : __builtin_amdgcn_mfma_f32_32x32x8f16(savn, sn.sw[0], zf, 0, 0, 0);
     anchor(sx, acc[t]);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[t][v] = __builtin_fmaf(cf[v], s[v], acc[t][v]);
+    for (int v = 10; v < 16; ++v) acc[t][v] = __builtin_fmaf(cf[v], s[v], acc[t][v]);
     anchor(acc[t]);
+    dn = dnn;
+    cf = cfn;
+    s = sx;
+  }
+}
+
+// One block of the down pipeline.  Per tile t: int8 MFMA(t+1) from the 1.5f
+// bias, half of acc(t) = fma(D(t), S(t), acc(t)), scale MFMA(t+1), the other
+// half; after the k-step's last block the correction MFMA subtracts its
+// 1.5 * S terms from acc(t).
+__device__ __forceinline__ void compute_block(const Ops& o, const DnScales& sc, int b, const Ops& on,
+                                              const DnScales& sn, int bn, const Ctx& cx, int lane,
+                                              v16i& c, v16f&, v16f& s, v16f (&acc)[4]) {
+  const v16f zf = {0};
+  v4h sav = dn_sa_slot(sc.q, b, lane);
+  v4h savn = dn_sa_slot(sn.q, bn, lane);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    // Each MFMA is followed by 8 fmas (32 cycles), the time it occupies the
+    // matrix pipe, so that neither MFMA waits at issue for the other.
+    v16i cn = t < 3 ? __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a, o.b[t + 1], cx.magic, 0, 0, 0)
+                    : __builtin_amdgcn_mfma_i32_32x32x32_i8(on.a, on.b[0], cx.magic, 0, 0, 0);
+    anchor(cn, c);
+    const v16f d = __builtin_bit_cast(v16f, c);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) acc[t][v] = __builtin_fmaf(d[v], s[v], acc[t][v]);
+    if (t < 3)
+      anchor(acc[t], sav);
+    else
+      anchor(acc[t], savn);
+    v16f sx = t < 3 ? __builtin_amdgcn_mfma_f32_32x32x8f16(sav, as_v4h(sc.wb[t + 1]), zf, 0, 0, 0)
+                    : __builtin_amdgcn_mfma_f32_32x32x8f16(savn, as_v4h(sn.wb[0]), zf, 0, 0, 0);
+    anchor(sx, acc[t]);
+#pragma unroll
+    for (int v = 8; v < 16; ++v) acc[t][v] = __builtin_fmaf(d[v], s[v], acc[t][v]);
+    anchor(acc[t]);
+    if (b == KSTEP - 1) {
+      acc[t] = __builtin_amdgcn_mfma_f32_32x32x8f16(cx.corr, as_v4h(sc.wb[t]), acc[t], 0, 0, 0);
+      anchor(acc[t]);
+    }
     c = cn;
     s = sx;
   }
 }
 
+template <bool GATEUP>
+using ScalesT = typename std::conditional<GATEUP, GuScales, DnScales>::type;
+
 // K-step j of an active wavefront, from buffer `cur`; k-step j+1 is (or, for
 // the last k-step, stale data standing in for it is) in `nxt`.  On entry X
-// holds block 0's operands, sc the k-step's scales and c/s the MFMAs of
-// (block 0, tile 0); on exit X, sn and c/s are those of k-step j+1 (after the
-// last k-step they belong to no k-step and are discarded).
+// holds block 0's operands, sc the k-step's scales and c/cf/s the pipeline
+// state of (block 0, tile 0); on exit X, sn and c/cf/s are those of k-step
+// j+1 (after the last k-step they belong to no k-step and are discarded).
+template <bool GATEUP>
 __device__ __forceinline__ void kstep(const Src& src, int j, int KS, int wave, int lane, const char* cur,
                                       const char* nxt, uint32_t cur_lds, uint32_t nxt_lds, Ops& X,
-                                      Ops& Y, const Scales& sc, Scales& sn, v16i& c, v16f& s,
-                                      v16f (&acc)[4]) {
+                                      Ops& Y, const ScalesT<GATEUP>& sc, ScalesT<GATEUP>& sn,
+                                      Ctx& cx, v16i& c, v16f& cf, v16f& s, v16f (&acc)[4]) {
   // The activation half of k-step j+1 (its weight half went out at the
   // barrier of k-step j-1; k-steps 0 and 1 are copied whole by the prologue).
-  if (j >= 1 && j + 1 < KS) issue_acts(src, j + 1, nxt_lds, wave, lane);
-  read_block(cur, 1, wave, lane, Y);
-  compute_block(X, sc, 0, Y, sc, 1, c, s, acc);
-  read_block(cur, 2, wave, lane, X);
-  compute_block(Y, sc, 1, X, sc, 2, c, s, acc);
-  read_block(cur, 3, wave, lane, Y);
-  compute_block(X, sc, 2, Y, sc, 3, c, s, acc);
+  if (j >= 1 && j + 1 < KS) issue_acts<GATEUP>(src, j + 1, nxt_lds, wave, lane);
+  if constexpr (!GATEUP) cx.corr = dn_corr_a(sc.q);
+  read_block<GATEUP>(cur, 1, wave, lane, Y);
+  compute_block(X, sc, 0, Y, sc, 1, cx, lane, c, cf, s, acc);
+  read_block<GATEUP>(cur, 2, wave, lane, X);
+  compute_block(Y, sc, 1, X, sc, 2, cx, lane, c, cf, s, acc);
+  read_block<GATEUP>(cur, 3, wave, lane, Y);
+  compute_block(X, sc, 2, Y, sc, 3, cx, lane, c, cf, s, acc);
   if (j + 1 < KS) {
     // k-step j+1 has landed for every wavefront, and every wavefront has read
     // all of k-step j: its buffer takes k-step j+2.
     wait_copies_barrier_0();
-    if (j + 2 < KS) issue_weights(src, j + 2, cur_lds, wave);
+    if (j + 2 < KS) issue_weights<GATEUP>(src, j + 2, cur_lds, wave);
   }
-  read_block(nxt, 0, wave, lane, X);
+  read_block<GATEUP>(nxt, 0, wave, lane, X);
   read_scales(nxt, wave, lane, sn);
-  compute_block(Y, sc, 3, X, sn, 0, c, s, acc);
+  compute_block(Y, sc, 3, X, sn, 0, cx, lane, c, cf, s, acc);
 }
 
 // Grouped GEMM.  GATEUP: A = the int8 token rows of the tile's (token, slot)
@@ -274,7 +405,8 @@ __device__ __forceinline__ void kstep(const Src& src, int j, int KS, int wave, i
 // rows to partial[token][slot] (the unweighted down-partials of #129 "Scope").
 template <bool GATEUP>
 __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds[2][STAGE];
+  using L = Lay<GATEUP>;
+  __shared__ __attribute__((aligned(1024))) char lds[2][L::STAGE];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_tiles = min(a.tiles[0], a.tile_bound);
@@ -299,7 +431,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
   const int KS = KB / KSTEP;
   const uint8_t* strip = GATEUP ? (shared ? a.sh_gu : a.gu + (size_t)g * a.gu_group)
                                 : (shared ? a.sh_dn : a.dn + (size_t)g * a.dn_group);
-  strip += (size_t)cs * KS * KSTEP_BYTES;
+  strip += (size_t)cs * KS * L::W_BYTES;
 
   const int wrow0 = row0 + MT_WAVE * wave;  // first CSR row of this wavefront
   const bool active = wrow0 < row_end;      // wavefront-uniform
@@ -310,19 +442,19 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
   Src src;
   src.w = strip;
   src.o_w = lane * 16;
-  src.o_ws = 16 * 1024 + wave * 256 + lane * 4;
+  src.o_ws = 16 * 1024 + wave * (GATEUP ? 256 : 512) + lane * 4;
   src.a = (GATEUP ? a.gq : a.hq) + (size_t)t32 * a_kb * 1024;
   src.as = (GATEUP ? a.gqs : a.hs) + (size_t)t32 * a_kb * 32;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)&lds[0][0];
   const uint32_t lds1 = (uint32_t)(uintptr_t)(lds_char*)&lds[1][0];
 
   // Prologue: k-steps 0 and 1 in flight; wait for k-step 0.
-  issue_weights(src, 0, lds0, wave);
-  issue_acts(src, 0, lds0, wave, lane);
+  issue_weights<GATEUP>(src, 0, lds0, wave);
+  issue_acts<GATEUP>(src, 0, lds0, wave, lane);
   if (KS > 1) {
-    issue_weights(src, 1, lds1, wave);
-    issue_acts(src, 1, lds1, wave, lane);
-    wait_copies_barrier_1kstep();
+    issue_weights<GATEUP>(src, 1, lds1, wave);
+    issue_acts<GATEUP>(src, 1, lds1, wave, lane);
+    wait_copies_barrier_n<L::DMA>();
   } else {
     wait_copies_barrier_0();
   }
@@ -331,26 +463,47 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = (v16f){0};
     Ops X, Y;
-    Scales s0, s1;
-    read_block(lds[0], 0, wave, lane, X);
+    ScalesT<GATEUP> s0, s1;
+    Ctx cx;
+    read_block<GATEUP>(lds[0], 0, wave, lane, X);
     read_scales(lds[0], wave, lane, s0);
-    const v16i zi = {0};
     const v16f zf = {0};
-    v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(X.a, X.b[0], zi, 0, 0, 0);
-    v16f s = __builtin_amdgcn_mfma_f32_32x32x8f16(sa_slot(s0.sa, 0), s0.sw[0], zf, 0, 0, 0);
+    v16i c;
+    v16f cf, s;
+    if constexpr (GATEUP) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) cx.magic[v] = 0x4b400000;  // 1.5 * 2^23
+      anchor(cx.magic);  // one register copy, never rematerialised
+      const _Float16 h0 = 0;
+      cx.sub_a = lane < 32 ? (v4h){(_Float16)-3072.0f, h0, h0, h0} : (v4h){h0, h0, h0, h0};
+      cx.sub_b = lane < 32 ? (v4h){(_Float16)4096.0f, h0, h0, h0} : (v4h){h0, h0, h0, h0};
+      anchor(cx.sub_a, cx.sub_b);
+      // pipeline state of (block 0, tile 0): int8 MFMA of tile 1, float(C)
+      // and scale product of tile 0
+      const v16i d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(X.a, X.b[0], cx.magic, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_i32_32x32x32_i8(X.a, X.b[1], cx.magic, 0, 0, 0);
+      cf = __builtin_amdgcn_mfma_f32_32x32x8f16(cx.sub_a, cx.sub_b, __builtin_bit_cast(v16f, d0), 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x8f16(sa_slot(s0.sa, 0), s0.sw[0], zf, 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) cx.magic[v] = 0x3fc00000;  // 1.5f
+      anchor(cx.magic);
+      c = __builtin_amdgcn_mfma_i32_32x32x32_i8(X.a, X.b[0], cx.magic, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x8f16(dn_sa_slot(s0.q, 0, lane), as_v4h(s0.wb[0]), zf, 0, 0, 0);
+    }
     // Unrolled by two so that each buffer and scale set has a fixed role.
     for (int j = 0; j < KS; j += 2) {
-      kstep(src, j, KS, wave, lane, lds[0], lds[1], lds0, lds1, X, Y, s0, s1, c, s, acc);
+      kstep<GATEUP>(src, j, KS, wave, lane, lds[0], lds[1], lds0, lds1, X, Y, s0, s1, cx, c, cf, s, acc);
       if (j + 1 < KS)
-        kstep(src, j + 1, KS, wave, lane, lds[1], lds[0], lds1, lds0, X, Y, s1, s0, c, s, acc);
+        kstep<GATEUP>(src, j + 1, KS, wave, lane, lds[1], lds[0], lds1, lds0, X, Y, s1, s0, cx, c, cf, s, acc);
     }
   } else {
     // A wavefront past the tile's rows computes nothing but still does its
     // share of the copies and meets every barrier.
     for (int j = 0; j + 1 < KS; ++j) {
-      if (j >= 1) issue_acts(src, j + 1, (j & 1) ? lds0 : lds1, wave, lane);
+      if (j >= 1) issue_acts<GATEUP>(src, j + 1, (j & 1) ? lds0 : lds1, wave, lane);
       wait_copies_barrier_0();
-      if (j + 2 < KS) issue_weights(src, j + 2, (j & 1) ? lds1 : lds0, wave);
+      if (j + 2 < KS) issue_weights<GATEUP>(src, j + 2, (j & 1) ? lds1 : lds0, wave);
     }
   }
   __syncthreads();  // every wavefront is out of the k loop: LDS is free for the epilogue
@@ -423,6 +576,15 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
     for (int v = 0; v < 16; ++v) rows[v] = __shfl(ri, out_row(v, lane), 64);
     const bool full = (cs + 1) * DN_COLS <= a.d;  // the strip has no padding columns
     const int col0 = cs * DN_COLS + (lane & 31);
+    // acc holds 2^-eg times the down product; scaled in place (pinned, so that
+    // the scaling is not sunk into the conditional stores below)
+    const int eg = __builtin_amdgcn_readfirstlane(a.dn_exp[g]);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[tt][v] = ldexpf(acc[tt][v], eg);
+      anchor(acc[tt]);
+    }
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       if (rows[v] >= 0) {

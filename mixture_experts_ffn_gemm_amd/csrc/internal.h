@@ -13,8 +13,13 @@
 //               so lane l of a wavefront reads bytes [16 l, 16 l + 16).  Strip c
 //               holds tiles tt = 0,1: gate rows 64c + 32tt + r; tt = 2,3: the up
 //               rows 64c + 32(tt-2) + r (so gate and up of one column meet in one lane).
-//   down        per expert [d_pad/128 strips][F_pad/128 k-steps][17 KiB], tile tt =
-//               down rows 128c + 32tt + r.
+//   down        per expert [d_pad/128 strips][F_pad/128 k-steps][18 KiB], tile tt =
+//               down rows 128c + 32tt + r.  The 16 code chunks are followed by
+//               2 KiB of binary16 scale pairs [tt][half][32 rows][4]: half h of
+//               row r holds {W, W/2} of blocks 2h and 2h+1, where W = scale *
+//               2^(23 - e) and e = dn_exp[group] is the smallest exponent >= 0
+//               that keeps every W of the group finite (so W and W/2 are exact).
+//               Lane l of a wavefront reads bytes [8 l, 8 l + 8) of a tile's 512.
 //   The shared expert has its own planes of the same form (F replaced by Fs).
 //   Padding rows/blocks hold zero codes and zero scales.
 //
@@ -56,7 +61,8 @@ constexpr int MT_WAVE = 32;       // rows per wavefront
 constexpr int GU_COLS = 64;       // SwiGLU output columns per gate/up strip
 constexpr int DN_COLS = 128;      // output columns per down strip
 constexpr int KSTEP = 4;          // 32-blocks per GEMM k-step
-constexpr int KSTEP_BYTES = 17 * 1024;  // codes (16 KiB) + scales (1 KiB) of a k-step
+constexpr int KSTEP_BYTES = 17 * 1024;     // gate/up k-step: codes (16 KiB) + scales (1 KiB)
+constexpr int DN_KSTEP_BYTES = 18 * 1024;  // down k-step: codes (16 KiB) + scale pairs (2 KiB)
 constexpr int MAX_TOPK = 16;
 constexpr int MAX_EXPERTS = 256;
 constexpr int DECODE_MAX_TOKENS = 8;
@@ -95,16 +101,23 @@ struct moe_ffn_weights {
   uint8_t* dn;
   uint8_t* sh_gu;
   uint8_t* sh_dn;
+  int32_t* dn_exp;  // [G] exponent e of each group's down scale plane
   size_t gu_per_expert, dn_per_expert;  // bytes
 };
 
 namespace moe {
 
 // ---- launchers (each returns hipGetLastError() of its launch) ----
+// Gate/up form (dn_exp == NULL, 17 KiB k-steps) or down form (dn_exp = the
+// groups' exponents, 18 KiB k-steps with scale pairs).
 hipError_t launch_repack_q8(const uint8_t* src0, const uint8_t* src1, int n_groups,
                             size_t src_group_bytes, int src_rows, int src_blocks, int tiles_per_src,
                             int n_strips, int kb_pad, uint8_t* dst, size_t dst_group_bytes,
-                            hipStream_t s);
+                            const int32_t* dn_exp, hipStream_t s);
+// e[g] = the smallest e >= 0 with |scale| * 2^(23 - e) <= 65504 for every Q8_0
+// block of group g (n_groups groups of n_blocks blocks, src_group_bytes apart).
+hipError_t launch_scale_exponent(const uint8_t* src, int n_groups, size_t src_group_bytes,
+                                 long n_blocks, int32_t* e, hipStream_t s);
 hipError_t launch_transpose_router(const float* w, int E, int d, int E64, float* wt, hipStream_t s);
 
 hipError_t launch_router(const float* x, int n, int d, const float* wt, const float* bias, int E,
@@ -150,6 +163,7 @@ struct GemmArgs {
   const uint8_t* dn;
   size_t dn_group;
   const uint8_t* sh_dn;
+  const int32_t* dn_exp;
   float* partial;
   int d;
   int kk;
