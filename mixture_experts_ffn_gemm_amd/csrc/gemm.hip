@@ -451,10 +451,20 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
   // Prologue: k-steps 0 and 1 in flight; wait for k-step 0.
   issue_weights<GATEUP>(src, 0, lds0, wave);
   issue_acts<GATEUP>(src, 0, lds0, wave, lane);
+  // Down: the (token, slot) of this lane's CSR row wrow0 + lane%32, loaded
+  // now (and first used in the epilogue) so that the load's latency hides
+  // under the k loop.  Every wavefront issues both loads (the row clamped
+  // into the CSR arrays), so that the vmcnt count below holds for all.
+  int tok = -1, slt = -1;
+  if (!GATEUP) {
+    const int p_lane = min(wrow0 + (lane & 31), a.p_total - 1);
+    tok = a.tok_i[p_lane];
+    slt = a.tok_k[p_lane];
+  }
   if (KS > 1) {
     issue_weights<GATEUP>(src, 1, lds1, wave);
     issue_acts<GATEUP>(src, 1, lds1, wave, lane);
-    wait_copies_barrier_n<L::DMA>();
+    wait_copies_barrier_n<L::DMA + 2 * !GATEUP>();
   } else {
     wait_copies_barrier_0();
   }
@@ -506,7 +516,9 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
       if (j + 2 < KS) issue_weights<GATEUP>(src, j + 2, (j & 1) ? lds1 : lds0, wave);
     }
   }
-  __syncthreads();  // every wavefront is out of the k loop: LDS is free for the epilogue
+  // gate/up: every wavefront is out of the k loop, so LDS is free for the
+  // epilogue (the down epilogue uses no LDS)
+  if (GATEUP) __syncthreads();
   if (!active) return;
 
   if (GATEUP) {
@@ -563,14 +575,12 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
         make_uint4(packed[4], packed[5], packed[6], packed[7]);
     a.hs[(((size_t)t32 * (a.kbmax / KSTEP) + (kbf >> 2)) * 32 + r) * KSTEP + (kbf & 3)] = s16;
   } else {
-    // Destination row of each of the lane's 16 output rows: lane r looks up
-    // CSR row wrow0 + r once; all 16 exchanges are issued before any store.
-    const int p_lane = wrow0 + (lane & 31);
+    // Destination row of each of the lane's 16 output rows (lane r holds that
+    // of CSR row wrow0 + r); all 16 exchanges are issued before any store.
     int ri = -1;
-    if (p_lane < row_end) {
-      const int tok = a.tok_i[p_lane], slt = a.tok_k[p_lane];
-      if ((unsigned)tok < (unsigned)a.n_tokens && (unsigned)slt < (unsigned)a.kk) ri = tok * a.kk + slt;
-    }
+    if (wrow0 + (lane & 31) < row_end && (unsigned)tok < (unsigned)a.n_tokens &&
+        (unsigned)slt < (unsigned)a.kk)
+      ri = tok * a.kk + slt;
     int rows[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) rows[v] = __shfl(ri, out_row(v, lane), 64);
