@@ -19,7 +19,7 @@ typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int RJC = 64;          // router: j values per LDS chunk
 constexpr int RJQ = RJC / 4;     // 4-j quads per chunk
-constexpr int RNB = 4;           // chunk buffers in the LDS ring
+constexpr int RNB = 8;           // chunk buffers in the LDS ring (144 KiB: one workgroup per CU)
 constexpr int RPF = RNB - 1;     // chunks copied ahead
 constexpr int RDMA = 6;          // copies per wavefront per chunk
 constexpr int RT = 2;            // tokens per wavefront
@@ -118,13 +118,17 @@ __global__ __launch_bounds__(256, 1) void router_kernel(
 
   // Wait until chunk c is copied for every wavefront, given how many chunks
   // this wavefront has issued after it (vector loads complete in order).
+  static_assert(RPF <= 7 && RPF * RDMA <= 63, "vmcnt counts at most 63 copies");
   auto wait_chunk = [&](int newer) {
-    if (newer >= 2)
-      rwait_vm<2 * RDMA>();
-    else if (newer == 1)
-      rwait_vm<RDMA>();
-    else
-      rwait_vm<0>();
+    switch (newer) {
+      case 0: rwait_vm<0>(); break;
+      case 1: rwait_vm<RDMA>(); break;
+      case 2: rwait_vm<2 * RDMA>(); break;
+      case 3: rwait_vm<3 * RDMA>(); break;
+      case 4: rwait_vm<4 * RDMA>(); break;
+      case 5: rwait_vm<5 * RDMA>(); break;
+      default: rwait_vm<6 * RDMA>(); break;
+    }
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
@@ -148,7 +152,6 @@ __global__ __launch_bounds__(256, 1) void router_kernel(
   // chunk c+1 is read, chunk c+1 is waited for and published; every wavefront
   // has then read all of chunk c-1, whose buffer takes chunk c+RPF.
   const int CF = d / RJC;
-  static_assert(RPF == 3, "the in-loop wait below assumes chunks c+1 and c+2 in flight");
   wait_chunk(np - 1);  // chunks 1..np-1 were issued after chunk 0
   load_sub(0, 0);
   for (int c = 0; c < CF; ++c) {
@@ -156,8 +159,8 @@ __global__ __launch_bounds__(256, 1) void router_kernel(
     for (int q = 0; q < 4; ++q) {
       const int b = q & 1;
       if (q == 3 && c + 1 < C) {
-        // issued so far: chunks 0 .. min(c+2, C-1); newer than c+1: c+2 if it exists
-        wait_chunk(c + 2 < C ? 1 : 0);
+        // issued so far: chunks 0 .. min(c+RPF-1, C-1); newer than c+1: the rest
+        wait_chunk(min(RPF - 2, C - c - 2));
         if (c + RPF < C) issue(c + RPF);
       }
       load_sub(4 * c + q + 1, b ^ 1);
