@@ -191,18 +191,38 @@ def main():
     B.lib()
     wl = mw.WORKLOADS[args.workload]
     s = wl.shape
+    n_layers = wl.n_layers
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
     t0 = time.perf_counter()
     lw = mw.workload_layer(args.workload)
     x_np = mw.workload_tokens(args.workload)
-    log(f"[bench] {args.workload}: inputs generated in {time.perf_counter() - t0:.1f} s")
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     layer = MoeLayer.from_workload(lw, device=dev)
     n = x_np.shape[0]
+    stack = [layer]
+    for li in range(1, n_layers):  # a stack: every layer resident in HBM
+        stack.append(MoeLayer.from_workload(mw.workload_layer(args.workload, layer=li), device=dev))
+        log(f"[bench] {args.workload}: layer {li} created")
+    log(f"[bench] {args.workload}: inputs generated in {time.perf_counter() - t0:.1f} s")
     x = torch.from_numpy(x_np).to(dev)
+    eps = 1e-5
+    if n_layers > 1:
+        # the stack's input is h0; each layer sees RMSNorm(h) (unit gain) and
+        # adds its output to the residual stream
+        h0 = x
+        h = torch.empty_like(h0)
+        x = torch.empty_like(h0)
+        B.moe_ffn_residual_rmsnorm(h0, None, x, n, s.d, eps, stream)
     out = torch.empty((n, s.d), dtype=torch.float32, device=dev)
     ws = layer.workspace(n)
-    stream = torch.cuda.current_stream(dev)
+
+    def stack_pass():
+        h.copy_(h0)
+        B.moe_ffn_residual_rmsnorm(h, None, x, n, s.d, eps, stream)
+        for lay in stack:
+            B.moe_ffn_prefill(lay.handle, x, n, out, ws, ws.numel(), None, stream)
+            B.moe_ffn_residual_rmsnorm(h, out, x, n, s.d, eps, stream)
     exp_start = torch.empty(s.n_experts + 1 + (1 if s.shared_ffn else 0), dtype=torch.int32, device=dev)
     B.moe_ffn_prefill(layer.handle, x, n, out, ws, ws.numel(), B.make_routing(exp_start=exp_start), stream)
     for _ in range(args.warmup):
@@ -211,16 +231,25 @@ def main():
     counts = np.diff(exp_start.cpu().numpy())
 
     # Timed region: K plain prefill passes (the product entry point; no events
-    # between its kernels).
+    # between its kernels), or K passes through the whole stack.
+    if n_layers > 1:
+        for _ in range(args.warmup):
+            stack_pass()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
-        B.moe_ffn_prefill(layer.handle, x, n, out, ws, ws.numel(), None, stream)
+        if n_layers > 1:
+            stack_pass()
+        else:
+            B.moe_ffn_prefill(layer.handle, x, n, out, ws, ws.numel(), None, stream)
     stop.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / args.steps
+    if n_layers > 1:
+        # the per-stage passes below run the first layer on its normalised input
+        B.moe_ffn_residual_rmsnorm(h0, None, x, n, s.d, eps, stream)
 
     # Then K passes of the profiled entry point: the library records HIP events
     # between its stages on its launch stream (each event adds a dispatch gap,
@@ -264,7 +293,10 @@ def main():
     cpu = None
     if args.cpu_seconds > 0:
         log("[bench] timing the CPU oracle sample")
-        cpu = cpu_baseline(lw, x_np, args.cpu_seconds)
+        cpu = cpu_baseline(lw, x.cpu().numpy() if n_layers > 1 else x_np, args.cpu_seconds)
+        if n_layers > 1:  # the oracle's per-layer rate over the stack's depth
+            cpu["value"] /= n_layers
+            cpu["sample"] += f"; one layer of the {n_layers}, rate divided by {n_layers}"
 
     res = {
         "metric": METRIC, "value": round(n / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
@@ -277,7 +309,12 @@ def main():
         "experts_touched": int((counts[:s.n_experts] > 0).sum()),
         "stages": stages, "roofline": roofline, "cpu_baseline": cpu,
     }
-    layer.close()
+    if n_layers > 1:
+        res["stack"] = {"layers": n_layers, "ms_per_layer": round(ms_step / n_layers, 5),
+                        "step": "h = h0; xn = RMSNorm(h); per layer: y = MoE(xn), h += y, xn = RMSNorm(h)",
+                        "stages_and_roofline": "first layer, profiled passes on its normalised input"}
+    for lay in stack:
+        lay.close()
     print(json.dumps(res), flush=True)
 
 

@@ -280,3 +280,45 @@ def test_n4096_prefill_sampled():
     check_routing(lw, x, g)
     toks = np.unique(np.concatenate([[0, 4095], np.random.default_rng(7).integers(0, 4096, 10)]))
     check_outputs(lw, x, g, toks)
+
+
+@pytest.mark.slow
+def test_olmoe_stack16():
+    """The 16-layer OLMoE-shaped stack: h_{l+1} = h_l + MoE_l(RMSNorm(h_l)) with
+    independent seeded weights per layer.  Every layer is checked against the
+    oracle fed the GPU's own normalised input: routing of all 2048 tokens
+    bit-exact, the layer output on sampled tokens to the fp32 bar, the
+    residual add bit for bit (one fp32 add) and the RMSNorm against the
+    oracle's."""
+    from mixture_experts_ffn_gemm_amd import binding as B
+    from mixture_experts_ffn_gemm_amd.layer import MoeLayer
+    wl = mw.WORKLOADS["olmoe_stack16"]
+    n, d, eps = wl.n_tokens, wl.shape.d, 1e-5
+    dev = torch.device("cuda")
+    h = torch.from_numpy(mw.workload_tokens("olmoe_stack16")).to(dev)
+    xn = torch.empty_like(h)
+    y = torch.empty_like(h)
+    B.moe_ffn_residual_rmsnorm(h, None, xn, n, d, eps)
+    toks = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(11).integers(0, n, 6)]))
+    for layer_idx in range(wl.n_layers):
+        lw = mw.workload_layer("olmoe_stack16", layer=layer_idx)
+        layer = MoeLayer.from_workload(lw)
+        try:
+            ids = torch.full((n, wl.shape.top_k), -7, dtype=torch.int32, device=dev)
+            r = B.make_routing(topk_ids=ids)
+            torch.cuda.synchronize()
+            xn_np = xn.cpu().numpy()
+            h_before = h.cpu().numpy()
+            layer.prefill(xn, out=y, routing=r)
+            B.moe_ffn_residual_rmsnorm(h, y, xn, n, d, eps)
+            torch.cuda.synchronize()
+            y_np, h_np, xn_next = y.cpu().numpy(), h.cpu().numpy(), xn.cpu().numpy()
+        finally:
+            layer.close()
+        o = O.routing(lw, xn_np)
+        assert np.array_equal(ids.cpu().numpy(), o["ids"]), f"layer {layer_idx}: top-k ids differ"
+        ref = O.moe_tokens(lw, xn_np, tokens=toks)
+        rel, emax = moe_close(y_np[toks], ref["out"])
+        assert np.array_equal(h_np, h_before + y_np), f"layer {layer_idx}: residual add differs"
+        np.testing.assert_allclose(xn_next[toks], O.rmsnorm(h_np[toks], eps), rtol=2e-6, atol=1e-6)
+        say(f"olmoe_stack16 layer {layer_idx}: routing bit-exact, rel_l2={rel:.2e} max_elem={emax:.2e}")
