@@ -6,7 +6,8 @@
 // levers" 1: the selection must not round-trip to the host):
 //   1. router                   (fp32 fused-chain logits for all experts)
 //   2. routing                  (top-k, softmax weights, per-tile expert
-//                                histograms and ranks)
+//                                histograms and ranks; in the router's
+//                                launch when E <= 64)
 //   3. bucketing                (CSR expStart/expTokI/expTokK, the 128-row tile
 //                                table, each pair's padded GEMM row), then the
 //                                int8 quantiser of x (and the shared-expert
@@ -153,10 +154,17 @@ int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, v
   auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
 
   HIP_TRY(mark(0));
-  HIP_TRY(launch_router(x, n, dm.d, W->router_wt, W->has_bias ? W->router_bias : nullptr, dm.E,
-                        dm.E64, logits, s));
-  HIP_TRY(mark(1));
-  HIP_TRY(launch_route(logits, n, dm.E, dm.k, dm.norm, ids, w, rank, hist, s));
+  const float* rbias = W->has_bias ? W->router_bias : nullptr;
+  if (dm.E <= 64) {
+    // one workgroup holds all logits of its tokens: router and routing fused
+    HIP_TRY(launch_router_route(x, n, dm.d, W->router_wt, rbias, dm.E, dm.k, dm.norm, ids, w, rank,
+                                hist, s));
+    HIP_TRY(mark(1));
+  } else {
+    HIP_TRY(launch_router(x, n, dm.d, W->router_wt, rbias, dm.E, dm.E64, logits, s));
+    HIP_TRY(mark(1));
+    HIP_TRY(launch_route(logits, n, dm.E, dm.k, dm.norm, ids, w, rank, hist, s));
+  }
   HIP_TRY(mark(2));
   HIP_TRY(launch_bucket(ids, rank, hist, n, dm.E, dm.k, dm.has_shared, exp_start, tok_i, tok_k, pos,
                         tiles, L.tile_bound, s));

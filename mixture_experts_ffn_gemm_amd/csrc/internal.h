@@ -122,6 +122,11 @@ hipError_t launch_transpose_router(const float* w, int E, int d, int E64, float*
 
 hipError_t launch_router(const float* x, int n, int d, const float* wt, const float* bias, int E,
                          int E64, float* logits, hipStream_t s);
+// Router and routing in one launch (E <= 64): ids, w, rank and the tile
+// histograms as launch_route writes them; no logits in global memory.
+hipError_t launch_router_route(const float* x, int n, int d, const float* wt, const float* bias,
+                               int E, int k, int norm, int32_t* ids, float* w, int32_t* rank,
+                               int32_t* hist, hipStream_t s);
 // Quantise every token row per 32-block and write its codes and scales to the
 // padded GEMM rows pos[t][0..kk) in the gq/gqs layout (rows past pad_rows or
 // -1 are skipped); with sh_gate_vec != NULL also gs[t] = sigmoid(x[t] . g);

@@ -19,7 +19,7 @@ typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int RJC = 64;          // router: j values per LDS chunk
 constexpr int RJQ = RJC / 4;     // 4-j quads per chunk
-constexpr int RNB = 8;           // chunk buffers in the LDS ring (144 KiB: one workgroup per CU)
+constexpr int RNB = 6;           // chunk buffers in the LDS ring (108 KiB: one workgroup per CU)
 constexpr int RPF = RNB - 1;     // chunks copied ahead
 constexpr int RDMA = 6;          // copies per wavefront per chunk
 constexpr int RT = 2;            // tokens per wavefront
@@ -70,6 +70,136 @@ __device__ __forceinline__ void router_fma16(float& acc0, float& acc1, float xa,
 }
 #undef RFMA2
 
+// Routing of one tile of ROUTE_TILE tokens, 16 threads per token (threads
+// tid < ROUTE_THREADS of the workgroup; every thread of the workgroup calls
+// this, since it meets workgroup barriers).  The tile's logits l[token][e]
+// are in LDS.  Each (token,
+// expert) finds its rank among the token's experts -- the number of experts
+// with a larger logit, or an equal logit and a lower id -- and the experts of
+// rank < k take slot = rank.  This is the top-k of the contract (logit
+// descending, id ascending) computed without any serial reduction.  Then
+// softmax over all E, optional renormalisation, and the per-expert rank of
+// each (token, slot) pair among the tile's pairs in (token, slot) order, with
+// the tile's histogram, for the bucketing kernel.
+struct RouteLds {
+  float l[ROUTE_TILE][MAX_EXPERTS];
+  unsigned long long key[ROUTE_TILE][MAX_EXPERTS];
+  int ids[ROUTE_TILE * MAX_TOPK];
+  float val[ROUTE_TILE][MAX_TOPK];
+  int cnt[MAX_EXPERTS];
+};
+
+// A 64-bit key per (logit, expert id) whose unsigned order is the top-k order
+// (logit descending, then id ascending): the float's bits mapped to an
+// unsigned order (-0 taken as +0, so that equal logits tie as in a float
+// comparison) above the inverted id.
+__device__ __forceinline__ unsigned long long topk_key(float l, int e) {
+  const uint32_t b = l == 0.0f ? 0u : __float_as_uint(l);
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((unsigned long long)ord << 32) | (uint32_t)~(uint32_t)e;
+}
+
+__device__ __forceinline__ void route_tile(RouteLds& R, int tile, int t0, int nt, int E, int k, int norm, int tid,
+                           int nthreads, int32_t* __restrict__ ids, float* __restrict__ wout,
+                           int32_t* __restrict__ rank, int32_t* __restrict__ hist) {
+  for (int e = tid; e < E; e += nthreads) R.cnt[e] = 0;
+  __syncthreads();  // the caller's logit writes are visible to every thread
+  // ranks: thread (token tl = tid/16, expert group g = tid%16) owns experts g + 16c
+  const int tl = tid >> 4, g = tid & 15;
+  const bool mine = tid < ROUTE_THREADS;
+  // Padding instead of per-element tests (a test of a uniform bound next to a
+  // per-lane compare becomes a scalar mask operation per element): keys up to
+  // E rounded up to 32 (0 past E, below every real key), and ids -1 in every
+  // slot that the ranks below do not fill (slots >= k, tokens >= nt).
+  const int E32 = (E + 31) & ~31;
+  if (mine) {
+    for (int e = g; e < E32; e += 16) R.key[tl][e] = e < E ? topk_key(R.l[tl][e], e) : 0ull;
+    R.ids[tl * MAX_TOPK + g] = -1;
+  }
+  __syncthreads();
+  if (mine)
+    for (int e = g; e < E; e += 16) {
+      const unsigned long long ke = R.key[tl][e];
+      int r = 0;
+      // the rank of e is the number of larger keys; 32 keys per pass, all
+      // reads issued before the compares
+      // (unconditional reads: a conditional read would be a branch of its own
+      // and wait alone)
+      for (int e0 = 0; e0 < E; e0 += 32) {
+        ulonglong2 v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const ulonglong2*>(&R.key[tl][e0 + 2 * i]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) r += (int)(v[i].x > ke) + (int)(v[i].y > ke);
+      }
+      if (r < k && tl < nt) {
+        R.ids[tl * MAX_TOPK + r] = e;
+        R.val[tl][r] = R.l[tl][e];
+      }
+    }
+  __syncthreads();
+
+  if (mine) {
+    // softmax over all E (the 16 threads of a token share the sum), weights of the k slots
+    const float m = R.val[tl][0];
+    float part = 0.0f;
+    for (int e = g; e < E; e += 16) part += expf(R.l[tl][e] - m);
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) part += __shfl_xor(part, off, 16);
+    float p = (g < k) ? expf(R.val[tl][min(g, k - 1)] - m) / part : 0.0f;
+    if (norm) {
+      float sum = p;
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 16);
+      p = p / sum;
+    }
+    if (tl < nt && g < k) {
+      ids[(size_t)(t0 + tl) * k + g] = R.ids[tl * MAX_TOPK + g];
+      wout[(size_t)(t0 + tl) * k + g] = p;
+    }
+  }
+
+  // rank of pair q = (token, slot) among the tile's earlier pairs of the same expert
+  const int np = nt * k;
+  if (tid < np) {
+    const int q = tid;
+    const int e = R.ids[(q / k) * MAX_TOPK + q % k];
+    int r = 0, later = 0;
+    // pairs of earlier tokens (all their k slots), then this token's earlier
+    // slots; the ids of two tokens are read per pass, all reads issued before
+    // the compares
+    for (int t2 = 0; t2 < nt; t2 += 2) {
+      // unconditional reads (inside R.ids: t2 + 1 < ROUTE_TILE), masked below
+      int4 v[2][MAX_TOPK / 4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int c4 = 0; c4 < MAX_TOPK / 4; ++c4)
+          v[h][c4] = reinterpret_cast<const int4*>(&R.ids[(t2 + h) * MAX_TOPK])[c4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int c4 = 0; c4 < MAX_TOPK / 4; ++c4) {
+          const int ev[4] = {v[h][c4].x, v[h][c4].y, v[h][c4].z, v[h][c4].w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            // slots past k and absent tokens hold -1; the order tests are
+            // sign bits of differences (no mask operations)
+            const int q2 = (t2 + h) * k + 4 * c4 + u;
+            const int before = (int)((uint32_t)(q2 - q) >> 31), after = (int)((uint32_t)(q - q2) >> 31);
+            const bool same = ev[u] == e;
+            r += same ? before : 0;
+            later |= same ? after : 0;
+          }
+        }
+    }
+    rank[(size_t)(t0 + q / k) * k + q % k] = r;
+    if (!later) R.cnt[e] = r + 1;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += nthreads) hist[(size_t)tile * E + e] = R.cnt[e];
+}
+
 // Router logits for 4*RT tokens x 64 experts per workgroup (lane = expert, RT
 // tokens per wavefront).  Each logit is one fp32 fused multiply-add chain over
 // ascending j, from +0, then + bias (a separate fp32 add); the chain order is
@@ -83,12 +213,18 @@ __device__ __forceinline__ void router_fma16(float& acc0, float& acc1, float xa,
 // one value of each of its wavefront's two token rows (lane i of every
 // 16-lane row reads column i), and the token value of each step reaches all
 // lanes through a DPP row broadcast inside the FMA: 6 LDS reads per 32 FMAs.
-// The reads of the next 16 j are issued before the current 16 j are
-// computed.  Only the d/16 sub-chunks inside d are visited (d % 32 == 0), so
+// The reads of each 16 j are issued three 16-j steps before they are used.  Only the d/16 sub-chunks inside d are visited (d % 32 == 0), so
 // no padding term enters a chain.
+//
+// FUSE (E <= 64, so a workgroup holds every logit of its ROUTE_TILE tokens):
+// the logits stay in LDS and the workgroup routes its tile (route_tile), with
+// no logits in global memory and no separate routing launch.
+template <bool FUSE>
 __global__ __launch_bounds__(256, 1) void router_kernel(
     const float* __restrict__ x, int n, int d, const float* __restrict__ wt,
-    const float* __restrict__ bias, int E, int E64, float* __restrict__ logits) {
+    const float* __restrict__ bias, int E, int E64, float* __restrict__ logits, int k, int norm,
+    int32_t* __restrict__ ids, float* __restrict__ wout, int32_t* __restrict__ rank,
+    int32_t* __restrict__ hist) {
   __shared__ __attribute__((aligned(1024))) char ring[RNB * R_BUF];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -132,9 +268,9 @@ __global__ __launch_bounds__(256, 1) void router_kernel(
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  // operands of one 16-j sub-chunk
-  f4v w[2][4];
-  float xa[2], xb[2];
+  // operands of 16-j sub-chunks, a ring of 4 (read 3 sub-chunks ahead)
+  f4v w[4][4];
+  float xa[4], xb[4];
   auto load_sub = [&](int sub, int b) {
     const int c = sub >> 2, q0 = (sub & 3) * 4;
     const char* buf = ring + (c % RNB) * R_BUF;
@@ -146,37 +282,52 @@ __global__ __launch_bounds__(256, 1) void router_kernel(
   };
   float acc0 = 0.0f, acc1 = 0.0f;
   // One full chunk (4 sub-chunks of 16 j) per iteration, then the trailing
-  // half chunk when d % 64 == 32.  The reads of sub-chunk s+1 are issued
-  // before sub-chunk s is computed, unconditionally (after the last sub-chunk
-  // they read stale LDS and are discarded).  Before the first sub-chunk of
-  // chunk c+1 is read, chunk c+1 is waited for and published; every wavefront
-  // has then read all of chunk c-1, whose buffer takes chunk c+RPF.
+  // half chunk when d % 64 == 32.  The reads of sub-chunk s+3 are issued
+  // before sub-chunk s is computed, unconditionally (past the last sub-chunk
+  // they read stale LDS and are discarded).  At the first sub-chunk of chunk c
+  // chunk c+1 is waited for and published (its sub-chunk 0 is read from the
+  // next step on); every wavefront has then read all of chunk c-1, whose
+  // buffer takes chunk c+RPF.
   const int CF = d / RJC;
   wait_chunk(np - 1);  // chunks 1..np-1 were issued after chunk 0
   load_sub(0, 0);
+  load_sub(1, 1);
+  load_sub(2, 2);
   for (int c = 0; c < CF; ++c) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int b = q & 1;
-      if (q == 3 && c + 1 < C) {
+      if (q == 0 && c + 1 < C) {
         // issued so far: chunks 0 .. min(c+RPF-1, C-1); newer than c+1: the rest
         wait_chunk(min(RPF - 2, C - c - 2));
         if (c + RPF < C) issue(c + RPF);
       }
-      load_sub(4 * c + q + 1, b ^ 1);
-      router_fma16(acc0, acc1, xa[b], xb[b], w[b][0], w[b][1], w[b][2], w[b][3]);
+      load_sub(4 * c + q + 3, (q + 3) & 3);
+      router_fma16(acc0, acc1, xa[q], xb[q], w[q][0], w[q][1], w[q][2], w[q][3]);
     }
   }
-  if (CF < C) {  // 32 trailing j: sub-chunks 4 CF (already requested) and 4 CF + 1
-    load_sub(4 * CF + 1, 1);
+  if (CF < C) {  // 32 trailing j: sub-chunks 4 CF and 4 CF + 1 (already requested)
     router_fma16(acc0, acc1, xa[0], xb[0], w[0][0], w[0][1], w[0][2], w[0][3]);
     router_fma16(acc0, acc1, xa[1], xb[1], w[1][0], w[1][1], w[1][2], w[1][3]);
   }
   const int e = eg * 64 + lane;
-  if (e < E) {
-    const float bb = bias ? bias[e] : 0.0f;
-    if (tw < n) logits[(size_t)tw * E + e] = bias ? acc0 + bb : acc0;
-    if (tw + 1 < n) logits[(size_t)(tw + 1) * E + e] = bias ? acc1 + bb : acc1;
+  if constexpr (FUSE) {
+    static_assert(4 * RT == ROUTE_TILE, "a router workgroup covers one routing tile");
+    __shared__ __attribute__((aligned(16))) RouteLds R;
+    const int tl = wave * RT;
+    if (e < E) {
+      const float bb = bias ? bias[e] : 0.0f;
+      R.l[tl][e] = bias ? acc0 + bb : acc0;
+      R.l[tl + 1][e] = bias ? acc1 + bb : acc1;
+    }
+    const int t0 = blockIdx.x * ROUTE_TILE;
+    route_tile(R, blockIdx.x, t0, min(ROUTE_TILE, n - t0), E, k, norm, threadIdx.x, 256, ids, wout,
+               rank, hist);
+  } else {
+    if (e < E) {
+      const float bb = bias ? bias[e] : 0.0f;
+      if (tw < n) logits[(size_t)tw * E + e] = bias ? acc0 + bb : acc0;
+      if (tw + 1 < n) logits[(size_t)(tw + 1) * E + e] = bias ? acc1 + bb : acc1;
+    }
   }
 }
 
@@ -201,11 +352,15 @@ __global__ __launch_bounds__(256) void quantize_scatter_kernel(
   if (t >= n) return;
   const float* xr = x + (size_t)t * d;
   const int KS = d_pad / (QB * KSTEP);
+  // the slots' padded rows; the loads are unconditional (index clamped into
+  // this token's row) so that they issue together, and slots past kk masked
   int prow[MAX_TOPK + 1];
 #pragma unroll
+  for (int s = 0; s < MAX_TOPK + 1; ++s) prow[s] = pos[(size_t)t * kk + min(s, kk - 1)];
+#pragma unroll
   for (int s = 0; s < MAX_TOPK + 1; ++s) {
-    const int v = s < kk ? pos[(size_t)t * kk + s] : -1;
-    prow[s] = (v >= 0 && v < pad_rows) ? v : -1;
+    const int v = prow[s];
+    prow[s] = (s < kk && v >= 0 && v < pad_rows) ? v : -1;
   }
   float gacc = 0.0f;
   // Each pass covers 8 k-steps; the next pass's row values are loaded before
@@ -272,106 +427,25 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
-// One workgroup per ROUTE_TILE tokens, 16 threads per token.  The tile's logits are staged in LDS; each
-// (token, expert) finds its rank among the token's experts -- the number of
-// experts with a larger logit, or an equal logit and a lower id -- and the
-// experts of rank < k take slot = rank.  This is the top-k of the contract
-// (logit descending, id ascending) computed without any serial reduction.
-// Then softmax over all E, optional renormalisation, and the per-expert rank
-// of each (token, slot) pair among the tile's pairs in (token, slot) order,
-// with the tile's histogram, for the bucketing kernel.
+// The tile's logits from global memory into LDS.
+__device__ __forceinline__ void route_load_logits(RouteLds& R, const float* __restrict__ logits, int t0, int nt, int E,
+                                  int tid, int nthreads) {
+  for (int i = tid; i < ROUTE_TILE * E; i += nthreads) {
+    const int tl = i / E, e = i - tl * E;
+    R.l[tl][e] = (tl < nt) ? logits[(size_t)(t0 + tl) * E + e] : 0.0f;
+  }
+}
+
+// Routing as its own kernel (E > 64: a router workgroup holds only a 64-expert
+// slice of its tokens' logits).  One workgroup per ROUTE_TILE tokens.
 __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(
     const float* __restrict__ logits, int n, int E, int k, int norm, int32_t* __restrict__ ids,
     float* __restrict__ wout, int32_t* __restrict__ rank, int32_t* __restrict__ hist) {
-  __shared__ __attribute__((aligned(16))) float s_l[ROUTE_TILE][MAX_EXPERTS + 4];
-  __shared__ __attribute__((aligned(16))) int s_ids[ROUTE_TILE * MAX_TOPK];
-  __shared__ float s_val[ROUTE_TILE][MAX_TOPK];
-  __shared__ int s_cnt[MAX_EXPERTS];
-  const int tid = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) RouteLds R;
   const int t0 = blockIdx.x * ROUTE_TILE;
   const int nt = min(ROUTE_TILE, n - t0);
-  for (int i = tid; i < ROUTE_TILE * E; i += ROUTE_THREADS) {
-    const int tl = i / E, e = i - tl * E;
-    s_l[tl][e] = (tl < nt) ? logits[(size_t)(t0 + tl) * E + e] : 0.0f;
-  }
-  if (E & 3)  // pad each row to a multiple of 4 with -inf
-    for (int i = tid; i < ROUTE_TILE * 4; i += ROUTE_THREADS) {
-      const int tl = i >> 2, e = E + (i & 3);
-      if (e < ((E + 3) & ~3)) s_l[tl][e] = -__builtin_huge_valf();
-    }
-  for (int e = tid; e < E; e += ROUTE_THREADS) s_cnt[e] = 0;
-  __syncthreads();
-
-  // ranks: thread (token tl = tid/16, expert group g = tid%16) owns experts g + 16c
-  const int tl = tid >> 4, g = tid & 15;
-  const int E4 = (E + 3) & ~3;  // logits row padded to 4 with -inf (never outranks)
-  for (int e = g; e < E; e += 16) {
-    const float le = s_l[tl][e];
-    int r = 0;
-#pragma unroll 4
-    for (int e2 = 0; e2 < E4; e2 += 4) {
-      const float4 l4 = *reinterpret_cast<const float4*>(&s_l[tl][e2]);
-      r += (l4.x > le || (l4.x == le && e2 + 0 < e)) ? 1 : 0;
-      r += (l4.y > le || (l4.y == le && e2 + 1 < e)) ? 1 : 0;
-      r += (l4.z > le || (l4.z == le && e2 + 2 < e)) ? 1 : 0;
-      r += (l4.w > le || (l4.w == le && e2 + 3 < e)) ? 1 : 0;
-    }
-    if (r < k) {
-      s_ids[tl * MAX_TOPK + r] = e;
-      s_val[tl][r] = le;
-    }
-  }
-  __syncthreads();
-
-  // softmax over all E (the 16 threads of a token share the sum), weights of the k slots
-  const float m = s_val[tl][0];
-  float part = 0.0f;
-  for (int e = g; e < E; e += 16) part += expf(s_l[tl][e] - m);
-#pragma unroll
-  for (int off = 8; off > 0; off >>= 1) part += __shfl_xor(part, off, 16);
-  float p = (g < k) ? expf(s_val[tl][min(g, k - 1)] - m) / part : 0.0f;
-  if (norm) {
-    float sum = p;
-#pragma unroll
-    for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 16);
-    p = p / sum;
-  }
-  if (tl < nt && g < k) {
-    ids[(size_t)(t0 + tl) * k + g] = s_ids[tl * MAX_TOPK + g];
-    wout[(size_t)(t0 + tl) * k + g] = p;
-  }
-
-  // rank of pair q = (token, slot) among the tile's earlier pairs of the same expert
-  const int np = nt * k;
-  if (tid < np) {
-    const int q = tid;
-    const int e = s_ids[(q / k) * MAX_TOPK + q % k];
-    int r = 0;
-    bool last = true;
-    // pairs of earlier tokens (all their k slots), then this token's earlier slots
-    for (int t2 = 0; t2 < nt; ++t2) {
-      const int4* row = reinterpret_cast<const int4*>(&s_ids[t2 * MAX_TOPK]);
-#pragma unroll
-      for (int c4 = 0; c4 < MAX_TOPK / 4; ++c4) {
-        if (4 * c4 >= k) break;
-        const int4 v = row[c4];
-        const int ev[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int s2 = 4 * c4 + u;
-          if (s2 < k && ev[u] == e) {
-            const int q2 = t2 * k + s2;
-            r += (q2 < q) ? 1 : 0;
-            if (q2 > q) last = false;
-          }
-        }
-      }
-    }
-    rank[(size_t)(t0 + q / k) * k + q % k] = r;
-    if (last) s_cnt[e] = r + 1;
-  }
-  __syncthreads();
-  for (int e = tid; e < E; e += ROUTE_THREADS) hist[(size_t)blockIdx.x * E + e] = s_cnt[e];
+  route_load_logits(R, logits, t0, nt, E, threadIdx.x, ROUTE_THREADS);
+  route_tile(R, blockIdx.x, t0, nt, E, k, norm, threadIdx.x, ROUTE_THREADS, ids, wout, rank, hist);
 }
 
 __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ v, int64_t n_values,
@@ -394,7 +468,18 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
 hipError_t launch_router(const float* x, int n, int d, const float* wt, const float* bias, int E,
                          int E64, float* logits, hipStream_t s) {
   dim3 grid((unsigned)((n + 4 * RT - 1) / (4 * RT)), (unsigned)(E64 / 64));
-  router_kernel<<<grid, 256, 0, s>>>(x, n, d, wt, bias, E, E64, logits);
+  router_kernel<false><<<grid, 256, 0, s>>>(x, n, d, wt, bias, E, E64, logits, 0, 0, nullptr,
+                                            nullptr, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_route(const float* x, int n, int d, const float* wt, const float* bias,
+                               int E, int k, int norm, int32_t* ids, float* w, int32_t* rank,
+                               int32_t* hist, hipStream_t s) {
+  if (E > 64) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((n + ROUTE_TILE - 1) / ROUTE_TILE), 1);
+  router_kernel<true><<<grid, 256, 0, s>>>(x, n, d, wt, bias, E, 64, nullptr, k, norm, ids, w, rank,
+                                           hist);
   return hipGetLastError();
 }
 
