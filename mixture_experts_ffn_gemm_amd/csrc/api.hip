@@ -60,6 +60,16 @@ WsLayout ws_layout(const Dims& dm, int max_tokens) {
   L.hq = take(t32 * kbmax * 1024);
   L.hs = take(t32 * 32 * kbmax * 2);
   L.partial = take(Nn * kk * dm.d * 4);
+  if (max_tokens >= 1 && max_tokens <= DECODE_MAX_TOKENS) {
+    const size_t nb = std::min((size_t)dm.E, Nn * dm.k) + dm.has_shared;
+    L.dlist = take((4 + DLIST_ENTRY * nb) * 4);
+    L.dxq = take(Nn * dm.d_pad);
+    L.dxs = take(Nn * (dm.d_pad / QB) * 2);
+    L.dhq = take(Nn * kk * dm.kmax_pad);
+    L.dhs = take(Nn * kk * (dm.kmax_pad / QB) * 2);
+  } else {
+    L.dlist = L.dxq = L.dxs = L.dhq = L.dhs = off;
+  }
   L.total = off;
   return L;
 }
@@ -115,6 +125,29 @@ int current_device_matches(const moe_ffn_weights* w) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return MOE_FFN_HIP_ERROR;
   return dev == w->device ? MOE_FFN_OK : MOE_FFN_INVALID_ARG;
+}
+
+// The optional routing outputs of a call (device-to-device copies on s).
+hipError_t copy_routing(const Dims& dm, int n, const moe_ffn_routing* r, const int32_t* ids,
+                        const float* w, const float* gs, const int32_t* exp_start,
+                        const int32_t* tok_i, const int32_t* tok_k, const float* partial,
+                        hipStream_t s) {
+  if (!r) return hipSuccess;
+  const int kk = dm.k + dm.has_shared;
+  const size_t nk = (size_t)n * dm.k;
+  const size_t ptot = nk + (dm.has_shared ? (size_t)n : 0);
+  hipError_t e = hipSuccess;
+  auto cp = [&](void* dst, const void* src, size_t bytes) {
+    if (e == hipSuccess && dst) e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
+  };
+  cp(r->topk_ids, ids, nk * 4);
+  cp(r->topk_w, w, nk * 4);
+  if (dm.has_shared) cp(r->shared_gate, gs, (size_t)n * 4);
+  cp(r->exp_start, exp_start, (size_t)(dm.E + 1 + dm.has_shared) * 4);
+  cp(r->exp_tok_i, tok_i, ptot * 4);
+  cp(r->exp_tok_k, tok_k, ptot * 4);
+  cp(r->partial, partial, (size_t)n * kk * dm.d * 4);
+  return e;
 }
 
 int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, void* ws,
@@ -206,21 +239,84 @@ int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, v
   HIP_TRY(launch_combine(partial, w, dm.has_shared ? gs : nullptr, n, dm.k, kk, dm.d, out, s));
   HIP_TRY(mark(6));
 
-  if (r) {
-    const size_t nk = (size_t)n * dm.k;
-    const size_t ptot = nk + (dm.has_shared ? (size_t)n : 0);
-    if (r->topk_ids) HIP_TRY(hipMemcpyAsync(r->topk_ids, ids, nk * 4, hipMemcpyDeviceToDevice, s));
-    if (r->topk_w) HIP_TRY(hipMemcpyAsync(r->topk_w, w, nk * 4, hipMemcpyDeviceToDevice, s));
-    if (r->shared_gate && dm.has_shared)
-      HIP_TRY(hipMemcpyAsync(r->shared_gate, gs, (size_t)n * 4, hipMemcpyDeviceToDevice, s));
-    if (r->exp_start)
-      HIP_TRY(hipMemcpyAsync(r->exp_start, exp_start, (size_t)(dm.E + 1 + dm.has_shared) * 4,
+  HIP_TRY(copy_routing(dm, n, r, ids, w, gs, exp_start, tok_i, tok_k, partial, s));
+  return MOE_FFN_OK;
+}
+
+
+// Decode (1 <= n <= DECODE_MAX_TOKENS): router chains spread over the chip
+// (plus the token-major quantiser), one-workgroup routing that also lists the
+// active groups, the two gathered matvec launches over that list, and the
+// ordered combine (#408 "Hypothesis" levers 1 and 3).
+int run_decode(const moe_ffn_weights* W, const float* x, int32_t n, float* out, void* ws,
+               size_t ws_bytes, const moe_ffn_routing* r, hipStream_t s) {
+  if (!W || n < 1 || n > DECODE_MAX_TOKENS) return MOE_FFN_INVALID_ARG;
+  if (!x || !out || !ws) return MOE_FFN_INVALID_ARG;
+  const Dims& dm = W->dm;
+  const WsLayout L = ws_layout(dm, n);
+  if (ws_bytes < L.total) return MOE_FFN_WORKSPACE_TOO_SMALL;
+  if (((uintptr_t)ws & 255u) || ((uintptr_t)x & 15u) || ((uintptr_t)out & 15u))
+    return MOE_FFN_INVALID_ARG;
+  const size_t xb = (size_t)n * dm.d * sizeof(float);
+  if (overlaps(x, xb, out, xb) || overlaps(out, xb, ws, ws_bytes)) return MOE_FFN_INVALID_ARG;
+  if (r && r->xq && ((uintptr_t)r->xq & 15u)) return MOE_FFN_INVALID_ARG;
+  const int dev_ok = current_device_matches(W);
+  if (dev_ok != MOE_FFN_OK) return dev_ok;
+
+  char* base = (char*)ws;
+  float* logits = (float*)(base + L.logits);
+  int32_t* ids = (int32_t*)(base + L.ids);
+  int32_t* rank = (int32_t*)(base + L.rank);
+  float* w = (float*)(base + L.w);
+  float* gs = (float*)(base + L.gs);
+  int32_t* hist = (int32_t*)(base + L.hist);
+  int32_t* exp_start = (int32_t*)(base + L.exp_start);
+  int32_t* tok_i = (int32_t*)(base + L.tok_i);
+  int32_t* tok_k = (int32_t*)(base + L.tok_k);
+  int32_t* dlist = (int32_t*)(base + L.dlist);
+  int8_t* dxq = (int8_t*)(base + L.dxq);
+  uint16_t* dxs = (uint16_t*)(base + L.dxs);
+  float* partial = (float*)(base + L.partial);
+  const int kk = dm.k + dm.has_shared;
+
+  HIP_TRY(launch_decode_router(x, n, dm.d, dm.d_pad, W->router_wt, W->has_bias ? W->router_bias : nullptr,
+                               dm.E, dm.E64, logits, dm.has_shared ? W->sh_gate_vec : nullptr, gs, dxq,
+                               dxs, s));
+  HIP_TRY(launch_decode_route(logits, n, dm.E, dm.k, dm.norm, dm.has_shared, ids, w, rank, hist,
+                              exp_start, tok_i, tok_k, dlist, s));
+  DecodeArgs a{};
+  a.dlist = dlist;
+  a.E = dm.E;
+  a.kk = kk;
+  a.n_bound = std::min(dm.E, n * dm.k) + dm.has_shared;
+  a.xq = dxq;
+  a.xs = dxs;
+  a.gu = W->gu;
+  a.gu_group = W->gu_per_expert;
+  a.sh_gu = W->sh_gu;
+  a.d = dm.d;
+  a.d_pad = dm.d_pad;
+  a.F_pad = dm.F_pad;
+  a.Fs_pad = dm.Fs_pad;
+  a.kmax_pad = dm.kmax_pad;
+  a.hq = (int8_t*)(base + L.dhq);
+  a.hs = (uint16_t*)(base + L.dhs);
+  a.dn = W->dn;
+  a.dn_group = W->dn_per_expert;
+  a.sh_dn = W->sh_dn;
+  a.dn_exp = W->dn_exp;
+  a.partial = partial;
+  HIP_TRY(launch_decode_gateup(a, s));
+  HIP_TRY(launch_decode_down(a, s));
+  HIP_TRY(launch_combine(partial, w, dm.has_shared ? gs : nullptr, n, dm.k, kk, dm.d, out, s));
+
+  HIP_TRY(copy_routing(dm, n, r, ids, w, gs, exp_start, tok_i, tok_k, partial, s));
+  if (r && r->xq)
+    HIP_TRY(hipMemcpy2DAsync(r->xq, (size_t)dm.d, dxq, (size_t)dm.d_pad, (size_t)dm.d, (size_t)n,
                              hipMemcpyDeviceToDevice, s));
-    if (r->exp_tok_i) HIP_TRY(hipMemcpyAsync(r->exp_tok_i, tok_i, ptot * 4, hipMemcpyDeviceToDevice, s));
-    if (r->exp_tok_k) HIP_TRY(hipMemcpyAsync(r->exp_tok_k, tok_k, ptot * 4, hipMemcpyDeviceToDevice, s));
-    if (r->partial)
-      HIP_TRY(hipMemcpyAsync(r->partial, partial, (size_t)n * kk * dm.d * 4, hipMemcpyDeviceToDevice, s));
-  }
+  if (r && r->xs)
+    HIP_TRY(hipMemcpy2DAsync(r->xs, (size_t)(dm.d / QB) * 2, dxs, (size_t)(dm.d_pad / QB) * 2,
+                             (size_t)(dm.d / QB) * 2, (size_t)n, hipMemcpyDeviceToDevice, s));
   return MOE_FFN_OK;
 }
 
@@ -366,8 +462,7 @@ int moe_ffn_prefill_profiled(const moe_ffn_weights* w, const float* x, int32_t n
 
 int moe_ffn_decode(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* out, void* ws,
                    size_t ws_bytes, const moe_ffn_routing* routing, hipStream_t stream) {
-  if (n_tokens < 1 || n_tokens > DECODE_MAX_TOKENS) return MOE_FFN_INVALID_ARG;
-  return run_layer(w, x, n_tokens, out, ws, ws_bytes, routing, stream);
+  return run_decode(w, x, n_tokens, out, ws, ws_bytes, routing, stream);
 }
 
 int moe_ffn_combine(const float* partial, const float* topk_w, const float* shared_gate, int32_t n,

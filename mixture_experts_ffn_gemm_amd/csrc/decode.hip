@@ -1,0 +1,338 @@
+// decode.hip -- the decode-time expert matvecs (1 <= N <= 8 tokens).
+//
+// SharpInference #408 "Hypothesis" lever 1: at decode the expert FFN is eight
+// small matvecs per token, launched one by one; the lever is one gathered
+// launch per stage over the selected experts, each expert's weights read once
+// for all the tokens that picked it.  With at most 8 rows per expert the
+// grouped GEMM's 32-row MFMA tiles would be mostly padding and its per-tile
+// prologue dominates, so these kernels are matvecs on the int8 dot unit
+// (v_dot4_i32_i8) that stream the weights straight into registers:
+//
+// * Unit of work: one active group (from the decode routing list) and 32
+//   output columns: a gate/up unit is one SwiGLU block of 32 h columns (gate
+//   tile + up tile of the same strip), a down unit two 32-row tiles of the
+//   down matrix.  Both read the planes the grouped GEMMs read (no second copy
+//   of the weights): per k-step 8 chunks of 1 KiB, lane l holding row l%32 and
+//   codes [16 (l/32), +16) of each 32-block.
+// * The 8 wavefronts of a workgroup split the k-steps (wavefront w takes
+//   k-steps w and w+8 of each pass of 16), requesting both before it waits
+//   for either: a workgroup has its whole 128 KiB share in flight at once.  The group's activation rows (<= 8) are staged in LDS
+//   per pass of up to DPK k-steps; a lane reads its 16 codes of each block
+//   there (two distinct addresses per read: a broadcast).
+// * Per block, row and token: exact int32 dot of the lane's 16 codes, then
+//   acc += float(dot) * (sw * sa), where sw * sa is exact in fp32 (two
+//   binary16 values).  The two half-block partial sums of a row meet in the
+//   final reduction (over the lane pair, then the 8 wavefronts in order).
+// * Gate/up epilogue: h = silu(gate) * up and its per-32 requantisation
+//   (the decisions of quant_block32, one block per token) into the pair's h
+//   row; down epilogue: times 2^(e - 23) (the down plane stores W =
+//   sw * 2^(23 - e)) into partial[pair].
+#include "device_util.h"
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int DW = 8;                  // wavefronts per workgroup
+constexpr int DPK = 16;                // k-steps per staged activation pass
+constexpr int ACT_BYTES = DECODE_MAX_TOKENS * DPK * 128;            // 16 KiB of codes
+constexpr int ACS_BYTES = DECODE_MAX_TOKENS * DPK * KSTEP * 2;      // 1 KiB of scales
+constexpr int RED_BYTES = DW * 2 * DECODE_MAX_TOKENS * 32 * 4;      // 16 KiB reduction
+constexpr int DEC_LDS = (ACT_BYTES + ACS_BYTES > RED_BYTES) ? ACT_BYTES + ACS_BYTES : RED_BYTES;
+
+// One k-step of a unit for this lane: codes of blocks kbi = 0..3 for the two
+// tiles, and the scales of the lane's row in both tiles (gate/up: 4 binary16
+// scales per tile; down: two {W, W/2} pair words per tile, blocks 0-1 and 2-3).
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+struct Piece {
+  v4u w[KSTEP][2];
+  v2u s[2][2];
+};
+
+// The weights are read with buffer loads: one resource over the unit's strip
+// (SGPRs), the per-chunk byte offset in an SGPR and the lane's offset in one
+// VGPR that never changes, so no load ever waits to reuse an address register
+// of a load still in flight (with 64-bit VGPR addresses the second k-step's
+// loads did).  The range check is off (num_records = 2^32 - 1): every offset
+// is inside the strip by construction.
+constexpr int BUF_DWORD3 = 0x00020000;  // raw buffer, 32-bit data format
+
+template <bool GATEUP>
+__device__ __forceinline__ void load_piece(__amdgpu_buffer_rsrc_t rs, int step_off, int tsel0, int tstride,
+                                           uint32_t o_code, uint32_t o_scale, Piece& p) {
+#pragma unroll
+  for (int kbi = 0; kbi < KSTEP; ++kbi)
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+      p.w[kbi][ti] = __builtin_amdgcn_raw_buffer_load_b128(rs, o_code, step_off + (kbi * 4 + tsel0 + tstride * ti) * 1024, 0);
+    }
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti) {
+    const int tt = tsel0 + tstride * ti;
+    if constexpr (GATEUP) {
+      p.s[ti][0] = __builtin_amdgcn_raw_buffer_load_b64(rs, o_scale, step_off + 16 * 1024 + tt * 256, 0);
+      p.s[ti][1] = p.s[ti][0];
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        p.s[ti][h] = __builtin_amdgcn_raw_buffer_load_b64(rs, o_scale, step_off + 16 * 1024 + tt * 512 + h * 256, 0);
+      }
+    }
+  }
+}
+
+// Force the arguments a kernel uses into SGPRs at this point (the entry
+// block), in one statement, so that they are fetched as one batch of scalar
+// loads.
+template <bool GATEUP>
+__device__ __forceinline__ void pin_args(const DecodeArgs& a) {
+  // input operands only: the code below keeps using the fields themselves
+  if constexpr (GATEUP)
+    asm volatile("" ::"s"(a.dlist), "s"(a.E), "s"(a.kk), "s"(a.n_bound), "s"(a.xq), "s"(a.xs), "s"(a.gu),
+                 "s"(a.gu_group), "s"(a.sh_gu), "s"(a.d_pad), "s"(a.F_pad), "s"(a.Fs_pad), "s"(a.kmax_pad),
+                 "s"(a.hq), "s"(a.hs));
+  else
+    asm volatile("" ::"s"(a.dlist), "s"(a.E), "s"(a.n_bound), "s"(a.d), "s"(a.d_pad), "s"(a.F_pad),
+                 "s"(a.Fs_pad), "s"(a.kmax_pad), "s"(a.hq), "s"(a.hs), "s"(a.dn), "s"(a.dn_group),
+                 "s"(a.sh_dn), "s"(a.dn_exp), "s"(a.partial));
+}
+
+// The rows' pairs live in lanes 0..7 of one register (written lane by lane),
+// so a per-lane row index selects one with a cross-lane read: no indexed
+// private array, which the compiler would otherwise place in LDS.
+template <int J>
+__device__ __forceinline__ void write_lane(int& tbl, int v) {
+  asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(tbl) : "s"(v), "n"(J));
+}
+__device__ __forceinline__ int pairs_table(const int (&ev)[DLIST_ENTRY], int c) {
+  int tbl = 0;
+  write_lane<0>(tbl, ev[DLIST_PAIRS]);
+  write_lane<1>(tbl, 1 < c ? ev[DLIST_PAIRS + 1] : ev[DLIST_PAIRS]);
+  write_lane<2>(tbl, 2 < c ? ev[DLIST_PAIRS + 2] : ev[DLIST_PAIRS]);
+  write_lane<3>(tbl, 3 < c ? ev[DLIST_PAIRS + 3] : ev[DLIST_PAIRS]);
+  write_lane<4>(tbl, 4 < c ? ev[DLIST_PAIRS + 4] : ev[DLIST_PAIRS]);
+  write_lane<5>(tbl, 5 < c ? ev[DLIST_PAIRS + 5] : ev[DLIST_PAIRS]);
+  write_lane<6>(tbl, 6 < c ? ev[DLIST_PAIRS + 6] : ev[DLIST_PAIRS]);
+  write_lane<7>(tbl, 7 < c ? ev[DLIST_PAIRS + 7] : ev[DLIST_PAIRS]);
+  return tbl;
+}
+__device__ __forceinline__ int pick(int tbl, int j) { return __shfl(tbl, j, 64); }
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+  return __half2float(__ushort_as_half((uint16_t)(bits16 & 0xffffu)));
+}
+
+// The piece's contribution for every staged row j < c: act = the k-step's
+// 128 codes of the staged rows (row stride DPK * 128), as = their scales.
+template <bool GATEUP>
+__device__ __forceinline__ void compute_piece(const Piece& p, const int8_t* act, const uint16_t* as, int c,
+                                              int lane, float (&acc)[2][DECODE_MAX_TOKENS]) {
+  float sw[2][KSTEP];
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti) {
+    if constexpr (GATEUP) {
+      sw[ti][0] = h2f(p.s[ti][0][0]);
+      sw[ti][1] = h2f(p.s[ti][0][0] >> 16);
+      sw[ti][2] = h2f(p.s[ti][0][1]);
+      sw[ti][3] = h2f(p.s[ti][0][1] >> 16);
+    } else {  // W of blocks 2h, 2h+1: the low halves of the two pair words
+      sw[ti][0] = h2f(p.s[ti][0][0]);
+      sw[ti][1] = h2f(p.s[ti][0][1]);
+      sw[ti][2] = h2f(p.s[ti][1][0]);
+      sw[ti][3] = h2f(p.s[ti][1][1]);
+    }
+  }
+  const int half = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < DECODE_MAX_TOKENS; ++j) {
+    if (j < c) {  // workgroup-uniform
+      const int8_t* arow = act + j * (DPK * 128) + half * 16;
+      uint4 av[KSTEP];
+#pragma unroll
+      for (int kbi = 0; kbi < KSTEP; ++kbi) av[kbi] = *reinterpret_cast<const uint4*>(arow + kbi * 32);
+      const uint2 s2 = *reinterpret_cast<const uint2*>(as + j * (DPK * KSTEP));
+      const float sa[KSTEP] = {h2f(s2.x), h2f(s2.x >> 16), h2f(s2.y), h2f(s2.y >> 16)};
+#pragma unroll
+      for (int kbi = 0; kbi < KSTEP; ++kbi)
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti) {
+          const v4u wv = p.w[kbi][ti];
+          int dot = __builtin_amdgcn_sdot4((int)wv[0], (int)av[kbi].x, 0, false);
+          dot = __builtin_amdgcn_sdot4((int)wv[1], (int)av[kbi].y, dot, false);
+          dot = __builtin_amdgcn_sdot4((int)wv[2], (int)av[kbi].z, dot, false);
+          dot = __builtin_amdgcn_sdot4((int)wv[3], (int)av[kbi].w, dot, false);
+          acc[ti][j] = __builtin_fmaf((float)dot, sw[ti][kbi] * sa[kbi], acc[ti][j]);
+        }
+    }
+  }
+}
+
+// GATEUP: unit u = (strip u/2, tile pair u%2) of the [gate;up] plane, columns
+// 32u .. 32u+31 of h.  !GATEUP: unit u = (strip u/2, tiles 2(u%2), 2(u%2)+1)
+// of the down plane, output rows 64u .. 64u+63.
+template <bool GATEUP>
+__global__ __launch_bounds__(DW * 64) void decode_gemv_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[DEC_LDS];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Start-up latency is the cost that matters for a kernel of one workgroup
+  // per CU: every argument is requested at once (one scalar round trip, not
+  // one per branch that first needs a field), then the list count and this
+  // workgroup's whole entry together (entry ei < n_bound always lies inside
+  // the list; it is only used once ei < count is known).
+  pin_args<GATEUP>(a);
+  const int units = GATEUP ? a.kmax_pad / 32 : a.d_pad / 64;
+  const int ei = (int)blockIdx.x / units, u = (int)blockIdx.x - ei * units;
+  const int32_t* ent = a.dlist + 4 + DLIST_ENTRY * ei;
+  int n_act = __builtin_amdgcn_readfirstlane(a.dlist[0]);
+  int ev[DLIST_ENTRY];
+#pragma unroll
+  for (int i = 0; i < DLIST_ENTRY; ++i) ev[i] = __builtin_amdgcn_readfirstlane(ent[i]);
+  asm volatile("" ::"s"(n_act), "s"(ev[0]), "s"(ev[1]), "s"(ev[2]), "s"(ev[3]), "s"(ev[4]), "s"(ev[5]),
+               "s"(ev[6]), "s"(ev[7]), "s"(ev[8]), "s"(ev[9]), "s"(ev[10]), "s"(ev[11]), "s"(ev[12]),
+               "s"(ev[13]), "s"(ev[14]), "s"(ev[15]));
+  if (ei >= min(n_act, a.n_bound)) return;
+  const int g = ev[0];
+  const int c = min(max(ev[1], 1), DECODE_MAX_TOKENS);
+  if (g < 0 || g > a.E) return;
+  const bool shared = g == a.E;
+  if (shared && !(GATEUP ? a.sh_gu : a.sh_dn)) return;
+  const int Fg_pad = shared ? a.Fs_pad : a.F_pad;
+  if (GATEUP && u * 32 >= Fg_pad) return;
+  const int pr = pairs_table(ev, c);  // the rows' (token, slot) pairs (clamped past c)
+
+  const int KS = (GATEUP ? a.d_pad : Fg_pad) / (KSTEP * QB);
+  const int step_bytes = GATEUP ? KSTEP_BYTES : DN_KSTEP_BYTES;
+  const uint8_t* plane = GATEUP ? (shared ? a.sh_gu : a.gu + (size_t)g * a.gu_group)
+                                : (shared ? a.sh_dn : a.dn + (size_t)g * a.dn_group);
+  plane += (size_t)(u >> 1) * KS * step_bytes;
+  const int tsel0 = GATEUP ? (u & 1) : 2 * (u & 1);  // first tile; the second is +2 (up) or +1
+  const int tstride = GATEUP ? 2 : 1;
+  const uint32_t o_code = (uint32_t)lane * 16, o_scale = (uint32_t)(lane & 31) * 8;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(plane), (short)0, -1, BUF_DWORD3);
+
+  int8_t* s_act = reinterpret_cast<int8_t*>(lds);
+  uint16_t* s_as = reinterpret_cast<uint16_t*>(lds + ACT_BYTES);
+  float acc[2][DECODE_MAX_TOKENS];
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+    for (int j = 0; j < DECODE_MAX_TOKENS; ++j) acc[ti][j] = 0.0f;
+
+  // Per pass of DPK = 2 * DW k-steps, wavefront w computes k-steps ks0 + w and
+  // ks0 + w + DW; both are requested before the activations are staged, so
+  // each wavefront has its whole share of the pass in flight at once.
+  static_assert(DPK == 2 * DW, "two k-steps per wavefront and pass");
+  static_assert(DECODE_MAX_TOKENS * DPK * 8 <= 2 * DW * 64, "two 16-byte activation pieces per thread");
+  static_assert(DECODE_MAX_TOKENS * DPK <= DW * 64, "one scale word per thread");
+  auto pass = [&](int ks0) {
+    const int ks_end = min(ks0 + DPK, KS), npk = ks_end - ks0;
+    const int k0 = ks0 + wave, k1 = ks0 + wave + DW;
+    // The pass's activation rows (codes [j][npk * 128], scales [j][npk * 4];
+    // at most 2 x 512 16-byte pieces and 128 scale words) are requested
+    // first: they hit in the caches, and waiting for them then does not wait
+    // for the weights requested after them.  Addresses are clamped into the
+    // rows (unconditional loads), the LDS writes masked.
+    const int nq = c * npk * 8, ns = c * npk;
+    auto code_src = [&](int q) {
+      q = min(q, nq - 1);
+      const int j = q / (npk * 8), o = q - j * (npk * 8);
+      const int prj = pick(pr, j);
+      return GATEUP ? reinterpret_cast<const uint4*>(a.xq + (size_t)(prj / a.kk) * a.d_pad + ks0 * 128) + o
+                    : reinterpret_cast<const uint4*>(a.hq + (size_t)prj * a.kmax_pad + ks0 * 128) + o;
+    };
+    const int q0 = threadIdx.x, q1 = threadIdx.x + DW * 64;
+    const uint4 c0 = *code_src(q0), c1 = *code_src(q1);
+    const int qs = min((int)threadIdx.x, ns - 1), js = qs / npk, os = qs - js * npk;
+    const int prs = pick(pr, js);
+    const uint2 sv = GATEUP
+        ? reinterpret_cast<const uint2*>(a.xs + (size_t)(prs / a.kk) * (a.d_pad / QB) + ks0 * KSTEP)[os]
+        : reinterpret_cast<const uint2*>(a.hs + (size_t)prs * (a.kmax_pad / QB) + ks0 * KSTEP)[os];
+    // both k-steps requested unconditionally (a k-step past the pass re-reads
+    // the pass's last one and is not computed): no branch between requests
+    Piece p0, p1;
+    load_piece<GATEUP>(rs, min(k0, ks_end - 1) * step_bytes, tsel0, tstride, o_code, o_scale, p0);
+    load_piece<GATEUP>(rs, min(k1, ks_end - 1) * step_bytes, tsel0, tstride, o_code, o_scale, p1);
+    __builtin_amdgcn_sched_barrier(0);  // every request is out before any wait
+    if (ks0 > 0) lds_barrier();  // every wavefront is done with the previous pass
+    if (q0 < nq) reinterpret_cast<uint4*>(s_act + (q0 / (npk * 8)) * (DPK * 128))[q0 % (npk * 8)] = c0;
+    if (q1 < nq) reinterpret_cast<uint4*>(s_act + (q1 / (npk * 8)) * (DPK * 128))[q1 % (npk * 8)] = c1;
+    if ((int)threadIdx.x < ns) reinterpret_cast<uint2*>(s_as + js * (DPK * KSTEP))[os] = sv;
+    lds_barrier();
+    if (k0 < ks_end) compute_piece<GATEUP>(p0, s_act + (k0 - ks0) * 128, s_as + (k0 - ks0) * KSTEP, c, lane, acc);
+    if (k1 < ks_end) compute_piece<GATEUP>(p1, s_act + (k1 - ks0) * 128, s_as + (k1 - ks0) * KSTEP, c, lane, acc);
+  };
+  // One pass (K <= 2048) has its own straight-line copy: inside a loop the
+  // second k-step's loads would wait for the first's (the compiler cannot
+  // tell that no load of a previous pass is still pending into them).
+  if (KS <= DPK) {
+    pass(0);
+  } else {
+    for (int ks0 = 0; ks0 < KS; ks0 += DPK) pass(ks0);
+  }
+
+  // Reduction: the lane pair (two halves of each block), then the wavefronts
+  // in order.  red[w][ti][j][r].
+  __syncthreads();  // the staging buffers are reused
+  float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+    for (int j = 0; j < DECODE_MAX_TOKENS; ++j) {
+      if (j < c) {
+        const float v = acc[ti][j] + __shfl_xor(acc[ti][j], 32, 64);
+        if (lane < 32) red[((wave * 2 + ti) * DECODE_MAX_TOKENS + j) * 32 + lane] = v;
+      }
+    }
+  __syncthreads();
+  if constexpr (GATEUP) {
+    // thread (j = tid / 32, r = tid % 32): column 32u + r of h for row j
+    const int tid = threadIdx.x;
+    if (tid >= DECODE_MAX_TOKENS * 32) return;
+    const int j = tid >> 5, r = tid & 31;
+    if (j >= c) return;  // half-wavefront-uniform: the quantiser's exchanges stay inside
+    float gv = 0.0f, uv = 0.0f;
+#pragma unroll
+    for (int w = 0; w < DW; ++w) {
+      gv += red[((w * 2 + 0) * DECODE_MAX_TOKENS + j) * 32 + r];
+      uv += red[((w * 2 + 1) * DECODE_MAX_TOKENS + j) * 32 + r];
+    }
+    const float h = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+    int8_t q;
+    uint16_t s16;
+    quant_block32(h, q, s16);
+    const int prj = pick(pr, j);
+    a.hq[(size_t)prj * a.kmax_pad + u * 32 + r] = q;
+    if (r == 0) a.hs[(size_t)prj * (a.kmax_pad / QB) + u] = s16;
+  } else {
+    // thread (ti, j, r): output row 64u + 32 ti + r of pair row j
+    const int tid = threadIdx.x;
+    const int ti = tid >> 8, j = (tid >> 5) & 7, r = tid & 31;
+    if (j >= c) return;
+    const int row = 64 * u + 32 * ti + r;
+    if (row >= a.d) return;
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < DW; ++w) v += red[((w * 2 + ti) * DECODE_MAX_TOKENS + j) * 32 + r];
+    const int prj = pick(pr, j);
+    const int eg = a.dn_exp[g];
+    a.partial[(size_t)prj * a.d + row] = ldexpf(v, eg - 23);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_gateup(const DecodeArgs& a, hipStream_t s) {
+  const long wgs = (long)a.n_bound * (a.kmax_pad / 32);
+  decode_gemv_kernel<true><<<(unsigned)wgs, DW * 64, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s) {
+  const long wgs = (long)a.n_bound * (a.d_pad / 64);
+  decode_gemv_kernel<false><<<(unsigned)wgs, DW * 64, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -41,6 +41,16 @@
 //   hq int8 [4*T_bound][KBMAX/4][32][128], hs fp16 [4*T_bound][KBMAX/4][32][4]
 //                               (the same for h, the down GEMM's A operand);
 //   partial fp32 [N][k + has_shared][d].
+// Decode (N <= DECODE_MAX_TOKENS) additionally:
+//   dlist i32 [4 + 16 * (min(E, N*k) + has_shared)]  (dlist[0] = number of
+//                               active groups; entry a = dlist + 4 + 16 a:
+//                               {group, rows c, 6 unused, pair p[8]}, where
+//                               row j < c is the (token, slot) pair
+//                               p = token * kk + slot, tokens ascending;
+//                               routed groups ascending, then the shared one);
+//   dxq int8 [N][d_pad], dxs fp16 [N][d_pad/32]   (token-major activation
+//                               codes/scales, zero past d);
+//   dhq int8 [N*kk][kmax_pad], dhs fp16 [N*kk][kmax_pad/32]  (h per pair).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -66,6 +76,8 @@ constexpr int DN_KSTEP_BYTES = 18 * 1024;  // down k-step: codes (16 KiB) + scal
 constexpr int MAX_TOPK = 16;
 constexpr int MAX_EXPERTS = 256;
 constexpr int DECODE_MAX_TOKENS = 8;
+constexpr int DLIST_ENTRY = 16;   // ints per decode active-group entry
+constexpr int DLIST_PAIRS = 8;    // offset of the pair list in an entry
 
 struct Dims {
   int d, E, k, F, Fs, norm;
@@ -79,6 +91,7 @@ inline int round_up(int v, int m) { return (v + m - 1) / m * m; }
 
 struct WsLayout {
   size_t logits, ids, rank, w, gs, hist, exp_start, tok_i, tok_k, pos, tiles, gq, gqs, hq, hs, partial;
+  size_t dlist, dxq, dxs, dhq, dhs;  // decode only (offset `total`, size 0, otherwise)
   size_t total;
   int n_route_tiles;
   int tile_bound;
@@ -176,6 +189,43 @@ struct GemmArgs {
 
 hipError_t launch_gateup(const GemmArgs& a, hipStream_t s);
 hipError_t launch_down(const GemmArgs& a, hipStream_t s);
+
+// ---- decode (1 <= N <= DECODE_MAX_TOKENS) ----
+// Router logits [N][E] (fp32 FMA chains, as launch_router), plus the
+// token-major activation codes dxq/dxs (row strides d_pad and d_pad/32, zero
+// past d) and, with sh_gate_vec != NULL, gs[t] = sigmoid(x[t] . g).
+hipError_t launch_decode_router(const float* x, int n, int d, int d_pad, const float* wt,
+                                const float* bias, int E, int E64, float* logits,
+                                const float* sh_gate_vec, float* gs, int8_t* dxq, uint16_t* dxs,
+                                hipStream_t s);
+// One workgroup: top-k, weights, ranks (as launch_route), the CSR
+// (exp_start [E+2], tok_i/tok_k [N*k + N]) and the active-group list dlist.
+hipError_t launch_decode_route(const float* logits, int n, int E, int k, int norm, int has_shared,
+                               int32_t* ids, float* w, int32_t* rank, int32_t* hist,
+                               int32_t* exp_start, int32_t* tok_i, int32_t* tok_k, int32_t* dlist,
+                               hipStream_t s);
+
+struct DecodeArgs {
+  const int32_t* dlist;
+  int E, kk, n_bound;  // n_bound: upper bound on dlist[0]
+  // gate/up: A = dxq/dxs rows of the pairs' tokens
+  const int8_t* xq;
+  const uint16_t* xs;
+  const uint8_t* gu;
+  size_t gu_group;
+  const uint8_t* sh_gu;
+  int d, d_pad, F_pad, Fs_pad, kmax_pad;
+  int8_t* hq;
+  uint16_t* hs;
+  // down: A = hq/hs rows of the pairs, output partial[pair][d]
+  const uint8_t* dn;
+  size_t dn_group;
+  const uint8_t* sh_dn;
+  const int32_t* dn_exp;
+  float* partial;
+};
+hipError_t launch_decode_gateup(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s);
 
 hipError_t launch_combine(const float* partial, const float* w, const float* gs, int n, int k,
                           int kk, int d, float* out, hipStream_t s);

@@ -289,10 +289,15 @@ __global__ __launch_bounds__(256, 1) void router_kernel(
   // next step on); every wavefront has then read all of chunk c-1, whose
   // buffer takes chunk c+RPF.
   const int CF = d / RJC;
+  // A wavefront whose tokens are all past n (small batches) computes nothing
+  // but still does its share of the copies and meets every barrier.
+  const bool busy = tw < n;  // wavefront-uniform
   wait_chunk(np - 1);  // chunks 1..np-1 were issued after chunk 0
-  load_sub(0, 0);
-  load_sub(1, 1);
-  load_sub(2, 2);
+  if (busy) {
+    load_sub(0, 0);
+    load_sub(1, 1);
+    load_sub(2, 2);
+  }
   for (int c = 0; c < CF; ++c) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -301,11 +306,13 @@ __global__ __launch_bounds__(256, 1) void router_kernel(
         wait_chunk(min(RPF - 2, C - c - 2));
         if (c + RPF < C) issue(c + RPF);
       }
-      load_sub(4 * c + q + 3, (q + 3) & 3);
-      router_fma16(acc0, acc1, xa[q], xb[q], w[q][0], w[q][1], w[q][2], w[q][3]);
+      if (busy) {
+        load_sub(4 * c + q + 3, (q + 3) & 3);
+        router_fma16(acc0, acc1, xa[q], xb[q], w[q][0], w[q][1], w[q][2], w[q][3]);
+      }
     }
   }
-  if (CF < C) {  // 32 trailing j: sub-chunks 4 CF and 4 CF + 1 (already requested)
+  if (busy && CF < C) {  // 32 trailing j: sub-chunks 4 CF and 4 CF + 1 (already requested)
     router_fma16(acc0, acc1, xa[0], xb[0], w[0][0], w[0][1], w[0][2], w[0][3]);
     router_fma16(acc0, acc1, xa[1], xb[1], w[1][0], w[1][1], w[1][2], w[1][3]);
   }
@@ -448,6 +455,249 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(
   route_tile(R, blockIdx.x, t0, nt, E, k, norm, threadIdx.x, ROUTE_THREADS, ids, wout, rank, hist);
 }
 
+// ---------------------------------------------------------------- decode
+// Decode router (1 <= N <= 8).  The logits are the same fp32 chains as
+// router_kernel's, but the batch is too small to share the router matrix
+// among many tokens, so the chains are spread over the chip instead: one
+// workgroup per 8 experts, lane 8t + i of its first wavefront running the
+// chain of (token t, expert 8 * blockIdx.x + i).  Per 256 j, the 8 experts'
+// slab (8 KiB) and the N token rows (1 KiB each) are copied into a ring of
+// LDS buffers by all four wavefronts, up to 7 chunks ahead (the whole chain
+// at d = 2048).  The workgroups past the router ones quantise one token row
+// each (the same pieces, decisions and shared-gate order as
+// quantize_scatter_kernel), writing the token-major codes the decode GEMVs
+// read.
+constexpr int DR_E = 8;                               // experts per router workgroup
+constexpr int DR_J = 256;                             // j per chunk
+constexpr int DR_NB = 8;                              // chunk buffers in the ring
+constexpr int DR_PF = DR_NB - 1;                      // chunks copied ahead
+constexpr int DR_WB = (DR_J / 4) * DR_E * 16;         // slab [quad][expert][4 j] (8 KiB)
+constexpr int DR_XROW = DR_J * 4 + 16;                // one token row, padded (bank offset)
+constexpr int DR_BUF = DR_WB + DECODE_MAX_TOKENS * DR_XROW;
+constexpr int DR_DMA = 4;                             // copies per wavefront per chunk
+static_assert(DR_NB * DR_BUF <= 160 * 1024, "decode router ring must fit in the LDS");
+static_assert(4 * DR_DMA == 8 + DECODE_MAX_TOKENS, "16 copies per chunk: 8 slab + 8 rows");
+
+// Quantise token row xr (one wavefront): pass j0 covers values [1024 j0', +1024),
+// lane l the 16 values from 16 l; codes/scales to xq_row/xs_row up to d_pad
+// (zero past d); with shg the shared-gate dot product in the prefill order.
+__device__ __forceinline__ void decode_quantize_row(const float* __restrict__ xr, int d, int d_pad,
+                                                    const float* __restrict__ shg, float* __restrict__ gs_t,
+                                                    int8_t* __restrict__ xq_row,
+                                                    uint16_t* __restrict__ xs_row, int lane) {
+  float gacc = 0.0f;
+  for (int c00 = 0; c00 < d_pad; c00 += 1024) {
+    const int c0 = c00 + lane * 16;
+    const bool valid = c0 < d;  // d % 32 == 0: a piece is all valid or all padding
+    const float* src = xr + (valid ? c0 : 0);
+    f4v a4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a4[i] = *reinterpret_cast<const f4v*>(src + 4 * i);
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[4 * i] = valid ? a4[i].x : 0.0f;
+      v[4 * i + 1] = valid ? a4[i].y : 0.0f;
+      v[4 * i + 2] = valid ? a4[i].z : 0.0f;
+      v[4 * i + 3] = valid ? a4[i].w : 0.0f;
+    }
+    uint32_t pk[4];
+    uint16_t s16;
+    quant_half_block16(v, pk, s16);
+    if (c0 < d_pad) {
+      *reinterpret_cast<uint4*>(xq_row + c0) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      if ((lane & 1) == 0) xs_row[c0 / QB] = s16;
+    }
+    if (shg && valid) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) gacc = __builtin_fmaf(v[i], shg[c0 + i], gacc);
+    }
+  }
+  if (shg) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) gacc += __shfl_xor(gacc, off, 64);
+    if (lane == 0) *gs_t = 1.0f / (1.0f + expf(-gacc));
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void decode_router_kernel(
+    const float* __restrict__ x, int n, int d, int d_pad, const float* __restrict__ wt,
+    const float* __restrict__ bias, int E, int E64, int n_rwg, float* __restrict__ logits,
+    const float* __restrict__ shg, float* __restrict__ gs, int8_t* __restrict__ xq,
+    uint16_t* __restrict__ xs) {
+  __shared__ __attribute__((aligned(1024))) char ring[DR_NB * DR_BUF];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if ((int)blockIdx.x >= n_rwg) {
+    const int t = (int)blockIdx.x - n_rwg;
+    if (wave == 0 && t < n)
+      decode_quantize_row(x + (size_t)t * d, d, d_pad, shg, gs + t, xq + (size_t)t * d_pad,
+                          xs + (size_t)t * (d_pad / QB), lane);
+    return;
+  }
+  const int C = (d + DR_J - 1) / DR_J, NQ = d / 4;
+  const uint32_t lbase = (uint32_t)(uintptr_t)(lds_char*)ring;
+  // Copy i of a chunk (wavefront w issues 4w .. 4w+3): i < 8 moves slab quads
+  // 8i .. 8i+7 (lane l: quad 8i + l/8, expert l%8; quads past d re-read the
+  // last one), i >= 8 token row i-8 (rows past n re-read row n-1; columns
+  // past d re-read the last 4).
+  auto issue = [&](int c) {
+    const uint32_t buf = lbase + (uint32_t)((c % DR_NB) * DR_BUF);
+#pragma unroll
+    for (int ii = 0; ii < DR_DMA; ++ii) {
+      const int i = wave * DR_DMA + ii;
+      if (i < 8) {
+        const int jq = min(c * (DR_J / 4) + 8 * i + (lane >> 3), NQ - 1);
+        rdma16(wt, (uint32_t)(((size_t)jq * E64 + DR_E * blockIdx.x + (lane & 7)) * 16),
+               buf + i * 1024);
+      } else {
+        const int t = min(i - 8, n - 1);
+        const int j = min(c * DR_J + 4 * lane, d - 4);
+        rdma16(x + (size_t)t * d, (uint32_t)j * 4, buf + DR_WB + (i - 8) * DR_XROW);
+      }
+    }
+  };
+  const int np = min(DR_PF, C);
+  for (int c = 0; c < np; ++c) issue(c);
+  static_assert(DR_PF * DR_DMA <= 63, "vmcnt counts at most 63 copies");
+  const int t = lane >> 3, i = lane & 7;
+  float acc = 0.0f;
+  for (int c = 0; c < C; ++c) {
+    // issued so far: chunks 0 .. min(c + DR_PF - 1, C - 1); wait for chunk c
+    switch (min(DR_PF - 1, C - 1 - c)) {
+      case 0: rwait_vm<0>(); break;
+      case 1: rwait_vm<DR_DMA>(); break;
+      case 2: rwait_vm<2 * DR_DMA>(); break;
+      case 3: rwait_vm<3 * DR_DMA>(); break;
+      case 4: rwait_vm<4 * DR_DMA>(); break;
+      case 5: rwait_vm<5 * DR_DMA>(); break;
+      default: rwait_vm<6 * DR_DMA>(); break;
+    }
+    // every wavefront's copies of chunk c have landed, and wavefront 0 has
+    // finished chunk c-1, whose buffer now takes chunk c + DR_PF
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (c + DR_PF < C) issue(c + DR_PF);
+    if (wave == 0) {
+      const char* buf = ring + (c % DR_NB) * DR_BUF;
+      const f4v* xr = reinterpret_cast<const f4v*>(buf + DR_WB + t * DR_XROW);
+      const f4v* wr = reinterpret_cast<const f4v*>(buf) + i;
+      const int nq = min(DR_J, d - c * DR_J) / 4;
+      if (nq == DR_J / 4) {
+        // groups of 8 quads, double-buffered in registers: the reads of
+        // group g+1 are in flight while the chain runs through group g
+        constexpr int GQ = 8, NG = DR_J / 4 / GQ;
+        f4v xa[2][GQ], wa[2][GQ];
+#pragma unroll
+        for (int q = 0; q < GQ; ++q) {
+          xa[0][q] = xr[q];
+          wa[0][q] = wr[q * DR_E];
+        }
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          const int b = gi & 1;
+          if (gi + 1 < NG) {
+#pragma unroll
+            for (int q = 0; q < GQ; ++q) {
+              xa[b ^ 1][q] = xr[(gi + 1) * GQ + q];
+              wa[b ^ 1][q] = wr[((gi + 1) * GQ + q) * DR_E];
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of this group's chain
+#pragma unroll
+          for (int q = 0; q < GQ; ++q) {
+            acc = __builtin_fmaf(xa[b][q].x, wa[b][q].x, acc);
+            acc = __builtin_fmaf(xa[b][q].y, wa[b][q].y, acc);
+            acc = __builtin_fmaf(xa[b][q].z, wa[b][q].z, acc);
+            acc = __builtin_fmaf(xa[b][q].w, wa[b][q].w, acc);
+          }
+        }
+      } else {
+        for (int q = 0; q < nq; ++q) {
+          const f4v xv = xr[q], wv = wr[q * DR_E];
+          acc = __builtin_fmaf(xv.x, wv.x, acc);
+          acc = __builtin_fmaf(xv.y, wv.y, acc);
+          acc = __builtin_fmaf(xv.z, wv.z, acc);
+          acc = __builtin_fmaf(xv.w, wv.w, acc);
+        }
+      }
+    }
+  }
+  const int e = DR_E * (int)blockIdx.x + i;
+  if (wave == 0 && t < n && e < E) logits[(size_t)t * E + e] = bias ? acc + bias[e] : acc;
+}
+
+// Decode routing, one workgroup for all N <= 8 tokens: route_tile (top-k,
+// weights, ranks, counts), then the CSR of the tile (expStart = exclusive scan
+// of the counts; a pair's row = expStart[e] + its rank) and the list of active
+// groups the decode GEMVs run over (routed experts with a non-zero count in
+// ascending order, then the shared expert with all N tokens).
+__global__ __launch_bounds__(256) void decode_route_kernel(
+    const float* __restrict__ logits, int n, int E, int k, int norm, int has_shared,
+    int32_t* __restrict__ ids, float* __restrict__ wout, int32_t* __restrict__ rank,
+    int32_t* __restrict__ hist, int32_t* __restrict__ exp_start, int32_t* __restrict__ tok_i,
+    int32_t* __restrict__ tok_k, int32_t* __restrict__ dlist) {
+  __shared__ __attribute__((aligned(16))) RouteLds R;
+  __shared__ int s_start[MAX_EXPERTS], s_act[MAX_EXPERTS], s_wtot[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  route_load_logits(R, logits, 0, n, E, tid, 256);
+  route_tile(R, 0, 0, n, E, k, norm, tid, 256, ids, wout, rank, hist);
+  // route_tile ends past a barrier: R.cnt holds every expert's count.  One
+  // exclusive scan gives both the CSR start (low 16 bits) and the index among
+  // the active experts (high 16 bits).
+  const int cnt = tid < E ? R.cnt[tid] : 0;
+  const int v = cnt | ((cnt > 0 ? 1 : 0) << 16);
+  int inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int up = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += up;
+  }
+  if (lane == 63) s_wtot[wave] = inc;
+  __syncthreads();
+  int pre = 0;
+  for (int w2 = 0; w2 < wave; ++w2) pre += s_wtot[w2];
+  const int ex = pre + inc - v;
+  const int n_act = (s_wtot[0] + s_wtot[1] + s_wtot[2] + s_wtot[3]) >> 16;
+  const int P = n * k, kk = k + has_shared;
+  if (tid < E) {
+    s_start[tid] = ex & 0xffff;
+    s_act[tid] = ex >> 16;
+    exp_start[tid] = ex & 0xffff;
+    if (cnt > 0) {
+      int32_t* ent = dlist + 4 + DLIST_ENTRY * (ex >> 16);
+      ent[0] = tid;
+      ent[1] = cnt;
+    }
+  }
+  if (tid == 0) {
+    exp_start[E] = P;
+    if (has_shared) exp_start[E + 1] = P + n;
+    dlist[0] = n_act + has_shared;
+  }
+  __syncthreads();
+  if (tid < P) {
+    const int t = tid / k, s = tid - (tid / k) * k;
+    const int e = R.ids[t * MAX_TOPK + s];
+    const int r = rank[tid];  // written by this thread in route_tile
+    tok_i[s_start[e] + r] = t;
+    tok_k[s_start[e] + r] = s;
+    dlist[4 + DLIST_ENTRY * s_act[e] + DLIST_PAIRS + r] = t * kk + s;
+  }
+  if (has_shared) {
+    int32_t* ent = dlist + 4 + DLIST_ENTRY * n_act;
+    if (tid == 0) {
+      ent[0] = E;
+      ent[1] = n;
+    }
+    if (tid < n) {
+      tok_i[P + tid] = tid;
+      tok_k[P + tid] = k;
+      ent[DLIST_PAIRS + tid] = tid * kk + k;
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ v, int64_t n_values,
                                                        int8_t* __restrict__ q,
                                                        uint16_t* __restrict__ scales) {
@@ -496,6 +746,27 @@ hipError_t launch_route(const float* logits, int n, int E, int k, int norm, int3
                         int32_t* rank, int32_t* hist, hipStream_t s) {
   const int tiles = (n + ROUTE_TILE - 1) / ROUTE_TILE;
   route_kernel<<<tiles, ROUTE_THREADS, 0, s>>>(logits, n, E, k, norm, ids, w, rank, hist);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_router(const float* x, int n, int d, int d_pad, const float* wt,
+                                const float* bias, int E, int E64, float* logits,
+                                const float* sh_gate_vec, float* gs, int8_t* dxq, uint16_t* dxs,
+                                hipStream_t s) {
+  if (n < 1 || n > DECODE_MAX_TOKENS) return hipErrorInvalidValue;
+  const int n_rwg = (E + DR_E - 1) / DR_E;
+  decode_router_kernel<<<n_rwg + n, 256, 0, s>>>(x, n, d, d_pad, wt, bias, E, E64, n_rwg, logits,
+                                                 sh_gate_vec, gs, dxq, dxs);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_route(const float* logits, int n, int E, int k, int norm, int has_shared,
+                               int32_t* ids, float* w, int32_t* rank, int32_t* hist,
+                               int32_t* exp_start, int32_t* tok_i, int32_t* tok_k, int32_t* dlist,
+                               hipStream_t s) {
+  if (n < 1 || n > DECODE_MAX_TOKENS || n * k > 256) return hipErrorInvalidValue;
+  decode_route_kernel<<<1, 256, 0, s>>>(logits, n, E, k, norm, has_shared, ids, w, rank, hist,
+                                        exp_start, tok_i, tok_k, dlist);
   return hipGetLastError();
 }
 

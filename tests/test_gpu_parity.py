@@ -189,6 +189,32 @@ def test_shape_edge_cases(case, n):
     check_outputs(lw, x, g)
 
 
+# Decode: the same shapes through moe_ffn_decode, plus one whose K spans
+# several staged activation passes of the decode matvecs (d and F above 2048,
+# both ragged against the 128-value k-step) and whose router chain runs past
+# the LDS ring.
+DECODE_SHAPES = SHAPES + [dict(d=4160, E=8, k=2, F=2080, Fs=96)]
+
+
+@pytest.mark.parametrize("case", range(len(DECODE_SHAPES)))
+@pytest.mark.parametrize("n", [1, 3, 8])
+def test_decode_shapes(case, n):
+    shape, lw = mw.random_shape_case(case, **DECODE_SHAPES[case])
+    x = mw.make_tokens(300 + case, n, shape.d)
+    g = run_gpu(lw, x, api="decode")
+    check_routing(lw, x, g)
+    check_outputs(lw, x, g)
+
+
+def test_decode_repeat_is_bitwise_identical():
+    lw = mw.workload_layer("tiny")
+    x = mw.make_tokens(2, 8, 128)
+    a = run_gpu(lw, x, api="decode")
+    b = run_gpu(lw, x, api="decode")
+    for key in ("out", "partial", "topk_w", "exp_tok_i", "xq", "xs"):
+        assert np.array_equal(a[key], b[key]), key
+
+
 def test_empty_batch_is_a_noop():
     from mixture_experts_ffn_gemm_amd.layer import MoeLayer
     lw = mw.workload_layer("tiny")
