@@ -245,9 +245,9 @@ int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, v
 
 
 // Decode (1 <= n <= DECODE_MAX_TOKENS): router chains spread over the chip
-// (plus the token-major quantiser), one-workgroup routing that also lists the
-// active groups, the two gathered matvec launches over that list, and the
-// ordered combine (#408 "Hypothesis" levers 1 and 3).
+// (plus the token-major quantiser), the gate/up matvec launch (which also
+// routes the tokens and lists the active groups), the down matvec launch over
+// that list, and the ordered combine (#408 "Hypothesis" levers 1 and 3).
 int run_decode(const moe_ffn_weights* W, const float* x, int32_t n, float* out, void* ws,
                size_t ws_bytes, const moe_ffn_routing* r, hipStream_t s) {
   if (!W || n < 1 || n > DECODE_MAX_TOKENS) return MOE_FFN_INVALID_ARG;
@@ -266,10 +266,8 @@ int run_decode(const moe_ffn_weights* W, const float* x, int32_t n, float* out, 
   char* base = (char*)ws;
   float* logits = (float*)(base + L.logits);
   int32_t* ids = (int32_t*)(base + L.ids);
-  int32_t* rank = (int32_t*)(base + L.rank);
   float* w = (float*)(base + L.w);
   float* gs = (float*)(base + L.gs);
-  int32_t* hist = (int32_t*)(base + L.hist);
   int32_t* exp_start = (int32_t*)(base + L.exp_start);
   int32_t* tok_i = (int32_t*)(base + L.tok_i);
   int32_t* tok_k = (int32_t*)(base + L.tok_k);
@@ -282,13 +280,22 @@ int run_decode(const moe_ffn_weights* W, const float* x, int32_t n, float* out, 
   HIP_TRY(launch_decode_router(x, n, dm.d, dm.d_pad, W->router_wt, W->has_bias ? W->router_bias : nullptr,
                                dm.E, dm.E64, logits, dm.has_shared ? W->sh_gate_vec : nullptr, gs, dxq,
                                dxs, s));
-  HIP_TRY(launch_decode_route(logits, n, dm.E, dm.k, dm.norm, dm.has_shared, ids, w, rank, hist,
-                              exp_start, tok_i, tok_k, dlist, s));
   DecodeArgs a{};
+  a.logits = logits;
+  a.n = n;
+  a.k = dm.k;
+  a.norm = dm.norm;
+  a.has_shared = dm.has_shared;
+  a.ids = ids;
+  a.w = w;
+  a.exp_start = exp_start;
+  a.tok_i = tok_i;
+  a.tok_k = tok_k;
   a.dlist = dlist;
   a.E = dm.E;
   a.kk = kk;
   a.n_bound = std::min(dm.E, n * dm.k) + dm.has_shared;
+  a.n_cu = W->n_cu;
   a.xq = dxq;
   a.xs = dxs;
   a.gu = W->gu;
@@ -344,7 +351,10 @@ int moe_ffn_weights_create(const moe_ffn_dims* dims, const float* router_w,
   W->user = *dims;
   W->dm = make_dims(dims);
   const Dims& dm = W->dm;
-  if (hipGetDevice(&W->device) != hipSuccess) {
+  if (hipGetDevice(&W->device) != hipSuccess ||
+      hipDeviceGetAttribute(&W->n_cu, hipDeviceAttributeMultiprocessorCount, W->device) != hipSuccess ||
+      W->n_cu <= 0) {
+    (void)hipGetLastError();
     delete W;
     return MOE_FFN_HIP_ERROR;
   }

@@ -8,7 +8,12 @@
 // prologue dominates, so these kernels are matvecs on the int8 dot unit
 // (v_dot4_i32_i8) that stream the weights straight into registers:
 //
-// * Unit of work: one active group (from the decode routing list) and 32
+// * Routing: the gate/up launch derives the top-k of its N tokens itself in
+//   every workgroup (from the N x E logits: a few microseconds less than a
+//   launch of its own); its workgroup 0 writes the routing outputs and the
+//   group list the down launch reads.
+// * Unit of work: one active group (routed experts ascending, then the
+//   shared expert) and 32
 //   output columns: a gate/up unit is one SwiGLU block of 32 h columns (gate
 //   tile + up tile of the same strip), a down unit two 32-row tiles of the
 //   down matrix.  Both read the planes the grouped GEMMs read (no second copy
@@ -27,6 +32,8 @@
 //   (the decisions of quant_block32, one block per token) into the pair's h
 //   row; down epilogue: times 2^(e - 23) (the down plane stores W =
 //   sw * 2^(23 - e)) into partial[pair].
+#include <algorithm>
+
 #include "device_util.h"
 #include "internal.h"
 
@@ -89,34 +96,16 @@ template <bool GATEUP>
 __device__ __forceinline__ void pin_args(const DecodeArgs& a) {
   // input operands only: the code below keeps using the fields themselves
   if constexpr (GATEUP)
-    asm volatile("" ::"s"(a.dlist), "s"(a.E), "s"(a.kk), "s"(a.n_bound), "s"(a.xq), "s"(a.xs), "s"(a.gu),
-                 "s"(a.gu_group), "s"(a.sh_gu), "s"(a.d_pad), "s"(a.F_pad), "s"(a.Fs_pad), "s"(a.kmax_pad),
-                 "s"(a.hq), "s"(a.hs));
+    asm volatile("" ::"s"(a.logits), "s"(a.n), "s"(a.k), "s"(a.has_shared), "s"(a.E), "s"(a.kk), "s"(a.xq),
+                 "s"(a.xs), "s"(a.gu), "s"(a.gu_group), "s"(a.sh_gu), "s"(a.d_pad), "s"(a.F_pad), "s"(a.Fs_pad),
+                 "s"(a.kmax_pad), "s"(a.hq), "s"(a.hs));
   else
     asm volatile("" ::"s"(a.dlist), "s"(a.E), "s"(a.n_bound), "s"(a.d), "s"(a.d_pad), "s"(a.F_pad),
                  "s"(a.Fs_pad), "s"(a.kmax_pad), "s"(a.hq), "s"(a.hs), "s"(a.dn), "s"(a.dn_group),
                  "s"(a.sh_dn), "s"(a.dn_exp), "s"(a.partial));
 }
 
-// The rows' pairs live in lanes 0..7 of one register (written lane by lane),
-// so a per-lane row index selects one with a cross-lane read: no indexed
-// private array, which the compiler would otherwise place in LDS.
-template <int J>
-__device__ __forceinline__ void write_lane(int& tbl, int v) {
-  asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(tbl) : "s"(v), "n"(J));
-}
-__device__ __forceinline__ int pairs_table(const int (&ev)[DLIST_ENTRY], int c) {
-  int tbl = 0;
-  write_lane<0>(tbl, ev[DLIST_PAIRS]);
-  write_lane<1>(tbl, 1 < c ? ev[DLIST_PAIRS + 1] : ev[DLIST_PAIRS]);
-  write_lane<2>(tbl, 2 < c ? ev[DLIST_PAIRS + 2] : ev[DLIST_PAIRS]);
-  write_lane<3>(tbl, 3 < c ? ev[DLIST_PAIRS + 3] : ev[DLIST_PAIRS]);
-  write_lane<4>(tbl, 4 < c ? ev[DLIST_PAIRS + 4] : ev[DLIST_PAIRS]);
-  write_lane<5>(tbl, 5 < c ? ev[DLIST_PAIRS + 5] : ev[DLIST_PAIRS]);
-  write_lane<6>(tbl, 6 < c ? ev[DLIST_PAIRS + 6] : ev[DLIST_PAIRS]);
-  write_lane<7>(tbl, 7 < c ? ev[DLIST_PAIRS + 7] : ev[DLIST_PAIRS]);
-  return tbl;
-}
+// pr[j] for a per-lane j (the pairs sit in lanes 0..c-1 of one register)
 __device__ __forceinline__ int pick(int tbl, int j) { return __shfl(tbl, j, 64); }
 
 __device__ __forceinline__ float h2f(uint32_t bits16) {
@@ -168,170 +157,381 @@ __device__ __forceinline__ void compute_piece(const Piece& p, const int8_t* act,
   }
 }
 
+// ---- routing inside the gate/up launch ----
+// The routing state of one workgroup: for every token the slot of each expert
+// (0xff: not picked), the picked experts in slot order and their logits.
+struct DecRoute {
+  uint8_t slot[DECODE_MAX_TOKENS][MAX_EXPERTS];
+  int sel[DECODE_MAX_TOKENS][MAX_TOPK];
+  float selv[DECODE_MAX_TOKENS][MAX_TOPK];
+  int wtot[4];
+};
+// The active groups in list order (routed experts ascending, then the shared
+// expert): group id, row count and the rows' (token, slot) pairs.
+constexpr int MAX_GROUPS = DECODE_MAX_TOKENS * MAX_TOPK + 1;
+struct GroupList {
+  int g[MAX_GROUPS];
+  int c[MAX_GROUPS];
+  int pairs[MAX_GROUPS][DECODE_MAX_TOKENS];
+};
+
+// Wavefront maximum of an unsigned value: prefix maxima within each row of
+// 16 lanes by DPP shifts, the row maxima carried into rows 1 and 3, then into
+// rows 2 and 3 by DPP row broadcasts; lane 63 ends with the maximum.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true));  // row_shr:1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true));  // row_shr:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true));  // row_shr:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true));  // row_shr:8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Inclusive prefix sum over the wavefront (same DPP pattern with additions).
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Route the N <= 8 tokens from their logits (every workgroup of the launch
+// does this; the top-k of the contract: logit descending, then id
+// ascending, by the same 64-bit keys as the prefill routing).  Wavefront t
+// takes token t's k largest keys one at a time (a wavefront maximum per
+// slot: of the high words, then of the low words among the lanes that hold
+// that high word).  Thread e then counts the tokens that picked expert e; one
+// scan gives each active expert its index in the group list and its CSR
+// start.  Fills GL and returns the number of groups.  Workgroup 0 also writes
+// ids, w (softmax over all E, then the optional renormalisation over the k
+// slots), expStart/expTokI/expTokK and the group list the down launch reads.
+__device__ __forceinline__ int decode_route(const DecodeArgs& a, DecRoute& R, GroupList& GL, int wave, int lane) {
+  const int n = a.n, E = a.E, k = a.k, kk = a.kk, tid = threadIdx.x;
+  const bool wg0 = blockIdx.x == 0;
+  if (wave < n) {
+    float lv[4];
+    unsigned long long kv[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) lv[m] = a.logits[(size_t)wave * E + min(lane + 64 * m, E - 1)];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e = lane + 64 * m;
+      kv[m] = e < E ? topk_key(lv[m], e) : 0ull;  // every real key is > 0
+      R.slot[wave][e] = 0xff;
+    }
+    for (int s = 0; s < k; ++s) {
+      unsigned long long b = kv[0];
+#pragma unroll
+      for (int m = 1; m < 4; ++m) b = kv[m] > b ? kv[m] : b;
+      const uint32_t mh = wave_max_u32((uint32_t)(b >> 32));
+      const uint32_t ml = wave_max_u32((uint32_t)(b >> 32) == mh ? (uint32_t)b : 0u);
+      const unsigned long long mx = ((unsigned long long)mh << 32) | ml;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        if (kv[m] == mx) {  // keys are distinct: one lane, one m
+          R.slot[wave][lane + 64 * m] = (uint8_t)s;
+          R.selv[wave][s] = lv[m];
+          kv[m] = 0ull;
+        }
+      if (lane == 0) R.sel[wave][s] = (int)~ml;
+    }
+    if (wg0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const float m0 = R.selv[wave][0];
+      float part = 0.0f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        if (lane + 64 * m < E) part += expf(lv[m] - m0);
+      part = wave_sum_f32(part);
+      float p = lane < k ? expf(R.selv[wave][min(lane, MAX_TOPK - 1)] - m0) / part : 0.0f;
+      if (a.norm) p = p / wave_sum_f32(p);
+      if (lane < k) {
+        a.ids[(size_t)wave * k + lane] = R.sel[wave][lane];
+        a.w[(size_t)wave * k + lane] = p;
+      }
+    }
+  }
+  __syncthreads();
+  // thread e < E: its token count (low 16 bits) and active flag (high 16),
+  // exclusive-scanned over the first four wavefronts together
+  int cnt = 0;
+  if (tid < E)
+    for (int t = 0; t < n; ++t) cnt += R.slot[t][tid] != 0xff ? 1 : 0;
+  const int v = cnt | ((cnt > 0 ? 1 : 0) << 16);
+  const int inc = wave_inclusive_sum(v);
+  if (lane == 63 && wave < 4) R.wtot[wave] = inc;
+  __syncthreads();
+  int pre = 0;
+  for (int w2 = 0; w2 < min(wave, 4); ++w2) pre += R.wtot[w2];
+  const int ex = pre + inc - v;
+  const int n_act = (R.wtot[0] + R.wtot[1] + R.wtot[2] + R.wtot[3]) >> 16;
+  const int start = ex & 0xffff, aidx = ex >> 16;
+  const int P = n * k;
+  if (tid < E && cnt > 0) {
+    GL.g[aidx] = tid;
+    GL.c[aidx] = cnt;
+    int32_t* ent = a.dlist + 4 + DLIST_ENTRY * aidx;
+    if (wg0) {
+      ent[0] = tid;
+      ent[1] = cnt;
+    }
+    int j = 0;
+    for (int t = 0; t < n; ++t) {
+      const int s = R.slot[t][tid];
+      if (s != 0xff) {
+        GL.pairs[aidx][j] = t * kk + s;
+        if (wg0) {
+          ent[DLIST_PAIRS + j] = t * kk + s;
+          a.tok_i[start + j] = t;
+          a.tok_k[start + j] = s;
+        }
+        ++j;
+      }
+    }
+  }
+  if (a.has_shared) {
+    if (tid == 0) {
+      GL.g[n_act] = E;
+      GL.c[n_act] = n;
+    }
+    if (tid < n) GL.pairs[n_act][tid] = tid * kk + k;
+  }
+  if (wg0) {
+    if (tid < E) a.exp_start[tid] = start;
+    if (tid == 0) {
+      a.exp_start[E] = P;
+      if (a.has_shared) a.exp_start[E + 1] = P + n;
+      a.dlist[0] = n_act + a.has_shared;
+    }
+    if (a.has_shared) {
+      int32_t* ent = a.dlist + 4 + DLIST_ENTRY * n_act;
+      if (tid == 0) {
+        ent[0] = E;
+        ent[1] = n;
+      }
+      if (tid < n) {
+        ent[DLIST_PAIRS + tid] = tid * kk + k;
+        a.tok_i[P + tid] = tid;
+        a.tok_k[P + tid] = k;
+      }
+    }
+  }
+  __syncthreads();
+  return n_act + a.has_shared;
+}
+
+// The group list the gate/up launch wrote, copied into LDS (its count and
+// all entries in one round trip: the entries read past the count stay
+// inside the list's n_bound entries and are not used).
+__device__ __forceinline__ int load_group_list(const DecodeArgs& a, GroupList& GL) {
+  const int tid = threadIdx.x;
+  const int n_groups = min(a.dlist[0], a.n_bound);
+  for (int q = tid; q < a.n_bound * DLIST_ENTRY; q += DW * 64) {
+    const int ei = q / DLIST_ENTRY, f = q - ei * DLIST_ENTRY;
+    const int v = a.dlist[4 + q];
+    if (f == 0) GL.g[ei] = v;
+    else if (f == 1) GL.c[ei] = min(max(v, 1), DECODE_MAX_TOKENS);
+    else if (f >= DLIST_PAIRS) GL.pairs[ei][f - DLIST_PAIRS] = v;
+  }
+  __syncthreads();
+  return n_groups;
+}
+
 // GATEUP: unit u = (strip u/2, tile pair u%2) of the [gate;up] plane, columns
 // 32u .. 32u+31 of h.  !GATEUP: unit u = (strip u/2, tiles 2(u%2), 2(u%2)+1)
-// of the down plane, output rows 64u .. 64u+63.
+// of the down plane, output rows 64u .. 64u+63.  A workgroup takes units
+// blockIdx.x, + gridDim.x, ... of the (group, unit) list, so that the routing
+// (or the list) is read once per workgroup and no workgroup is surplus.
 template <bool GATEUP>
 __global__ __launch_bounds__(DW * 64) void decode_gemv_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[DEC_LDS];
+  __shared__ GroupList GL;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // Start-up latency is the cost that matters for a kernel of one workgroup
-  // per CU: every argument is requested at once (one scalar round trip, not
-  // one per branch that first needs a field), then the list count and this
-  // workgroup's whole entry together (entry ei < n_bound always lies inside
-  // the list; it is only used once ei < count is known).
+  // Start-up latency is the cost that matters for a kernel of a few
+  // workgroups per CU: every argument is requested at once (one scalar round
+  // trip, not one per branch that first needs a field); then the routing
+  // input (gate/up: the logits; down: the group list) in one more.
   pin_args<GATEUP>(a);
   const int units = GATEUP ? a.kmax_pad / 32 : a.d_pad / 64;
-  const int ei = (int)blockIdx.x / units, u = (int)blockIdx.x - ei * units;
-  const int32_t* ent = a.dlist + 4 + DLIST_ENTRY * ei;
-  int n_act = __builtin_amdgcn_readfirstlane(a.dlist[0]);
-  int ev[DLIST_ENTRY];
-#pragma unroll
-  for (int i = 0; i < DLIST_ENTRY; ++i) ev[i] = __builtin_amdgcn_readfirstlane(ent[i]);
-  asm volatile("" ::"s"(n_act), "s"(ev[0]), "s"(ev[1]), "s"(ev[2]), "s"(ev[3]), "s"(ev[4]), "s"(ev[5]),
-               "s"(ev[6]), "s"(ev[7]), "s"(ev[8]), "s"(ev[9]), "s"(ev[10]), "s"(ev[11]), "s"(ev[12]),
-               "s"(ev[13]), "s"(ev[14]), "s"(ev[15]));
-  if (ei >= min(n_act, a.n_bound)) return;
-  const int g = ev[0];
-  const int c = min(max(ev[1], 1), DECODE_MAX_TOKENS);
-  if (g < 0 || g > a.E) return;
-  const bool shared = g == a.E;
-  if (shared && !(GATEUP ? a.sh_gu : a.sh_dn)) return;
-  const int Fg_pad = shared ? a.Fs_pad : a.F_pad;
-  if (GATEUP && u * 32 >= Fg_pad) return;
-  const int pr = pairs_table(ev, c);  // the rows' (token, slot) pairs (clamped past c)
-
-  const int KS = (GATEUP ? a.d_pad : Fg_pad) / (KSTEP * QB);
-  const int step_bytes = GATEUP ? KSTEP_BYTES : DN_KSTEP_BYTES;
-  const uint8_t* plane = GATEUP ? (shared ? a.sh_gu : a.gu + (size_t)g * a.gu_group)
-                                : (shared ? a.sh_dn : a.dn + (size_t)g * a.dn_group);
-  plane += (size_t)(u >> 1) * KS * step_bytes;
-  const int tsel0 = GATEUP ? (u & 1) : 2 * (u & 1);  // first tile; the second is +2 (up) or +1
-  const int tstride = GATEUP ? 2 : 1;
+  int n_groups;
+  if constexpr (GATEUP) {
+    __shared__ DecRoute R;
+    n_groups = decode_route(a, R, GL, wave, lane);
+  } else {
+    n_groups = load_group_list(a, GL);
+  }
+  const int total = n_groups * units;
   const uint32_t o_code = (uint32_t)lane * 16, o_scale = (uint32_t)(lane & 31) * 8;
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(plane), (short)0, -1, BUF_DWORD3);
-
   int8_t* s_act = reinterpret_cast<int8_t*>(lds);
   uint16_t* s_as = reinterpret_cast<uint16_t*>(lds + ACT_BYTES);
-  float acc[2][DECODE_MAX_TOKENS];
-#pragma unroll
-  for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-    for (int j = 0; j < DECODE_MAX_TOKENS; ++j) acc[ti][j] = 0.0f;
-
-  // Per pass of DPK = 2 * DW k-steps, wavefront w computes k-steps ks0 + w and
-  // ks0 + w + DW; both are requested before the activations are staged, so
-  // each wavefront has its whole share of the pass in flight at once.
-  static_assert(DPK == 2 * DW, "two k-steps per wavefront and pass");
-  static_assert(DECODE_MAX_TOKENS * DPK * 8 <= 2 * DW * 64, "two 16-byte activation pieces per thread");
-  static_assert(DECODE_MAX_TOKENS * DPK <= DW * 64, "one scale word per thread");
-  auto pass = [&](int ks0) {
-    const int ks_end = min(ks0 + DPK, KS), npk = ks_end - ks0;
-    const int k0 = ks0 + wave, k1 = ks0 + wave + DW;
-    // The pass's activation rows (codes [j][npk * 128], scales [j][npk * 4];
-    // at most 2 x 512 16-byte pieces and 128 scale words) are requested
-    // first: they hit in the caches, and waiting for them then does not wait
-    // for the weights requested after them.  Addresses are clamped into the
-    // rows (unconditional loads), the LDS writes masked.
-    const int nq = c * npk * 8, ns = c * npk;
-    auto code_src = [&](int q) {
-      q = min(q, nq - 1);
-      const int j = q / (npk * 8), o = q - j * (npk * 8);
-      const int prj = pick(pr, j);
-      return GATEUP ? reinterpret_cast<const uint4*>(a.xq + (size_t)(prj / a.kk) * a.d_pad + ks0 * 128) + o
-                    : reinterpret_cast<const uint4*>(a.hq + (size_t)prj * a.kmax_pad + ks0 * 128) + o;
-    };
-    const int q0 = threadIdx.x, q1 = threadIdx.x + DW * 64;
-    const uint4 c0 = *code_src(q0), c1 = *code_src(q1);
-    const int qs = min((int)threadIdx.x, ns - 1), js = qs / npk, os = qs - js * npk;
-    const int prs = pick(pr, js);
-    const uint2 sv = GATEUP
-        ? reinterpret_cast<const uint2*>(a.xs + (size_t)(prs / a.kk) * (a.d_pad / QB) + ks0 * KSTEP)[os]
-        : reinterpret_cast<const uint2*>(a.hs + (size_t)prs * (a.kmax_pad / QB) + ks0 * KSTEP)[os];
-    // both k-steps requested unconditionally (a k-step past the pass re-reads
-    // the pass's last one and is not computed): no branch between requests
-    Piece p0, p1;
-    load_piece<GATEUP>(rs, min(k0, ks_end - 1) * step_bytes, tsel0, tstride, o_code, o_scale, p0);
-    load_piece<GATEUP>(rs, min(k1, ks_end - 1) * step_bytes, tsel0, tstride, o_code, o_scale, p1);
-    __builtin_amdgcn_sched_barrier(0);  // every request is out before any wait
-    if (ks0 > 0) lds_barrier();  // every wavefront is done with the previous pass
-    if (q0 < nq) reinterpret_cast<uint4*>(s_act + (q0 / (npk * 8)) * (DPK * 128))[q0 % (npk * 8)] = c0;
-    if (q1 < nq) reinterpret_cast<uint4*>(s_act + (q1 / (npk * 8)) * (DPK * 128))[q1 % (npk * 8)] = c1;
-    if ((int)threadIdx.x < ns) reinterpret_cast<uint2*>(s_as + js * (DPK * KSTEP))[os] = sv;
-    lds_barrier();
-    if (k0 < ks_end) compute_piece<GATEUP>(p0, s_act + (k0 - ks0) * 128, s_as + (k0 - ks0) * KSTEP, c, lane, acc);
-    if (k1 < ks_end) compute_piece<GATEUP>(p1, s_act + (k1 - ks0) * 128, s_as + (k1 - ks0) * KSTEP, c, lane, acc);
-  };
-  // One pass (K <= 2048) has its own straight-line copy: inside a loop the
-  // second k-step's loads would wait for the first's (the compiler cannot
-  // tell that no load of a previous pass is still pending into them).
-  if (KS <= DPK) {
-    pass(0);
-  } else {
-    for (int ks0 = 0; ks0 < KS; ks0 += DPK) pass(ks0);
-  }
-
-  // Reduction: the lane pair (two halves of each block), then the wavefronts
-  // in order.  red[w][ti][j][r].
-  __syncthreads();  // the staging buffers are reused
   float* red = reinterpret_cast<float*>(lds);
+
+  for (int id = blockIdx.x; id < total; id += gridDim.x) {
+    const int ei = id / units, u = id - ei * units;
+    const int g = __builtin_amdgcn_readfirstlane(GL.g[ei]);
+    const int c = __builtin_amdgcn_readfirstlane(GL.c[ei]);
+    if (g < 0 || g > a.E || c < 1 || c > DECODE_MAX_TOKENS) continue;
+    const bool shared = g == a.E;
+    if (shared && !(GATEUP ? a.sh_gu : a.sh_dn)) continue;
+    const int Fg_pad = shared ? a.Fs_pad : a.F_pad;
+    if (GATEUP && u * 32 >= Fg_pad) continue;
+    // the rows' (token, slot) pairs in lanes 0..c-1
+    const int pr = GL.pairs[ei][min(lane, c - 1)];
+
+    const int KS = (GATEUP ? a.d_pad : Fg_pad) / (KSTEP * QB);
+    const int step_bytes = GATEUP ? KSTEP_BYTES : DN_KSTEP_BYTES;
+    const uint8_t* plane = GATEUP ? (shared ? a.sh_gu : a.gu + (size_t)g * a.gu_group)
+                                  : (shared ? a.sh_dn : a.dn + (size_t)g * a.dn_group);
+    plane += (size_t)(u >> 1) * KS * step_bytes;
+    const int tsel0 = GATEUP ? (u & 1) : 2 * (u & 1);  // first tile; the second is +2 (up) or +1
+    const int tstride = GATEUP ? 2 : 1;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(plane), (short)0, -1, BUF_DWORD3);
+
+    float acc[2][DECODE_MAX_TOKENS];
 #pragma unroll
-  for (int ti = 0; ti < 2; ++ti)
+    for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-    for (int j = 0; j < DECODE_MAX_TOKENS; ++j) {
-      if (j < c) {
-        const float v = acc[ti][j] + __shfl_xor(acc[ti][j], 32, 64);
-        if (lane < 32) red[((wave * 2 + ti) * DECODE_MAX_TOKENS + j) * 32 + lane] = v;
+      for (int j = 0; j < DECODE_MAX_TOKENS; ++j) acc[ti][j] = 0.0f;
+
+    // Per pass of DPK = 2 * DW k-steps, wavefront w computes k-steps ks0 + w
+    // and ks0 + w + DW; both are requested before the activations are staged,
+    // so each wavefront has its whole share of the pass in flight at once.
+    static_assert(DPK == 2 * DW, "two k-steps per wavefront and pass");
+    static_assert(DECODE_MAX_TOKENS * DPK * 8 <= 2 * DW * 64, "two 16-byte activation pieces per thread");
+    static_assert(DECODE_MAX_TOKENS * DPK <= DW * 64, "one scale word per thread");
+    for (int ks0 = 0; ks0 < KS; ks0 += DPK) {
+      const int ks_end = min(ks0 + DPK, KS), npk = ks_end - ks0;
+      const int k0 = ks0 + wave, k1 = ks0 + wave + DW;
+      // The pass's activation rows (codes [j][npk * 128], scales [j][npk * 4];
+      // at most 2 x 512 16-byte pieces and 128 scale words) are requested
+      // first: they hit in the caches, and waiting for them then does not
+      // wait for the weights requested after them.  Addresses are clamped
+      // into the rows (unconditional loads), the LDS writes masked.
+      const int nq = c * npk * 8, ns = c * npk;
+      auto code_src = [&](int q) {
+        q = min(q, nq - 1);
+        const int j = q / (npk * 8), o = q - j * (npk * 8);
+        const int prj = pick(pr, j);
+        return GATEUP ? reinterpret_cast<const uint4*>(a.xq + (size_t)(prj / a.kk) * a.d_pad + ks0 * 128) + o
+                      : reinterpret_cast<const uint4*>(a.hq + (size_t)prj * a.kmax_pad + ks0 * 128) + o;
+      };
+      const int q0 = threadIdx.x, q1 = threadIdx.x + DW * 64;
+      const uint4 c0 = *code_src(q0), c1 = *code_src(q1);
+      const int qs = min((int)threadIdx.x, ns - 1), js = qs / npk, os = qs - js * npk;
+      const int prs = pick(pr, js);
+      const uint2 sv = GATEUP
+          ? reinterpret_cast<const uint2*>(a.xs + (size_t)(prs / a.kk) * (a.d_pad / QB) + ks0 * KSTEP)[os]
+          : reinterpret_cast<const uint2*>(a.hs + (size_t)prs * (a.kmax_pad / QB) + ks0 * KSTEP)[os];
+      // both k-steps requested unconditionally (a k-step past the pass
+      // re-reads the pass's last one and is not computed): no branch between
+      // requests
+      Piece p0, p1;
+      load_piece<GATEUP>(rs, min(k0, ks_end - 1) * step_bytes, tsel0, tstride, o_code, o_scale, p0);
+      load_piece<GATEUP>(rs, min(k1, ks_end - 1) * step_bytes, tsel0, tstride, o_code, o_scale, p1);
+      __builtin_amdgcn_sched_barrier(0);  // every request is out before any wait
+      lds_barrier();  // every wavefront is done with the LDS of the previous pass or unit
+      if (q0 < nq) reinterpret_cast<uint4*>(s_act + (q0 / (npk * 8)) * (DPK * 128))[q0 % (npk * 8)] = c0;
+      if (q1 < nq) reinterpret_cast<uint4*>(s_act + (q1 / (npk * 8)) * (DPK * 128))[q1 % (npk * 8)] = c1;
+      if ((int)threadIdx.x < ns) reinterpret_cast<uint2*>(s_as + js * (DPK * KSTEP))[os] = sv;
+      lds_barrier();
+      if (k0 < ks_end) compute_piece<GATEUP>(p0, s_act + (k0 - ks0) * 128, s_as + (k0 - ks0) * KSTEP, c, lane, acc);
+      if (k1 < ks_end) compute_piece<GATEUP>(p1, s_act + (k1 - ks0) * 128, s_as + (k1 - ks0) * KSTEP, c, lane, acc);
+    }
+
+    // Reduction: the lane pair (two halves of each block), then the
+    // wavefronts in order.  red[w][ti][j][r] reuses the staging buffer.
+    lds_barrier();
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int j = 0; j < DECODE_MAX_TOKENS; ++j) {
+        if (j < c) {
+          const float v = acc[ti][j] + __shfl_xor(acc[ti][j], 32, 64);
+          if (lane < 32) red[((wave * 2 + ti) * DECODE_MAX_TOKENS + j) * 32 + lane] = v;
+        }
+      }
+    lds_barrier();
+    const int tid = threadIdx.x;
+    if constexpr (GATEUP) {
+      // thread (j = tid / 32, r = tid % 32): column 32u + r of h for row j;
+      // a row's 32 threads are one half-wavefront (the quantiser's exchanges
+      // stay inside it)
+      const int j = tid >> 5, r = tid & 31;
+      if (tid < DECODE_MAX_TOKENS * 32 && j < c) {
+        float gv = 0.0f, uv = 0.0f;
+#pragma unroll
+        for (int w = 0; w < DW; ++w) {
+          gv += red[((w * 2 + 0) * DECODE_MAX_TOKENS + j) * 32 + r];
+          uv += red[((w * 2 + 1) * DECODE_MAX_TOKENS + j) * 32 + r];
+        }
+        const float h = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+        int8_t q;
+        uint16_t s16;
+        quant_block32(h, q, s16);
+        const int prj = pick(pr, j);
+        a.hq[(size_t)prj * a.kmax_pad + u * 32 + r] = q;
+        if (r == 0) a.hs[(size_t)prj * (a.kmax_pad / QB) + u] = s16;
+      }
+    } else {
+      // thread (ti, j, r): output row 64u + 32 ti + r of pair row j
+      const int ti = tid >> 8, j = (tid >> 5) & 7, r = tid & 31;
+      const int row = 64 * u + 32 * ti + r;
+      const int prj = pick(pr, j);
+      if (j < c && row < a.d) {
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < DW; ++w) v += red[((w * 2 + ti) * DECODE_MAX_TOKENS + j) * 32 + r];
+        const int eg = a.dn_exp[g];
+        a.partial[(size_t)prj * a.d + row] = ldexpf(v, eg - 23);
       }
     }
-  __syncthreads();
-  if constexpr (GATEUP) {
-    // thread (j = tid / 32, r = tid % 32): column 32u + r of h for row j
-    const int tid = threadIdx.x;
-    if (tid >= DECODE_MAX_TOKENS * 32) return;
-    const int j = tid >> 5, r = tid & 31;
-    if (j >= c) return;  // half-wavefront-uniform: the quantiser's exchanges stay inside
-    float gv = 0.0f, uv = 0.0f;
-#pragma unroll
-    for (int w = 0; w < DW; ++w) {
-      gv += red[((w * 2 + 0) * DECODE_MAX_TOKENS + j) * 32 + r];
-      uv += red[((w * 2 + 1) * DECODE_MAX_TOKENS + j) * 32 + r];
-    }
-    const float h = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
-    int8_t q;
-    uint16_t s16;
-    quant_block32(h, q, s16);
-    const int prj = pick(pr, j);
-    a.hq[(size_t)prj * a.kmax_pad + u * 32 + r] = q;
-    if (r == 0) a.hs[(size_t)prj * (a.kmax_pad / QB) + u] = s16;
-  } else {
-    // thread (ti, j, r): output row 64u + 32 ti + r of pair row j
-    const int tid = threadIdx.x;
-    const int ti = tid >> 8, j = (tid >> 5) & 7, r = tid & 31;
-    if (j >= c) return;
-    const int row = 64 * u + 32 * ti + r;
-    if (row >= a.d) return;
-    float v = 0.0f;
-#pragma unroll
-    for (int w = 0; w < DW; ++w) v += red[((w * 2 + ti) * DECODE_MAX_TOKENS + j) * 32 + r];
-    const int prj = pick(pr, j);
-    const int eg = a.dn_exp[g];
-    a.partial[(size_t)prj * a.d + row] = ldexpf(v, eg - 23);
   }
 }
 
 }  // namespace
 
+// Workgroups per CU that fit at once (registers and LDS), from the runtime's
+// occupancy calculator: a grid of n_cu times this many has every workgroup
+// resident from the start.
+template <bool GATEUP>
+int resident_per_cu() {
+  static int cached = 0;
+  if (cached == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_gemv_kernel<GATEUP>, DW * 64, 0) != hipSuccess) {
+      (void)hipGetLastError();
+      nb = 1;
+    }
+    cached = std::max(nb, 1);
+  }
+  return cached;
+}
+
 hipError_t launch_decode_gateup(const DecodeArgs& a, hipStream_t s) {
-  const long wgs = (long)a.n_bound * (a.kmax_pad / 32);
-  decode_gemv_kernel<true><<<(unsigned)wgs, DW * 64, 0, s>>>(a);
+  const long units = (long)a.n_bound * (a.kmax_pad / 32);
+  const long grid = std::min<long>(units, (long)a.n_cu * resident_per_cu<true>());
+  decode_gemv_kernel<true><<<(unsigned)grid, DW * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s) {
-  const long wgs = (long)a.n_bound * (a.d_pad / 64);
-  decode_gemv_kernel<false><<<(unsigned)wgs, DW * 64, 0, s>>>(a);
+  const long units = (long)a.n_bound * (a.d_pad / 64);
+  const long grid = std::min<long>(units, (long)a.n_cu * resident_per_cu<false>());
+  decode_gemv_kernel<false><<<(unsigned)grid, DW * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 

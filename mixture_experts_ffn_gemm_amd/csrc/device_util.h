@@ -61,6 +61,16 @@ __device__ inline void quant_half_block16(const float (&v)[16], uint32_t (&packe
   s16 = __half_as_ushort(__float2half_rn(dd));
 }
 
+// A 64-bit key per (logit, expert id) whose unsigned order is the top-k order
+// (logit descending, then id ascending): the float's bits mapped to an
+// unsigned order (-0 taken as +0, so that equal logits tie as in a float
+// comparison) above the inverted id.  Every real key is > 0.
+__device__ __forceinline__ unsigned long long topk_key(float l, int e) {
+  const uint32_t b = l == 0.0f ? 0u : __float_as_uint(l);
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((unsigned long long)ord << 32) | (uint32_t)~(uint32_t)e;
+}
+
 // Workgroup barrier that orders LDS accesses only: global loads still in flight
 // (a register prefetch ring) are not drained, unlike __syncthreads().
 __device__ inline void lds_barrier() {

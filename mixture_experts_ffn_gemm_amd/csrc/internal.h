@@ -115,6 +115,7 @@ struct moe_ffn_weights {
   uint8_t* sh_gu;
   uint8_t* sh_dn;
   int32_t* dn_exp;  // [G] exponent e of each group's down scale plane
+  int n_cu;         // compute units of the device
   size_t gu_per_expert, dn_per_expert;  // bytes
 };
 
@@ -198,16 +199,22 @@ hipError_t launch_decode_router(const float* x, int n, int d, int d_pad, const f
                                 const float* bias, int E, int E64, float* logits,
                                 const float* sh_gate_vec, float* gs, int8_t* dxq, uint16_t* dxs,
                                 hipStream_t s);
-// One workgroup: top-k, weights, ranks (as launch_route), the CSR
-// (exp_start [E+2], tok_i/tok_k [N*k + N]) and the active-group list dlist.
-hipError_t launch_decode_route(const float* logits, int n, int E, int k, int norm, int has_shared,
-                               int32_t* ids, float* w, int32_t* rank, int32_t* hist,
-                               int32_t* exp_start, int32_t* tok_i, int32_t* tok_k, int32_t* dlist,
-                               hipStream_t s);
-
+// The decode matvecs.  The gate/up launch also routes: every workgroup
+// derives the top-k of the N tokens from the logits and so its own group and
+// (token, slot) pairs; workgroup 0 writes ids, w, the CSR and dlist, which
+// the down launch reads.
 struct DecodeArgs {
-  const int32_t* dlist;
-  int E, kk, n_bound;  // n_bound: upper bound on dlist[0]
+  // routing (gate/up launch)
+  const float* logits;  // [N][E]
+  int n, k, norm, has_shared;
+  int32_t* ids;
+  float* w;
+  int32_t* exp_start;
+  int32_t* tok_i;
+  int32_t* tok_k;
+  int32_t* dlist;  // written by the gate/up launch, read by the down launch
+  int E, kk, n_bound;  // n_bound: upper bound on the number of active groups
+  int n_cu;            // compute units of the device (the matvec grids are sized to what is resident)
   // gate/up: A = dxq/dxs rows of the pairs' tokens
   const int8_t* xq;
   const uint16_t* xs;

@@ -89,16 +89,6 @@ struct RouteLds {
   int cnt[MAX_EXPERTS];
 };
 
-// A 64-bit key per (logit, expert id) whose unsigned order is the top-k order
-// (logit descending, then id ascending): the float's bits mapped to an
-// unsigned order (-0 taken as +0, so that equal logits tie as in a float
-// comparison) above the inverted id.
-__device__ __forceinline__ unsigned long long topk_key(float l, int e) {
-  const uint32_t b = l == 0.0f ? 0u : __float_as_uint(l);
-  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((unsigned long long)ord << 32) | (uint32_t)~(uint32_t)e;
-}
-
 __device__ __forceinline__ void route_tile(RouteLds& R, int tile, int t0, int nt, int E, int k, int norm, int tid,
                            int nthreads, int32_t* __restrict__ ids, float* __restrict__ wout,
                            int32_t* __restrict__ rank, int32_t* __restrict__ hist) {
@@ -459,24 +449,74 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(
 // Decode router (1 <= N <= 8).  The logits are the same fp32 chains as
 // router_kernel's, but the batch is too small to share the router matrix
 // among many tokens, so the chains are spread over the chip instead: one
-// workgroup per 8 experts, lane 8t + i of its first wavefront running the
-// chain of (token t, expert 8 * blockIdx.x + i).  Per 256 j, the 8 experts'
-// slab (8 KiB) and the N token rows (1 KiB each) are copied into a ring of
-// LDS buffers by all four wavefronts, up to 7 chunks ahead (the whole chain
-// at d = 2048).  The workgroups past the router ones quantise one token row
-// each (the same pieces, decisions and shared-gate order as
-// quantize_scatter_kernel), writing the token-major codes the decode GEMVs
-// read.
-constexpr int DR_E = 8;                               // experts per router workgroup
+// workgroup per 16 experts.  Wavefront w < 2 runs tokens 4w .. 4w+3, one per
+// 16-lane row, lane i of a row running the chain of expert 16 * blockIdx.x + i
+// (one chain per lane: a wavefront issues one instruction at a time, so
+// what bounds a chain is the number of instructions per step).  Per 64 j a
+// lane reads 4 values of its row's token (row lane q holds j0 + 4q .. +3) and
+// 16 quads of its expert's weights from LDS; the token value of each step
+// reaches the row through a DPP row broadcast inside the FMA.  Per 256 j, the
+// 16 experts' slab (16 KiB) and the N token rows (1 KiB each) are copied into
+// a ring of LDS buffers by all four wavefronts, 5 chunks ahead.  The
+// workgroups past the router ones quantise one token row each (the same
+// pieces, decisions and shared-gate order as quantize_scatter_kernel),
+// writing the token-major codes the decode matvecs read.
+constexpr int DR_E = 16;                              // experts per router workgroup
 constexpr int DR_J = 256;                             // j per chunk
-constexpr int DR_NB = 8;                              // chunk buffers in the ring
+constexpr int DR_NB = 6;                              // chunk buffers in the ring
 constexpr int DR_PF = DR_NB - 1;                      // chunks copied ahead
-constexpr int DR_WB = (DR_J / 4) * DR_E * 16;         // slab [quad][expert][4 j] (8 KiB)
+constexpr int DR_WB = (DR_J / 4) * DR_E * 16;         // slab [quad][expert][4 j] (16 KiB)
 constexpr int DR_XROW = DR_J * 4 + 16;                // one token row, padded (bank offset)
 constexpr int DR_BUF = DR_WB + DECODE_MAX_TOKENS * DR_XROW;
-constexpr int DR_DMA = 4;                             // copies per wavefront per chunk
+constexpr int DR_DMA = 6;                             // copies per wavefront per chunk
 static_assert(DR_NB * DR_BUF <= 160 * 1024, "decode router ring must fit in the LDS");
-static_assert(4 * DR_DMA == 8 + DECODE_MAX_TOKENS, "16 copies per chunk: 8 slab + 8 rows");
+static_assert(4 * DR_DMA == DR_WB / 1024 + DECODE_MAX_TOKENS, "24 copies per chunk: 16 slab + 8 rows");
+
+// 16 steps of one fp32 fused multiply-add chain over the 16 quads' weights
+// w0..w15 (component c of quad q: j = j0 + 4q + c) for quads q0 .. q0+3:
+// acc = fma(x, w, acc) where x is component c of lane q of this lane's
+// 16-lane row (DPP row_newbcast); the leading s_nop covers the wait states a
+// DPP read needs after a VALU write of its source.
+#define DFMA(Q, C, W) "v_fmac_f32_dpp %0, %" #C ", " W " row_newbcast:" #Q " row_mask:0xf bank_mask:0xf\n\t"
+#define DFMA4(Q, W0, W1, W2, W3) DFMA(Q, 1, W0) DFMA(Q, 2, W1) DFMA(Q, 3, W2) DFMA(Q, 4, W3)
+template <int Q0>
+__device__ __forceinline__ void decode_fma16(float& acc, const f4v& x, const f4v& w0, const f4v& w1, const f4v& w2,
+                                             const f4v& w3) {
+  if constexpr (Q0 == 0)
+    asm volatile("s_nop 1\n\t"
+                 DFMA4(0, "%5", "%6", "%7", "%8") DFMA4(1, "%9", "%10", "%11", "%12")
+                 DFMA4(2, "%13", "%14", "%15", "%16") DFMA4(3, "%17", "%18", "%19", "%20")
+                 : "+v"(acc)
+                 : "v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w), "v"(w0.x), "v"(w0.y), "v"(w0.z), "v"(w0.w),
+                   "v"(w1.x), "v"(w1.y), "v"(w1.z), "v"(w1.w), "v"(w2.x), "v"(w2.y), "v"(w2.z), "v"(w2.w),
+                   "v"(w3.x), "v"(w3.y), "v"(w3.z), "v"(w3.w));
+  else if constexpr (Q0 == 4)
+    asm volatile("s_nop 1\n\t"
+                 DFMA4(4, "%5", "%6", "%7", "%8") DFMA4(5, "%9", "%10", "%11", "%12")
+                 DFMA4(6, "%13", "%14", "%15", "%16") DFMA4(7, "%17", "%18", "%19", "%20")
+                 : "+v"(acc)
+                 : "v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w), "v"(w0.x), "v"(w0.y), "v"(w0.z), "v"(w0.w),
+                   "v"(w1.x), "v"(w1.y), "v"(w1.z), "v"(w1.w), "v"(w2.x), "v"(w2.y), "v"(w2.z), "v"(w2.w),
+                   "v"(w3.x), "v"(w3.y), "v"(w3.z), "v"(w3.w));
+  else if constexpr (Q0 == 8)
+    asm volatile("s_nop 1\n\t"
+                 DFMA4(8, "%5", "%6", "%7", "%8") DFMA4(9, "%9", "%10", "%11", "%12")
+                 DFMA4(10, "%13", "%14", "%15", "%16") DFMA4(11, "%17", "%18", "%19", "%20")
+                 : "+v"(acc)
+                 : "v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w), "v"(w0.x), "v"(w0.y), "v"(w0.z), "v"(w0.w),
+                   "v"(w1.x), "v"(w1.y), "v"(w1.z), "v"(w1.w), "v"(w2.x), "v"(w2.y), "v"(w2.z), "v"(w2.w),
+                   "v"(w3.x), "v"(w3.y), "v"(w3.z), "v"(w3.w));
+  else
+    asm volatile("s_nop 1\n\t"
+                 DFMA4(12, "%5", "%6", "%7", "%8") DFMA4(13, "%9", "%10", "%11", "%12")
+                 DFMA4(14, "%13", "%14", "%15", "%16") DFMA4(15, "%17", "%18", "%19", "%20")
+                 : "+v"(acc)
+                 : "v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w), "v"(w0.x), "v"(w0.y), "v"(w0.z), "v"(w0.w),
+                   "v"(w1.x), "v"(w1.y), "v"(w1.z), "v"(w1.w), "v"(w2.x), "v"(w2.y), "v"(w2.z), "v"(w2.w),
+                   "v"(w3.x), "v"(w3.y), "v"(w3.z), "v"(w3.w));
+}
+#undef DFMA4
+#undef DFMA
 
 // Quantise token row xr (one wavefront): pass j0 covers values [1024 j0', +1024),
 // lane l the 16 values from 16 l; codes/scales to xq_row/xs_row up to d_pad
@@ -537,30 +577,32 @@ __global__ __launch_bounds__(256, 1) void decode_router_kernel(
   }
   const int C = (d + DR_J - 1) / DR_J, NQ = d / 4;
   const uint32_t lbase = (uint32_t)(uintptr_t)(lds_char*)ring;
-  // Copy i of a chunk (wavefront w issues 4w .. 4w+3): i < 8 moves slab quads
-  // 8i .. 8i+7 (lane l: quad 8i + l/8, expert l%8; quads past d re-read the
-  // last one), i >= 8 token row i-8 (rows past n re-read row n-1; columns
-  // past d re-read the last 4).
+  // Copy i of a chunk (wavefront w issues 6w .. 6w+5): i < 16 moves slab
+  // quads 4i .. 4i+3 (lane l: quad 4i + l/16, expert l%16; quads past d
+  // re-read the last one), i >= 16 token row i-16 (rows past n re-read row
+  // n-1; columns past d re-read the last 4).
   auto issue = [&](int c) {
     const uint32_t buf = lbase + (uint32_t)((c % DR_NB) * DR_BUF);
 #pragma unroll
     for (int ii = 0; ii < DR_DMA; ++ii) {
       const int i = wave * DR_DMA + ii;
-      if (i < 8) {
-        const int jq = min(c * (DR_J / 4) + 8 * i + (lane >> 3), NQ - 1);
-        rdma16(wt, (uint32_t)(((size_t)jq * E64 + DR_E * blockIdx.x + (lane & 7)) * 16),
-               buf + i * 1024);
+      if (i < DR_WB / 1024) {
+        const int jq = min(c * (DR_J / 4) + 4 * i + (lane >> 4), NQ - 1);
+        rdma16(wt, (uint32_t)(((size_t)jq * E64 + DR_E * blockIdx.x + (lane & 15)) * 16), buf + i * 1024);
       } else {
-        const int t = min(i - 8, n - 1);
+        const int tr = i - DR_WB / 1024;
+        const int t = min(tr, n - 1);
         const int j = min(c * DR_J + 4 * lane, d - 4);
-        rdma16(x + (size_t)t * d, (uint32_t)j * 4, buf + DR_WB + (i - 8) * DR_XROW);
+        rdma16(x + (size_t)t * d, (uint32_t)j * 4, buf + DR_WB + tr * DR_XROW);
       }
     }
   };
   const int np = min(DR_PF, C);
   for (int c = 0; c < np; ++c) issue(c);
   static_assert(DR_PF * DR_DMA <= 63, "vmcnt counts at most 63 copies");
-  const int t = lane >> 3, i = lane & 7;
+  const int row = lane >> 4, i = lane & 15;
+  const int t = 4 * wave + row;  // this lane's token (wavefronts 0 and 1)
+  const bool busy = wave < 2 && 4 * wave < n;  // wavefront-uniform
   float acc = 0.0f;
   for (int c = 0; c < C; ++c) {
     // issued so far: chunks 0 .. min(c + DR_PF - 1, C - 1); wait for chunk c
@@ -569,133 +611,72 @@ __global__ __launch_bounds__(256, 1) void decode_router_kernel(
       case 1: rwait_vm<DR_DMA>(); break;
       case 2: rwait_vm<2 * DR_DMA>(); break;
       case 3: rwait_vm<3 * DR_DMA>(); break;
-      case 4: rwait_vm<4 * DR_DMA>(); break;
-      case 5: rwait_vm<5 * DR_DMA>(); break;
-      default: rwait_vm<6 * DR_DMA>(); break;
+      default: rwait_vm<4 * DR_DMA>(); break;
     }
-    // every wavefront's copies of chunk c have landed, and wavefront 0 has
-    // finished chunk c-1, whose buffer now takes chunk c + DR_PF
+    // every wavefront's copies of chunk c have landed, and the computing
+    // wavefronts have finished chunk c-1, whose buffer now takes chunk
+    // c + DR_PF
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (c + DR_PF < C) issue(c + DR_PF);
-    if (wave == 0) {
+    if (busy) {
       const char* buf = ring + (c % DR_NB) * DR_BUF;
-      const f4v* xr = reinterpret_cast<const f4v*>(buf + DR_WB + t * DR_XROW);
-      const f4v* wr = reinterpret_cast<const f4v*>(buf) + i;
-      const int nq = min(DR_J, d - c * DR_J) / 4;
-      if (nq == DR_J / 4) {
-        // groups of 8 quads, double-buffered in registers: the reads of
-        // group g+1 are in flight while the chain runs through group g
-        constexpr int GQ = 8, NG = DR_J / 4 / GQ;
-        f4v xa[2][GQ], wa[2][GQ];
-#pragma unroll
-        for (int q = 0; q < GQ; ++q) {
-          xa[0][q] = xr[q];
-          wa[0][q] = wr[q * DR_E];
+      const f4v* xr = reinterpret_cast<const f4v*>(buf + DR_WB + t * DR_XROW) + i;  // + 16 per 64 j
+      const f4v* wr = reinterpret_cast<const f4v*>(buf) + i;                         // + 16 per quad
+      const int n64 = min(DR_J, d - c * DR_J) / 64;  // d % 32 == 0: a trailing 32 j are handled below
+      auto fma_group = [&](int gq, const f4v& xv, const f4v (&w)[4]) {  // quads 4 gq .. 4 gq + 3
+        switch (gq & 3) {
+          case 0: decode_fma16<0>(acc, xv, w[0], w[1], w[2], w[3]); break;
+          case 1: decode_fma16<4>(acc, xv, w[0], w[1], w[2], w[3]); break;
+          case 2: decode_fma16<8>(acc, xv, w[0], w[1], w[2], w[3]); break;
+          default: decode_fma16<12>(acc, xv, w[0], w[1], w[2], w[3]); break;
         }
+      };
+      if (n64 == 4) {
+        // a whole chunk as 16 groups of 4 quads; the reads of group g + 2
+        // are issued before group g's 16 steps (at most 9 reads in flight:
+        // every wait is expressible in the 4-bit LDS counter), order pinned
+        f4v xs[4], wg[3][4];
+        auto load_group = [&](int gq, f4v (&w)[4]) {
 #pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-          const int b = gi & 1;
-          if (gi + 1 < NG) {
+          for (int qq = 0; qq < 4; ++qq) w[qq] = wr[16 * (4 * gq + qq)];
+        };
+        xs[0] = xr[0];
+        load_group(0, wg[0]);
+        load_group(1, wg[1]);
 #pragma unroll
-            for (int q = 0; q < GQ; ++q) {
-              xa[b ^ 1][q] = xr[(gi + 1) * GQ + q];
-              wa[b ^ 1][q] = wr[((gi + 1) * GQ + q) * DR_E];
-            }
+        for (int gq = 0; gq < 16; ++gq) {
+          if (gq + 2 < 16) {
+            if ((gq + 2) % 4 == 0) xs[(gq + 2) / 4] = xr[16 * ((gq + 2) / 4)];
+            load_group(gq + 2, wg[(gq + 2) % 3]);
           }
-          __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of this group's chain
-#pragma unroll
-          for (int q = 0; q < GQ; ++q) {
-            acc = __builtin_fmaf(xa[b][q].x, wa[b][q].x, acc);
-            acc = __builtin_fmaf(xa[b][q].y, wa[b][q].y, acc);
-            acc = __builtin_fmaf(xa[b][q].z, wa[b][q].z, acc);
-            acc = __builtin_fmaf(xa[b][q].w, wa[b][q].w, acc);
-          }
+          __builtin_amdgcn_sched_barrier(0);
+          fma_group(gq, xs[gq / 4], wg[gq % 3]);
         }
       } else {
-        for (int q = 0; q < nq; ++q) {
-          const f4v xv = xr[q], wv = wr[q * DR_E];
-          acc = __builtin_fmaf(xv.x, wv.x, acc);
-          acc = __builtin_fmaf(xv.y, wv.y, acc);
-          acc = __builtin_fmaf(xv.z, wv.z, acc);
-          acc = __builtin_fmaf(xv.w, wv.w, acc);
+        for (int sc = 0; sc < n64; ++sc) {
+          const f4v xv = xr[16 * sc];
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            f4v w[4];
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) w[qq] = wr[16 * (16 * sc + 4 * g4 + qq)];
+            fma_group(g4, xv, w);
+          }
         }
+      }
+      if (n64 * 64 < min(DR_J, d - c * DR_J)) {  // 32 trailing j: quads 0..7 of the last 64
+        const f4v xv = xr[16 * n64];
+        f4v w[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) w[q] = wr[16 * (16 * n64 + q)];
+        decode_fma16<0>(acc, xv, w[0], w[1], w[2], w[3]);
+        decode_fma16<4>(acc, xv, w[4], w[5], w[6], w[7]);
       }
     }
   }
   const int e = DR_E * (int)blockIdx.x + i;
-  if (wave == 0 && t < n && e < E) logits[(size_t)t * E + e] = bias ? acc + bias[e] : acc;
-}
-
-// Decode routing, one workgroup for all N <= 8 tokens: route_tile (top-k,
-// weights, ranks, counts), then the CSR of the tile (expStart = exclusive scan
-// of the counts; a pair's row = expStart[e] + its rank) and the list of active
-// groups the decode GEMVs run over (routed experts with a non-zero count in
-// ascending order, then the shared expert with all N tokens).
-__global__ __launch_bounds__(256) void decode_route_kernel(
-    const float* __restrict__ logits, int n, int E, int k, int norm, int has_shared,
-    int32_t* __restrict__ ids, float* __restrict__ wout, int32_t* __restrict__ rank,
-    int32_t* __restrict__ hist, int32_t* __restrict__ exp_start, int32_t* __restrict__ tok_i,
-    int32_t* __restrict__ tok_k, int32_t* __restrict__ dlist) {
-  __shared__ __attribute__((aligned(16))) RouteLds R;
-  __shared__ int s_start[MAX_EXPERTS], s_act[MAX_EXPERTS], s_wtot[4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  route_load_logits(R, logits, 0, n, E, tid, 256);
-  route_tile(R, 0, 0, n, E, k, norm, tid, 256, ids, wout, rank, hist);
-  // route_tile ends past a barrier: R.cnt holds every expert's count.  One
-  // exclusive scan gives both the CSR start (low 16 bits) and the index among
-  // the active experts (high 16 bits).
-  const int cnt = tid < E ? R.cnt[tid] : 0;
-  const int v = cnt | ((cnt > 0 ? 1 : 0) << 16);
-  int inc = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int up = __shfl_up(inc, off, 64);
-    if (lane >= off) inc += up;
-  }
-  if (lane == 63) s_wtot[wave] = inc;
-  __syncthreads();
-  int pre = 0;
-  for (int w2 = 0; w2 < wave; ++w2) pre += s_wtot[w2];
-  const int ex = pre + inc - v;
-  const int n_act = (s_wtot[0] + s_wtot[1] + s_wtot[2] + s_wtot[3]) >> 16;
-  const int P = n * k, kk = k + has_shared;
-  if (tid < E) {
-    s_start[tid] = ex & 0xffff;
-    s_act[tid] = ex >> 16;
-    exp_start[tid] = ex & 0xffff;
-    if (cnt > 0) {
-      int32_t* ent = dlist + 4 + DLIST_ENTRY * (ex >> 16);
-      ent[0] = tid;
-      ent[1] = cnt;
-    }
-  }
-  if (tid == 0) {
-    exp_start[E] = P;
-    if (has_shared) exp_start[E + 1] = P + n;
-    dlist[0] = n_act + has_shared;
-  }
-  __syncthreads();
-  if (tid < P) {
-    const int t = tid / k, s = tid - (tid / k) * k;
-    const int e = R.ids[t * MAX_TOPK + s];
-    const int r = rank[tid];  // written by this thread in route_tile
-    tok_i[s_start[e] + r] = t;
-    tok_k[s_start[e] + r] = s;
-    dlist[4 + DLIST_ENTRY * s_act[e] + DLIST_PAIRS + r] = t * kk + s;
-  }
-  if (has_shared) {
-    int32_t* ent = dlist + 4 + DLIST_ENTRY * n_act;
-    if (tid == 0) {
-      ent[0] = E;
-      ent[1] = n;
-    }
-    if (tid < n) {
-      tok_i[P + tid] = tid;
-      tok_k[P + tid] = k;
-      ent[DLIST_PAIRS + tid] = tid * kk + k;
-    }
-  }
+  if (busy && t < n && e < E) logits[(size_t)t * E + e] = bias ? acc + bias[e] : acc;
 }
 
 __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ v, int64_t n_values,
@@ -757,16 +738,6 @@ hipError_t launch_decode_router(const float* x, int n, int d, int d_pad, const f
   const int n_rwg = (E + DR_E - 1) / DR_E;
   decode_router_kernel<<<n_rwg + n, 256, 0, s>>>(x, n, d, d_pad, wt, bias, E, E64, n_rwg, logits,
                                                  sh_gate_vec, gs, dxq, dxs);
-  return hipGetLastError();
-}
-
-hipError_t launch_decode_route(const float* logits, int n, int E, int k, int norm, int has_shared,
-                               int32_t* ids, float* w, int32_t* rank, int32_t* hist,
-                               int32_t* exp_start, int32_t* tok_i, int32_t* tok_k, int32_t* dlist,
-                               hipStream_t s) {
-  if (n < 1 || n > DECODE_MAX_TOKENS || n * k > 256) return hipErrorInvalidValue;
-  decode_route_kernel<<<1, 256, 0, s>>>(logits, n, E, k, norm, has_shared, ids, w, rank, hist,
-                                        exp_start, tok_i, tok_k, dlist);
   return hipGetLastError();
 }
 
