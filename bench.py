@@ -147,18 +147,22 @@ def copy_calibration(mib, reps):
 
 
 def cpu_baseline(lw, x, target_s):
+    """The oracle on a bounded sample of the same batch: m token evaluations
+    (the batch's tokens in order, cycled when m exceeds a small batch)."""
     from oracle import oracle as O
     n = x.shape[0]
+    probe = [i % n for i in range(8)]
     t0 = time.perf_counter()
-    O.moe_tokens(lw, x, tokens=list(range(min(8, n))))
-    per = (time.perf_counter() - t0) / min(8, n)
-    m = int(max(8, min(n, target_s / max(per, 1e-9))))
-    toks = list(range(m))
+    O.moe_tokens(lw, x, tokens=probe)
+    per = (time.perf_counter() - t0) / len(probe)
+    m = int(max(8, min(max(n, 8), target_s / max(per, 1e-9))))
+    toks = [i % n for i in range(m)]
     t0 = time.perf_counter()
     O.moe_tokens(lw, x, tokens=toks)
     dt = time.perf_counter() - t0
+    what = f"first {m} of the {n} tokens" if m <= n else f"{m} evaluations cycling the batch's {n} tokens"
     return {"value": m / dt, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
-            "sample": f"first {m} of the {n} tokens of the same layer (per-token oracle loop, "
+            "sample": f"{what} of the same layer (per-token oracle loop, "
                       f"router + top-k + quantiser + k experts + combine), {dt:.1f} s wall"}
 
 
@@ -228,9 +232,10 @@ def main():
             B.moe_ffn_prefill(lay.handle, x, n, out, ws, ws.numel(), None, stream)
             B.moe_ffn_residual_rmsnorm(h, out, x, n, s.d, eps, stream)
     exp_start = torch.empty(s.n_experts + 1 + (1 if s.shared_ffn else 0), dtype=torch.int32, device=dev)
-    B.moe_ffn_prefill(layer.handle, x, n, out, ws, ws.numel(), B.make_routing(exp_start=exp_start), stream)
+    step_fn = B.moe_ffn_decode if decode else B.moe_ffn_prefill
+    step_fn(layer.handle, x, n, out, ws, ws.numel(), B.make_routing(exp_start=exp_start), stream)
     for _ in range(args.warmup):
-        B.moe_ffn_prefill(layer.handle, x, n, out, ws, ws.numel(), None, stream)
+        step_fn(layer.handle, x, n, out, ws, ws.numel(), None, stream)
     torch.cuda.synchronize()
     counts = np.diff(exp_start.cpu().numpy())
 
@@ -242,7 +247,6 @@ def main():
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    step_fn = B.moe_ffn_decode if decode else B.moe_ffn_prefill
     for i in range(args.steps):
         if n_layers > 1:
             stack_pass()
@@ -260,31 +264,44 @@ def main():
     # between its stages on its launch stream (each event adds a dispatch gap,
     # so these passes are slower and are not the timed region).
     hip = HipEvents()
-    evs = [hip.create(B.N_STAGE_EVENTS) for _ in range(args.steps)]
+    if decode:
+        n_ev, stage_names, prof_fn = B.N_DECODE_STAGE_EVENTS, B.DECODE_STAGES, B.moe_ffn_decode_profiled
+    else:
+        n_ev, stage_names, prof_fn = B.N_STAGE_EVENTS, B.STAGES, B.moe_ffn_prefill_profiled
+    evs = [hip.create(n_ev) for _ in range(args.steps)]
     for i in range(args.steps):
-        B.moe_ffn_prefill_profiled(layer.handle, x, n, out, ws, ws.numel(), evs[i], None, stream)
+        prof_fn(layer.handle, x, n, out, ws, ws.numel(), evs[i], None, stream)
     torch.cuda.synchronize()
-    stage_ms = {name: 0.0 for name in B.STAGES}
+    stage_ms = {name: 0.0 for name in stage_names}
     for i in range(args.steps):
-        for j, name in enumerate(B.STAGES):
+        for j, name in enumerate(stage_names):
             stage_ms[name] += hip.elapsed_ms(evs[i][j], evs[i][j + 1]) / args.steps
     for e in evs:
         hip.destroy(e)
 
     gu_ops, dn_ops = gemm_ops(s, n)
     sb = stage_bytes(s, n, counts)
-    gu_us = stage_ms["gateup_swiglu"] * 1e3
+    if decode:
+        # decode stages: the router launch also quantises; the gate/up launch
+        # also routes
+        sb["router_quantise"] = sb.pop("router_logits") + n * s.d * (1 + 2 / 32)
+        sb["route_gateup_swiglu"] = sb.pop("gateup_swiglu")
+        gu_us = stage_ms["route_gateup_swiglu"] * 1e3
+    else:
+        gu_us = stage_ms["gateup_swiglu"] * 1e3
     dn_us = stage_ms["down"] * 1e3
     gu_tops = gu_ops / (gu_us * 1e-6) / 1e12
     if decode:
-        # a handful of tokens: the GEMMs stream each touched expert's weights
+        # a handful of tokens: the matvecs stream each touched expert's weights
         # once, so HBM bandwidth is the roof
-        gu_gbs = sb["gateup_swiglu"] / (gu_us * 1e-6) / 1e9
-        roofline = {"bound": "hbm", "kernel": "grouped_gemm_kernel<true> (grouped gate/up + SwiGLU + requantise)",
+        gu_gbs = sb["route_gateup_swiglu"] / (gu_us * 1e-6) / 1e9
+        roofline = {"bound": "hbm",
+                    "kernel": "decode_gemv_kernel<true> (routing + gathered gate/up int8 matvec + SwiGLU + requantise)",
                     "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                    "algorithmic_bytes_per_launch": int(sb["gateup_swiglu"]), "avg_launch_us": round(gu_us, 2),
-                    "layer_hbm_frac": round(sum(sb[k] for k in ("router_logits", "gateup_swiglu", "down", "combine"))
+                    "algorithmic_bytes_per_launch": int(sb["route_gateup_swiglu"]), "avg_launch_us": round(gu_us, 2),
+                    "layer_hbm_frac": round(sum(sb[k] for k in ("router_quantise", "route_gateup_swiglu", "down",
+                                                                "combine"))
                                             / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     else:
         roofline = {"bound": "mfma", "kernel": "grouped_gemm_kernel<true> (grouped gate/up + SwiGLU + requantise)",
@@ -296,14 +313,14 @@ def main():
                                   "frac": round(gu_tops / PIPE_ROOF_TOPS, 4),
                                   "why": "3 MFMAs per 32-block per 32x32 tile (int8, conversion, scale)"}}
     stages = {}
-    for name in B.STAGES:
+    for name in stage_names:
         us = stage_ms[name] * 1e3
         ent = {"avg_us": round(us, 2)}
         if name in sb:
             ent["hbm_GBps_algorithmic"] = round(sb[name] / (us * 1e-6) / 1e9, 1)
             ent["hbm_frac"] = round(sb[name] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
         stages[name] = ent
-    stages["gateup_swiglu"]["int8_TOPs"] = round(gu_tops, 1)
+    stages["route_gateup_swiglu" if decode else "gateup_swiglu"]["int8_TOPs"] = round(gu_tops, 1)
     stages["down"]["int8_TOPs"] = round(dn_ops / (dn_us * 1e-6) / 1e12, 1)
     gemm_frac = (gu_ops + dn_ops) / ((gu_us + dn_us) * 1e-6) / 1e12 / INT8_PEAK_TOPS
 

@@ -178,6 +178,18 @@ int moe_ffn_decode(const moe_ffn_weights* w, const float* x, int32_t n_tokens, f
                    void* ws, size_t ws_bytes, const moe_ffn_routing* routing,
                    hipStream_t stream);
 
+/* moe_ffn_decode with stage timing (#388 "Measurement discipline"), like
+ * moe_ffn_prefill_profiled: stage_events points to MOE_FFN_N_DECODE_STAGE_EVENTS
+ * caller-created hipEvent_t handles; event i is recorded on `stream` before
+ * decode stage i and the last one after the final stage: 0 router logits +
+ * activation quantiser, 1 routing + gathered gate/up matvec + SwiGLU, 2
+ * gathered down matvec, 3 combine.  Same arguments and results as
+ * moe_ffn_decode otherwise. */
+#define MOE_FFN_N_DECODE_STAGE_EVENTS 5
+int moe_ffn_decode_profiled(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* out,
+                            void* ws, size_t ws_bytes, const moe_ffn_routing* routing,
+                            hipStream_t stream, hipEvent_t* stage_events);
+
 /* Stage entry point: the ordered weighted combine on its own (#129 "Scope").
  * partial fp32 [n][kk][d] (kk = k, or k+1 when shared_gate != NULL, slot k
  * being the shared row), topk_w fp32 [n][k], shared_gate fp32 [n] or NULL,

@@ -25,7 +25,7 @@ MOE_FFN_HIP_ERROR = -5
 
 EXPORTED = ("moe_ffn_weights_create", "moe_ffn_weights_destroy", "moe_ffn_weights_dims",
             "moe_ffn_workspace_size", "moe_ffn_prefill", "moe_ffn_prefill_profiled", "moe_ffn_decode",
-            "moe_ffn_combine",
+            "moe_ffn_decode_profiled", "moe_ffn_combine",
             "moe_ffn_quantize", "moe_ffn_residual_rmsnorm", "moe_ffn_status_str")
 
 
@@ -68,6 +68,8 @@ def lib():
             "moe_ffn_decode": [vp, vp, i32, vp, vp, sz, C.POINTER(moe_ffn_routing), vp],
             "moe_ffn_prefill_profiled": [vp, vp, i32, vp, vp, sz, C.POINTER(moe_ffn_routing), vp,
                                          C.POINTER(vp)],
+            "moe_ffn_decode_profiled": [vp, vp, i32, vp, vp, sz, C.POINTER(moe_ffn_routing), vp,
+                                        C.POINTER(vp)],
             "moe_ffn_combine": [vp, vp, vp, i32, i32, i32, vp, vp],
             "moe_ffn_quantize": [vp, i64, vp, vp, vp],
             "moe_ffn_residual_rmsnorm": [vp, vp, vp, i32, i32, C.c_float, vp],
@@ -172,6 +174,20 @@ def moe_ffn_decode(handle: int, x, n_tokens: int, out, ws, ws_bytes: int,
     rc = lib().moe_ffn_decode(handle, _ptr(x), int(n_tokens), _ptr(out), _ptr(ws), int(ws_bytes),
                               C.byref(routing) if routing is not None else None, _stream(stream))
     _check("moe_ffn_decode", rc)
+
+
+N_DECODE_STAGE_EVENTS = 5
+DECODE_STAGES = ("router_quantise", "route_gateup_swiglu", "down", "combine")
+
+
+def moe_ffn_decode_profiled(handle: int, x, n_tokens: int, out, ws, ws_bytes: int, stage_events,
+                            routing: Optional[moe_ffn_routing] = None, stream=None) -> None:
+    """stage_events: N_DECODE_STAGE_EVENTS hipEvent_t handles (ints)."""
+    ev = (C.c_void_p * N_DECODE_STAGE_EVENTS)(*stage_events)
+    rc = lib().moe_ffn_decode_profiled(handle, _ptr(x), int(n_tokens), _ptr(out), _ptr(ws), int(ws_bytes),
+                                       C.byref(routing) if routing is not None else None,
+                                       _stream(stream), ev)
+    _check("moe_ffn_decode_profiled", rc)
 
 
 def moe_ffn_combine(partial, topk_w, shared_gate, n: int, k: int, d: int, out, stream=None) -> None:

@@ -249,7 +249,7 @@ int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, v
 // routes the tokens and lists the active groups), the down matvec launch over
 // that list, and the ordered combine (#408 "Hypothesis" levers 1 and 3).
 int run_decode(const moe_ffn_weights* W, const float* x, int32_t n, float* out, void* ws,
-               size_t ws_bytes, const moe_ffn_routing* r, hipStream_t s) {
+               size_t ws_bytes, const moe_ffn_routing* r, hipStream_t s, hipEvent_t* ev = nullptr) {
   if (!W || n < 1 || n > DECODE_MAX_TOKENS) return MOE_FFN_INVALID_ARG;
   if (!x || !out || !ws) return MOE_FFN_INVALID_ARG;
   const Dims& dm = W->dm;
@@ -276,10 +276,13 @@ int run_decode(const moe_ffn_weights* W, const float* x, int32_t n, float* out, 
   uint16_t* dxs = (uint16_t*)(base + L.dxs);
   float* partial = (float*)(base + L.partial);
   const int kk = dm.k + dm.has_shared;
+  auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
 
+  HIP_TRY(mark(0));
   HIP_TRY(launch_decode_router(x, n, dm.d, dm.d_pad, W->router_wt, W->has_bias ? W->router_bias : nullptr,
                                dm.E, dm.E64, logits, dm.has_shared ? W->sh_gate_vec : nullptr, gs, dxq,
                                dxs, s));
+  HIP_TRY(mark(1));
   DecodeArgs a{};
   a.logits = logits;
   a.n = n;
@@ -314,8 +317,11 @@ int run_decode(const moe_ffn_weights* W, const float* x, int32_t n, float* out, 
   a.dn_exp = W->dn_exp;
   a.partial = partial;
   HIP_TRY(launch_decode_gateup(a, s));
+  HIP_TRY(mark(2));
   HIP_TRY(launch_decode_down(a, s));
+  HIP_TRY(mark(3));
   HIP_TRY(launch_combine(partial, w, dm.has_shared ? gs : nullptr, n, dm.k, kk, dm.d, out, s));
+  HIP_TRY(mark(4));
 
   HIP_TRY(copy_routing(dm, n, r, ids, w, gs, exp_start, tok_i, tok_k, partial, s));
   if (r && r->xq)
@@ -473,6 +479,15 @@ int moe_ffn_prefill_profiled(const moe_ffn_weights* w, const float* x, int32_t n
 int moe_ffn_decode(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* out, void* ws,
                    size_t ws_bytes, const moe_ffn_routing* routing, hipStream_t stream) {
   return run_decode(w, x, n_tokens, out, ws, ws_bytes, routing, stream);
+}
+
+int moe_ffn_decode_profiled(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* out,
+                            void* ws, size_t ws_bytes, const moe_ffn_routing* routing,
+                            hipStream_t stream, hipEvent_t* stage_events) {
+  if (!stage_events) return MOE_FFN_INVALID_ARG;
+  for (int i = 0; i < MOE_FFN_N_DECODE_STAGE_EVENTS; ++i)
+    if (!stage_events[i]) return MOE_FFN_INVALID_ARG;
+  return run_decode(w, x, n_tokens, out, ws, ws_bytes, routing, stream, stage_events);
 }
 
 int moe_ffn_combine(const float* partial, const float* topk_w, const float* shared_gate, int32_t n,

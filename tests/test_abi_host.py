@@ -90,4 +90,7 @@ def test_stage_entry_points_validate_on_the_host(B):
     assert L.moe_ffn_prefill(None, 16, 4, 32, 64, 1 << 20, None, None) == -1
     assert L.moe_ffn_decode(None, 16, 9, 32, 64, 1 << 20, None, None) == -1
     assert L.moe_ffn_decode(None, 16, 0, 32, 64, 1 << 20, None, None) == -1
+    assert L.moe_ffn_decode_profiled(None, 16, 1, 32, 64, 1 << 20, None, None, None) == -1   # no events
+    ev = (C.c_void_p * 5)(*([None] * 5))
+    assert L.moe_ffn_decode_profiled(None, 16, 1, 32, 64, 1 << 20, None, None, ev) == -1     # null events
     assert L.moe_ffn_weights_destroy(None) == 0
