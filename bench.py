@@ -99,19 +99,24 @@ def stage_bytes(shape, n_tokens, counts):
     }
 
 
-KERNEL_SOURCES = ("gemm.hip", "internal.h", "device_util.h")
+# The sources each measured kernel is compiled from: a traffic summary is
+# valid only while their digest matches the one it records.
+KERNEL_SOURCES = {
+    "grouped_gemm": ("gemm.hip", "internal.h", "device_util.h"),
+    "decode_gemv": ("decode.hip", "internal.h", "device_util.h"),
+}
 
 
-def kernel_source_sha256():
-    """Digest of the sources the grouped GEMM kernels are compiled from."""
+def kernel_source_sha256(family="grouped_gemm"):
+    """Digest of the sources a kernel family is compiled from."""
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, "mixture_experts_ffn_gemm_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def read_traffic(kernel_tag):
+def read_traffic(kernel_tag, family="grouped_gemm"):
     """HBM bytes per launch of a kernel from the committed rocprofv3 PMC
     summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy kernel's
     reading), valid only while the kernel's sources are unchanged."""
@@ -123,7 +128,7 @@ def read_traffic(kernel_tag):
         if ":" in line and not line.startswith("#"):
             key, val = line.split(":", 1)
             rec[key.strip()] = val.strip()
-    if rec.get("sources_sha256") != kernel_source_sha256():
+    if rec.get("sources_sha256") != kernel_source_sha256(family):
         return None
     try:
         return int(float(rec["hbm_bytes_per_launch"]))
@@ -298,7 +303,8 @@ def main():
         roofline = {"bound": "hbm",
                     "kernel": "decode_gemv_kernel<true> (routing + gathered gate/up int8 matvec + SwiGLU + requantise)",
                     "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                    "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+                    "traffic": read_traffic(f"decode_gateup_{args.workload}", "decode_gemv"),
                     "algorithmic_bytes_per_launch": int(sb["route_gateup_swiglu"]), "avg_launch_us": round(gu_us, 2),
                     "layer_hbm_frac": round(sum(sb[k] for k in ("router_quantise", "route_gateup_swiglu", "down",
                                                                 "combine"))
