@@ -62,24 +62,23 @@ __global__ __launch_bounds__(256) void bucket_kernel(
   // small E several threads share an expert's column and their sums meet in LDS.
   __shared__ int s_part_tot[256], s_part_pre[256];
   const int nparts = max(1, 256 / E);
+  // Every workgroup reads every histogram, so this is the kernel's critical
+  // path: a thread requests RB histogram entries at once (the index clamped
+  // into the table, the surplus masked), one memory round trip per RB tiles.
+  constexpr int RB = 32;
   if (threadIdx.x < E * nparts) {
     const int e = threadIdx.x % E, part = threadIdx.x / E;
     int tot = 0, pre = 0;
-    int tt = part;
-    for (; tt + 3 * nparts < n_tiles; tt += 4 * nparts) {
-      int h[4];
+    for (int tt = part; tt < n_tiles; tt += RB * nparts) {
+      int h[RB];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) h[u] = hist[(size_t)(tt + u * nparts) * E + e];
+      for (int u = 0; u < RB; ++u) h[u] = hist[(size_t)min(tt + u * nparts, n_tiles - 1) * E + e];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        tot += h[u];
-        pre += (tt + u * nparts < tile) ? h[u] : 0;
+      for (int u = 0; u < RB; ++u) {
+        const int tu = tt + u * nparts;
+        tot += (tu < n_tiles) ? h[u] : 0;
+        pre += (tu < tile) ? h[u] : 0;
       }
-    }
-    for (; tt < n_tiles; tt += nparts) {
-      const int h = hist[(size_t)tt * E + e];
-      tot += h;
-      pre += (tt < tile) ? h : 0;
     }
     s_part_tot[threadIdx.x] = tot;
     s_part_pre[threadIdx.x] = pre;
