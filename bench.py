@@ -177,6 +177,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="olmoe_n2048")
+    ap.add_argument("--stack-form", choices=("fused-graph", "fused", "unfused"), default="fused-graph",
+                    help="stack workloads: each layer as moe_ffn_prefill_residual (combine + residual + "
+                         "RMSNorm in one kernel) replayed from one HIP graph of the whole pass, the same "
+                         "launched eagerly, or moe_ffn_prefill + moe_ffn_residual_rmsnorm launched eagerly")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-time budget of the CPU oracle sample (0 disables it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -230,12 +234,15 @@ def main():
     out = torch.empty((n, s.d), dtype=torch.float32, device=dev)
     ws = layer.workspace(n)
 
-    def stack_pass():
+    def stack_pass(st=stream):
         h.copy_(h0)
-        B.moe_ffn_residual_rmsnorm(h, None, x, n, s.d, eps, stream)
+        B.moe_ffn_residual_rmsnorm(h, None, x, n, s.d, eps, st)
         for lay in stack:
-            B.moe_ffn_prefill(lay.handle, x, n, out, ws, ws.numel(), None, stream)
-            B.moe_ffn_residual_rmsnorm(h, out, x, n, s.d, eps, stream)
+            if args.stack_form == "unfused":
+                B.moe_ffn_prefill(lay.handle, x, n, out, ws, ws.numel(), None, st)
+                B.moe_ffn_residual_rmsnorm(h, out, x, n, s.d, eps, st)
+            else:  # the next layer's input is written over this one's
+                B.moe_ffn_prefill_residual(lay.handle, x, n, h, x, eps, ws, ws.numel(), None, st)
     exp_start = torch.empty(s.n_experts + 1 + (1 if s.shared_ffn else 0), dtype=torch.int32, device=dev)
     step_fn = B.moe_ffn_decode if decode else B.moe_ffn_prefill
     step_fn(layer.handle, x, n, out, ws, ws.numel(), B.make_routing(exp_start=exp_start), stream)
@@ -246,14 +253,30 @@ def main():
 
     # Timed region: K plain prefill passes (the product entry point; no events
     # between its kernels), or K passes through the whole stack.
+    graph = None
     if n_layers > 1:
         for _ in range(args.warmup):
             stack_pass()
+        if args.stack_form == "fused-graph":
+            # one HIP graph of the whole pass (kernels only, no memset nodes),
+            # captured on a side stream and replayed on the timed stream
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream(dev)
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(graph, stream=side):
+                    stack_pass(torch.cuda.current_stream(dev))
+            torch.cuda.synchronize()
+            for _ in range(args.warmup):
+                graph.replay()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
-        if n_layers > 1:
+        if graph is not None:
+            graph.replay()
+        elif n_layers > 1:
             stack_pass()
         else:
             step_fn(layer.handle, x, n, out, ws, ws.numel(), None, stream)
@@ -352,6 +375,7 @@ def main():
     if n_layers > 1:
         res["stack"] = {"layers": n_layers, "ms_per_layer": round(ms_step / n_layers, 5),
                         "step": "h = h0; xn = RMSNorm(h); per layer: y = MoE(xn), h += y, xn = RMSNorm(h)",
+                        "form": args.stack_form,
                         "stages_and_roofline": "first layer, profiled passes on its normalised input"}
     for lay in stack:
         lay.close()

@@ -156,6 +156,23 @@ int moe_ffn_prefill(const moe_ffn_weights* w, const float* x, int32_t n_tokens, 
                     void* ws, size_t ws_bytes, const moe_ffn_routing* routing,
                     hipStream_t stream);
 
+/* The layer in a residual stack (#388 "Why 676 needs a per-layer rewrite":
+ * the residual stream runs through the layers one after another; the
+ * combine + residual + RMSNorm fusion of the stack).  Computes the layer's
+ * output y exactly as moe_ffn_prefill does, but never stores it: its combine
+ * adds y to the residual stream and normalises the result,
+ *   h  <- h + y                        (fp32 [n_tokens][d], in place)
+ *   xn <- h / sqrt(mean(h^2) + eps)    (fp32 [n_tokens][d], unit gain),
+ * with the same arithmetic, bit for bit, as moe_ffn_prefill followed by
+ * moe_ffn_residual_rmsnorm(h, y, xn) on 16-byte aligned rows.  h and xn are
+ * 16-byte aligned.  xn may be x itself (the next layer's input written over
+ * this one's); otherwise xn, h, x and the workspace must not overlap.
+ * eps >= 0.  The other arguments are those of moe_ffn_prefill.
+ * Returns without a host synchronisation. */
+int moe_ffn_prefill_residual(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* h,
+                             float* xn, float eps, void* ws, size_t ws_bytes,
+                             const moe_ffn_routing* routing, hipStream_t stream);
+
 /* moe_ffn_prefill with stage timing (#388 "Measurement discipline": per-phase
  * timing buckets measured warm, with setup excluded).  stage_events points to
  * MOE_FFN_N_STAGE_EVENTS caller-created hipEvent_t handles (host array); event
@@ -207,7 +224,9 @@ int moe_ffn_quantize(const float* v, int64_t n_values, int8_t* q, uint16_t* scal
  * needs a per-layer rewrite": the residual stream is sequential across
  * layers).  h fp32 [n][d] is updated in place to h + y when y != NULL (y
  * fp32 [n][d]); then xn fp32 [n][d] receives h / sqrt(mean(h^2) + eps)
- * (unit gain).  xn must not overlap h or y. */
+ * (unit gain).  xn must not overlap h or y.  When d % 4 == 0 and h, y, xn
+ * are 16-byte aligned, the sum of squares is taken in the order of
+ * moe_ffn_prefill_residual's fused combine (4-column chunks per thread). */
 int moe_ffn_residual_rmsnorm(float* h, const float* y, float* xn, int32_t n, int32_t d,
                              float eps, hipStream_t stream);
 

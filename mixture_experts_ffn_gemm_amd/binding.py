@@ -24,7 +24,8 @@ MOE_FFN_OUT_OF_MEMORY = -4
 MOE_FFN_HIP_ERROR = -5
 
 EXPORTED = ("moe_ffn_weights_create", "moe_ffn_weights_destroy", "moe_ffn_weights_dims",
-            "moe_ffn_workspace_size", "moe_ffn_prefill", "moe_ffn_prefill_profiled", "moe_ffn_decode",
+            "moe_ffn_workspace_size", "moe_ffn_prefill", "moe_ffn_prefill_residual", "moe_ffn_prefill_profiled",
+            "moe_ffn_decode",
             "moe_ffn_decode_profiled", "moe_ffn_combine",
             "moe_ffn_quantize", "moe_ffn_residual_rmsnorm", "moe_ffn_status_str")
 
@@ -65,6 +66,7 @@ def lib():
             "moe_ffn_weights_dims": [vp, C.POINTER(moe_ffn_dims)],
             "moe_ffn_workspace_size": [vp, i32, C.POINTER(sz)],
             "moe_ffn_prefill": [vp, vp, i32, vp, vp, sz, C.POINTER(moe_ffn_routing), vp],
+            "moe_ffn_prefill_residual": [vp, vp, i32, vp, vp, C.c_float, vp, sz, C.POINTER(moe_ffn_routing), vp],
             "moe_ffn_decode": [vp, vp, i32, vp, vp, sz, C.POINTER(moe_ffn_routing), vp],
             "moe_ffn_prefill_profiled": [vp, vp, i32, vp, vp, sz, C.POINTER(moe_ffn_routing), vp,
                                          C.POINTER(vp)],
@@ -153,6 +155,15 @@ def moe_ffn_prefill(handle: int, x, n_tokens: int, out, ws, ws_bytes: int,
     rc = lib().moe_ffn_prefill(handle, _ptr(x), int(n_tokens), _ptr(out), _ptr(ws), int(ws_bytes),
                                C.byref(routing) if routing is not None else None, _stream(stream))
     _check("moe_ffn_prefill", rc)
+
+
+def moe_ffn_prefill_residual(handle: int, x, n_tokens: int, h, xn, eps: float, ws, ws_bytes: int,
+                             routing: Optional[moe_ffn_routing] = None, stream=None) -> None:
+    """The layer inside a residual stack: h += layer(x), xn = RMSNorm(h) (xn may be x)."""
+    rc = lib().moe_ffn_prefill_residual(handle, _ptr(x), int(n_tokens), _ptr(h), _ptr(xn), float(eps),
+                                        _ptr(ws), int(ws_bytes),
+                                        C.byref(routing) if routing is not None else None, _stream(stream))
+    _check("moe_ffn_prefill_residual", rc)
 
 
 N_STAGE_EVENTS = 7

@@ -150,18 +150,38 @@ hipError_t copy_routing(const Dims& dm, int n, const moe_ffn_routing* r, const i
   return e;
 }
 
+// The stack form of a layer: instead of writing the layer's output, its
+// combine adds it to the residual stream h and writes the next layer's
+// input xn = RMSNorm(h).
+struct ResidualOut {
+  float* h;
+  float* xn;
+  float eps;
+};
+
 int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, void* ws,
-              size_t ws_bytes, const moe_ffn_routing* r, hipStream_t s, hipEvent_t* ev = nullptr) {
+              size_t ws_bytes, const moe_ffn_routing* r, hipStream_t s, hipEvent_t* ev = nullptr,
+              const ResidualOut* res = nullptr) {
   if (!W || n < 0 || n > MAX_TOKENS) return MOE_FFN_INVALID_ARG;
   if (n == 0) return current_device_matches(W);  // no-op; buffers may be NULL
-  if (!x || !out || !ws) return MOE_FFN_INVALID_ARG;
+  if (!x || !ws || (!res && !out)) return MOE_FFN_INVALID_ARG;
   const Dims& dm = W->dm;
   const WsLayout L = ws_layout(dm, n);
   if (ws_bytes < L.total) return MOE_FFN_WORKSPACE_TOO_SMALL;
-  if (((uintptr_t)ws & 255u) || ((uintptr_t)x & 15u) || ((uintptr_t)out & 15u))
+  if (((uintptr_t)ws & 255u) || ((uintptr_t)x & 15u) || (!res && ((uintptr_t)out & 15u)))
     return MOE_FFN_INVALID_ARG;
   const size_t xb = (size_t)n * dm.d * sizeof(float);
-  if (overlaps(x, xb, out, xb) || overlaps(out, xb, ws, ws_bytes)) return MOE_FFN_INVALID_ARG;
+  if (res) {
+    // xn may be x itself: x is last read before the combine runs
+    if (!res->h || !res->xn || !(res->eps >= 0.0f)) return MOE_FFN_INVALID_ARG;
+    if (((uintptr_t)res->h & 15u) || ((uintptr_t)res->xn & 15u)) return MOE_FFN_INVALID_ARG;
+    if (overlaps(res->h, xb, x, xb) || overlaps(res->h, xb, ws, ws_bytes) ||
+        overlaps(res->xn, xb, res->h, xb) || overlaps(res->xn, xb, ws, ws_bytes) ||
+        (res->xn != x && overlaps(res->xn, xb, x, xb)))
+      return MOE_FFN_INVALID_ARG;
+  } else if (overlaps(x, xb, out, xb) || overlaps(out, xb, ws, ws_bytes)) {
+    return MOE_FFN_INVALID_ARG;
+  }
   if (r && r->xq && ((uintptr_t)r->xq & 15u)) return MOE_FFN_INVALID_ARG;
   const int dev_ok = current_device_matches(W);
   if (dev_ok != MOE_FFN_OK) return dev_ok;
@@ -236,7 +256,11 @@ int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, v
   HIP_TRY(mark(4));
   HIP_TRY(launch_down(a, s));
   HIP_TRY(mark(5));
-  HIP_TRY(launch_combine(partial, w, dm.has_shared ? gs : nullptr, n, dm.k, kk, dm.d, out, s));
+  if (res)
+    HIP_TRY(launch_combine_residual_rmsnorm(partial, w, dm.has_shared ? gs : nullptr, n, dm.k, kk, dm.d,
+                                            res->h, res->xn, res->eps, s));
+  else
+    HIP_TRY(launch_combine(partial, w, dm.has_shared ? gs : nullptr, n, dm.k, kk, dm.d, out, s));
   HIP_TRY(mark(6));
 
   HIP_TRY(copy_routing(dm, n, r, ids, w, gs, exp_start, tok_i, tok_k, partial, s));
@@ -465,6 +489,13 @@ int moe_ffn_workspace_size(const moe_ffn_weights* w, int32_t max_tokens, size_t*
 int moe_ffn_prefill(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* out,
                     void* ws, size_t ws_bytes, const moe_ffn_routing* routing, hipStream_t stream) {
   return run_layer(w, x, n_tokens, out, ws, ws_bytes, routing, stream);
+}
+
+int moe_ffn_prefill_residual(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* h,
+                             float* xn, float eps, void* ws, size_t ws_bytes,
+                             const moe_ffn_routing* routing, hipStream_t stream) {
+  const ResidualOut res{h, xn, eps};
+  return run_layer(w, x, n_tokens, nullptr, ws, ws_bytes, routing, stream, nullptr, &res);
 }
 
 int moe_ffn_prefill_profiled(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* out,

@@ -236,6 +236,9 @@ hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s);
 
 hipError_t launch_combine(const float* partial, const float* w, const float* gs, int n, int k,
                           int kk, int d, float* out, hipStream_t s);
+hipError_t launch_combine_residual_rmsnorm(const float* partial, const float* w, const float* gs, int n,
+                                           int k, int kk, int d, float* h, float* xn, float eps,
+                                           hipStream_t s);
 hipError_t launch_residual_rmsnorm(float* h, const float* y, float* xn, int n, int d, float eps,
                                    hipStream_t s);
 

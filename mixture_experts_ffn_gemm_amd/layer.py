@@ -79,6 +79,13 @@ class MoeLayer:
     def prefill(self, x: torch.Tensor, out: Optional[torch.Tensor] = None, routing=None, stream=None):
         return self._run(B.moe_ffn_prefill, x, out, routing, stream)
 
+    def prefill_residual(self, x: torch.Tensor, h: torch.Tensor, xn: torch.Tensor, eps: float = 1e-5,
+                         routing=None, stream=None):
+        """The layer inside a residual stack: h += layer(x), xn = RMSNorm(h); xn may be x."""
+        n = x.shape[0]
+        ws = self.workspace(n)
+        B.moe_ffn_prefill_residual(self.handle, x, n, h, xn, eps, ws, ws.numel(), routing, stream)
+
     def decode(self, x: torch.Tensor, out: Optional[torch.Tensor] = None, routing=None, stream=None):
         return self._run(B.moe_ffn_decode, x, out, routing, stream)
 

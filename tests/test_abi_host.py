@@ -88,6 +88,7 @@ def test_stage_entry_points_validate_on_the_host(B):
     dm = B.moe_ffn_dims()
     assert L.moe_ffn_weights_dims(None, C.byref(dm)) == -1
     assert L.moe_ffn_prefill(None, 16, 4, 32, 64, 1 << 20, None, None) == -1
+    assert L.moe_ffn_prefill_residual(None, 16, 4, 32, 16, 1e-5, 64, 1 << 20, None, None) == -1
     assert L.moe_ffn_decode(None, 16, 9, 32, 64, 1 << 20, None, None) == -1
     assert L.moe_ffn_decode(None, 16, 0, 32, 64, 1 << 20, None, None) == -1
     assert L.moe_ffn_decode_profiled(None, 16, 1, 32, 64, 1 << 20, None, None, None) == -1   # no events

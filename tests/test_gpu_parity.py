@@ -189,6 +189,86 @@ def test_shape_edge_cases(case, n):
     check_outputs(lw, x, g)
 
 
+# ------------------------------------------------------------- stack form
+@pytest.mark.parametrize("case", [1, 2, 5])
+def test_prefill_residual_matches_unfused(case):
+    """moe_ffn_prefill_residual (combine fused with the residual add and the
+    RMSNorm) against moe_ffn_prefill followed by moe_ffn_residual_rmsnorm: h
+    and xn bit for bit, also with xn written over the layer's own input.
+    Cases: top-1, shared expert with skewed routing, and E = 256 (routing in
+    its own launch)."""
+    from mixture_experts_ffn_gemm_amd import binding as B
+    from mixture_experts_ffn_gemm_amd.layer import MoeLayer
+    shape, lw = mw.random_shape_case(case, **SHAPES[case])
+    n, d, eps = 53, shape.d, 1e-5
+    dev = torch.device("cuda")
+    say(f"prefill_residual case {case}: d={d} E={shape.n_experts} k={shape.top_k} n={n}")
+    x = torch.from_numpy(mw.make_tokens(300 + case, n, d)).to(dev)
+    h0 = torch.from_numpy(mw.make_tokens(400 + case, n, d)).to(dev)
+    layer = MoeLayer.from_workload(lw)
+    try:
+        y = layer.prefill(x)
+        h_ref, xn_ref = h0.clone(), torch.empty_like(h0)
+        B.moe_ffn_residual_rmsnorm(h_ref, y, xn_ref, n, d, eps)
+        h1, xn1 = h0.clone(), torch.full_like(h0, float("nan"))
+        layer.prefill_residual(x, h1, xn1, eps)
+        h2, x2 = h0.clone(), x.clone()
+        layer.prefill_residual(x2, h2, x2, eps)
+        torch.cuda.synchronize()
+    finally:
+        layer.close()
+    assert torch.equal(h1, h_ref) and torch.equal(h2, h_ref)
+    assert torch.equal(xn1, xn_ref) and torch.equal(x2, xn_ref)
+
+
+def test_stack_graph_replays_match_eager():
+    """Two layers in the stack form captured in one HIP graph (no memset
+    nodes: the library issues kernels only) and replayed three times, with
+    eager passes and host synchronisations in between; every replay gives the
+    eager pass's residual stream and next input bit for bit."""
+    from mixture_experts_ffn_gemm_amd.layer import MoeLayer
+    shapes = [mw.random_shape_case(2, **SHAPES[2]), mw.random_shape_case(12, **SHAPES[2])]
+    d, n, eps = SHAPES[2]["d"], 37, 1e-5
+    dev = torch.device("cuda")
+    layers = [MoeLayer.from_workload(lw) for _, lw in shapes]
+    try:
+        h_in = torch.from_numpy(mw.make_tokens(500, n, d)).to(dev)
+        x_in = torch.from_numpy(mw.make_tokens(501, n, d)).to(dev)
+        h, x = torch.empty_like(h_in), torch.empty_like(x_in)
+        for lay in layers:
+            lay.workspace(n)   # allocated before the capture
+
+        def stack_pass(stream=None):
+            h.copy_(h_in)
+            x.copy_(x_in)
+            for lay in layers:
+                lay.prefill_residual(x, h, x, eps, stream=stream)
+
+        stack_pass()
+        torch.cuda.synchronize()
+        h_eager, x_eager = h.clone(), x.clone()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                stack_pass(stream=torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        for rep in range(3):
+            h.zero_()
+            x.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(h, h_eager) and torch.equal(x, x_eager), f"replay {rep} differs"
+            say(f"graph replay {rep}: bit-identical to the eager pass")
+            stack_pass()
+            torch.cuda.synchronize()
+            assert torch.equal(h, h_eager) and torch.equal(x, x_eager)
+    finally:
+        for lay in layers:
+            lay.close()
+
+
 # Decode: the same shapes through moe_ffn_decode, plus one whose K spans
 # several staged activation passes of the decode matvecs (d and F above 2048,
 # both ragged against the 128-value k-step) and whose router chain runs past
