@@ -73,22 +73,22 @@ __device__ __forceinline__ void router_fma16(float& acc0, float& acc1, float xa,
 // Routing of one tile of ROUTE_TILE tokens, 16 threads per token (threads
 // tid < ROUTE_THREADS of the workgroup; every thread of the workgroup calls
 // this, since it meets workgroup barriers).  The tile's logits l[token][e]
-// are in LDS.  Each (token,
-// expert) finds its rank among the token's experts -- the number of experts
-// with a larger logit, or an equal logit and a lower id -- and the experts of
-// rank < k take slot = rank.  This is the top-k of the contract (logit
-// descending, id ascending) computed without any serial reduction.  Then
+// are in LDS.  Top-k by the contract's order (logit descending, id
+// ascending): each expert's 64-bit key orders exactly that way and is unique,
+// the token's 16 threads hold its keys in registers (expert g + 16c in thread
+// g, NKEY >= E/16 of them), and slot r takes the largest key left after r
+// rounds of a maximum over the 16 threads, its owner clearing it.  Then
 // softmax over all E, optional renormalisation, and the per-expert rank of
 // each (token, slot) pair among the tile's pairs in (token, slot) order, with
 // the tile's histogram, for the bucketing kernel.
 struct RouteLds {
   float l[ROUTE_TILE][MAX_EXPERTS];
-  unsigned long long key[ROUTE_TILE][MAX_EXPERTS];
   int ids[ROUTE_TILE * MAX_TOPK];
   float val[ROUTE_TILE][MAX_TOPK];
   int cnt[MAX_EXPERTS];
 };
 
+template <int NKEY>
 __device__ __forceinline__ void route_tile(RouteLds& R, int tile, int t0, int nt, int E, int k, int norm, int tid,
                            int nthreads, int32_t* __restrict__ ids, float* __restrict__ wout,
                            int32_t* __restrict__ rank, int32_t* __restrict__ hist) {
@@ -97,36 +97,34 @@ __device__ __forceinline__ void route_tile(RouteLds& R, int tile, int t0, int nt
   // ranks: thread (token tl = tid/16, expert group g = tid%16) owns experts g + 16c
   const int tl = tid >> 4, g = tid & 15;
   const bool mine = tid < ROUTE_THREADS;
-  // Padding instead of per-element tests (a test of a uniform bound next to a
-  // per-lane compare becomes a scalar mask operation per element): keys up to
-  // E rounded up to 32 (0 past E, below every real key), and ids -1 in every
-  // slot that the ranks below do not fill (slots >= k, tokens >= nt).
-  const int E32 = (E + 31) & ~31;
   if (mine) {
-    for (int e = g; e < E32; e += 16) R.key[tl][e] = e < E ? topk_key(R.l[tl][e], e) : 0ull;
+    // slots >= k and absent tokens keep -1 (the same wavefront's later
+    // stores below land after this one)
     R.ids[tl * MAX_TOPK + g] = -1;
-  }
-  __syncthreads();
-  if (mine)
-    for (int e = g; e < E; e += 16) {
-      const unsigned long long ke = R.key[tl][e];
-      int r = 0;
-      // the rank of e is the number of larger keys; 32 keys per pass, all
-      // reads issued before the compares
-      // (unconditional reads: a conditional read would be a branch of its own
-      // and wait alone)
-      for (int e0 = 0; e0 < E; e0 += 32) {
-        ulonglong2 v[16];
+    unsigned long long key[NKEY];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const ulonglong2*>(&R.key[tl][e0 + 2 * i]);
+    for (int c = 0; c < NKEY; ++c) {
+      const int e = g + 16 * c;
+      key[c] = (e < E) ? topk_key(R.l[tl][e], e) : 0ull;  // 0: below every real key
+    }
+    for (int r = 0; r < k; ++r) {
+      unsigned long long m = 0ull;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) r += (int)(v[i].x > ke) + (int)(v[i].y > ke);
+      for (int c = 0; c < NKEY; ++c) m = key[c] > m ? key[c] : m;
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) {
+        const unsigned long long o = __shfl_xor(m, off, 16);
+        m = o > m ? o : m;
       }
-      if (r < k && tl < nt) {
+#pragma unroll
+      for (int c = 0; c < NKEY; ++c) key[c] = key[c] == m ? 0ull : key[c];
+      if (g == 0 && tl < nt) {
+        const int e = (int)~(uint32_t)m;
         R.ids[tl * MAX_TOPK + r] = e;
         R.val[tl][r] = R.l[tl][e];
       }
     }
+  }
   __syncthreads();
 
   if (mine) {
@@ -317,7 +315,7 @@ __global__ __launch_bounds__(256, 1) void router_kernel(
       R.l[tl + 1][e] = bias ? acc1 + bb : acc1;
     }
     const int t0 = blockIdx.x * ROUTE_TILE;
-    route_tile(R, blockIdx.x, t0, min(ROUTE_TILE, n - t0), E, k, norm, threadIdx.x, 256, ids, wout,
+    route_tile<4>(R, blockIdx.x, t0, min(ROUTE_TILE, n - t0), E, k, norm, threadIdx.x, 256, ids, wout,
                rank, hist);
   } else {
     if (e < E) {
@@ -442,7 +440,7 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(
   const int t0 = blockIdx.x * ROUTE_TILE;
   const int nt = min(ROUTE_TILE, n - t0);
   route_load_logits(R, logits, t0, nt, E, threadIdx.x, ROUTE_THREADS);
-  route_tile(R, blockIdx.x, t0, nt, E, k, norm, threadIdx.x, ROUTE_THREADS, ids, wout, rank, hist);
+  route_tile<MAX_EXPERTS / 16>(R, blockIdx.x, t0, nt, E, k, norm, threadIdx.x, ROUTE_THREADS, ids, wout, rank, hist);
 }
 
 // ---------------------------------------------------------------- decode
