@@ -177,10 +177,13 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="olmoe_n2048")
-    ap.add_argument("--stack-form", choices=("fused-graph", "fused", "unfused"), default="fused-graph",
+    ap.add_argument("--stack-form", choices=("fused", "fused-graph", "unfused"), default="fused",
                     help="stack workloads: each layer as moe_ffn_prefill_residual (combine + residual + "
-                         "RMSNorm in one kernel) replayed from one HIP graph of the whole pass, the same "
-                         "launched eagerly, or moe_ffn_prefill + moe_ffn_residual_rmsnorm launched eagerly")
+                         "RMSNorm in one kernel), the same replayed from one HIP graph of the whole pass, "
+                         "or moe_ffn_prefill + moe_ffn_residual_rmsnorm")
+    ap.add_argument("--decode-launch", choices=("eager", "graph"), default="eager",
+                    help="decode workloads: call moe_ffn_decode directly, or replay one HIP graph of a call "
+                         "per timed step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-time budget of the CPU oracle sample (0 disables it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -252,8 +255,22 @@ def main():
     counts = np.diff(exp_start.cpu().numpy())
 
     # Timed region: K plain prefill passes (the product entry point; no events
-    # between its kernels), or K passes through the whole stack.
+    # between its kernels), K passes through the whole stack, or K decode
+    # calls.
     graph = None
+    if decode and args.decode_launch == "graph":
+        # one HIP graph of a decode call (kernels only), captured on a side
+        # stream and replayed on the timed stream
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                step_fn(layer.handle, x, n, out, ws, ws.numel(), None, torch.cuda.current_stream(dev))
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
     if n_layers > 1:
         for _ in range(args.warmup):
             stack_pass()
@@ -369,6 +386,7 @@ def main():
         "config": {"workload": args.workload, **{k: v for k, v in mw.describe(args.workload).items()
                                                  if k != "workload"}},
         "grouped_gemm_int8_frac": round(gemm_frac, 4),
+        "launch": ("graph replay" if graph is not None else "eager calls"),
         "experts_touched": int((counts[:s.n_experts] > 0).sum()),
         "stages": stages, "roofline": roofline, "cpu_baseline": cpu,
     }

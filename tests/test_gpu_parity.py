@@ -269,6 +269,43 @@ def test_stack_graph_replays_match_eager():
             lay.close()
 
 
+def test_decode_graph_replays_match_eager():
+    """A moe_ffn_decode call captured in a HIP graph and replayed three times,
+    with eager calls and host synchronisations in between: every replay's
+    output is the eager call's, bit for bit."""
+    from mixture_experts_ffn_gemm_amd import binding as B
+    from mixture_experts_ffn_gemm_amd.layer import MoeLayer
+    shape, lw = mw.random_shape_case(2, **SHAPES[2])
+    n = 3
+    dev = torch.device("cuda")
+    layer = MoeLayer.from_workload(lw)
+    try:
+        x = torch.from_numpy(mw.make_tokens(600, n, shape.d)).to(dev)
+        out = torch.empty((n, shape.d), dtype=torch.float32, device=dev)
+        ws = layer.workspace(n)
+        B.moe_ffn_decode(layer.handle, x, n, out, ws, ws.numel(), None)
+        torch.cuda.synchronize()
+        ref = out.clone()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                B.moe_ffn_decode(layer.handle, x, n, out, ws, ws.numel(), None, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        for rep in range(3):
+            out.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref), f"replay {rep} differs"
+            B.moe_ffn_decode(layer.handle, x, n, out, ws, ws.numel(), None)
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref)
+        say("decode graph: 3 replays bit-identical to the eager call")
+    finally:
+        layer.close()
+
+
 # Decode: the same shapes through moe_ffn_decode, plus one whose K spans
 # several staged activation passes of the decode matvecs (d and F above 2048,
 # both ragged against the 128-value k-step) and whose router chain runs past
