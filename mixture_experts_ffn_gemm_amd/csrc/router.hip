@@ -21,11 +21,13 @@ constexpr int RJC = 64;          // router: j values per LDS chunk
 constexpr int RJQ = RJC / 4;     // 4-j quads per chunk
 constexpr int RNB = 6;           // chunk buffers in the LDS ring (108 KiB: one workgroup per CU)
 constexpr int RPF = RNB - 1;     // chunks copied ahead
-constexpr int RDMA = 6;          // copies per wavefront per chunk
-constexpr int RT = 2;            // tokens per wavefront
+constexpr int RDMA = 3;          // copies per wavefront per chunk
+constexpr int RT = 1;            // tokens per wavefront
+constexpr int RW = 8;            // wavefronts per workgroup
 constexpr int R_WB = RJQ * 64 * 16;       // transposed router slab per chunk (16 KiB)
-constexpr int R_XB = 4 * RT * RJC * 4;    // the workgroup's token rows per chunk (2 KiB)
+constexpr int R_XB = RW * RT * RJC * 4;   // the workgroup's token rows per chunk (2 KiB)
 constexpr int R_BUF = R_WB + R_XB;
+static_assert(RJQ == 2 * RW && RDMA == 3, "each wavefront copies two slab quads and its token row per chunk");
 
 // global -> LDS copies: lane l writes LDS address m0 + size * l
 __device__ __forceinline__ void rdma16(const void* base, uint32_t voff, uint32_t lds) {
@@ -45,30 +47,27 @@ __device__ __forceinline__ void rwait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// 16 steps of two fp32 fused multiply-add chains: for i = 0..15,
-//   acc0 = fma(xa[i], w[i], acc0); acc1 = fma(xb[i], w[i], acc1),
-// where xa/xb[i] is lane i of each 16-lane row of xa/xb, broadcast to the
-// row by DPP row_newbcast (every row holds the same 16 values), and w[i] is
-// this lane's weight (quads w0..w3).  v_fmac_f32 is fused (one rounding), as
-// the chain's definition requires; the leading s_nop covers the wait states
-// a DPP read needs after a VALU write of its source.
-#define RFMA2(I, W)                                                                          \
-  "v_fmac_f32_dpp %0, %2, " W " row_newbcast:" #I " row_mask:0xf bank_mask:0xf\n\t"         \
-  "v_fmac_f32_dpp %1, %3, " W " row_newbcast:" #I " row_mask:0xf bank_mask:0xf\n\t"
-__device__ __forceinline__ void router_fma16(float& acc0, float& acc1, float xa, float xb,
-                                             const f4v& w0, const f4v& w1, const f4v& w2,
-                                             const f4v& w3) {
+// 16 steps of one fp32 fused multiply-add chain: for i = 0..15,
+//   acc0 = fma(xa[i], w[i], acc0),
+// where xa[i] is lane i of this lane's 16-lane row of xa, broadcast to the row
+// by DPP row_newbcast (every row holds the same 16 values), and w[i] is this
+// lane's weight (quads w0..w3).  v_fmac_f32 is fused (one rounding), as the
+// chain's definition requires; the leading s_nop covers the wait states a DPP
+// read needs after a VALU write of its source.
+#define RFMA1(I, W) "v_fmac_f32_dpp %0, %1, " W " row_newbcast:" #I " row_mask:0xf bank_mask:0xf\n\t"
+__device__ __forceinline__ void router_fma16_1(float& acc0, float xa, const f4v& w0, const f4v& w1,
+                                               const f4v& w2, const f4v& w3) {
   asm volatile("s_nop 1\n\t"
-      RFMA2(0, "%4") RFMA2(1, "%5") RFMA2(2, "%6") RFMA2(3, "%7")
-      RFMA2(4, "%8") RFMA2(5, "%9") RFMA2(6, "%10") RFMA2(7, "%11")
-      RFMA2(8, "%12") RFMA2(9, "%13") RFMA2(10, "%14") RFMA2(11, "%15")
-      RFMA2(12, "%16") RFMA2(13, "%17") RFMA2(14, "%18") RFMA2(15, "%19")
-      : "+v"(acc0), "+v"(acc1)
-      : "v"(xa), "v"(xb), "v"(w0.x), "v"(w0.y), "v"(w0.z), "v"(w0.w), "v"(w1.x), "v"(w1.y),
+      RFMA1(0, "%2") RFMA1(1, "%3") RFMA1(2, "%4") RFMA1(3, "%5")
+      RFMA1(4, "%6") RFMA1(5, "%7") RFMA1(6, "%8") RFMA1(7, "%9")
+      RFMA1(8, "%10") RFMA1(9, "%11") RFMA1(10, "%12") RFMA1(11, "%13")
+      RFMA1(12, "%14") RFMA1(13, "%15") RFMA1(14, "%16") RFMA1(15, "%17")
+      : "+v"(acc0)
+      : "v"(xa), "v"(w0.x), "v"(w0.y), "v"(w0.z), "v"(w0.w), "v"(w1.x), "v"(w1.y),
         "v"(w1.z), "v"(w1.w), "v"(w2.x), "v"(w2.y), "v"(w2.z), "v"(w2.w), "v"(w3.x), "v"(w3.y),
         "v"(w3.z), "v"(w3.w));
 }
-#undef RFMA2
+#undef RFMA1
 
 // Routing of one tile of ROUTE_TILE tokens, 16 threads per token (threads
 // tid < ROUTE_THREADS of the workgroup; every thread of the workgroup calls
@@ -188,27 +187,32 @@ __device__ __forceinline__ void route_tile(RouteLds& R, int tile, int t0, int nt
   for (int e = tid; e < E; e += nthreads) hist[(size_t)tile * E + e] = R.cnt[e];
 }
 
-// Router logits for 4*RT tokens x 64 experts per workgroup (lane = expert, RT
-// tokens per wavefront).  Each logit is one fp32 fused multiply-add chain over
-// ascending j, from +0, then + bias (a separate fp32 add); the chain order is
-// the contract that makes top-k ids reproducible bit for bit.
+// Router logits for RW tokens x 64 experts per workgroup (lane = expert, one
+// token per wavefront, two wavefronts per SIMD).  Each logit is one fp32 fused
+// multiply-add chain over ascending j, from +0, then + bias (a separate fp32
+// add); the chain order is the contract that makes top-k ids reproducible bit
+// for bit.
 //
-// The chains are latency- and operand-bound (two per lane across the whole
-// chip at OLMoE sizes), so every operand takes the cheapest path.  Per chunk of
-// 64 j the transposed router slab (64 experts x 64 j, 16 KiB) and the
-// workgroup's 8 token rows (2 KiB) are copied into a ring of LDS buffers RPF
-// chunks ahead.  Per 16 j a lane reads its expert's 16 weights (4 x 16 B) and
-// one value of each of its wavefront's two token rows (lane i of every
-// 16-lane row reads column i), and the token value of each step reaches all
-// lanes through a DPP row broadcast inside the FMA: 6 LDS reads per 32 FMAs.
-// The reads of each 16 j are issued three 16-j steps before they are used.  Only the d/16 sub-chunks inside d are visited (d % 32 == 0), so
-// no padding term enters a chain.
+// The chains are latency- and operand-bound (one per lane across the whole
+// chip at OLMoE sizes), so every operand takes the cheapest path, and two
+// wavefronts share each SIMD so that one's LDS reads overlap the other's
+// chain.  Per chunk of 64 j the transposed router slab (64 experts x 64 j,
+// 16 KiB) and the workgroup's 8 token rows (2 KiB) are copied into a ring of
+// LDS buffers RPF chunks ahead.  Per 16 j a lane reads its expert's 16
+// weights (4 x 16 B) and one value of its wavefront's token row (lane i of
+// every 16-lane row reads column i), and the token value of each step
+// reaches all lanes through a DPP row broadcast inside the FMA.  The reads of
+// each 16 j are issued three 16-j steps before they are used.  Only the d/16
+// sub-chunks inside d are visited (d % 32 == 0), so no padding term enters a
+// chain.  (Measured: two wavefronts of one token each run the launch 14 %
+// faster than one wavefront per SIMD holding two tokens' chains, although
+// they read the slab from LDS twice as often.)
 //
 // FUSE (E <= 64, so a workgroup holds every logit of its ROUTE_TILE tokens):
 // the logits stay in LDS and the workgroup routes its tile (route_tile), with
 // no logits in global memory and no separate routing launch.
 template <bool FUSE>
-__global__ __launch_bounds__(256, 1) void router_kernel(
+__global__ __launch_bounds__(512, 1) void router_kernel(
     const float* __restrict__ x, int n, int d, const float* __restrict__ wt,
     const float* __restrict__ bias, int E, int E64, float* __restrict__ logits, int k, int norm,
     int32_t* __restrict__ ids, float* __restrict__ wout, int32_t* __restrict__ rank,
@@ -217,25 +221,23 @@ __global__ __launch_bounds__(256, 1) void router_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int eg = blockIdx.y;
-  const int tw = blockIdx.x * 4 * RT + wave * RT;  // this wavefront's first token
+  const int tw = blockIdx.x * RW * RT + wave * RT;  // this wavefront's token
   const int C = (d + RJC - 1) / RJC, NQ = d / 4;
   const uint32_t lbase = (uint32_t)(uintptr_t)(lds_char*)ring;
   const float* xr0 = x + (size_t)min(tw, n - 1) * d;
-  const float* xr1 = x + (size_t)min(tw + 1, n - 1) * d;
 
-  // Wavefront w copies quads 4w..4w+3 of the slab (1 KiB each: the 64
-  // experts' 4 j; quads past d re-read the last one) and its own two token
-  // rows (columns past d re-read column d-1).
+  // Wavefront w copies quads 2w, 2w+1 of the slab (1 KiB each: the 64
+  // experts' 4 j; quads past d re-read the last one) and its own token row
+  // (columns past d re-read column d-1).
   auto issue = [&](int c) {
     const uint32_t buf = lbase + (uint32_t)((c % RNB) * R_BUF);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int jq = min(c * RJQ + 4 * wave + i, NQ - 1);
-      rdma16(wt + ((size_t)jq * E64 + eg * 64) * 4, lane * 16, buf + (4 * wave + i) * 1024);
+    for (int i = 0; i < 2; ++i) {
+      const int jq = min(c * RJQ + 2 * wave + i, NQ - 1);
+      rdma16(wt + ((size_t)jq * E64 + eg * 64) * 4, lane * 16, buf + (2 * wave + i) * 1024);
     }
     const uint32_t xo = (uint32_t)min(c * RJC + lane, d - 1) * 4;
     rdma4(xr0, xo, buf + R_WB + (RT * wave) * (RJC * 4));
-    rdma4(xr1, xo, buf + R_WB + (RT * wave + 1) * (RJC * 4));
   };
   const int np = min(RPF, C);
   for (int c = 0; c < np; ++c) issue(c);
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(256, 1) void router_kernel(
   };
   // operands of 16-j sub-chunks, a ring of 4 (read 3 sub-chunks ahead)
   f4v w[4][4];
-  float xa[4], xb[4];
+  float xa[4];
   auto load_sub = [&](int sub, int b) {
     const int c = sub >> 2, q0 = (sub & 3) * 4;
     const char* buf = ring + (c % RNB) * R_BUF;
@@ -266,9 +268,8 @@ __global__ __launch_bounds__(256, 1) void router_kernel(
     for (int q = 0; q < 4; ++q) w[b][q] = *reinterpret_cast<const f4v*>(buf + (q0 + q) * 1024 + lane * 16);
     const float* xrow = reinterpret_cast<const float*>(buf + R_WB) + (RT * wave) * RJC + q0 * 4 + (lane & 15);
     xa[b] = xrow[0];
-    xb[b] = xrow[RJC];
   };
-  float acc0 = 0.0f, acc1 = 0.0f;
+  float acc0 = 0.0f;
   // One full chunk (4 sub-chunks of 16 j) per iteration, then the trailing
   // half chunk when d % 64 == 32.  The reads of sub-chunk s+3 are issued
   // before sub-chunk s is computed, unconditionally (past the last sub-chunk
@@ -296,32 +297,30 @@ __global__ __launch_bounds__(256, 1) void router_kernel(
       }
       if (busy) {
         load_sub(4 * c + q + 3, (q + 3) & 3);
-        router_fma16(acc0, acc1, xa[q], xb[q], w[q][0], w[q][1], w[q][2], w[q][3]);
+        router_fma16_1(acc0, xa[q], w[q][0], w[q][1], w[q][2], w[q][3]);
       }
     }
   }
   if (busy && CF < C) {  // 32 trailing j: sub-chunks 4 CF and 4 CF + 1 (already requested)
-    router_fma16(acc0, acc1, xa[0], xb[0], w[0][0], w[0][1], w[0][2], w[0][3]);
-    router_fma16(acc0, acc1, xa[1], xb[1], w[1][0], w[1][1], w[1][2], w[1][3]);
+    router_fma16_1(acc0, xa[0], w[0][0], w[0][1], w[0][2], w[0][3]);
+    router_fma16_1(acc0, xa[1], w[1][0], w[1][1], w[1][2], w[1][3]);
   }
   const int e = eg * 64 + lane;
   if constexpr (FUSE) {
-    static_assert(4 * RT == ROUTE_TILE, "a router workgroup covers one routing tile");
+    static_assert(RW * RT == ROUTE_TILE, "a router workgroup covers one routing tile");
     __shared__ __attribute__((aligned(16))) RouteLds R;
     const int tl = wave * RT;
     if (e < E) {
       const float bb = bias ? bias[e] : 0.0f;
       R.l[tl][e] = bias ? acc0 + bb : acc0;
-      R.l[tl + 1][e] = bias ? acc1 + bb : acc1;
     }
     const int t0 = blockIdx.x * ROUTE_TILE;
-    route_tile<4>(R, blockIdx.x, t0, min(ROUTE_TILE, n - t0), E, k, norm, threadIdx.x, 256, ids, wout,
+    route_tile<4>(R, blockIdx.x, t0, min(ROUTE_TILE, n - t0), E, k, norm, threadIdx.x, 512, ids, wout,
                rank, hist);
   } else {
     if (e < E) {
       const float bb = bias ? bias[e] : 0.0f;
       if (tw < n) logits[(size_t)tw * E + e] = bias ? acc0 + bb : acc0;
-      if (tw + 1 < n) logits[(size_t)(tw + 1) * E + e] = bias ? acc1 + bb : acc1;
     }
   }
 }
@@ -696,8 +695,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
 
 hipError_t launch_router(const float* x, int n, int d, const float* wt, const float* bias, int E,
                          int E64, float* logits, hipStream_t s) {
-  dim3 grid((unsigned)((n + 4 * RT - 1) / (4 * RT)), (unsigned)(E64 / 64));
-  router_kernel<false><<<grid, 256, 0, s>>>(x, n, d, wt, bias, E, E64, logits, 0, 0, nullptr,
+  dim3 grid((unsigned)((n + RW * RT - 1) / (RW * RT)), (unsigned)(E64 / 64));
+  router_kernel<false><<<grid, 512, 0, s>>>(x, n, d, wt, bias, E, E64, logits, 0, 0, nullptr,
                                             nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
@@ -707,7 +706,7 @@ hipError_t launch_router_route(const float* x, int n, int d, const float* wt, co
                                int32_t* hist, hipStream_t s) {
   if (E > 64) return hipErrorInvalidValue;
   dim3 grid((unsigned)((n + ROUTE_TILE - 1) / ROUTE_TILE), 1);
-  router_kernel<true><<<grid, 256, 0, s>>>(x, n, d, wt, bias, E, 64, nullptr, k, norm, ids, w, rank,
+  router_kernel<true><<<grid, 512, 0, s>>>(x, n, d, wt, bias, E, 64, nullptr, k, norm, ids, w, rank,
                                            hist);
   return hipGetLastError();
 }
