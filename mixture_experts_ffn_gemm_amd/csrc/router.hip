@@ -422,11 +422,23 @@ __device__ inline float wave_sum(float v) {
 }
 
 // The tile's logits from global memory into LDS.
+// (ROUTE_THREADS threads; every load is issued before the first LDS store,
+// one memory round trip: the index is clamped into the tile's logits and the
+// surplus masked)
 __device__ __forceinline__ void route_load_logits(RouteLds& R, const float* __restrict__ logits, int t0, int nt, int E,
-                                  int tid, int nthreads) {
-  for (int i = tid; i < ROUTE_TILE * E; i += nthreads) {
-    const int tl = i / E, e = i - tl * E;
-    R.l[tl][e] = (tl < nt) ? logits[(size_t)(t0 + tl) * E + e] : 0.0f;
+                                  int tid) {
+  constexpr int PER = ROUTE_TILE * MAX_EXPERTS / ROUTE_THREADS;
+  const int tot = nt * E;
+  float v[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) v[u] = logits[(size_t)t0 * E + min(tid + u * ROUTE_THREADS, tot - 1)];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int i = tid + u * ROUTE_THREADS;
+    if (i < ROUTE_TILE * E) {
+      const int tl = i / E, e = i - tl * E;
+      R.l[tl][e] = (i < tot) ? v[u] : 0.0f;
+    }
   }
 }
 
@@ -438,7 +450,7 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(
   __shared__ __attribute__((aligned(16))) RouteLds R;
   const int t0 = blockIdx.x * ROUTE_TILE;
   const int nt = min(ROUTE_TILE, n - t0);
-  route_load_logits(R, logits, t0, nt, E, threadIdx.x, ROUTE_THREADS);
+  route_load_logits(R, logits, t0, nt, E, threadIdx.x);
   route_tile<MAX_EXPERTS / 16>(R, blockIdx.x, t0, nt, E, k, norm, threadIdx.x, ROUTE_THREADS, ids, wout, rank, hist);
 }
 
