@@ -65,7 +65,6 @@ constexpr int QB = 32;            // int8 block length (Q8_0 / activation blocks
 constexpr int Q8_BYTES = 34;      // Q8_0 block: binary16 scale + 32 codes
 constexpr int KPAD = 128;         // K-dimension padding granule (4 blocks)
 constexpr int ROUTE_TILE = 8;     // tokens per routing workgroup
-constexpr int ROUTE_THREADS = 16 * ROUTE_TILE;  // 16 threads per token
 constexpr int MT_WG = 128;        // rows per grouped-GEMM workgroup tile
 constexpr int MT_WAVE = 32;       // rows per wavefront
 constexpr int GU_COLS = 64;       // SwiGLU output columns per gate/up strip

@@ -69,14 +69,16 @@ __device__ __forceinline__ void router_fma16_1(float& acc0, float xa, const f4v&
 }
 #undef RFMA1
 
-// Routing of one tile of ROUTE_TILE tokens, 16 threads per token (threads
-// tid < ROUTE_THREADS of the workgroup; every thread of the workgroup calls
-// this, since it meets workgroup barriers).  The tile's logits l[token][e]
-// are in LDS.  Top-k by the contract's order (logit descending, id
-// ascending): each expert's 64-bit key orders exactly that way and is unique,
-// the token's 16 threads hold its keys in registers (expert g + 16c in thread
-// g, NKEY >= E/16 of them), and slot r takes the largest key left after r
-// rounds of a maximum over the 16 threads, its owner clearing it.  Then
+// Routing of one tile of ROUTE_TILE tokens, TPT threads per token (threads
+// tid < ROUTE_TILE * TPT of the workgroup; every thread of the workgroup
+// calls this, since it meets workgroup barriers; the fused router uses 16,
+// the routing launch for E > 64 a wavefront per token).  The tile's logits
+// l[token][e] are in LDS.  Top-k by the contract's order (logit descending,
+// id ascending): each expert's 64-bit key orders exactly that way and is
+// unique, the token's TPT threads hold its keys in registers (expert
+// g + TPT c in thread g, NKEY >= E/TPT of them), and slot r takes the largest
+// key left after r rounds of a maximum over the TPT threads, its owner
+// clearing it.  Then
 // softmax over all E, optional renormalisation, and the per-expert rank of
 // each (token, slot) pair among the tile's pairs in (token, slot) order, with
 // the tile's histogram, for the bucketing kernel.
@@ -87,23 +89,24 @@ struct RouteLds {
   int cnt[MAX_EXPERTS];
 };
 
-template <int NKEY>
+template <int NKEY, int TPT>
 __device__ __forceinline__ void route_tile(RouteLds& R, int tile, int t0, int nt, int E, int k, int norm, int tid,
                            int nthreads, int32_t* __restrict__ ids, float* __restrict__ wout,
                            int32_t* __restrict__ rank, int32_t* __restrict__ hist) {
+  static_assert(TPT == 16 || TPT == 64, "a token's threads stay inside one wavefront");
   for (int e = tid; e < E; e += nthreads) R.cnt[e] = 0;
   __syncthreads();  // the caller's logit writes are visible to every thread
-  // ranks: thread (token tl = tid/16, expert group g = tid%16) owns experts g + 16c
-  const int tl = tid >> 4, g = tid & 15;
-  const bool mine = tid < ROUTE_THREADS;
+  // thread (token tl = tid / TPT, lane g = tid % TPT of the token) owns experts g + TPT c
+  const int tl = tid / TPT, g = tid % TPT;
+  const bool mine = tid < ROUTE_TILE * TPT;
   if (mine) {
     // slots >= k and absent tokens keep -1 (the same wavefront's later
     // stores below land after this one)
-    R.ids[tl * MAX_TOPK + g] = -1;
+    if (g < MAX_TOPK) R.ids[tl * MAX_TOPK + g] = -1;
     unsigned long long key[NKEY];
 #pragma unroll
     for (int c = 0; c < NKEY; ++c) {
-      const int e = g + 16 * c;
+      const int e = g + TPT * c;
       key[c] = (e < E) ? topk_key(R.l[tl][e], e) : 0ull;  // 0: below every real key
     }
     for (int r = 0; r < k; ++r) {
@@ -111,8 +114,8 @@ __device__ __forceinline__ void route_tile(RouteLds& R, int tile, int t0, int nt
 #pragma unroll
       for (int c = 0; c < NKEY; ++c) m = key[c] > m ? key[c] : m;
 #pragma unroll
-      for (int off = 8; off > 0; off >>= 1) {
-        const unsigned long long o = __shfl_xor(m, off, 16);
+      for (int off = TPT / 2; off > 0; off >>= 1) {
+        const unsigned long long o = __shfl_xor(m, off, TPT);
         m = o > m ? o : m;
       }
 #pragma unroll
@@ -127,17 +130,17 @@ __device__ __forceinline__ void route_tile(RouteLds& R, int tile, int t0, int nt
   __syncthreads();
 
   if (mine) {
-    // softmax over all E (the 16 threads of a token share the sum), weights of the k slots
+    // softmax over all E (the TPT threads of a token share the sum), weights of the k slots
     const float m = R.val[tl][0];
     float part = 0.0f;
-    for (int e = g; e < E; e += 16) part += expf(R.l[tl][e] - m);
+    for (int e = g; e < E; e += TPT) part += expf(R.l[tl][e] - m);
 #pragma unroll
-    for (int off = 8; off > 0; off >>= 1) part += __shfl_xor(part, off, 16);
+    for (int off = TPT / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, TPT);
     float p = (g < k) ? expf(R.val[tl][min(g, k - 1)] - m) / part : 0.0f;
     if (norm) {
       float sum = p;
 #pragma unroll
-      for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 16);
+      for (int off = TPT / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, TPT);
       p = p / sum;
     }
     if (tl < nt && g < k) {
@@ -315,7 +318,7 @@ __global__ __launch_bounds__(512, 1) void router_kernel(
       R.l[tl][e] = bias ? acc0 + bb : acc0;
     }
     const int t0 = blockIdx.x * ROUTE_TILE;
-    route_tile<4>(R, blockIdx.x, t0, min(ROUTE_TILE, n - t0), E, k, norm, threadIdx.x, 512, ids, wout,
+    route_tile<4, 16>(R, blockIdx.x, t0, min(ROUTE_TILE, n - t0), E, k, norm, threadIdx.x, 512, ids, wout,
                rank, hist);
   } else {
     if (e < E) {
@@ -422,19 +425,20 @@ __device__ inline float wave_sum(float v) {
 }
 
 // The tile's logits from global memory into LDS.
-// (ROUTE_THREADS threads; every load is issued before the first LDS store,
-// one memory round trip: the index is clamped into the tile's logits and the
-// surplus masked)
+// (ROUTE_WIDE_THREADS threads; every load is issued before the first LDS
+// store, one memory round trip: the index is clamped into the tile's logits
+// and the surplus masked)
+constexpr int ROUTE_WIDE_THREADS = ROUTE_TILE * 64;  // one wavefront per token
 __device__ __forceinline__ void route_load_logits(RouteLds& R, const float* __restrict__ logits, int t0, int nt, int E,
                                   int tid) {
-  constexpr int PER = ROUTE_TILE * MAX_EXPERTS / ROUTE_THREADS;
+  constexpr int PER = ROUTE_TILE * MAX_EXPERTS / ROUTE_WIDE_THREADS;
   const int tot = nt * E;
   float v[PER];
 #pragma unroll
-  for (int u = 0; u < PER; ++u) v[u] = logits[(size_t)t0 * E + min(tid + u * ROUTE_THREADS, tot - 1)];
+  for (int u = 0; u < PER; ++u) v[u] = logits[(size_t)t0 * E + min(tid + u * ROUTE_WIDE_THREADS, tot - 1)];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
-    const int i = tid + u * ROUTE_THREADS;
+    const int i = tid + u * ROUTE_WIDE_THREADS;
     if (i < ROUTE_TILE * E) {
       const int tl = i / E, e = i - tl * E;
       R.l[tl][e] = (i < tot) ? v[u] : 0.0f;
@@ -444,14 +448,15 @@ __device__ __forceinline__ void route_load_logits(RouteLds& R, const float* __re
 
 // Routing as its own kernel (E > 64: a router workgroup holds only a 64-expert
 // slice of its tokens' logits).  One workgroup per ROUTE_TILE tokens.
-__global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(
+__global__ __launch_bounds__(ROUTE_WIDE_THREADS) void route_kernel(
     const float* __restrict__ logits, int n, int E, int k, int norm, int32_t* __restrict__ ids,
     float* __restrict__ wout, int32_t* __restrict__ rank, int32_t* __restrict__ hist) {
   __shared__ __attribute__((aligned(16))) RouteLds R;
   const int t0 = blockIdx.x * ROUTE_TILE;
   const int nt = min(ROUTE_TILE, n - t0);
   route_load_logits(R, logits, t0, nt, E, threadIdx.x);
-  route_tile<MAX_EXPERTS / 16>(R, blockIdx.x, t0, nt, E, k, norm, threadIdx.x, ROUTE_THREADS, ids, wout, rank, hist);
+  route_tile<MAX_EXPERTS / 64, 64>(R, blockIdx.x, t0, nt, E, k, norm, threadIdx.x, ROUTE_WIDE_THREADS, ids, wout, rank,
+                                   hist);
 }
 
 // ---------------------------------------------------------------- decode
@@ -735,7 +740,7 @@ hipError_t launch_quantize_scatter(const float* x, int n, int d, int d_pad, cons
 hipError_t launch_route(const float* logits, int n, int E, int k, int norm, int32_t* ids, float* w,
                         int32_t* rank, int32_t* hist, hipStream_t s) {
   const int tiles = (n + ROUTE_TILE - 1) / ROUTE_TILE;
-  route_kernel<<<tiles, ROUTE_THREADS, 0, s>>>(logits, n, E, k, norm, ids, w, rank, hist);
+  route_kernel<<<tiles, ROUTE_WIDE_THREADS, 0, s>>>(logits, n, E, k, norm, ids, w, rank, hist);
   return hipGetLastError();
 }
 
