@@ -71,8 +71,8 @@ __device__ __forceinline__ void router_fma16_1(float& acc0, float xa, const f4v&
 
 // Routing of one tile of ROUTE_TILE tokens, TPT threads per token (threads
 // tid < ROUTE_TILE * TPT of the workgroup; every thread of the workgroup
-// calls this, since it meets workgroup barriers; the fused router uses 16,
-// the routing launch for E > 64 a wavefront per token).  The tile's logits
+// calls this, since it meets workgroup barriers; both the fused router and
+// the routing launch for E > 64 give each token a wavefront).  The tile's logits
 // l[token][e] are in LDS.  Top-k by the contract's order (logit descending,
 // id ascending): each expert's 64-bit key orders exactly that way and is
 // unique, the token's TPT threads hold its keys in registers (expert
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(512, 1) void router_kernel(
       R.l[tl][e] = bias ? acc0 + bb : acc0;
     }
     const int t0 = blockIdx.x * ROUTE_TILE;
-    route_tile<4, 16>(R, blockIdx.x, t0, min(ROUTE_TILE, n - t0), E, k, norm, threadIdx.x, 512, ids, wout,
+    route_tile<1, 64>(R, blockIdx.x, t0, min(ROUTE_TILE, n - t0), E, k, norm, threadIdx.x, 512, ids, wout,
                rank, hist);
   } else {
     if (e < E) {
