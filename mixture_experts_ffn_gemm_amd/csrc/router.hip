@@ -328,8 +328,10 @@ __global__ __launch_bounds__(512, 1) void router_kernel(
   }
 }
 
-// Activation quantiser and scatter, after the bucketing: one wavefront per
-// token row.  Lane pairs quantise 32-blocks (each lane 16 values), and each
+// Activation quantiser and scatter, after the bucketing: two wavefronts per
+// token row, taking its passes of 8 k-steps (1024 values) alternately, so
+// that twice as many rows' loads are in flight.  Lane pairs quantise
+// 32-blocks (each lane 16 values), and each
 // block's codes and scale are written once per expert slot of the token,
 // straight into the GEMM operand layout at the slot's padded row
 // (t32 = row / 32, r = row % 32): one 4 KiB slab per (t32, k-step) holding
@@ -337,32 +339,35 @@ __global__ __launch_bounds__(512, 1) void router_kernel(
 // of row r at 16 * (p ^ (r % 8)), and the scales at [t32][k-step][r][block].
 // The 8 lanes of one k-step therefore write one whole 128-byte line per slot.
 // The K-padding blocks past d get zero codes and scales.  With a shared
-// expert the wavefront also computes the gate sigmoid(x . g) (a fixed-order
-// reduction).  Optionally the token-major codes and scales are written out.
+// expert the two wavefronts also compute the gate sigmoid(x . g) (a
+// fixed-order reduction: per lane over its values, over each wavefront, then
+// the first wavefront's sum plus the second's).  Optionally the token-major
+// codes and scales are written out.
 __global__ __launch_bounds__(256) void quantize_scatter_kernel(
     const float* __restrict__ x, int n, int d, int d_pad, const int32_t* __restrict__ pos, int kk,
     int pad_rows, int8_t* __restrict__ gq, uint16_t* __restrict__ gqs,
     const float* __restrict__ shg, float* __restrict__ gs, int8_t* __restrict__ xq_out,
     uint16_t* __restrict__ xs_out) {
+  __shared__ float s_g[4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= n) return;
-  const float* xr = x + (size_t)t * d;
+  const int t = blockIdx.x * 2 + (wave >> 1), h = wave & 1;
+  const bool active = t < n;  // wavefront-uniform; every wavefront meets the barrier below
+  const float* xr = x + (size_t)min(t, n - 1) * d;
   const int KS = d_pad / (QB * KSTEP);
   // the slots' padded rows; the loads are unconditional (index clamped into
   // this token's row) so that they issue together, and slots past kk masked
   int prow[MAX_TOPK + 1];
 #pragma unroll
-  for (int s = 0; s < MAX_TOPK + 1; ++s) prow[s] = pos[(size_t)t * kk + min(s, kk - 1)];
+  for (int s = 0; s < MAX_TOPK + 1; ++s) prow[s] = pos[(size_t)min(t, n - 1) * kk + min(s, kk - 1)];
 #pragma unroll
   for (int s = 0; s < MAX_TOPK + 1; ++s) {
     const int v = prow[s];
     prow[s] = (s < kk && v >= 0 && v < pad_rows) ? v : -1;
   }
   float gacc = 0.0f;
-  // Each pass covers 8 k-steps; the next pass's row values are loaded before
-  // this pass is quantised and scattered (padding columns load column 0 and
-  // are zeroed).
+  // Each pass covers 8 k-steps; this wavefront's next pass's row values are
+  // loaded before this pass is quantised and scattered (padding columns load
+  // column 0 and are zeroed).
   auto load = [&](int j0, f4v (&v)[4]) {
     const int j = j0 + (lane >> 3), p = lane & 7;
     const int c0 = (KSTEP * j + (p >> 1)) * QB + (p & 1) * 16;
@@ -371,9 +376,9 @@ __global__ __launch_bounds__(256) void quantize_scatter_kernel(
     for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const f4v*>(src + 4 * i);
   };
   f4v cur[4], nxt[4];
-  load(0, cur);
-  for (int j0 = 0; j0 < KS; j0 += 8) {
-    if (j0 + 8 < KS) load(j0 + 8, nxt);
+  if (active) load(8 * h, cur);
+  for (int j0 = 8 * h; active && j0 < KS; j0 += 16) {
+    if (j0 + 16 < KS) load(j0 + 16, nxt);
     const int j = j0 + (lane >> 3), p = lane & 7;  // k-step, piece
     const int kb = KSTEP * j + (p >> 1), half = p & 1;
     const int c0 = kb * QB + half * 16;  // first column of the piece
@@ -414,7 +419,9 @@ __global__ __launch_bounds__(256) void quantize_scatter_kernel(
   if (shg) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) gacc += __shfl_xor(gacc, off, 64);
-    if (lane == 0) gs[t] = 1.0f / (1.0f + expf(-gacc));
+    if (lane == 0) s_g[wave] = gacc;
+    __syncthreads();
+    if (active && h == 0 && lane == 0) gs[t] = 1.0f / (1.0f + expf(-(s_g[wave] + s_g[wave + 1])));
   }
 }
 
@@ -732,7 +739,7 @@ hipError_t launch_quantize_scatter(const float* x, int n, int d, int d_pad, cons
                                   int kk, int pad_rows, int8_t* gq, uint16_t* gqs,
                                   const float* sh_gate_vec, float* gs, int8_t* xq_out,
                                   uint16_t* xs_out, hipStream_t s) {
-  quantize_scatter_kernel<<<(n + 3) / 4, 256, 0, s>>>(x, n, d, d_pad, pos, kk, pad_rows, gq, gqs,
+  quantize_scatter_kernel<<<(n + 1) / 2, 256, 0, s>>>(x, n, d, d_pad, pos, kk, pad_rows, gq, gqs,
                                                       sh_gate_vec, gs, xq_out, xs_out);
   return hipGetLastError();
 }
