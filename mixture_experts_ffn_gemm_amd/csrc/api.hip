@@ -219,11 +219,10 @@ int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, v
     HIP_TRY(launch_route(logits, n, dm.E, dm.k, dm.norm, ids, w, rank, hist, s));
   }
   HIP_TRY(mark(2));
-  HIP_TRY(launch_bucket(ids, rank, hist, n, dm.E, dm.k, dm.has_shared, exp_start, tok_i, tok_k, pos,
-                        tiles, L.tile_bound, s));
-  HIP_TRY(launch_quantize_scatter(x, n, dm.d, dm.d_pad, pos, kk, L.tile_bound * MT_WG, gq, gqs,
-                                  dm.has_shared ? W->sh_gate_vec : nullptr, gs,
-                                  r ? r->xq : nullptr, r ? r->xs : nullptr, s));
+  HIP_TRY(launch_bucket_quantize(ids, rank, hist, n, dm.E, dm.k, dm.has_shared, exp_start, tok_i, tok_k, pos,
+                                 tiles, L.tile_bound, x, dm.d, dm.d_pad, gq, gqs,
+                                 dm.has_shared ? W->sh_gate_vec : nullptr, gs, r ? r->xq : nullptr,
+                                 r ? r->xs : nullptr, s));
   GemmArgs a{};
   a.tiles = tiles;
   a.tok_i = tok_i;

@@ -13,6 +13,22 @@
 // quantiser can place the token's codes where the GEMM's tile reads them.
 // Workgroup 0 also writes expStart and the tile table that drives the grouped
 // GEMMs.
+//
+// The same workgroup then quantises its tile's token rows and scatters the
+// codes to the rows it has just computed (one launch for both stages: the
+// rows' loads are issued before the histograms are read, so their latency
+// hides under the bucketing).  One wavefront per token: lane pairs quantise
+// 32-blocks (each lane 16 values), and each block's codes and scale are
+// written once per expert slot of the token, straight into the GEMM operand
+// layout at the slot's padded row (t32 = row / 32, r = row % 32): one 4 KiB
+// slab per (t32, k-step) holding [32 rows][128 B], piece p (16 codes: block
+// p/2 of the k-step, half p%2) of row r at 16 * (p ^ (r % 8)), and the scales
+// at [t32][k-step][r][block].  The 8 lanes of one k-step therefore write one
+// whole 128-byte line per slot.  The K-padding blocks past d get zero codes
+// and scales.  With a shared expert the wavefront also computes the gate
+// sigmoid(x . g) (a fixed-order reduction).  Optionally the token-major codes
+// and scales are written out.
+#include "device_util.h"
 #include "internal.h"
 
 namespace moe {
@@ -45,23 +61,61 @@ __device__ void wave_exclusive_scan_512(int* s, int n, int lane) {
   }
 }
 
-__global__ __launch_bounds__(256) void bucket_kernel(
+typedef float f4v __attribute__((ext_vector_type(4)));
+constexpr int BQ_THREADS = 64 * ROUTE_TILE;  // a wavefront per token of the tile
+
+struct QuantArgs {
+  const float* x;
+  int d, d_pad;
+  int8_t* gq;
+  uint16_t* gqs;
+  const float* shg;  // shared-expert gate vector, or NULL
+  float* gs;
+  int8_t* xq_out;    // optional token-major copies
+  uint16_t* xs_out;
+};
+
+__global__ __launch_bounds__(BQ_THREADS) void bucket_quantize_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ rank,
     const int32_t* __restrict__ hist, int n, int E, int k, int has_shared, int n_tiles,
     int32_t* __restrict__ exp_start, int32_t* __restrict__ tok_i, int32_t* __restrict__ tok_k,
-    int32_t* __restrict__ pos_out, int32_t* __restrict__ tiles, int tile_bound) {
+    int32_t* __restrict__ pos_out, int32_t* __restrict__ tiles, int tile_bound, QuantArgs qa) {
   __shared__ int s_start[2 * 256 + 2];
   __shared__ int s_pre[MAX_EXPERTS];
   __shared__ int s_cnt[MAX_EXPERTS + 1];
   __shared__ int s_nt[2 * 256 + 2];
+  __shared__ int s_pos[ROUTE_TILE][MAX_TOPK + 1];
   const int tile = blockIdx.x;
   const int P = n * k;
   const int G = E + has_shared;
   const int kk = k + has_shared;
+  const int t0 = tile * ROUTE_TILE;
+  const int nt = min(ROUTE_TILE, n - t0);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // This wavefront's token row (the last one for a wavefront past the tile's
+  // tokens, which quantises nothing): the values of its first two passes of
+  // 8 k-steps are requested now (padding columns load column 0 and are
+  // zeroed later).
+  const int tq = t0 + min(wave, nt - 1);
+  const float* xr = qa.x + (size_t)tq * qa.d;
+  const int KS = qa.d_pad / (QB * KSTEP);
+  auto load = [&](int j0, f4v (&v)[4]) {
+    const int j = j0 + (lane >> 3), p = lane & 7;
+    const int c0 = (KSTEP * j + (p >> 1)) * QB + (p & 1) * 16;
+    const float* src = xr + (c0 < qa.d ? c0 : 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const f4v*>(src + 4 * i);
+  };
+  f4v cur[4], nxt[4] = {};
+  load(0, cur);
+  if (8 < KS) load(8, nxt);
+
   // Per-expert totals over all tiles and over the tiles before this one; for
   // small E several threads share an expert's column and their sums meet in LDS.
-  __shared__ int s_part_tot[256], s_part_pre[256];
-  const int nparts = max(1, 256 / E);
+  __shared__ int s_part_tot[BQ_THREADS], s_part_pre[BQ_THREADS];
+  const int nparts = max(1, BQ_THREADS / E);
   // Every workgroup reads every histogram, so this is the kernel's critical
   // path: a thread requests RB histogram entries at once (the index clamped
   // into the table, the surplus masked), one memory round trip per RB tiles.
@@ -84,7 +138,7 @@ __global__ __launch_bounds__(256) void bucket_kernel(
     s_part_pre[threadIdx.x] = pre;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) {
+  for (int e = threadIdx.x; e < E; e += BQ_THREADS) {
     int tot = 0, pre = 0;
     for (int part = 0; part < nparts; ++part) {
       tot += s_part_tot[part * E + e];
@@ -97,7 +151,7 @@ __global__ __launch_bounds__(256) void bucket_kernel(
   if (threadIdx.x == 0 && has_shared) s_cnt[E] = n;
   __syncthreads();
   // group tile counts (every workgroup needs the first tile of each group)
-  for (int g = threadIdx.x; g < G; g += 256) s_nt[g] = (s_cnt[g] + MT_WG - 1) / MT_WG;
+  for (int g = threadIdx.x; g < G; g += BQ_THREADS) s_nt[g] = (s_cnt[g] + MT_WG - 1) / MT_WG;
   __syncthreads();
   const int last_nt = s_nt[G - 1];
   __syncthreads();
@@ -106,9 +160,7 @@ __global__ __launch_bounds__(256) void bucket_kernel(
   __syncthreads();
 
   const int pad_rows = tile_bound * MT_WG;
-  const int t0 = tile * ROUTE_TILE;
-  const int nt = min(ROUTE_TILE, n - t0);
-  for (int q = threadIdx.x; q < nt * k; q += 256) {
+  for (int q = threadIdx.x; q < nt * k; q += BQ_THREADS) {
     const int t = t0 + q / k, s = q % k;
     const int e = ids[(size_t)t * k + s];
     const int local = s_pre[e] + rank[(size_t)t * k + s];
@@ -118,21 +170,25 @@ __global__ __launch_bounds__(256) void bucket_kernel(
       tok_k[pos] = s;
     }
     const int prow = s_nt[e] * MT_WG + local;
-    pos_out[(size_t)t * kk + s] = prow < pad_rows ? prow : -1;
+    const int pv = prow < pad_rows ? prow : -1;
+    pos_out[(size_t)t * kk + s] = pv;
+    s_pos[q / k][s] = pv;
   }
   if (has_shared)
-    for (int q = threadIdx.x; q < nt; q += 256) {
+    for (int q = threadIdx.x; q < nt; q += BQ_THREADS) {
       tok_i[P + t0 + q] = t0 + q;
       tok_k[P + t0 + q] = k;
       const int prow = s_nt[E] * MT_WG + t0 + q;
-      pos_out[(size_t)(t0 + q) * kk + k] = prow < pad_rows ? prow : -1;
+      const int pv = prow < pad_rows ? prow : -1;
+      pos_out[(size_t)(t0 + q) * kk + k] = pv;
+      s_pos[q][k] = pv;
     }
 
-  if (tile != 0) return;
-  // expStart, then the 128-row tile table over the E (+1) groups
-  for (int e = threadIdx.x; e <= E; e += 256) exp_start[e] = (e < E) ? s_start[e] : P;
-  if (has_shared && threadIdx.x == 0) exp_start[E + 1] = P + n;
-  for (int g = threadIdx.x; g < G; g += 256) {
+  if (tile == 0) {
+    // expStart, then the 128-row tile table over the E (+1) groups
+    for (int e = threadIdx.x; e <= E; e += BQ_THREADS) exp_start[e] = (e < E) ? s_start[e] : P;
+    if (has_shared && threadIdx.x == 0) exp_start[E + 1] = P + n;
+    for (int g = threadIdx.x; g < G; g += BQ_THREADS) {
     const int c = s_cnt[g];
     const int first = (g < E) ? s_start[g] : P;
     const int ntg = (c + MT_WG - 1) / MT_WG;
@@ -143,22 +199,86 @@ __global__ __launch_bounds__(256) void bucket_kernel(
       ent[2] = first + c;
     }
   }
-  if (threadIdx.x == 0) {
-    tiles[0] = min(s_nt[G - 1] + last_nt, tile_bound);
-    tiles[1] = 0;
-    tiles[2] = 0;
-    tiles[3] = 0;
+    if (threadIdx.x == 0) {
+      tiles[0] = min(s_nt[G - 1] + last_nt, tile_bound);
+      tiles[1] = 0;
+      tiles[2] = 0;
+      tiles[3] = 0;
+    }
+  }
+  __syncthreads();  // the tile's padded rows are in s_pos
+
+  // Quantise and scatter: wavefront w takes token t0 + w.
+  if (wave >= nt) return;
+  const int t = t0 + wave;
+  int prow[MAX_TOPK + 1];
+#pragma unroll
+  for (int s2 = 0; s2 < MAX_TOPK + 1; ++s2) prow[s2] = (s2 < kk) ? s_pos[wave][s2] : -1;
+  float gacc = 0.0f;
+  // Each pass covers 8 k-steps; the pass after next is requested before this
+  // pass is quantised and scattered.
+  for (int j0 = 0; j0 < KS; j0 += 8) {
+    f4v nn[4] = {};
+    if (j0 + 16 < KS) load(j0 + 16, nn);
+    const int j = j0 + (lane >> 3), p = lane & 7;  // k-step, piece
+    const int kb = KSTEP * j + (p >> 1), half = p & 1;
+    const int c0 = kb * QB + half * 16;  // first column of the piece
+    const bool valid = c0 < qa.d;        // d % 32 == 0: a piece is all valid or all padding
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[4 * i] = valid ? cur[i].x : 0.0f;
+      v[4 * i + 1] = valid ? cur[i].y : 0.0f;
+      v[4 * i + 2] = valid ? cur[i].z : 0.0f;
+      v[4 * i + 3] = valid ? cur[i].w : 0.0f;
+    }
+    uint32_t pk[4];
+    uint16_t s16;
+    quant_half_block16(v, pk, s16);  // lanes 2i, 2i+1 share a block; all take part
+    if (j < KS) {
+      const uint4 codes = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+#pragma unroll
+      for (int s2 = 0; s2 < MAX_TOPK + 1; ++s2) {
+        const int row = prow[s2];
+        if (row >= 0) {
+          const int t32 = row >> 5, r = row & 31;
+          const size_t slab = (size_t)t32 * KS + j;
+          *reinterpret_cast<uint4*>(qa.gq + (slab * 32 + r) * 128 + ((p ^ (r & 7)) << 4)) = codes;
+          if (half == 0) qa.gqs[(slab * 32 + r) * KSTEP + (p >> 1)] = s16;
+        }
+      }
+      if (qa.xq_out && valid) *reinterpret_cast<uint4*>(qa.xq_out + (size_t)t * qa.d + c0) = codes;
+      if (qa.xs_out && half == 0 && valid) qa.xs_out[(size_t)t * (qa.d / QB) + kb] = s16;
+    }
+    if (qa.shg && valid) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) gacc = __builtin_fmaf(v[i], qa.shg[c0 + i], gacc);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      cur[i] = nxt[i];
+      nxt[i] = nn[i];
+    }
+  }
+  if (qa.shg) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) gacc += __shfl_xor(gacc, off, 64);
+    if (lane == 0) qa.gs[t] = 1.0f / (1.0f + expf(-gacc));
   }
 }
 
 }  // namespace
 
-hipError_t launch_bucket(const int32_t* ids, const int32_t* rank, const int32_t* hist, int n, int E,
-                         int k, int has_shared, int32_t* exp_start, int32_t* tok_i, int32_t* tok_k,
-                         int32_t* pos, int32_t* tiles, int tile_bound, hipStream_t s) {
+hipError_t launch_bucket_quantize(const int32_t* ids, const int32_t* rank, const int32_t* hist, int n,
+                                  int E, int k, int has_shared, int32_t* exp_start, int32_t* tok_i,
+                                  int32_t* tok_k, int32_t* pos, int32_t* tiles, int tile_bound,
+                                  const float* x, int d, int d_pad, int8_t* gq, uint16_t* gqs,
+                                  const float* sh_gate_vec, float* gs, int8_t* xq_out, uint16_t* xs_out,
+                                  hipStream_t s) {
   const int n_tiles = (n + ROUTE_TILE - 1) / ROUTE_TILE;
-  bucket_kernel<<<n_tiles, 256, 0, s>>>(ids, rank, hist, n, E, k, has_shared, n_tiles, exp_start,
-                                        tok_i, tok_k, pos, tiles, tile_bound);
+  const QuantArgs qa{x, d, d_pad, gq, gqs, sh_gate_vec, gs, xq_out, xs_out};
+  bucket_quantize_kernel<<<n_tiles, BQ_THREADS, 0, s>>>(ids, rank, hist, n, E, k, has_shared, n_tiles, exp_start,
+                                                        tok_i, tok_k, pos, tiles, tile_bound, qa);
   return hipGetLastError();
 }
 

@@ -140,21 +140,23 @@ hipError_t launch_router(const float* x, int n, int d, const float* wt, const fl
 hipError_t launch_router_route(const float* x, int n, int d, const float* wt, const float* bias,
                                int E, int k, int norm, int32_t* ids, float* w, int32_t* rank,
                                int32_t* hist, hipStream_t s);
-// Quantise every token row per 32-block and write its codes and scales to the
-// padded GEMM rows pos[t][0..kk) in the gq/gqs layout (rows past pad_rows or
-// -1 are skipped); with sh_gate_vec != NULL also gs[t] = sigmoid(x[t] . g);
-// xq_out [N][d] / xs_out [N][d/32] (each optional) receive token-major copies.
-hipError_t launch_quantize_scatter(const float* x, int n, int d, int d_pad, const int32_t* pos,
-                                  int kk, int pad_rows, int8_t* gq, uint16_t* gqs,
-                                  const float* sh_gate_vec, float* gs, int8_t* xq_out,
-                                  uint16_t* xs_out, hipStream_t s);
 hipError_t launch_route(const float* logits, int n, int E, int k, int norm, int32_t* ids, float* w,
                         int32_t* rank, int32_t* hist, hipStream_t s);
 hipError_t launch_quantize(const float* v, int64_t n_values, int8_t* q, uint16_t* scales,
                            hipStream_t s);
-hipError_t launch_bucket(const int32_t* ids, const int32_t* rank, const int32_t* hist, int n,
-                         int E, int k, int has_shared, int32_t* exp_start, int32_t* tok_i,
-                         int32_t* tok_k, int32_t* pos, int32_t* tiles, int tile_bound, hipStream_t s);
+// The bucketing (expStart, expTokI/expTokK, each pair's padded GEMM row pos,
+// the tile table) and, in the same workgroups, the activation quantiser: every
+// token row quantised per 32-block, its codes and scales written to the
+// padded GEMM rows pos[t][0..kk) in the gq/gqs layout (rows past the tile
+// bound are -1 and skipped); with sh_gate_vec != NULL also
+// gs[t] = sigmoid(x[t] . g); xq_out [N][d] / xs_out [N][d/32] (each optional)
+// receive token-major copies.
+hipError_t launch_bucket_quantize(const int32_t* ids, const int32_t* rank, const int32_t* hist, int n,
+                                  int E, int k, int has_shared, int32_t* exp_start, int32_t* tok_i,
+                                  int32_t* tok_k, int32_t* pos, int32_t* tiles, int tile_bound,
+                                  const float* x, int d, int d_pad, int8_t* gq, uint16_t* gqs,
+                                  const float* sh_gate_vec, float* gs, int8_t* xq_out, uint16_t* xs_out,
+                                  hipStream_t s);
 
 struct GemmArgs {
   // common

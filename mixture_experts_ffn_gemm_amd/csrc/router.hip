@@ -1,7 +1,6 @@
 // router.hip -- router logits, top-k / softmax, the per-tile expert
-// histograms, and the per-32 int8 activation quantiser (with the shared gate),
-// which runs after the bucketing and scatters each token's codes to its
-// expert slots.
+// histograms, the decode router, and the standalone per-32 int8 quantiser.
+// (The prefill activation quantiser runs in the bucketing launch.)
 //
 // SharpInference #388 "Remaining levers" 1 moves the router matvec
 // norm[N x embDim] x routerW[numExperts x embDim] + softmax + top-k + shexp-gate
@@ -328,103 +327,6 @@ __global__ __launch_bounds__(512, 1) void router_kernel(
   }
 }
 
-// Activation quantiser and scatter, after the bucketing: two wavefronts per
-// token row, taking its passes of 8 k-steps (1024 values) alternately, so
-// that twice as many rows' loads are in flight.  Lane pairs quantise
-// 32-blocks (each lane 16 values), and each
-// block's codes and scale are written once per expert slot of the token,
-// straight into the GEMM operand layout at the slot's padded row
-// (t32 = row / 32, r = row % 32): one 4 KiB slab per (t32, k-step) holding
-// [32 rows][128 B], piece p (16 codes: block p/2 of the k-step, half p%2)
-// of row r at 16 * (p ^ (r % 8)), and the scales at [t32][k-step][r][block].
-// The 8 lanes of one k-step therefore write one whole 128-byte line per slot.
-// The K-padding blocks past d get zero codes and scales.  With a shared
-// expert the two wavefronts also compute the gate sigmoid(x . g) (a
-// fixed-order reduction: per lane over its values, over each wavefront, then
-// the first wavefront's sum plus the second's).  Optionally the token-major
-// codes and scales are written out.
-__global__ __launch_bounds__(256) void quantize_scatter_kernel(
-    const float* __restrict__ x, int n, int d, int d_pad, const int32_t* __restrict__ pos, int kk,
-    int pad_rows, int8_t* __restrict__ gq, uint16_t* __restrict__ gqs,
-    const float* __restrict__ shg, float* __restrict__ gs, int8_t* __restrict__ xq_out,
-    uint16_t* __restrict__ xs_out) {
-  __shared__ float s_g[4];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 2 + (wave >> 1), h = wave & 1;
-  const bool active = t < n;  // wavefront-uniform; every wavefront meets the barrier below
-  const float* xr = x + (size_t)min(t, n - 1) * d;
-  const int KS = d_pad / (QB * KSTEP);
-  // the slots' padded rows; the loads are unconditional (index clamped into
-  // this token's row) so that they issue together, and slots past kk masked
-  int prow[MAX_TOPK + 1];
-#pragma unroll
-  for (int s = 0; s < MAX_TOPK + 1; ++s) prow[s] = pos[(size_t)min(t, n - 1) * kk + min(s, kk - 1)];
-#pragma unroll
-  for (int s = 0; s < MAX_TOPK + 1; ++s) {
-    const int v = prow[s];
-    prow[s] = (s < kk && v >= 0 && v < pad_rows) ? v : -1;
-  }
-  float gacc = 0.0f;
-  // Each pass covers 8 k-steps; this wavefront's next pass's row values are
-  // loaded before this pass is quantised and scattered (padding columns load
-  // column 0 and are zeroed).
-  auto load = [&](int j0, f4v (&v)[4]) {
-    const int j = j0 + (lane >> 3), p = lane & 7;
-    const int c0 = (KSTEP * j + (p >> 1)) * QB + (p & 1) * 16;
-    const float* src = xr + (c0 < d ? c0 : 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const f4v*>(src + 4 * i);
-  };
-  f4v cur[4], nxt[4];
-  if (active) load(8 * h, cur);
-  for (int j0 = 8 * h; active && j0 < KS; j0 += 16) {
-    if (j0 + 16 < KS) load(j0 + 16, nxt);
-    const int j = j0 + (lane >> 3), p = lane & 7;  // k-step, piece
-    const int kb = KSTEP * j + (p >> 1), half = p & 1;
-    const int c0 = kb * QB + half * 16;  // first column of the piece
-    const bool valid = c0 < d;           // d % 32 == 0: a piece is all valid or all padding
-    float v[16];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[4 * i] = valid ? cur[i].x : 0.0f;
-      v[4 * i + 1] = valid ? cur[i].y : 0.0f;
-      v[4 * i + 2] = valid ? cur[i].z : 0.0f;
-      v[4 * i + 3] = valid ? cur[i].w : 0.0f;
-    }
-    uint32_t pk[4];
-    uint16_t s16;
-    quant_half_block16(v, pk, s16);  // lanes 2i, 2i+1 share a block; all take part
-    if (j < KS) {
-      const uint4 codes = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-#pragma unroll
-      for (int s = 0; s < MAX_TOPK + 1; ++s) {
-        const int row = prow[s];
-        if (s < kk && row >= 0) {
-          const int t32 = row >> 5, r = row & 31;
-          const size_t slab = (size_t)t32 * KS + j;
-          *reinterpret_cast<uint4*>(gq + (slab * 32 + r) * 128 + ((p ^ (r & 7)) << 4)) = codes;
-          if (half == 0) gqs[(slab * 32 + r) * KSTEP + (p >> 1)] = s16;
-        }
-      }
-      if (xq_out && valid) *reinterpret_cast<uint4*>(xq_out + (size_t)t * d + c0) = codes;
-      if (xs_out && half == 0 && valid) xs_out[(size_t)t * (d / QB) + kb] = s16;
-    }
-    if (shg && valid) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) gacc = __builtin_fmaf(v[i], shg[c0 + i], gacc);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
-  }
-  if (shg) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) gacc += __shfl_xor(gacc, off, 64);
-    if (lane == 0) s_g[wave] = gacc;
-    __syncthreads();
-    if (active && h == 0 && lane == 0) gs[t] = 1.0f / (1.0f + expf(-(s_g[wave] + s_g[wave + 1])));
-  }
-}
-
 __device__ inline float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -480,7 +382,8 @@ __global__ __launch_bounds__(ROUTE_WIDE_THREADS) void route_kernel(
 // 16 experts' slab (16 KiB) and the N token rows (1 KiB each) are copied into
 // a ring of LDS buffers by all four wavefronts, 5 chunks ahead.  The
 // workgroups past the router ones quantise one token row each (the same
-// pieces, decisions and shared-gate order as quantize_scatter_kernel),
+// pieces, decisions and shared-gate order as the prefill quantiser in the
+// bucketing launch),
 // writing the token-major codes the decode matvecs read.
 constexpr int DR_E = 16;                              // experts per router workgroup
 constexpr int DR_J = 256;                             // j per chunk
@@ -732,15 +635,6 @@ hipError_t launch_router_route(const float* x, int n, int d, const float* wt, co
   dim3 grid((unsigned)((n + ROUTE_TILE - 1) / ROUTE_TILE), 1);
   router_kernel<true><<<grid, 512, 0, s>>>(x, n, d, wt, bias, E, 64, nullptr, k, norm, ids, w, rank,
                                            hist);
-  return hipGetLastError();
-}
-
-hipError_t launch_quantize_scatter(const float* x, int n, int d, int d_pad, const int32_t* pos,
-                                  int kk, int pad_rows, int8_t* gq, uint16_t* gqs,
-                                  const float* sh_gate_vec, float* gs, int8_t* xq_out,
-                                  uint16_t* xs_out, hipStream_t s) {
-  quantize_scatter_kernel<<<(n + 1) / 2, 256, 0, s>>>(x, n, d, d_pad, pos, kk, pad_rows, gq, gqs,
-                                                      sh_gate_vec, gs, xq_out, xs_out);
   return hipGetLastError();
 }
 
