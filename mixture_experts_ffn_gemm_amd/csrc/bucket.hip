@@ -2,7 +2,7 @@
 // levers" 1: the expStart / expTokI / expTokK CSR must be built on the GPU or the
 // selection round-trips to the host).
 //
-// The routing kernel left, per 16-token tile, a histogram of expert counts and
+// The routing left, per 8-token tile, a histogram of expert counts and
 // each (token, slot) pair's rank among the tile's pairs of the same expert.  A
 // pair's CSR position is then
 //     expStart[e] + (pairs of e in earlier tiles) + rank,
@@ -189,16 +189,16 @@ __global__ __launch_bounds__(BQ_THREADS) void bucket_quantize_kernel(
     for (int e = threadIdx.x; e <= E; e += BQ_THREADS) exp_start[e] = (e < E) ? s_start[e] : P;
     if (has_shared && threadIdx.x == 0) exp_start[E + 1] = P + n;
     for (int g = threadIdx.x; g < G; g += BQ_THREADS) {
-    const int c = s_cnt[g];
-    const int first = (g < E) ? s_start[g] : P;
-    const int ntg = (c + MT_WG - 1) / MT_WG;
-    for (int i = 0; i < ntg && s_nt[g] + i < tile_bound; ++i) {
-      int32_t* ent = tiles + 4 + 3 * (size_t)(s_nt[g] + i);
-      ent[0] = g;
-      ent[1] = first + i * MT_WG;
-      ent[2] = first + c;
+      const int c = s_cnt[g];
+      const int first = (g < E) ? s_start[g] : P;
+      const int ntg = (c + MT_WG - 1) / MT_WG;
+      for (int i = 0; i < ntg && s_nt[g] + i < tile_bound; ++i) {
+        int32_t* ent = tiles + 4 + 3 * (size_t)(s_nt[g] + i);
+        ent[0] = g;
+        ent[1] = first + i * MT_WG;
+        ent[2] = first + c;
+      }
     }
-  }
     if (threadIdx.x == 0) {
       tiles[0] = min(s_nt[G - 1] + last_nt, tile_bound);
       tiles[1] = 0;

@@ -25,7 +25,7 @@
 //
 // Workspace (per call, caller-allocated, carved by ws_layout()):
 //   logits fp32 [N][E]; ids, rank i32 [N][k]; w fp32 [N][k]; gs fp32 [N];
-//   hist i32 [ceil(N/16)][E]; exp_start i32 [E+2]; tok_i, tok_k i32 [N*k + N];
+//   hist i32 [ceil(N/8)][E]; exp_start i32 [E+2]; tok_i, tok_k i32 [N*k + N];
 //   pos i32 [N][k + has_shared]  (padded GEMM row of each (token, slot) pair:
 //                               first tile of its group * 128 + its index in
 //                               the group; -1 if beyond the tile bound);
