@@ -9,9 +9,9 @@
  *        grouped/segmented expert GEMM, scatter the results back;
  *        "argmax-stable (int8 MMQ)" is the accepted numeric contract;
  *   #388 "Carnice prefill toward llama.cpp 676 t/s", "Remaining levers" 1:
- *        router matvec + softmax + top-k + shared-expert gate on the GPU, with
- *        the expert bucketing (expStart / expTokI / expTokK CSR) built on the
- *        GPU so that the selection never round-trips to the host;
+ *        routing (logits, softmax, top-k, shared-expert gate) and the
+ *        expStart / expTokI / expTokK bucketing both run on the device, so
+ *        no routing data crosses to the host inside a call;
  *   #408 "full-offload MoE decode", "Hypothesis": 64 experts / 8 active,
  *        norm_topk_prob=false; one fused gathered-expert launch instead of
  *        per-expert matvecs; int8 (Q8_1-style) activations;
@@ -138,8 +138,15 @@ int moe_ffn_weights_destroy(moe_ffn_weights* w);
 int moe_ffn_weights_dims(const moe_ffn_weights* w, moe_ffn_dims* dims_out);
 
 /* Workspace bytes needed by a prefill or decode call over up to max_tokens
- * tokens (host-side query, nothing enqueued). */
+ * tokens (host-side query, nothing enqueued).  The size never decreases as
+ * max_tokens grows, so a workspace sized once for max_tokens serves every
+ * prefill or decode call with n_tokens <= max_tokens. */
 int moe_ffn_workspace_size(const moe_ffn_weights* w, int32_t max_tokens, size_t* bytes);
+
+/* The same size from the layer shape alone, before any weights exist (pure
+ * host computation; no device call).  Returns the moe_ffn_weights_create
+ * status for dims it would reject. */
+int moe_ffn_workspace_size_for_dims(const moe_ffn_dims* dims, int32_t max_tokens, size_t* bytes);
 
 /* The batched MoE FFN over n_tokens tokens (#406 "The work" item 2):
  * router + top-k + weights (+ shared gate), per-32 int8 quantiser, CSR
@@ -229,6 +236,31 @@ int moe_ffn_quantize(const float* v, int64_t n_values, int8_t* q, uint16_t* scal
  * moe_ffn_prefill_residual's fused combine (4-column chunks per thread). */
 int moe_ffn_residual_rmsnorm(float* h, const float* y, float* xn, int32_t n, int32_t d,
                              float eps, hipStream_t stream);
+
+/* Parity hook: the integer core of a grouped GEMM (#406 "References": Q8_0
+ * MMQ -- the products are exact int32 sums per 32-block before any scale).
+ * Runs k-block `kblock` of 128-row tile `tile` against column strip `strip`
+ * of the gate/up GEMM (gemm = 0; A = the tile's int8 activation rows, strip s
+ * = gate rows 64s..64s+63 then up rows 64s..64s+63) or of the down GEMM
+ * (gemm = 1; A = the tile's int8 h rows, strip s = down rows 128s..128s+127),
+ * through the same copies, LDS layout, operand reads and int8 MFMA as the
+ * product kernels, and writes
+ *   sums     int32 [128][128]: sums[r][c] = sum over the block's 32 codes of
+ *            A row r times weight row c of the strip (exact integers);
+ *   a_codes  int8 [128][32] (16-byte aligned): the 32 codes A row r held;
+ *   info     int32 [4]: {group, first CSR row, end CSR row, tile count}.
+ *            Tile row r is CSR row first + r, valid while it is below end
+ *            (rows past it hold no pair).  group is -1 when `tile` is at or
+ *            past the tile count, -3 when strip or k-block lies outside that
+ *            group's planes (nothing else is written then).
+ * ws must hold the workspace of a moe_ffn_prefill (or _residual) call over
+ * n_tokens tokens enqueued earlier on `stream`, and is not modified.  All
+ * buffers are device memory; none may overlap the workspace.  Returns
+ * MOE_FFN_INVALID_ARG for a tile at or past the workspace's tile bound, or a
+ * strip or k-block outside every group's planes. */
+int moe_ffn_dbg_block_sums(const moe_ffn_weights* w, void* ws, size_t ws_bytes, int32_t n_tokens,
+                           int32_t gemm, int32_t tile, int32_t strip, int32_t kblock, int32_t* sums,
+                           int8_t* a_codes, int32_t* info, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* moe_ffn_status_str(int status);

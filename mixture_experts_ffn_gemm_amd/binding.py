@@ -24,10 +24,10 @@ MOE_FFN_OUT_OF_MEMORY = -4
 MOE_FFN_HIP_ERROR = -5
 
 EXPORTED = ("moe_ffn_weights_create", "moe_ffn_weights_destroy", "moe_ffn_weights_dims",
-            "moe_ffn_workspace_size", "moe_ffn_prefill", "moe_ffn_prefill_residual", "moe_ffn_prefill_profiled",
+            "moe_ffn_workspace_size", "moe_ffn_workspace_size_for_dims", "moe_ffn_prefill", "moe_ffn_prefill_residual", "moe_ffn_prefill_profiled",
             "moe_ffn_decode",
             "moe_ffn_decode_profiled", "moe_ffn_combine",
-            "moe_ffn_quantize", "moe_ffn_residual_rmsnorm", "moe_ffn_status_str")
+            "moe_ffn_quantize", "moe_ffn_residual_rmsnorm", "moe_ffn_dbg_block_sums", "moe_ffn_status_str")
 
 
 class MoeFfnError(RuntimeError):
@@ -65,6 +65,7 @@ def lib():
             "moe_ffn_weights_destroy": [vp],
             "moe_ffn_weights_dims": [vp, C.POINTER(moe_ffn_dims)],
             "moe_ffn_workspace_size": [vp, i32, C.POINTER(sz)],
+            "moe_ffn_workspace_size_for_dims": [C.POINTER(moe_ffn_dims), i32, C.POINTER(sz)],
             "moe_ffn_prefill": [vp, vp, i32, vp, vp, sz, C.POINTER(moe_ffn_routing), vp],
             "moe_ffn_prefill_residual": [vp, vp, i32, vp, vp, C.c_float, vp, sz, C.POINTER(moe_ffn_routing), vp],
             "moe_ffn_decode": [vp, vp, i32, vp, vp, sz, C.POINTER(moe_ffn_routing), vp],
@@ -75,6 +76,7 @@ def lib():
             "moe_ffn_combine": [vp, vp, vp, i32, i32, i32, vp, vp],
             "moe_ffn_quantize": [vp, i64, vp, vp, vp],
             "moe_ffn_residual_rmsnorm": [vp, vp, vp, i32, i32, C.c_float, vp],
+            "moe_ffn_dbg_block_sums": [vp, vp, sz, i32, i32, i32, i32, i32, vp, vp, vp, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -140,6 +142,13 @@ def moe_ffn_weights_dims(handle: int) -> moe_ffn_dims:
 def moe_ffn_workspace_size(handle: int, max_tokens: int) -> int:
     n = C.c_size_t()
     _check("moe_ffn_workspace_size", lib().moe_ffn_workspace_size(handle, int(max_tokens), C.byref(n)))
+    return n.value
+
+
+def moe_ffn_workspace_size_for_dims(dims: moe_ffn_dims, max_tokens: int) -> int:
+    n = C.c_size_t()
+    _check("moe_ffn_workspace_size_for_dims",
+           lib().moe_ffn_workspace_size_for_dims(C.byref(dims), int(max_tokens), C.byref(n)))
     return n.value
 
 
@@ -216,6 +225,16 @@ def moe_ffn_residual_rmsnorm(h, y, xn, n: int, d: int, eps: float, stream=None) 
     rc = lib().moe_ffn_residual_rmsnorm(_ptr(h), _ptr(y), _ptr(xn), int(n), int(d), float(eps),
                                         _stream(stream))
     _check("moe_ffn_residual_rmsnorm", rc)
+
+
+def moe_ffn_dbg_block_sums(handle: int, ws, ws_bytes: int, n_tokens: int, gemm: int, tile: int, strip: int,
+                           kblock: int, sums, a_codes, info, stream=None) -> None:
+    """The exact int32 block sums of one k-block of one (tile, strip) of the
+    gate/up (gemm=0) or down (gemm=1) GEMM of the last prefill on ws."""
+    rc = lib().moe_ffn_dbg_block_sums(handle, _ptr(ws), int(ws_bytes), int(n_tokens), int(gemm), int(tile),
+                                      int(strip), int(kblock), _ptr(sums), _ptr(a_codes), _ptr(info),
+                                      _stream(stream))
+    _check("moe_ffn_dbg_block_sums", rc)
 
 
 def moe_ffn_status_str(status: int) -> str:

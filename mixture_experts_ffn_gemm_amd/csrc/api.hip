@@ -2,8 +2,8 @@
 // workspace carving and the launch sequence of one MoE FFN layer.
 //
 // One prefill call enqueues, on the caller's stream and without any host
-// synchronisation or device-to-host transfer (SharpInference #388 "Remaining
-// levers" 1: the selection must not round-trip to the host):
+// synchronisation or device-to-host transfer (the routing result stays on
+// the device; SharpInference #388, "Remaining levers" 1):
 //   1. router                   (fp32 fused-chain logits for all experts)
 //   2. routing                  (top-k, softmax weights, per-tile expert
 //                                histograms and ranks; in the router's
@@ -60,16 +60,16 @@ WsLayout ws_layout(const Dims& dm, int max_tokens) {
   L.hq = take(t32 * kbmax * 1024);
   L.hs = take(t32 * 32 * kbmax * 2);
   L.partial = take(Nn * kk * dm.d * 4);
-  if (max_tokens >= 1 && max_tokens <= DECODE_MAX_TOKENS) {
-    const size_t nb = std::min((size_t)dm.E, Nn * dm.k) + dm.has_shared;
-    L.dlist = take((4 + DLIST_ENTRY * nb) * 4);
-    L.dxq = take(Nn * dm.d_pad);
-    L.dxs = take(Nn * (dm.d_pad / QB) * 2);
-    L.dhq = take(Nn * kk * dm.kmax_pad);
-    L.dhs = take(Nn * kk * (dm.kmax_pad / QB) * 2);
-  } else {
-    L.dlist = L.dxq = L.dxs = L.dhq = L.dhs = off;
-  }
+  // The decode region is always reserved, for min(max_tokens, 8) tokens, so
+  // that the total never shrinks as max_tokens grows: a workspace sized once
+  // for max_tokens serves every call with fewer tokens, decode included.
+  const size_t Nd = std::min(Nn, (size_t)DECODE_MAX_TOKENS);
+  const size_t nb = std::min((size_t)dm.E, Nd * dm.k) + dm.has_shared;
+  L.dlist = take((4 + DLIST_ENTRY * nb) * 4);
+  L.dxq = take(Nd * dm.d_pad);
+  L.dxs = take(Nd * (dm.d_pad / QB) * 2);
+  L.dhq = take(Nd * kk * dm.kmax_pad);
+  L.dhs = take(Nd * kk * (dm.kmax_pad / QB) * 2);
   L.total = off;
   return L;
 }
@@ -150,6 +150,40 @@ hipError_t copy_routing(const Dims& dm, int n, const moe_ffn_routing* r, const i
   return e;
 }
 
+// The arguments of the two grouped GEMMs of a call over n tokens whose
+// workspace (laid out as L) starts at base.
+GemmArgs gemm_args(const moe_ffn_weights* W, const WsLayout& L, char* base, int n) {
+  const Dims& dm = W->dm;
+  GemmArgs a{};
+  a.tiles = (const int32_t*)(base + L.tiles);
+  a.tok_i = (const int32_t*)(base + L.tok_i);
+  a.tok_k = (const int32_t*)(base + L.tok_k);
+  a.E = dm.E;
+  a.G = dm.G;
+  a.n_tokens = n;
+  a.p_total = n * dm.k + (dm.has_shared ? n : 0);
+  a.tile_bound = L.tile_bound;
+  a.kbmax = dm.kmax_pad / QB;
+  a.hq = (int8_t*)(base + L.hq);
+  a.hs = (uint16_t*)(base + L.hs);
+  a.gq = (const int8_t*)(base + L.gq);
+  a.gqs = (const uint16_t*)(base + L.gqs);
+  a.d_pad = dm.d_pad;
+  a.gu = W->gu;
+  a.gu_group = W->gu_per_expert;
+  a.sh_gu = W->sh_gu;
+  a.F_pad = dm.F_pad;
+  a.Fs_pad = dm.Fs_pad;
+  a.dn = W->dn;
+  a.dn_group = W->dn_per_expert;
+  a.sh_dn = W->sh_dn;
+  a.dn_exp = W->dn_exp;
+  a.partial = (float*)(base + L.partial);
+  a.d = dm.d;
+  a.kk = dm.k + dm.has_shared;
+  return a;
+}
+
 // The stack form of a layer: instead of writing the layer's output, its
 // combine adds it to the residual stream h and writes the next layer's
 // input xn = RMSNorm(h).
@@ -200,8 +234,6 @@ int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, v
   int32_t* tiles = (int32_t*)(base + L.tiles);
   int8_t* gq = (int8_t*)(base + L.gq);
   uint16_t* gqs = (uint16_t*)(base + L.gqs);
-  int8_t* hq = (int8_t*)(base + L.hq);
-  uint16_t* hs = (uint16_t*)(base + L.hs);
   float* partial = (float*)(base + L.partial);
   const int kk = dm.k + dm.has_shared;
   auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
@@ -223,33 +255,7 @@ int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, v
                                  tiles, L.tile_bound, x, dm.d, dm.d_pad, gq, gqs,
                                  dm.has_shared ? W->sh_gate_vec : nullptr, gs, r ? r->xq : nullptr,
                                  r ? r->xs : nullptr, s));
-  GemmArgs a{};
-  a.tiles = tiles;
-  a.tok_i = tok_i;
-  a.tok_k = tok_k;
-  a.E = dm.E;
-  a.G = dm.G;
-  a.n_tokens = n;
-  a.p_total = n * dm.k + (dm.has_shared ? n : 0);
-  a.tile_bound = L.tile_bound;
-  a.kbmax = dm.kmax_pad / QB;
-  a.hq = hq;
-  a.hs = hs;
-  a.gq = gq;
-  a.gqs = gqs;
-  a.d_pad = dm.d_pad;
-  a.gu = W->gu;
-  a.gu_group = W->gu_per_expert;
-  a.sh_gu = W->sh_gu;
-  a.F_pad = dm.F_pad;
-  a.Fs_pad = dm.Fs_pad;
-  a.dn = W->dn;
-  a.dn_group = W->dn_per_expert;
-  a.sh_dn = W->sh_dn;
-  a.dn_exp = W->dn_exp;
-  a.partial = partial;
-  a.d = dm.d;
-  a.kk = kk;
+  const GemmArgs a = gemm_args(W, L, base, n);
   HIP_TRY(mark(3));
   HIP_TRY(launch_gateup(a, s));
   HIP_TRY(mark(4));
@@ -485,6 +491,14 @@ int moe_ffn_workspace_size(const moe_ffn_weights* w, int32_t max_tokens, size_t*
   return MOE_FFN_OK;
 }
 
+int moe_ffn_workspace_size_for_dims(const moe_ffn_dims* dims, int32_t max_tokens, size_t* bytes) {
+  if (!bytes || max_tokens < 0 || max_tokens > MAX_TOKENS) return MOE_FFN_INVALID_ARG;
+  const int rc = check_dims(dims);
+  if (rc != MOE_FFN_OK) return rc;
+  *bytes = ws_layout(make_dims(dims), max_tokens).total;
+  return MOE_FFN_OK;
+}
+
 int moe_ffn_prefill(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* out,
                     void* ws, size_t ws_bytes, const moe_ffn_routing* routing, hipStream_t stream) {
   return run_layer(w, x, n_tokens, out, ws, ws_bytes, routing, stream);
@@ -554,6 +568,30 @@ int moe_ffn_residual_rmsnorm(float* h, const float* y, float* xn, int32_t n, int
   const size_t b = (size_t)n * d * 4;
   if (overlaps(xn, b, h, b) || (y && overlaps(xn, b, y, b))) return MOE_FFN_INVALID_ARG;
   HIP_TRY(launch_residual_rmsnorm(h, y, xn, n, d, eps, stream));
+  return MOE_FFN_OK;
+}
+
+int moe_ffn_dbg_block_sums(const moe_ffn_weights* w, void* ws, size_t ws_bytes, int32_t n_tokens,
+                           int32_t gemm, int32_t tile, int32_t strip, int32_t kblock, int32_t* sums,
+                           int8_t* a_codes, int32_t* info, hipStream_t stream) {
+  if (!w || !ws || !sums || !a_codes || !info) return MOE_FFN_INVALID_ARG;
+  if (n_tokens < 1 || n_tokens > MAX_TOKENS || (gemm != 0 && gemm != 1)) return MOE_FFN_INVALID_ARG;
+  const Dims& dm = w->dm;
+  const WsLayout L = ws_layout(dm, n_tokens);
+  if (ws_bytes < L.total) return MOE_FFN_WORKSPACE_TOO_SMALL;
+  if ((uintptr_t)ws & 255u) return MOE_FFN_INVALID_ARG;
+  // a bound over every group; the kernel checks the tile's own group
+  const int strips = gemm == 0 ? dm.kmax_pad / GU_COLS : dm.d_pad / DN_COLS;
+  const int kbs = gemm == 0 ? dm.d_pad / QB : dm.kmax_pad / QB;
+  if (tile < 0 || tile >= L.tile_bound || strip < 0 || strip >= strips || kblock < 0 || kblock >= kbs)
+    return MOE_FFN_INVALID_ARG;
+  if (overlaps(sums, 128 * 128 * 4, ws, ws_bytes) || overlaps(a_codes, 128 * 32, ws, ws_bytes) ||
+      overlaps(info, 16, ws, ws_bytes) || ((uintptr_t)a_codes & 15u))
+    return MOE_FFN_INVALID_ARG;
+  const int dev_ok = current_device_matches(w);
+  if (dev_ok != MOE_FFN_OK) return dev_ok;
+  const GemmArgs a = gemm_args(w, L, (char*)ws, n_tokens);
+  HIP_TRY(launch_block_sums(a, gemm == 0, tile, strip, kblock, sums, a_codes, info, stream));
   return MOE_FFN_OK;
 }
 

@@ -1,6 +1,7 @@
-// bucket.hip -- expert bucketing on the GPU (SharpInference #388 "Remaining
-// levers" 1: the expStart / expTokI / expTokK CSR must be built on the GPU or the
-// selection round-trips to the host).
+// bucket.hip -- expert bucketing on the GPU: the expStart / expTokI / expTokK
+// CSR is built on the device, so the routing result never travels to the host
+// between routing and the expert GEMMs (SharpInference #388, "Remaining
+// levers" 1).
 //
 // The routing left, per 8-token tile, a histogram of expert counts and
 // each (token, slot) pair's rank among the tile's pairs of the same expert.  A

@@ -1,11 +1,11 @@
 // combine.hip -- the ordered weighted combine and the layer-stack helper.
 //
-// SharpInference #129 "Scope": one launch over N x embDim that, for each token
-// row, sums the na unweighted down-partials in top-k slot order (k = 0..na-1)
-// with their per-(token, slot) weights, then adds the shared-expert row.  The
-// per-token accumulation order is load-bearing, so every output element is one
-// fp32 fused multiply-add chain in exactly that order.  The kernel is a pure
-// stream (HBM-bound): each thread owns 4 consecutive columns of one token.
+// SharpInference #129, "Scope": a single launch covers all N x d outputs.
+// Output element (t, j) is an fp32 fused multiply-add chain that starts at +0,
+// takes slot 0, 1, ..., k-1 of token t (weight times unweighted partial) and
+// ends with the gated shared-expert row.  Results must not depend on how the
+// work is split, so that chain order is fixed.  The kernel is a pure stream
+// (HBM-bound): each thread owns 4 consecutive columns of one token.
 #include "internal.h"
 
 namespace moe {

@@ -129,9 +129,13 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t l
 }
 
 // Wait until at most n of this wavefront's copies are in flight (vector loads
-// complete in order), then meet the other wavefronts.
+// complete in order), then meet the other wavefronts.  The k-loop form also
+// waits for this wavefront's LDS reads: operands of the buffer that the
+// copies issued right after the barrier overwrite may still be in flight
+// (their registers are consumed only after the barrier), and the barrier
+// itself does not order them against other wavefronts' copies.
 __device__ __forceinline__ void wait_copies_barrier_0() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -609,7 +613,88 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
 
 int grid_for(long wgs) { return (int)((wgs + 7) / 8 * 8); }
 
+// The integer core of a grouped GEMM, exposed for parity checks: k-block kb
+// of tile T against strip cs, through the product kernels' own path -- the
+// same global->LDS copies of the same planes, the same LDS layout and operand
+// reads, and the same int8 MFMA from the same accumulator bias -- with the
+// bias subtracted again, so sums[r][c] is the exact int32 block sum of tile
+// row r (wavefront r/32) and strip column c = 32 * tile + column.  acodes[r]
+// receives the 32 activation codes the A operand held for row r; info =
+// {group, first CSR row, end CSR row, tile count} (group -1: T is past the
+// tile count; -2: a malformed tile entry; -3: strip or k-block outside the
+// group's planes).  One workgroup, launched after a prefill call on the same
+// workspace.
+template <bool GATEUP>
+__global__ __launch_bounds__(256) void block_sums_kernel(GemmArgs a, int T, int cs, int kb,
+                                                         int32_t* __restrict__ sums,
+                                                         int8_t* __restrict__ acodes,
+                                                         int32_t* __restrict__ info) {
+  using L = Lay<GATEUP>;
+  __shared__ __attribute__((aligned(1024))) char lds[L::STAGE];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_tiles = min(a.tiles[0], a.tile_bound);
+  auto fail = [&](int code, int g, int r0, int r1) {
+    if (threadIdx.x == 0) {
+      info[0] = code < 0 ? code : g;
+      info[1] = r0;
+      info[2] = r1;
+      info[3] = n_tiles;
+    }
+  };
+  if (T >= n_tiles) return fail(-1, 0, 0, 0);
+  const int32_t* ent = a.tiles + 4 + 3 * T;
+  const int g = ent[0], row0 = ent[1], row_end = ent[2];
+  if (g < 0 || g >= a.G || row0 < 0 || row_end <= row0 || row_end > a.p_total) return fail(-2, 0, 0, 0);
+  const bool shared = g >= a.E;
+  const int Fg_pad = shared ? a.Fs_pad : a.F_pad;
+  const int nstrips = GATEUP ? Fg_pad / GU_COLS : a.d_pad / DN_COLS;
+  const int KB = GATEUP ? a.d_pad / QB : Fg_pad / QB;
+  if (cs < 0 || cs >= nstrips || kb < 0 || kb >= KB) return fail(-3, 0, 0, 0);
+  const int KS = KB / KSTEP;
+  const uint8_t* strip = GATEUP ? (shared ? a.sh_gu : a.gu + (size_t)g * a.gu_group)
+                                : (shared ? a.sh_dn : a.dn + (size_t)g * a.dn_group);
+  strip += (size_t)cs * KS * L::W_BYTES;
+  const int t32 = T * NWAVE + wave;
+  const int a_kb = GATEUP ? a.d_pad / QB : a.kbmax;
+  Src src;
+  src.w = strip;
+  src.o_w = lane * 16;
+  src.o_ws = 16 * 1024 + wave * (GATEUP ? 256 : 512) + lane * 4;
+  src.a = (GATEUP ? a.gq : a.hq) + (size_t)t32 * a_kb * 1024;
+  src.as = (GATEUP ? a.gqs : a.hs) + (size_t)t32 * a_kb * 32;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)&lds[0];
+  const int j = kb / KSTEP, b = kb % KSTEP;
+  issue_weights<GATEUP>(src, j, lds0, wave);
+  issue_acts<GATEUP>(src, j, lds0, wave, lane);
+  wait_copies_barrier_0();
+  Ops X;
+  read_block<GATEUP>(lds, b, wave, lane, X);
+  const int bias = GATEUP ? 0x4b400000 : 0x3fc00000;  // 1.5 * 2^23, 1.5f
+  v16i magic;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) magic[v] = bias;
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(X.a, X.b[tt], magic, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      sums[(size_t)(wave * 32 + out_row(v, lane)) * 128 + tt * 32 + (lane & 31)] = c[v] - bias;
+  }
+  *reinterpret_cast<v4i*>(acodes + (size_t)(wave * 32 + (lane & 31)) * 32 + 16 * (lane >> 5)) = X.a;
+  fail(0, g, row0, row_end);
+}
+
 }  // namespace
+
+hipError_t launch_block_sums(const GemmArgs& a, bool gateup, int tile, int strip, int kblock, int32_t* sums,
+                             int8_t* acodes, int32_t* info, hipStream_t s) {
+  if (gateup)
+    block_sums_kernel<true><<<1, 256, 0, s>>>(a, tile, strip, kblock, sums, acodes, info);
+  else
+    block_sums_kernel<false><<<1, 256, 0, s>>>(a, tile, strip, kblock, sums, acodes, info);
+  return hipGetLastError();
+}
 
 hipError_t launch_gateup(const GemmArgs& a, hipStream_t s) {
   const long wgs = (long)a.tile_bound * (max(a.F_pad, a.Fs_pad) / GU_COLS);

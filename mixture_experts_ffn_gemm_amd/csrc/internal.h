@@ -41,16 +41,17 @@
 //   hq int8 [4*T_bound][KBMAX/4][32][128], hs fp16 [4*T_bound][KBMAX/4][32][4]
 //                               (the same for h, the down GEMM's A operand);
 //   partial fp32 [N][k + has_shared][d].
-// Decode (N <= DECODE_MAX_TOKENS) additionally:
-//   dlist i32 [4 + 16 * (min(E, N*k) + has_shared)]  (dlist[0] = number of
+// The decode region, always reserved for Nd = min(N, DECODE_MAX_TOKENS) tokens
+// (so the total never shrinks as N grows), used by decode calls only:
+//   dlist i32 [4 + 16 * (min(E, Nd*k) + has_shared)]  (dlist[0] = number of
 //                               active groups; entry a = dlist + 4 + 16 a:
 //                               {group, rows c, 6 unused, pair p[8]}, where
 //                               row j < c is the (token, slot) pair
 //                               p = token * kk + slot, tokens ascending;
 //                               routed groups ascending, then the shared one);
-//   dxq int8 [N][d_pad], dxs fp16 [N][d_pad/32]   (token-major activation
+//   dxq int8 [Nd][d_pad], dxs fp16 [Nd][d_pad/32]   (token-major activation
 //                               codes/scales, zero past d);
-//   dhq int8 [N*kk][kmax_pad], dhs fp16 [N*kk][kmax_pad/32]  (h per pair).
+//   dhq int8 [Nd*kk][kmax_pad], dhs fp16 [Nd*kk][kmax_pad/32]  (h per pair).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -90,7 +91,7 @@ inline int round_up(int v, int m) { return (v + m - 1) / m * m; }
 
 struct WsLayout {
   size_t logits, ids, rank, w, gs, hist, exp_start, tok_i, tok_k, pos, tiles, gq, gqs, hq, hs, partial;
-  size_t dlist, dxq, dxs, dhq, dhs;  // decode only (offset `total`, size 0, otherwise)
+  size_t dlist, dxq, dxs, dhq, dhs;  // decode region (min(N, 8) tokens)
   size_t total;
   int n_route_tiles;
   int tile_bound;
@@ -191,6 +192,11 @@ struct GemmArgs {
 
 hipError_t launch_gateup(const GemmArgs& a, hipStream_t s);
 hipError_t launch_down(const GemmArgs& a, hipStream_t s);
+// One k-block of one (tile, strip) of a grouped GEMM through the product's
+// copies, LDS layout and int8 MFMA: exact int32 block sums [128][128], the A
+// codes [128][32] and {group, row0, row_end, n_tiles} (one workgroup).
+hipError_t launch_block_sums(const GemmArgs& a, bool gateup, int tile, int strip, int kblock, int32_t* sums,
+                             int8_t* acodes, int32_t* info, hipStream_t s);
 
 // ---- decode (1 <= N <= DECODE_MAX_TOKENS) ----
 // Router logits [N][E] (fp32 FMA chains, as launch_router), plus the

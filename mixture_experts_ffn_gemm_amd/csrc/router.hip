@@ -2,9 +2,10 @@
 // histograms, the decode router, and the standalone per-32 int8 quantiser.
 // (The prefill activation quantiser runs in the bucketing launch.)
 //
-// SharpInference #388 "Remaining levers" 1 moves the router matvec
-// norm[N x embDim] x routerW[numExperts x embDim] + softmax + top-k + shexp-gate
-// onto the GPU; #408 "Hypothesis" lever 3 folds it into the GPU path for decode.
+// The routing step of the layer runs on the device for prefill
+// (SharpInference #388, "Remaining levers" 1) and for decode (#408,
+// "Hypothesis" lever 3): every token's logits against every expert row, the
+// softmax, the top-k selection and the shared-expert gate.
 #include <hip/hip_fp16.h>
 
 #include "device_util.h"

@@ -84,8 +84,9 @@ void ora_float_to_half(const float* f, uint16_t* h, int64_t n) {
 }
 
 /* -------------------------------------------------------------- router */
-/* #388 lever 1: norm[N x embDim] x routerW[numExperts x embDim].  Each logit
- * is one fp32 chain of fused multiply-adds over ascending j. */
+/* #388, "Remaining levers" 1: the logits of every token against every
+ * expert's router row.  Each logit is one fp32 chain of fused multiply-adds
+ * over ascending j. */
 void ora_router_logits(const float* x, int32_t n, int32_t d, const float* w,
                        const float* bias, int32_t n_experts, float* logits) {
   for (int32_t t = 0; t < n; ++t) {
@@ -230,6 +231,19 @@ double ora_q8_dot(const int8_t* qa, const uint16_t* sa16, const uint8_t* w_row, 
     acc += (double)c * s;
   }
   return acc;
+}
+
+/* The integer core of the int8 MMQ product, one block at a time: the same
+ * exact int32 block sum ora_q8_dot forms, for a grid of rows. */
+void ora_q8_block_sums(const int8_t* qa, int32_t m, const uint8_t* w, int32_t n, int64_t row_bytes,
+                       int32_t kblock, int32_t* out) {
+  for (int32_t i = 0; i < m; ++i)
+    for (int32_t j = 0; j < n; ++j) {
+      const int8_t* qw = (const int8_t*)(w + (int64_t)j * row_bytes + (int64_t)kblock * QBYTES + 2);
+      int32_t c = 0;
+      for (int t = 0; t < QB; ++t) c += (int32_t)qa[(int64_t)i * QB + t] * (int32_t)qw[t];
+      out[(int64_t)i * n + j] = c;
+    }
 }
 
 /* ------------------------------------------------------------- expert */

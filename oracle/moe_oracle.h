@@ -15,8 +15,8 @@
  *        64 experts / 8 active, norm_topk_prob=false; Q8_1 (int8 block)
  *        activations for the expert matvec; router on the GPU.
  *   #388 "Carnice prefill toward llama.cpp 676 t/s", "Remaining levers" 1:
- *        router matvec norm[N x embDim] x routerW[numExperts x embDim] +
- *        softmax + top-k + shared-expert gate, bucketed into the CSR
+ *        per-token logits against all expert rows, softmax, top-k and the
+ *        shared-expert gate, with the pairs bucketed into the CSR
  *        expStart / expTokI / expTokK.
  *   #129 (batched weighted scatter-reduce), "Scope": per token, sum the na
  *        unweighted down-partials in top-k slot order with the per-(token,
@@ -85,6 +85,15 @@ void ora_quantize_q8(const float* v, int64_t n_values, int8_t* q, uint16_t* scal
 /* Q8 dot of an activation row (codes + fp16 scales) with one Q8_0 weight row:
  * sum over blocks of exact int32 block sums times sa*sw, in fp64. */
 double ora_q8_dot(const int8_t* qa, const uint16_t* sa16, const uint8_t* w_row, int32_t n_blocks);
+
+/* The exact int32 sums of one 32-block of an int8 MMQ product (#406
+ * "References": Q8_0 MMQ): for activation rows i < m (32 codes each, qa
+ * [m][32]) and Q8_0 weight rows j < n (row j starts at w + j * row_bytes),
+ *   out[i][j] = sum over t < 32 of qa[i][t] * code t of block kblock of row j.
+ * No scale enters: these are the integers the scaled block products are
+ * formed from. */
+void ora_q8_block_sums(const int8_t* qa, int32_t m, const uint8_t* w, int32_t n, int64_t row_bytes,
+                       int32_t kblock, int32_t* out);
 
 /* One SwiGLU expert on one quantised token row: g,u = Q8 dots; h = silu(g)*u
  * (fp64), requantised per 32 in fp32; y = Q8 dot with the down rows.

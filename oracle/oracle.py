@@ -42,6 +42,7 @@ def lib():
             "ora_csr": (None, [vp, i32, i32, i32, i32, vp, vp, vp]),
             "ora_quantize_q8": (None, [vp, i64, vp, vp]),
             "ora_q8_dot": (dbl, [vp, vp, vp, i32]),
+            "ora_q8_block_sums": (None, [vp, i32, vp, i32, i64, i32, vp]),
             "ora_expert_ffn": (None, [i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "ora_moe_tokens": (i32, [C.POINTER(OraDims), vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                      vp, vp, i32, vp, vp, vp, vp, vp]),
@@ -145,6 +146,18 @@ def q8_dot(qa, sa16, w_row) -> float:
     sa16 = _c(sa16, np.uint16)
     w_row = _c(w_row, np.uint8)
     return lib().ora_q8_dot(_p(qa), _p(sa16), _p(w_row), qa.size // 32)
+
+
+def q8_block_sums(qa, w_rows, kblock: int) -> np.ndarray:
+    """Exact int32 sums of block `kblock`: qa int8 [m][32] codes against the
+    Q8_0 weight rows w_rows (uint8 [n][row_bytes]) -> int32 [m][n]."""
+    qa = _c(qa, np.int8).reshape(-1, 32)
+    w_rows = _c(w_rows, np.uint8)
+    m, n = qa.shape[0], w_rows.shape[0]
+    assert 0 <= kblock and (kblock + 1) * 34 <= w_rows.shape[1]
+    out = np.empty((m, n), np.int32)
+    lib().ora_q8_block_sums(_p(qa), m, _p(w_rows), n, w_rows.shape[1], int(kblock), _p(out))
+    return out
 
 
 def expert_ffn(d, ffn, xq, xs, gate, up, down):

@@ -95,3 +95,31 @@ def test_stage_entry_points_validate_on_the_host(B):
     ev = (C.c_void_p * 5)(*([None] * 5))
     assert L.moe_ffn_decode_profiled(None, 16, 1, 32, 64, 1 << 20, None, None, ev) == -1     # null events
     assert L.moe_ffn_weights_destroy(None) == 0
+
+
+@pytest.mark.parametrize("dims", [
+    (2048, 64, 8, 1024, 0, 0),      # OLMoE-shaped layer
+    (128, 8, 2, 256, 0, 0),         # tiny
+    (2048, 256, 8, 512, 512, 1),    # 35B-A3B-shaped layer with a shared expert
+    (160, 16, 3, 96, 64, 0),
+    (128, 256, 16, 64, 32, 0),
+])
+def test_workspace_size_never_shrinks_with_max_tokens(B, dims):
+    """A workspace sized once for max_tokens must serve every call with fewer
+    tokens (prefill or decode), so the size is non-decreasing in max_tokens."""
+    dm = B.moe_ffn_dims(*dims)
+    sizes = [B.moe_ffn_workspace_size_for_dims(dm, n) for n in range(0, 70)]
+    sizes += [B.moe_ffn_workspace_size_for_dims(dm, n) for n in (127, 128, 129, 511, 512, 513, 2048, 4096)]
+    assert all(a <= b for a, b in zip(sizes, sizes[1:])), sizes
+    assert sizes[0] > 0
+
+
+def test_workspace_size_for_dims_validates(B):
+    n = C.c_size_t()
+    L = B.lib()
+    assert L.moe_ffn_workspace_size_for_dims(None, 16, C.byref(n)) == -1
+    dm = B.moe_ffn_dims(100, 8, 2, 256, 0, 0)
+    assert L.moe_ffn_workspace_size_for_dims(C.byref(dm), 16, C.byref(n)) == -2
+    dm = B.moe_ffn_dims(128, 8, 2, 256, 0, 0)
+    assert L.moe_ffn_workspace_size_for_dims(C.byref(dm), -1, C.byref(n)) == -1
+    assert L.moe_ffn_workspace_size_for_dims(C.byref(dm), 16, None) == -1

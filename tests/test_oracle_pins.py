@@ -266,6 +266,35 @@ def test_q8_dot_block_sums_are_exact_integers():
     assert got == float(prod.sum() + prod[64:96].sum())
 
 
+def test_q8_block_sums_match_int64_matmul():
+    """The integer core: per-block int32 sums equal numpy's int64 product of
+    the unpacked int8 codes, block by block; extreme codes (+-127 everywhere,
+    the largest |sum| a block can reach) stay exact."""
+    rng = np.random.default_rng(16)
+    d, m, n = 256, 7, 5
+    W = mw.pack_q8_0((rng.standard_normal((n, d)) * 0.02).astype(np.float32))
+    codes, _ = mw.unpack_q8_0(W, d)
+    qa = rng.integers(-127, 128, (m, d)).astype(np.int8)
+    for kb in range(d // 32):
+        got = O.q8_block_sums(qa[:, 32 * kb:32 * kb + 32], W, kb)
+        ref = qa[:, 32 * kb:32 * kb + 32].astype(np.int64) @ codes[:, 32 * kb:32 * kb + 32].astype(np.int64).T
+        assert np.array_equal(got, ref)
+    # block kb reads its own 32 codes only: an extreme block next to zeros
+    Wx = W.copy().reshape(n, d // 32, 34)
+    Wx[:, :, 2:] = 0
+    Wx[:, 3, 2:] = np.int8(-127).view(np.uint8)
+    Wx = Wx.reshape(n, -1)
+    qx = np.full((1, 32), 127, np.int8)
+    assert np.all(O.q8_block_sums(qx, Wx, 3) == -127 * 127 * 32)
+    assert np.all(O.q8_block_sums(qx, Wx, 2) == 0)
+    # the scaled Q8 dot is the sum of these integers times the block scales
+    xs = np.full(d // 32, np.float16(1.0).view(np.uint16), np.uint16)
+    tot = sum(int(O.q8_block_sums(qa[0:1, 32 * kb:32 * kb + 32], W[0:1], kb)[0, 0]) *
+              float(np.float16(W[0].reshape(-1, 34)[kb, :2].view(np.float16)[0]))
+              for kb in range(d // 32))
+    assert abs(O.q8_dot(qa[0], xs, W[0]) - tot) <= 1e-12 * abs(tot) + 1e-15
+
+
 # ---------------------------------------------------------------- expert
 def test_expert_ffn_against_numpy():
     rng = np.random.default_rng(12)
@@ -335,6 +364,31 @@ def test_output_is_weighted_sum_of_partials_plus_gated_shared():
     e = r["ids"][4, 1]
     y, *_ = O.expert_ffn(128, 64, xq[4], xs[4], lw.gate_q8[e], lw.up_q8[e], lw.down_q8[e])
     assert np.array_equal(P[4, 1], y)
+
+
+@pytest.mark.parametrize("norm", [False, True])
+def test_layer_routing_follows_the_biased_logits(norm):
+    """The whole-layer loop routes each token by its biased fp32 logits: the
+    ids it reports are numpy's stable argsort of those logits (largest first,
+    lower id on ties) and its weights are scipy's softmax over all experts,
+    renormalised over the picks when norm_topk_prob is set.  Zipf-biased
+    router, so that dropping the bias changes the selection."""
+    shape, lw = mw.random_shape_case(5, d=128, E=32, k=4, F=32, Fs=32, norm=norm, zipf=1.1)
+    x = mw.make_tokens(105, 40, 128)
+    r = O.moe_tokens(lw, x)
+    logits = O.router_logits(x, lw.router_w, lw.router_bias)
+    ids = np.argsort(-logits, axis=1, kind="stable")[:, :4]
+    assert np.array_equal(r["ids"], ids)
+    p = scipy.special.softmax(logits.astype(np.float64), axis=1)
+    w = np.take_along_axis(p, ids, axis=1)
+    if norm:
+        w = w / w.sum(1, keepdims=True)
+    np.testing.assert_allclose(r["w"], w, rtol=1e-13, atol=0)
+    # the bias is load-bearing for this workload: without it the picks differ
+    unbiased = O.router_logits(x, lw.router_w)
+    assert not np.array_equal(np.argsort(-unbiased, axis=1, kind="stable")[:, :4], ids)
+    # the grouped evaluation routes the same way: its output is the per-token one
+    assert np.array_equal(O.moe_grouped(lw, x), r["out"])
 
 
 @pytest.mark.parametrize("case", [
