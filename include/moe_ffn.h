@@ -71,7 +71,9 @@ typedef enum moe_ffn_status {
   MOE_FFN_UNSUPPORTED = -2,        /* a shape outside the supported set */
   MOE_FFN_WORKSPACE_TOO_SMALL = -3,/* ws_bytes below moe_ffn_workspace_size(n_tokens) */
   MOE_FFN_OUT_OF_MEMORY = -4,      /* device allocation failed (weights create) */
-  MOE_FFN_HIP_ERROR = -5           /* a HIP runtime call or launch failed */
+  MOE_FFN_HIP_ERROR = -5,          /* a HIP runtime call or launch failed */
+  MOE_FFN_SCRATCH_TOO_SMALL = -6   /* moe_ffn_prefill_static: the batch needs more
+                                      than MOE_FFN_STATIC_SCRATCH_BYTES of workspace */
 } moe_ffn_status;
 
 /* Layer shape.  norm_topk_prob: #408 "Hypothesis" names it; OLMoE uses 0. */
@@ -179,6 +181,24 @@ int moe_ffn_prefill(const moe_ffn_weights* w, const float* x, int32_t n_tokens, 
 int moe_ffn_prefill_residual(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* h,
                              float* xn, float eps, void* ws, size_t ws_bytes,
                              const moe_ffn_routing* routing, hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation and results as moe_ffn_prefill, with the workspace taken from a
+ * static device array of MOE_FFN_STATIC_SCRATCH_BYTES inside the library
+ * instead of a caller buffer.  The call allocates nothing.  Every GPU the
+ * library runs on holds its own copy of the array until the process ends;
+ * all calls on one GPU share it, so calls that overlap in time on one GPU
+ * (other streams, other threads) race and must be serialised by the caller.
+ * A batch whose workspace (moe_ffn_workspace_size(n_tokens)) exceeds the
+ * array returns MOE_FFN_SCRATCH_TOO_SMALL before anything is enqueued: at
+ * the OLMoE-shaped layer (d 2048, 64 experts, top-8, ffn 1024) that is above
+ * 1527 tokens, at the 35B-A3B-shaped layer (256 experts, top-8, ffn 512 +
+ * shared 512) above 791.  x, out, routing and stream are those of
+ * moe_ffn_prefill. */
+#define MOE_FFN_STATIC_SCRATCH_BYTES (160u << 20)
+int moe_ffn_prefill_static(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* out,
+                           const moe_ffn_routing* routing, hipStream_t stream);
 
 /* moe_ffn_prefill with stage timing (#388 "Measurement discipline": per-phase
  * timing buckets measured warm, with setup excluded).  stage_events points to

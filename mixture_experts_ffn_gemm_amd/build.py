@@ -13,7 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_ffn.so")
-SOURCES = ["api.hip", "repack.hip", "router.hip", "bucket.hip", "gemm.hip", "decode.hip", "combine.hip"]
+SOURCES = ["api.hip", "repack.hip", "router.hip", "bucket.hip", "gemm.hip", "decode.hip", "combine.hip",
+           "noalloc.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", f"--offload-arch={ARCH}", "-fno-gpu-rdc",

@@ -603,6 +603,7 @@ const char* moe_ffn_status_str(int status) {
     case MOE_FFN_WORKSPACE_TOO_SMALL: return "workspace too small";
     case MOE_FFN_OUT_OF_MEMORY: return "out of device memory";
     case MOE_FFN_HIP_ERROR: return "HIP runtime error";
+    case MOE_FFN_SCRATCH_TOO_SMALL: return "batch exceeds the static scratch of moe_ffn_prefill_static";
     default: return "unknown status";
   }
 }
