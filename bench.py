@@ -151,24 +151,113 @@ def copy_calibration(mib, reps):
                                            "launches": reps}}), flush=True)
 
 
-def cpu_baseline(lw, x, target_s):
-    """The oracle on a bounded sample of the same batch: m token evaluations
-    (the batch's tokens in order, cycled when m exceeds a small batch)."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_pass(layers, x, toks, eps):
+    """The sampled tokens through the oracle's layers: one layer is the
+    per-token loop on x; a stack is h <- h + layer(RMSNorm(h)) per layer."""
+    import numpy as np
+    from oracle import oracle as O
+    if len(layers) == 1:
+        O.moe_tokens(layers[0], x, tokens=toks)
+        return
+    h = x[toks].astype(np.float32)
+    for lw in layers:
+        xn = O.rmsnorm(h, eps).astype(np.float32)
+        y = O.moe_tokens(lw, xn)["out"]
+        h = (h + y.astype(np.float32)).astype(np.float32)
+
+
+def cpu_baseline(layers, x, target_s, eps=1e-5):
+    """The oracle as it stands on a bounded sample of the same workload: m
+    tokens (the batch's first m, cycled when m exceeds a small batch) through
+    the layer or the whole stack, timed three times with every host thread and
+    three times with one; the median of each is reported."""
+    import statistics
     from oracle import oracle as O
     n = x.shape[0]
-    probe = [i % n for i in range(8)]
-    t0 = time.perf_counter()
-    O.moe_tokens(lw, x, tokens=probe)
-    per = (time.perf_counter() - t0) / len(probe)
-    m = int(max(8, min(max(n, 8), target_s / max(per, 1e-9))))
-    toks = [i % n for i in range(m)]
-    t0 = time.perf_counter()
-    O.moe_tokens(lw, x, tokens=toks)
-    dt = time.perf_counter() - t0
-    what = f"first {m} of the {n} tokens" if m <= n else f"{m} evaluations cycling the batch's {n} tokens"
-    return {"value": m / dt, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
-            "sample": f"{what} of the same layer (per-token oracle loop, "
-                      f"router + top-k + quantiser + k experts + combine), {dt:.1f} s wall"}
+    threads = O.num_threads()
+
+    def timed(m):
+        toks = [i % n for i in range(m)]
+        t0 = time.perf_counter()
+        _oracle_pass(layers, x, toks, eps)
+        return time.perf_counter() - t0
+
+    res = {}
+    for label, nthr, share, probe in (("all", threads, 0.6, 2 * threads), ("single", 1, 0.4, 2)):
+        O.set_num_threads(nthr)
+        per = timed(probe) / probe   # seconds per token at this thread count
+        m = int(max(probe, min(max(n, probe), share * target_s / 3 / max(per, 1e-9))))
+        rates = [m / timed(m) for _ in range(3)]
+        res[label] = (statistics.median(rates), rates, m, nthr)
+    O.set_num_threads(threads)
+    v, rates, m, nthr = res["all"]
+    v1, rates1, m1, _ = res["single"]
+    what = "one layer (per-token loop: router + top-k + quantiser + k experts + combine)" if len(layers) == 1 \
+        else f"the whole {len(layers)}-layer stack (per layer: RMSNorm, per-token layer loop, residual add)"
+    return {"value": v, "unit": "tokens/s", "cores": nthr, "kind": "oracle",
+            "sample": f"{m} of the batch's {n} tokens through {what}; median of 3 runs "
+                      f"({', '.join('%.1f' % r for r in rates)} tokens/s)",
+            "cpu_model": cpu_model(),
+            "single_thread": {"value": v1, "unit": "tokens/s", "cores": 1,
+                              "sample": f"{m1} tokens, median of 3 runs "
+                                        f"({', '.join('%.2f' % r for r in rates1)} tokens/s)"}}
+
+
+def measured_peaks(stream):
+    """The int8 matrix-core rate and HBM streaming rate of this GPU, measured
+    with the calibration kernels of libmoe_probe.so (timed with HIP events on
+    the launch stream): the ceilings next to the datasheet peaks."""
+    import torch
+    from mixture_experts_ffn_gemm_amd import build as hb
+    P = C.CDLL(hb.PROBE_LIB)
+    P.moe_probe_int8_mfma.argtypes = [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]
+    P.moe_probe_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+    dev = torch.cuda.current_device()
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    st = stream.cuda_stream
+
+    def time_launches(fn, reps=5):
+        for _ in range(2):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    wgs, iters = 2 * n_cu, 4096  # two workgroups of 4 wavefronts per CU: 2 wavefronts per SIMD
+    sink = torch.empty(wgs * 256, dtype=torch.int32, device="cuda")
+
+    def mfma():
+        if P.moe_probe_int8_mfma(iters, wgs, sink.data_ptr(), st) != 0:
+            raise RuntimeError("moe_probe_int8_mfma failed")
+    ms = time_launches(mfma)
+    tops = wgs * 4 * iters * 4 * 65536 / (ms * 1e-3) / 1e12
+    nbytes = 1 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+
+    def copy():
+        if P.moe_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, st) != 0:
+            raise RuntimeError("moe_probe_copy failed")
+    ms_c = time_launches(copy)
+    gbs = 2 * nbytes / (ms_c * 1e-3) / 1e9
+    del src, dst
+    return {"int8_mfma_TOPs": round(tops, 1), "copy_GBps": round(gbs, 1),
+            "how": f"int8: {wgs} workgroups x 4 wavefronts x {iters} x 4 independent v_mfma_i32_32x32x32_i8, "
+                   f"{ms:.3f} ms; copy: 1 GiB read + 1 GiB written with 16-byte loads/stores, {ms_c:.3f} ms"}
 
 
 def main():
@@ -184,7 +273,7 @@ def main():
     ap.add_argument("--decode-launch", choices=("eager", "graph"), default="eager",
                     help="decode workloads: call moe_ffn_decode directly, or replay one HIP graph of a call "
                          "per timed step")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="wall-time budget of the CPU oracle sample (0 disables it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain MIB-MiB streaming kernel (counter calibration)")
@@ -370,13 +459,17 @@ def main():
     stages["down"]["int8_TOPs"] = round(dn_ops / (dn_us * 1e-6) / 1e12, 1)
     gemm_frac = (gu_ops + dn_ops) / ((gu_us + dn_us) * 1e-6) / 1e12 / INT8_PEAK_TOPS
 
+    log("[bench] measuring the int8 MFMA and copy ceilings")
+    peaks = measured_peaks(stream)
+    peak_key = "copy_GBps" if roofline["unit"] == "GB/s" else "int8_mfma_TOPs"
+    roofline["measured_peak"] = peaks[peak_key]
+    roofline["frac_of_measured_peak"] = round(roofline["achieved"] / peaks[peak_key], 4)
+
     cpu = None
     if args.cpu_seconds > 0:
         log("[bench] timing the CPU oracle sample")
-        cpu = cpu_baseline(lw, x.cpu().numpy() if n_layers > 1 else x_np, args.cpu_seconds)
-        if n_layers > 1:  # the oracle's per-layer rate over the stack's depth
-            cpu["value"] /= n_layers
-            cpu["sample"] += f"; one layer of the {n_layers}, rate divided by {n_layers}"
+        layers_cpu = [lw] + [mw.workload_layer(args.workload, layer=li) for li in range(1, n_layers)]
+        cpu = cpu_baseline(layers_cpu, h0.cpu().numpy() if n_layers > 1 else x_np, args.cpu_seconds, eps)
 
     res = {
         "metric": METRIC, "value": round(n / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
@@ -388,7 +481,7 @@ def main():
         "grouped_gemm_int8_frac": round(gemm_frac, 4),
         "launch": ("graph replay" if graph is not None else "eager calls"),
         "experts_touched": int((counts[:s.n_experts] > 0).sum()),
-        "stages": stages, "roofline": roofline, "cpu_baseline": cpu,
+        "stages": stages, "roofline": roofline, "measured_peaks": peaks, "cpu_baseline": cpu,
     }
     if n_layers > 1:
         res["stack"] = {"layers": n_layers, "ms_per_layer": round(ms_step / n_layers, 5),

@@ -42,18 +42,28 @@ def _compile(src, obj, verbose):
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 6) -> str:
-    bdir = os.path.join(PKG, "_build")
-    os.makedirs(bdir, exist_ok=True)
-    objs = [os.path.join(bdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        list(ex.map(lambda p: _compile(p[0], p[1], verbose), zip(SOURCES, objs)))
-    tmp = LIB + ".tmp%d" % os.getpid()
+PROBE_LIB = os.path.join(PKG, "libmoe_probe.so")
+PROBE_SOURCES = ["probe.hip"]
+
+
+def _link(objs, out, verbose):
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, jobs: int = 6) -> str:
+    bdir = os.path.join(PKG, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    objs = [os.path.join(bdir, os.path.splitext(s)[0] + ".o") for s in srcs]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        list(ex.map(lambda p: _compile(p[0], p[1], verbose), zip(srcs, objs)))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], PROBE_LIB, verbose)
     return LIB
 
 

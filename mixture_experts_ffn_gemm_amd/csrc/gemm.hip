@@ -295,7 +295,7 @@ struct Ctx {
 // and block; the conversion runs on the matrix pipe, and the result is the
 // same as fma(float(C), S, acc).
 __device__ __forceinline__ void compute_block(const Ops& o, const GuScales& sc, int b, const Ops& on,
-                                              const GuScales& sn, int bn, const Ctx& cx, int,
+                                              const GuScales& sn, int bn, bool, const Ctx& cx, int,
                                               v16i& dn, v16f& cf, v16f& s, v16f (&acc)[4]) {
   const v16f zf = {0};
   v4h sav = sa_slot(sc.sa, b);
@@ -330,11 +330,11 @@ __device__ __forceinline__ void compute_block(const Ops& o, const GuScales& sc, 
 
 // One block of the down pipeline.  Per tile t: int8 MFMA(t+1) from the 1.5f
 // bias, half of acc(t) = fma(D(t), S(t), acc(t)), scale MFMA(t+1), the other
-// half; after the k-step's last block the correction MFMA subtracts its
-// 1.5 * S terms from acc(t).
+// half; after the wavefront's last block of the k-step (corr) the correction
+// MFMA subtracts the 1.5 * S terms of the k-step's blocks it computed.
 __device__ __forceinline__ void compute_block(const Ops& o, const DnScales& sc, int b, const Ops& on,
-                                              const DnScales& sn, int bn, const Ctx& cx, int lane,
-                                              v16i& c, v16f&, v16f& s, v16f (&acc)[4]) {
+                                              const DnScales& sn, int bn, bool corr, const Ctx& cx,
+                                              int lane, v16i& c, v16f&, v16f& s, v16f (&acc)[4]) {
   const v16f zf = {0};
   v4h sav = dn_sa_slot(sc.q, b, lane);
   v4h savn = dn_sa_slot(sn.q, bn, lane);
@@ -358,7 +358,7 @@ __device__ __forceinline__ void compute_block(const Ops& o, const DnScales& sc, 
 #pragma unroll
     for (int v = 8; v < 16; ++v) acc[t][v] = __builtin_fmaf(d[v], s[v], acc[t][v]);
     anchor(acc[t]);
-    if (b == KSTEP - 1) {
+    if (corr) {
       acc[t] = __builtin_amdgcn_mfma_f32_32x32x8f16(cx.corr, as_v4h(sc.wb[t]), acc[t], 0, 0, 0);
       anchor(acc[t]);
     }
@@ -385,11 +385,11 @@ __device__ __forceinline__ void kstep(const Src& src, int j, int KS, int wave, i
   if (j >= 1 && j + 1 < KS) issue_acts<GATEUP>(src, j + 1, nxt_lds, wave, lane);
   if constexpr (!GATEUP) cx.corr = dn_corr_a(sc.q);
   read_block<GATEUP>(cur, 1, wave, lane, Y);
-  compute_block(X, sc, 0, Y, sc, 1, cx, lane, c, cf, s, acc);
+  compute_block(X, sc, 0, Y, sc, 1, false, cx, lane, c, cf, s, acc);
   read_block<GATEUP>(cur, 2, wave, lane, X);
-  compute_block(Y, sc, 1, X, sc, 2, cx, lane, c, cf, s, acc);
+  compute_block(Y, sc, 1, X, sc, 2, false, cx, lane, c, cf, s, acc);
   read_block<GATEUP>(cur, 3, wave, lane, Y);
-  compute_block(X, sc, 2, Y, sc, 3, cx, lane, c, cf, s, acc);
+  compute_block(X, sc, 2, Y, sc, 3, false, cx, lane, c, cf, s, acc);
   if (j + 1 < KS) {
     // k-step j+1 has landed for every wavefront, and every wavefront has read
     // all of k-step j: its buffer takes k-step j+2.
@@ -398,7 +398,85 @@ __device__ __forceinline__ void kstep(const Src& src, int j, int KS, int wave, i
   }
   read_block<GATEUP>(nxt, 0, wave, lane, X);
   read_scales(nxt, wave, lane, sn);
-  compute_block(Y, sc, 3, X, sn, 0, cx, lane, c, cf, s, acc);
+  compute_block(Y, sc, 3, X, sn, 0, true, cx, lane, c, cf, s, acc);
+}
+
+// Split-K: the correction operand of the blocks a split wavefront computes
+// (S = 4: block si; S = 2: blocks si and si + 2).  Lane half h holds the
+// slots of blocks 2h and 2h + 1; the slots of blocks left to other
+// wavefronts are zeroed, so their (never added) 1.5 * S terms are not
+// subtracted either.
+template <int S>
+__device__ __forceinline__ v4h dn_corr_split(uint32_t q, int lane, int si) {
+  const int h = lane >> 5;
+  const bool keep_lo = (S == 4) ? (2 * h == si) : (si == 0);
+  const bool keep_hi = (S == 4) ? (2 * h + 1 == si) : (si == 1);
+  return dn_corr_a(q & ((keep_lo ? 0x0000ffffu : 0u) | (keep_hi ? 0xffff0000u : 0u)));
+}
+
+// K-step j of a split-K wavefront (SharpInference #406 "References": the
+// split-K int8 GEMM follow-up).  A tile whose rows fill only one (S = 4) or
+// two (S = 2) of the four 32-row wavefront slots would leave the other
+// wavefronts idle; instead the S wavefronts of each row group share its
+// blocks: wavefront si computes blocks b = si (mod S) of every k-step into
+// its own partial accumulators, which the kernel sums in a fixed order at the
+// end.  Copies, barriers and their placement are those of kstep (every
+// wavefront meets the same barriers and issues the same copies; each copies
+// its row group's activation slab into its own LDS area).  On entry X holds
+// block si of k-step j; on exit the same for k-step j+1.
+template <bool GATEUP, int S>
+__device__ __forceinline__ void kstep_split(const Src& src, int j, int KS, int wave, int lane, int si,
+                                            const char* cur, const char* nxt, uint32_t cur_lds,
+                                            uint32_t nxt_lds, Ops& X, Ops& Y, const ScalesT<GATEUP>& sc,
+                                            ScalesT<GATEUP>& sn, Ctx& cx, v16i& c, v16f& cf, v16f& s,
+                                            v16f (&acc)[4]) {
+  static_assert(S == 2 || S == 4, "split factors");
+  if (j >= 1 && j + 1 < KS) issue_acts<GATEUP>(src, j + 1, nxt_lds, wave, lane);
+  if constexpr (!GATEUP) cx.corr = dn_corr_split<S>(sc.q, lane, si);
+  if constexpr (S == 2) {
+    read_block<GATEUP>(cur, si + 2, wave, lane, Y);
+    compute_block(X, sc, si, Y, sc, si + 2, false, cx, lane, c, cf, s, acc);
+  }
+  if (j + 1 < KS) {
+    wait_copies_barrier_0();
+    if (j + 2 < KS) issue_weights<GATEUP>(src, j + 2, cur_lds, wave);
+  }
+  if constexpr (S == 2) {
+    read_block<GATEUP>(nxt, si, wave, lane, X);
+    read_scales(nxt, wave, lane, sn);
+    compute_block(Y, sc, si + 2, X, sn, si, true, cx, lane, c, cf, s, acc);
+  } else {
+    read_block<GATEUP>(nxt, si, wave, lane, Y);
+    read_scales(nxt, wave, lane, sn);
+    compute_block(X, sc, si, Y, sn, si, true, cx, lane, c, cf, s, acc);
+    X = Y;
+  }
+}
+
+// The partial accumulators of a split row group, summed into its first
+// wavefront (si = 0) in the fixed order ((p0 + p1) + p2) + p3 through the
+// (then idle) stage buffers.  Every wavefront of the workgroup calls this.
+__device__ __forceinline__ void split_reduce(char* lds, int S, int rg, int si, int lane, v16f (&acc)[4]) {
+  __syncthreads();  // every wavefront is out of the k loop: the stage buffers are free
+  float* red = reinterpret_cast<float*>(lds);
+  if (si > 0) {
+    float* dst = red + (size_t)(rg * (S - 1) + si - 1) * 64 * 64;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) dst[(t * 16 + v) * 64 + lane] = acc[t][v];
+  }
+  __syncthreads();
+  if (si == 0) {
+    for (int p = 1; p < S; ++p) {
+      const float* src = red + (size_t)(rg * (S - 1) + p - 1) * 64 * 64;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[t][v] = acc[t][v] + src[(t * 16 + v) * 64 + lane];
+    }
+  }
+  __syncthreads();  // the reduction buffers are read before any epilogue reuses the LDS
 }
 
 // Grouped GEMM.  GATEUP: A = the int8 token rows of the tile's (token, slot)
@@ -407,39 +485,20 @@ __device__ __forceinline__ void kstep(const Src& src, int j, int KS, int wave, i
 // requantised per 32 into the down GEMM's A-operand chunks.  !GATEUP: A = those
 // chunks, B = a 128-column strip of the down matrix; epilogue scatters the fp32
 // rows to partial[token][slot] (the unweighted down-partials of #129 "Scope").
-template <bool GATEUP>
-__global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
-  using L = Lay<GATEUP>;
-  __shared__ __attribute__((aligned(1024))) char lds[2][L::STAGE];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n_tiles = min(a.tiles[0], a.tile_bound);
-  const int nstrips = GATEUP ? max(a.F_pad, a.Fs_pad) / GU_COLS : a.d_pad / DN_COLS;
-  if (n_tiles <= 0) return;
-  // The valid workgroups (n_tiles * nstrips <= gridDim.x) are spread evenly
-  // over the 8 XCDs, consecutive logical indices on the same XCD.
-  const int n_valid = n_tiles * nstrips;
-  const int per_xcd = (n_valid + 7) >> 3;
-  const int slot = (int)blockIdx.x >> 3;
-  if (slot >= per_xcd) return;
-  const int blk = ((int)blockIdx.x & 7) * per_xcd + slot;
-  if (blk >= n_valid) return;
-  const int T = blk / nstrips, cs = blk - (blk / nstrips) * nstrips;
-  const int32_t* ent = a.tiles + 4 + 3 * T;
-  const int g = ent[0], row0 = ent[1], row_end = ent[2];
-  if (g < 0 || g >= a.G || row0 < 0 || row_end <= row0 || row_end > a.p_total) return;
-  const bool shared = g >= a.E;
-  const int Fg_pad = shared ? a.Fs_pad : a.F_pad;
-  if (GATEUP && cs >= Fg_pad / GU_COLS) return;
-  const int KB = GATEUP ? a.d_pad / QB : Fg_pad / QB;
-  const int KS = KB / KSTEP;
-  const uint8_t* strip = GATEUP ? (shared ? a.sh_gu : a.gu + (size_t)g * a.gu_group)
-                                : (shared ? a.sh_dn : a.dn + (size_t)g * a.dn_group);
-  strip += (size_t)cs * KS * L::W_BYTES;
+// The work of one (tile, strip) workgroup with split factor S (1: one 32-row
+// row group per wavefront; 2, 4: see kstep_split).  Each split factor is a
+// separate, self-contained body (nothing it computes is live across the
+// others), so that each gets its own register allocation.
+template <bool GATEUP, int S>
+__device__ __forceinline__ void tile_work(const GemmArgs& a, char (&lds)[2][Lay<GATEUP>::STAGE], int lane,
+                                          int wave, int T, int cs, int g, int row0, int row_end, int KS,
+                                          const uint8_t* strip) {
 
-  const int wrow0 = row0 + MT_WAVE * wave;  // first CSR row of this wavefront
-  const bool active = wrow0 < row_end;      // wavefront-uniform
-  const int t32 = T * NWAVE + wave;         // 32-row tile index of the h chunks
+  using L = Lay<GATEUP>;
+  const int rg = wave / S, si = wave - rg * S;
+  const int wrow0 = row0 + MT_WAVE * rg;    // first CSR row of this wavefront's row group
+  const bool active = wrow0 < row_end;      // wavefront-uniform (every wavefront when S > 1)
+  const int t32 = T * NWAVE + rg;           // 32-row tile index of the A slab and the h chunks
   // A operand: this wavefront's run of 1 KiB chunks (one per 32-block) and
   // their scales, per 32-row quarter t32 of the tile.
   const int a_kb = GATEUP ? a.d_pad / QB : a.kbmax;
@@ -479,7 +538,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
     Ops X, Y;
     ScalesT<GATEUP> s0, s1;
     Ctx cx;
-    read_block<GATEUP>(lds[0], 0, wave, lane, X);
+    read_block<GATEUP>(lds[0], si, wave, lane, X);  // the wavefront's first block
     read_scales(lds[0], wave, lane, s0);
     const v16f zf = {0};
     v16i c;
@@ -497,21 +556,39 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
       const v16i d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(X.a, X.b[0], cx.magic, 0, 0, 0);
       c = __builtin_amdgcn_mfma_i32_32x32x32_i8(X.a, X.b[1], cx.magic, 0, 0, 0);
       cf = __builtin_amdgcn_mfma_f32_32x32x8f16(cx.sub_a, cx.sub_b, __builtin_bit_cast(v16f, d0), 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_32x32x8f16(sa_slot(s0.sa, 0), s0.sw[0], zf, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x8f16(sa_slot(s0.sa, si), s0.sw[0], zf, 0, 0, 0);
     } else {
 #pragma unroll
       for (int v = 0; v < 16; ++v) cx.magic[v] = 0x3fc00000;  // 1.5f
       anchor(cx.magic);
       c = __builtin_amdgcn_mfma_i32_32x32x32_i8(X.a, X.b[0], cx.magic, 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_32x32x8f16(dn_sa_slot(s0.q, 0, lane), as_v4h(s0.wb[0]), zf, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x8f16(dn_sa_slot(s0.q, si, lane), as_v4h(s0.wb[0]), zf, 0, 0, 0);
     }
     // Unrolled by two so that each buffer and scale set has a fixed role.
-    for (int j = 0; j < KS; j += 2) {
-      kstep<GATEUP>(src, j, KS, wave, lane, lds[0], lds[1], lds0, lds1, X, Y, s0, s1, cx, c, cf, s, acc);
-      if (j + 1 < KS)
-        kstep<GATEUP>(src, j + 1, KS, wave, lane, lds[1], lds[0], lds1, lds0, X, Y, s1, s0, cx, c, cf, s, acc);
+    if constexpr (S == 1) {
+      for (int j = 0; j < KS; j += 2) {
+        kstep<GATEUP>(src, j, KS, wave, lane, lds[0], lds[1], lds0, lds1, X, Y, s0, s1, cx, c, cf, s, acc);
+        if (j + 1 < KS)
+          kstep<GATEUP>(src, j + 1, KS, wave, lane, lds[1], lds[0], lds1, lds0, X, Y, s1, s0, cx, c, cf, s, acc);
+      }
+    } else if constexpr (S == 2) {
+      for (int j = 0; j < KS; j += 2) {
+        kstep_split<GATEUP, 2>(src, j, KS, wave, lane, si, lds[0], lds[1], lds0, lds1, X, Y, s0, s1, cx, c, cf,
+                               s, acc);
+        if (j + 1 < KS)
+          kstep_split<GATEUP, 2>(src, j + 1, KS, wave, lane, si, lds[1], lds[0], lds1, lds0, X, Y, s1, s0, cx, c,
+                                 cf, s, acc);
+      }
+    } else {
+      for (int j = 0; j < KS; j += 2) {
+        kstep_split<GATEUP, 4>(src, j, KS, wave, lane, si, lds[0], lds[1], lds0, lds1, X, Y, s0, s1, cx, c, cf,
+                               s, acc);
+        if (j + 1 < KS)
+          kstep_split<GATEUP, 4>(src, j + 1, KS, wave, lane, si, lds[1], lds[0], lds1, lds0, X, Y, s1, s0, cx, c,
+                                 cf, s, acc);
+      }
     }
-  } else {
+  } else if constexpr (S == 1) {
     // A wavefront past the tile's rows computes nothing but still does its
     // share of the copies and meets every barrier.
     for (int j = 0; j + 1 < KS; ++j) {
@@ -521,9 +598,13 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
     }
   }
   // gate/up: every wavefront is out of the k loop, so LDS is free for the
-  // epilogue (the down epilogue uses no LDS)
-  if (GATEUP) __syncthreads();
-  if (!active) return;
+  // epilogue (the down epilogue uses no LDS).  Split-K: the row group's
+  // partial sums meet in its first wavefront, which alone runs the epilogue.
+  if constexpr (S > 1)
+    split_reduce(&lds[0][0], S, rg, si, lane, acc);
+  else if (GATEUP)
+    __syncthreads();
+  if (!active || si != 0) return;
 
   if (GATEUP) {
     // h = silu(gate) * up for the wavefront's 32 rows x 64 columns, transposed
@@ -609,6 +690,48 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
       }
     }
   }
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
+  using L = Lay<GATEUP>;
+  __shared__ __attribute__((aligned(1024))) char lds[2][L::STAGE];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_tiles = min(a.tiles[0], a.tile_bound);
+  const int nstrips = GATEUP ? max(a.F_pad, a.Fs_pad) / GU_COLS : a.d_pad / DN_COLS;
+  if (n_tiles <= 0) return;
+  // The valid workgroups (n_tiles * nstrips <= gridDim.x) are spread evenly
+  // over the 8 XCDs, consecutive logical indices on the same XCD.
+  const int n_valid = n_tiles * nstrips;
+  const int per_xcd = (n_valid + 7) >> 3;
+  const int slot = (int)blockIdx.x >> 3;
+  if (slot >= per_xcd) return;
+  const int blk = ((int)blockIdx.x & 7) * per_xcd + slot;
+  if (blk >= n_valid) return;
+  const int T = blk / nstrips, cs = blk - (blk / nstrips) * nstrips;
+  const int32_t* ent = a.tiles + 4 + 3 * T;
+  const int g = ent[0], row0 = ent[1], row_end = ent[2];
+  if (g < 0 || g >= a.G || row0 < 0 || row_end <= row0 || row_end > a.p_total) return;
+  const bool shared = g >= a.E;
+  const int Fg_pad = shared ? a.Fs_pad : a.F_pad;
+  if (GATEUP && cs >= Fg_pad / GU_COLS) return;
+  const int KB = GATEUP ? a.d_pad / QB : Fg_pad / QB;
+  const int KS = KB / KSTEP;
+  const uint8_t* strip = GATEUP ? (shared ? a.sh_gu : a.gu + (size_t)g * a.gu_group)
+                                : (shared ? a.sh_dn : a.dn + (size_t)g * a.dn_group);
+  strip += (size_t)cs * KS * L::W_BYTES;
+
+  // Split-K: when the tile's rows fill only one (or two) of the four 32-row
+  // wavefront slots, the wavefronts of each row group share its blocks (see
+  // kstep_split).
+  const int nact = (min(row_end - row0, MT_WG) + MT_WAVE - 1) / MT_WAVE;
+  if (nact >= 3)
+    tile_work<GATEUP, 1>(a, lds, lane, wave, T, cs, g, row0, row_end, KS, strip);
+  else if (nact == 2)
+    tile_work<GATEUP, 2>(a, lds, lane, wave, T, cs, g, row0, row_end, KS, strip);
+  else
+    tile_work<GATEUP, 4>(a, lds, lane, wave, T, cs, g, row0, row_end, KS, strip);
 }
 
 int grid_for(long wgs) { return (int)((wgs + 7) / 8 * 8); }

@@ -439,3 +439,7 @@ void ora_rmsnorm(const float* x, int32_t n, int32_t d, double eps, double* out) 
 }
 
 int32_t ora_num_threads(void) { return (int32_t)omp_get_max_threads(); }
+
+void ora_set_num_threads(int32_t n) {
+  if (n >= 1) omp_set_num_threads(n);
+}

@@ -132,6 +132,9 @@ void ora_combine_f32(const float* partial, const float* w, const float* gs, int3
 
 /* Number of OpenMP threads the parallel loops above use. */
 int32_t ora_num_threads(void);
+/* Set the number of host threads later calls use (timing only; no effect on
+ * any result: every token is evaluated by one thread). */
+void ora_set_num_threads(int32_t n);
 
 /* RMSNorm with unit gain in fp64: x / sqrt(mean(x^2) + eps). */
 void ora_rmsnorm(const float* x, int32_t n, int32_t d, double eps, double* out);

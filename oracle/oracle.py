@@ -51,6 +51,7 @@ def lib():
             "ora_combine_f32": (None, [vp, vp, vp, i32, i32, i32, i32, vp]),
             "ora_rmsnorm": (None, [vp, i32, i32, dbl, vp]),
             "ora_num_threads": (i32, []),
+            "ora_set_num_threads": (None, [i32]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -258,3 +259,7 @@ def routing(lw, x):
 
 def num_threads() -> int:
     return int(lib().ora_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    lib().ora_set_num_threads(int(n))

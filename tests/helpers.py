@@ -20,7 +20,7 @@ def moe_close(got, ref, rel_l2=REL_L2_TOL, elem=ELEM_TOL):
     return r, e
 
 
-def public_header_symbols(path):
+def public_header_symbols(path, prefix="moe_ffn_"):
     import re
     txt = open(path).read()
-    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(moe_ffn_\w+)\s*\(", txt, re.M)))
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(" + prefix + r"\w+)\s*\(", txt, re.M)))

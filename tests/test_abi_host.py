@@ -123,3 +123,23 @@ def test_workspace_size_for_dims_validates(B):
     dm = B.moe_ffn_dims(128, 8, 2, 256, 0, 0)
     assert L.moe_ffn_workspace_size_for_dims(C.byref(dm), -1, C.byref(n)) == -1
     assert L.moe_ffn_workspace_size_for_dims(C.byref(dm), 16, None) == -1
+
+
+def test_probe_library_exports_its_header_and_validates(B):
+    """libmoe_probe.so (the calibration kernels of the benchmark) exports what
+    include/moe_probe.h declares and rejects bad arguments on the host."""
+    from mixture_experts_ffn_gemm_amd import build
+    syms = public_header_symbols(os.path.join(ROOT, "include", "moe_probe.h"), prefix="moe_probe_")
+    assert syms == ["moe_probe_copy", "moe_probe_int8_mfma"]
+    P = C.CDLL(build.PROBE_LIB)
+    for s in syms:
+        assert hasattr(P, s), s
+    P.moe_probe_int8_mfma.argtypes = [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]
+    P.moe_probe_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+    assert P.moe_probe_int8_mfma(0, 4, 64, None) == -1
+    assert P.moe_probe_int8_mfma(10, 0, 64, None) == -1
+    assert P.moe_probe_int8_mfma(10, 4, None, None) == -1
+    assert P.moe_probe_copy(None, 64, 64, None) == -1
+    assert P.moe_probe_copy(64, 128, 24, None) == -1      # not a multiple of 16
+    assert P.moe_probe_copy(64, 96, 64, None) == -1       # overlapping
+    assert P.moe_probe_copy(64, 4096, 0, None) == 0       # nothing to do
