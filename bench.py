@@ -273,6 +273,10 @@ def main():
     ap.add_argument("--decode-launch", choices=("eager", "graph"), default="eager",
                     help="decode workloads: call moe_ffn_decode directly, or replay one HIP graph of a call "
                          "per timed step")
+    ap.add_argument("--chunk", type=int, default=0, metavar="TOKENS",
+                    help="prefill workloads: time moe_ffn_prefill_chunked with chunks of TOKENS tokens "
+                         "(stages and roofline then describe one chunk-sized call)")
+    ap.add_argument("--chunk-order", choices=("forward", "serpentine"), default="serpentine")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="wall-time budget of the CPU oracle sample (0 disables it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -325,6 +329,7 @@ def main():
         B.moe_ffn_residual_rmsnorm(h0, None, x, n, s.d, eps, stream)
     out = torch.empty((n, s.d), dtype=torch.float32, device=dev)
     ws = layer.workspace(n)
+    chunk = args.chunk if (args.chunk and not decode and n_layers == 1) else 0
 
     def stack_pass(st=stream):
         h.copy_(h0)
@@ -337,6 +342,11 @@ def main():
                 B.moe_ffn_prefill_residual(lay.handle, x, n, h, x, eps, ws, ws.numel(), None, st)
     exp_start = torch.empty(s.n_experts + 1 + (1 if s.shared_ffn else 0), dtype=torch.int32, device=dev)
     step_fn = B.moe_ffn_decode if decode else B.moe_ffn_prefill
+    if chunk:
+        flags = B.CHUNK_SERPENTINE if args.chunk_order == "serpentine" else 0
+
+        def step_fn(h, xx, nn, oo, w_, wb, r, st):  # the whole batch, chunk by chunk
+            B.moe_ffn_prefill_chunked(h, xx, nn, chunk, flags, oo, w_, wb, st)
     step_fn(layer.handle, x, n, out, ws, ws.numel(), B.make_routing(exp_start=exp_start), stream)
     for _ in range(args.warmup):
         step_fn(layer.handle, x, n, out, ws, ws.numel(), None, stream)
@@ -403,8 +413,9 @@ def main():
     else:
         n_ev, stage_names, prof_fn = B.N_STAGE_EVENTS, B.STAGES, B.moe_ffn_prefill_profiled
     evs = [hip.create(n_ev) for _ in range(args.steps)]
+    n_prof = min(n, chunk) if chunk else n   # a chunked run profiles one chunk-sized call
     for i in range(args.steps):
-        prof_fn(layer.handle, x, n, out, ws, ws.numel(), evs[i], None, stream)
+        prof_fn(layer.handle, x, n_prof, out, ws, ws.numel(), evs[i], None, stream)
     torch.cuda.synchronize()
     stage_ms = {name: 0.0 for name in stage_names}
     for i in range(args.steps):
@@ -413,8 +424,12 @@ def main():
     for e in evs:
         hip.destroy(e)
 
-    gu_ops, dn_ops = gemm_ops(s, n)
-    sb = stage_bytes(s, n, counts)
+    if chunk:  # the routing of the profiled chunk
+        B.moe_ffn_prefill(layer.handle, x, n_prof, out, ws, ws.numel(), B.make_routing(exp_start=exp_start), stream)
+        torch.cuda.synchronize()
+        counts = np.diff(exp_start.cpu().numpy())
+    gu_ops, dn_ops = gemm_ops(s, n_prof)
+    sb = stage_bytes(s, n_prof, counts)
     if decode:
         # decode stages: the router launch also quantises; the gate/up launch
         # also routes
@@ -442,7 +457,8 @@ def main():
         roofline = {"bound": "mfma", "kernel": "grouped_gemm_kernel<true> (grouped gate/up + SwiGLU + requantise)",
                     "achieved": round(gu_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
                     "frac": round(gu_tops / INT8_PEAK_TOPS, 4),
-                    "traffic": read_traffic("gateup_olmoe_n2048") if args.workload == "olmoe_n2048" else None,
+                    "traffic": (read_traffic("gateup_olmoe_n2048")
+                                if args.workload == "olmoe_n2048" and not chunk else None),
                     "algorithmic_ops_per_launch": gu_ops, "avg_launch_us": round(gu_us, 2),
                     "pipe_roof": {"peak": round(PIPE_ROOF_TOPS, 1), "unit": "TOP/s",
                                   "frac": round(gu_tops / PIPE_ROOF_TOPS, 4),
@@ -483,6 +499,10 @@ def main():
         "experts_touched": int((counts[:s.n_experts] > 0).sum()),
         "stages": stages, "roofline": roofline, "measured_peaks": peaks, "cpu_baseline": cpu,
     }
+    if chunk:
+        res["chunked"] = {"chunk_tokens": chunk, "order": args.chunk_order, "chunks": (n + chunk - 1) // chunk,
+                          "entry_point": "moe_ffn_prefill_chunked",
+                          "stages_and_roofline": f"one {n_prof}-token call (the first chunk)"}
     if n_layers > 1:
         res["stack"] = {"layers": n_layers, "ms_per_layer": round(ms_step / n_layers, 5),
                         "step": "h = h0; xn = RMSNorm(h); per layer: y = MoE(xn), h += y, xn = RMSNorm(h)",

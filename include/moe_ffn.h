@@ -200,6 +200,30 @@ int moe_ffn_prefill_residual(const moe_ffn_weights* w, const float* x, int32_t n
 int moe_ffn_prefill_static(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* out,
                            const moe_ffn_routing* routing, hipStream_t stream);
 
+/* Chunked prefill (#388, second comment, "Prefill chunking": a long prompt
+ * processed as consecutive micro-batches of a fixed size, 512 by default in
+ * the pages' engines; the pages' idea is to upload each layer's experts once
+ * per prompt across chunks).  Here every expert stays resident in HBM, and
+ * what consecutive chunks can share is the GPU's 256 MB last-level cache
+ * (MALL): the call runs moe_ffn_prefill over tokens [c0, c0 + chunk_tokens)
+ * for c0 = 0, chunk_tokens, ... (the last chunk may be shorter), one after
+ * another on `stream`, reusing one workspace.  With flags &
+ * MOE_FFN_CHUNK_SERPENTINE, every second chunk walks its grouped GEMMs' tile
+ * table from the last tile (experts in descending order), so that each chunk
+ * starts on the experts whose weights the previous one streamed last.
+ * Each token's routing and output are those of its own chunk's call, which
+ * routes every token exactly as an unchunked call does (token-separable
+ * routing); outputs agree with moe_ffn_prefill's to the fp32 output bar
+ * (accumulation order inside a grouped GEMM tile depends on how many rows
+ * share the tile).  ws_bytes >= moe_ffn_workspace_size(min(chunk_tokens,
+ * n_tokens)).  x and out as for moe_ffn_prefill (whole batch); chunk_tokens
+ * >= 1; unknown flag bits are MOE_FFN_INVALID_ARG.  Every check is made
+ * before the first chunk is enqueued. */
+#define MOE_FFN_CHUNK_SERPENTINE 1
+int moe_ffn_prefill_chunked(const moe_ffn_weights* w, const float* x, int32_t n_tokens,
+                            int32_t chunk_tokens, int32_t flags, float* out, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
 /* moe_ffn_prefill with stage timing (#388 "Measurement discipline": per-phase
  * timing buckets measured warm, with setup excluded).  stage_events points to
  * MOE_FFN_N_STAGE_EVENTS caller-created hipEvent_t handles (host array); event

@@ -25,7 +25,7 @@ MOE_FFN_HIP_ERROR = -5
 MOE_FFN_SCRATCH_TOO_SMALL = -6
 
 EXPORTED = ("moe_ffn_weights_create", "moe_ffn_weights_destroy", "moe_ffn_weights_dims",
-            "moe_ffn_workspace_size", "moe_ffn_workspace_size_for_dims", "moe_ffn_prefill", "moe_ffn_prefill_static", "moe_ffn_prefill_residual", "moe_ffn_prefill_profiled",
+            "moe_ffn_workspace_size", "moe_ffn_workspace_size_for_dims", "moe_ffn_prefill", "moe_ffn_prefill_static", "moe_ffn_prefill_chunked", "moe_ffn_prefill_residual", "moe_ffn_prefill_profiled",
             "moe_ffn_decode",
             "moe_ffn_decode_profiled", "moe_ffn_combine",
             "moe_ffn_quantize", "moe_ffn_residual_rmsnorm", "moe_ffn_dbg_block_sums", "moe_ffn_status_str")
@@ -69,6 +69,7 @@ def lib():
             "moe_ffn_workspace_size_for_dims": [C.POINTER(moe_ffn_dims), i32, C.POINTER(sz)],
             "moe_ffn_prefill": [vp, vp, i32, vp, vp, sz, C.POINTER(moe_ffn_routing), vp],
             "moe_ffn_prefill_static": [vp, vp, i32, vp, C.POINTER(moe_ffn_routing), vp],
+            "moe_ffn_prefill_chunked": [vp, vp, i32, i32, i32, vp, vp, sz, vp],
             "moe_ffn_prefill_residual": [vp, vp, i32, vp, vp, C.c_float, vp, sz, C.POINTER(moe_ffn_routing), vp],
             "moe_ffn_decode": [vp, vp, i32, vp, vp, sz, C.POINTER(moe_ffn_routing), vp],
             "moe_ffn_prefill_profiled": [vp, vp, i32, vp, vp, sz, C.POINTER(moe_ffn_routing), vp,
@@ -166,6 +167,17 @@ def moe_ffn_prefill(handle: int, x, n_tokens: int, out, ws, ws_bytes: int,
     rc = lib().moe_ffn_prefill(handle, _ptr(x), int(n_tokens), _ptr(out), _ptr(ws), int(ws_bytes),
                                C.byref(routing) if routing is not None else None, _stream(stream))
     _check("moe_ffn_prefill", rc)
+
+
+CHUNK_SERPENTINE = 1
+
+
+def moe_ffn_prefill_chunked(handle: int, x, n_tokens: int, chunk_tokens: int, flags: int, out, ws, ws_bytes: int,
+                            stream=None) -> None:
+    """The layer over consecutive chunks of chunk_tokens tokens on one workspace."""
+    rc = lib().moe_ffn_prefill_chunked(handle, _ptr(x), int(n_tokens), int(chunk_tokens), int(flags), _ptr(out),
+                                       _ptr(ws), int(ws_bytes), _stream(stream))
+    _check("moe_ffn_prefill_chunked", rc)
 
 
 STATIC_SCRATCH_BYTES = 160 << 20

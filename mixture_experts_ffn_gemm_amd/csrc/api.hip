@@ -195,7 +195,7 @@ struct ResidualOut {
 
 int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, void* ws,
               size_t ws_bytes, const moe_ffn_routing* r, hipStream_t s, hipEvent_t* ev = nullptr,
-              const ResidualOut* res = nullptr) {
+              const ResidualOut* res = nullptr, int reverse_tiles = 0) {
   if (!W || n < 0 || n > MAX_TOKENS) return MOE_FFN_INVALID_ARG;
   if (n == 0) return current_device_matches(W);  // no-op; buffers may be NULL
   if (!x || !ws || (!res && !out)) return MOE_FFN_INVALID_ARG;
@@ -255,7 +255,8 @@ int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, v
                                  tiles, L.tile_bound, x, dm.d, dm.d_pad, gq, gqs,
                                  dm.has_shared ? W->sh_gate_vec : nullptr, gs, r ? r->xq : nullptr,
                                  r ? r->xs : nullptr, s));
-  const GemmArgs a = gemm_args(W, L, base, n);
+  GemmArgs a = gemm_args(W, L, base, n);
+  a.reverse = reverse_tiles;
   HIP_TRY(mark(3));
   HIP_TRY(launch_gateup(a, s));
   HIP_TRY(mark(4));
@@ -502,6 +503,32 @@ int moe_ffn_workspace_size_for_dims(const moe_ffn_dims* dims, int32_t max_tokens
 int moe_ffn_prefill(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* out,
                     void* ws, size_t ws_bytes, const moe_ffn_routing* routing, hipStream_t stream) {
   return run_layer(w, x, n_tokens, out, ws, ws_bytes, routing, stream);
+}
+
+int moe_ffn_prefill_chunked(const moe_ffn_weights* w, const float* x, int32_t n_tokens,
+                            int32_t chunk_tokens, int32_t flags, float* out, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  if (!w || n_tokens < 0 || n_tokens > MAX_TOKENS || chunk_tokens < 1 || (flags & ~MOE_FFN_CHUNK_SERPENTINE))
+    return MOE_FFN_INVALID_ARG;
+  if (n_tokens == 0) return current_device_matches(w);
+  if (!x || !out || !ws) return MOE_FFN_INVALID_ARG;
+  // Every chunk's checks, done once before anything is enqueued: the
+  // workspace covers the largest chunk, and the whole of x and out.
+  const int32_t m0 = std::min(chunk_tokens, n_tokens);
+  if (ws_bytes < ws_layout(w->dm, m0).total) return MOE_FFN_WORKSPACE_TOO_SMALL;
+  if (((uintptr_t)ws & 255u) || ((uintptr_t)x & 15u) || ((uintptr_t)out & 15u)) return MOE_FFN_INVALID_ARG;
+  const size_t xb = (size_t)n_tokens * w->dm.d * sizeof(float);
+  if (overlaps(x, xb, out, xb) || overlaps(out, xb, ws, ws_bytes)) return MOE_FFN_INVALID_ARG;
+  const int dev_ok = current_device_matches(w);
+  if (dev_ok != MOE_FFN_OK) return dev_ok;
+  for (int32_t c0 = 0, c = 0; c0 < n_tokens; c0 += chunk_tokens, ++c) {
+    const int32_t m = std::min(chunk_tokens, n_tokens - c0);
+    const size_t off = (size_t)c0 * w->dm.d;
+    const int rev = (flags & MOE_FFN_CHUNK_SERPENTINE) ? (c & 1) : 0;
+    const int rc = run_layer(w, x + off, m, out + off, ws, ws_bytes, nullptr, stream, nullptr, nullptr, rev);
+    if (rc != MOE_FFN_OK) return rc;
+  }
+  return MOE_FFN_OK;
 }
 
 int moe_ffn_prefill_residual(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* h,

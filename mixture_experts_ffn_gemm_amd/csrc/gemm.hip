@@ -709,7 +709,10 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
   if (slot >= per_xcd) return;
   const int blk = ((int)blockIdx.x & 7) * per_xcd + slot;
   if (blk >= n_valid) return;
-  const int T = blk / nstrips, cs = blk - (blk / nstrips) * nstrips;
+  const int Tl = blk / nstrips, cs = blk - Tl * nstrips;
+  // reverse: the same work in the opposite tile order, so that each XCD
+  // starts on the tiles another finished last (serpentine chunk order)
+  const int T = a.reverse ? n_tiles - 1 - Tl : Tl;
   const int32_t* ent = a.tiles + 4 + 3 * T;
   const int g = ent[0], row0 = ent[1], row_end = ent[2];
   if (g < 0 || g >= a.G || row0 < 0 || row_end <= row0 || row_end > a.p_total) return;

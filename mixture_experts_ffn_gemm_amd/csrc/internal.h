@@ -188,6 +188,7 @@ struct GemmArgs {
   float* partial;
   int d;
   int kk;
+  int reverse;  // 1: walk the tile table from its last tile (serpentine chunk order)
 };
 
 hipError_t launch_gateup(const GemmArgs& a, hipStream_t s);

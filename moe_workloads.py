@@ -81,6 +81,10 @@ WORKLOADS = {
     "olmoe_decode1": Workload("olmoe_decode1", 5, 1, OLMOE, description="decode, 1 token"),
     "olmoe_decode8": Workload("olmoe_decode8", 5, 8, OLMOE, description="decode, 8 tokens"),
     "olmoe_n4096": Workload("olmoe_n4096", 5, 4096, OLMOE, description="prefill stress, 4096 tokens"),
+    # #388's second comment: a 2048-token logical batch prefilled as ubatch-512
+    # chunks on the 35B-A3B shape (same layer seeds as a3b_n512)
+    "a3b_n2048": Workload("a3b_n2048", 4, 2048, A3B,
+                          description="35B-A3B-shaped layer, logical batch 2048 (ubatch-512 chunking)"),
 }
 
 

@@ -143,3 +143,11 @@ def test_probe_library_exports_its_header_and_validates(B):
     assert P.moe_probe_copy(64, 128, 24, None) == -1      # not a multiple of 16
     assert P.moe_probe_copy(64, 96, 64, None) == -1       # overlapping
     assert P.moe_probe_copy(64, 4096, 0, None) == 0       # nothing to do
+
+
+def test_chunked_prefill_validates_on_the_host(B):
+    L = B.lib()
+    assert L.moe_ffn_prefill_chunked(None, 16, 4, 2, 0, 32, 64, 1 << 20, None) == -1   # no handle
+    assert L.moe_ffn_prefill_chunked(16, 16, 4, 0, 0, 32, 64, 1 << 20, None) == -1     # chunk 0
+    assert L.moe_ffn_prefill_chunked(16, 16, 4, 2, 2, 32, 64, 1 << 20, None) == -1     # unknown flag
+    assert L.moe_ffn_prefill_chunked(16, 16, -1, 2, 0, 32, 64, 1 << 20, None) == -1    # negative n

@@ -386,6 +386,57 @@ def _tile_group(counts, t):
     raise AssertionError("tile past the table")
 
 
+# ------------------------------------------------------------- chunked prefill
+@pytest.mark.parametrize("flags", [0, 1])
+@pytest.mark.parametrize("case,n,chunk", [(0, 300, 128), (1, 300, 100), (1, 37, 512)])
+def test_chunked_prefill(case, n, chunk, flags):
+    """moe_ffn_prefill_chunked: consecutive chunks on one workspace sized for
+    one chunk, in forward and serpentine tile order; every token's output
+    against the oracle to the fp32 bar, and against the unchunked call's."""
+    from mixture_experts_ffn_gemm_amd import binding as B
+    from mixture_experts_ffn_gemm_amd.layer import MoeLayer
+    shape, lw = mw.random_shape_case(20 + case, **MID_SHAPES[case])
+    x = mw.make_tokens(750 + case, n, shape.d)
+    layer = MoeLayer.from_workload(lw)
+    try:
+        xt = torch.from_numpy(x).cuda()
+        full = layer.prefill(xt)
+        ws = torch.empty(layer.workspace_size(min(chunk, n)), dtype=torch.uint8, device="cuda")
+        out = torch.full((n, shape.d), float("nan"), dtype=torch.float32, device="cuda")
+        B.moe_ffn_prefill_chunked(layer.handle, xt, n, chunk, flags, out, ws, ws.numel())
+        torch.cuda.synchronize()
+        got, ref_full = out.cpu().numpy(), full.cpu().numpy()
+    finally:
+        layer.close()
+    ref = O.moe_tokens(lw, x)
+    r, e = moe_close(got, ref["out"])
+    moe_close(got, ref_full)
+    say(f"chunked case {case} n={n} chunk={chunk} flags={flags}: rel_l2={r:.2e} max_elem={e:.2e}")
+
+
+@pytest.mark.slow
+def test_chunked_prefill_olmoe_ubatch512():
+    """The OLMoE-shaped N=2048 layer as four ubatch-512 chunks in serpentine
+    order: every token against the oracle."""
+    from mixture_experts_ffn_gemm_amd import binding as B
+    from mixture_experts_ffn_gemm_amd.layer import MoeLayer
+    lw = mw.workload_layer("olmoe_n2048")
+    x = mw.workload_tokens("olmoe_n2048")
+    n, d = x.shape
+    layer = MoeLayer.from_workload(lw)
+    try:
+        xt = torch.from_numpy(x).cuda()
+        ws = torch.empty(layer.workspace_size(512), dtype=torch.uint8, device="cuda")
+        out = torch.full((n, d), float("nan"), dtype=torch.float32, device="cuda")
+        B.moe_ffn_prefill_chunked(layer.handle, xt, n, 512, B.CHUNK_SERPENTINE, out, ws, ws.numel())
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+    finally:
+        layer.close()
+    r, e = moe_close(got, O.moe_tokens(lw, x)["out"])
+    say(f"olmoe_n2048 in 4 serpentine chunks of 512: rel_l2={r:.2e} max_elem={e:.2e} on all 2048 tokens")
+
+
 # ------------------------------------------------------------- stack form
 @pytest.mark.parametrize("case", [1, 2, 5])
 def test_prefill_residual_matches_unfused(case):
