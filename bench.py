@@ -213,10 +213,12 @@ def cpu_baseline(layers, x, target_s, eps=1e-5):
                                         f"({', '.join('%.2f' % r for r in rates1)} tokens/s)"}}
 
 
-def measured_peaks(stream):
+def measured_peaks(stream, settle_s=0.3):
     """The int8 matrix-core rate and HBM streaming rate of this GPU, measured
     with the calibration kernels of libmoe_probe.so (timed with HIP events on
-    the launch stream): the ceilings next to the datasheet peaks."""
+    the launch stream, each after settle_s seconds of the same launches, so at
+    the clock the GPU holds under that load): the ceilings next to the
+    datasheet peaks."""
     import torch
     from mixture_experts_ffn_gemm_amd import build as hb
     P = C.CDLL(hb.PROBE_LIB)
@@ -227,8 +229,13 @@ def measured_peaks(stream):
     st = stream.cuda_stream
 
     def time_launches(fn, reps=5):
-        for _ in range(2):
-            fn()
+        t0 = time.perf_counter()
+        while True:
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= settle_s:
+                break
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         for _ in range(reps):
@@ -277,6 +284,9 @@ def main():
                     help="prefill workloads: time moe_ffn_prefill_chunked with chunks of TOKENS tokens "
                          "(stages and roofline then describe one chunk-sized call)")
     ap.add_argument("--chunk-order", choices=("forward", "serpentine"), default="serpentine")
+    ap.add_argument("--settle-seconds", type=float, default=1.0,
+                    help="untimed: run the step back to back for this long before the warmup steps, so that "
+                         "the GPU clock has reached its steady state under this load (0 disables it)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="wall-time budget of the CPU oracle sample (0 disables it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -348,6 +358,18 @@ def main():
         def step_fn(h, xx, nn, oo, w_, wb, r, st):  # the whole batch, chunk by chunk
             B.moe_ffn_prefill_chunked(h, xx, nn, chunk, flags, oo, w_, wb, st)
     step_fn(layer.handle, x, n, out, ws, ws.numel(), B.make_routing(exp_start=exp_start), stream)
+    # Clock settling (untimed): from idle the GPU ramps its clock up over tens
+    # of milliseconds, so a few warmup steps would time a partly ramped clock.
+    settle_t0 = time.perf_counter()
+    settle_calls = 0
+    while time.perf_counter() - settle_t0 < args.settle_seconds:
+        for _ in range(20):
+            if n_layers > 1:
+                stack_pass()
+            else:
+                step_fn(layer.handle, x, n, out, ws, ws.numel(), None, stream)
+        settle_calls += 20
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step_fn(layer.handle, x, n, out, ws, ws.numel(), None, stream)
     torch.cuda.synchronize()
@@ -476,7 +498,7 @@ def main():
     gemm_frac = (gu_ops + dn_ops) / ((gu_us + dn_us) * 1e-6) / 1e12 / INT8_PEAK_TOPS
 
     log("[bench] measuring the int8 MFMA and copy ceilings")
-    peaks = measured_peaks(stream)
+    peaks = measured_peaks(stream, settle_s=min(args.settle_seconds, 0.3))
     peak_key = "copy_GBps" if roofline["unit"] == "GB/s" else "int8_mfma_TOPs"
     roofline["measured_peak"] = peaks[peak_key]
     roofline["frac_of_measured_peak"] = round(roofline["achieved"] / peaks[peak_key], 4)
@@ -490,6 +512,9 @@ def main():
     res = {
         "metric": METRIC, "value": round(n / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "clock_settle": {"seconds": args.settle_seconds, "steps": settle_calls,
+                         "why": "untimed steps before the warmup, so that the timed steps run at the clock "
+                                "the GPU holds under this load rather than one still ramping up from idle"},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
         "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights packed as Q8_0)",
         "config": {"workload": args.workload, **{k: v for k, v in mw.describe(args.workload).items()

@@ -193,16 +193,19 @@ struct Ops {
   v4i b[4];
 };
 
-template <bool GATEUP>
-__device__ __forceinline__ void read_block(const char* buf, int b, int wave, int lane, Ops& o) {
+// a_off: LDS offset of the 32-row activation slab within the stage buffer.
+__device__ __forceinline__ void read_block_at(const char* buf, int a_off, int b, int lane, Ops& o) {
   // A: row lane%32, piece 2b + lane/32 of the k-step, stored at its row's
   // 128-byte line position (piece ^ row%8)
   const int r = lane & 31, p = 2 * b + (lane >> 5);
-  o.a = *reinterpret_cast<const v4i*>(buf + Lay<GATEUP>::A_OFF + wave * (KSTEP * 1024) + r * 128 +
-                                      ((p ^ (r & 7)) << 4));
+  o.a = *reinterpret_cast<const v4i*>(buf + a_off + r * 128 + ((p ^ (r & 7)) << 4));
 #pragma unroll
   for (int t = 0; t < 4; ++t)
     o.b[t] = *reinterpret_cast<const v4i*>(buf + B_OFF + (b * 4 + t) * 1024 + lane * 16);
+}
+template <bool GATEUP>
+__device__ __forceinline__ void read_block(const char* buf, int b, int wave, int lane, Ops& o) {
+  read_block_at(buf, Lay<GATEUP>::A_OFF + wave * (KSTEP * 1024), b, lane, o);
 }
 
 // Gate/up: the k-step's weight scales of the 4 tiles (column lane%32, blocks
@@ -213,13 +216,14 @@ struct GuScales {
   uint2 sa;
 };
 
-__device__ __forceinline__ void read_scales(const char* buf, int wave, int lane, GuScales& s) {
+// as_off: LDS offset of the slab's activation scales within the stage buffer.
+__device__ __forceinline__ void read_scales_at(const char* buf, int as_off, int lane, GuScales& s) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const uint2 p = *reinterpret_cast<const uint2*>(buf + BS_OFF + (t * 32 + (lane & 31)) * 8);
     s.sw[t] = as_v4h(p.x, p.y);
   }
-  const uint2 p = *reinterpret_cast<const uint2*>(buf + Lay<true>::AS_OFF + wave * 256 + (lane & 31) * 8);
+  const uint2 p = *reinterpret_cast<const uint2*>(buf + as_off + (lane & 31) * 8);
   const uint32_t m = lane < 32 ? 0xffffffffu : 0u;
   s.sa = make_uint2(p.x & m, p.y & m);
 }
@@ -239,11 +243,17 @@ struct DnScales {
   uint32_t q;
 };
 
-__device__ __forceinline__ void read_scales(const char* buf, int wave, int lane, DnScales& s) {
+__device__ __forceinline__ void read_scales_at(const char* buf, int as_off, int lane, DnScales& s) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) s.wb[t] = *reinterpret_cast<const uint2*>(buf + BS_OFF + t * 512 + lane * 8);
-  const uint2 p = *reinterpret_cast<const uint2*>(buf + Lay<false>::AS_OFF + wave * 256 + (lane & 31) * 8);
+  const uint2 p = *reinterpret_cast<const uint2*>(buf + as_off + (lane & 31) * 8);
   s.q = lane < 32 ? p.x : p.y;
+}
+
+template <typename SC>
+__device__ __forceinline__ void read_scales(const char* buf, int wave, int lane, SC& s) {
+  constexpr bool GATEUP = std::is_same<SC, GuScales>::value;
+  read_scales_at(buf, Lay<GATEUP>::AS_OFF + wave * 256, lane, s);
 }
 
 // A operand of the down scale MFMA for block b: K slot 2b (the slot whose B
@@ -414,43 +424,101 @@ __device__ __forceinline__ v4h dn_corr_split(uint32_t q, int lane, int si) {
   return dn_corr_a(q & ((keep_lo ? 0x0000ffffu : 0u) | (keep_hi ? 0xffff0000u : 0u)));
 }
 
-// K-step j of a split-K wavefront (SharpInference #406 "References": the
-// split-K int8 GEMM follow-up).  A tile whose rows fill only one (S = 4) or
-// two (S = 2) of the four 32-row wavefront slots would leave the other
-// wavefronts idle; instead the S wavefronts of each row group share its
-// blocks: wavefront si computes blocks b = si (mod S) of every k-step into
-// its own partial accumulators, which the kernel sums in a fixed order at the
+// K-step j of a split-K wavefront of a two-row-group tile (SharpInference
+// #406 "References": the split-K int8 GEMM follow-up).  A tile whose rows
+// fill only two of the four 32-row wavefront slots would leave two
+// wavefronts idle; instead the two wavefronts of each row group share its
+// blocks: wavefront si computes blocks si and si + 2 of every k-step into its
+// own partial accumulators, which the kernel sums in a fixed order at the
 // end.  Copies, barriers and their placement are those of kstep (every
 // wavefront meets the same barriers and issues the same copies; each copies
 // its row group's activation slab into its own LDS area).  On entry X holds
 // block si of k-step j; on exit the same for k-step j+1.
-template <bool GATEUP, int S>
-__device__ __forceinline__ void kstep_split(const Src& src, int j, int KS, int wave, int lane, int si,
-                                            const char* cur, const char* nxt, uint32_t cur_lds,
-                                            uint32_t nxt_lds, Ops& X, Ops& Y, const ScalesT<GATEUP>& sc,
-                                            ScalesT<GATEUP>& sn, Ctx& cx, v16i& c, v16f& cf, v16f& s,
-                                            v16f (&acc)[4]) {
-  static_assert(S == 2 || S == 4, "split factors");
+template <bool GATEUP>
+__device__ __forceinline__ void kstep_split2(const Src& src, int j, int KS, int wave, int lane, int si,
+                                             const char* cur, const char* nxt, uint32_t cur_lds,
+                                             uint32_t nxt_lds, Ops& X, Ops& Y, const ScalesT<GATEUP>& sc,
+                                             ScalesT<GATEUP>& sn, Ctx& cx, v16i& c, v16f& cf, v16f& s,
+                                             v16f (&acc)[4]) {
   if (j >= 1 && j + 1 < KS) issue_acts<GATEUP>(src, j + 1, nxt_lds, wave, lane);
-  if constexpr (!GATEUP) cx.corr = dn_corr_split<S>(sc.q, lane, si);
-  if constexpr (S == 2) {
-    read_block<GATEUP>(cur, si + 2, wave, lane, Y);
-    compute_block(X, sc, si, Y, sc, si + 2, false, cx, lane, c, cf, s, acc);
-  }
+  if constexpr (!GATEUP) cx.corr = dn_corr_split<2>(sc.q, lane, si);
+  read_block<GATEUP>(cur, si + 2, wave, lane, Y);
+  compute_block(X, sc, si, Y, sc, si + 2, false, cx, lane, c, cf, s, acc);
   if (j + 1 < KS) {
     wait_copies_barrier_0();
     if (j + 2 < KS) issue_weights<GATEUP>(src, j + 2, cur_lds, wave);
   }
-  if constexpr (S == 2) {
-    read_block<GATEUP>(nxt, si, wave, lane, X);
-    read_scales(nxt, wave, lane, sn);
-    compute_block(Y, sc, si + 2, X, sn, si, true, cx, lane, c, cf, s, acc);
-  } else {
-    read_block<GATEUP>(nxt, si, wave, lane, Y);
-    read_scales(nxt, wave, lane, sn);
-    compute_block(X, sc, si, Y, sn, si, true, cx, lane, c, cf, s, acc);
-    X = Y;
+  read_block<GATEUP>(nxt, si, wave, lane, X);
+  read_scales(nxt, wave, lane, sn);
+  compute_block(Y, sc, si + 2, X, sn, si, true, cx, lane, c, cf, s, acc);
+}
+
+// One-row-group tiles (at most 32 rows): the four wavefronts split every
+// k-step, wavefront si computing block si.  Each wavefront then does a
+// quarter of a full tile's matrix work per k-step while the workgroup still
+// stages the whole weight k-step, so the k loop is bound by the latency of
+// the global->LDS copies rather than by the matrix pipe.  This pipeline
+// therefore keeps three k-steps in LDS instead of two (a stage holds the
+// weight k-step and the single activation slab) and issues the copies of
+// k-step j+3 at the barrier of k-step j, two k-steps earlier than they are
+// needed.
+template <bool GATEUP>
+struct Lay1 {
+  static constexpr int A_OFF = Lay<GATEUP>::W_BYTES;      // the slab's 4 chunks [row][128 B]
+  static constexpr int AS_OFF = A_OFF + KSTEP * 1024;     // their scales [32 rows][4 blocks]
+  static constexpr int STAGE = AS_OFF + 32 * KSTEP * 2;   // 21.25 / 22.25 KiB
+  static constexpr int DMA = Lay<GATEUP>::DMA - KSTEP + 1;  // copies per wavefront per k-step
+};
+static_assert(3 * Lay1<true>::STAGE <= 2 * Lay<true>::STAGE, "three stages must fit in the LDS buffers");
+static_assert(3 * Lay1<false>::STAGE <= 2 * Lay<false>::STAGE, "three stages must fit in the LDS buffers");
+static_assert(Lay1<true>::STAGE % 256 == 0 && Lay1<false>::STAGE % 256 == 0, "stage alignment");
+
+// This wavefront's copies of k-step j into the stage at LDS address L: its
+// share of the weight k-step, activation chunk `wave` of the slab, and the
+// slab's scales (every wavefront copies the same 256 bytes, so that all issue
+// the same number of copies).
+template <bool GATEUP>
+__device__ __forceinline__ void issue_kstep1(const Src& s, int j, uint32_t L, int wave, int lane) {
+  issue_weights<GATEUP>(s, j, L, wave);
+  dma16(s.a + (size_t)j * KSTEP * 1024 + wave * 1024, lane * 16, L + Lay1<GATEUP>::A_OFF + wave * 1024);
+  dma4(s.as + (size_t)j * 32 * KSTEP, lane * 4, L + Lay1<GATEUP>::AS_OFF);
+}
+
+// Wait until at most N of this wavefront's copies are in flight and its LDS
+// reads have returned, then meet the other wavefronts.
+template <int N>
+__device__ __forceinline__ void wait_copies_reads_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// K-step j of a one-row-group tile.  On entry X and sc hold block si of
+// k-step j (read from its stage in the previous k-step); k-steps j+1 and j+2
+// are in flight.  The barrier publishes k-step j+1 and proves that every
+// wavefront has read k-step j, whose stage then receives k-step j+3.  On exit
+// Y and sn hold block si of k-step j+1 (stale data after the last k-step,
+// never used).
+template <bool GATEUP>
+__device__ __forceinline__ void kstep1(const Src& src, int j, int KS, int wave, int lane, int si,
+                                       const char* lds, uint32_t lds_base, const Ops& X, Ops& Y,
+                                       const ScalesT<GATEUP>& sc, ScalesT<GATEUP>& sn, Ctx& cx, v16i& c,
+                                       v16f& cf, v16f& s, v16f (&acc)[4]) {
+  using L1 = Lay1<GATEUP>;
+  if constexpr (!GATEUP) cx.corr = dn_corr_split<4>(sc.q, lane, si);
+  const int st = j % 3;
+  const int sn1 = st == 2 ? 0 : st + 1;
+  if (j + 1 < KS) {
+    if (j + 2 < KS)
+      wait_copies_reads_barrier<L1::DMA>();
+    else
+      wait_copies_reads_barrier<0>();
+    if (j + 3 < KS) issue_kstep1<GATEUP>(src, j + 3, lds_base + st * L1::STAGE, wave, lane);
   }
+  const char* nb = lds + sn1 * L1::STAGE;
+  read_block_at(nb, L1::A_OFF, si, lane, Y);
+  read_scales_at(nb, L1::AS_OFF, lane, sn);
+  compute_block(X, sc, si, Y, sn, si, true, cx, lane, c, cf, s, acc);
 }
 
 // The partial accumulators of a split row group, summed into its first
@@ -479,139 +547,54 @@ __device__ __forceinline__ void split_reduce(char* lds, int S, int rg, int si, i
   __syncthreads();  // the reduction buffers are read before any epilogue reuses the LDS
 }
 
+// Pipeline constants and the state of (block si, tile 0) from the first
+// block's operands X and scales s0: for gate/up the int8 MFMA of tile 1,
+// float(C) and the scale product of tile 0; for down the int8 MFMA and the
+// scale product of tile 0.
+template <bool GATEUP>
+__device__ __forceinline__ void pipeline_init(const Ops& X, const ScalesT<GATEUP>& s0, int si, int lane, Ctx& cx,
+                                              v16i& c, v16f& cf, v16f& s) {
+  const v16f zf = {0};
+  if constexpr (GATEUP) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) cx.magic[v] = 0x4b400000;  // 1.5 * 2^23
+    anchor(cx.magic);  // one register copy, never rematerialised
+    const _Float16 h0 = 0;
+    cx.sub_a = lane < 32 ? (v4h){(_Float16)-3072.0f, h0, h0, h0} : (v4h){h0, h0, h0, h0};
+    cx.sub_b = lane < 32 ? (v4h){(_Float16)4096.0f, h0, h0, h0} : (v4h){h0, h0, h0, h0};
+    anchor(cx.sub_a, cx.sub_b);
+    const v16i d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(X.a, X.b[0], cx.magic, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_i32_32x32x32_i8(X.a, X.b[1], cx.magic, 0, 0, 0);
+    cf = __builtin_amdgcn_mfma_f32_32x32x8f16(cx.sub_a, cx.sub_b, __builtin_bit_cast(v16f, d0), 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x8f16(sa_slot(s0.sa, si), s0.sw[0], zf, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) cx.magic[v] = 0x3fc00000;  // 1.5f
+    anchor(cx.magic);
+    c = __builtin_amdgcn_mfma_i32_32x32x32_i8(X.a, X.b[0], cx.magic, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x8f16(dn_sa_slot(s0.q, si, lane), as_v4h(s0.wb[0]), zf, 0, 0, 0);
+  }
+}
+
 // Grouped GEMM.  GATEUP: A = the int8 token rows of the tile's (token, slot)
 // pairs, which the quantiser wrote in chunk form at their padded rows; B = the
 // [gate;up] strip of 64 SwiGLU columns; epilogue h = silu(gate) * up,
 // requantised per 32 into the down GEMM's A-operand chunks.  !GATEUP: A = those
 // chunks, B = a 128-column strip of the down matrix; epilogue scatters the fp32
 // rows to partial[token][slot] (the unweighted down-partials of #129 "Scope").
-// The work of one (tile, strip) workgroup with split factor S (1: one 32-row
-// row group per wavefront; 2, 4: see kstep_split).  Each split factor is a
-// separate, self-contained body (nothing it computes is live across the
-// others), so that each gets its own register allocation.
-template <bool GATEUP, int S>
-__device__ __forceinline__ void tile_work(const GemmArgs& a, char (&lds)[2][Lay<GATEUP>::STAGE], int lane,
-                                          int wave, int T, int cs, int g, int row0, int row_end, int KS,
-                                          const uint8_t* strip) {
-
-  using L = Lay<GATEUP>;
-  const int rg = wave / S, si = wave - rg * S;
-  const int wrow0 = row0 + MT_WAVE * rg;    // first CSR row of this wavefront's row group
-  const bool active = wrow0 < row_end;      // wavefront-uniform (every wavefront when S > 1)
-  const int t32 = T * NWAVE + rg;           // 32-row tile index of the A slab and the h chunks
-  // A operand: this wavefront's run of 1 KiB chunks (one per 32-block) and
-  // their scales, per 32-row quarter t32 of the tile.
-  const int a_kb = GATEUP ? a.d_pad / QB : a.kbmax;
-  Src src;
-  src.w = strip;
-  src.o_w = lane * 16;
-  src.o_ws = 16 * 1024 + wave * (GATEUP ? 256 : 512) + lane * 4;
-  src.a = (GATEUP ? a.gq : a.hq) + (size_t)t32 * a_kb * 1024;
-  src.as = (GATEUP ? a.gqs : a.hs) + (size_t)t32 * a_kb * 32;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)&lds[0][0];
-  const uint32_t lds1 = (uint32_t)(uintptr_t)(lds_char*)&lds[1][0];
-
-  // Prologue: k-steps 0 and 1 in flight; wait for k-step 0.
-  issue_weights<GATEUP>(src, 0, lds0, wave);
-  issue_acts<GATEUP>(src, 0, lds0, wave, lane);
-  // Down: the (token, slot) of this lane's CSR row wrow0 + lane%32, loaded
-  // now (and first used in the epilogue) so that the load's latency hides
-  // under the k loop.  Every wavefront issues both loads (the row clamped
-  // into the CSR arrays), so that the vmcnt count below holds for all.
-  int tok = -1, slt = -1;
-  if (!GATEUP) {
-    const int p_lane = min(wrow0 + (lane & 31), a.p_total - 1);
-    tok = a.tok_i[p_lane];
-    slt = a.tok_k[p_lane];
-  }
-  if (KS > 1) {
-    issue_weights<GATEUP>(src, 1, lds1, wave);
-    issue_acts<GATEUP>(src, 1, lds1, wave, lane);
-    wait_copies_barrier_n<L::DMA + 2 * !GATEUP>();
-  } else {
-    wait_copies_barrier_0();
-  }
-  v16f acc[4];
-  if (active) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = (v16f){0};
-    Ops X, Y;
-    ScalesT<GATEUP> s0, s1;
-    Ctx cx;
-    read_block<GATEUP>(lds[0], si, wave, lane, X);  // the wavefront's first block
-    read_scales(lds[0], wave, lane, s0);
-    const v16f zf = {0};
-    v16i c;
-    v16f cf, s;
-    if constexpr (GATEUP) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) cx.magic[v] = 0x4b400000;  // 1.5 * 2^23
-      anchor(cx.magic);  // one register copy, never rematerialised
-      const _Float16 h0 = 0;
-      cx.sub_a = lane < 32 ? (v4h){(_Float16)-3072.0f, h0, h0, h0} : (v4h){h0, h0, h0, h0};
-      cx.sub_b = lane < 32 ? (v4h){(_Float16)4096.0f, h0, h0, h0} : (v4h){h0, h0, h0, h0};
-      anchor(cx.sub_a, cx.sub_b);
-      // pipeline state of (block 0, tile 0): int8 MFMA of tile 1, float(C)
-      // and scale product of tile 0
-      const v16i d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(X.a, X.b[0], cx.magic, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_i32_32x32x32_i8(X.a, X.b[1], cx.magic, 0, 0, 0);
-      cf = __builtin_amdgcn_mfma_f32_32x32x8f16(cx.sub_a, cx.sub_b, __builtin_bit_cast(v16f, d0), 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_32x32x8f16(sa_slot(s0.sa, si), s0.sw[0], zf, 0, 0, 0);
-    } else {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) cx.magic[v] = 0x3fc00000;  // 1.5f
-      anchor(cx.magic);
-      c = __builtin_amdgcn_mfma_i32_32x32x32_i8(X.a, X.b[0], cx.magic, 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_32x32x8f16(dn_sa_slot(s0.q, si, lane), as_v4h(s0.wb[0]), zf, 0, 0, 0);
-    }
-    // Unrolled by two so that each buffer and scale set has a fixed role.
-    if constexpr (S == 1) {
-      for (int j = 0; j < KS; j += 2) {
-        kstep<GATEUP>(src, j, KS, wave, lane, lds[0], lds[1], lds0, lds1, X, Y, s0, s1, cx, c, cf, s, acc);
-        if (j + 1 < KS)
-          kstep<GATEUP>(src, j + 1, KS, wave, lane, lds[1], lds[0], lds1, lds0, X, Y, s1, s0, cx, c, cf, s, acc);
-      }
-    } else if constexpr (S == 2) {
-      for (int j = 0; j < KS; j += 2) {
-        kstep_split<GATEUP, 2>(src, j, KS, wave, lane, si, lds[0], lds[1], lds0, lds1, X, Y, s0, s1, cx, c, cf,
-                               s, acc);
-        if (j + 1 < KS)
-          kstep_split<GATEUP, 2>(src, j + 1, KS, wave, lane, si, lds[1], lds[0], lds1, lds0, X, Y, s1, s0, cx, c,
-                                 cf, s, acc);
-      }
-    } else {
-      for (int j = 0; j < KS; j += 2) {
-        kstep_split<GATEUP, 4>(src, j, KS, wave, lane, si, lds[0], lds[1], lds0, lds1, X, Y, s0, s1, cx, c, cf,
-                               s, acc);
-        if (j + 1 < KS)
-          kstep_split<GATEUP, 4>(src, j + 1, KS, wave, lane, si, lds[1], lds[0], lds1, lds0, X, Y, s1, s0, cx, c,
-                                 cf, s, acc);
-      }
-    }
-  } else if constexpr (S == 1) {
-    // A wavefront past the tile's rows computes nothing but still does its
-    // share of the copies and meets every barrier.
-    for (int j = 0; j + 1 < KS; ++j) {
-      if (j >= 1) issue_acts<GATEUP>(src, j + 1, (j & 1) ? lds0 : lds1, wave, lane);
-      wait_copies_barrier_0();
-      if (j + 2 < KS) issue_weights<GATEUP>(src, j + 2, (j & 1) ? lds1 : lds0, wave);
-    }
-  }
-  // gate/up: every wavefront is out of the k loop, so LDS is free for the
-  // epilogue (the down epilogue uses no LDS).  Split-K: the row group's
-  // partial sums meet in its first wavefront, which alone runs the epilogue.
-  if constexpr (S > 1)
-    split_reduce(&lds[0][0], S, rg, si, lane, acc);
-  else if (GATEUP)
-    __syncthreads();
-  if (!active || si != 0) return;
-
-  if (GATEUP) {
+//
+// The epilogue of one wavefront's 32 rows (CSR rows wrow0.., 32-row tile
+// t32) against strip cs of group g; tok / slt are this lane's (token, slot)
+// for down.  Gate/up uses this wavefront's area at the start of the LDS.
+template <bool GATEUP>
+__device__ __forceinline__ void epilogue(const GemmArgs& a, char* lds, int lane, int wave, int t32, int cs, int g,
+                                         int wrow0, int row_end, int tok, int slt, v16f (&acc)[4]) {
+  if constexpr (GATEUP) {
     // h = silu(gate) * up for the wavefront's 32 rows x 64 columns, transposed
     // through LDS ([32][65] floats, conflict-free) so that lane l then owns the
     // whole 32-block (row l%32, sub-strip l/32): amax, the two divisions and 32
     // codes per lane, written as two 16-byte pieces of the down GEMM's A chunk.
-    float* hl = reinterpret_cast<float*>(&lds[0][0]) + wave * (32 * EPI_STRIDE);
+    float* hl = reinterpret_cast<float*>(lds) + wave * (32 * EPI_STRIDE);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -692,6 +675,159 @@ __device__ __forceinline__ void tile_work(const GemmArgs& a, char (&lds)[2][Lay<
   }
 }
 
+// The work of one (tile, strip) workgroup whose tile has three or four
+// 32-row groups (S = 1: one row group per wavefront) or two (S = 2: see
+// kstep_split2).  Each split factor is a separate, self-contained body
+// (nothing it computes is live across the others), so that each gets its own
+// register allocation.
+template <bool GATEUP, int S>
+__device__ __forceinline__ void tile_work(const GemmArgs& a, char (&lds)[2][Lay<GATEUP>::STAGE], int lane,
+                                          int wave, int T, int cs, int g, int row0, int row_end, int KS,
+                                          const uint8_t* strip) {
+  static_assert(S == 1 || S == 2, "split factors of tile_work");
+  using L = Lay<GATEUP>;
+  const int rg = wave / S, si = wave - rg * S;
+  const int wrow0 = row0 + MT_WAVE * rg;    // first CSR row of this wavefront's row group
+  const bool active = wrow0 < row_end;      // wavefront-uniform (every wavefront when S > 1)
+  const int t32 = T * NWAVE + rg;           // 32-row tile index of the A slab and the h chunks
+  // A operand: this wavefront's run of 1 KiB chunks (one per 32-block) and
+  // their scales, per 32-row quarter t32 of the tile.
+  const int a_kb = GATEUP ? a.d_pad / QB : a.kbmax;
+  Src src;
+  src.w = strip;
+  src.o_w = lane * 16;
+  src.o_ws = 16 * 1024 + wave * (GATEUP ? 256 : 512) + lane * 4;
+  src.a = (GATEUP ? a.gq : a.hq) + (size_t)t32 * a_kb * 1024;
+  src.as = (GATEUP ? a.gqs : a.hs) + (size_t)t32 * a_kb * 32;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)&lds[0][0];
+  const uint32_t lds1 = (uint32_t)(uintptr_t)(lds_char*)&lds[1][0];
+
+  // Prologue: k-steps 0 and 1 in flight; wait for k-step 0.
+  issue_weights<GATEUP>(src, 0, lds0, wave);
+  issue_acts<GATEUP>(src, 0, lds0, wave, lane);
+  // Down: the (token, slot) of this lane's CSR row wrow0 + lane%32, loaded
+  // now (and first used in the epilogue) so that the load's latency hides
+  // under the k loop.  Every wavefront issues both loads (the row clamped
+  // into the CSR arrays), so that the vmcnt count below holds for all.
+  int tok = -1, slt = -1;
+  if (!GATEUP) {
+    const int p_lane = min(wrow0 + (lane & 31), a.p_total - 1);
+    tok = a.tok_i[p_lane];
+    slt = a.tok_k[p_lane];
+  }
+  if (KS > 1) {
+    issue_weights<GATEUP>(src, 1, lds1, wave);
+    issue_acts<GATEUP>(src, 1, lds1, wave, lane);
+    wait_copies_barrier_n<L::DMA + 2 * !GATEUP>();
+  } else {
+    wait_copies_barrier_0();
+  }
+  v16f acc[4];
+  if (active) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = (v16f){0};
+    Ops X, Y;
+    ScalesT<GATEUP> s0, s1;
+    Ctx cx;
+    read_block<GATEUP>(lds[0], si, wave, lane, X);  // the wavefront's first block
+    read_scales(lds[0], wave, lane, s0);
+    v16i c;
+    v16f cf, s;
+    pipeline_init<GATEUP>(X, s0, si, lane, cx, c, cf, s);
+    // Unrolled by two so that each buffer and scale set has a fixed role.
+    if constexpr (S == 1) {
+      for (int j = 0; j < KS; j += 2) {
+        kstep<GATEUP>(src, j, KS, wave, lane, lds[0], lds[1], lds0, lds1, X, Y, s0, s1, cx, c, cf, s, acc);
+        if (j + 1 < KS)
+          kstep<GATEUP>(src, j + 1, KS, wave, lane, lds[1], lds[0], lds1, lds0, X, Y, s1, s0, cx, c, cf, s, acc);
+      }
+    } else {
+      for (int j = 0; j < KS; j += 2) {
+        kstep_split2<GATEUP>(src, j, KS, wave, lane, si, lds[0], lds[1], lds0, lds1, X, Y, s0, s1, cx, c, cf, s,
+                             acc);
+        if (j + 1 < KS)
+          kstep_split2<GATEUP>(src, j + 1, KS, wave, lane, si, lds[1], lds[0], lds1, lds0, X, Y, s1, s0, cx, c,
+                               cf, s, acc);
+      }
+    }
+  } else if constexpr (S == 1) {
+    // A wavefront past the tile's rows computes nothing but still does its
+    // share of the copies and meets every barrier.
+    for (int j = 0; j + 1 < KS; ++j) {
+      if (j >= 1) issue_acts<GATEUP>(src, j + 1, (j & 1) ? lds0 : lds1, wave, lane);
+      wait_copies_barrier_0();
+      if (j + 2 < KS) issue_weights<GATEUP>(src, j + 2, (j & 1) ? lds1 : lds0, wave);
+    }
+  }
+  // gate/up: every wavefront is out of the k loop, so LDS is free for the
+  // epilogue (the down epilogue uses no LDS).  Split-K: the row group's
+  // partial sums meet in its first wavefront, which alone runs the epilogue.
+  if constexpr (S > 1)
+    split_reduce(&lds[0][0], S, rg, si, lane, acc);
+  else if (GATEUP)
+    __syncthreads();
+  if (!active || si != 0) return;
+  epilogue<GATEUP>(a, &lds[0][0], lane, wave, t32, cs, g, wrow0, row_end, tok, slt, acc);
+}
+
+// The work of a (tile, strip) workgroup whose tile has one 32-row group: the
+// three-stage pipeline of kstep1, then the fixed-order sum of the four
+// wavefronts' partial accumulators and the epilogue in wavefront 0.
+template <bool GATEUP>
+__device__ __forceinline__ void tile_work1(const GemmArgs& a, char* lds, int lane, int wave, int T, int cs, int g,
+                                           int row0, int row_end, int KS, const uint8_t* strip) {
+  using L1 = Lay1<GATEUP>;
+  const int si = wave;
+  const int t32 = T * NWAVE;
+  const int a_kb = GATEUP ? a.d_pad / QB : a.kbmax;
+  Src src;
+  src.w = strip;
+  src.o_w = lane * 16;
+  src.o_ws = 16 * 1024 + wave * (GATEUP ? 256 : 512) + lane * 4;
+  src.a = (GATEUP ? a.gq : a.hq) + (size_t)t32 * a_kb * 1024;
+  src.as = (GATEUP ? a.gqs : a.hs) + (size_t)t32 * a_kb * 32;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_char*)lds;
+
+  // Down: the (token, slot) of this lane's CSR row, loaded before any copy
+  // (vector loads complete in order, so the waits below cover them too).
+  int tok = -1, slt = -1;
+  if (!GATEUP) {
+    const int p_lane = min(row0 + (lane & 31), a.p_total - 1);
+    tok = a.tok_i[p_lane];
+    slt = a.tok_k[p_lane];
+  }
+  // Prologue: k-steps 0, 1 and 2 in flight; wait for k-step 0.
+  issue_kstep1<GATEUP>(src, 0, lds_base, wave, lane);
+  if (KS > 1) issue_kstep1<GATEUP>(src, 1, lds_base + L1::STAGE, wave, lane);
+  if (KS > 2) issue_kstep1<GATEUP>(src, 2, lds_base + 2 * L1::STAGE, wave, lane);
+  if (KS > 2)
+    wait_copies_reads_barrier<2 * L1::DMA>();
+  else if (KS > 1)
+    wait_copies_reads_barrier<L1::DMA>();
+  else
+    wait_copies_reads_barrier<0>();
+
+  v16f acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = (v16f){0};
+  Ops X, Y;
+  ScalesT<GATEUP> s0, s1;
+  Ctx cx;
+  read_block_at(lds, L1::A_OFF, si, lane, X);
+  read_scales_at(lds, L1::AS_OFF, lane, s0);
+  v16i c;
+  v16f cf, s;
+  pipeline_init<GATEUP>(X, s0, si, lane, cx, c, cf, s);
+  // Unrolled by two so that each operand and scale set has a fixed role.
+  for (int j = 0; j < KS; j += 2) {
+    kstep1<GATEUP>(src, j, KS, wave, lane, si, lds, lds_base, X, Y, s0, s1, cx, c, cf, s, acc);
+    if (j + 1 < KS) kstep1<GATEUP>(src, j + 1, KS, wave, lane, si, lds, lds_base, Y, X, s1, s0, cx, c, cf, s, acc);
+  }
+  split_reduce(lds, 4, 0, si, lane, acc);
+  if (si != 0) return;
+  epilogue<GATEUP>(a, lds, lane, 0, t32, cs, g, row0, row_end, tok, slt, acc);
+}
+
 template <bool GATEUP>
 __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
   using L = Lay<GATEUP>;
@@ -727,14 +863,14 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
 
   // Split-K: when the tile's rows fill only one (or two) of the four 32-row
   // wavefront slots, the wavefronts of each row group share its blocks (see
-  // kstep_split).
+  // kstep1 and kstep_split2).
   const int nact = (min(row_end - row0, MT_WG) + MT_WAVE - 1) / MT_WAVE;
   if (nact >= 3)
     tile_work<GATEUP, 1>(a, lds, lane, wave, T, cs, g, row0, row_end, KS, strip);
   else if (nact == 2)
     tile_work<GATEUP, 2>(a, lds, lane, wave, T, cs, g, row0, row_end, KS, strip);
   else
-    tile_work<GATEUP, 4>(a, lds, lane, wave, T, cs, g, row0, row_end, KS, strip);
+    tile_work1<GATEUP>(a, &lds[0][0], lane, wave, T, cs, g, row0, row_end, KS, strip);
 }
 
 int grid_for(long wgs) { return (int)((wgs + 7) / 8 * 8); }
