@@ -69,6 +69,49 @@ __device__ __forceinline__ void router_fma16_1(float& acc0, float xa, const f4v&
 }
 #undef RFMA1
 
+// Reductions over all 64 lanes of a wavefront (every lane active), without
+// the LDS crossbar: four DPP steps inside each 16-lane row (swap neighbours,
+// swap pairs, mirror the halves of 8, mirror the halves of 16) leave the
+// row's result in all of its lanes, then the four rows' results are read
+// with v_readlane and combined in a fixed order.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp64(unsigned long long v) {
+  const uint32_t lo = dpp32<CTRL>((uint32_t)v), hi = dpp32<CTRL>((uint32_t)(v >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
+__device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) {
+  return a > b ? a : b;
+}
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+  v = umax64(v, dpp64<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = umax64(v, dpp64<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = umax64(v, dpp64<0x141>(v));  // row_half_mirror
+  v = umax64(v, dpp64<0x140>(v));  // row_mirror
+  unsigned long long r = 0ull;
+#pragma unroll
+  for (int row = 0; row < 4; ++row) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * row);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * row);
+    r = umax64(r, ((unsigned long long)hi << 32) | lo);
+  }
+  return r;
+}
+__device__ __forceinline__ float wave_sum_rows(float v) {
+  v += __uint_as_float(dpp32<0xB1>(__float_as_uint(v)));
+  v += __uint_as_float(dpp32<0x4E>(__float_as_uint(v)));
+  v += __uint_as_float(dpp32<0x141>(__float_as_uint(v)));
+  v += __uint_as_float(dpp32<0x140>(__float_as_uint(v)));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 // Routing of one tile of ROUTE_TILE tokens, TPT threads per token (threads
 // tid < ROUTE_TILE * TPT of the workgroup; every thread of the workgroup
 // calls this, since it meets workgroup barriers; both the fused router and
@@ -113,10 +156,14 @@ __device__ __forceinline__ void route_tile(RouteLds& R, int tile, int t0, int nt
       unsigned long long m = 0ull;
 #pragma unroll
       for (int c = 0; c < NKEY; ++c) m = key[c] > m ? key[c] : m;
+      if constexpr (TPT == 64) {
+        m = wave_max_u64(m);
+      } else {
 #pragma unroll
-      for (int off = TPT / 2; off > 0; off >>= 1) {
-        const unsigned long long o = __shfl_xor(m, off, TPT);
-        m = o > m ? o : m;
+        for (int off = TPT / 2; off > 0; off >>= 1) {
+          const unsigned long long o = __shfl_xor(m, off, TPT);
+          m = o > m ? o : m;
+        }
       }
 #pragma unroll
       for (int c = 0; c < NKEY; ++c) key[c] = key[c] == m ? 0ull : key[c];
@@ -134,13 +181,21 @@ __device__ __forceinline__ void route_tile(RouteLds& R, int tile, int t0, int nt
     const float m = R.val[tl][0];
     float part = 0.0f;
     for (int e = g; e < E; e += TPT) part += expf(R.l[tl][e] - m);
+    if constexpr (TPT == 64) {
+      part = wave_sum_rows(part);
+    } else {
 #pragma unroll
-    for (int off = TPT / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, TPT);
+      for (int off = TPT / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, TPT);
+    }
     float p = (g < k) ? expf(R.val[tl][min(g, k - 1)] - m) / part : 0.0f;
     if (norm) {
       float sum = p;
+      if constexpr (TPT == 64) {
+        sum = wave_sum_rows(sum);
+      } else {
 #pragma unroll
-      for (int off = TPT / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, TPT);
+        for (int off = TPT / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, TPT);
+      }
       p = p / sum;
     }
     if (tl < nt && g < k) {
