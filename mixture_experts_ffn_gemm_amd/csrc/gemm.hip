@@ -187,6 +187,44 @@ __device__ __forceinline__ void issue_acts(const Src& s, int j, uint32_t L, int 
   dma4(s.as + (size_t)j * 32 * KSTEP, lane * 4, L + Lay<GATEUP>::AS_OFF + wave * 256);
 }
 
+// The same copies issued in parts, one part per tile of a block (the hook
+// of compute_block calls part t right after tile t's int8 MFMA), so that a
+// wavefront's copies go out between matrix instructions instead of in one
+// burst that stalls its issue: parts 0 and 1 two 1 KiB chunks each, part 2
+// the scales, part 3 nothing.
+template <bool GATEUP>
+__device__ __forceinline__ void issue_weights_part(const Src& s, int j, uint32_t L, int wave, int p) {
+  const uint8_t* w = s.w + (size_t)j * Lay<GATEUP>::W_BYTES;
+  if (p < 2) {
+#pragma unroll
+    for (int i = 2 * p; i < 2 * p + 2; ++i) {
+      const int c = wave + 4 * i;
+      dma16(w + c * 1024, s.o_w, L + B_OFF + c * 1024);
+    }
+  } else if (p == 2) {
+    if (GATEUP) {
+      dma4(w, s.o_ws, L + BS_OFF + wave * 256);
+    } else {
+      dma4(w, s.o_ws, L + BS_OFF + wave * 512);
+      dma4(w, s.o_ws + 256, L + BS_OFF + wave * 512 + 256);
+    }
+  }
+}
+template <bool GATEUP>
+__device__ __forceinline__ void issue_acts_part(const Src& s, int j, uint32_t L, int wave, int lane, int p) {
+  const int8_t* a = s.a + (size_t)j * KSTEP * 1024;
+  if (p < 2) {
+#pragma unroll
+    for (int i = 2 * p; i < 2 * p + 2; ++i)
+      dma16(a + i * 1024, lane * 16, L + Lay<GATEUP>::A_OFF + (wave * KSTEP + i) * 1024);
+  } else if (p == 2) {
+    dma4(s.as + (size_t)j * 32 * KSTEP, lane * 4, L + Lay<GATEUP>::AS_OFF + wave * 256);
+  }
+}
+struct NoHook {
+  __device__ void operator()(int) const {}
+};
+
 // Register operands of one block: this wavefront's A chunk and the 4 B chunks.
 struct Ops {
   v4i a;
@@ -304,9 +342,10 @@ struct Ctx {
 // third, scale MFMA(t+1), the last third.  The VALU does one fma per element
 // and block; the conversion runs on the matrix pipe, and the result is the
 // same as fma(float(C), S, acc).
+template <typename H = NoHook>
 __device__ __forceinline__ void compute_block(const Ops& o, const GuScales& sc, int b, const Ops& on,
                                               const GuScales& sn, int bn, bool, const Ctx& cx, int,
-                                              v16i& dn, v16f& cf, v16f& s, v16f (&acc)[4]) {
+                                              v16i& dn, v16f& cf, v16f& s, v16f (&acc)[4], const H& hook = H()) {
   const v16f zf = {0};
   v4h sav = sa_slot(sc.sa, b);
   v4h savn = sa_slot(sn.sa, bn);
@@ -315,6 +354,7 @@ __device__ __forceinline__ void compute_block(const Ops& o, const GuScales& sc, 
     v16i dnn = t < 2 ? __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a, o.b[t + 2], cx.magic, 0, 0, 0)
                      : __builtin_amdgcn_mfma_i32_32x32x32_i8(on.a, on.b[t - 2], cx.magic, 0, 0, 0);
     anchor(dnn, dn);
+    hook(t);
 #pragma unroll
     for (int v = 0; v < 5; ++v) acc[t][v] = __builtin_fmaf(cf[v], s[v], acc[t][v]);
     anchor(acc[t]);
@@ -342,9 +382,11 @@ __device__ __forceinline__ void compute_block(const Ops& o, const GuScales& sc, 
 // bias, half of acc(t) = fma(D(t), S(t), acc(t)), scale MFMA(t+1), the other
 // half; after the wavefront's last block of the k-step (corr) the correction
 // MFMA subtracts the 1.5 * S terms of the k-step's blocks it computed.
+template <typename H = NoHook>
 __device__ __forceinline__ void compute_block(const Ops& o, const DnScales& sc, int b, const Ops& on,
                                               const DnScales& sn, int bn, bool corr, const Ctx& cx,
-                                              int lane, v16i& c, v16f&, v16f& s, v16f (&acc)[4]) {
+                                              int lane, v16i& c, v16f&, v16f& s, v16f (&acc)[4],
+                                              const H& hook = H()) {
   const v16f zf = {0};
   v4h sav = dn_sa_slot(sc.q, b, lane);
   v4h savn = dn_sa_slot(sn.q, bn, lane);
@@ -355,6 +397,7 @@ __device__ __forceinline__ void compute_block(const Ops& o, const DnScales& sc, 
     v16i cn = t < 3 ? __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a, o.b[t + 1], cx.magic, 0, 0, 0)
                     : __builtin_amdgcn_mfma_i32_32x32x32_i8(on.a, on.b[0], cx.magic, 0, 0, 0);
     anchor(cn, c);
+    hook(t);
     const v16f d = __builtin_bit_cast(v16f, c);
 #pragma unroll
     for (int v = 0; v < 8; ++v) acc[t][v] = __builtin_fmaf(d[v], s[v], acc[t][v]);
@@ -390,25 +433,29 @@ __device__ __forceinline__ void kstep(const Src& src, int j, int KS, int wave, i
                                       const char* nxt, uint32_t cur_lds, uint32_t nxt_lds, Ops& X,
                                       Ops& Y, const ScalesT<GATEUP>& sc, ScalesT<GATEUP>& sn,
                                       Ctx& cx, v16i& c, v16f& cf, v16f& s, v16f (&acc)[4]) {
-  // The activation half of k-step j+1 (its weight half went out at the
-  // barrier of k-step j-1; k-steps 0 and 1 are copied whole by the prologue).
-  if (j >= 1 && j + 1 < KS) issue_acts<GATEUP>(src, j + 1, nxt_lds, wave, lane);
+  // The activation half of k-step j+1 goes out during block 0 (its weight
+  // half during block 3 of k-step j-1; k-steps 0 and 1 are copied whole by
+  // the prologue).
+  const bool acts = j >= 1 && j + 1 < KS;
   if constexpr (!GATEUP) cx.corr = dn_corr_a(sc.q);
   read_block<GATEUP>(cur, 1, wave, lane, Y);
-  compute_block(X, sc, 0, Y, sc, 1, false, cx, lane, c, cf, s, acc);
+  compute_block(X, sc, 0, Y, sc, 1, false, cx, lane, c, cf, s, acc, [&](int t) {
+    if (acts) issue_acts_part<GATEUP>(src, j + 1, nxt_lds, wave, lane, t);
+  });
   read_block<GATEUP>(cur, 2, wave, lane, X);
   compute_block(Y, sc, 1, X, sc, 2, false, cx, lane, c, cf, s, acc);
   read_block<GATEUP>(cur, 3, wave, lane, Y);
   compute_block(X, sc, 2, Y, sc, 3, false, cx, lane, c, cf, s, acc);
-  if (j + 1 < KS) {
-    // k-step j+1 has landed for every wavefront, and every wavefront has read
-    // all of k-step j: its buffer takes k-step j+2.
-    wait_copies_barrier_0();
-    if (j + 2 < KS) issue_weights<GATEUP>(src, j + 2, cur_lds, wave);
-  }
+  // k-step j+1 has landed for every wavefront, and every wavefront has read
+  // all of k-step j: its buffer takes k-step j+2 (the weight half, during
+  // block 3).
+  if (j + 1 < KS) wait_copies_barrier_0();
+  const bool weights = j + 2 < KS;
   read_block<GATEUP>(nxt, 0, wave, lane, X);
   read_scales(nxt, wave, lane, sn);
-  compute_block(Y, sc, 3, X, sn, 0, true, cx, lane, c, cf, s, acc);
+  compute_block(Y, sc, 3, X, sn, 0, true, cx, lane, c, cf, s, acc, [&](int t) {
+    if (weights) issue_weights_part<GATEUP>(src, j + 2, cur_lds, wave, t);
+  });
 }
 
 // Split-K: the correction operand of the blocks a split wavefront computes
@@ -440,17 +487,19 @@ __device__ __forceinline__ void kstep_split2(const Src& src, int j, int KS, int 
                                              uint32_t nxt_lds, Ops& X, Ops& Y, const ScalesT<GATEUP>& sc,
                                              ScalesT<GATEUP>& sn, Ctx& cx, v16i& c, v16f& cf, v16f& s,
                                              v16f (&acc)[4]) {
-  if (j >= 1 && j + 1 < KS) issue_acts<GATEUP>(src, j + 1, nxt_lds, wave, lane);
+  const bool acts = j >= 1 && j + 1 < KS;
   if constexpr (!GATEUP) cx.corr = dn_corr_split<2>(sc.q, lane, si);
   read_block<GATEUP>(cur, si + 2, wave, lane, Y);
-  compute_block(X, sc, si, Y, sc, si + 2, false, cx, lane, c, cf, s, acc);
-  if (j + 1 < KS) {
-    wait_copies_barrier_0();
-    if (j + 2 < KS) issue_weights<GATEUP>(src, j + 2, cur_lds, wave);
-  }
+  compute_block(X, sc, si, Y, sc, si + 2, false, cx, lane, c, cf, s, acc, [&](int t) {
+    if (acts) issue_acts_part<GATEUP>(src, j + 1, nxt_lds, wave, lane, t);
+  });
+  if (j + 1 < KS) wait_copies_barrier_0();
+  const bool weights = j + 2 < KS;
   read_block<GATEUP>(nxt, si, wave, lane, X);
   read_scales(nxt, wave, lane, sn);
-  compute_block(Y, sc, si + 2, X, sn, si, true, cx, lane, c, cf, s, acc);
+  compute_block(Y, sc, si + 2, X, sn, si, true, cx, lane, c, cf, s, acc, [&](int t) {
+    if (weights) issue_weights_part<GATEUP>(src, j + 2, cur_lds, wave, t);
+  });
 }
 
 // One-row-group tiles (at most 32 rows): the four wavefronts split every
