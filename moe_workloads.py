@@ -26,6 +26,12 @@ Expert weights are drawn as N(0, 0.02) in fp32 and packed as Q8_0: per
 (34 bytes, no padding), rows of ``in/32`` blocks.  The packing rule used here
 (scale = fp16(amax/127), code = clamp(rint(w/scale))) is input preparation
 only: both sides read the same bytes, so any rule would do.
+
+Workloads with ``fmt="q4_k"`` pack the same draws as Q4_K (the other MMQ
+weight format issue #406 names): per 256 values {binary16 d, binary16 dmin,
+12 bytes of 6-bit sub-block scales and mins, 128 bytes of 4-bit codes}
+(144 bytes), a value being d*sc*q - dmin*m for its 32-value sub-block.  The
+choice of d, dmin, sc, m and q below is again input preparation only.
 """
 
 from __future__ import annotations
@@ -39,6 +45,8 @@ import numpy as np
 
 Q8_BLOCK = 32          # elements per Q8_0 block
 Q8_BLOCK_BYTES = 34    # fp16 scale + 32 int8 codes
+Q4K_VALUES = 256       # elements per Q4_K super-block
+Q4K_BYTES = 144        # fp16 d, fp16 dmin, 12 scale bytes, 128 code bytes
 
 ROLE_X, ROLE_ROUTER, ROLE_BIAS_PERM, ROLE_SHARED_GATE = 0, 1, 2, 3
 ROLE_GATE, ROLE_UP, ROLE_DOWN = 4, 5, 6
@@ -63,6 +71,7 @@ class Workload:
     shape: LayerShape
     n_layers: int = 1
     description: str = ""
+    fmt: str = "q8_0"      # expert weight format: "q8_0" or "q4_k"
 
 
 OLMOE = LayerShape(d=2048, n_experts=64, top_k=8, ffn=1024)
@@ -85,6 +94,11 @@ WORKLOADS = {
     # chunks on the 35B-A3B shape (same layer seeds as a3b_n512)
     "a3b_n2048": Workload("a3b_n2048", 4, 2048, A3B,
                           description="35B-A3B-shaped layer, logical batch 2048 (ubatch-512 chunking)"),
+    # the OLMoE and 35B-A3B layers with their experts in Q4_K
+    "olmoe_n2048_q4k": Workload("olmoe_n2048_q4k", 2, 2048, OLMOE, fmt="q4_k",
+                                description="OLMoE-shaped layer, pp2048, Q4_K experts"),
+    "a3b_n512_q4k": Workload("a3b_n512_q4k", 4, 512, A3B, fmt="q4_k",
+                             description="35B-A3B-shaped layer, ubatch 512, Q4_K experts"),
 }
 
 
@@ -113,6 +127,79 @@ def pack_q8_0(w: np.ndarray) -> np.ndarray:
     return out.reshape(rows, nb * Q8_BLOCK_BYTES)
 
 
+def q4k_parts(w: np.ndarray):
+    """Choose the Q4_K fields of an fp32 matrix [rows][cols] (cols % 256 == 0):
+    returns d, dmin (fp16 [rows][cols/256]), sc, m (uint8 [rows][cols/32], 0..63)
+    and q (uint8 [rows][cols], 0..15).  Per 32-value sub-block the codes span
+    [min(block, 0), max(block, 0)] in 15 steps; d and dmin take the largest
+    sub-block step and offset over 63."""
+    w = np.asarray(w, dtype=np.float32)
+    rows, cols = w.shape
+    assert cols % Q4K_VALUES == 0
+    nsb = cols // Q4K_VALUES
+    sb = w.reshape(rows, nsb, 8, 32).astype(np.float64)
+    lo = np.minimum(sb.min(axis=3), 0.0)
+    hi = np.maximum(sb.max(axis=3), 0.0)
+    step = (hi - lo) / 15.0
+    off = -lo
+    d16 = (step.max(axis=2) / 63.0).astype(np.float16)
+    dmin16 = (off.max(axis=2) / 63.0).astype(np.float16)
+    d = d16.astype(np.float64)[:, :, None]
+    dmin = dmin16.astype(np.float64)[:, :, None]
+    sc = np.clip(np.rint(np.divide(step, d, out=np.zeros_like(step), where=d > 0)), 0, 63)
+    m = np.clip(np.rint(np.divide(off, dmin, out=np.zeros_like(off), where=dmin > 0)), 0, 63)
+    unit = (d * sc)[..., None]
+    base = (dmin * m)[..., None]
+    q = np.clip(np.rint(np.divide(sb + base, unit, out=np.zeros_like(sb), where=unit > 0)), 0, 15)
+    return (d16, dmin16, sc.astype(np.uint8).reshape(rows, nsb * 8), m.astype(np.uint8).reshape(rows, nsb * 8),
+            q.astype(np.uint8).reshape(rows, cols))
+
+
+def pack_q4_k(w: np.ndarray) -> np.ndarray:
+    """Pack an fp32 matrix [rows][cols] (cols % 256 == 0) into Q4_K bytes
+    [rows][cols/256*144]."""
+    d16, dmin16, sc, m, q = q4k_parts(w)
+    rows, cols = q.shape
+    nsb = cols // Q4K_VALUES
+    sc = sc.reshape(rows, nsb, 8).astype(np.uint16)
+    m = m.reshape(rows, nsb, 8).astype(np.uint16)
+    out = np.zeros((rows, nsb, Q4K_BYTES), dtype=np.uint8)
+    out[:, :, 0:2] = d16.view(np.uint8).reshape(rows, nsb, 2)
+    out[:, :, 2:4] = dmin16.view(np.uint8).reshape(rows, nsb, 2)
+    # scale bytes: 0..3 = sc_j (6 bits) | high 2 bits of sc_{j+4} << 6;
+    # 4..7 = m_j | high 2 bits of m_{j+4} << 6; 8..11 = low 4 bits of
+    # sc_{j+4} | low 4 bits of m_{j+4} << 4
+    out[:, :, 4:8] = (sc[:, :, 0:4] | ((sc[:, :, 4:8] >> 4) << 6)).astype(np.uint8)
+    out[:, :, 8:12] = (m[:, :, 0:4] | ((m[:, :, 4:8] >> 4) << 6)).astype(np.uint8)
+    out[:, :, 12:16] = ((sc[:, :, 4:8] & 15) | ((m[:, :, 4:8] & 15) << 4)).astype(np.uint8)
+    # code bytes: byte 32c + i = code i of sub-block 2c (low nibble) and of
+    # sub-block 2c + 1 (high nibble)
+    qs = q.reshape(rows, nsb, 4, 2, 32)
+    out[:, :, 16:] = (qs[:, :, :, 0, :] | (qs[:, :, :, 1, :] << 4)).reshape(rows, nsb, 128)
+    return out.reshape(rows, nsb * Q4K_BYTES)
+
+
+def q4k_represented(w: np.ndarray) -> np.ndarray:
+    """The values the Q4_K fields chosen for w stand for, d*sc*q - dmin*m in
+    fp64 [rows][cols] (from the fields, not from the packed bytes)."""
+    d16, dmin16, sc, m, q = q4k_parts(w)
+    rows, cols = q.shape
+    nsb = cols // Q4K_VALUES
+    d = np.repeat(d16.astype(np.float64), 8, axis=1)
+    dmin = np.repeat(dmin16.astype(np.float64), 8, axis=1)
+    unit = np.repeat(d * sc, 32, axis=1)
+    base = np.repeat(dmin * m, 32, axis=1)
+    return unit * q.astype(np.float64) - base
+
+
+def pack_weights(w: np.ndarray, fmt: str) -> np.ndarray:
+    return pack_q4_k(w) if fmt == "q4_k" else pack_q8_0(w)
+
+
+def row_bytes(fmt: str, in_dim: int) -> int:
+    return in_dim // Q4K_VALUES * Q4K_BYTES if fmt == "q4_k" else in_dim // Q8_BLOCK * Q8_BLOCK_BYTES
+
+
 def unpack_q8_0(b: np.ndarray, cols: int):
     """Split Q8_0 bytes [rows][cols/32*34] into (codes int8 [rows][cols],
     scales fp16 [rows][cols/32])."""
@@ -136,6 +223,7 @@ class LayerWeights:
     sh_up_q8: Optional[np.ndarray] = None     # uint8 [Fs][d/32*34]
     sh_down_q8: Optional[np.ndarray] = None   # uint8 [d][Fs/32*34]
     sh_gate_vec: Optional[np.ndarray] = None  # fp32 [d]
+    fmt: str = "q8_0"    # format of the expert rows above (the *_q8 arrays hold Q4_K rows for "q4_k")
 
 
 def _normal(rng: np.random.Generator, shape, std: float) -> np.ndarray:
@@ -151,19 +239,20 @@ def _cache_path(tag: str) -> Optional[str]:
 
 
 def make_layer(shape: LayerShape, cfg_id: int, layer: int = 0,
-               n_experts_override: Optional[int] = None) -> LayerWeights:
+               n_experts_override: Optional[int] = None, fmt: str = "q8_0") -> LayerWeights:
     """Draw one layer's weights.  Expert e of role r always comes from
-    ``rng_for(cfg_id, layer, r, e)`` so a subset of experts can be drawn alone."""
+    ``rng_for(cfg_id, layer, r, e)`` so a subset of experts can be drawn alone;
+    the expert rows are packed in ``fmt`` ("q8_0" or "q4_k")."""
     E = shape.n_experts if n_experts_override is None else n_experts_override
     d, F, Fs = shape.d, shape.ffn, shape.shared_ffn
-    tag = f"layer_c{cfg_id}_l{layer}_d{d}_e{E}_f{F}_s{Fs}_z{shape.zipf_bias}"
+    tag = f"layer_c{cfg_id}_l{layer}_d{d}_e{E}_f{F}_s{Fs}_z{shape.zipf_bias}" + ("" if fmt == "q8_0" else "_" + fmt)
     cp = _cache_path(tag)
     if cp and os.path.exists(cp):
         z = np.load(cp, allow_pickle=False)
         get = lambda k: (z[k] if k in z.files else None)
         return LayerWeights(shape, z["router_w"], get("router_bias"), z["gate_q8"], z["up_q8"],
                             z["down_q8"], get("sh_gate_q8"), get("sh_up_q8"), get("sh_down_q8"),
-                            get("sh_gate_vec"))
+                            get("sh_gate_vec"), fmt)
 
     router_w = _normal(rng_for(cfg_id, layer, ROLE_ROUTER), (E, d), 0.02)
     router_bias = None
@@ -172,21 +261,20 @@ def make_layer(shape: LayerShape, cfg_id: int, layer: int = 0,
         # bias_e = -s * ln(rank_e), rank_e in 1..E.
         perm = rng_for(cfg_id, layer, ROLE_BIAS_PERM).permutation(E)
         router_bias = (-shape.zipf_bias * np.log(perm.astype(np.float64) + 1.0)).astype(np.float32)
-    nbd = d // Q8_BLOCK
-    nbf = F // Q8_BLOCK
-    gate = np.empty((E, F, nbd * Q8_BLOCK_BYTES), np.uint8)
-    up = np.empty((E, F, nbd * Q8_BLOCK_BYTES), np.uint8)
-    down = np.empty((E, d, nbf * Q8_BLOCK_BYTES), np.uint8)
+    pack = lambda w: pack_weights(w, fmt)
+    gate = np.empty((E, F, row_bytes(fmt, d)), np.uint8)
+    up = np.empty((E, F, row_bytes(fmt, d)), np.uint8)
+    down = np.empty((E, d, row_bytes(fmt, F)), np.uint8)
     for e in range(E):
-        gate[e] = pack_q8_0(_normal(rng_for(cfg_id, layer, ROLE_GATE, e), (F, d), 0.02))
-        up[e] = pack_q8_0(_normal(rng_for(cfg_id, layer, ROLE_UP, e), (F, d), 0.02))
-        down[e] = pack_q8_0(_normal(rng_for(cfg_id, layer, ROLE_DOWN, e), (d, F), 0.02))
-    lw = LayerWeights(shape, router_w, router_bias, gate, up, down)
+        gate[e] = pack(_normal(rng_for(cfg_id, layer, ROLE_GATE, e), (F, d), 0.02))
+        up[e] = pack(_normal(rng_for(cfg_id, layer, ROLE_UP, e), (F, d), 0.02))
+        down[e] = pack(_normal(rng_for(cfg_id, layer, ROLE_DOWN, e), (d, F), 0.02))
+    lw = LayerWeights(shape, router_w, router_bias, gate, up, down, fmt=fmt)
     if Fs:
         se = shape.n_experts
-        lw.sh_gate_q8 = pack_q8_0(_normal(rng_for(cfg_id, layer, ROLE_GATE, se), (Fs, d), 0.02))
-        lw.sh_up_q8 = pack_q8_0(_normal(rng_for(cfg_id, layer, ROLE_UP, se), (Fs, d), 0.02))
-        lw.sh_down_q8 = pack_q8_0(_normal(rng_for(cfg_id, layer, ROLE_DOWN, se), (d, Fs), 0.02))
+        lw.sh_gate_q8 = pack(_normal(rng_for(cfg_id, layer, ROLE_GATE, se), (Fs, d), 0.02))
+        lw.sh_up_q8 = pack(_normal(rng_for(cfg_id, layer, ROLE_UP, se), (Fs, d), 0.02))
+        lw.sh_down_q8 = pack(_normal(rng_for(cfg_id, layer, ROLE_DOWN, se), (d, Fs), 0.02))
         lw.sh_gate_vec = _normal(rng_for(cfg_id, layer, ROLE_SHARED_GATE), (d,), 0.02)
     if cp:
         arrs = {k: v for k, v in dataclasses.asdict(lw).items() if isinstance(v, np.ndarray)}
@@ -201,7 +289,7 @@ def make_tokens(cfg_id: int, n_tokens: int, d: int, layer: int = 0) -> np.ndarra
 
 def workload_layer(name: str, layer: int = 0) -> LayerWeights:
     w = WORKLOADS[name]
-    return make_layer(w.shape, w.cfg_id, layer)
+    return make_layer(w.shape, w.cfg_id, layer, fmt=w.fmt)
 
 
 def workload_tokens(name: str, n_tokens: Optional[int] = None) -> np.ndarray:
@@ -210,16 +298,15 @@ def workload_tokens(name: str, n_tokens: Optional[int] = None) -> np.ndarray:
 
 
 def random_shape_case(seed: int, d: int, E: int, k: int, F: int, Fs: int = 0,
-                      norm: bool = False, zipf: float = 0.0):
+                      norm: bool = False, zipf: float = 0.0, fmt: str = "q8_0"):
     """A small arbitrary-shape case for edge-case tests (cfg id 100 + seed)."""
     shape = LayerShape(d=d, n_experts=E, top_k=k, ffn=F, shared_ffn=Fs,
                        norm_topk_prob=norm, zipf_bias=zipf)
-    return shape, make_layer(shape, 100 + seed)
+    return shape, make_layer(shape, 100 + seed, fmt=fmt)
 
 
-def expert_bytes(shape: LayerShape) -> int:
-    per = (2 * shape.ffn * shape.d + shape.d * shape.ffn) // Q8_BLOCK * Q8_BLOCK_BYTES
-    return per
+def expert_bytes(shape: LayerShape, fmt: str = "q8_0") -> int:
+    return 2 * shape.ffn * row_bytes(fmt, shape.d) + shape.d * row_bytes(fmt, shape.ffn)
 
 
 def describe(name: str) -> dict:
@@ -229,4 +316,5 @@ def describe(name: str) -> dict:
             "top_k": s.top_k, "ffn": s.ffn, "shared_ffn": s.shared_ffn,
             "norm_topk_prob": bool(s.norm_topk_prob), "n_layers": w.n_layers,
             "router_bias": ("zipf(%.1f)" % s.zipf_bias) if s.zipf_bias else "none",
-            "weights": "Q8_0 (int8, 32-elem blocks, fp16 scale)"}
+            "weights": ("Q4_K (4-bit codes, 256-elem super-blocks, 6-bit sub-block scales and mins)"
+                        if w.fmt == "q4_k" else "Q8_0 (int8, 32-elem blocks, fp16 scale)")}

@@ -26,6 +26,8 @@
 
 #define QB 32
 #define QBYTES 34
+#define Q4K_VALUES 256 /* values per Q4_K super-block */
+#define Q4K_BYTES 144  /* bytes per Q4_K super-block */
 
 /* ---------------------------------------------------------------- fp16 */
 /* IEEE 754 binary16 decoding: sign, 5-bit exponent (bias 15), 10-bit fraction. */
@@ -246,26 +248,74 @@ void ora_q8_block_sums(const int8_t* qa, int32_t m, const uint8_t* w, int32_t n,
     }
 }
 
+/* ------------------------------------------------------------- Q4_K */
+/* Scale and min of sub-block j from the 12 packed bytes (moe_oracle.h). */
+static void q4k_scale_min(const uint8_t* s12, int j, int* sc, int* m) {
+  if (j < 4) {
+    *sc = s12[j] & 63;
+    *m = s12[j + 4] & 63;
+  } else {
+    *sc = (s12[j + 4] & 15) | ((s12[j - 4] >> 6) << 4);
+    *m = (s12[j + 4] >> 4) | ((s12[j] >> 6) << 4);
+  }
+}
+
+/* Value i (0..255) of a super-block, dequantised in fp64. */
+static double q4k_value(const uint8_t* blk, int i) {
+  const double d = (double)half_bits_to_float((uint16_t)(blk[0] | (blk[1] << 8)));
+  const double dmin = (double)half_bits_to_float((uint16_t)(blk[2] | (blk[3] << 8)));
+  const int j = i / 32, t = i % 32;
+  int sc, m;
+  q4k_scale_min(blk + 4, j, &sc, &m);
+  const uint8_t byte = blk[16 + 32 * (j / 2) + t];
+  const int q = (j & 1) ? (byte >> 4) : (byte & 15);
+  return d * (double)sc * (double)q - dmin * (double)m;
+}
+
+void ora_q4k_dequant(const uint8_t* w_row, int32_t in_dim, double* out) {
+  for (int32_t i = 0; i < in_dim; ++i)
+    out[i] = q4k_value(w_row + (int64_t)(i / Q4K_VALUES) * Q4K_BYTES, i % Q4K_VALUES);
+}
+
+/* Q4_K MMQ (#406 "References"): the product of the dequantised activation
+ * and weight rows, written as its definition. */
+double ora_q4k_dot(const int8_t* qa, const uint16_t* sa16, const uint8_t* w_row, int32_t in_dim) {
+  double acc = 0.0;
+  for (int32_t i = 0; i < in_dim; ++i) {
+    const double a = (double)half_bits_to_float(sa16[i / QB]) * (double)qa[i];
+    acc += a * q4k_value(w_row + (int64_t)(i / Q4K_VALUES) * Q4K_BYTES, i % Q4K_VALUES);
+  }
+  return acc;
+}
+
+/* Bytes of one weight row of in_dim values and the dot product of format fmt. */
+static int64_t row_bytes_of(int32_t fmt, int32_t in_dim) {
+  return fmt == ORA_FMT_Q4_K ? (int64_t)(in_dim / Q4K_VALUES) * Q4K_BYTES : (int64_t)(in_dim / QB) * QBYTES;
+}
+static double wdot(int32_t fmt, const int8_t* qa, const uint16_t* sa16, const uint8_t* w_row, int32_t in_dim) {
+  return fmt == ORA_FMT_Q4_K ? ora_q4k_dot(qa, sa16, w_row, in_dim) : ora_q8_dot(qa, sa16, w_row, in_dim / QB);
+}
+
 /* ------------------------------------------------------------- expert */
 /* Routed-expert gate/up/down (#129 opening paragraph): h = silu(gate) * up,
  * requantised per 32 for the int8 down GEMM; y is the unweighted partial. */
-void ora_expert_ffn(int32_t d, int32_t ffn, const int8_t* xq, const uint16_t* xs,
-                    const uint8_t* gate, const uint8_t* up, const uint8_t* down, double* y,
-                    int8_t* hq, uint16_t* hs, double* h) {
-  const int32_t nbd = d / QB, nbf = ffn / QB;
-  const int64_t row_d = (int64_t)nbd * QBYTES, row_f = (int64_t)nbf * QBYTES;
+void ora_expert_ffn_fmt(int32_t fmt, int32_t d, int32_t ffn, const int8_t* xq, const uint16_t* xs,
+                        const uint8_t* gate, const uint8_t* up, const uint8_t* down, double* y,
+                        int8_t* hq, uint16_t* hs, double* h) {
+  const int32_t nbf = ffn / QB;
+  const int64_t row_d = row_bytes_of(fmt, d), row_f = row_bytes_of(fmt, ffn);
   float* hf = (float*)malloc(sizeof(float) * (size_t)ffn);
   int8_t* q = (int8_t*)malloc((size_t)ffn);
   uint16_t* sc = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)nbf);
   for (int32_t i = 0; i < ffn; ++i) {
-    double g = ora_q8_dot(xq, xs, gate + i * row_d, nbd);
-    double u = ora_q8_dot(xq, xs, up + i * row_d, nbd);
+    double g = wdot(fmt, xq, xs, gate + i * row_d, d);
+    double u = wdot(fmt, xq, xs, up + i * row_d, d);
     double hv = g / (1.0 + exp(-g)) * u;
     if (h) h[i] = hv;
     hf[i] = (float)hv;
   }
   ora_quantize_q8(hf, ffn, q, sc);
-  for (int32_t j = 0; j < d; ++j) y[j] = ora_q8_dot(q, sc, down + j * row_f, nbf);
+  for (int32_t j = 0; j < d; ++j) y[j] = wdot(fmt, q, sc, down + j * row_f, ffn);
   if (hq) memcpy(hq, q, (size_t)ffn);
   if (hs) memcpy(hs, sc, sizeof(uint16_t) * (size_t)nbf);
   free(hf);
@@ -273,10 +323,18 @@ void ora_expert_ffn(int32_t d, int32_t ffn, const int8_t* xq, const uint16_t* xs
   free(sc);
 }
 
+void ora_expert_ffn(int32_t d, int32_t ffn, const int8_t* xq, const uint16_t* xs,
+                    const uint8_t* gate, const uint8_t* up, const uint8_t* down, double* y,
+                    int8_t* hq, uint16_t* hs, double* h) {
+  ora_expert_ffn_fmt(ORA_FMT_Q8_0, d, ffn, xq, xs, gate, up, down, y, hq, hs, h);
+}
+
 static int dims_ok(const ora_dims* dm) {
   if (!dm) return 0;
-  if (dm->d <= 0 || dm->d % QB || dm->ffn <= 0 || dm->ffn % QB) return 0;
-  if (dm->shared_ffn < 0 || dm->shared_ffn % QB) return 0;
+  if (dm->weight_format != ORA_FMT_Q8_0 && dm->weight_format != ORA_FMT_Q4_K) return 0;
+  const int32_t unit = dm->weight_format == ORA_FMT_Q4_K ? Q4K_VALUES : QB;
+  if (dm->d <= 0 || dm->d % unit || dm->ffn <= 0 || dm->ffn % unit) return 0;
+  if (dm->shared_ffn < 0 || dm->shared_ffn % unit) return 0;
   if (dm->n_experts <= 0 || dm->top_k <= 0 || dm->top_k > dm->n_experts) return 0;
   return 1;
 }
@@ -297,9 +355,9 @@ int32_t ora_moe_tokens(const ora_dims* dm, const float* x, int32_t n_tokens,
   if (has_sh && (!sh_gate_q8 || !sh_up_q8 || !sh_down_q8 || !sh_gate_vec)) return -1;
   for (int32_t i = 0; i < n_list; ++i)
     if (token_list[i] < 0 || token_list[i] >= n_tokens) return -1;
-  const int32_t kk = k + has_sh;
-  const int64_t ex_gu = (int64_t)F * (d / QB) * QBYTES;  /* bytes per expert, gate or up */
-  const int64_t ex_dn = (int64_t)d * (F / QB) * QBYTES;  /* bytes per expert, down */
+  const int32_t kk = k + has_sh, fmt = dm->weight_format;
+  const int64_t ex_gu = (int64_t)F * row_bytes_of(fmt, d);  /* bytes per expert, gate or up */
+  const int64_t ex_dn = (int64_t)d * row_bytes_of(fmt, F);  /* bytes per expert, down */
 
 #pragma omp parallel for schedule(dynamic, 1)
   for (int32_t i = 0; i < n_list; ++i) {
@@ -318,14 +376,14 @@ int32_t ora_moe_tokens(const ora_dims* dm, const float* x, int32_t n_tokens,
     ora_quantize_q8(xt, d, xq, xs);
     for (int32_t s = 0; s < k; ++s) {
       int32_t e = ids[s];
-      ora_expert_ffn(d, F, xq, xs, gate_q8 + e * ex_gu, up_q8 + e * ex_gu, down_q8 + e * ex_dn,
-                     y + (int64_t)s * d, NULL, NULL, NULL);
+      ora_expert_ffn_fmt(fmt, d, F, xq, xs, gate_q8 + e * ex_gu, up_q8 + e * ex_gu, down_q8 + e * ex_dn,
+                         y + (int64_t)s * d, NULL, NULL, NULL);
     }
     double gs = 0.0;
     if (has_sh) {
       ora_shared_gate(xt, 1, d, sh_gate_vec, &gs);
-      ora_expert_ffn(d, Fs, xq, xs, sh_gate_q8, sh_up_q8, sh_down_q8, y + (int64_t)k * d, NULL,
-                     NULL, NULL);
+      ora_expert_ffn_fmt(fmt, d, Fs, xq, xs, sh_gate_q8, sh_up_q8, sh_down_q8, y + (int64_t)k * d, NULL,
+                         NULL, NULL);
     }
     /* #129 "Scope": slot order k = 0..na-1, then the shared row. */
     for (int32_t j = 0; j < d; ++j) {
@@ -359,9 +417,9 @@ int32_t ora_moe_grouped(const ora_dims* dm, const float* x, int32_t n_tokens,
   const int32_t d = dm->d, E = dm->n_experts, k = dm->top_k, F = dm->ffn, Fs = dm->shared_ffn;
   const int has_sh = Fs > 0;
   if (has_sh && (!sh_gate_q8 || !sh_up_q8 || !sh_down_q8 || !sh_gate_vec)) return -1;
-  const int32_t N = n_tokens, kk = k + has_sh;
-  const int64_t ex_gu = (int64_t)F * (d / QB) * QBYTES;
-  const int64_t ex_dn = (int64_t)d * (F / QB) * QBYTES;
+  const int32_t N = n_tokens, kk = k + has_sh, fmt = dm->weight_format;
+  const int64_t ex_gu = (int64_t)F * row_bytes_of(fmt, d);
+  const int64_t ex_dn = (int64_t)d * row_bytes_of(fmt, F);
 
   float* logits = (float*)malloc(sizeof(float) * (size_t)N * E + 1);
   int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)N * k + 1);
@@ -390,8 +448,8 @@ int32_t ora_moe_grouped(const ora_dims* dm, const float* x, int32_t n_tokens,
 #pragma omp parallel for schedule(dynamic, 1)
     for (int32_t p = start[g]; p < start[g + 1]; ++p) {
       int32_t t = tok_i[p], s = tok_k[p];
-      ora_expert_ffn(d, Fg, xq + (int64_t)t * d, xs + (int64_t)t * (d / QB), gw, uw, dw,
-                     part + ((int64_t)t * kk + s) * d, NULL, NULL, NULL);
+      ora_expert_ffn_fmt(fmt, d, Fg, xq + (int64_t)t * d, xs + (int64_t)t * (d / QB), gw, uw, dw,
+                         part + ((int64_t)t * kk + s) * d, NULL, NULL, NULL);
     }
   }
   for (int32_t t = 0; t < N; ++t)

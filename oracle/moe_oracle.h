@@ -31,6 +31,16 @@
  * Q8_0 weight rows: in/32 blocks of {binary16 scale, int8 q[32]} = 34 bytes,
  * little-endian, unpadded.  Activation blocks: int8 codes plus one binary16
  * scale per 32 values (the Q8_1-style block of #408).
+ *
+ * Q4_K weight rows (the other MMQ weight format #406 "References" names next
+ * to Q8_0; the k-quant super-block of the GGUF format): in/256 super-blocks of
+ * 144 bytes = {binary16 d, binary16 dmin, 12 bytes of 6-bit sub-block scales
+ * and mins, 128 bytes of 4-bit codes}.  Sub-block j (values 32j..32j+31)
+ * holds scale sc_j and min m_j: for j < 4, sc_j = byte j & 63 and m_j =
+ * byte j+4 & 63; for j >= 4, sc_j = (byte j+4 & 15) | (byte j-4 >> 6) << 4 and
+ * m_j = (byte j+4 >> 4) | (byte j >> 6) << 4 (bytes of the 12).  Code i of
+ * sub-block j is the low (j even) or high (j odd) nibble of code byte
+ * 32*(j/2) + i.  A value dequantises to d*sc_j*q - dmin*m_j.
  */
 #ifndef MOE_ORACLE_H
 #define MOE_ORACLE_H
@@ -41,13 +51,17 @@
 extern "C" {
 #endif
 
+#define ORA_FMT_Q8_0 0
+#define ORA_FMT_Q4_K 1
+
 typedef struct ora_dims {
-  int32_t d;              /* hidden size, multiple of 32 */
+  int32_t d;              /* hidden size, multiple of 32 (of 256 for Q4_K) */
   int32_t n_experts;      /* E */
   int32_t top_k;          /* k = na */
-  int32_t ffn;            /* routed expert intermediate size, multiple of 32 */
+  int32_t ffn;            /* routed expert intermediate size, multiple of 32 (of 256 for Q4_K) */
   int32_t shared_ffn;     /* shared expert intermediate size, 0 = none */
   int32_t norm_topk_prob; /* 1: renormalise the k selected weights */
+  int32_t weight_format;  /* ORA_FMT_Q8_0 or ORA_FMT_Q4_K: the expert weight rows */
 } ora_dims;
 
 /* IEEE binary16 <-> binary32, round to nearest even (n values). */
@@ -86,6 +100,15 @@ void ora_quantize_q8(const float* v, int64_t n_values, int8_t* q, uint16_t* scal
  * sum over blocks of exact int32 block sums times sa*sw, in fp64. */
 double ora_q8_dot(const int8_t* qa, const uint16_t* sa16, const uint8_t* w_row, int32_t n_blocks);
 
+/* One Q4_K weight row of in_dim values (in_dim % 256 == 0) dequantised to
+ * fp64: out[i] = d*sc_j*q_i - dmin*m_j. */
+void ora_q4k_dequant(const uint8_t* w_row, int32_t in_dim, double* out);
+
+/* Q8 activation row (codes + binary16 scales, 32 per block) against one Q4_K
+ * weight row of in_dim values: the dot product of the two dequantised rows,
+ * sum over i of (sa_b * qa_i) * (d*sc_j*q_i - dmin*m_j), in fp64. */
+double ora_q4k_dot(const int8_t* qa, const uint16_t* sa16, const uint8_t* w_row, int32_t in_dim);
+
 /* The exact int32 sums of one 32-block of an int8 MMQ product (#406
  * "References": Q8_0 MMQ): for activation rows i < m (32 codes each, qa
  * [m][32]) and Q8_0 weight rows j < n (row j starts at w + j * row_bytes),
@@ -102,6 +125,12 @@ void ora_q8_block_sums(const int8_t* qa, int32_t m, const uint8_t* w, int32_t n,
 void ora_expert_ffn(int32_t d, int32_t ffn, const int8_t* xq, const uint16_t* xs,
                     const uint8_t* gate, const uint8_t* up, const uint8_t* down, double* y,
                     int8_t* hq, uint16_t* hs, double* h);
+
+/* ora_expert_ffn with the expert weight rows in format fmt (ORA_FMT_*):
+ * gate/up rows of d values, down rows of ffn values. */
+void ora_expert_ffn_fmt(int32_t fmt, int32_t d, int32_t ffn, const int8_t* xq, const uint16_t* xs,
+                        const uint8_t* gate, const uint8_t* up, const uint8_t* down, double* y,
+                        int8_t* hq, uint16_t* hs, double* h);
 
 /* The per-token loop over the listed tokens (OpenMP over the list):
  * router, top-k, weights, quantiser, k experts (+ shared), combine in fp64.

@@ -18,7 +18,11 @@ _lib = None
 
 class OraDims(C.Structure):
     _fields_ = [("d", C.c_int32), ("n_experts", C.c_int32), ("top_k", C.c_int32),
-                ("ffn", C.c_int32), ("shared_ffn", C.c_int32), ("norm_topk_prob", C.c_int32)]
+                ("ffn", C.c_int32), ("shared_ffn", C.c_int32), ("norm_topk_prob", C.c_int32),
+                ("weight_format", C.c_int32)]
+
+
+FMT = {"q8_0": 0, "q4_k": 1}
 
 
 def _p(a: Optional[np.ndarray]):
@@ -43,6 +47,9 @@ def lib():
             "ora_quantize_q8": (None, [vp, i64, vp, vp]),
             "ora_q8_dot": (dbl, [vp, vp, vp, i32]),
             "ora_q8_block_sums": (None, [vp, i32, vp, i32, i64, i32, vp]),
+            "ora_q4k_dequant": (None, [vp, i32, vp]),
+            "ora_q4k_dot": (dbl, [vp, vp, vp, i32]),
+            "ora_expert_ffn_fmt": (None, [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "ora_expert_ffn": (None, [i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "ora_moe_tokens": (i32, [C.POINTER(OraDims), vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                      vp, vp, i32, vp, vp, vp, vp, vp]),
@@ -65,9 +72,9 @@ def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
 
 
-def dims_of(shape) -> OraDims:
+def dims_of(shape, fmt: str = "q8_0") -> OraDims:
     return OraDims(shape.d, shape.n_experts, shape.top_k, shape.ffn, shape.shared_ffn,
-                   1 if shape.norm_topk_prob else 0)
+                   1 if shape.norm_topk_prob else 0, FMT[fmt])
 
 
 def half_to_float(h: np.ndarray) -> np.ndarray:
@@ -161,7 +168,23 @@ def q8_block_sums(qa, w_rows, kblock: int) -> np.ndarray:
     return out
 
 
-def expert_ffn(d, ffn, xq, xs, gate, up, down):
+def q4k_dequant(w_rows, in_dim: int) -> np.ndarray:
+    """Q4_K rows (uint8 [rows][in_dim/256*144]) -> fp64 [rows][in_dim]."""
+    w_rows = _c(np.atleast_2d(w_rows), np.uint8)
+    out = np.empty((w_rows.shape[0], in_dim), np.float64)
+    for r in range(w_rows.shape[0]):
+        lib().ora_q4k_dequant(_p(w_rows[r]), in_dim, out[r].ctypes.data_as(C.c_void_p))
+    return out
+
+
+def q4k_dot(qa, sa16, w_row) -> float:
+    qa = _c(qa, np.int8)
+    sa16 = _c(sa16, np.uint16)
+    w_row = _c(w_row, np.uint8)
+    return lib().ora_q4k_dot(_p(qa), _p(sa16), _p(w_row), qa.size)
+
+
+def expert_ffn(d, ffn, xq, xs, gate, up, down, fmt: str = "q8_0"):
     xq = _c(xq, np.int8)
     xs = _c(xs, np.uint16)
     gate = _c(gate, np.uint8)
@@ -171,8 +194,8 @@ def expert_ffn(d, ffn, xq, xs, gate, up, down):
     hq = np.empty(ffn, np.int8)
     hs = np.empty(ffn // 32, np.uint16)
     h = np.empty(ffn, np.float64)
-    lib().ora_expert_ffn(d, ffn, _p(xq), _p(xs), _p(gate), _p(up), _p(down), _p(y), _p(hq), _p(hs),
-                         _p(h))
+    lib().ora_expert_ffn_fmt(FMT[fmt], d, ffn, _p(xq), _p(xs), _p(gate), _p(up), _p(down), _p(y), _p(hq),
+                             _p(hs), _p(h))
     return y, hq, hs, h
 
 
@@ -200,7 +223,7 @@ def moe_tokens(lw, x, tokens: Optional[Sequence[int]] = None, want_partial: bool
     ids = np.empty((n, s.top_k), np.int32)
     w = np.empty((n, s.top_k), np.float64)
     gs = np.empty(n, np.float64)
-    dm = dims_of(s)
+    dm = dims_of(s, lw.fmt)
     args = _weights_args(lw)
     rc = lib().ora_moe_tokens(C.byref(dm), _p(x), n_tokens, *[_p(a) for a in args], _p(tl), n,
                               _p(out), _p(part), _p(ids), _p(w), _p(gs))
@@ -216,7 +239,7 @@ def moe_grouped(lw, x) -> np.ndarray:
     s = lw.shape
     x = _c(x, np.float32)
     out = np.empty((x.shape[0], s.d), np.float64)
-    dm = dims_of(s)
+    dm = dims_of(s, lw.fmt)
     args = _weights_args(lw)
     rc = lib().ora_moe_grouped(C.byref(dm), _p(x), x.shape[0], *[_p(a) for a in args], _p(out))
     if rc != 0:

@@ -487,3 +487,121 @@ def test_rmsnorm_closed_forms():
     np.testing.assert_allclose((out ** 2).mean(1), ms / (ms + 1e-5), rtol=1e-13)
     np.testing.assert_allclose(out / x, np.broadcast_to((1 / np.sqrt(ms + 1e-5))[:, None], x.shape),
                                rtol=1e-13)
+
+
+# ------------------------------------------------------------------- Q4_K
+# Q4_K weight rows (#406 "References" names Q4_K MMQ next to Q8_0): the byte
+# layout is pinned by the packer's own field choice (numpy), the dot product
+# by an integer decomposition of the same sum, the expert by a numpy matmul
+# of dequantised rows.
+
+def _q4k_matrix(rng, rows, cols):
+    """Weights with the awkward cases: an all-zero sub-block, an all-positive
+    and an all-negative one, and rows of very different magnitude."""
+    w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    w[0, 0:32] = 0.0
+    w[0, 32:64] = np.abs(w[0, 32:64]) + 0.01
+    w[0, 64:96] = -np.abs(w[0, 64:96]) - 0.01
+    if rows > 2:
+        w[2] *= np.float32(40.0)
+    return w
+
+
+def test_q4k_dequant_matches_the_packed_fields():
+    rng = np.random.default_rng(40)
+    w = _q4k_matrix(rng, 5, 768)
+    b = mw.pack_q4_k(w)
+    assert b.shape == (5, 3 * 144)
+    dq = O.q4k_dequant(b, 768)
+    assert np.array_equal(dq, mw.q4k_represented(w))
+    # the represented values stay within a few code steps of the draw
+    d16, dmin16, sc, m, q = mw.q4k_parts(w)
+    step = np.repeat(np.repeat(d16.astype(np.float64), 8, axis=1) * sc, 32, axis=1)
+    slack = np.repeat(np.repeat(dmin16.astype(np.float64), 8, axis=1), 32, axis=1)
+    assert np.all(np.abs(dq - w) <= step + slack + 1e-9)
+    assert np.all(dq[0, 0:32] == 0.0)
+
+
+def test_q4k_layout_of_one_super_block_by_hand():
+    """One super-block written byte by byte: d = 1, dmin = 0.5, sub-block j
+    scale j+1 and min 2j (six-bit fields split as the format packs them), code
+    i of sub-block j equal to (i + j) % 16."""
+    blk = np.zeros(144, np.uint8)
+    blk[0:2] = np.array([1.0], np.float16).view(np.uint8)
+    blk[2:4] = np.array([0.5], np.float16).view(np.uint8)
+    sc = [j + 1 for j in range(8)]
+    m = [2 * j for j in range(8)]
+    sc[5], m[7] = 45, 63   # values that need the high two bits
+    for j in range(4):
+        blk[4 + j] = sc[j] | ((sc[j + 4] >> 4) << 6)
+        blk[8 + j] = m[j] | ((m[j + 4] >> 4) << 6)
+        blk[12 + j] = (sc[j + 4] & 15) | ((m[j + 4] & 15) << 4)
+    for c in range(4):
+        for i in range(32):
+            blk[16 + 32 * c + i] = ((i + 2 * c) % 16) | (((i + 2 * c + 1) % 16) << 4)
+    got = O.q4k_dequant(blk[None, :], 256)[0]
+    want = np.array([1.0 * sc[j] * ((i + j) % 16) - 0.5 * m[j] for j in range(8) for i in range(32)])
+    assert np.array_equal(got, want)
+
+
+def test_q4k_dot_integer_decomposition():
+    rng = np.random.default_rng(41)
+    d = 1024
+    w = _q4k_matrix(rng, 3, d)
+    b = mw.pack_q4_k(w)
+    d16, dmin16, sc, m, q = mw.q4k_parts(w)
+    x = (rng.standard_normal((1, d)) * 3).astype(np.float32)
+    qa, sa = O.quantize_q8(x)
+    qa, sa = qa[0], sa[0]
+    saf = sa.view(np.float16).astype(np.float64)
+    for r in range(3):
+        got = O.q4k_dot(qa, sa, b[r])
+        # per 32-block: sa * (d*sc * sum(qa*q) - dmin*m * sum(qa)), the sums in int64
+        cq = (qa.astype(np.int64) * q[r].astype(np.int64)).reshape(-1, 32).sum(1)
+        ca = qa.astype(np.int64).reshape(-1, 32).sum(1)
+        dd = np.repeat(d16[r].astype(np.float64), 8)
+        dm = np.repeat(dmin16[r].astype(np.float64), 8)
+        ref = float(np.sum(saf * (dd * sc[r] * cq - dm * m[r] * ca)))
+        assert abs(got - ref) <= 1e-12 * np.sum(np.abs(saf * (dd * sc[r] * cq) + saf * (dm * m[r] * ca))) + 1e-300
+    # a row whose codes are all zero leaves only the mins
+    w0 = np.full((1, 256), -0.05, np.float32)
+    b0 = mw.pack_q4_k(w0)
+    d0, dmin0, sc0, m0, q0 = mw.q4k_parts(w0)
+    assert not q0.any()
+    ref0 = -float(np.sum(saf[:8] * dmin0[0, 0].astype(np.float64) * m0[0] * qa[:256].astype(np.int64).reshape(8, 32).sum(1)))
+    assert O.q4k_dot(qa[:256], sa[:8], b0[0]) == pytest.approx(ref0, rel=1e-12, abs=1e-300)
+
+
+def test_q4k_expert_ffn_against_numpy():
+    rng = np.random.default_rng(42)
+    d, F = 512, 256
+    x = rng.standard_normal((1, d)).astype(np.float32)
+    xq, xs = O.quantize_q8(x)
+    G = mw.pack_q4_k((rng.standard_normal((F, d)) * 0.02).astype(np.float32))
+    U = mw.pack_q4_k((rng.standard_normal((F, d)) * 0.02).astype(np.float32))
+    D = mw.pack_q4_k((rng.standard_normal((d, F)) * 0.02).astype(np.float32))
+    y, hq, hs, h = O.expert_ffn(d, F, xq[0], xs[0], G, U, D, fmt="q4_k")
+    xd = xq[0].astype(np.float64) * np.repeat(xs[0].view(np.float16).astype(np.float64), 32)
+    g = O.q4k_dequant(G, d) @ xd
+    u = O.q4k_dequant(U, d) @ xd
+    np.testing.assert_allclose(h, g * scipy.special.expit(g) * u, rtol=1e-12, atol=1e-15)
+    hd = hq.astype(np.float64) * np.repeat(hs.view(np.float16).astype(np.float64), 32)
+    np.testing.assert_allclose(y, O.q4k_dequant(D, F) @ hd, rtol=1e-11, atol=1e-14)
+    # the same draws in Q8_0 give a different (but close) expert
+    y8, _, _, _ = O.expert_ffn(d, F, xq[0], xs[0], mw.pack_q8_0(O.q4k_dequant(G, d).astype(np.float32)),
+                               mw.pack_q8_0(O.q4k_dequant(U, d).astype(np.float32)),
+                               mw.pack_q8_0(O.q4k_dequant(D, F).astype(np.float32)))
+    assert np.linalg.norm(y8 - y) < 0.05 * np.linalg.norm(y)
+
+
+@pytest.mark.parametrize("case", [
+    dict(d=256, E=8, k=2, F=256),
+    dict(d=512, E=6, k=3, F=256, Fs=256, zipf=1.1, norm=True),
+])
+def test_q4k_grouped_equals_per_token_bitwise(case):
+    shape, lw = mw.random_shape_case(5, fmt="q4_k", **case)
+    assert lw.fmt == "q4_k" and lw.gate_q8.shape[-1] == case["d"] // 256 * 144
+    x = mw.make_tokens(105, 19, case["d"])
+    a = O.moe_tokens(lw, x)["out"]
+    b = O.moe_grouped(lw, x)
+    assert np.array_equal(a, b)
