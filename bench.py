@@ -77,13 +77,14 @@ def gemm_ops(shape, n_tokens):
     return gu, dn
 
 
-def stage_bytes(shape, n_tokens, counts):
+def stage_bytes(shape, n_tokens, counts, fmt="q8_0"):
     """Algorithmic HBM bytes per stage: what the method must read or write
-    once (weights of the experts the batch touches, activations, partials)."""
+    once (weights of the experts the batch touches, activations, partials).
+    Weight bytes per value: Q8_0 34/32, Q4_K 144/256."""
     d, F, k, E = shape.d, shape.ffn, shape.top_k, shape.n_experts
     kk = k + (1 if shape.shared_ffn else 0)
     touched = sum(1 for c in counts[:E] if c > 0)
-    q8 = 34.0 / 32.0
+    q8 = 144.0 / 256.0 if fmt == "q4_k" else 34.0 / 32.0
     gu_w = touched * 2 * F * d * q8 + (2 * shape.shared_ffn * d * q8 if shape.shared_ffn else 0)
     dn_w = touched * d * F * q8 + (d * shape.shared_ffn * q8 if shape.shared_ffn else 0)
     P = n_tokens * k + (n_tokens if shape.shared_ffn else 0)
@@ -102,7 +103,8 @@ def stage_bytes(shape, n_tokens, counts):
 # The sources each measured kernel is compiled from: a traffic summary is
 # valid only while their digest matches the one it records.
 KERNEL_SOURCES = {
-    "grouped_gemm": ("gemm.hip", "internal.h", "device_util.h"),
+    "grouped_gemm": ("gemm.hip", "gemm_common.h", "internal.h", "device_util.h"),
+    "grouped_gemm_q4k": ("gemm_q4k.hip", "gemm_common.h", "internal.h", "device_util.h"),
     "decode_gemv": ("decode.hip", "internal.h", "device_util.h"),
 }
 
@@ -451,7 +453,7 @@ def main():
         torch.cuda.synchronize()
         counts = np.diff(exp_start.cpu().numpy())
     gu_ops, dn_ops = gemm_ops(s, n_prof)
-    sb = stage_bytes(s, n_prof, counts)
+    sb = stage_bytes(s, n_prof, counts, wl.fmt)
     if decode:
         # decode stages: the router launch also quantises; the gate/up launch
         # also routes
@@ -476,15 +478,22 @@ def main():
                                                                 "combine"))
                                             / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     else:
-        roofline = {"bound": "mfma", "kernel": "grouped_gemm_kernel<true> (grouped gate/up + SwiGLU + requantise)",
+        q4k = wl.fmt == "q4_k"
+        # Q4_K adds one min-term MFMA (about 34 cycles) per tile and k-step of 4 blocks
+        pipe_roof = INT8_PEAK_TOPS * 32 / (3 * 32 + 34 / 4) if q4k else PIPE_ROOF_TOPS
+        roofline = {"bound": "mfma",
+                    "kernel": ("grouped_gemm_q4k_kernel<true> (grouped Q4_K gate/up + SwiGLU + requantise)" if q4k
+                               else "grouped_gemm_kernel<true> (grouped gate/up + SwiGLU + requantise)"),
                     "achieved": round(gu_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
                     "frac": round(gu_tops / INT8_PEAK_TOPS, 4),
-                    "traffic": (read_traffic("gateup_olmoe_n2048")
-                                if args.workload == "olmoe_n2048" and not chunk else None),
+                    "traffic": (read_traffic(f"gateup_{args.workload}", "grouped_gemm_q4k" if q4k else "grouped_gemm")
+                                if not chunk else None),
                     "algorithmic_ops_per_launch": gu_ops, "avg_launch_us": round(gu_us, 2),
-                    "pipe_roof": {"peak": round(PIPE_ROOF_TOPS, 1), "unit": "TOP/s",
-                                  "frac": round(gu_tops / PIPE_ROOF_TOPS, 4),
-                                  "why": "3 MFMAs per 32-block per 32x32 tile (int8, conversion, scale)"}}
+                    "pipe_roof": {"peak": round(pipe_roof, 1), "unit": "TOP/s",
+                                  "frac": round(gu_tops / pipe_roof, 4),
+                                  "why": ("3 MFMAs per 32-block per 32x32 tile (int8, conversion, scale) plus one "
+                                          "min-term MFMA per tile and k-step" if q4k else
+                                          "3 MFMAs per 32-block per 32x32 tile (int8, conversion, scale)")}}
     stages = {}
     for name in stage_names:
         us = stage_ms[name] * 1e3
@@ -516,7 +525,8 @@ def main():
                          "why": "untimed steps before the warmup, so that the timed steps run at the clock "
                                 "the GPU holds under this load rather than one still ramping up from idle"},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
-        "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights packed as Q8_0)",
+        "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights packed as %s)"
+                % ("Q4_K" if wl.fmt == "q4_k" else "Q8_0"),
         "config": {"workload": args.workload, **{k: v for k, v in mw.describe(args.workload).items()
                                                  if k != "workload"}},
         "grouped_gemm_int8_frac": round(gemm_frac, 4),

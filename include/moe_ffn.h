@@ -132,6 +132,38 @@ int moe_ffn_weights_create(const moe_ffn_dims* dims, const float* router_w,
                            const void* sh_down_q8, const float* sh_gate_vec, hipStream_t stream,
                            moe_ffn_weights** out);
 
+/* Expert weight formats of moe_ffn_weights_create_fmt. */
+#define MOE_FFN_FMT_Q8_0 0 /* 34-byte blocks of 32 {binary16 scale, int8 q[32]} */
+#define MOE_FFN_FMT_Q4_K 1 /* 144-byte super-blocks of 256, see below */
+
+/* moe_ffn_weights_create with the expert rows (routed and shared, gate, up
+ * and down) in `format`.  MOE_FFN_FMT_Q8_0 is moe_ffn_weights_create.
+ * MOE_FFN_FMT_Q4_K (#406 "References" names Q4_K beside Q8_0 among the
+ * formats of the int8 MMQ path): each row of n values is n/256 super-blocks
+ * of 144 bytes {binary16 d, binary16 dmin, 12 bytes of 6-bit sub-block
+ * scales sc_j and mins m_j, 128 bytes of 4-bit codes}, the k-quant
+ * super-block: weight i of sub-block j (32 values) is
+ * d * sc_j * q_i - dmin * m_j; sub-blocks 0-3 keep sc_j and m_j in the low 6
+ * bits of bytes j and j+4, sub-blocks 4-7 take the low (sc) or high (m)
+ * nibble of byte j+4 as the low 4 bits and the top 2 bits of byte j-4 (sc)
+ * or byte j (m) as the high 2; code i of sub-block j is the low (j even) or
+ * high (j odd) nibble of code byte 32*(j/2)+i.  Layouts: gate/up [E][F][d/256]
+ * super-blocks, down [E][d][F/256], shared [Fs][d/256] and [d][Fs/256].
+ * The expert products are then the int8 activation blocks dotted with the
+ * dequantised rows, per 32-block sa * (d * sc * C - dmin * m * A) with C the
+ * int32 code dot product and A the sum of the activation codes, summed in
+ * fp32.  Q4_K needs d_model, d_ffn and d_shared_ffn to be multiples of 256
+ * (else MOE_FFN_UNSUPPORTED), and rejects with MOE_FFN_UNSUPPORTED weights
+ * whose d * sc or dmin * m overflows binary16.  A Q4_K handle serves every
+ * prefill entry point; moe_ffn_decode and moe_ffn_dbg_block_sums return
+ * MOE_FFN_UNSUPPORTED for it.  Any other format is MOE_FFN_INVALID_ARG.  The
+ * other arguments and the ownership rules are those of moe_ffn_weights_create. */
+int moe_ffn_weights_create_fmt(const moe_ffn_dims* dims, int32_t format, const float* router_w,
+                               const float* router_bias, const void* gate, const void* up,
+                               const void* down, const void* sh_gate, const void* sh_up,
+                               const void* sh_down, const float* sh_gate_vec, hipStream_t stream,
+                               moe_ffn_weights** out);
+
 /* Release a handle (NULL is accepted).  The caller must ensure no enqueued
  * work still reads it. */
 int moe_ffn_weights_destroy(moe_ffn_weights* w);
@@ -241,7 +273,7 @@ int moe_ffn_prefill_profiled(const moe_ffn_weights* w, const float* x, int32_t n
  * 1 <= n_tokens <= 8, with the expert FFN run by one gathered launch per
  * stage in which each selected expert's weights are read once for all the
  * tokens that picked it.  Returns MOE_FFN_INVALID_ARG for n_tokens outside
- * [1, 8]. */
+ * [1, 8], MOE_FFN_UNSUPPORTED for Q4_K weights. */
 int moe_ffn_decode(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* out,
                    void* ws, size_t ws_bytes, const moe_ffn_routing* routing,
                    hipStream_t stream);

@@ -24,7 +24,7 @@ MOE_FFN_OUT_OF_MEMORY = -4
 MOE_FFN_HIP_ERROR = -5
 MOE_FFN_SCRATCH_TOO_SMALL = -6
 
-EXPORTED = ("moe_ffn_weights_create", "moe_ffn_weights_destroy", "moe_ffn_weights_dims",
+EXPORTED = ("moe_ffn_weights_create", "moe_ffn_weights_create_fmt", "moe_ffn_weights_destroy", "moe_ffn_weights_dims",
             "moe_ffn_workspace_size", "moe_ffn_workspace_size_for_dims", "moe_ffn_prefill", "moe_ffn_prefill_static", "moe_ffn_prefill_chunked", "moe_ffn_prefill_residual", "moe_ffn_prefill_profiled",
             "moe_ffn_decode",
             "moe_ffn_decode_profiled", "moe_ffn_combine",
@@ -63,6 +63,8 @@ def lib():
         sig = {
             "moe_ffn_weights_create": [C.POINTER(moe_ffn_dims), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        C.POINTER(vp)],
+            "moe_ffn_weights_create_fmt": [C.POINTER(moe_ffn_dims), i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                           C.POINTER(vp)],
             "moe_ffn_weights_destroy": [vp],
             "moe_ffn_weights_dims": [vp, C.POINTER(moe_ffn_dims)],
             "moe_ffn_workspace_size": [vp, i32, C.POINTER(sz)],
@@ -129,6 +131,22 @@ def moe_ffn_weights_create(dims: moe_ffn_dims, router_w, router_bias, gate_q8, u
                                       _ptr(up_q8), _ptr(down_q8), _ptr(sh_gate_q8), _ptr(sh_up_q8),
                                       _ptr(sh_down_q8), _ptr(sh_gate_vec), _stream(stream), C.byref(h))
     _check("moe_ffn_weights_create", rc)
+    return h.value
+
+
+FMT_Q8_0 = 0
+FMT_Q4_K = 1
+FORMATS = {"q8_0": FMT_Q8_0, "q4_k": FMT_Q4_K}
+
+
+def moe_ffn_weights_create_fmt(dims: moe_ffn_dims, fmt: int, router_w, router_bias, gate, up, down,
+                               sh_gate=None, sh_up=None, sh_down=None, sh_gate_vec=None, stream=None) -> int:
+    """moe_ffn_weights_create with the expert rows in format fmt (FMT_Q8_0 or FMT_Q4_K)."""
+    h = C.c_void_p()
+    rc = lib().moe_ffn_weights_create_fmt(C.byref(dims), int(fmt), _ptr(router_w), _ptr(router_bias), _ptr(gate),
+                                          _ptr(up), _ptr(down), _ptr(sh_gate), _ptr(sh_up), _ptr(sh_down),
+                                          _ptr(sh_gate_vec), _stream(stream), C.byref(h))
+    _check("moe_ffn_weights_create_fmt", rc)
     return h.value
 
 

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_ffn.so")
-SOURCES = ["api.hip", "repack.hip", "router.hip", "bucket.hip", "gemm.hip", "decode.hip", "combine.hip",
+SOURCES = ["api.hip", "repack.hip", "router.hip", "bucket.hip", "gemm.hip", "gemm_q4k.hip", "decode.hip", "combine.hip",
            "noalloc.hip"]
 ARCH = "gfx950"
 

@@ -258,9 +258,10 @@ int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, v
   GemmArgs a = gemm_args(W, L, base, n);
   a.reverse = reverse_tiles;
   HIP_TRY(mark(3));
-  HIP_TRY(launch_gateup(a, s));
+  const bool q4k = W->fmt == MOE_FFN_FMT_Q4_K;
+  HIP_TRY(q4k ? launch_gateup_q4k(a, s) : launch_gateup(a, s));
   HIP_TRY(mark(4));
-  HIP_TRY(launch_down(a, s));
+  HIP_TRY(q4k ? launch_down_q4k(a, s) : launch_down(a, s));
   HIP_TRY(mark(5));
   if (res)
     HIP_TRY(launch_combine_residual_rmsnorm(partial, w, dm.has_shared ? gs : nullptr, n, dm.k, kk, dm.d,
@@ -282,6 +283,7 @@ int run_decode(const moe_ffn_weights* W, const float* x, int32_t n, float* out, 
                size_t ws_bytes, const moe_ffn_routing* r, hipStream_t s, hipEvent_t* ev = nullptr) {
   if (!W || n < 1 || n > DECODE_MAX_TOKENS) return MOE_FFN_INVALID_ARG;
   if (!x || !out || !ws) return MOE_FFN_INVALID_ARG;
+  if (W->fmt != MOE_FFN_FMT_Q8_0) return MOE_FFN_UNSUPPORTED;  // the matvecs read Q8_0 planes only
   const Dims& dm = W->dm;
   const WsLayout L = ws_layout(dm, n);
   if (ws_bytes < L.total) return MOE_FFN_WORKSPACE_TOO_SMALL;
@@ -372,20 +374,34 @@ int moe_ffn_weights_create(const moe_ffn_dims* dims, const float* router_w,
                            const void* down_q8, const void* sh_gate_q8, const void* sh_up_q8,
                            const void* sh_down_q8, const float* sh_gate_vec, hipStream_t stream,
                            moe_ffn_weights** out) {
+  return moe_ffn_weights_create_fmt(dims, MOE_FFN_FMT_Q8_0, router_w, router_bias, gate_q8, up_q8, down_q8,
+                                    sh_gate_q8, sh_up_q8, sh_down_q8, sh_gate_vec, stream, out);
+}
+
+int moe_ffn_weights_create_fmt(const moe_ffn_dims* dims, int32_t format, const float* router_w,
+                               const float* router_bias, const void* gate, const void* up,
+                               const void* down, const void* sh_gate, const void* sh_up,
+                               const void* sh_down, const float* sh_gate_vec, hipStream_t stream,
+                               moe_ffn_weights** out) {
   if (!out) return MOE_FFN_INVALID_ARG;
   *out = nullptr;
+  if (format != MOE_FFN_FMT_Q8_0 && format != MOE_FFN_FMT_Q4_K) return MOE_FFN_INVALID_ARG;
   const int rc = check_dims(dims);
   if (rc != MOE_FFN_OK) return rc;
-  if (!router_w || !gate_q8 || !up_q8 || !down_q8) return MOE_FFN_INVALID_ARG;
+  const bool q4k = format == MOE_FFN_FMT_Q4_K;
+  if (q4k && (dims->d_model % Q4K_VALUES || dims->d_ffn % Q4K_VALUES || dims->d_shared_ffn % Q4K_VALUES))
+    return MOE_FFN_UNSUPPORTED;
+  if (!router_w || !gate || !up || !down) return MOE_FFN_INVALID_ARG;
   const bool has_sh = dims->d_shared_ffn > 0;
-  const bool any_sh = sh_gate_q8 || sh_up_q8 || sh_down_q8 || sh_gate_vec;
-  const bool all_sh = sh_gate_q8 && sh_up_q8 && sh_down_q8 && sh_gate_vec;
+  const bool any_sh = sh_gate || sh_up || sh_down || sh_gate_vec;
+  const bool all_sh = sh_gate && sh_up && sh_down && sh_gate_vec;
   if (has_sh ? !all_sh : any_sh) return MOE_FFN_INVALID_ARG;
 
   moe_ffn_weights* W = new (std::nothrow) moe_ffn_weights();
   if (!W) return MOE_FFN_OUT_OF_MEMORY;
   W->user = *dims;
   W->dm = make_dims(dims);
+  W->fmt = format;
   const Dims& dm = W->dm;
   if (hipGetDevice(&W->device) != hipSuccess ||
       hipDeviceGetAttribute(&W->n_cu, hipDeviceAttributeMultiprocessorCount, W->device) != hipSuccess ||
@@ -395,11 +411,13 @@ int moe_ffn_weights_create(const moe_ffn_dims* dims, const float* router_w,
     return MOE_FFN_HIP_ERROR;
   }
   W->has_bias = router_bias ? 1 : 0;
-  // [strips][k-steps][17 KiB (gate/up) or 18 KiB (down)] per expert (see internal.h)
-  W->gu_per_expert = (size_t)(dm.F_pad / GU_COLS) * (dm.d_pad / QB / KSTEP) * KSTEP_BYTES;
-  W->dn_per_expert = (size_t)(dm.d_pad / DN_COLS) * (dm.F_pad / QB / KSTEP) * DN_KSTEP_BYTES;
-  const size_t sh_gu = (size_t)(dm.Fs_pad / GU_COLS) * (dm.d_pad / QB / KSTEP) * KSTEP_BYTES;
-  const size_t sh_dn = (size_t)(dm.d_pad / DN_COLS) * (dm.Fs_pad / QB / KSTEP) * DN_KSTEP_BYTES;
+  // [strips][k-steps][k-step bytes] per expert (see internal.h)
+  const size_t gu_step = q4k ? Q4K_KSTEP_BYTES : KSTEP_BYTES;
+  const size_t dn_step = q4k ? Q4K_KSTEP_BYTES : DN_KSTEP_BYTES;
+  W->gu_per_expert = (size_t)(dm.F_pad / GU_COLS) * (dm.d_pad / QB / KSTEP) * gu_step;
+  W->dn_per_expert = (size_t)(dm.d_pad / DN_COLS) * (dm.F_pad / QB / KSTEP) * dn_step;
+  const size_t sh_gu = (size_t)(dm.Fs_pad / GU_COLS) * (dm.d_pad / QB / KSTEP) * gu_step;
+  const size_t sh_dn = (size_t)(dm.d_pad / DN_COLS) * (dm.Fs_pad / QB / KSTEP) * dn_step;
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -411,6 +429,7 @@ int moe_ffn_weights_create(const moe_ffn_dims* dims, const float* router_w,
   const size_t o_rb = take((size_t)dm.E * 4);
   const size_t o_sg = take((size_t)dm.d * 4);
   const size_t o_ex = take((size_t)dm.G * 4);
+  const size_t o_of = take(4);  // Q4_K repack overflow flag
   const size_t o_gu = take(W->gu_per_expert * dm.E);
   const size_t o_dn = take(W->dn_per_expert * dm.E);
   const size_t o_sgu = take(sh_gu), o_sdn = take(sh_dn);
@@ -424,12 +443,12 @@ int moe_ffn_weights_create(const moe_ffn_dims* dims, const float* router_w,
   W->router_bias = (float*)(b + o_rb);
   W->sh_gate_vec = (float*)(b + o_sg);
   W->dn_exp = (int32_t*)(b + o_ex);
+  int32_t* overflow = (int32_t*)(b + o_of);
   W->gu = (uint8_t*)(b + o_gu);
   W->dn = (uint8_t*)(b + o_dn);
   W->sh_gu = has_sh ? (uint8_t*)(b + o_sgu) : nullptr;
   W->sh_dn = has_sh ? (uint8_t*)(b + o_sdn) : nullptr;
 
-  const int nbd = dm.d / QB, nbf = dm.F / QB;
   hipError_t e = hipSuccess;
   if (e == hipSuccess) e = launch_transpose_router(router_w, dm.E, dm.d, dm.E64, W->router_wt, stream);
   if (e == hipSuccess)
@@ -438,36 +457,59 @@ int moe_ffn_weights_create(const moe_ffn_dims* dims, const float* router_w,
   if (e == hipSuccess)
     e = has_sh ? hipMemcpyAsync(W->sh_gate_vec, sh_gate_vec, (size_t)dm.d * 4, hipMemcpyDeviceToDevice, stream)
                : hipMemsetAsync(W->sh_gate_vec, 0, (size_t)dm.d * 4, stream);
-  if (e == hipSuccess)
-    e = launch_repack_q8((const uint8_t*)gate_q8, (const uint8_t*)up_q8, dm.E,
-                         (size_t)dm.F * nbd * Q8_BYTES, dm.F, nbd, 2, dm.F_pad / GU_COLS, dm.d_pad / QB,
-                         W->gu, W->gu_per_expert, nullptr, stream);
-  if (e == hipSuccess)
-    e = launch_scale_exponent((const uint8_t*)down_q8, dm.E, (size_t)dm.d * nbf * Q8_BYTES,
-                              (long)dm.d * nbf, W->dn_exp, stream);
-  if (e == hipSuccess)
-    e = launch_repack_q8((const uint8_t*)down_q8, (const uint8_t*)down_q8, dm.E,
-                         (size_t)dm.d * nbf * Q8_BYTES, dm.d, nbf, 4, dm.d_pad / DN_COLS, dm.F_pad / QB,
-                         W->dn, W->dn_per_expert, W->dn_exp, stream);
-  if (e == hipSuccess && has_sh) {
-    const int nbs = dm.Fs / QB;
-    e = launch_repack_q8((const uint8_t*)sh_gate_q8, (const uint8_t*)sh_up_q8, 1,
-                         (size_t)dm.Fs * nbd * Q8_BYTES, dm.Fs, nbd, 2, dm.Fs_pad / GU_COLS,
-                         dm.d_pad / QB, W->sh_gu, sh_gu, nullptr, stream);
+  if (q4k) {
+    // the down planes carry no rescaling exponent (the epilogue's 2^e is 1)
+    const int nsd = dm.d / Q4K_VALUES, nsf = dm.F / Q4K_VALUES;
+    const size_t row_d = (size_t)nsd * Q4K_BYTES, row_f = (size_t)nsf * Q4K_BYTES;
+    if (e == hipSuccess) e = hipMemsetAsync(W->dn_exp, 0, (size_t)dm.G * 4, stream);
+    if (e == hipSuccess) e = hipMemsetAsync(overflow, 0, 4, stream);
     if (e == hipSuccess)
-      e = launch_scale_exponent((const uint8_t*)sh_down_q8, 1, (size_t)dm.d * nbs * Q8_BYTES,
-                                (long)dm.d * nbs, W->dn_exp + dm.E, stream);
+      e = launch_repack_q4k((const uint8_t*)gate, (const uint8_t*)up, dm.E, (size_t)dm.F * row_d, dm.F, nsd, 2,
+                            dm.F_pad / GU_COLS, dm.d_pad / QB / KSTEP, W->gu, W->gu_per_expert, overflow, stream);
     if (e == hipSuccess)
-      e = launch_repack_q8((const uint8_t*)sh_down_q8, (const uint8_t*)sh_down_q8, 1,
-                           (size_t)dm.d * nbs * Q8_BYTES, dm.d, nbs, 4, dm.d_pad / DN_COLS,
-                           dm.Fs_pad / QB, W->sh_dn, sh_dn, W->dn_exp + dm.E, stream);
+      e = launch_repack_q4k((const uint8_t*)down, (const uint8_t*)down, dm.E, (size_t)dm.d * row_f, dm.d, nsf, 4,
+                            dm.d_pad / DN_COLS, dm.F_pad / QB / KSTEP, W->dn, W->dn_per_expert, overflow, stream);
+    if (e == hipSuccess && has_sh) {
+      const int nss = dm.Fs / Q4K_VALUES;
+      e = launch_repack_q4k((const uint8_t*)sh_gate, (const uint8_t*)sh_up, 1, (size_t)dm.Fs * row_d, dm.Fs, nsd,
+                            2, dm.Fs_pad / GU_COLS, dm.d_pad / QB / KSTEP, W->sh_gu, sh_gu, overflow, stream);
+      if (e == hipSuccess)
+        e = launch_repack_q4k((const uint8_t*)sh_down, (const uint8_t*)sh_down, 1,
+                              (size_t)dm.d * nss * Q4K_BYTES, dm.d, nss, 4, dm.d_pad / DN_COLS,
+                              dm.Fs_pad / QB / KSTEP, W->sh_dn, sh_dn, overflow, stream);
+    }
+  } else {
+    const int nbd = dm.d / QB, nbf = dm.F / QB;
+    if (e == hipSuccess)
+      e = launch_repack_q8((const uint8_t*)gate, (const uint8_t*)up, dm.E, (size_t)dm.F * nbd * Q8_BYTES, dm.F,
+                           nbd, 2, dm.F_pad / GU_COLS, dm.d_pad / QB, W->gu, W->gu_per_expert, nullptr, stream);
+    if (e == hipSuccess)
+      e = launch_scale_exponent((const uint8_t*)down, dm.E, (size_t)dm.d * nbf * Q8_BYTES, (long)dm.d * nbf,
+                                W->dn_exp, stream);
+    if (e == hipSuccess)
+      e = launch_repack_q8((const uint8_t*)down, (const uint8_t*)down, dm.E, (size_t)dm.d * nbf * Q8_BYTES, dm.d,
+                           nbf, 4, dm.d_pad / DN_COLS, dm.F_pad / QB, W->dn, W->dn_per_expert, W->dn_exp, stream);
+    if (e == hipSuccess && has_sh) {
+      const int nbs = dm.Fs / QB;
+      e = launch_repack_q8((const uint8_t*)sh_gate, (const uint8_t*)sh_up, 1, (size_t)dm.Fs * nbd * Q8_BYTES,
+                           dm.Fs, nbd, 2, dm.Fs_pad / GU_COLS, dm.d_pad / QB, W->sh_gu, sh_gu, nullptr, stream);
+      if (e == hipSuccess)
+        e = launch_scale_exponent((const uint8_t*)sh_down, 1, (size_t)dm.d * nbs * Q8_BYTES, (long)dm.d * nbs,
+                                  W->dn_exp + dm.E, stream);
+      if (e == hipSuccess)
+        e = launch_repack_q8((const uint8_t*)sh_down, (const uint8_t*)sh_down, 1, (size_t)dm.d * nbs * Q8_BYTES,
+                             dm.d, nbs, 4, dm.d_pad / DN_COLS, dm.Fs_pad / QB, W->sh_dn, sh_dn,
+                             W->dn_exp + dm.E, stream);
+    }
   }
+  int32_t overflow_h = 0;
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
-  if (e != hipSuccess) {
+  if (e == hipSuccess && q4k) e = hipMemcpy(&overflow_h, overflow, 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess || overflow_h) {
     (void)hipGetLastError();
     (void)hipFree(W->base);
     delete W;
-    return MOE_FFN_HIP_ERROR;
+    return e != hipSuccess ? MOE_FFN_HIP_ERROR : MOE_FFN_UNSUPPORTED;
   }
   *out = W;
   return MOE_FFN_OK;
@@ -603,6 +645,7 @@ int moe_ffn_dbg_block_sums(const moe_ffn_weights* w, void* ws, size_t ws_bytes, 
                            int8_t* a_codes, int32_t* info, hipStream_t stream) {
   if (!w || !ws || !sums || !a_codes || !info) return MOE_FFN_INVALID_ARG;
   if (n_tokens < 1 || n_tokens > MAX_TOKENS || (gemm != 0 && gemm != 1)) return MOE_FFN_INVALID_ARG;
+  if (w->fmt != MOE_FFN_FMT_Q8_0) return MOE_FFN_UNSUPPORTED;  // reads the Q8_0 code planes
   const Dims& dm = w->dm;
   const WsLayout L = ws_layout(dm, n_tokens);
   if (ws_bytes < L.total) return MOE_FFN_WORKSPACE_TOO_SMALL;

@@ -74,22 +74,15 @@
 #include <type_traits>
 
 #include "device_util.h"
+#include "gemm_common.h"
 #include "internal.h"
 
 namespace moe {
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-typedef _Float16 v4h __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char;
-
-constexpr int NWAVE = MT_WG / MT_WAVE;                   // 4 wavefronts x 32 rows
 constexpr int B_OFF = 0;                                 // weight codes [block][tile] x 1 KiB
 constexpr int BS_OFF = 16 * 1024;                        // weight scales (gate/up: [tile][32 rows][4
                                                          // blocks]; down: [tile][half][32 rows][4])
-constexpr int EPI_STRIDE = 65;                           // gate/up epilogue scratch row (floats)
 
 // Stage layout of one k-step buffer: the weight k-step (17 or 18 KiB), then
 // the activation chunks [wave][block] x 1 KiB and their scales [wave][32 rows][4 blocks].
@@ -103,60 +96,6 @@ struct Lay {
 };
 static_assert(NWAVE * 32 * EPI_STRIDE * 4 <= Lay<true>::STAGE, "epilogue scratch must fit in one buffer");
 static_assert(2 * 2 * Lay<false>::STAGE <= 160 * 1024, "two workgroups per CU must fit in the LDS");
-
-__device__ inline int out_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
-
-__device__ inline v4h as_v4h(uint32_t lo, uint32_t hi) {
-  const uint2 u = make_uint2(lo, hi);
-  return __builtin_bit_cast(v4h, u);
-}
-__device__ inline v4h as_v4h(uint2 u) { return __builtin_bit_cast(v4h, u); }
-
-// global -> LDS copies: lane l moves `size` bytes from base + voff (base is
-// wavefront-uniform, voff this lane's 32-bit offset) to LDS address
-// m0 + size * l (m0 is wavefront-uniform).
-__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(base), "s"(lds)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
-               :
-               : "v"(voff), "s"(base), "s"(lds)
-               : "memory", "m0");
-}
-
-// Wait until at most n of this wavefront's copies are in flight (vector loads
-// complete in order), then meet the other wavefronts.  The k-loop form also
-// waits for this wavefront's LDS reads: operands of the buffer that the
-// copies issued right after the barrier overwrite may still be in flight
-// (their registers are consumed only after the barrier), and the barrier
-// itself does not order them against other wavefronts' copies.
-__device__ __forceinline__ void wait_copies_barrier_0() {
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_copies_barrier_n() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Copy sources of k-step 0: wavefront-uniform bases and per-lane 32-bit
-// offsets.  K-step j adds j * KSTEP_BYTES to the weight base, KSTEP chunks to
-// the activation base and one k-step of scales (32 rows x KSTEP) to the scale
-// base.
-struct Src {
-  const uint8_t* w;    // the strip's first k-step
-  const int8_t* a;     // this wavefront's activation chunks (gq or hq)
-  const uint16_t* as;  // their scales (gqs or hs)
-  uint32_t o_w;        // 16 * lane: code chunk piece
-  uint32_t o_ws;       // 16 KiB + 4 * lane + this wavefront's share of the weight scales
-};
 
 // This wavefront's copies of k-step j into the buffer at LDS address L, in
 // two halves issued at different points of the k loop, so that the copies of
@@ -221,9 +160,6 @@ __device__ __forceinline__ void issue_acts_part(const Src& s, int j, uint32_t L,
     dma4(s.as + (size_t)j * 32 * KSTEP, lane * 4, L + Lay<GATEUP>::AS_OFF + wave * 256);
   }
 }
-struct NoHook {
-  __device__ void operator()(int) const {}
-};
 
 // Register operands of one block: this wavefront's A chunk and the 4 B chunks.
 struct Ops {
@@ -307,31 +243,6 @@ __device__ __forceinline__ v4h dn_corr_a(uint32_t q) {
   const uint32_t lo = q & 0xffffu, hi = q >> 16;
   return as_v4h((lo | (lo << 16)) ^ 0x80008000u, (hi | (hi << 16)) ^ 0x80008000u);
 }
-
-// Empty asm statements that take values "in and out" without emitting an
-// instruction.  Volatile asm statements keep their order, so threading the
-// pipeline's values through them pins the issue order of the MFMAs and the
-// VALU groups (instruction selection would otherwise hoist all of a k-step's
-// scale MFMAs, whose operands are known at its start, and run out of registers).
-template <typename T>
-__device__ __forceinline__ void anchor(T& v) {
-  asm volatile("" : "+v"(v));
-}
-template <typename T, typename U>
-__device__ __forceinline__ void anchor(T& v, U& u) {
-  asm volatile("" : "+v"(v), "+v"(u));
-}
-
-// Per-wavefront constants of the pipelines: the accumulator input of every
-// int8 MFMA (gate/up: the bits of 1.5 * 2^23; down: the bits of 1.5f), the
-// constant A and B operands of the gate/up conversion MFMA (one non-zero K
-// slot: -3072 * 4096 = -1.5 * 2^23) and, for down, the k-step's correction A
-// operand.
-struct Ctx {
-  v16i magic;
-  v4h sub_a, sub_b;
-  v4h corr;
-};
 
 // One block (4 tiles) of the gate/up pipeline, which runs two tiles ahead.
 // On entry dn holds the int8 MFMA of tile 1 of this block (as the float
@@ -533,15 +444,6 @@ __device__ __forceinline__ void issue_kstep1(const Src& s, int j, uint32_t L, in
   dma4(s.as + (size_t)j * 32 * KSTEP, lane * 4, L + Lay1<GATEUP>::AS_OFF);
 }
 
-// Wait until at most N of this wavefront's copies are in flight and its LDS
-// reads have returned, then meet the other wavefronts.
-template <int N>
-__device__ __forceinline__ void wait_copies_reads_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // K-step j of a one-row-group tile.  On entry X and sc hold block si of
 // k-step j (read from its stage in the previous k-step); k-steps j+1 and j+2
 // are in flight.  The barrier publishes k-step j+1 and proves that every
@@ -622,105 +524,6 @@ __device__ __forceinline__ void pipeline_init(const Ops& X, const ScalesT<GATEUP
     anchor(cx.magic);
     c = __builtin_amdgcn_mfma_i32_32x32x32_i8(X.a, X.b[0], cx.magic, 0, 0, 0);
     s = __builtin_amdgcn_mfma_f32_32x32x8f16(dn_sa_slot(s0.q, si, lane), as_v4h(s0.wb[0]), zf, 0, 0, 0);
-  }
-}
-
-// Grouped GEMM.  GATEUP: A = the int8 token rows of the tile's (token, slot)
-// pairs, which the quantiser wrote in chunk form at their padded rows; B = the
-// [gate;up] strip of 64 SwiGLU columns; epilogue h = silu(gate) * up,
-// requantised per 32 into the down GEMM's A-operand chunks.  !GATEUP: A = those
-// chunks, B = a 128-column strip of the down matrix; epilogue scatters the fp32
-// rows to partial[token][slot] (the unweighted down-partials of #129 "Scope").
-//
-// The epilogue of one wavefront's 32 rows (CSR rows wrow0.., 32-row tile
-// t32) against strip cs of group g; tok / slt are this lane's (token, slot)
-// for down.  Gate/up uses this wavefront's area at the start of the LDS.
-template <bool GATEUP>
-__device__ __forceinline__ void epilogue(const GemmArgs& a, char* lds, int lane, int wave, int t32, int cs, int g,
-                                         int wrow0, int row_end, int tok, int slt, v16f (&acc)[4]) {
-  if constexpr (GATEUP) {
-    // h = silu(gate) * up for the wavefront's 32 rows x 64 columns, transposed
-    // through LDS ([32][65] floats, conflict-free) so that lane l then owns the
-    // whole 32-block (row l%32, sub-strip l/32): amax, the two divisions and 32
-    // codes per lane, written as two 16-byte pieces of the down GEMM's A chunk.
-    float* hl = reinterpret_cast<float*>(lds) + wave * (32 * EPI_STRIDE);
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float gv = acc[sub][v], uv = acc[2 + sub][v];
-        const float h = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
-        hl[out_row(v, lane) * EPI_STRIDE + sub * 32 + (lane & 31)] = h;
-      }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    const int r = lane & 31, sub = lane >> 5;
-    float hv[32];
-    float amax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      hv[j] = hl[r * EPI_STRIDE + sub * 32 + j];
-      amax = fmaxf(amax, fabsf(hv[j]));
-    }
-    uint32_t packed[8];
-    uint16_t s16 = 0;
-    if (amax == 0.0f) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) packed[i] = 0u;
-    } else {
-      const float id = 127.0f / amax;
-      s16 = __half_as_ushort(__float2half_rn(amax / 127.0f));
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint32_t w = 0u;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          float q = rintf(hv[4 * i + b] * id);
-          q = fminf(fmaxf(q, -127.0f), 127.0f);
-          w |= ((uint32_t)(int)q & 0xffu) << (8 * b);
-        }
-        packed[i] = w;
-      }
-    }
-    // block kbf of h = pieces 2(kbf%4), +1 of k-step kbf/4 in row r's line
-    const int kbf = 2 * cs + sub, p0 = 2 * (kbf & 3);
-    char* line = reinterpret_cast<char*>(a.hq) +
-                 (((size_t)t32 * (a.kbmax / KSTEP) + (kbf >> 2)) * 32 + r) * 128;
-    *reinterpret_cast<uint4*>(line + ((p0 ^ (r & 7)) << 4)) =
-        make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    *reinterpret_cast<uint4*>(line + (((p0 + 1) ^ (r & 7)) << 4)) =
-        make_uint4(packed[4], packed[5], packed[6], packed[7]);
-    a.hs[(((size_t)t32 * (a.kbmax / KSTEP) + (kbf >> 2)) * 32 + r) * KSTEP + (kbf & 3)] = s16;
-  } else {
-    // Destination row of each of the lane's 16 output rows (lane r holds that
-    // of CSR row wrow0 + r); all 16 exchanges are issued before any store.
-    int ri = -1;
-    if (wrow0 + (lane & 31) < row_end && (unsigned)tok < (unsigned)a.n_tokens &&
-        (unsigned)slt < (unsigned)a.kk)
-      ri = tok * a.kk + slt;
-    int rows[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) rows[v] = __shfl(ri, out_row(v, lane), 64);
-    const bool full = (cs + 1) * DN_COLS <= a.d;  // the strip has no padding columns
-    const int col0 = cs * DN_COLS + (lane & 31);
-    // acc holds 2^-eg times the down product; scaled in place (pinned, so that
-    // the scaling is not sunk into the conditional stores below)
-    const int eg = __builtin_amdgcn_readfirstlane(a.dn_exp[g]);
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[tt][v] = ldexpf(acc[tt][v], eg);
-      anchor(acc[tt]);
-    }
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      if (rows[v] >= 0) {
-        float* dst = a.partial + (size_t)rows[v] * a.d + col0;
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-          if (full || col0 + tt * 32 < a.d) dst[tt * 32] = acc[tt][v];
-      }
-    }
   }
 }
 
@@ -921,8 +724,6 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
   else
     tile_work1<GATEUP>(a, &lds[0][0], lane, wave, T, cs, g, row0, row_end, KS, strip);
 }
-
-int grid_for(long wgs) { return (int)((wgs + 7) / 8 * 8); }
 
 // The integer core of a grouped GEMM, exposed for parity checks: k-block kb
 // of tile T against strip cs, through the product kernels' own path -- the

@@ -22,6 +22,9 @@
 //               Lane l of a wavefront reads bytes [8 l, 8 l + 8) of a tile's 512.
 //   The shared expert has its own planes of the same form (F replaced by Fs).
 //   Padding rows/blocks hold zero codes and zero scales.
+//   Q4_K weights use the same strips and tiles with 12 KiB k-steps (4-bit
+//   codes and binary16 {hi, lo} pairs of the sub-block scales and mins; the
+//   layout is described in gemm_q4k.hip); their dn_exp entries are zero.
 //
 // Workspace (per call, caller-allocated, carved by ws_layout()):
 //   logits fp32 [N][E]; ids, rank i32 [N][k]; w fp32 [N][k]; gs fp32 [N];
@@ -73,6 +76,9 @@ constexpr int DN_COLS = 128;      // output columns per down strip
 constexpr int KSTEP = 4;          // 32-blocks per GEMM k-step
 constexpr int KSTEP_BYTES = 17 * 1024;     // gate/up k-step: codes (16 KiB) + scales (1 KiB)
 constexpr int DN_KSTEP_BYTES = 18 * 1024;  // down k-step: codes (16 KiB) + scale pairs (2 KiB)
+constexpr int Q4K_VALUES = 256;            // weights per Q4_K super-block
+constexpr int Q4K_BYTES = 144;             // Q4_K super-block: d, dmin, 12 scale/min bytes, 128 code bytes
+constexpr int Q4K_KSTEP_BYTES = 12 * 1024; // Q4_K k-step (gate/up and down): codes 8 KiB + D and M pairs 2 KiB each
 constexpr int MAX_TOPK = 16;
 constexpr int MAX_EXPERTS = 256;
 constexpr int DECODE_MAX_TOKENS = 8;
@@ -115,6 +121,7 @@ struct moe_ffn_weights {
   uint8_t* sh_gu;
   uint8_t* sh_dn;
   int32_t* dn_exp;  // [G] exponent e of each group's down scale plane
+  int fmt;          // MOE_FFN_FMT_Q8_0 or MOE_FFN_FMT_Q4_K
   int n_cu;         // compute units of the device
   size_t gu_per_expert, dn_per_expert;  // bytes
 };
@@ -130,6 +137,13 @@ hipError_t launch_repack_q8(const uint8_t* src0, const uint8_t* src1, int n_grou
                             const int32_t* dn_exp, hipStream_t s);
 // e[g] = the smallest e >= 0 with |scale| * 2^(23 - e) <= 65504 for every Q8_0
 // block of group g (n_groups groups of n_blocks blocks, src_group_bytes apart).
+// Q4_K rows (super-blocks of 144 bytes, src_supers per row) to the Q4_K
+// planes: n_strips strips of n_ksteps k-steps per group; tiles_per_src as for
+// launch_repack_q8.  *overflow (device) is set to 1 when a finite sub-block
+// scale or min d * sc or dmin * m exceeds the binary16 range.
+hipError_t launch_repack_q4k(const uint8_t* src0, const uint8_t* src1, int n_groups, size_t src_group_bytes,
+                             int src_rows, int src_supers, int tiles_per_src, int n_strips, int n_ksteps,
+                             uint8_t* dst, size_t dst_group_bytes, int32_t* overflow, hipStream_t s);
 hipError_t launch_scale_exponent(const uint8_t* src, int n_groups, size_t src_group_bytes,
                                  long n_blocks, int32_t* e, hipStream_t s);
 hipError_t launch_transpose_router(const float* w, int E, int d, int E64, float* wt, hipStream_t s);
@@ -193,6 +207,9 @@ struct GemmArgs {
 
 hipError_t launch_gateup(const GemmArgs& a, hipStream_t s);
 hipError_t launch_down(const GemmArgs& a, hipStream_t s);
+// The same two GEMMs on Q4_K weight planes.
+hipError_t launch_gateup_q4k(const GemmArgs& a, hipStream_t s);
+hipError_t launch_down_q4k(const GemmArgs& a, hipStream_t s);
 // One k-block of one (tile, strip) of a grouped GEMM through the product's
 // copies, LDS layout and int8 MFMA: exact int32 block sums [128][128], the A
 // codes [128][32] and {group, row0, row_end, n_tiles} (one workgroup).

@@ -1,4 +1,5 @@
 // repack.hip -- load-time repacking of the layer weights (not on the timed path).
+// Q8_0 and Q4_K expert rows; the router matrix transposed.
 //
 // Q8_0 rows arrive as 34-byte blocks {binary16 scale, int8 q[32]} (the format of
 // the Q8_0 MMQ path in SharpInference #406 "References").  34-byte blocks are not
@@ -65,6 +66,100 @@ __global__ __launch_bounds__(256) void repack_q8_kernel(
       pair;
 }
 
+// Q4_K (the k-quant format beside Q8_0 in SharpInference #406 "References"):
+// a row is a run of 144-byte super-blocks of 256 weights {binary16 d,
+// binary16 dmin, 12 bytes of packed 6-bit sub-block scales and mins, 128
+// bytes of 4-bit codes}; weight i of sub-block j (32 weights) is
+// d * sc_j * q_i - dmin * m_j.  Sub-blocks 0-3 keep their scale and min in
+// the low 6 bits of bytes j and j + 4 of the 12; sub-blocks 4-7 take the low
+// (scale) or high (min) nibble of byte j + 4 as their low 4 bits and the top
+// 2 bits of byte j - 4 (scale) or byte j (min) as their high 2 bits.  Code i
+// of sub-block j is the low (j even) or high (j odd) nibble of code byte
+// 32 * (j / 2) + i.
+__device__ inline void q4k_scale_min(const uint8_t* s12, int j, int& sc, int& m) {
+  if (j < 4) {
+    sc = s12[j] & 63;
+    m = s12[j + 4] & 63;
+  } else {
+    sc = (s12[j + 4] & 15) | ((s12[j - 4] >> 6) << 4);
+    m = (s12[j + 4] >> 4) | ((s12[j] >> 6) << 4);
+  }
+}
+
+// v as the binary16 pair {hi, lo}: hi = v rounded to binary16, lo = the
+// remainder v - hi (exact in fp32) rounded to binary16.  A product d * sc or
+// dmin * m has at most 17 significant bits, so hi + lo == v exactly unless
+// the remainder lies below the binary16 normal range, where its error stays
+// below 2^-25.  Sets bad when a finite v overflows binary16.
+__device__ inline void split_half(float v, uint16_t& hi, uint16_t& lo, bool& bad) {
+  const __half h = __float2half_rn(v);
+  const float hf = __half2float(h);
+  if (isfinite(v) && !isfinite(hf)) bad = true;
+  hi = __half_as_ushort(h);
+  lo = __half_as_ushort(__float2half_rn(v - hf));
+}
+
+// One thread per (strip c, k-step ks, tile tt, lane) of group blockIdx.y: its
+// 8-byte code piece of each of the k-step's 4 blocks, and its 8 bytes of the
+// D and M pair planes (layout in gemm_q4k.hip).
+__global__ __launch_bounds__(256) void repack_q4k_kernel(
+    const uint8_t* __restrict__ src0, const uint8_t* __restrict__ src1, size_t src_group_bytes,
+    int src_rows, int src_supers, int tiles_per_src, int n_strips, int n_ks, uint8_t* __restrict__ dst,
+    size_t dst_group_bytes, int32_t* __restrict__ overflow) {
+  const int g = blockIdx.y;
+  const long piece = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long n_pieces = (long)n_strips * n_ks * 4 * 64;
+  if (piece >= n_pieces) return;
+  const int lane = (int)(piece % 64);
+  const int tt = (int)((piece / 64) % 4);
+  const int ks = (int)((piece / 256) % n_ks);
+  const int c = (int)(piece / (256L * n_ks));
+  const int half = lane / 32, r = lane % 32;
+  const int row = c * 32 * tiles_per_src + 32 * (tt % tiles_per_src) + r;
+  const uint8_t* src = (tt / tiles_per_src) ? src1 : src0;
+  const int sb = ks / 2, j0 = 4 * (ks % 2);  // super-block and its first sub-block in this k-step
+  const bool valid = row < src_rows && sb < src_supers;
+  uint8_t* step = dst + (size_t)g * dst_group_bytes + ((size_t)c * n_ks + ks) * Q4K_KSTEP_BYTES;
+  uint16_t dpl[4] = {0, 0, 0, 0}, mpl[4] = {0, 0, 0, 0};
+  bool bad = false;
+  const uint8_t* blk = valid ? src + (size_t)g * src_group_bytes + ((size_t)row * src_supers + sb) * Q4K_BYTES
+                             : nullptr;
+  const float d = valid ? __half2float(__ushort_as_half((uint16_t)(blk[0] | (blk[1] << 8)))) : 0.0f;
+  const float dmin = valid ? __half2float(__ushort_as_half((uint16_t)(blk[2] | (blk[3] << 8)))) : 0.0f;
+#pragma unroll
+  for (int kbi = 0; kbi < 4; ++kbi) {
+    uint32_t X = 0u, Y = 0u;
+    if (valid) {
+      const int j = j0 + kbi;
+      const uint8_t* qb = blk + 16 + 32 * (j / 2) + 16 * half;
+      const int sh = (j & 1) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t q0 = (qb[i] >> sh) & 15u, q4 = (qb[i + 4] >> sh) & 15u;
+        const uint32_t q8 = (qb[i + 8] >> sh) & 15u, q12 = (qb[i + 12] >> sh) & 15u;
+        X |= (q0 | (q4 << 4)) << (8 * i);
+        Y |= (q8 | (q12 << 4)) << (8 * i);
+      }
+      int sc, m;
+      q4k_scale_min(blk + 4, j, sc, m);
+      uint16_t hi, lo;
+      split_half(d * (float)sc, hi, lo, bad);  // exact in fp32: 11 + 6 significant bits
+      dpl[kbi] = half ? lo : hi;
+      split_half(dmin * (float)m, hi, lo, bad);
+      if ((kbi >> 1) == half) {
+        mpl[2 * (kbi & 1)] = hi;
+        mpl[2 * (kbi & 1) + 1] = lo;
+      }
+    }
+    *reinterpret_cast<uint2*>(step + (kbi * 4 + tt) * 512 + lane * 8) = make_uint2(X, Y);
+  }
+  *reinterpret_cast<uint2*>(step + 8 * 1024 + tt * 512 + lane * 8) =
+      make_uint2(dpl[0] | ((uint32_t)dpl[1] << 16), dpl[2] | ((uint32_t)dpl[3] << 16));
+  *reinterpret_cast<uint2*>(step + 10 * 1024 + tt * 512 + lane * 8) =
+      make_uint2(mpl[0] | ((uint32_t)mpl[1] << 16), mpl[2] | ((uint32_t)mpl[3] << 16));
+  if (bad) *overflow = 1;
+}
+
 // One workgroup per group: the largest |scale| of its Q8_0 blocks, then the
 // smallest e >= 0 with largest * 2^(23 - e) <= 65504 (the largest binary16).
 __global__ __launch_bounds__(256) void scale_exponent_kernel(const uint8_t* __restrict__ src,
@@ -115,6 +210,16 @@ hipError_t launch_repack_q8(const uint8_t* src0, const uint8_t* src1, int n_grou
   repack_q8_kernel<<<grid, 256, 0, s>>>(src0, src1, src_group_bytes, src_rows, src_blocks,
                                         tiles_per_src, n_strips, kb_pad, dst, dst_group_bytes,
                                         dn_exp);
+  return hipGetLastError();
+}
+
+hipError_t launch_repack_q4k(const uint8_t* src0, const uint8_t* src1, int n_groups, size_t src_group_bytes,
+                             int src_rows, int src_supers, int tiles_per_src, int n_strips, int n_ksteps,
+                             uint8_t* dst, size_t dst_group_bytes, int32_t* overflow, hipStream_t s) {
+  const long n_pieces = (long)n_strips * n_ksteps * 4 * 64;
+  dim3 grid((unsigned)((n_pieces + 255) / 256), (unsigned)n_groups);
+  repack_q4k_kernel<<<grid, 256, 0, s>>>(src0, src1, src_group_bytes, src_rows, src_supers, tiles_per_src,
+                                         n_strips, n_ksteps, dst, dst_group_bytes, overflow);
   return hipGetLastError();
 }
 

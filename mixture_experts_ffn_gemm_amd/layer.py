@@ -25,25 +25,28 @@ def _dev(a, device, dtype=None):
 class MoeLayer:
     """Weights handle for one MoE FFN layer.
 
-    Arguments follow moe_ffn_weights_create: router_w [E][d] fp32, router_bias
-    [E] or None, gate/up Q8_0 bytes [E][F][d/32*34], down [E][d][F/32*34],
-    and the optional shared expert (sh_gate/sh_up [Fs][d/32*34], sh_down
-    [d][Fs/32*34], sh_gate_vec [d]).  Host or device arrays are accepted.
+    Arguments follow moe_ffn_weights_create_fmt: router_w [E][d] fp32,
+    router_bias [E] or None, gate/up rows [E][F][...], down rows [E][d][...]
+    and the optional shared expert (sh_gate/sh_up [Fs][...], sh_down [d][...],
+    sh_gate_vec [d]), the rows in format ``fmt``: "q8_0" (d/32 or F/32 blocks
+    of 34 bytes) or "q4_k" (d/256 or F/256 super-blocks of 144 bytes).  Host
+    or device arrays are accepted.
     """
 
     def __init__(self, d_model, n_experts, top_k, d_ffn, router_w, gate_q8, up_q8, down_q8,
                  router_bias=None, d_shared_ffn=0, norm_topk_prob=False, sh_gate_q8=None,
-                 sh_up_q8=None, sh_down_q8=None, sh_gate_vec=None, device="cuda"):
+                 sh_up_q8=None, sh_down_q8=None, sh_gate_vec=None, device="cuda", fmt="q8_0"):
         self.device = torch.device(device)
+        self.fmt = fmt
         self.dims = B.make_dims(d_model, n_experts, top_k, d_ffn, d_shared_ffn, norm_topk_prob)
         up = dict(router_w=_dev(router_w, self.device, torch.float32),
                   router_bias=_dev(router_bias, self.device, torch.float32),
-                  gate_q8=_dev(gate_q8, self.device), up_q8=_dev(up_q8, self.device),
-                  down_q8=_dev(down_q8, self.device), sh_gate_q8=_dev(sh_gate_q8, self.device),
-                  sh_up_q8=_dev(sh_up_q8, self.device), sh_down_q8=_dev(sh_down_q8, self.device),
+                  gate=_dev(gate_q8, self.device), up=_dev(up_q8, self.device),
+                  down=_dev(down_q8, self.device), sh_gate=_dev(sh_gate_q8, self.device),
+                  sh_up=_dev(sh_up_q8, self.device), sh_down=_dev(sh_down_q8, self.device),
                   sh_gate_vec=_dev(sh_gate_vec, self.device, torch.float32))
         with torch.cuda.device(self.device):
-            self.handle = B.moe_ffn_weights_create(self.dims, **up)
+            self.handle = B.moe_ffn_weights_create_fmt(self.dims, B.FORMATS[fmt], **up)
         del up  # the call synchronised its stream; the library holds its own copy
         self._ws = None
 
@@ -53,7 +56,8 @@ class MoeLayer:
         return cls(s.d, s.n_experts, s.top_k, s.ffn, lw.router_w, lw.gate_q8, lw.up_q8, lw.down_q8,
                    router_bias=lw.router_bias, d_shared_ffn=s.shared_ffn,
                    norm_topk_prob=s.norm_topk_prob, sh_gate_q8=lw.sh_gate_q8, sh_up_q8=lw.sh_up_q8,
-                   sh_down_q8=lw.sh_down_q8, sh_gate_vec=lw.sh_gate_vec, device=device)
+                   sh_down_q8=lw.sh_down_q8, sh_gate_vec=lw.sh_gate_vec, device=device,
+                   fmt=getattr(lw, "fmt", "q8_0"))
 
     @property
     def d(self):

@@ -260,30 +260,41 @@ static void q4k_scale_min(const uint8_t* s12, int j, int* sc, int* m) {
   }
 }
 
-/* Value i (0..255) of a super-block, dequantised in fp64. */
-static double q4k_value(const uint8_t* blk, int i) {
+/* The 256 values of one super-block, dequantised in fp64: value i of
+ * sub-block j is d * sc_j * q_i - dmin * m_j. */
+static void q4k_super_block(const uint8_t* blk, double* out) {
   const double d = (double)half_bits_to_float((uint16_t)(blk[0] | (blk[1] << 8)));
   const double dmin = (double)half_bits_to_float((uint16_t)(blk[2] | (blk[3] << 8)));
-  const int j = i / 32, t = i % 32;
-  int sc, m;
-  q4k_scale_min(blk + 4, j, &sc, &m);
-  const uint8_t byte = blk[16 + 32 * (j / 2) + t];
-  const int q = (j & 1) ? (byte >> 4) : (byte & 15);
-  return d * (double)sc * (double)q - dmin * (double)m;
+  for (int j = 0; j < 8; ++j) {
+    int sc, m;
+    q4k_scale_min(blk + 4, j, &sc, &m);
+    for (int t = 0; t < 32; ++t) {
+      const uint8_t byte = blk[16 + 32 * (j / 2) + t];
+      const int q = (j & 1) ? (byte >> 4) : (byte & 15);
+      out[32 * j + t] = d * (double)sc * (double)q - dmin * (double)m;
+    }
+  }
 }
 
 void ora_q4k_dequant(const uint8_t* w_row, int32_t in_dim, double* out) {
-  for (int32_t i = 0; i < in_dim; ++i)
-    out[i] = q4k_value(w_row + (int64_t)(i / Q4K_VALUES) * Q4K_BYTES, i % Q4K_VALUES);
+  for (int32_t s = 0; s < in_dim / Q4K_VALUES; ++s) q4k_super_block(w_row + (int64_t)s * Q4K_BYTES, out + (int64_t)s * Q4K_VALUES);
 }
 
 /* Q4_K MMQ (#406 "References"): the product of the dequantised activation
- * and weight rows, written as its definition. */
+ * and weight rows, written as its definition (the sum over ascending i). */
 double ora_q4k_dot(const int8_t* qa, const uint16_t* sa16, const uint8_t* w_row, int32_t in_dim) {
   double acc = 0.0;
-  for (int32_t i = 0; i < in_dim; ++i) {
-    const double a = (double)half_bits_to_float(sa16[i / QB]) * (double)qa[i];
-    acc += a * q4k_value(w_row + (int64_t)(i / Q4K_VALUES) * Q4K_BYTES, i % Q4K_VALUES);
+  double w[Q4K_VALUES];
+  for (int32_t s = 0; s < in_dim / Q4K_VALUES; ++s) {
+    q4k_super_block(w_row + (int64_t)s * Q4K_BYTES, w);
+    for (int32_t b = 0; b < Q4K_VALUES / QB; ++b) {
+      const int32_t i0 = s * Q4K_VALUES + b * QB;
+      const double sa = (double)half_bits_to_float(sa16[i0 / QB]);
+      for (int32_t t = 0; t < QB; ++t) {
+        const double a = sa * (double)qa[i0 + t];
+        acc += a * w[b * QB + t];
+      }
+    }
   }
   return acc;
 }

@@ -391,6 +391,115 @@ def _tile_group(counts, t):
     raise AssertionError("tile past the table")
 
 
+# ------------------------------------------------------------- Q4_K weights
+# The Q4_K grouped GEMMs (#406 "References": Q4_K beside Q8_0 in the int8
+# MMQ path) against the oracle's Q4_K expert path (per value the dequantised
+# activation times the dequantised super-block value, summed in fp64).  d, F
+# and Fs are multiples of 256 (one super-block = two 128-value k-steps).
+Q4K_SHAPES = [
+    dict(d=256, E=8, k=2, F=256),                                 # one super-block per row
+    dict(d=512, E=16, k=3, F=256, Fs=512, zipf=1.1, norm=True),   # shared expert, Fs != F, skew
+    dict(d=256, E=70, k=4, F=512),                                # E > 64: routing in its own launch
+]
+
+
+@pytest.mark.parametrize("case", range(len(Q4K_SHAPES)))
+@pytest.mark.parametrize("n", [1, 53])
+def test_q4k_shapes(case, n):
+    shape, lw = mw.random_shape_case(40 + case, fmt="q4_k", **Q4K_SHAPES[case])
+    say(f"q4k case {case}: {Q4K_SHAPES[case]} n={n}")
+    x = mw.make_tokens(900 + case, n, shape.d)
+    g = run_gpu(lw, x)
+    check_routing(lw, x, g)
+    r, e = check_outputs(lw, x, g)
+    say(f"q4k case {case} n={n}: rel_l2={r:.2e} max_elem={e:.2e}")
+
+
+def test_q4k_mid_size_all_tokens():
+    """Groups of several 128-row tiles (every wavefront of a tile computes),
+    6 gate/up and 4 down k-steps, a shared expert of a different width."""
+    shape, lw = mw.random_shape_case(45, d=768, E=4, k=2, F=512, Fs=256, zipf=1.1, fmt="q4_k")
+    x = mw.make_tokens(945, 600, shape.d)
+    say("q4k mid: d=768 E=4 k=2 F=512 Fs=256 n=600")
+    g = run_gpu(lw, x)
+    check_routing(lw, x, g)
+    counts = np.diff(g["exp_start"])
+    assert counts.max() > 128, "the case must put more than one GEMM tile in a group"
+    r, e = check_outputs(lw, x, g)
+    say(f"q4k mid: max group {int(counts.max())} rows, rel_l2={r:.2e} max_elem={e:.2e}")
+
+
+def test_q4k_unsupported_entry_points():
+    """Decode and the Q8_0 block-sum dump reject a Q4_K handle before
+    enqueueing anything; a prefill on the same handle still works after."""
+    from mixture_experts_ffn_gemm_amd import binding as B
+    from mixture_experts_ffn_gemm_amd.layer import MoeLayer
+    shape, lw = mw.random_shape_case(40, fmt="q4_k", **Q4K_SHAPES[0])
+    x = mw.make_tokens(940, 4, shape.d)
+    layer = MoeLayer.from_workload(lw)
+    try:
+        xt = torch.from_numpy(x).cuda()
+        with pytest.raises(B.MoeFfnError) as ei:
+            layer.decode(xt)
+        assert ei.value.status == B.MOE_FFN_UNSUPPORTED
+        layer.prefill(xt)
+        ws = layer.workspace(4)
+        sums = torch.empty((128, 128), dtype=torch.int32, device="cuda")
+        ac = torch.empty((128, 32), dtype=torch.int8, device="cuda")
+        info = torch.empty(4, dtype=torch.int32, device="cuda")
+        with pytest.raises(B.MoeFfnError) as ei:
+            B.moe_ffn_dbg_block_sums(layer.handle, ws, ws.numel(), 4, 0, 0, 0, 0, sums, ac, info)
+        assert ei.value.status == B.MOE_FFN_UNSUPPORTED
+        out = layer.prefill(xt)
+        torch.cuda.synchronize()
+        moe_close(out.cpu().numpy(), O.moe_tokens(lw, x)["out"])
+    finally:
+        layer.close()
+
+
+def test_q4k_scale_overflow_is_rejected():
+    """A super-block whose d * sc exceeds the binary16 range cannot be held by
+    the kernels' binary16 scale pairs: weights create returns
+    MOE_FFN_UNSUPPORTED (and allocates nothing that outlives the call)."""
+    import dataclasses
+    from mixture_experts_ffn_gemm_amd import binding as B
+    from mixture_experts_ffn_gemm_amd.layer import MoeLayer
+    shape, lw = mw.random_shape_case(40, fmt="q4_k", **Q4K_SHAPES[0])
+    up = lw.up_q8.copy()
+    up[3, 5, 0:2] = np.array([60000.0], np.float16).view(np.uint8)   # d of row 5, super-block 0
+    up[3, 5, 4] = (up[3, 5, 4] & 0xC0) | 63                          # sc of sub-block 0 = 63
+    with pytest.raises(B.MoeFfnError) as ei:
+        MoeLayer.from_workload(dataclasses.replace(lw, up_q8=up))
+    assert ei.value.status == B.MOE_FFN_UNSUPPORTED
+
+
+@pytest.mark.slow
+def test_q4k_olmoe_layer_full_size():
+    """OLMoE-shaped layer at N=2048 on Q4_K experts, in the launch
+    configuration the benchmark times: every token's routing bit-exact, every
+    token's output and partials against the oracle."""
+    lw = mw.workload_layer("olmoe_n2048_q4k")
+    x = mw.workload_tokens("olmoe_n2048_q4k")
+    say("olmoe_n2048_q4k: weights generated")
+    g = run_gpu(lw, x)
+    check_routing(lw, x, g)
+    r, e = check_outputs(lw, x, g)
+    say(f"olmoe_n2048_q4k: rel_l2={r:.2e} max_elem={e:.2e} on all 2048 tokens")
+
+
+@pytest.mark.slow
+def test_q4k_a3b_layer_full_size():
+    """35B-A3B-shaped layer on Q4_K experts (E=256, shared expert, Zipf-skewed
+    routing): every token against the oracle."""
+    lw = mw.workload_layer("a3b_n512_q4k")
+    x = mw.workload_tokens("a3b_n512_q4k")
+    say("a3b_n512_q4k: weights generated")
+    g = run_gpu(lw, x)
+    check_routing(lw, x, g)
+    r, e = check_outputs(lw, x, g)
+    say(f"a3b_n512_q4k: rel_l2={r:.2e} max_elem={e:.2e} on all 512 tokens")
+
+
 # ------------------------------------------------------------- chunked prefill
 @pytest.mark.parametrize("flags", [0, 1])
 @pytest.mark.parametrize("case,n,chunk", [(0, 300, 128), (1, 300, 100), (1, 37, 512)])
