@@ -32,6 +32,12 @@ weight format issue #406 names): per 256 values {binary16 d, binary16 dmin,
 12 bytes of 6-bit sub-block scales and mins, 128 bytes of 4-bit codes}
 (144 bytes), a value being d*sc*q - dmin*m for its 32-value sub-block.  The
 choice of d, dmin, sc, m and q below is again input preparation only.
+
+Workloads with ``fmt="q3_k"`` pack the draws as Q3_K (the format of the
+Q3_K expert kernel issue #388 names): per 256 values {32 bytes of high bits,
+64 bytes of 2-bit codes, 12 bytes of 6-bit sub-block scales, binary16 d}
+(110 bytes), a value being d*(sc-32)*q, q in -4..3, for its 16-value
+sub-block; the field choice is input preparation only.
 """
 
 from __future__ import annotations
@@ -47,6 +53,7 @@ Q8_BLOCK = 32          # elements per Q8_0 block
 Q8_BLOCK_BYTES = 34    # fp16 scale + 32 int8 codes
 Q4K_VALUES = 256       # elements per Q4_K super-block
 Q4K_BYTES = 144        # fp16 d, fp16 dmin, 12 scale bytes, 128 code bytes
+Q3K_BYTES = 110        # 32 high-bit bytes, 64 code bytes, 12 scale bytes, fp16 d
 
 ROLE_X, ROLE_ROUTER, ROLE_BIAS_PERM, ROLE_SHARED_GATE = 0, 1, 2, 3
 ROLE_GATE, ROLE_UP, ROLE_DOWN = 4, 5, 6
@@ -71,7 +78,7 @@ class Workload:
     shape: LayerShape
     n_layers: int = 1
     description: str = ""
-    fmt: str = "q8_0"      # expert weight format: "q8_0" or "q4_k"
+    fmt: str = "q8_0"      # expert weight format: "q8_0", "q4_k" or "q3_k"
 
 
 OLMOE = LayerShape(d=2048, n_experts=64, top_k=8, ffn=1024)
@@ -99,6 +106,9 @@ WORKLOADS = {
                                 description="OLMoE-shaped layer, pp2048, Q4_K experts"),
     "a3b_n512_q4k": Workload("a3b_n512_q4k", 4, 512, A3B, fmt="q4_k",
                              description="35B-A3B-shaped layer, ubatch 512, Q4_K experts"),
+    # the OLMoE layer with its experts in Q3_K
+    "olmoe_n2048_q3k": Workload("olmoe_n2048_q3k", 2, 2048, OLMOE, fmt="q3_k",
+                                description="OLMoE-shaped layer, pp2048, Q3_K experts"),
 }
 
 
@@ -179,25 +189,66 @@ def pack_q4_k(w: np.ndarray) -> np.ndarray:
     return out.reshape(rows, nsb * Q4K_BYTES)
 
 
-def q4k_represented(w: np.ndarray) -> np.ndarray:
-    """The values the Q4_K fields chosen for w stand for, d*sc*q - dmin*m in
-    fp64 [rows][cols] (from the fields, not from the packed bytes)."""
-    d16, dmin16, sc, m, q = q4k_parts(w)
+def q3k_parts(w: np.ndarray):
+    """Choose the Q3_K fields of an fp32 matrix [rows][cols] (cols % 256 ==
+    0): returns d (fp16 [rows][cols/256]), sc (uint8 [rows][cols/16], 1..63)
+    and q (int8 [rows][cols], -4..3).  Per 16-value sub-block the multiplier
+    sc - 32 takes the sign that puts the value of largest magnitude on the
+    code -4 side, and its size a quarter of that magnitude over d; d is the
+    largest such quarter over 31."""
+    w = np.asarray(w, dtype=np.float32)
+    rows, cols = w.shape
+    assert cols % Q4K_VALUES == 0
+    nsb = cols // Q4K_VALUES
+    sb = w.reshape(rows, nsb, 16, 16).astype(np.float64)
+    pos, neg = sb.max(axis=3), -sb.min(axis=3)
+    sign = np.where(pos > neg, -1.0, 1.0)
+    step = np.maximum(pos, neg) / 4.0
+    d16 = (step.max(axis=2) / 31.0).astype(np.float16)
+    d = d16.astype(np.float64)[:, :, None]
+    k = sign * np.clip(np.rint(np.divide(step, d, out=np.zeros_like(step), where=d > 0)), 0, 31)
+    unit = (d * k)[..., None]
+    q = np.clip(np.rint(np.divide(sb, unit, out=np.zeros_like(sb), where=unit != 0)), -4, 3)
+    return d16, (k + 32).astype(np.uint8).reshape(rows, nsb * 16), q.astype(np.int8).reshape(rows, cols)
+
+
+def pack_q3_k(w: np.ndarray) -> np.ndarray:
+    """Pack an fp32 matrix [rows][cols] (cols % 256 == 0) into Q3_K bytes
+    [rows][cols/256*110]."""
+    d16, sc, q = q3k_parts(w)
     rows, cols = q.shape
     nsb = cols // Q4K_VALUES
-    d = np.repeat(d16.astype(np.float64), 8, axis=1)
-    dmin = np.repeat(dmin16.astype(np.float64), 8, axis=1)
-    unit = np.repeat(d * sc, 32, axis=1)
-    base = np.repeat(dmin * m, 32, axis=1)
-    return unit * q.astype(np.float64) - base
+    out = np.zeros((rows, nsb, Q3K_BYTES), dtype=np.uint8)
+    # value 128h + 32g + l: 2-bit code in bits 2g of code byte 32h + l, its
+    # high bit (set when q >= 0, else the code is q + 4) in bit 4h + g of
+    # high-bit byte l
+    qv = q.reshape(rows, nsb, 2, 4, 32).astype(np.int16)
+    high = (qv >= 0).astype(np.uint16)
+    code = np.where(qv >= 0, qv, qv + 4).astype(np.uint16)
+    shifts = (2 * np.arange(4)).reshape(1, 1, 1, 4, 1)
+    out[:, :, 32:96] = (code << shifts).sum(axis=3).reshape(rows, nsb, 64).astype(np.uint8)
+    hb = (4 * np.arange(2).reshape(1, 1, 2, 1, 1) + np.arange(4).reshape(1, 1, 1, 4, 1))
+    out[:, :, 0:32] = (high << hb).sum(axis=(2, 3)).astype(np.uint8)
+    # sub-block s: low 4 bits in nibble s/8 of byte s%8, high 2 bits in
+    # bits 2(s/4) of byte 8 + s%4
+    s = sc.reshape(rows, nsb, 16).astype(np.uint16)
+    out[:, :, 96:104] = ((s[:, :, 0:8] & 15) | ((s[:, :, 8:16] & 15) << 4)).astype(np.uint8)
+    hi2 = ((s >> 4) & 3).reshape(rows, nsb, 4, 4)          # [t][k] for s = 4t + k
+    out[:, :, 104:108] = (hi2 << (2 * np.arange(4)).reshape(1, 1, 4, 1)).sum(axis=2).astype(np.uint8)
+    out[:, :, 108:110] = d16.view(np.uint8).reshape(rows, nsb, 2)
+    return out.reshape(rows, nsb * Q3K_BYTES)
 
 
 def pack_weights(w: np.ndarray, fmt: str) -> np.ndarray:
-    return pack_q4_k(w) if fmt == "q4_k" else pack_q8_0(w)
+    return {"q4_k": pack_q4_k, "q3_k": pack_q3_k}.get(fmt, pack_q8_0)(w)
 
 
 def row_bytes(fmt: str, in_dim: int) -> int:
-    return in_dim // Q4K_VALUES * Q4K_BYTES if fmt == "q4_k" else in_dim // Q8_BLOCK * Q8_BLOCK_BYTES
+    if fmt == "q4_k":
+        return in_dim // Q4K_VALUES * Q4K_BYTES
+    if fmt == "q3_k":
+        return in_dim // Q4K_VALUES * Q3K_BYTES
+    return in_dim // Q8_BLOCK * Q8_BLOCK_BYTES
 
 
 def unpack_q8_0(b: np.ndarray, cols: int):
@@ -223,7 +274,7 @@ class LayerWeights:
     sh_up_q8: Optional[np.ndarray] = None     # uint8 [Fs][d/32*34]
     sh_down_q8: Optional[np.ndarray] = None   # uint8 [d][Fs/32*34]
     sh_gate_vec: Optional[np.ndarray] = None  # fp32 [d]
-    fmt: str = "q8_0"    # format of the expert rows above (the *_q8 arrays hold Q4_K rows for "q4_k")
+    fmt: str = "q8_0"    # format of the expert rows above (the *_q8 arrays hold Q4_K / Q3_K rows for those formats)
 
 
 def _normal(rng: np.random.Generator, shape, std: float) -> np.ndarray:
@@ -242,7 +293,7 @@ def make_layer(shape: LayerShape, cfg_id: int, layer: int = 0,
                n_experts_override: Optional[int] = None, fmt: str = "q8_0") -> LayerWeights:
     """Draw one layer's weights.  Expert e of role r always comes from
     ``rng_for(cfg_id, layer, r, e)`` so a subset of experts can be drawn alone;
-    the expert rows are packed in ``fmt`` ("q8_0" or "q4_k")."""
+    the expert rows are packed in ``fmt`` ("q8_0", "q4_k" or "q3_k")."""
     E = shape.n_experts if n_experts_override is None else n_experts_override
     d, F, Fs = shape.d, shape.ffn, shape.shared_ffn
     tag = f"layer_c{cfg_id}_l{layer}_d{d}_e{E}_f{F}_s{Fs}_z{shape.zipf_bias}" + ("" if fmt == "q8_0" else "_" + fmt)
@@ -316,5 +367,6 @@ def describe(name: str) -> dict:
             "top_k": s.top_k, "ffn": s.ffn, "shared_ffn": s.shared_ffn,
             "norm_topk_prob": bool(s.norm_topk_prob), "n_layers": w.n_layers,
             "router_bias": ("zipf(%.1f)" % s.zipf_bias) if s.zipf_bias else "none",
-            "weights": ("Q4_K (4-bit codes, 256-elem super-blocks, 6-bit sub-block scales and mins)"
-                        if w.fmt == "q4_k" else "Q8_0 (int8, 32-elem blocks, fp16 scale)")}
+            "weights": {"q4_k": "Q4_K (4-bit codes, 256-elem super-blocks, 6-bit sub-block scales and mins)",
+                        "q3_k": "Q3_K (3-bit codes, 256-elem super-blocks, 6-bit signed 16-elem sub-block scales)"}
+                       .get(w.fmt, "Q8_0 (int8, 32-elem blocks, fp16 scale)")}

@@ -28,6 +28,7 @@
 #define QBYTES 34
 #define Q4K_VALUES 256 /* values per Q4_K super-block */
 #define Q4K_BYTES 144  /* bytes per Q4_K super-block */
+#define Q3K_BYTES 110  /* bytes per Q3_K super-block (256 values) */
 
 /* ---------------------------------------------------------------- fp16 */
 /* IEEE 754 binary16 decoding: sign, 5-bit exponent (bias 15), 10-bit fraction. */
@@ -299,12 +300,60 @@ double ora_q4k_dot(const int8_t* qa, const uint16_t* sa16, const uint8_t* w_row,
   return acc;
 }
 
+/* ------------------------------------------------------------- Q3_K */
+/* The 256 values of one Q3_K super-block, dequantised in fp64 (layout in
+ * moe_oracle.h): value i = d * (sc_s - 32) * q_i. */
+static void q3k_super_block(const uint8_t* blk, double* out) {
+  const uint8_t* hbits = blk;
+  const uint8_t* codes = blk + 32;
+  const uint8_t* sc = blk + 96;
+  const double d = (double)half_bits_to_float((uint16_t)(blk[108] | (blk[109] << 8)));
+  for (int i = 0; i < Q4K_VALUES; ++i) {
+    const int h = i / 128, g = (i % 128) / 32, l = i % 32;
+    const int code = (codes[32 * h + l] >> (2 * g)) & 3;
+    const int high = (hbits[l] >> (4 * h + g)) & 1;
+    const int q = high ? code : code - 4;
+    const int s = 8 * h + 2 * g + l / 16;
+    const int lo4 = (sc[s % 8] >> (4 * (s / 8))) & 15;
+    const int hi2 = (sc[8 + s % 4] >> (2 * (s / 4))) & 3;
+    const int scale = lo4 | (hi2 << 4);
+    out[i] = d * (double)(scale - 32) * (double)q;
+  }
+}
+
+void ora_q3k_dequant(const uint8_t* w_row, int32_t in_dim, double* out) {
+  for (int32_t s = 0; s < in_dim / Q4K_VALUES; ++s) q3k_super_block(w_row + (int64_t)s * Q3K_BYTES, out + (int64_t)s * Q4K_VALUES);
+}
+
+/* The product of the dequantised activation and Q3_K weight rows, written
+ * as its definition (the sum over ascending i). */
+double ora_q3k_dot(const int8_t* qa, const uint16_t* sa16, const uint8_t* w_row, int32_t in_dim) {
+  double acc = 0.0;
+  double w[Q4K_VALUES];
+  for (int32_t s = 0; s < in_dim / Q4K_VALUES; ++s) {
+    q3k_super_block(w_row + (int64_t)s * Q3K_BYTES, w);
+    for (int32_t b = 0; b < Q4K_VALUES / QB; ++b) {
+      const int32_t i0 = s * Q4K_VALUES + b * QB;
+      const double sa = (double)half_bits_to_float(sa16[i0 / QB]);
+      for (int32_t t = 0; t < QB; ++t) {
+        const double a = sa * (double)qa[i0 + t];
+        acc += a * w[b * QB + t];
+      }
+    }
+  }
+  return acc;
+}
+
 /* Bytes of one weight row of in_dim values and the dot product of format fmt. */
 static int64_t row_bytes_of(int32_t fmt, int32_t in_dim) {
-  return fmt == ORA_FMT_Q4_K ? (int64_t)(in_dim / Q4K_VALUES) * Q4K_BYTES : (int64_t)(in_dim / QB) * QBYTES;
+  if (fmt == ORA_FMT_Q4_K) return (int64_t)(in_dim / Q4K_VALUES) * Q4K_BYTES;
+  if (fmt == ORA_FMT_Q3_K) return (int64_t)(in_dim / Q4K_VALUES) * Q3K_BYTES;
+  return (int64_t)(in_dim / QB) * QBYTES;
 }
 static double wdot(int32_t fmt, const int8_t* qa, const uint16_t* sa16, const uint8_t* w_row, int32_t in_dim) {
-  return fmt == ORA_FMT_Q4_K ? ora_q4k_dot(qa, sa16, w_row, in_dim) : ora_q8_dot(qa, sa16, w_row, in_dim / QB);
+  if (fmt == ORA_FMT_Q4_K) return ora_q4k_dot(qa, sa16, w_row, in_dim);
+  if (fmt == ORA_FMT_Q3_K) return ora_q3k_dot(qa, sa16, w_row, in_dim);
+  return ora_q8_dot(qa, sa16, w_row, in_dim / QB);
 }
 
 /* ------------------------------------------------------------- expert */
@@ -342,8 +391,9 @@ void ora_expert_ffn(int32_t d, int32_t ffn, const int8_t* xq, const uint16_t* xs
 
 static int dims_ok(const ora_dims* dm) {
   if (!dm) return 0;
-  if (dm->weight_format != ORA_FMT_Q8_0 && dm->weight_format != ORA_FMT_Q4_K) return 0;
-  const int32_t unit = dm->weight_format == ORA_FMT_Q4_K ? Q4K_VALUES : QB;
+  if (dm->weight_format != ORA_FMT_Q8_0 && dm->weight_format != ORA_FMT_Q4_K && dm->weight_format != ORA_FMT_Q3_K)
+    return 0;
+  const int32_t unit = dm->weight_format == ORA_FMT_Q8_0 ? QB : Q4K_VALUES;
   if (dm->d <= 0 || dm->d % unit || dm->ffn <= 0 || dm->ffn % unit) return 0;
   if (dm->shared_ffn < 0 || dm->shared_ffn % unit) return 0;
   if (dm->n_experts <= 0 || dm->top_k <= 0 || dm->top_k > dm->n_experts) return 0;

@@ -41,6 +41,18 @@
  * m_j = (byte j+4 >> 4) | (byte j >> 6) << 4 (bytes of the 12).  Code i of
  * sub-block j is the low (j even) or high (j odd) nibble of code byte
  * 32*(j/2) + i.  A value dequantises to d*sc_j*q - dmin*m_j.
+ *
+ * Q3_K weight rows (the format of the Q3_K expert GEMM #388 "Key references"
+ * names; the 3-bit k-quant super-block of the GGUF format): in/256
+ * super-blocks of 110 bytes = {32 bytes of high bits, 64 bytes of 2-bit
+ * codes, 12 bytes of 6-bit sub-block scales, binary16 d}.  Value i of a
+ * super-block (half h = i/128, group g = (i%128)/32, position l = i%32) has
+ * the 2-bit code (byte 32h+l of the codes >> 2g) & 3, the high bit = bit
+ * 4h+g of high-bit byte l, and q = code - 4 when that bit is clear (q in
+ * -4..3).  It belongs to 16-value sub-block s = 8h + 2g + l/16, whose scale
+ * sc_s has as low 4 bits nibble s/8 (low nibble first) of scale byte s%8 and
+ * as high 2 bits bits 2(s/4), 2(s/4)+1 of scale byte 8 + s%4.  A value
+ * dequantises to d*(sc_s - 32)*q.
  */
 #ifndef MOE_ORACLE_H
 #define MOE_ORACLE_H
@@ -53,15 +65,16 @@ extern "C" {
 
 #define ORA_FMT_Q8_0 0
 #define ORA_FMT_Q4_K 1
+#define ORA_FMT_Q3_K 2
 
 typedef struct ora_dims {
-  int32_t d;              /* hidden size, multiple of 32 (of 256 for Q4_K) */
+  int32_t d;              /* hidden size, multiple of 32 (of 256 for Q4_K, Q3_K) */
   int32_t n_experts;      /* E */
   int32_t top_k;          /* k = na */
-  int32_t ffn;            /* routed expert intermediate size, multiple of 32 (of 256 for Q4_K) */
+  int32_t ffn;            /* routed expert intermediate size, multiple of 32 (of 256 for Q4_K, Q3_K) */
   int32_t shared_ffn;     /* shared expert intermediate size, 0 = none */
   int32_t norm_topk_prob; /* 1: renormalise the k selected weights */
-  int32_t weight_format;  /* ORA_FMT_Q8_0 or ORA_FMT_Q4_K: the expert weight rows */
+  int32_t weight_format;  /* ORA_FMT_Q8_0, ORA_FMT_Q4_K or ORA_FMT_Q3_K: the expert weight rows */
 } ora_dims;
 
 /* IEEE binary16 <-> binary32, round to nearest even (n values). */
@@ -108,6 +121,15 @@ void ora_q4k_dequant(const uint8_t* w_row, int32_t in_dim, double* out);
  * weight row of in_dim values: the dot product of the two dequantised rows,
  * sum over i of (sa_b * qa_i) * (d*sc_j*q_i - dmin*m_j), in fp64. */
 double ora_q4k_dot(const int8_t* qa, const uint16_t* sa16, const uint8_t* w_row, int32_t in_dim);
+
+/* One Q3_K weight row of in_dim values (in_dim % 256 == 0) dequantised to
+ * fp64: out[i] = d*(sc_s - 32)*q_i. */
+void ora_q3k_dequant(const uint8_t* w_row, int32_t in_dim, double* out);
+
+/* Q8 activation row against one Q3_K weight row of in_dim values: the dot
+ * product of the two dequantised rows, sum over i of (sa_b * qa_i) *
+ * (d*(sc_s - 32)*q_i), in fp64. */
+double ora_q3k_dot(const int8_t* qa, const uint16_t* sa16, const uint8_t* w_row, int32_t in_dim);
 
 /* The exact int32 sums of one 32-block of an int8 MMQ product (#406
  * "References": Q8_0 MMQ): for activation rows i < m (32 codes each, qa

@@ -22,7 +22,7 @@ class OraDims(C.Structure):
                 ("weight_format", C.c_int32)]
 
 
-FMT = {"q8_0": 0, "q4_k": 1}
+FMT = {"q8_0": 0, "q4_k": 1, "q3_k": 2}
 
 
 def _p(a: Optional[np.ndarray]):
@@ -49,6 +49,8 @@ def lib():
             "ora_q8_block_sums": (None, [vp, i32, vp, i32, i64, i32, vp]),
             "ora_q4k_dequant": (None, [vp, i32, vp]),
             "ora_q4k_dot": (dbl, [vp, vp, vp, i32]),
+            "ora_q3k_dequant": (None, [vp, i32, vp]),
+            "ora_q3k_dot": (dbl, [vp, vp, vp, i32]),
             "ora_expert_ffn_fmt": (None, [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "ora_expert_ffn": (None, [i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "ora_moe_tokens": (i32, [C.POINTER(OraDims), vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -182,6 +184,22 @@ def q4k_dot(qa, sa16, w_row) -> float:
     sa16 = _c(sa16, np.uint16)
     w_row = _c(w_row, np.uint8)
     return lib().ora_q4k_dot(_p(qa), _p(sa16), _p(w_row), qa.size)
+
+
+def q3k_dequant(w_rows, in_dim: int) -> np.ndarray:
+    """Q3_K rows (uint8 [rows][in_dim/256*110]) -> fp64 [rows][in_dim]."""
+    w_rows = _c(np.atleast_2d(w_rows), np.uint8)
+    out = np.empty((w_rows.shape[0], in_dim), np.float64)
+    for r in range(w_rows.shape[0]):
+        lib().ora_q3k_dequant(_p(w_rows[r]), in_dim, out[r].ctypes.data_as(C.c_void_p))
+    return out
+
+
+def q3k_dot(qa, sa16, w_row) -> float:
+    qa = _c(qa, np.int8)
+    sa16 = _c(sa16, np.uint16)
+    w_row = _c(w_row, np.uint8)
+    return lib().ora_q3k_dot(_p(qa), _p(sa16), _p(w_row), qa.size)
 
 
 def expert_ffn(d, ffn, xq, xs, gate, up, down, fmt: str = "q8_0"):

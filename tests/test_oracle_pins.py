@@ -507,13 +507,22 @@ def _q4k_matrix(rng, rows, cols):
     return w
 
 
+def _q4k_represented(w):
+    """The values the Q4_K fields chosen for w stand for, d*sc*q - dmin*m in
+    fp64 (from the fields, not from the packed bytes)."""
+    d16, dmin16, sc, m, q = mw.q4k_parts(w)
+    d = np.repeat(d16.astype(np.float64), 8, axis=1)
+    dmin = np.repeat(dmin16.astype(np.float64), 8, axis=1)
+    return np.repeat(d * sc, 32, axis=1) * q.astype(np.float64) - np.repeat(dmin * m, 32, axis=1)
+
+
 def test_q4k_dequant_matches_the_packed_fields():
     rng = np.random.default_rng(40)
     w = _q4k_matrix(rng, 5, 768)
     b = mw.pack_q4_k(w)
     assert b.shape == (5, 3 * 144)
     dq = O.q4k_dequant(b, 768)
-    assert np.array_equal(dq, mw.q4k_represented(w))
+    assert np.array_equal(dq, _q4k_represented(w))
     # the represented values stay within a few code steps of the draw
     d16, dmin16, sc, m, q = mw.q4k_parts(w)
     step = np.repeat(np.repeat(d16.astype(np.float64), 8, axis=1) * sc, 32, axis=1)
@@ -602,6 +611,107 @@ def test_q4k_grouped_equals_per_token_bitwise(case):
     shape, lw = mw.random_shape_case(5, fmt="q4_k", **case)
     assert lw.fmt == "q4_k" and lw.gate_q8.shape[-1] == case["d"] // 256 * 144
     x = mw.make_tokens(105, 19, case["d"])
+    a = O.moe_tokens(lw, x)["out"]
+    b = O.moe_grouped(lw, x)
+    assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------- Q3_K
+def _q3k_represented(w):
+    """d*(sc-32)*q in fp64 from the Q3_K fields chosen for w."""
+    d16, sc, q = mw.q3k_parts(w)
+    d = np.repeat(d16.astype(np.float64), 16, axis=1)
+    return np.repeat(d * (sc.astype(np.float64) - 32.0), 16, axis=1) * q.astype(np.float64)
+
+
+def test_q3k_dequant_matches_the_packed_fields():
+    rng = np.random.default_rng(50)
+    w = _q4k_matrix(rng, 5, 768)
+    b = mw.pack_q3_k(w)
+    assert b.shape == (5, 3 * 110)
+    dq = O.q3k_dequant(b, 768)
+    assert np.array_equal(dq, _q3k_represented(w))
+    d16, sc, q = mw.q3k_parts(w)
+    assert q.min() == -4 and q.max() == 3 and sc.min() < 32 < sc.max()   # both code signs, both scale signs
+    # every value within one step (d*|sc-32|) of the draw, except the top of
+    # a sub-block whose largest value sits on the 3 side
+    step = np.repeat(np.repeat(d16.astype(np.float64), 16, axis=1) * np.abs(sc.astype(np.float64) - 32), 16, axis=1)
+    assert np.mean(np.abs(dq - w) <= step + 1e-9) > 0.98
+    assert np.all(dq[0, 0:32] == 0.0)
+
+
+def test_q3k_layout_of_one_super_block_by_hand():
+    """One super-block written byte by byte: d = 0.25, sub-block s scale
+    field sc_s (0 and 63 included: multipliers -32 and +31), and value i of
+    the super-block q_i = (i * 5 + 3) % 8 - 4, placed as the format places
+    it: value 128h + 32g + l has its 2-bit code in bits 2g of code byte
+    32h + l and its high bit (q >= 0) in bit 4h + g of high-bit byte l."""
+    blk = np.zeros(110, np.uint8)
+    sc = [(7 * s + 5) % 64 for s in range(16)]
+    sc[3], sc[12] = 0, 63
+    for s in range(16):
+        blk[96 + s % 8] |= (sc[s] & 15) << (4 * (s // 8))
+        blk[104 + s % 4] |= ((sc[s] >> 4) & 3) << (2 * (s // 4))
+    qv = [(i * 5 + 3) % 8 - 4 for i in range(256)]
+    for i in range(256):
+        h, g, l = i // 128, (i % 128) // 32, i % 32
+        code = qv[i] if qv[i] >= 0 else qv[i] + 4
+        blk[32 + 32 * h + l] |= code << (2 * g)
+        if qv[i] >= 0:
+            blk[l] |= 1 << (4 * h + g)
+    blk[108:110] = np.array([0.25], np.float16).view(np.uint8)
+    got = O.q3k_dequant(blk[None, :], 256)[0]
+    want = np.array([0.25 * (sc[i // 16] - 32) * qv[i] for i in range(256)])
+    assert np.array_equal(got, want)
+    assert got[3 * 16] == 0.25 * -32 * qv[48] and qv[48] != 0
+
+
+def test_q3k_dot_integer_decomposition():
+    """Per 32-block: sa * d * sum over its two 16-value sub-blocks of
+    (sc - 32) * sum(qa * q), the sums in int64."""
+    rng = np.random.default_rng(51)
+    d = 1024
+    w = _q4k_matrix(rng, 3, d)
+    b = mw.pack_q3_k(w)
+    d16, sc, q = mw.q3k_parts(w)
+    x = (rng.standard_normal((1, d)) * 3).astype(np.float32)
+    qa, sa = O.quantize_q8(x)
+    qa, sa = qa[0], sa[0]
+    saf = sa.view(np.float16).astype(np.float64)
+    for r in range(3):
+        got = O.q3k_dot(qa, sa, b[r])
+        c16 = (qa.astype(np.int64) * q[r].astype(np.int64)).reshape(-1, 16).sum(1)
+        per32 = (c16 * (sc[r].astype(np.int64) - 32)).reshape(-1, 2).sum(1)
+        dd = np.repeat(d16[r].astype(np.float64), 8)
+        ref = float(np.sum(saf * dd * per32))
+        assert abs(got - ref) <= 1e-12 * np.sum(np.abs(saf * dd * per32)) + 1e-300
+
+
+def test_q3k_expert_ffn_against_numpy():
+    rng = np.random.default_rng(52)
+    d, F = 512, 256
+    x = rng.standard_normal((1, d)).astype(np.float32)
+    xq, xs = O.quantize_q8(x)
+    G = mw.pack_q3_k((rng.standard_normal((F, d)) * 0.02).astype(np.float32))
+    U = mw.pack_q3_k((rng.standard_normal((F, d)) * 0.02).astype(np.float32))
+    D = mw.pack_q3_k((rng.standard_normal((d, F)) * 0.02).astype(np.float32))
+    y, hq, hs, h = O.expert_ffn(d, F, xq[0], xs[0], G, U, D, fmt="q3_k")
+    xd = xq[0].astype(np.float64) * np.repeat(xs[0].view(np.float16).astype(np.float64), 32)
+    g = O.q3k_dequant(G, d) @ xd
+    u = O.q3k_dequant(U, d) @ xd
+    np.testing.assert_allclose(h, g * scipy.special.expit(g) * u, rtol=1e-12, atol=1e-15)
+    hd = hq.astype(np.float64) * np.repeat(hs.view(np.float16).astype(np.float64), 32)
+    np.testing.assert_allclose(y, O.q3k_dequant(D, F) @ hd, rtol=1e-11, atol=1e-14)
+
+
+@pytest.mark.parametrize("case", [
+    dict(d=256, E=8, k=2, F=256),
+    dict(d=512, E=6, k=3, F=256, Fs=256, zipf=1.1, norm=True),
+])
+def test_q3k_grouped_equals_per_token_bitwise(case):
+    shape, lw = mw.random_shape_case(6, fmt="q3_k", **case)
+    assert lw.fmt == "q3_k" and lw.gate_q8.shape[-1] == case["d"] // 256 * 110
+    x = mw.make_tokens(106, 19, case["d"])
     a = O.moe_tokens(lw, x)["out"]
     b = O.moe_grouped(lw, x)
     assert np.array_equal(a, b)
