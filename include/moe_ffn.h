@@ -135,6 +135,7 @@ int moe_ffn_weights_create(const moe_ffn_dims* dims, const float* router_w,
 /* Expert weight formats of moe_ffn_weights_create_fmt. */
 #define MOE_FFN_FMT_Q8_0 0 /* 34-byte blocks of 32 {binary16 scale, int8 q[32]} */
 #define MOE_FFN_FMT_Q4_K 1 /* 144-byte super-blocks of 256, see below */
+#define MOE_FFN_FMT_Q3_K 2 /* 110-byte super-blocks of 256, see below */
 
 /* moe_ffn_weights_create with the expert rows (routed and shared, gate, up
  * and down) in `format`.  MOE_FFN_FMT_Q8_0 is moe_ffn_weights_create.
@@ -156,8 +157,25 @@ int moe_ffn_weights_create(const moe_ffn_dims* dims, const float* router_w,
  * (else MOE_FFN_UNSUPPORTED), and rejects with MOE_FFN_UNSUPPORTED weights
  * whose d * sc or dmin * m overflows binary16.  A Q4_K handle serves every
  * prefill entry point; moe_ffn_decode and moe_ffn_dbg_block_sums return
- * MOE_FFN_UNSUPPORTED for it.  Any other format is MOE_FFN_INVALID_ARG.  The
- * other arguments and the ownership rules are those of moe_ffn_weights_create. */
+ * MOE_FFN_UNSUPPORTED for it.
+ * MOE_FFN_FMT_Q3_K (the format of the Q3_K expert GEMM of #388 "Key
+ * references"): each row of n values is n/256 super-blocks of 110 bytes {32
+ * bytes of high bits, 64 bytes of 2-bit codes, 12 bytes of 6-bit sub-block
+ * scales, binary16 d}, the 3-bit k-quant super-block: weight 128h+32g+l has
+ * the 2-bit code (code byte 32h+l >> 2g) & 3 and the high bit (high-bit byte
+ * l >> 4h+g) & 1, q = code - 4 when that bit is clear; it lies in 16-value
+ * sub-block s = 8h+2g+l/16, whose scale sc_s takes nibble s/8 (low first) of
+ * scale byte s%8 as its low 4 bits and bits 2(s/4)..2(s/4)+1 of scale byte
+ * 8+s%4 as its high 2; the weight is d * (sc_s - 32) * q.  Layouts as for
+ * Q4_K with 110-byte super-blocks; d_model, d_ffn and d_shared_ffn multiples
+ * of 256.  The library expands Q3_K rows at load into int8 blocks holding the
+ * same values exactly (per 32 values the scale -d and the codes
+ * -(sc_s - 32) * q, which lie in [-128, 124]), so a Q3_K handle serves every
+ * entry point, decode and the block-sum dump included (the dump's sums are
+ * those of the expanded codes), with the Q8_0 planes' memory footprint.
+ * The expansion needs a temporary device buffer of 34/32 bytes per weight
+ * during the call.  Any other format is MOE_FFN_INVALID_ARG.  The other
+ * arguments and the ownership rules are those of moe_ffn_weights_create. */
 int moe_ffn_weights_create_fmt(const moe_ffn_dims* dims, int32_t format, const float* router_w,
                                const float* router_bias, const void* gate, const void* up,
                                const void* down, const void* sh_gate, const void* sh_up,

@@ -136,12 +136,13 @@ def moe_ffn_weights_create(dims: moe_ffn_dims, router_w, router_bias, gate_q8, u
 
 FMT_Q8_0 = 0
 FMT_Q4_K = 1
-FORMATS = {"q8_0": FMT_Q8_0, "q4_k": FMT_Q4_K}
+FMT_Q3_K = 2
+FORMATS = {"q8_0": FMT_Q8_0, "q4_k": FMT_Q4_K, "q3_k": FMT_Q3_K}
 
 
 def moe_ffn_weights_create_fmt(dims: moe_ffn_dims, fmt: int, router_w, router_bias, gate, up, down,
                                sh_gate=None, sh_up=None, sh_down=None, sh_gate_vec=None, stream=None) -> int:
-    """moe_ffn_weights_create with the expert rows in format fmt (FMT_Q8_0 or FMT_Q4_K)."""
+    """moe_ffn_weights_create with the expert rows in format fmt (FMT_Q8_0, FMT_Q4_K or FMT_Q3_K)."""
     h = C.c_void_p()
     rc = lib().moe_ffn_weights_create_fmt(C.byref(dims), int(fmt), _ptr(router_w), _ptr(router_bias), _ptr(gate),
                                           _ptr(up), _ptr(down), _ptr(sh_gate), _ptr(sh_up), _ptr(sh_down),

@@ -385,11 +385,13 @@ int moe_ffn_weights_create_fmt(const moe_ffn_dims* dims, int32_t format, const f
                                moe_ffn_weights** out) {
   if (!out) return MOE_FFN_INVALID_ARG;
   *out = nullptr;
-  if (format != MOE_FFN_FMT_Q8_0 && format != MOE_FFN_FMT_Q4_K) return MOE_FFN_INVALID_ARG;
+  if (format != MOE_FFN_FMT_Q8_0 && format != MOE_FFN_FMT_Q4_K && format != MOE_FFN_FMT_Q3_K)
+    return MOE_FFN_INVALID_ARG;
   const int rc = check_dims(dims);
   if (rc != MOE_FFN_OK) return rc;
   const bool q4k = format == MOE_FFN_FMT_Q4_K;
-  if (q4k && (dims->d_model % Q4K_VALUES || dims->d_ffn % Q4K_VALUES || dims->d_shared_ffn % Q4K_VALUES))
+  if (format != MOE_FFN_FMT_Q8_0 &&
+      (dims->d_model % Q4K_VALUES || dims->d_ffn % Q4K_VALUES || dims->d_shared_ffn % Q4K_VALUES))
     return MOE_FFN_UNSUPPORTED;
   if (!router_w || !gate || !up || !down) return MOE_FFN_INVALID_ARG;
   const bool has_sh = dims->d_shared_ffn > 0;
@@ -401,7 +403,7 @@ int moe_ffn_weights_create_fmt(const moe_ffn_dims* dims, int32_t format, const f
   if (!W) return MOE_FFN_OUT_OF_MEMORY;
   W->user = *dims;
   W->dm = make_dims(dims);
-  W->fmt = format;
+  W->fmt = format == MOE_FFN_FMT_Q3_K ? MOE_FFN_FMT_Q8_0 : format;  // Q3_K runs on Q8_0 planes
   const Dims& dm = W->dm;
   if (hipGetDevice(&W->device) != hipSuccess ||
       hipDeviceGetAttribute(&W->n_cu, hipDeviceAttributeMultiprocessorCount, W->device) != hipSuccess ||
@@ -450,6 +452,7 @@ int moe_ffn_weights_create_fmt(const moe_ffn_dims* dims, int32_t format, const f
   W->sh_dn = has_sh ? (uint8_t*)(b + o_sdn) : nullptr;
 
   hipError_t e = hipSuccess;
+  void* tmp = nullptr;  // Q3_K: the expanded Q8_0 rows (load time only)
   if (e == hipSuccess) e = launch_transpose_router(router_w, dm.E, dm.d, dm.E64, W->router_wt, stream);
   if (e == hipSuccess)
     e = router_bias ? hipMemcpyAsync(W->router_bias, router_bias, (size_t)dm.E * 4, hipMemcpyDeviceToDevice, stream)
@@ -479,31 +482,61 @@ int moe_ffn_weights_create_fmt(const moe_ffn_dims* dims, int32_t format, const f
                               dm.Fs_pad / QB / KSTEP, W->sh_dn, sh_dn, overflow, stream);
     }
   } else {
-    const int nbd = dm.d / QB, nbf = dm.F / QB;
+    // Q8_0 rows: as given, or (Q3_K) expanded at load into Q8_0 rows with the
+    // same values, all six matrices in one temporary buffer freed below
+    const int nbd = dm.d / QB, nbf = dm.F / QB, nbs = dm.Fs / QB;
+    const size_t q8_gu = (size_t)dm.F * nbd * Q8_BYTES, q8_dn = (size_t)dm.d * nbf * Q8_BYTES;
+    const size_t q8_sgu = (size_t)dm.Fs * nbd * Q8_BYTES, q8_sdn = (size_t)dm.d * nbs * Q8_BYTES;
+    const void *g8 = gate, *u8 = up, *d8 = down, *sg8 = sh_gate, *su8 = sh_up, *sd8 = sh_down;
+    if (format == MOE_FFN_FMT_Q3_K && e == hipSuccess) {
+      const size_t total = dm.E * (2 * q8_gu + q8_dn) + 2 * q8_sgu + q8_sdn;
+      if (hipMalloc(&tmp, total) != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipFree(W->base);
+        delete W;
+        return MOE_FFN_OUT_OF_MEMORY;
+      }
+      {
+        uint8_t* p = (uint8_t*)tmp;
+        const int ssd = dm.d / Q4K_VALUES, ssf = dm.F / Q4K_VALUES, sss = dm.Fs / Q4K_VALUES;
+        const size_t row_d = (size_t)ssd * Q3K_BYTES, row_f = (size_t)ssf * Q3K_BYTES;
+        auto expand = [&](const void* src, int groups, size_t src_group, int rows, int supers, size_t dst_group,
+                          const void** dst) {
+          if (e == hipSuccess) e = launch_q3k_to_q8((const uint8_t*)src, groups, src_group, rows, supers, p, dst_group, stream);
+          *dst = p;
+          p += (size_t)groups * dst_group;
+        };
+        expand(gate, dm.E, (size_t)dm.F * row_d, dm.F, ssd, q8_gu, &g8);
+        expand(up, dm.E, (size_t)dm.F * row_d, dm.F, ssd, q8_gu, &u8);
+        expand(down, dm.E, (size_t)dm.d * row_f, dm.d, ssf, q8_dn, &d8);
+        if (has_sh) {
+          expand(sh_gate, 1, (size_t)dm.Fs * row_d, dm.Fs, ssd, q8_sgu, &sg8);
+          expand(sh_up, 1, (size_t)dm.Fs * row_d, dm.Fs, ssd, q8_sgu, &su8);
+          expand(sh_down, 1, (size_t)dm.d * sss * Q3K_BYTES, dm.d, sss, q8_sdn, &sd8);
+        }
+      }
+    }
     if (e == hipSuccess)
-      e = launch_repack_q8((const uint8_t*)gate, (const uint8_t*)up, dm.E, (size_t)dm.F * nbd * Q8_BYTES, dm.F,
-                           nbd, 2, dm.F_pad / GU_COLS, dm.d_pad / QB, W->gu, W->gu_per_expert, nullptr, stream);
+      e = launch_repack_q8((const uint8_t*)g8, (const uint8_t*)u8, dm.E, q8_gu, dm.F, nbd, 2, dm.F_pad / GU_COLS,
+                           dm.d_pad / QB, W->gu, W->gu_per_expert, nullptr, stream);
     if (e == hipSuccess)
-      e = launch_scale_exponent((const uint8_t*)down, dm.E, (size_t)dm.d * nbf * Q8_BYTES, (long)dm.d * nbf,
-                                W->dn_exp, stream);
+      e = launch_scale_exponent((const uint8_t*)d8, dm.E, q8_dn, (long)dm.d * nbf, W->dn_exp, stream);
     if (e == hipSuccess)
-      e = launch_repack_q8((const uint8_t*)down, (const uint8_t*)down, dm.E, (size_t)dm.d * nbf * Q8_BYTES, dm.d,
-                           nbf, 4, dm.d_pad / DN_COLS, dm.F_pad / QB, W->dn, W->dn_per_expert, W->dn_exp, stream);
+      e = launch_repack_q8((const uint8_t*)d8, (const uint8_t*)d8, dm.E, q8_dn, dm.d, nbf, 4, dm.d_pad / DN_COLS,
+                           dm.F_pad / QB, W->dn, W->dn_per_expert, W->dn_exp, stream);
     if (e == hipSuccess && has_sh) {
-      const int nbs = dm.Fs / QB;
-      e = launch_repack_q8((const uint8_t*)sh_gate, (const uint8_t*)sh_up, 1, (size_t)dm.Fs * nbd * Q8_BYTES,
-                           dm.Fs, nbd, 2, dm.Fs_pad / GU_COLS, dm.d_pad / QB, W->sh_gu, sh_gu, nullptr, stream);
+      e = launch_repack_q8((const uint8_t*)sg8, (const uint8_t*)su8, 1, q8_sgu, dm.Fs, nbd, 2, dm.Fs_pad / GU_COLS,
+                           dm.d_pad / QB, W->sh_gu, sh_gu, nullptr, stream);
       if (e == hipSuccess)
-        e = launch_scale_exponent((const uint8_t*)sh_down, 1, (size_t)dm.d * nbs * Q8_BYTES, (long)dm.d * nbs,
-                                  W->dn_exp + dm.E, stream);
+        e = launch_scale_exponent((const uint8_t*)sd8, 1, q8_sdn, (long)dm.d * nbs, W->dn_exp + dm.E, stream);
       if (e == hipSuccess)
-        e = launch_repack_q8((const uint8_t*)sh_down, (const uint8_t*)sh_down, 1, (size_t)dm.d * nbs * Q8_BYTES,
-                             dm.d, nbs, 4, dm.d_pad / DN_COLS, dm.Fs_pad / QB, W->sh_dn, sh_dn,
-                             W->dn_exp + dm.E, stream);
+        e = launch_repack_q8((const uint8_t*)sd8, (const uint8_t*)sd8, 1, q8_sdn, dm.d, nbs, 4, dm.d_pad / DN_COLS,
+                             dm.Fs_pad / QB, W->sh_dn, sh_dn, W->dn_exp + dm.E, stream);
     }
   }
   int32_t overflow_h = 0;
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (tmp && hipFree(tmp) != hipSuccess && e == hipSuccess) e = hipErrorUnknown;
   if (e == hipSuccess && q4k) e = hipMemcpy(&overflow_h, overflow, 4, hipMemcpyDeviceToHost);
   if (e != hipSuccess || overflow_h) {
     (void)hipGetLastError();

@@ -25,6 +25,8 @@
 //   Q4_K weights use the same strips and tiles with 12 KiB k-steps (4-bit
 //   codes and binary16 {hi, lo} pairs of the sub-block scales and mins; the
 //   layout is described in gemm_q4k.hip); their dn_exp entries are zero.
+//   Q3_K weights are expanded at load into Q8_0 rows holding the same values
+//   exactly (repack.hip) and then use the Q8_0 planes.
 //
 // Workspace (per call, caller-allocated, carved by ws_layout()):
 //   logits fp32 [N][E]; ids, rank i32 [N][k]; w fp32 [N][k]; gs fp32 [N];
@@ -79,6 +81,7 @@ constexpr int DN_KSTEP_BYTES = 18 * 1024;  // down k-step: codes (16 KiB) + scal
 constexpr int Q4K_VALUES = 256;            // weights per Q4_K super-block
 constexpr int Q4K_BYTES = 144;             // Q4_K super-block: d, dmin, 12 scale/min bytes, 128 code bytes
 constexpr int Q4K_KSTEP_BYTES = 12 * 1024; // Q4_K k-step (gate/up and down): codes 8 KiB + D and M pairs 2 KiB each
+constexpr int Q3K_BYTES = 110;             // Q3_K super-block: 32 high-bit bytes, 64 code bytes, 12 scale bytes, d
 constexpr int MAX_TOPK = 16;
 constexpr int MAX_EXPERTS = 256;
 constexpr int DECODE_MAX_TOKENS = 8;
@@ -121,7 +124,7 @@ struct moe_ffn_weights {
   uint8_t* sh_gu;
   uint8_t* sh_dn;
   int32_t* dn_exp;  // [G] exponent e of each group's down scale plane
-  int fmt;          // MOE_FFN_FMT_Q8_0 or MOE_FFN_FMT_Q4_K
+  int fmt;          // format of the planes: MOE_FFN_FMT_Q8_0 (also for Q3_K rows) or MOE_FFN_FMT_Q4_K
   int n_cu;         // compute units of the device
   size_t gu_per_expert, dn_per_expert;  // bytes
 };
@@ -144,6 +147,11 @@ hipError_t launch_repack_q8(const uint8_t* src0, const uint8_t* src1, int n_grou
 hipError_t launch_repack_q4k(const uint8_t* src0, const uint8_t* src1, int n_groups, size_t src_group_bytes,
                              int src_rows, int src_supers, int tiles_per_src, int n_strips, int n_ksteps,
                              uint8_t* dst, size_t dst_group_bytes, int32_t* overflow, hipStream_t s);
+// Q3_K rows (supers super-blocks per row, rows rows per group) to Q8_0 rows
+// with the same values exactly: per 32-block scale -d and codes
+// -(sc - 32) * q (dst holds n_groups * rows * supers * 8 blocks of 34 bytes).
+hipError_t launch_q3k_to_q8(const uint8_t* src, int n_groups, size_t src_group_bytes, int rows, int supers,
+                            uint8_t* dst, size_t dst_group_bytes, hipStream_t s);
 hipError_t launch_scale_exponent(const uint8_t* src, int n_groups, size_t src_group_bytes,
                                  long n_blocks, int32_t* e, hipStream_t s);
 hipError_t launch_transpose_router(const float* w, int E, int d, int E64, float* wt, hipStream_t s);

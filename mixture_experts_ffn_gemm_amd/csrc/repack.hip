@@ -1,5 +1,5 @@
 // repack.hip -- load-time repacking of the layer weights (not on the timed path).
-// Q8_0 and Q4_K expert rows; the router matrix transposed.
+// Q8_0, Q4_K and Q3_K expert rows; the router matrix transposed.
 //
 // Q8_0 rows arrive as 34-byte blocks {binary16 scale, int8 q[32]} (the format of
 // the Q8_0 MMQ path in SharpInference #406 "References").  34-byte blocks are not
@@ -160,6 +160,54 @@ __global__ __launch_bounds__(256) void repack_q4k_kernel(
   if (bad) *overflow = 1;
 }
 
+// Q3_K (the format of the Q3_K expert GEMM of SharpInference #388 "Key
+// references"): a row is a run of 110-byte super-blocks of 256 weights {32
+// bytes of high bits, 64 bytes of 2-bit codes, 12 bytes of 6-bit sub-block
+// scales, binary16 d}.  Weight 128h + 32g + l takes its 2-bit code from bits
+// 2g of code byte 32h + l and its high bit from bit 4h + g of high-bit byte
+// l; q = code, minus 4 when the high bit is clear (q in -4..3).  It lies in
+// 16-weight sub-block s = 8h + 2g + l/16, whose scale sc_s has nibble s/8
+// (low first) of scale byte s%8 as its low 4 bits and bits 2(s/4), 2(s/4)+1
+// of scale byte 8 + s%4 as its high 2; the weight is d * (sc_s - 32) * q.
+//
+// The products (sc_s - 32) * q lie in [-124, 128], so their negations fit
+// int8, and a Q3_K 32-block is exactly the Q8_0 block {scale -d, codes
+// -(sc_s - 32) * q}: one thread per output block writes that 34-byte block.
+// The Q8_0 planes built from these rows then give every GEMM and matvec the
+// exact Q3_K products.  (|code sum| <= 32 * 127 * 128 < 2^19, the bound the
+// down pipeline's exact form needs.)
+__global__ __launch_bounds__(256) void q3k_to_q8_kernel(const uint8_t* __restrict__ src, size_t src_group_bytes,
+                                                        int rows, int supers, uint8_t* __restrict__ dst,
+                                                        size_t dst_group_bytes) {
+  const int g = blockIdx.y;
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long n = (long)rows * supers * 8;
+  if (idx >= n) return;
+  const long row = idx / (supers * 8);
+  const int b = (int)(idx % (supers * 8));
+  const uint8_t* blk = src + (size_t)g * src_group_bytes + ((size_t)row * supers + b / 8) * Q3K_BYTES;
+  uint8_t* out = dst + (size_t)g * dst_group_bytes + (size_t)idx * Q8_BYTES;
+  const int h = (b % 8) / 4, gq = (b % 8) % 4;
+  int mult[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int s = 8 * h + 2 * gq + u;
+    const int lo4 = (blk[96 + s % 8] >> (4 * (s / 8))) & 15;
+    const int hi2 = (blk[104 + s % 4] >> (2 * (s / 4))) & 3;
+    mult[u] = (lo4 | (hi2 << 4)) - 32;
+  }
+  const uint16_t dbits = (uint16_t)(blk[108] | (blk[109] << 8)) ^ 0x8000u;  // -d
+  out[0] = (uint8_t)(dbits & 0xff);
+  out[1] = (uint8_t)(dbits >> 8);
+#pragma unroll 4
+  for (int t = 0; t < 32; ++t) {
+    const int code = (blk[32 + 32 * h + t] >> (2 * gq)) & 3;
+    const int high = (blk[t] >> (4 * h + gq)) & 1;
+    const int q = high ? code : code - 4;
+    out[2 + t] = (uint8_t)(int8_t)(-mult[t / 16] * q);
+  }
+}
+
 // One workgroup per group: the largest |scale| of its Q8_0 blocks, then the
 // smallest e >= 0 with largest * 2^(23 - e) <= 65504 (the largest binary16).
 __global__ __launch_bounds__(256) void scale_exponent_kernel(const uint8_t* __restrict__ src,
@@ -220,6 +268,14 @@ hipError_t launch_repack_q4k(const uint8_t* src0, const uint8_t* src1, int n_gro
   dim3 grid((unsigned)((n_pieces + 255) / 256), (unsigned)n_groups);
   repack_q4k_kernel<<<grid, 256, 0, s>>>(src0, src1, src_group_bytes, src_rows, src_supers, tiles_per_src,
                                          n_strips, n_ksteps, dst, dst_group_bytes, overflow);
+  return hipGetLastError();
+}
+
+hipError_t launch_q3k_to_q8(const uint8_t* src, int n_groups, size_t src_group_bytes, int rows, int supers,
+                            uint8_t* dst, size_t dst_group_bytes, hipStream_t s) {
+  const long n = (long)rows * supers * 8;
+  dim3 grid((unsigned)((n + 255) / 256), (unsigned)n_groups);
+  q3k_to_q8_kernel<<<grid, 256, 0, s>>>(src, src_group_bytes, rows, supers, dst, dst_group_bytes);
   return hipGetLastError();
 }
 

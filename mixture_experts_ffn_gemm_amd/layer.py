@@ -29,8 +29,8 @@ class MoeLayer:
     router_bias [E] or None, gate/up rows [E][F][...], down rows [E][d][...]
     and the optional shared expert (sh_gate/sh_up [Fs][...], sh_down [d][...],
     sh_gate_vec [d]), the rows in format ``fmt``: "q8_0" (d/32 or F/32 blocks
-    of 34 bytes) or "q4_k" (d/256 or F/256 super-blocks of 144 bytes).  Host
-    or device arrays are accepted.
+    of 34 bytes), "q4_k" or "q3_k" (d/256 or F/256 super-blocks of 144 or 110
+    bytes).  Host or device arrays are accepted.
     """
 
     def __init__(self, d_model, n_experts, top_k, d_ffn, router_w, gate_q8, up_q8, down_q8,

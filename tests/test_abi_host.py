@@ -71,7 +71,7 @@ def test_weights_create_rejects_null_and_partial_shared(B):
                                           None, None) == -1
 
 
-def test_weights_create_fmt_rejects_formats_and_q4k_shapes_before_any_device_call(B):
+def test_weights_create_fmt_rejects_formats_and_kquant_shapes_before_any_device_call(B):
     h = C.c_void_p(1234)
     L = B.lib()
 
@@ -79,12 +79,14 @@ def test_weights_create_fmt_rejects_formats_and_q4k_shapes_before_any_device_cal
         dm = B.moe_ffn_dims(*dims)
         return L.moe_ffn_weights_create_fmt(C.byref(dm), fmt, 8, None, 16, 16, 16, sh, sh, sh, sh, None,
                                             C.byref(h))
-    assert create((256, 8, 2, 256, 0, 0), 2) == -1             # unknown format
+    assert create((256, 8, 2, 256, 0, 0), 3) == -1             # unknown format
     assert create((256, 8, 2, 256, 0, 0), -1) == -1
     assert create((128, 8, 2, 256, 0, 0), B.FMT_Q4_K) == -2    # d not a multiple of 256
     assert create((256, 8, 2, 128, 0, 0), B.FMT_Q4_K) == -2    # ffn not a multiple of 256
     assert create((256, 8, 2, 256, 64, 0), B.FMT_Q4_K, 16) == -2   # shared ffn not a multiple of 256
     assert create((0, 8, 2, 256, 0, 0), B.FMT_Q4_K) == -1      # the common dims checks still apply
+    assert create((128, 8, 2, 256, 0, 0), B.FMT_Q3_K) == -2    # Q3_K: multiples of 256 as well
+    assert create((256, 8, 2, 256, 32, 0), B.FMT_Q3_K, 16) == -2
     assert h.value is None
 
 

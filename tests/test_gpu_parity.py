@@ -500,6 +500,73 @@ def test_q4k_a3b_layer_full_size():
     say(f"a3b_n512_q4k: rel_l2={r:.2e} max_elem={e:.2e} on all 512 tokens")
 
 
+# ------------------------------------------------------------- Q3_K weights
+# Q3_K rows (#388 "Key references": the Q3_K expert GEMM) expanded at load
+# into the Q8_0 planes; prefill and decode against the oracle's Q3_K path.
+Q3K_SHAPES = [
+    dict(d=256, E=8, k=2, F=256),
+    dict(d=512, E=16, k=3, F=256, Fs=512, zipf=1.1, norm=True),
+    dict(d=256, E=70, k=4, F=512),
+]
+
+
+@pytest.mark.parametrize("case", range(len(Q3K_SHAPES)))
+@pytest.mark.parametrize("api,n", [("prefill", 1), ("prefill", 53), ("prefill", 300), ("decode", 1), ("decode", 8)])
+def test_q3k_shapes(case, api, n):
+    shape, lw = mw.random_shape_case(50 + case, fmt="q3_k", **Q3K_SHAPES[case])
+    say(f"q3k case {case}: {Q3K_SHAPES[case]} {api} n={n}")
+    x = mw.make_tokens(950 + case, n, shape.d)
+    g = run_gpu(lw, x, api=api)
+    check_routing(lw, x, g)
+    r, e = check_outputs(lw, x, g)
+    say(f"q3k case {case} {api} n={n}: rel_l2={r:.2e} max_elem={e:.2e}")
+
+
+def test_q3k_extreme_products():
+    """Sub-blocks with scale field 0 (multiplier -32) and codes -4: the
+    product 128 whose negation, -128, is the one expanded code at the edge of
+    int8; also multiplier +31 against codes 3 and -1.  Rows 0-63 of expert
+    0's gate, up and down matrices get these sub-blocks in super-block 0."""
+    import dataclasses
+    shape, lw = mw.random_shape_case(50, fmt="q3_k", **Q3K_SHAPES[0])
+    gate, up, down = lw.gate_q8.copy(), lw.up_q8.copy(), lw.down_q8.copy()
+    for arr, rows in ((gate[0], slice(0, 64)), (up[0], slice(0, 64)), (down[0], slice(0, 64))):
+        blk = arr[rows, 0:110]
+        blk[:, 96:108] = 0            # every scale field 0 -> multiplier -32
+        blk[:, 104:108] = 0
+        blk[:, 32:96] = 0             # codes 0 ...
+        blk[:, 0:32] = 0              # ... with the high bit clear: q = -4
+        # sub-blocks 8..15 (second half): scale 63 (+31), codes alternating 3 and -1
+        blk[:, 96:104] |= 0xF0
+        blk[:, 104:108] |= 0xF0
+        blk[:, 64:96] = 0xFF                     # code 3 in every group ...
+        blk[:, 0:32:2] |= 0xF0                   # ... with the high bit set on even l (q = 3), clear on odd (q = -1)
+        arr[rows, 0:110] = blk
+    lw = dataclasses.replace(lw, gate_q8=gate, up_q8=up, down_q8=down)
+    dq = O.q3k_dequant(gate[0, 0:1], shape.d)[0]
+    d0 = float(np.frombuffer(gate[0, 0, 108:110].tobytes(), np.float16)[0])
+    assert dq[0] == d0 * -32 * -4 and dq[128] == d0 * 31 * 3 and dq[129] == d0 * 31 * -1
+    x = mw.make_tokens(960, 64, shape.d)
+    g = run_gpu(lw, x)
+    check_routing(lw, x, g)
+    assert (g["topk_ids"] == 0).any(), "expert 0 must be selected"
+    r, e = check_outputs(lw, x, g)
+    say(f"q3k extreme products: rel_l2={r:.2e} max_elem={e:.2e}")
+
+
+@pytest.mark.slow
+def test_q3k_olmoe_layer_full_size():
+    """OLMoE-shaped layer at N=2048 on Q3_K experts: every token's routing
+    bit-exact, every token's output and partials against the oracle."""
+    lw = mw.workload_layer("olmoe_n2048_q3k")
+    x = mw.workload_tokens("olmoe_n2048_q3k")
+    say("olmoe_n2048_q3k: weights generated")
+    g = run_gpu(lw, x)
+    check_routing(lw, x, g)
+    r, e = check_outputs(lw, x, g)
+    say(f"olmoe_n2048_q3k: rel_l2={r:.2e} max_elem={e:.2e} on all 2048 tokens")
+
+
 # ------------------------------------------------------------- chunked prefill
 @pytest.mark.parametrize("flags", [0, 1])
 @pytest.mark.parametrize("case,n,chunk", [(0, 300, 128), (1, 300, 100), (1, 37, 512)])
