@@ -472,32 +472,6 @@ __device__ __forceinline__ void kstep1(const Src& src, int j, int KS, int wave, 
   compute_block(X, sc, si, Y, sn, si, true, cx, lane, c, cf, s, acc);
 }
 
-// The partial accumulators of a split row group, summed into its first
-// wavefront (si = 0) in the fixed order ((p0 + p1) + p2) + p3 through the
-// (then idle) stage buffers.  Every wavefront of the workgroup calls this.
-__device__ __forceinline__ void split_reduce(char* lds, int S, int rg, int si, int lane, v16f (&acc)[4]) {
-  __syncthreads();  // every wavefront is out of the k loop: the stage buffers are free
-  float* red = reinterpret_cast<float*>(lds);
-  if (si > 0) {
-    float* dst = red + (size_t)(rg * (S - 1) + si - 1) * 64 * 64;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) dst[(t * 16 + v) * 64 + lane] = acc[t][v];
-  }
-  __syncthreads();
-  if (si == 0) {
-    for (int p = 1; p < S; ++p) {
-      const float* src = red + (size_t)(rg * (S - 1) + p - 1) * 64 * 64;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[t][v] = acc[t][v] + src[(t * 16 + v) * 64 + lane];
-    }
-  }
-  __syncthreads();  // the reduction buffers are read before any epilogue reuses the LDS
-}
-
 // Pipeline constants and the state of (block si, tile 0) from the first
 // block's operands X and scales s0: for gate/up the int8 MFMA of tile 1,
 // float(C) and the scale product of tile 0; for down the int8 MFMA and the

@@ -111,6 +111,44 @@ struct Ctx {
   v4h corr;
 };
 
+// The partial row [token][slot] of this lane's CSR row wrow0 + lane%32 (the
+// down GEMM's destination), or -1 past the tile's rows or for a malformed pair.
+__device__ __forceinline__ int partial_row(const GemmArgs& a, int lane, int wrow0, int row_end, int tok, int slt) {
+  int ri = -1;
+  if (wrow0 + (lane & 31) < row_end && (unsigned)tok < (unsigned)a.n_tokens && (unsigned)slt < (unsigned)a.kk)
+    ri = tok * a.kk + slt;
+  return ri;
+}
+
+// The down epilogue: the wavefront's 32 x 128 outputs scattered to the
+// partial rows; ri is this lane's partial_row (lane r holds that of row r of
+// the wavefront's 32).  All 16 exchanges are issued before any store.
+__device__ __forceinline__ void epilogue_down(const GemmArgs& a, int lane, int cs, int g, int ri, v16f (&acc)[4]) {
+  int rows[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) rows[v] = __shfl(ri, out_row(v, lane), 64);
+  const bool full = (cs + 1) * DN_COLS <= a.d;  // the strip has no padding columns
+  const int col0 = cs * DN_COLS + (lane & 31);
+  // acc holds 2^-eg times the down product; scaled in place (pinned, so that
+  // the scaling is not sunk into the conditional stores below)
+  const int eg = __builtin_amdgcn_readfirstlane(a.dn_exp[g]);
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[tt][v] = ldexpf(acc[tt][v], eg);
+    anchor(acc[tt]);
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    if (rows[v] >= 0) {
+      float* dst = a.partial + (size_t)rows[v] * a.d + col0;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+        if (full || col0 + tt * 32 < a.d) dst[tt * 32] = acc[tt][v];
+    }
+  }
+}
+
 // Grouped GEMM.  GATEUP: A = the int8 token rows of the tile's (token, slot)
 // pairs, which the quantiser wrote in chunk form at their padded rows; B = the
 // [gate;up] strip of 64 SwiGLU columns; epilogue h = silu(gate) * up,
@@ -178,36 +216,34 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, char* lds, int lane,
         make_uint4(packed[4], packed[5], packed[6], packed[7]);
     a.hs[(((size_t)t32 * (a.kbmax / KSTEP) + (kbf >> 2)) * 32 + r) * KSTEP + (kbf & 3)] = s16;
   } else {
-    // Destination row of each of the lane's 16 output rows (lane r holds that
-    // of CSR row wrow0 + r); all 16 exchanges are issued before any store.
-    int ri = -1;
-    if (wrow0 + (lane & 31) < row_end && (unsigned)tok < (unsigned)a.n_tokens &&
-        (unsigned)slt < (unsigned)a.kk)
-      ri = tok * a.kk + slt;
-    int rows[16];
+    epilogue_down(a, lane, cs, g, partial_row(a, lane, wrow0, row_end, tok, slt), acc);
+  }
+}
+
+// The partial accumulators of a split row group, summed into its first
+// wavefront (si = 0) in the fixed order ((p0 + p1) + p2) + p3 through the
+// (then idle) stage buffers.  Every wavefront of the workgroup calls this.
+__device__ __forceinline__ void split_reduce(char* lds, int S, int rg, int si, int lane, v16f (&acc)[4]) {
+  __syncthreads();  // every wavefront is out of the k loop: the stage buffers are free
+  float* red = reinterpret_cast<float*>(lds);
+  if (si > 0) {
+    float* dst = red + (size_t)(rg * (S - 1) + si - 1) * 64 * 64;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) rows[v] = __shfl(ri, out_row(v, lane), 64);
-    const bool full = (cs + 1) * DN_COLS <= a.d;  // the strip has no padding columns
-    const int col0 = cs * DN_COLS + (lane & 31);
-    // acc holds 2^-eg times the down product; scaled in place (pinned, so that
-    // the scaling is not sunk into the conditional stores below)
-    const int eg = __builtin_amdgcn_readfirstlane(a.dn_exp[g]);
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+      for (int v = 0; v < 16; ++v) dst[(t * 16 + v) * 64 + lane] = acc[t][v];
+  }
+  __syncthreads();
+  if (si == 0) {
+    for (int p = 1; p < S; ++p) {
+      const float* src = red + (size_t)(rg * (S - 1) + p - 1) * 64 * 64;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[tt][v] = ldexpf(acc[tt][v], eg);
-      anchor(acc[tt]);
-    }
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      if (rows[v] >= 0) {
-        float* dst = a.partial + (size_t)rows[v] * a.d + col0;
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-          if (full || col0 + tt * 32 < a.d) dst[tt * 32] = acc[tt][v];
-      }
+        for (int v = 0; v < 16; ++v) acc[t][v] = acc[t][v] + src[(t * 16 + v) * 64 + lane];
     }
   }
+  __syncthreads();  // the reduction buffers are read before any epilogue reuses the LDS
 }
 
 inline int grid_for(long wgs) { return (int)((wgs + 7) / 8 * 8); }

@@ -110,12 +110,16 @@ struct OpsQ4 {
   uint2 b[4];
 };
 
-__device__ __forceinline__ void read_block_q4(const char* buf, int b, int wave, int lane, OpsQ4& o) {
+// a_off: LDS offset of the 32-row activation slab within the stage buffer.
+__device__ __forceinline__ void read_block_q4_at(const char* buf, int a_off, int b, int lane, OpsQ4& o) {
   // A: row lane%32, piece 2b + lane/32 of the k-step at its swizzled place
   const int r = lane & 31, p = 2 * b + (lane >> 5);
-  o.a = *reinterpret_cast<const v4i*>(buf + LayQ4::A_OFF + wave * (KSTEP * 1024) + r * 128 + ((p ^ (r & 7)) << 4));
+  o.a = *reinterpret_cast<const v4i*>(buf + a_off + r * 128 + ((p ^ (r & 7)) << 4));
 #pragma unroll
   for (int t = 0; t < 4; ++t) o.b[t] = *reinterpret_cast<const uint2*>(buf + (b * 4 + t) * 512 + lane * 8);
+}
+__device__ __forceinline__ void read_block_q4(const char* buf, int b, int wave, int lane, OpsQ4& o) {
+  read_block_q4_at(buf, LayQ4::A_OFF + wave * (KSTEP * 1024), b, lane, o);
 }
 
 // The k-step's scale operands: per tile the D and M pairs of this lane's
@@ -126,13 +130,19 @@ struct ScalesQ4 {
   uint2 sa;
 };
 
-__device__ __forceinline__ void read_scales_q4(const char* buf, int wave, int lane, ScalesQ4& s) {
+// as_off: LDS offset of the slab's activation scales within the stage buffer;
+// WITH_M: also the M pairs (the one-row-group form reads them separately).
+template <bool WITH_M = true>
+__device__ __forceinline__ void read_scales_q4_at(const char* buf, int as_off, int lane, ScalesQ4& s) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     s.dp[t] = *reinterpret_cast<const uint2*>(buf + Q4_D_OFF + t * 512 + lane * 8);
-    s.mp[t] = *reinterpret_cast<const uint2*>(buf + Q4_M_OFF + t * 512 + lane * 8);
+    if (WITH_M) s.mp[t] = *reinterpret_cast<const uint2*>(buf + Q4_M_OFF + t * 512 + lane * 8);
   }
-  s.sa = *reinterpret_cast<const uint2*>(buf + LayQ4::AS_OFF + wave * 256 + (lane & 31) * 8);
+  s.sa = *reinterpret_cast<const uint2*>(buf + as_off + (lane & 31) * 8);
+}
+__device__ __forceinline__ void read_scales_q4(const char* buf, int wave, int lane, ScalesQ4& s) {
+  read_scales_q4_at(buf, LayQ4::AS_OFF + wave * 256, lane, s);
 }
 
 // The 16 codes of a packed B piece widened to bytes (0..15), in K order.
@@ -157,14 +167,18 @@ __device__ __forceinline__ uint32_t half_code_sum(const v4i a) {
   return (uint32_t)__builtin_amdgcn_sdot4(a.w, 0x01010101, s, false);
 }
 
+// This lane's biased half code sums of a k-step's 4 blocks, 16 bits each:
+// x = blocks 0 and 1, y = blocks 2 and 3 (low half first).
+constexpr uint32_t PS_ZERO = 0x08000800u;  // both fields at the bias: P = 0
+
 // A operand of the min-term MFMA of a k-step: lane half h covers blocks 2h
 // and 2h+1 of its row, K slots {-P_hi, -P_hi, -P_lo, -P_lo} per block against
-// the B slots {M_hi, M_lo, M_hi, M_lo}.  ps[b] are this lane's biased half
-// sums; the partner lane (l ^ 32) supplies the other halves.
-__device__ __forceinline__ v8h min_term_a(const uint32_t (&ps)[4], const uint2 sa, int lane) {
+// the B slots {M_hi, M_lo, M_hi, M_lo}.  The partner lane (l ^ 32) supplies
+// the other halves of the sums.
+__device__ __forceinline__ v8h min_term_a(const uint2 ps, const uint2 sa, int lane) {
   const bool hi_half = lane >= 32;
-  const uint32_t own = hi_half ? (ps[2] | (ps[3] << 16)) : (ps[0] | (ps[1] << 16));
-  const uint32_t give = hi_half ? (ps[0] | (ps[1] << 16)) : (ps[2] | (ps[3] << 16));
+  const uint32_t own = hi_half ? ps.y : ps.x;
+  const uint32_t give = hi_half ? ps.x : ps.y;
   // The two results are this lane's own value and its partner's, in an order
   // that depends on the lane half; their sum minus the own value is the
   // partner's.
@@ -194,15 +208,21 @@ __device__ __forceinline__ v8h min_term_b(const uint2 mp) {
 // pipeline: per tile t the int8 MFMA(t+2) on the widened codes, a third of
 // acc(t) = fma(cf(t), s(t), acc(t)), the conversion MFMA(t+1), a third, the
 // scale MFMA(t+1), the last third; in the k-step's last block (last) the
-// min-term MFMA of tile t follows.  ps collects the half code sums of the
-// k-step's blocks.
+// min-term MFMA of tile t follows, with the k-step's M pairs mp.  ps collects
+// the half code sums of the k-step's blocks.
 template <typename H = NoHook>
 __device__ __forceinline__ void compute_block_q4(const OpsQ4& o, const ScalesQ4& sc, int b, const OpsQ4& on,
-                                                 const ScalesQ4& sn, int bn, bool last, const Ctx& cx, int lane,
-                                                 uint32_t (&ps)[4], v16i& dn, v16f& cf, v16f& s, v16f (&acc)[4],
-                                                 const H& hook = H()) {
+                                                 const ScalesQ4& sn, int bn, bool last, const uint2 (&mp)[4],
+                                                 const Ctx& cx, int lane, uint2& ps, v16i& dn, v16f& cf,
+                                                 v16f& s, v16f (&acc)[4], const H& hook = H()) {
   const v16f zf = {0};
-  ps[b] = half_code_sum(o.a);
+  // (b may be a run-time value in the split forms: selects, not an indexed store)
+  const uint32_t hs = half_code_sum(o.a);
+  const uint32_t field = (b & 1) ? (hs << 16) : hs, keep = (b & 1) ? 0x0000ffffu : 0xffff0000u;
+  if (b < 2)
+    ps.x = (ps.x & keep) | field;
+  else
+    ps.y = (ps.y & keep) | field;
   v8h pa;
   if (last) pa = min_term_a(ps, sc.sa, lane);
   v4h sav = sa_slot_q4(sc.sa, b);
@@ -231,7 +251,10 @@ __device__ __forceinline__ void compute_block_q4(const OpsQ4& o, const ScalesQ4&
     for (int v = 10; v < 16; ++v) acc[t][v] = __builtin_fmaf(cf[v], s[v], acc[t][v]);
     anchor(acc[t]);
     if (last) {
-      acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa, min_term_b(sc.mp[t]), acc[t], 0, 0, 0);
+      // the B operand built here, not hoisted: one at a time is live
+      v8h mb = min_term_b(mp[t]);
+      anchor(mb, acc[t]);
+      acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa, mb, acc[t], 0, 0, 0);
       anchor(acc[t]);
     }
     dn = dnn;
@@ -247,36 +270,142 @@ __device__ __forceinline__ void compute_block_q4(const OpsQ4& o, const ScalesQ4&
 // before block 3, and the weights of k-step j+2 go out during block 3.
 __device__ __forceinline__ void kstep_q4(const Src& src, int j, int KS, int wave, int lane, const char* cur,
                                          const char* nxt, uint32_t cur_lds, uint32_t nxt_lds, OpsQ4& X, OpsQ4& Y,
-                                         const ScalesQ4& sc, ScalesQ4& sn, const Ctx& cx, uint32_t (&ps)[4],
+                                         const ScalesQ4& sc, ScalesQ4& sn, const Ctx& cx, uint2& ps,
                                          v16i& c, v16f& cf, v16f& s, v16f (&acc)[4]) {
   const bool acts = j >= 1 && j + 1 < KS;
   read_block_q4(cur, 1, wave, lane, Y);
-  compute_block_q4(X, sc, 0, Y, sc, 1, false, cx, lane, ps, c, cf, s, acc, [&](int t) {
+  compute_block_q4(X, sc, 0, Y, sc, 1, false, sc.mp, cx, lane, ps, c, cf, s, acc, [&](int t) {
     if (acts) issue_acts_part_q4(src, j + 1, nxt_lds, wave, lane, t);
   });
   read_block_q4(cur, 2, wave, lane, X);
-  compute_block_q4(Y, sc, 1, X, sc, 2, false, cx, lane, ps, c, cf, s, acc);
+  compute_block_q4(Y, sc, 1, X, sc, 2, false, sc.mp, cx, lane, ps, c, cf, s, acc);
   read_block_q4(cur, 3, wave, lane, Y);
-  compute_block_q4(X, sc, 2, Y, sc, 3, false, cx, lane, ps, c, cf, s, acc);
+  compute_block_q4(X, sc, 2, Y, sc, 3, false, sc.mp, cx, lane, ps, c, cf, s, acc);
   if (j + 1 < KS) wait_copies_barrier_0();
   const bool weights = j + 2 < KS;
   read_block_q4(nxt, 0, wave, lane, X);
   read_scales_q4(nxt, wave, lane, sn);
-  compute_block_q4(Y, sc, 3, X, sn, 0, true, cx, lane, ps, c, cf, s, acc, [&](int t) {
+  compute_block_q4(Y, sc, 3, X, sn, 0, true, sc.mp, cx, lane, ps, c, cf, s, acc, [&](int t) {
     if (weights) issue_weights_part_q4(src, j + 2, cur_lds, wave, t);
   });
 }
 
-// One (tile, strip) workgroup: wavefront w computes the tile's 32-row group w
-// (a wavefront past the tile's rows only copies and meets the barriers), then
-// runs the format-independent epilogue.
-template <bool GATEUP>
+// Split-K k-step of a two-row-group tile (the split-K follow-up of #406
+// "References"): the two wavefronts of a row group compute blocks si and
+// si + 2 of every k-step into their own accumulators (the min term over those
+// two blocks only: the code sums of the other two stay at their bias, so
+// their P is zero).  Copies, barrier and their placement are those of
+// kstep_q4; each wavefront copies its row group's slab into its own area.
+__device__ __forceinline__ void kstep_q4_split2(const Src& src, int j, int KS, int wave, int lane, int si,
+                                                const char* cur, const char* nxt, uint32_t cur_lds,
+                                                uint32_t nxt_lds, OpsQ4& X, OpsQ4& Y, const ScalesQ4& sc,
+                                                ScalesQ4& sn, const Ctx& cx, uint2& ps, v16i& c, v16f& cf,
+                                                v16f& s, v16f (&acc)[4]) {
+  const bool acts = j >= 1 && j + 1 < KS;
+  read_block_q4(cur, si + 2, wave, lane, Y);
+  compute_block_q4(X, sc, si, Y, sc, si + 2, false, sc.mp, cx, lane, ps, c, cf, s, acc, [&](int t) {
+    if (acts) issue_acts_part_q4(src, j + 1, nxt_lds, wave, lane, t);
+  });
+  if (j + 1 < KS) wait_copies_barrier_0();
+  const bool weights = j + 2 < KS;
+  read_block_q4(nxt, si, wave, lane, X);
+  read_scales_q4(nxt, wave, lane, sn);
+  compute_block_q4(Y, sc, si + 2, X, sn, si, true, sc.mp, cx, lane, ps, c, cf, s, acc, [&](int t) {
+    if (weights) issue_weights_part_q4(src, j + 2, cur_lds, wave, t);
+  });
+}
+
+// One-row-group tiles: the four wavefronts split every k-step (wavefront si
+// computes block si), so the k loop is bound by the copies' latency; as in
+// the Q8_0 kernel these tiles keep three k-steps in LDS (a stage holds the
+// weight k-step and the single activation slab) and issue k-step j+3's copies
+// at k-step j's barrier.
+struct Lay1Q4 {
+  static constexpr int A_OFF = Q4K_KSTEP_BYTES;                    // the slab [row][128 B]
+  static constexpr int AS_OFF = A_OFF + KSTEP * 1024;              // its scales [32 rows][4 blocks]
+  static constexpr int STAGE = AS_OFF + 32 * KSTEP * 2;            // 16.25 KiB
+  static constexpr int DMA = Q4K_KSTEP_BYTES / 1024 / NWAVE + 2;   // copies per wavefront per k-step
+};
+static_assert(3 * Lay1Q4::STAGE <= 2 * LayQ4::STAGE, "three stages must fit in the LDS buffers");
+// Down: the (token, slot) of each lane's CSR row, copied into LDS past the
+// three stages (and past the split reduction's buffers), so that they occupy
+// no registers during the k loop.
+constexpr int T1_PAIR_OFF = 3 * Lay1Q4::STAGE;
+static_assert(T1_PAIR_OFF + 2 * 64 * 4 <= 2 * LayQ4::STAGE, "pair slots must fit in the LDS buffers");
+static_assert(3 * 64 * 64 * 4 <= T1_PAIR_OFF, "the split reduction must not reach the pair slots");
+static_assert(Lay1Q4::STAGE % 256 == 0, "stage alignment");
+
+// This wavefront's copies of k-step j into the stage at LDS address L: its
+// three weight pieces, chunk `wave` of the slab and the slab's scales (every
+// wavefront copies the same 256 bytes, so that all issue the same number).
+__device__ __forceinline__ void issue_kstep1_q4(const Src& s, int j, uint32_t L, int wave, int lane) {
+  issue_weights_q4(s, j, L, wave);
+  dma16(s.a + (size_t)j * KSTEP * 1024 + wave * 1024, lane * 16, L + Lay1Q4::A_OFF + wave * 1024);
+  dma4(s.as + (size_t)j * 32 * KSTEP, lane * 4, L + Lay1Q4::AS_OFF);
+}
+
+// K-step j of a one-row-group tile.  On entry X and sc hold block si of
+// k-step j; k-steps j+1 and j+2 are in flight.  The barrier publishes k-step
+// j+1 and proves that every wavefront has read k-step j, whose stage then
+// receives k-step j+3.  On exit Y and sn hold block si of k-step j+1.
+__device__ __forceinline__ void kstep1_q4(const Src& src, int j, int KS, int wave, int lane, int si, const char* lds,
+                                          uint32_t lds_base, const OpsQ4& X, OpsQ4& Y, const ScalesQ4& sc,
+                                          ScalesQ4& sn, const Ctx& cx, uint2& ps, v16i& c, v16f& cf, v16f& s,
+                                          v16f (&acc)[4]) {
+  const int st = j % 3;
+  const int sn1 = st == 2 ? 0 : st + 1;
+  // This k-step's M pairs, read here rather than with its other scales one
+  // k-step earlier (fewer registers live across a k-step); its stage takes
+  // new copies only after the barrier below, which waits for these reads.
+  uint2 mp[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) mp[t] = *reinterpret_cast<const uint2*>(lds + st * Lay1Q4::STAGE + Q4_M_OFF + t * 512 + lane * 8);
+  if (j + 1 < KS) {
+    if (j + 2 < KS)
+      wait_copies_reads_barrier<Lay1Q4::DMA>();
+    else
+      wait_copies_reads_barrier<0>();
+    if (j + 3 < KS) issue_kstep1_q4(src, j + 3, lds_base + st * Lay1Q4::STAGE, wave, lane);
+  }
+  const char* nb = lds + sn1 * Lay1Q4::STAGE;
+  read_block_q4_at(nb, Lay1Q4::A_OFF, si, lane, Y);
+  read_scales_q4_at<false>(nb, Lay1Q4::AS_OFF, lane, sn);
+  compute_block_q4(X, sc, si, Y, sn, si, true, mp, cx, lane, ps, c, cf, s, acc);
+}
+
+// Pipeline constants and the state of (block si, tile 0) from the first
+// block's operands X and scales s0: the int8 MFMA of tile 1, float(C) and the
+// scale product of tile 0.
+__device__ __forceinline__ void pipeline_init_q4(const OpsQ4& X, const ScalesQ4& s0, int si, int lane, Ctx& cx,
+                                                 v16i& c, v16f& cf, v16f& s) {
+  const v16f zf = {0};
+#pragma unroll
+  for (int v = 0; v < 16; ++v) cx.magic[v] = 0x4b400000;  // 1.5 * 2^23
+  anchor(cx.magic);
+  const _Float16 h0 = 0;
+  cx.sub_a = lane < 32 ? (v4h){(_Float16)-3072.0f, h0, h0, h0} : (v4h){h0, h0, h0, h0};
+  cx.sub_b = lane < 32 ? (v4h){(_Float16)4096.0f, h0, h0, h0} : (v4h){h0, h0, h0, h0};
+  anchor(cx.sub_a, cx.sub_b);
+  const v16i d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(X.a, widen_codes(X.b[0]), cx.magic, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_i32_32x32x32_i8(X.a, widen_codes(X.b[1]), cx.magic, 0, 0, 0);
+  cf = __builtin_amdgcn_mfma_f32_32x32x8f16(cx.sub_a, cx.sub_b, __builtin_bit_cast(v16f, d0), 0, 0, 0);
+  s = __builtin_amdgcn_mfma_f32_32x32x8f16(sa_slot_q4(s0.sa, si), as_v4h(s0.dp[0]), zf, 0, 0, 0);
+}
+
+// One (tile, strip) workgroup whose tile has three or four 32-row groups (S =
+// 1: wavefront w computes row group w; a wavefront past the tile's rows only
+// copies and meets the barriers) or two (S = 2: kstep_q4_split2, the row
+// group's partial sums added in a fixed order), then the format-independent
+// epilogue.  Each S is a self-contained body with its own register allocation.
+template <bool GATEUP, int S>
 __device__ __forceinline__ void tile_work_q4(const GemmArgs& a, char (&lds)[2][LayQ4::STAGE], int lane, int wave,
                                              int T, int cs, int g, int row0, int row_end, int KS,
                                              const uint8_t* strip) {
-  const int wrow0 = row0 + MT_WAVE * wave;
-  const bool active = wrow0 < row_end;
-  const int t32 = T * NWAVE + wave;
+  static_assert(S == 1 || S == 2, "split factors of tile_work_q4");
+  const int rg = wave / S, si = wave - rg * S;
+  const int wrow0 = row0 + MT_WAVE * rg;
+  const bool active = wrow0 < row_end;  // every wavefront when S > 1
+  const int t32 = T * NWAVE + rg;
   const int a_kb = GATEUP ? a.d_pad / QB : a.kbmax;
   Src src;
   src.w = strip;
@@ -312,30 +441,27 @@ __device__ __forceinline__ void tile_work_q4(const GemmArgs& a, char (&lds)[2][L
     OpsQ4 X, Y;
     ScalesQ4 s0, s1;
     Ctx cx;
-    read_block_q4(lds[0], 0, wave, lane, X);
+    read_block_q4(lds[0], si, wave, lane, X);
     read_scales_q4(lds[0], wave, lane, s0);
-#pragma unroll
-    for (int v = 0; v < 16; ++v) cx.magic[v] = 0x4b400000;  // 1.5 * 2^23
-    anchor(cx.magic);
-    const _Float16 h0 = 0;
-    cx.sub_a = lane < 32 ? (v4h){(_Float16)-3072.0f, h0, h0, h0} : (v4h){h0, h0, h0, h0};
-    cx.sub_b = lane < 32 ? (v4h){(_Float16)4096.0f, h0, h0, h0} : (v4h){h0, h0, h0, h0};
-    anchor(cx.sub_a, cx.sub_b);
-    // pipeline state of (block 0, tile 0): int8 MFMA of tile 1, float(C) and
-    // the scale product of tile 0
-    const v16f zf = {0};
-    const v16i d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(X.a, widen_codes(X.b[0]), cx.magic, 0, 0, 0);
-    v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(X.a, widen_codes(X.b[1]), cx.magic, 0, 0, 0);
-    v16f cf = __builtin_amdgcn_mfma_f32_32x32x8f16(cx.sub_a, cx.sub_b, __builtin_bit_cast(v16f, d0), 0, 0, 0);
-    v16f s = __builtin_amdgcn_mfma_f32_32x32x8f16(sa_slot_q4(s0.sa, 0), as_v4h(s0.dp[0]), zf, 0, 0, 0);
-    uint32_t ps[4] = {0u, 0u, 0u, 0u};
+    v16i c;
+    v16f cf, s;
+    pipeline_init_q4(X, s0, si, lane, cx, c, cf, s);
+    uint2 ps = make_uint2(PS_ZERO, PS_ZERO);  // code sums of blocks this wavefront skips stay zero
     // Unrolled by two so that each buffer and scale set has a fixed role.
     for (int j = 0; j < KS; j += 2) {
-      kstep_q4(src, j, KS, wave, lane, lds[0], lds[1], lds0, lds1, X, Y, s0, s1, cx, ps, c, cf, s, acc);
-      if (j + 1 < KS)
-        kstep_q4(src, j + 1, KS, wave, lane, lds[1], lds[0], lds1, lds0, X, Y, s1, s0, cx, ps, c, cf, s, acc);
+      if constexpr (S == 1) {
+        kstep_q4(src, j, KS, wave, lane, lds[0], lds[1], lds0, lds1, X, Y, s0, s1, cx, ps, c, cf, s, acc);
+        if (j + 1 < KS)
+          kstep_q4(src, j + 1, KS, wave, lane, lds[1], lds[0], lds1, lds0, X, Y, s1, s0, cx, ps, c, cf, s, acc);
+      } else {
+        kstep_q4_split2(src, j, KS, wave, lane, si, lds[0], lds[1], lds0, lds1, X, Y, s0, s1, cx, ps, c, cf, s,
+                        acc);
+        if (j + 1 < KS)
+          kstep_q4_split2(src, j + 1, KS, wave, lane, si, lds[1], lds[0], lds1, lds0, X, Y, s1, s0, cx, ps, c, cf,
+                          s, acc);
+      }
     }
-  } else {
+  } else if constexpr (S == 1) {
     for (int j = 0; j + 1 < KS; ++j) {
       if (j >= 1) issue_acts_q4(src, j + 1, (j & 1) ? lds0 : lds1, wave, lane);
       wait_copies_barrier_0();
@@ -343,10 +469,76 @@ __device__ __forceinline__ void tile_work_q4(const GemmArgs& a, char (&lds)[2][L
     }
   }
   // gate/up: every wavefront is out of the k loop, so LDS is free for the
-  // epilogue's scratch.
-  if (GATEUP) __syncthreads();
-  if (!active) return;
+  // epilogue's scratch.  Split-K: the row group's partial sums meet in its
+  // first wavefront, which alone runs the epilogue.
+  if constexpr (S > 1)
+    split_reduce(&lds[0][0], S, rg, si, lane, acc);
+  else if (GATEUP)
+    __syncthreads();
+  if (!active || si != 0) return;
   epilogue<GATEUP>(a, &lds[0][0], lane, wave, t32, cs, g, wrow0, row_end, tok, slt, acc);
+}
+
+// A (tile, strip) workgroup whose tile has one 32-row group: the three-stage
+// pipeline of kstep1_q4, the fixed-order sum of the four wavefronts' partial
+// accumulators, and the epilogue in wavefront 0.
+template <bool GATEUP>
+__device__ __forceinline__ void tile_work1_q4(const GemmArgs& a, char* lds, int lane, int wave, int T, int cs, int g,
+                                              int row0, int row_end, int KS, const uint8_t* strip) {
+  const int si = wave;
+  const int t32 = T * NWAVE;
+  const int a_kb = GATEUP ? a.d_pad / QB : a.kbmax;
+  Src src;
+  src.w = strip;
+  src.o_w = lane * 16;
+  src.o_ws = 0;
+  src.a = (GATEUP ? a.gq : a.hq) + (size_t)t32 * a_kb * 1024;
+  src.as = (GATEUP ? a.gqs : a.hs) + (size_t)t32 * a_kb * 32;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_char*)lds;
+
+  // Down: the (token, slot) of this lane's CSR row, copied into LDS before
+  // any other copy (vector loads complete in order, so the waits below cover
+  // them too; every wavefront issues the same two copies).
+  if (!GATEUP) {
+    const int p_lane = min(row0 + (lane & 31), a.p_total - 1);
+    dma4(a.tok_i, (uint32_t)p_lane * 4, lds_base + T1_PAIR_OFF);
+    dma4(a.tok_k, (uint32_t)p_lane * 4, lds_base + T1_PAIR_OFF + 256);
+  }
+  // Prologue: k-steps 0, 1 and 2 in flight; wait for k-step 0.
+  issue_kstep1_q4(src, 0, lds_base, wave, lane);
+  if (KS > 1) issue_kstep1_q4(src, 1, lds_base + Lay1Q4::STAGE, wave, lane);
+  if (KS > 2) issue_kstep1_q4(src, 2, lds_base + 2 * Lay1Q4::STAGE, wave, lane);
+  if (KS > 2)
+    wait_copies_reads_barrier<2 * Lay1Q4::DMA>();
+  else if (KS > 1)
+    wait_copies_reads_barrier<Lay1Q4::DMA>();
+  else
+    wait_copies_reads_barrier<0>();
+
+  v16f acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = (v16f){0};
+  OpsQ4 X, Y;
+  ScalesQ4 s0, s1;
+  Ctx cx;
+  read_block_q4_at(lds, Lay1Q4::A_OFF, si, lane, X);
+  read_scales_q4_at<false>(lds, Lay1Q4::AS_OFF, lane, s0);
+  v16i c;
+  v16f cf, s;
+  pipeline_init_q4(X, s0, si, lane, cx, c, cf, s);
+  uint2 ps = make_uint2(PS_ZERO, PS_ZERO);
+  for (int j = 0; j < KS; j += 2) {
+    kstep1_q4(src, j, KS, wave, lane, si, lds, lds_base, X, Y, s0, s1, cx, ps, c, cf, s, acc);
+    if (j + 1 < KS) kstep1_q4(src, j + 1, KS, wave, lane, si, lds, lds_base, Y, X, s1, s0, cx, ps, c, cf, s, acc);
+  }
+  split_reduce(lds, 4, 0, si, lane, acc);
+  if (si != 0) return;
+  if constexpr (GATEUP) {
+    epilogue<true>(a, lds, lane, 0, t32, cs, g, row0, row_end, -1, -1, acc);
+  } else {
+    const int* pairs = reinterpret_cast<const int*>(lds + T1_PAIR_OFF);
+    epilogue_down(a, lane, cs, g, partial_row(a, lane, row0, row_end, pairs[lane], pairs[64 + lane]), acc);
+  }
 }
 
 // Grouped Q4_K GEMM over the tile table, with the workgroup numbering of the
@@ -380,7 +572,15 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_q4k_kernel(GemmArgs a) {
   const uint8_t* strip = GATEUP ? (shared ? a.sh_gu : a.gu + (size_t)g * a.gu_group)
                                 : (shared ? a.sh_dn : a.dn + (size_t)g * a.dn_group);
   strip += (size_t)cs * KS * Q4K_KSTEP_BYTES;
-  tile_work_q4<GATEUP>(a, lds, lane, wave, T, cs, g, row0, row_end, KS, strip);
+  // Split-K when the tile's rows fill only one or two of the four 32-row
+  // wavefront slots (the skew-aware tiles of the Q8_0 kernel).
+  const int nact = (min(row_end - row0, MT_WG) + MT_WAVE - 1) / MT_WAVE;
+  if (nact >= 3)
+    tile_work_q4<GATEUP, 1>(a, lds, lane, wave, T, cs, g, row0, row_end, KS, strip);
+  else if (nact == 2)
+    tile_work_q4<GATEUP, 2>(a, lds, lane, wave, T, cs, g, row0, row_end, KS, strip);
+  else
+    tile_work1_q4<GATEUP>(a, &lds[0][0], lane, wave, T, cs, g, row0, row_end, KS, strip);
 }
 
 }  // namespace
