@@ -156,8 +156,8 @@ int moe_ffn_weights_create(const moe_ffn_dims* dims, const float* router_w,
  * fp32.  Q4_K needs d_model, d_ffn and d_shared_ffn to be multiples of 256
  * (else MOE_FFN_UNSUPPORTED), and rejects with MOE_FFN_UNSUPPORTED weights
  * whose d * sc or dmin * m overflows binary16.  A Q4_K handle serves every
- * prefill entry point; moe_ffn_decode and moe_ffn_dbg_block_sums return
- * MOE_FFN_UNSUPPORTED for it.
+ * prefill entry point and moe_ffn_decode (which then runs the prefill
+ * launches); moe_ffn_dbg_block_sums returns MOE_FFN_UNSUPPORTED for it.
  * MOE_FFN_FMT_Q3_K (the format of the Q3_K expert GEMM of #388 "Key
  * references"): each row of n values is n/256 super-blocks of 110 bytes {32
  * bytes of high bits, 64 bytes of 2-bit codes, 12 bytes of 6-bit sub-block
@@ -291,7 +291,8 @@ int moe_ffn_prefill_profiled(const moe_ffn_weights* w, const float* x, int32_t n
  * 1 <= n_tokens <= 8, with the expert FFN run by one gathered launch per
  * stage in which each selected expert's weights are read once for all the
  * tokens that picked it.  Returns MOE_FFN_INVALID_ARG for n_tokens outside
- * [1, 8], MOE_FFN_UNSUPPORTED for Q4_K weights. */
+ * [1, 8].  For Q4_K weights (whose planes the gathered matvecs do not read)
+ * the call runs the prefill launches instead, with the same results contract. */
 int moe_ffn_decode(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* out,
                    void* ws, size_t ws_bytes, const moe_ffn_routing* routing,
                    hipStream_t stream);

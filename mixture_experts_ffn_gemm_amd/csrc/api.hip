@@ -283,7 +283,16 @@ int run_decode(const moe_ffn_weights* W, const float* x, int32_t n, float* out, 
                size_t ws_bytes, const moe_ffn_routing* r, hipStream_t s, hipEvent_t* ev = nullptr) {
   if (!W || n < 1 || n > DECODE_MAX_TOKENS) return MOE_FFN_INVALID_ARG;
   if (!x || !out || !ws) return MOE_FFN_INVALID_ARG;
-  if (W->fmt != MOE_FFN_FMT_Q8_0) return MOE_FFN_UNSUPPORTED;  // the matvecs read Q8_0 planes only
+  // The gathered matvecs read the Q8_0 planes; Q4_K planes go through the
+  // prefill launches.  The decode stage events then bracket router, routing
+  // and bucketing + quantiser (event 1 is recorded again before each of
+  // those launches' successors, and its last record counts), gate/up, down
+  // and the combine.
+  if (W->fmt != MOE_FFN_FMT_Q8_0) {
+    if (!ev) return run_layer(W, x, n, out, ws, ws_bytes, r, s);
+    hipEvent_t pe[MOE_FFN_N_STAGE_EVENTS] = {ev[0], ev[1], ev[1], ev[1], ev[2], ev[3], ev[4]};
+    return run_layer(W, x, n, out, ws, ws_bytes, r, s, pe);
+  }
   const Dims& dm = W->dm;
   const WsLayout L = ws_layout(dm, n);
   if (ws_bytes < L.total) return MOE_FFN_WORKSPACE_TOO_SMALL;

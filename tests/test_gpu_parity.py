@@ -429,9 +429,55 @@ def test_q4k_mid_size_all_tokens():
     say(f"q4k mid: max group {int(counts.max())} rows, rel_l2={r:.2e} max_elem={e:.2e}")
 
 
+@pytest.mark.parametrize("n", [1, 8])
+def test_q4k_decode_runs_the_prefill_launches(n):
+    """moe_ffn_decode on a Q4_K handle (the gathered matvecs read Q8_0 planes
+    only, so the call runs the prefill launches): routing bit-exact, outputs
+    against the oracle."""
+    shape, lw = mw.random_shape_case(41, fmt="q4_k", **Q4K_SHAPES[1])
+    x = mw.make_tokens(941 + n, n, shape.d)
+    g = run_gpu(lw, x, api="decode")
+    check_routing(lw, x, g)
+    r, e = check_outputs(lw, x, g)
+    say(f"q4k decode n={n}: rel_l2={r:.2e} max_elem={e:.2e}")
+
+
+def test_q4k_chunked_residual_and_static():
+    """The Q4_K GEMMs through the other prefill entry points: chunked (100
+    tokens per chunk, serpentine) against the oracle, the stack form bit for
+    bit against prefill + residual RMSNorm, and the no-alloc entry point bit
+    for bit against prefill."""
+    from mixture_experts_ffn_gemm_amd import binding as B
+    from mixture_experts_ffn_gemm_amd.layer import MoeLayer
+    shape, lw = mw.random_shape_case(42, fmt="q4_k", **Q4K_SHAPES[1])
+    n, d, eps = 300, shape.d, 1e-5
+    x_np = mw.make_tokens(942, n, d)
+    layer = MoeLayer.from_workload(lw)
+    try:
+        x = torch.from_numpy(x_np).cuda()
+        full = layer.prefill(x)
+        ws = torch.empty(layer.workspace_size(100), dtype=torch.uint8, device="cuda")
+        ch = torch.full((n, d), float("nan"), dtype=torch.float32, device="cuda")
+        B.moe_ffn_prefill_chunked(layer.handle, x, n, 100, B.CHUNK_SERPENTINE, ch, ws, ws.numel())
+        h0 = torch.from_numpy(mw.make_tokens(943, n, d)).cuda()
+        h_ref, xn_ref = h0.clone(), torch.empty_like(h0)
+        B.moe_ffn_residual_rmsnorm(h_ref, full, xn_ref, n, d, eps)
+        h1, xn1 = h0.clone(), torch.empty_like(h0)
+        layer.prefill_residual(x, h1, xn1, eps)
+        st = torch.empty_like(full)
+        B.moe_ffn_prefill_static(layer.handle, x, n, st)
+        torch.cuda.synchronize()
+    finally:
+        layer.close()
+    r, e = moe_close(ch.cpu().numpy(), O.moe_tokens(lw, x_np)["out"])
+    assert torch.equal(h1, h_ref) and torch.equal(xn1, xn_ref)
+    assert torch.equal(st, full)
+    say(f"q4k chunked: rel_l2={r:.2e} max_elem={e:.2e}; stack form and no-alloc entry bit-identical")
+
+
 def test_q4k_unsupported_entry_points():
-    """Decode and the Q8_0 block-sum dump reject a Q4_K handle before
-    enqueueing anything; a prefill on the same handle still works after."""
+    """The Q8_0 block-sum dump rejects a Q4_K handle before enqueueing
+    anything; prefill and decode on the same handle work."""
     from mixture_experts_ffn_gemm_amd import binding as B
     from mixture_experts_ffn_gemm_amd.layer import MoeLayer
     shape, lw = mw.random_shape_case(40, fmt="q4_k", **Q4K_SHAPES[0])
@@ -439,9 +485,7 @@ def test_q4k_unsupported_entry_points():
     layer = MoeLayer.from_workload(lw)
     try:
         xt = torch.from_numpy(x).cuda()
-        with pytest.raises(B.MoeFfnError) as ei:
-            layer.decode(xt)
-        assert ei.value.status == B.MOE_FFN_UNSUPPORTED
+        dec = layer.decode(xt)
         layer.prefill(xt)
         ws = layer.workspace(4)
         sums = torch.empty((128, 128), dtype=torch.int32, device="cuda")
@@ -452,7 +496,9 @@ def test_q4k_unsupported_entry_points():
         assert ei.value.status == B.MOE_FFN_UNSUPPORTED
         out = layer.prefill(xt)
         torch.cuda.synchronize()
-        moe_close(out.cpu().numpy(), O.moe_tokens(lw, x)["out"])
+        ref = O.moe_tokens(lw, x)["out"]
+        moe_close(out.cpu().numpy(), ref)
+        moe_close(dec.cpu().numpy(), ref)
     finally:
         layer.close()
 
