@@ -80,11 +80,12 @@ def gemm_ops(shape, n_tokens):
 def stage_bytes(shape, n_tokens, counts, fmt="q8_0"):
     """Algorithmic HBM bytes per stage: what the method must read or write
     once (weights of the experts the batch touches, activations, partials).
-    Weight bytes per value: Q8_0 34/32, Q4_K 144/256."""
+    Weight bytes per value: Q8_0 34/32, Q4_K 144/256, Q3_K 110/256 (the
+    format's bytes; the library reads Q3_K experts from int8 planes)."""
     d, F, k, E = shape.d, shape.ffn, shape.top_k, shape.n_experts
     kk = k + (1 if shape.shared_ffn else 0)
     touched = sum(1 for c in counts[:E] if c > 0)
-    q8 = 144.0 / 256.0 if fmt == "q4_k" else 34.0 / 32.0
+    q8 = {"q4_k": 144.0 / 256.0, "q3_k": 110.0 / 256.0}.get(fmt, 34.0 / 32.0)
     gu_w = touched * 2 * F * d * q8 + (2 * shape.shared_ffn * d * q8 if shape.shared_ffn else 0)
     dn_w = touched * d * F * q8 + (d * shape.shared_ffn * q8 if shape.shared_ffn else 0)
     P = n_tokens * k + (n_tokens if shape.shared_ffn else 0)
@@ -526,7 +527,7 @@ def main():
                                 "the GPU holds under this load rather than one still ramping up from idle"},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
         "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights packed as %s)"
-                % ("Q4_K" if wl.fmt == "q4_k" else "Q8_0"),
+                % {"q4_k": "Q4_K", "q3_k": "Q3_K"}.get(wl.fmt, "Q8_0"),
         "config": {"workload": args.workload, **{k: v for k, v in mw.describe(args.workload).items()
                                                  if k != "workload"}},
         "grouped_gemm_int8_frac": round(gemm_frac, 4),
