@@ -400,6 +400,9 @@ Q4K_SHAPES = [
     dict(d=256, E=8, k=2, F=256),                                 # one super-block per row
     dict(d=512, E=16, k=3, F=256, Fs=512, zipf=1.1, norm=True),   # shared expert, Fs != F, skew
     dict(d=256, E=70, k=4, F=512),                                # E > 64: routing in its own launch
+    dict(d=256, E=1, k=1, F=256, norm=True),                      # a single expert (dense FFN)
+    dict(d=256, E=5, k=5, F=256, norm=True),                      # k = E
+    dict(d=256, E=256, k=16, F=256, Fs=256),                      # E = 256, k = 16, shared
 ]
 
 
@@ -553,6 +556,8 @@ Q3K_SHAPES = [
     dict(d=256, E=8, k=2, F=256),
     dict(d=512, E=16, k=3, F=256, Fs=512, zipf=1.1, norm=True),
     dict(d=256, E=70, k=4, F=512),
+    dict(d=256, E=1, k=1, F=256, norm=True),
+    dict(d=256, E=256, k=16, F=256, Fs=256),
 ]
 
 
