@@ -76,7 +76,9 @@ struct QuantArgs {
   uint16_t* xs_out;
 };
 
-__global__ __launch_bounds__(BQ_THREADS) void bucket_quantize_kernel(
+// At most 128 VGPRs (four wavefronts per SIMD), so that two 512-thread
+// workgroups share a CU when there are more tiles than CUs.
+__global__ __launch_bounds__(BQ_THREADS) __attribute__((amdgpu_waves_per_eu(4, 8))) void bucket_quantize_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ rank,
     const int32_t* __restrict__ hist, int n, int E, int k, int has_shared, int n_tiles,
     int32_t* __restrict__ exp_start, int32_t* __restrict__ tok_i, int32_t* __restrict__ tok_k,
@@ -212,9 +214,6 @@ __global__ __launch_bounds__(BQ_THREADS) void bucket_quantize_kernel(
   // Quantise and scatter: wavefront w takes token t0 + w.
   if (wave >= nt) return;
   const int t = t0 + wave;
-  int prow[MAX_TOPK + 1];
-#pragma unroll
-  for (int s2 = 0; s2 < MAX_TOPK + 1; ++s2) prow[s2] = (s2 < kk) ? s_pos[wave][s2] : -1;
   float gacc = 0.0f;
   // Each pass covers 8 k-steps; the pass after next is requested before this
   // pass is quantised and scattered.
@@ -240,7 +239,7 @@ __global__ __launch_bounds__(BQ_THREADS) void bucket_quantize_kernel(
       const uint4 codes = make_uint4(pk[0], pk[1], pk[2], pk[3]);
 #pragma unroll
       for (int s2 = 0; s2 < MAX_TOPK + 1; ++s2) {
-        const int row = prow[s2];
+        const int row = (s2 < kk) ? s_pos[wave][s2] : -1;  // read from LDS per store: no 17 live registers
         if (row >= 0) {
           const int t32 = row >> 5, r = row & 31;
           const size_t slab = (size_t)t32 * KS + j;

@@ -20,10 +20,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__
   const int t = (int)(i / d4);
   const int j = (int)(i - (long)t * d4);
   const float4* pr = partial + (size_t)t * kk * d4 + j;
+  // the partials are read once: non-temporal loads
+  typedef float f4n __attribute__((ext_vector_type(4)));
   float4 p[MAX_TOPK];
 #pragma unroll
   for (int s = 0; s < MAX_TOPK; ++s)
-    if (s < k) p[s] = pr[(size_t)s * d4];
+    if (s < k) {
+      const f4n v = __builtin_nontemporal_load(reinterpret_cast<const f4n*>(pr + (size_t)s * d4));
+      p[s] = make_float4(v.x, v.y, v.z, v.w);
+    }
   float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
   for (int s = 0; s < MAX_TOPK; ++s)
