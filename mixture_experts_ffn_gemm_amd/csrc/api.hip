@@ -243,10 +243,10 @@ int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, v
   if (dm.E <= 64) {
     // one workgroup holds all logits of its tokens: router and routing fused
     HIP_TRY(launch_router_route(x, n, dm.d, W->router_wt, rbias, dm.E, dm.k, dm.norm, ids, w, rank,
-                                hist, s));
+                                hist, W->n_cu, s));
     HIP_TRY(mark(1));
   } else {
-    HIP_TRY(launch_router(x, n, dm.d, W->router_wt, rbias, dm.E, dm.E64, logits, s));
+    HIP_TRY(launch_router(x, n, dm.d, W->router_wt, rbias, dm.E, dm.E64, logits, W->n_cu, s));
     HIP_TRY(mark(1));
     HIP_TRY(launch_route(logits, n, dm.E, dm.k, dm.norm, ids, w, rank, hist, s));
   }

@@ -156,13 +156,15 @@ hipError_t launch_scale_exponent(const uint8_t* src, int n_groups, size_t src_gr
                                  long n_blocks, int32_t* e, hipStream_t s);
 hipError_t launch_transpose_router(const float* w, int E, int d, int E64, float* wt, hipStream_t s);
 
+// n_cu: compute units of the device (the router's LDS ring is sized to how
+// many of its workgroups must share a CU).
 hipError_t launch_router(const float* x, int n, int d, const float* wt, const float* bias, int E,
-                         int E64, float* logits, hipStream_t s);
+                         int E64, float* logits, int n_cu, hipStream_t s);
 // Router and routing in one launch (E <= 64): ids, w, rank and the tile
 // histograms as launch_route writes them; no logits in global memory.
 hipError_t launch_router_route(const float* x, int n, int d, const float* wt, const float* bias,
                                int E, int k, int norm, int32_t* ids, float* w, int32_t* rank,
-                               int32_t* hist, hipStream_t s);
+                               int32_t* hist, int n_cu, hipStream_t s);
 hipError_t launch_route(const float* logits, int n, int E, int k, int norm, int32_t* ids, float* w,
                         int32_t* rank, int32_t* hist, hipStream_t s);
 hipError_t launch_quantize(const float* v, int64_t n_values, int8_t* q, uint16_t* scales,

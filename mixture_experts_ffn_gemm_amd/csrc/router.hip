@@ -19,8 +19,12 @@ typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int RJC = 64;          // router: j values per LDS chunk
 constexpr int RJQ = RJC / 4;     // 4-j quads per chunk
-constexpr int RNB = 6;           // chunk buffers in the LDS ring (108 KiB: one workgroup per CU)
-constexpr int RPF = RNB - 1;     // chunks copied ahead
+// chunk buffers in the LDS ring: 6 (108 KiB, one workgroup per CU) when every
+// workgroup of the launch fits on the chip at once, else 3 (54 KiB, two
+// workgroups per CU, so a second round of workgroups never waits for a whole
+// first round; the shallower ring costs the single-round case ~1.5 us)
+constexpr int RNB_DEEP = 6;
+constexpr int RNB_SHALLOW = 3;
 constexpr int RDMA = 3;          // copies per wavefront per chunk
 constexpr int RT = 1;            // tokens per wavefront
 constexpr int RW = 8;            // wavefronts per workgroup
@@ -269,12 +273,13 @@ __device__ __forceinline__ void route_tile(RouteLds& R, int tile, int t0, int nt
 // FUSE (E <= 64, so a workgroup holds every logit of its ROUTE_TILE tokens):
 // the logits stay in LDS and the workgroup routes its tile (route_tile), with
 // no logits in global memory and no separate routing launch.
-template <bool FUSE>
-__global__ __launch_bounds__(512, 1) void router_kernel(
+template <bool FUSE, int RNB>
+__global__ __launch_bounds__(512) void router_kernel(
     const float* __restrict__ x, int n, int d, const float* __restrict__ wt,
     const float* __restrict__ bias, int E, int E64, float* __restrict__ logits, int k, int norm,
     int32_t* __restrict__ ids, float* __restrict__ wout, int32_t* __restrict__ rank,
     int32_t* __restrict__ hist) {
+  constexpr int RPF = RNB - 1;  // chunks copied ahead
   __shared__ __attribute__((aligned(1024))) char ring[RNB * R_BUF];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -677,20 +682,28 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
 }  // namespace
 
 hipError_t launch_router(const float* x, int n, int d, const float* wt, const float* bias, int E,
-                         int E64, float* logits, hipStream_t s) {
+                         int E64, float* logits, int n_cu, hipStream_t s) {
   dim3 grid((unsigned)((n + RW * RT - 1) / (RW * RT)), (unsigned)(E64 / 64));
-  router_kernel<false><<<grid, 512, 0, s>>>(x, n, d, wt, bias, E, E64, logits, 0, 0, nullptr,
-                                            nullptr, nullptr, nullptr);
+  if ((long)grid.x * grid.y > n_cu)
+    router_kernel<false, RNB_SHALLOW><<<grid, 512, 0, s>>>(x, n, d, wt, bias, E, E64, logits, 0, 0, nullptr,
+                                                           nullptr, nullptr, nullptr);
+  else
+    router_kernel<false, RNB_DEEP><<<grid, 512, 0, s>>>(x, n, d, wt, bias, E, E64, logits, 0, 0, nullptr,
+                                                        nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_router_route(const float* x, int n, int d, const float* wt, const float* bias,
                                int E, int k, int norm, int32_t* ids, float* w, int32_t* rank,
-                               int32_t* hist, hipStream_t s) {
+                               int32_t* hist, int n_cu, hipStream_t s) {
   if (E > 64) return hipErrorInvalidValue;
   dim3 grid((unsigned)((n + ROUTE_TILE - 1) / ROUTE_TILE), 1);
-  router_kernel<true><<<grid, 512, 0, s>>>(x, n, d, wt, bias, E, 64, nullptr, k, norm, ids, w, rank,
-                                           hist);
+  if ((long)grid.x > n_cu)
+    router_kernel<true, RNB_SHALLOW><<<grid, 512, 0, s>>>(x, n, d, wt, bias, E, 64, nullptr, k, norm, ids, w,
+                                                          rank, hist);
+  else
+    router_kernel<true, RNB_DEEP><<<grid, 512, 0, s>>>(x, n, d, wt, bias, E, 64, nullptr, k, norm, ids, w,
+                                                       rank, hist);
   return hipGetLastError();
 }
 
