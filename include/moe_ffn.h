@@ -21,8 +21,10 @@
  *        N x embDim.
  *
  * Numerics (what every entry point computes):
- *   logit[t][e]  = fp32 fused multiply-add chain over ascending j of
- *                  x[t][j] * router_w[e][j], from +0, then + bias[e];
+ *   logit[t][e]  = fp32 sum of x[t][j] * router_w[e][j] in blocks of 64 j:
+ *                  per block a fused multiply-add chain over ascending j
+ *                  from +0, the block sums added in ascending block order
+ *                  to a total from +0, then + bias[e];
  *   top-k        = experts by (logit descending, id ascending); slot s = rank s;
  *   w[t][s]      = softmax over all E logits at ids[t][s]; divided by the sum
  *                  of the k picks when norm_topk_prob;

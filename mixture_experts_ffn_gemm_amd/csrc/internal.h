@@ -227,7 +227,7 @@ hipError_t launch_block_sums(const GemmArgs& a, bool gateup, int tile, int strip
                              int8_t* acodes, int32_t* info, hipStream_t s);
 
 // ---- decode (1 <= N <= DECODE_MAX_TOKENS) ----
-// Router logits [N][E] (fp32 FMA chains, as launch_router), plus the
+// Router logits [N][E] (the same fp32 block order as launch_router), plus the
 // token-major activation codes dxq/dxs (row strides d_pad and d_pad/32, zero
 // past d) and, with sh_gate_vec != NULL, gs[t] = sigmoid(x[t] . g).
 hipError_t launch_decode_router(const float* x, int n, int d, int d_pad, const float* wt,

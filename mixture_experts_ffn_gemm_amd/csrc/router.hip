@@ -250,10 +250,11 @@ __device__ __forceinline__ void route_tile(RouteLds& R, int tile, int t0, int nt
 }
 
 // Router logits for RW tokens x 64 experts per workgroup (lane = expert, one
-// token per wavefront, two wavefronts per SIMD).  Each logit is one fp32 fused
-// multiply-add chain over ascending j, from +0, then + bias (a separate fp32
-// add); the chain order is the contract that makes top-k ids reproducible bit
-// for bit.
+// token per wavefront, two wavefronts per SIMD).  Each logit is summed in
+// fp32 in blocks of 64 j: a fused multiply-add chain over ascending j from +0
+// per block, the block sums added in ascending order to a total from +0, then
+// + bias (a separate fp32 add); this order is the contract that makes top-k
+// ids reproducible bit for bit.
 //
 // The chains are latency- and operand-bound (one per lane across the whole
 // chip at OLMoE sizes), so every operand takes the cheapest path, and two
@@ -332,7 +333,9 @@ __global__ __launch_bounds__(512) void router_kernel(
     const float* xrow = reinterpret_cast<const float*>(buf + R_WB) + (RT * wave) * RJC + q0 * 4 + (lane & 15);
     xa[b] = xrow[0];
   };
-  float acc0 = 0.0f;
+  // The logit's blocks of 64 j are the chunks: acc0 chains one chunk from +0,
+  // total adds the finished chunks in order.
+  float acc0 = 0.0f, total = 0.0f;
   // One full chunk (4 sub-chunks of 16 j) per iteration, then the trailing
   // half chunk when d % 64 == 32.  The reads of sub-chunk s+3 are issued
   // before sub-chunk s is computed, unconditionally (past the last sub-chunk
@@ -363,10 +366,13 @@ __global__ __launch_bounds__(512) void router_kernel(
         router_fma16_1(acc0, xa[q], w[q][0], w[q][1], w[q][2], w[q][3]);
       }
     }
+    total += acc0;
+    acc0 = 0.0f;
   }
-  if (busy && CF < C) {  // 32 trailing j: sub-chunks 4 CF and 4 CF + 1 (already requested)
+  if (busy && CF < C) {  // 32 trailing j (the last block): sub-chunks 4 CF and 4 CF + 1 (already requested)
     router_fma16_1(acc0, xa[0], w[0][0], w[0][1], w[0][2], w[0][3]);
     router_fma16_1(acc0, xa[1], w[1][0], w[1][1], w[1][2], w[1][3]);
+    total += acc0;
   }
   const int e = eg * 64 + lane;
   if constexpr (FUSE) {
@@ -375,7 +381,7 @@ __global__ __launch_bounds__(512) void router_kernel(
     const int tl = wave * RT;
     if (e < E) {
       const float bb = bias ? bias[e] : 0.0f;
-      R.l[tl][e] = bias ? acc0 + bb : acc0;
+      R.l[tl][e] = bias ? total + bb : total;
     }
     const int t0 = blockIdx.x * ROUTE_TILE;
     route_tile<1, 64>(R, blockIdx.x, t0, min(ROUTE_TILE, n - t0), E, k, norm, threadIdx.x, 512, ids, wout,
@@ -383,7 +389,7 @@ __global__ __launch_bounds__(512) void router_kernel(
   } else {
     if (e < E) {
       const float bb = bias ? bias[e] : 0.0f;
-      if (tw < n) logits[(size_t)tw * E + e] = bias ? acc0 + bb : acc0;
+      if (tw < n) logits[(size_t)tw * E + e] = bias ? total + bb : total;
     }
   }
 }
@@ -430,78 +436,28 @@ __global__ __launch_bounds__(ROUTE_WIDE_THREADS) void route_kernel(
 }
 
 // ---------------------------------------------------------------- decode
-// Decode router (1 <= N <= 8).  The logits are the same fp32 chains as
-// router_kernel's, but the batch is too small to share the router matrix
-// among many tokens, so the chains are spread over the chip instead: one
-// workgroup per 16 experts.  Wavefront w < 2 runs tokens 4w .. 4w+3, one per
-// 16-lane row, lane i of a row running the chain of expert 16 * blockIdx.x + i
-// (one chain per lane: a wavefront issues one instruction at a time, so
-// what bounds a chain is the number of instructions per step).  Per 64 j a
-// lane reads 4 values of its row's token (row lane q holds j0 + 4q .. +3) and
-// 16 quads of its expert's weights from LDS; the token value of each step
-// reaches the row through a DPP row broadcast inside the FMA.  Per 256 j, the
-// 16 experts' slab (16 KiB) and the N token rows (1 KiB each) are copied into
-// a ring of LDS buffers by all four wavefronts, 5 chunks ahead.  The
+// Decode router (1 <= N <= 8).  The same logits as router_kernel (fp32;
+// blocks of 64 j, each chained by fused multiply-adds over ascending j from
+// +0; block sums added in ascending order, then the bias), but with too few
+// tokens to share the router matrix among many of them, so the blocks of a
+// logit run in parallel: one lane per (expert, block), and the block sums
+// are added in order afterwards.  A workgroup covers DR_E experts and, per
+// pass, DR_NBP blocks (2048 j): lane (e, b) reads its block's 16 weight quads
+// straight from the transposed matrix [d/4][E64][4] into registers (8
+// experts' quads of one j are 128 contiguous bytes) and its tokens' values
+// from LDS, where the workgroup stages the pass's N x 2048 slice of x.  The
+// block sums meet in LDS and lane (e, t) adds them in block order.  The
 // workgroups past the router ones quantise one token row each (the same
 // pieces, decisions and shared-gate order as the prefill quantiser in the
-// bucketing launch),
-// writing the token-major codes the decode matvecs read.
-constexpr int DR_E = 16;                              // experts per router workgroup
-constexpr int DR_J = 256;                             // j per chunk
-constexpr int DR_NB = 6;                              // chunk buffers in the ring
-constexpr int DR_PF = DR_NB - 1;                      // chunks copied ahead
-constexpr int DR_WB = (DR_J / 4) * DR_E * 16;         // slab [quad][expert][4 j] (16 KiB)
-constexpr int DR_XROW = DR_J * 4 + 16;                // one token row, padded (bank offset)
-constexpr int DR_BUF = DR_WB + DECODE_MAX_TOKENS * DR_XROW;
-constexpr int DR_DMA = 6;                             // copies per wavefront per chunk
-static_assert(DR_NB * DR_BUF <= 160 * 1024, "decode router ring must fit in the LDS");
-static_assert(4 * DR_DMA == DR_WB / 1024 + DECODE_MAX_TOKENS, "24 copies per chunk: 16 slab + 8 rows");
-
-// 16 steps of one fp32 fused multiply-add chain over the 16 quads' weights
-// w0..w15 (component c of quad q: j = j0 + 4q + c) for quads q0 .. q0+3:
-// acc = fma(x, w, acc) where x is component c of lane q of this lane's
-// 16-lane row (DPP row_newbcast); the leading s_nop covers the wait states a
-// DPP read needs after a VALU write of its source.
-#define DFMA(Q, C, W) "v_fmac_f32_dpp %0, %" #C ", " W " row_newbcast:" #Q " row_mask:0xf bank_mask:0xf\n\t"
-#define DFMA4(Q, W0, W1, W2, W3) DFMA(Q, 1, W0) DFMA(Q, 2, W1) DFMA(Q, 3, W2) DFMA(Q, 4, W3)
-template <int Q0>
-__device__ __forceinline__ void decode_fma16(float& acc, const f4v& x, const f4v& w0, const f4v& w1, const f4v& w2,
-                                             const f4v& w3) {
-  if constexpr (Q0 == 0)
-    asm volatile("s_nop 1\n\t"
-                 DFMA4(0, "%5", "%6", "%7", "%8") DFMA4(1, "%9", "%10", "%11", "%12")
-                 DFMA4(2, "%13", "%14", "%15", "%16") DFMA4(3, "%17", "%18", "%19", "%20")
-                 : "+v"(acc)
-                 : "v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w), "v"(w0.x), "v"(w0.y), "v"(w0.z), "v"(w0.w),
-                   "v"(w1.x), "v"(w1.y), "v"(w1.z), "v"(w1.w), "v"(w2.x), "v"(w2.y), "v"(w2.z), "v"(w2.w),
-                   "v"(w3.x), "v"(w3.y), "v"(w3.z), "v"(w3.w));
-  else if constexpr (Q0 == 4)
-    asm volatile("s_nop 1\n\t"
-                 DFMA4(4, "%5", "%6", "%7", "%8") DFMA4(5, "%9", "%10", "%11", "%12")
-                 DFMA4(6, "%13", "%14", "%15", "%16") DFMA4(7, "%17", "%18", "%19", "%20")
-                 : "+v"(acc)
-                 : "v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w), "v"(w0.x), "v"(w0.y), "v"(w0.z), "v"(w0.w),
-                   "v"(w1.x), "v"(w1.y), "v"(w1.z), "v"(w1.w), "v"(w2.x), "v"(w2.y), "v"(w2.z), "v"(w2.w),
-                   "v"(w3.x), "v"(w3.y), "v"(w3.z), "v"(w3.w));
-  else if constexpr (Q0 == 8)
-    asm volatile("s_nop 1\n\t"
-                 DFMA4(8, "%5", "%6", "%7", "%8") DFMA4(9, "%9", "%10", "%11", "%12")
-                 DFMA4(10, "%13", "%14", "%15", "%16") DFMA4(11, "%17", "%18", "%19", "%20")
-                 : "+v"(acc)
-                 : "v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w), "v"(w0.x), "v"(w0.y), "v"(w0.z), "v"(w0.w),
-                   "v"(w1.x), "v"(w1.y), "v"(w1.z), "v"(w1.w), "v"(w2.x), "v"(w2.y), "v"(w2.z), "v"(w2.w),
-                   "v"(w3.x), "v"(w3.y), "v"(w3.z), "v"(w3.w));
-  else
-    asm volatile("s_nop 1\n\t"
-                 DFMA4(12, "%5", "%6", "%7", "%8") DFMA4(13, "%9", "%10", "%11", "%12")
-                 DFMA4(14, "%13", "%14", "%15", "%16") DFMA4(15, "%17", "%18", "%19", "%20")
-                 : "+v"(acc)
-                 : "v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w), "v"(w0.x), "v"(w0.y), "v"(w0.z), "v"(w0.w),
-                   "v"(w1.x), "v"(w1.y), "v"(w1.z), "v"(w1.w), "v"(w2.x), "v"(w2.y), "v"(w2.z), "v"(w2.w),
-                   "v"(w3.x), "v"(w3.y), "v"(w3.z), "v"(w3.w));
-}
-#undef DFMA4
-#undef DFMA
+// bucketing launch), writing the token-major codes the decode matvecs read.
+constexpr int DR_E = 8;                       // experts per router workgroup
+constexpr int DR_RB = 64;                     // j per block of the logit's sum
+constexpr int DR_NBP = 32;                    // blocks per pass: DR_E x DR_NBP = 256 lanes
+constexpr int DR_JP = DR_RB * DR_NBP;         // j per pass
+constexpr int DR_XBLK = DR_RB + 4;            // staged floats per block (+4: the 8 blocks a
+                                              // wavefront reads at once start in different banks)
+constexpr int DR_XTOK = DR_NBP * DR_XBLK;     // staged floats per token and pass
+static_assert(DR_E * DR_NBP == 256, "one (expert, block) per lane");
 
 // Quantise token row xr (one wavefront): pass j0 covers values [1024 j0', +1024),
 // lane l the 16 values from 16 l; codes/scales to xq_row/xs_row up to d_pad
@@ -545,124 +501,91 @@ __device__ __forceinline__ void decode_quantize_row(const float* __restrict__ xr
   }
 }
 
+template <int NT>
 __global__ __launch_bounds__(256, 1) void decode_router_kernel(
     const float* __restrict__ x, int n, int d, int d_pad, const float* __restrict__ wt,
     const float* __restrict__ bias, int E, int E64, int n_rwg, float* __restrict__ logits,
     const float* __restrict__ shg, float* __restrict__ gs, int8_t* __restrict__ xq,
     uint16_t* __restrict__ xs) {
-  __shared__ __attribute__((aligned(1024))) char ring[DR_NB * DR_BUF];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __shared__ __attribute__((aligned(16))) float xl[NT * DR_XTOK];
+  __shared__ __attribute__((aligned(16))) float part[NT][DR_E][DR_NBP + 4];  // +4: bank offset per expert
+  const int tid = threadIdx.x, lane = tid & 63;
   if ((int)blockIdx.x >= n_rwg) {
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int t = (int)blockIdx.x - n_rwg;
     if (wave == 0 && t < n)
       decode_quantize_row(x + (size_t)t * d, d, d_pad, shg, gs + t, xq + (size_t)t * d_pad,
                           xs + (size_t)t * (d_pad / QB), lane);
     return;
   }
-  const int C = (d + DR_J - 1) / DR_J, NQ = d / 4;
-  const uint32_t lbase = (uint32_t)(uintptr_t)(lds_char*)ring;
-  // Copy i of a chunk (wavefront w issues 6w .. 6w+5): i < 16 moves slab
-  // quads 4i .. 4i+3 (lane l: quad 4i + l/16, expert l%16; quads past d
-  // re-read the last one), i >= 16 token row i-16 (rows past n re-read row
-  // n-1; columns past d re-read the last 4).
-  auto issue = [&](int c) {
-    const uint32_t buf = lbase + (uint32_t)((c % DR_NB) * DR_BUF);
+  const int el = tid % DR_E, bl = tid / DR_E;
+  const int e = DR_E * (int)blockIdx.x + el;  // < E64: the matrix holds zero rows past E
+  // lane (el, t) of the first DR_E * NT lanes adds the block sums of (e, t)
+  const int se = tid % DR_E, st = tid / DR_E;
+  float total = 0.0f;
+  for (int j0 = 0; j0 < d; j0 += DR_JP) {
+    // this pass's token values: [t][block][DR_XBLK], quads past d skipped
+    constexpr int XQ = NT * DR_JP / 4;  // quads to stage
+    f4v xv[(XQ + 255) / 256];
 #pragma unroll
-    for (int ii = 0; ii < DR_DMA; ++ii) {
-      const int i = wave * DR_DMA + ii;
-      if (i < DR_WB / 1024) {
-        const int jq = min(c * (DR_J / 4) + 4 * i + (lane >> 4), NQ - 1);
-        rdma16(wt, (uint32_t)(((size_t)jq * E64 + DR_E * blockIdx.x + (lane & 15)) * 16), buf + i * 1024);
-      } else {
-        const int tr = i - DR_WB / 1024;
-        const int t = min(tr, n - 1);
-        const int j = min(c * DR_J + 4 * lane, d - 4);
-        rdma16(x + (size_t)t * d, (uint32_t)j * 4, buf + DR_WB + tr * DR_XROW);
-      }
+    for (int u = 0; u < (XQ + 255) / 256; ++u) {
+      const int i = tid + 256 * u, t = i / (DR_JP / 4), jq = i % (DR_JP / 4);
+      if (i < XQ && j0 + 4 * jq < d)
+        xv[u] = *reinterpret_cast<const f4v*>(x + (size_t)t * d + j0 + 4 * jq);
     }
-  };
-  const int np = min(DR_PF, C);
-  for (int c = 0; c < np; ++c) issue(c);
-  static_assert(DR_PF * DR_DMA <= 63, "vmcnt counts at most 63 copies");
-  const int row = lane >> 4, i = lane & 15;
-  const int t = 4 * wave + row;  // this lane's token (wavefronts 0 and 1)
-  const bool busy = wave < 2 && 4 * wave < n;  // wavefront-uniform
-  float acc = 0.0f;
-  for (int c = 0; c < C; ++c) {
-    // issued so far: chunks 0 .. min(c + DR_PF - 1, C - 1); wait for chunk c
-    switch (min(DR_PF - 1, C - 1 - c)) {
-      case 0: rwait_vm<0>(); break;
-      case 1: rwait_vm<DR_DMA>(); break;
-      case 2: rwait_vm<2 * DR_DMA>(); break;
-      case 3: rwait_vm<3 * DR_DMA>(); break;
-      default: rwait_vm<4 * DR_DMA>(); break;
+    // this lane's weights: quads q of block bl (16 per full block; d % 32 == 0,
+    // so a block past d's last full one has 8 or none)
+    const int jb = j0 + DR_RB * bl;
+    const int nq = max(0, min(DR_RB, d - jb)) / 4;
+    f4v w[DR_RB / 4];
+#pragma unroll
+    for (int q = 0; q < DR_RB / 4; ++q)
+      if (q < nq) w[q] = *reinterpret_cast<const f4v*>(wt + ((size_t)(jb / 4 + q) * E64 + e) * 4);
+    if (j0 > 0) __syncthreads();  // every lane is done with the previous pass's values
+#pragma unroll
+    for (int u = 0; u < (XQ + 255) / 256; ++u) {
+      const int i = tid + 256 * u, t = i / (DR_JP / 4), jq = i % (DR_JP / 4);
+      if (i < XQ && j0 + 4 * jq < d)
+        *reinterpret_cast<f4v*>(xl + t * DR_XTOK + (jq / 16) * DR_XBLK + 4 * (jq % 16)) = xv[u];
     }
-    // every wavefront's copies of chunk c have landed, and the computing
-    // wavefronts have finished chunk c-1, whose buffer now takes chunk
-    // c + DR_PF
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (c + DR_PF < C) issue(c + DR_PF);
-    if (busy) {
-      const char* buf = ring + (c % DR_NB) * DR_BUF;
-      const f4v* xr = reinterpret_cast<const f4v*>(buf + DR_WB + t * DR_XROW) + i;  // + 16 per 64 j
-      const f4v* wr = reinterpret_cast<const f4v*>(buf) + i;                         // + 16 per quad
-      const int n64 = min(DR_J, d - c * DR_J) / 64;  // d % 32 == 0: a trailing 32 j are handled below
-      auto fma_group = [&](int gq, const f4v& xv, const f4v (&w)[4]) {  // quads 4 gq .. 4 gq + 3
-        switch (gq & 3) {
-          case 0: decode_fma16<0>(acc, xv, w[0], w[1], w[2], w[3]); break;
-          case 1: decode_fma16<4>(acc, xv, w[0], w[1], w[2], w[3]); break;
-          case 2: decode_fma16<8>(acc, xv, w[0], w[1], w[2], w[3]); break;
-          default: decode_fma16<12>(acc, xv, w[0], w[1], w[2], w[3]); break;
-        }
-      };
-      if (n64 == 4) {
-        // a whole chunk as 16 groups of 4 quads; the reads of group g + 2
-        // are issued before group g's 16 steps (at most 9 reads in flight:
-        // every wait is expressible in the 4-bit LDS counter), order pinned
-        f4v xs[4], wg[3][4];
-        auto load_group = [&](int gq, f4v (&w)[4]) {
+    __syncthreads();
+    float acc[NT];
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq) w[qq] = wr[16 * (4 * gq + qq)];
-        };
-        xs[0] = xr[0];
-        load_group(0, wg[0]);
-        load_group(1, wg[1]);
+    for (int t = 0; t < NT; ++t) acc[t] = 0.0f;
+    const float* xb = xl + bl * DR_XBLK;
+    auto quads = [&](int q0, int q1) {
 #pragma unroll
-        for (int gq = 0; gq < 16; ++gq) {
-          if (gq + 2 < 16) {
-            if ((gq + 2) % 4 == 0) xs[(gq + 2) / 4] = xr[16 * ((gq + 2) / 4)];
-            load_group(gq + 2, wg[(gq + 2) % 3]);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          fma_group(gq, xs[gq / 4], wg[gq % 3]);
-        }
-      } else {
-        for (int sc = 0; sc < n64; ++sc) {
-          const f4v xv = xr[16 * sc];
+      for (int q = q0; q < q1; ++q) {
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            f4v w[4];
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) w[qq] = wr[16 * (16 * sc + 4 * g4 + qq)];
-            fma_group(g4, xv, w);
-          }
+        for (int t = 0; t < NT; ++t) {
+          const f4v v = *reinterpret_cast<const f4v*>(xb + t * DR_XTOK + 4 * q);
+          acc[t] = __builtin_fmaf(v.x, w[q].x, acc[t]);
+          acc[t] = __builtin_fmaf(v.y, w[q].y, acc[t]);
+          acc[t] = __builtin_fmaf(v.z, w[q].z, acc[t]);
+          acc[t] = __builtin_fmaf(v.w, w[q].w, acc[t]);
         }
       }
-      if (n64 * 64 < min(DR_J, d - c * DR_J)) {  // 32 trailing j: quads 0..7 of the last 64
-        const f4v xv = xr[16 * n64];
-        f4v w[8];
+    };
+    if (nq > 0) quads(0, DR_RB / 8);
+    if (nq == DR_RB / 4) quads(DR_RB / 8, DR_RB / 4);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) w[q] = wr[16 * (16 * n64 + q)];
-        decode_fma16<0>(acc, xv, w[0], w[1], w[2], w[3]);
-        decode_fma16<4>(acc, xv, w[4], w[5], w[6], w[7]);
-      }
+    for (int t = 0; t < NT; ++t) part[t][el][bl] = acc[t];
+    __syncthreads();
+    if (st < NT) {
+      // all of the pass's block sums read at once (past nb: stale, unused)
+      const int nb = min(DR_NBP, (d - j0 + DR_RB - 1) / DR_RB);
+      f4v pv[DR_NBP / 4];
+#pragma unroll
+      for (int b4 = 0; b4 < DR_NBP / 4; ++b4) pv[b4] = *reinterpret_cast<const f4v*>(&part[st][se][4 * b4]);
+#pragma unroll
+      for (int b = 0; b < DR_NBP; ++b)
+        if (b < nb) total += pv[b / 4][b % 4];
     }
   }
-  const int e = DR_E * (int)blockIdx.x + i;
-  if (busy && t < n && e < E) logits[(size_t)t * E + e] = bias ? acc + bias[e] : acc;
+  const int eo = DR_E * (int)blockIdx.x + se;
+  if (st < NT && st < n && eo < E) logits[(size_t)st * E + eo] = bias ? total + bias[eo] : total;
 }
+
 
 __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ v, int64_t n_values,
                                                        int8_t* __restrict__ q,
@@ -720,8 +643,16 @@ hipError_t launch_decode_router(const float* x, int n, int d, int d_pad, const f
                                 hipStream_t s) {
   if (n < 1 || n > DECODE_MAX_TOKENS) return hipErrorInvalidValue;
   const int n_rwg = (E + DR_E - 1) / DR_E;
-  decode_router_kernel<<<n_rwg + n, 256, 0, s>>>(x, n, d, d_pad, wt, bias, E, E64, n_rwg, logits,
-                                                 sh_gate_vec, gs, dxq, dxs);
+#define DR_LAUNCH(NT)                                                                             \
+  case NT:                                                                                         \
+    decode_router_kernel<NT><<<n_rwg + n, 256, 0, s>>>(x, n, d, d_pad, wt, bias, E, E64, n_rwg, logits, \
+                                                       sh_gate_vec, gs, dxq, dxs);                 \
+    break;
+  static_assert(DECODE_MAX_TOKENS == 8, "one instantiation per batch size");
+  switch (n) {
+    DR_LAUNCH(1) DR_LAUNCH(2) DR_LAUNCH(3) DR_LAUNCH(4) DR_LAUNCH(5) DR_LAUNCH(6) DR_LAUNCH(7) DR_LAUNCH(8)
+  }
+#undef DR_LAUNCH
   return hipGetLastError();
 }
 

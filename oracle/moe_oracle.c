@@ -88,18 +88,25 @@ void ora_float_to_half(const float* f, uint16_t* h, int64_t n) {
 
 /* -------------------------------------------------------------- router */
 /* #388, "Remaining levers" 1: the logits of every token against every
- * expert's router row.  Each logit is one fp32 chain of fused multiply-adds
- * over ascending j. */
+ * expert's router row, in fp32 and in one fixed order (the pages fix none):
+ * j is cut into blocks of ORA_ROUTER_BLOCK; each block's products are
+ * summed by a chain of fused multiply-adds over ascending j from +0, and the
+ * block sums are added one by one in ascending block order. */
 void ora_router_logits(const float* x, int32_t n, int32_t d, const float* w,
                        const float* bias, int32_t n_experts, float* logits) {
   for (int32_t t = 0; t < n; ++t) {
     const float* xr = x + (int64_t)t * d;
     for (int32_t e = 0; e < n_experts; ++e) {
       const float* wr = w + (int64_t)e * d;
-      float acc = 0.0f;
-      for (int32_t j = 0; j < d; ++j) acc = fmaf(xr[j], wr[j], acc);
-      if (bias) acc = acc + bias[e];
-      logits[(int64_t)t * n_experts + e] = acc;
+      float total = 0.0f;
+      for (int32_t j0 = 0; j0 < d; j0 += ORA_ROUTER_BLOCK) {
+        const int32_t j1 = j0 + ORA_ROUTER_BLOCK < d ? j0 + ORA_ROUTER_BLOCK : d;
+        float block = 0.0f;
+        for (int32_t j = j0; j < j1; ++j) block = fmaf(xr[j], wr[j], block);
+        total = total + block;
+      }
+      if (bias) total = total + bias[e];
+      logits[(int64_t)t * n_experts + e] = total;
     }
   }
 }

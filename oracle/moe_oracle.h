@@ -81,8 +81,11 @@ typedef struct ora_dims {
 void ora_half_to_float(const uint16_t* h, float* f, int64_t n);
 void ora_float_to_half(const float* f, uint16_t* h, int64_t n);
 
-/* Router logits l[t][e] = fp32 fmaf chain over ascending j of x[t][j]*W[e][j],
- * starting from +0, then + bias[e] (fp32 add) when bias != NULL. */
+/* Router logits l[t][e] = sum over j of x[t][j]*W[e][j] in fp32: per block of
+ * ORA_ROUTER_BLOCK consecutive j an fmaf chain over ascending j from +0, the
+ * block sums added in ascending block order to a total that starts at +0,
+ * then + bias[e] (fp32 add) when bias != NULL. */
+#define ORA_ROUTER_BLOCK 64
 void ora_router_logits(const float* x, int32_t n, int32_t d, const float* w,
                        const float* bias, int32_t n_experts, float* logits);
 

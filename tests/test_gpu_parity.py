@@ -788,8 +788,8 @@ def test_decode_graph_replays_match_eager():
 
 # Decode: the same shapes through moe_ffn_decode, plus one whose K spans
 # several staged activation passes of the decode matvecs (d and F above 2048,
-# both ragged against the 128-value k-step) and whose router chain runs past
-# the LDS ring.
+# both ragged against the 128-value k-step) and whose router runs three
+# passes of 2048 j (the last one a single block).
 DECODE_SHAPES = SHAPES + [dict(d=4160, E=8, k=2, F=2080, Fs=96)]
 
 
