@@ -156,8 +156,8 @@ hipError_t launch_scale_exponent(const uint8_t* src, int n_groups, size_t src_gr
                                  long n_blocks, int32_t* e, hipStream_t s);
 hipError_t launch_transpose_router(const float* w, int E, int d, int E64, float* wt, hipStream_t s);
 
-// n_cu: compute units of the device (the router's LDS ring is sized to how
-// many of its workgroups must share a CU).
+// n_cu: compute units of the device (a grid larger than one workgroup per CU
+// takes the router form that fits two per CU).
 hipError_t launch_router(const float* x, int n, int d, const float* wt, const float* bias, int E,
                          int E64, float* logits, int n_cu, hipStream_t s);
 // Router and routing in one launch (E <= 64): ids, w, rank and the tile

@@ -15,63 +15,36 @@ namespace moe {
 namespace {
 
 typedef float f4v __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr int RJC = 64;          // router: j values per LDS chunk
-constexpr int RJQ = RJC / 4;     // 4-j quads per chunk
-// chunk buffers in the LDS ring: 6 (108 KiB, one workgroup per CU) when every
-// workgroup of the launch fits on the chip at once, else 3 (54 KiB, two
-// workgroups per CU, so a second round of workgroups never waits for a whole
-// first round; the shallower ring costs the single-round case ~1.5 us)
-constexpr int RNB_DEEP = 6;
-constexpr int RNB_SHALLOW = 3;
-constexpr int RDMA = 3;          // copies per wavefront per chunk
-constexpr int RT = 1;            // tokens per wavefront
-constexpr int RW = 8;            // wavefronts per workgroup
-constexpr int R_WB = RJQ * 64 * 16;       // transposed router slab per chunk (16 KiB)
-constexpr int R_XB = RW * RT * RJC * 4;   // the workgroup's token rows per chunk (2 KiB)
-constexpr int R_BUF = R_WB + R_XB;
-static_assert(RJQ == 2 * RW && RDMA == 3, "each wavefront copies two slab quads and its token row per chunk");
+constexpr int RB = 64;            // j per block of a logit's sum
+constexpr int RWV = 8;            // prefill router: wavefronts per workgroup
+constexpr int RJR = RB * RWV;     // j per round (one block per wavefront)
+static_assert(RWV == ROUTE_TILE, "thread (token, expert) of the block sums is (wavefront, lane)");
 
-// global -> LDS copies: lane l writes LDS address m0 + size * l
-__device__ __forceinline__ void rdma16(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(base), "s"(lds)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void rdma4(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
-               :
-               : "v"(voff), "s"(base), "s"(lds)
-               : "memory", "m0");
-}
-template <int N>
-__device__ __forceinline__ void rwait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// 16 steps of one fp32 fused multiply-add chain: for i = 0..15,
-//   acc0 = fma(xa[i], w[i], acc0),
-// where xa[i] is lane i of this lane's 16-lane row of xa, broadcast to the row
+// 16 steps of two fp32 fused multiply-add chains: for i = 0..15,
+//   acc0 = fma(x0[i], w[i], acc0),  acc1 = fma(x1[i], w[i], acc1),
+// where xN[i] is lane i of this lane's 16-lane row of xN, broadcast to the row
 // by DPP row_newbcast (every row holds the same 16 values), and w[i] is this
 // lane's weight (quads w0..w3).  v_fmac_f32 is fused (one rounding), as the
-// chain's definition requires; the leading s_nop covers the wait states a DPP
-// read needs after a VALU write of its source.
-#define RFMA1(I, W) "v_fmac_f32_dpp %0, %1, " W " row_newbcast:" #I " row_mask:0xf bank_mask:0xf\n\t"
-__device__ __forceinline__ void router_fma16_1(float& acc0, float xa, const f4v& w0, const f4v& w1,
-                                               const f4v& w2, const f4v& w3) {
+// block chain's definition requires; the two chains alternate so that each
+// step's dependency is two instructions old, and the leading s_nop covers the
+// wait states a DPP read needs after a VALU write of its source.
+#define RFMA2(I, W)                                                                  \
+  "v_fmac_f32_dpp %0, %2, " W " row_newbcast:" #I " row_mask:0xf bank_mask:0xf\n\t" \
+  "v_fmac_f32_dpp %1, %3, " W " row_newbcast:" #I " row_mask:0xf bank_mask:0xf\n\t"
+__device__ __forceinline__ void router_fma16_2(float& acc0, float& acc1, float x0, float x1, const f4v& w0,
+                                               const f4v& w1, const f4v& w2, const f4v& w3) {
   asm volatile("s_nop 1\n\t"
-      RFMA1(0, "%2") RFMA1(1, "%3") RFMA1(2, "%4") RFMA1(3, "%5")
-      RFMA1(4, "%6") RFMA1(5, "%7") RFMA1(6, "%8") RFMA1(7, "%9")
-      RFMA1(8, "%10") RFMA1(9, "%11") RFMA1(10, "%12") RFMA1(11, "%13")
-      RFMA1(12, "%14") RFMA1(13, "%15") RFMA1(14, "%16") RFMA1(15, "%17")
-      : "+v"(acc0)
-      : "v"(xa), "v"(w0.x), "v"(w0.y), "v"(w0.z), "v"(w0.w), "v"(w1.x), "v"(w1.y),
+      RFMA2(0, "%4") RFMA2(1, "%5") RFMA2(2, "%6") RFMA2(3, "%7")
+      RFMA2(4, "%8") RFMA2(5, "%9") RFMA2(6, "%10") RFMA2(7, "%11")
+      RFMA2(8, "%12") RFMA2(9, "%13") RFMA2(10, "%14") RFMA2(11, "%15")
+      RFMA2(12, "%16") RFMA2(13, "%17") RFMA2(14, "%18") RFMA2(15, "%19")
+      : "+v"(acc0), "+v"(acc1)
+      : "v"(x0), "v"(x1), "v"(w0.x), "v"(w0.y), "v"(w0.z), "v"(w0.w), "v"(w1.x), "v"(w1.y),
         "v"(w1.z), "v"(w1.w), "v"(w2.x), "v"(w2.y), "v"(w2.z), "v"(w2.w), "v"(w3.x), "v"(w3.y),
         "v"(w3.z), "v"(w3.w));
 }
-#undef RFMA1
+#undef RFMA2
 
 // Reductions over all 64 lanes of a wavefront (every lane active), without
 // the LDS crossbar: four DPP steps inside each 16-lane row (swap neighbours,
@@ -249,141 +222,150 @@ __device__ __forceinline__ void route_tile(RouteLds& R, int tile, int t0, int nt
   for (int e = tid; e < E; e += nthreads) hist[(size_t)tile * E + e] = R.cnt[e];
 }
 
-// Router logits for RW tokens x 64 experts per workgroup (lane = expert, one
-// token per wavefront, two wavefronts per SIMD).  Each logit is summed in
-// fp32 in blocks of 64 j: a fused multiply-add chain over ascending j from +0
-// per block, the block sums added in ascending order to a total from +0, then
-// + bias (a separate fp32 add); this order is the contract that makes top-k
-// ids reproducible bit for bit.
+// Router logits for ROUTE_TILE (8) tokens x 64 experts per workgroup (lane =
+// expert).  Each logit is summed in fp32 in blocks of 64 j: a fused
+// multiply-add chain over ascending j from +0 per block, the block sums added
+// in ascending order to a total from +0, then + bias (a separate fp32 add);
+// this order is the contract that makes top-k ids reproducible bit for bit.
 //
-// The chains are latency- and operand-bound (one per lane across the whole
-// chip at OLMoE sizes), so every operand takes the cheapest path, and two
-// wavefronts share each SIMD so that one's LDS reads overlap the other's
-// chain.  Per chunk of 64 j the transposed router slab (64 experts x 64 j,
-// 16 KiB) and the workgroup's 8 token rows (2 KiB) are copied into a ring of
-// LDS buffers RPF chunks ahead.  Per 16 j a lane reads its expert's 16
-// weights (4 x 16 B) and one value of its wavefront's token row (lane i of
-// every 16-lane row reads column i), and the token value of each step
-// reaches all lanes through a DPP row broadcast inside the FMA.  The reads of
-// each 16 j are issued three 16-j steps before they are used.  Only the d/16
-// sub-chunks inside d are visited (d % 32 == 0), so no padding term enters a
-// chain.  (Measured: two wavefronts of one token each run the launch 14 %
-// faster than one wavefront per SIMD holding two tokens' chains, although
-// they read the slab from LDS twice as often.)
+// The blocks of a logit are independent until they are added, so the work is
+// split by block: in round r wavefront w chains block 8r + w for all 8 tokens.
+// A lane holds its expert's 64 weights of the block in registers (16 quads
+// read straight from the transposed matrix [d/4][E64][4], where the 64
+// experts' quads of one j are 1 KiB), so each weight is read once per
+// workgroup and used for 8 tokens, and the only LDS traffic is the token
+// values: lane i of each 16-lane row reads value i of a 16-j piece, and a DPP
+// row broadcast inside the FMA hands each step's value to the row.  The
+// round's 8 block sums per (token, expert) meet in LDS, and thread (token w,
+// expert lane) adds them to its total in block order.  The token values of
+// round r+1 are staged through registers into LDS during round r, and each
+// wavefront's weights are requested two rounds ahead.
 //
 // FUSE (E <= 64, so a workgroup holds every logit of its ROUTE_TILE tokens):
 // the logits stay in LDS and the workgroup routes its tile (route_tile), with
 // no logits in global memory and no separate routing launch.
-template <bool FUSE, int RNB>
-__global__ __launch_bounds__(512) void router_kernel(
+// WB: weight buffers per wavefront.  2: round r+2's weights are requested
+// during round r (one workgroup per CU); 1: round r+1's after round r is
+// computed, at most 128 VGPRs, so that two workgroups share a CU and each
+// hides the other's waits (grids with more workgroups than CUs).
+template <bool FUSE, int WB>
+__global__ __launch_bounds__(512, 3 - WB) void router_kernel(
     const float* __restrict__ x, int n, int d, const float* __restrict__ wt,
     const float* __restrict__ bias, int E, int E64, float* __restrict__ logits, int k, int norm,
     int32_t* __restrict__ ids, float* __restrict__ wout, int32_t* __restrict__ rank,
     int32_t* __restrict__ hist) {
-  constexpr int RPF = RNB - 1;  // chunks copied ahead
-  __shared__ __attribute__((aligned(1024))) char ring[RNB * R_BUF];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __shared__ __attribute__((aligned(16))) float xs[2][ROUTE_TILE][RJR];   // token values per round
+  __shared__ __attribute__((aligned(16))) float ps[2][ROUTE_TILE][RWV][64];  // block sums per round
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int eg = blockIdx.y;
-  const int tw = blockIdx.x * RW * RT + wave * RT;  // this wavefront's token
-  const int C = (d + RJC - 1) / RJC, NQ = d / 4;
-  const uint32_t lbase = (uint32_t)(uintptr_t)(lds_char*)ring;
-  const float* xr0 = x + (size_t)min(tw, n - 1) * d;
+  const int t0 = blockIdx.x * ROUTE_TILE;
+  const int NB = (d + RB - 1) / RB, NR = (NB + RWV - 1) / RWV, NQ = d / 4;
+  const float* wcol = wt + (size_t)(eg * 64 + lane) * 4;
 
-  // Wavefront w copies quads 2w, 2w+1 of the slab (1 KiB each: the 64
-  // experts' 4 j; quads past d re-read the last one) and its own token row
-  // (columns past d re-read column d-1).
-  auto issue = [&](int c) {
-    const uint32_t buf = lbase + (uint32_t)((c % RNB) * R_BUF);
+  // Round r's token values: thread tid moves quads tid and tid + 512 of the
+  // 8 x 128 (tokens past n re-read token n-1, columns past d the last quad).
+  auto load_x = [&](int r, f4v (&v)[2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int jq = min(c * RJQ + 2 * wave + i, NQ - 1);
-      rdma16(wt + ((size_t)jq * E64 + eg * 64) * 4, lane * 16, buf + (2 * wave + i) * 1024);
+      const int q = tid + 512 * i, t = q >> 7, jq = q & 127;
+      const int tc = min(t0 + t, n - 1), j = min(r * RJR + 4 * jq, d - 4);
+      v[i] = *reinterpret_cast<const f4v*>(x + (size_t)tc * d + j);
     }
-    const uint32_t xo = (uint32_t)min(c * RJC + lane, d - 1) * 4;
-    rdma4(xr0, xo, buf + R_WB + (RT * wave) * (RJC * 4));
   };
-  const int np = min(RPF, C);
-  for (int c = 0; c < np; ++c) issue(c);
+  auto store_x = [&](int bi, const f4v (&v)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = tid + 512 * i, t = q >> 7, jq = q & 127;
+      *reinterpret_cast<f4v*>(&xs[bi][t][4 * jq]) = v[i];
+    }
+  };
+  // This wavefront's block of round r: the lane's 16 weight quads (a block
+  // past d re-reads the last one, quads past d the last quad; neither is used).
+  auto load_w = [&](int r, f4v (&w)[16]) {
+    const int b = min(r * RWV + wave, NB - 1);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int jq = min(16 * b + q, NQ - 1);
+      w[q] = *reinterpret_cast<const f4v*>(wcol + (size_t)jq * E64 * 4);
+    }
+  };
+  // Round r from buffer bi: the block sums of this wavefront's block for the
+  // 8 tokens into ps[bi][t][wave][lane] (0 past the last block).
+  auto compute = [&](int r, int bi, const f4v (&w)[16]) {
+    const int b = r * RWV + wave;
+    float acc[ROUTE_TILE];
+#pragma unroll
+    for (int t = 0; t < ROUTE_TILE; ++t) acc[t] = 0.0f;
+    if (b < NB) {  // wavefront-uniform
+      const bool full = d - RB * b >= RB;  // else 32 j (d % 32 == 0): sub-chunks 0 and 1
+      const float* xb = &xs[bi][0][RB * wave] + (lane & 15);
+#pragma unroll
+      for (int tp = 0; tp < ROUTE_TILE / 2; ++tp) {
+        const float* x0 = xb + (2 * tp) * RJR;
+        const float* x1 = x0 + RJR;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          if (s < 2 || full)
+            router_fma16_2(acc[2 * tp], acc[2 * tp + 1], x0[16 * s], x1[16 * s], w[4 * s], w[4 * s + 1],
+                           w[4 * s + 2], w[4 * s + 3]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < ROUTE_TILE; ++t) ps[bi][t][wave][lane] = acc[t];
+  };
 
-  // Wait until chunk c is copied for every wavefront, given how many chunks
-  // this wavefront has issued after it (vector loads complete in order).
-  static_assert(RPF <= 7 && RPF * RDMA <= 63, "vmcnt counts at most 63 copies");
-  auto wait_chunk = [&](int newer) {
-    switch (newer) {
-      case 0: rwait_vm<0>(); break;
-      case 1: rwait_vm<RDMA>(); break;
-      case 2: rwait_vm<2 * RDMA>(); break;
-      case 3: rwait_vm<3 * RDMA>(); break;
-      case 4: rwait_vm<4 * RDMA>(); break;
-      case 5: rwait_vm<5 * RDMA>(); break;
-      default: rwait_vm<6 * RDMA>(); break;
+  // token values are requested two rounds ahead (register sets xA, xB for
+  // even and odd rounds), weights per WB
+  f4v xA[2], xB[2], wA[16], wB[WB == 2 ? 16 : 1];
+  float total = 0.0f;
+  load_x(0, xA);
+  load_w(0, wA);
+  if (NR > 1) {
+    load_x(1, xB);
+    if constexpr (WB == 2) load_w(1, wB);
+  }
+  store_x(0, xA);
+  if (NR > 2) load_x(2, xA);
+  __syncthreads();
+  // One round: compute it, stage round r+1's values (their buffer was last
+  // read in round r-1, before its barrier) and request round r+3's into the
+  // freed registers, request the next weights, then (after the barrier) fold
+  // the round's block sums into the total in block order.
+  auto round = [&](int r, f4v (&w)[16], f4v (&xn)[2]) {
+    const int bi = r & 1;
+    compute(r, bi, w);
+    if (r + 1 < NR) store_x(bi ^ 1, xn);
+    if (r + 3 < NR) load_x(r + 3, xn);
+    if constexpr (WB == 2) {
+      if (r + 2 < NR) load_w(r + 2, w);
+    } else {
+      if (r + 1 < NR) load_w(r + 1, w);
     }
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
-  // operands of 16-j sub-chunks, a ring of 4 (read 3 sub-chunks ahead)
-  f4v w[4][4];
-  float xa[4];
-  auto load_sub = [&](int sub, int b) {
-    const int c = sub >> 2, q0 = (sub & 3) * 4;
-    const char* buf = ring + (c % RNB) * R_BUF;
+    __syncthreads();
+    const int nb = min(RWV, NB - r * RWV);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) w[b][q] = *reinterpret_cast<const f4v*>(buf + (q0 + q) * 1024 + lane * 16);
-    const float* xrow = reinterpret_cast<const float*>(buf + R_WB) + (RT * wave) * RJC + q0 * 4 + (lane & 15);
-    xa[b] = xrow[0];
+    for (int bb = 0; bb < RWV; ++bb)
+      if (bb < nb) total += ps[bi][wave][bb][lane];
   };
-  // The logit's blocks of 64 j are the chunks: acc0 chains one chunk from +0,
-  // total adds the finished chunks in order.
-  float acc0 = 0.0f, total = 0.0f;
-  // One full chunk (4 sub-chunks of 16 j) per iteration, then the trailing
-  // half chunk when d % 64 == 32.  The reads of sub-chunk s+3 are issued
-  // before sub-chunk s is computed, unconditionally (past the last sub-chunk
-  // they read stale LDS and are discarded).  At the first sub-chunk of chunk c
-  // chunk c+1 is waited for and published (its sub-chunk 0 is read from the
-  // next step on); every wavefront has then read all of chunk c-1, whose
-  // buffer takes chunk c+RPF.
-  const int CF = d / RJC;
-  // A wavefront whose tokens are all past n (small batches) computes nothing
-  // but still does its share of the copies and meets every barrier.
-  const bool busy = tw < n;  // wavefront-uniform
-  wait_chunk(np - 1);  // chunks 1..np-1 were issued after chunk 0
-  if (busy) {
-    load_sub(0, 0);
-    load_sub(1, 1);
-    load_sub(2, 2);
-  }
-  for (int c = 0; c < CF; ++c) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (q == 0 && c + 1 < C) {
-        // issued so far: chunks 0 .. min(c+RPF-1, C-1); newer than c+1: the rest
-        wait_chunk(min(RPF - 2, C - c - 2));
-        if (c + RPF < C) issue(c + RPF);
-      }
-      if (busy) {
-        load_sub(4 * c + q + 3, (q + 3) & 3);
-        router_fma16_1(acc0, xa[q], w[q][0], w[q][1], w[q][2], w[q][3]);
-      }
+  // unrolled by two so that each register set has a fixed role
+  for (int r = 0; r < NR; r += 2) {
+    round(r, wA, xB);
+    if constexpr (WB == 2) {
+      if (r + 1 < NR) round(r + 1, wB, xA);
+    } else {
+      if (r + 1 < NR) round(r + 1, wA, xA);
     }
-    total += acc0;
-    acc0 = 0.0f;
   }
-  if (busy && CF < C) {  // 32 trailing j (the last block): sub-chunks 4 CF and 4 CF + 1 (already requested)
-    router_fma16_1(acc0, xa[0], w[0][0], w[0][1], w[0][2], w[0][3]);
-    router_fma16_1(acc0, xa[1], w[1][0], w[1][1], w[1][2], w[1][3]);
-    total += acc0;
-  }
+
   const int e = eg * 64 + lane;
+  const int tw = t0 + wave;  // this thread's token
   if constexpr (FUSE) {
-    static_assert(RW * RT == ROUTE_TILE, "a router workgroup covers one routing tile");
     __shared__ __attribute__((aligned(16))) RouteLds R;
-    const int tl = wave * RT;
     if (e < E) {
       const float bb = bias ? bias[e] : 0.0f;
-      R.l[tl][e] = bias ? total + bb : total;
+      R.l[wave][e] = bias ? total + bb : total;
     }
-    const int t0 = blockIdx.x * ROUTE_TILE;
     route_tile<1, 64>(R, blockIdx.x, t0, min(ROUTE_TILE, n - t0), E, k, norm, threadIdx.x, 512, ids, wout,
                rank, hist);
   } else {
@@ -606,13 +588,13 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
 
 hipError_t launch_router(const float* x, int n, int d, const float* wt, const float* bias, int E,
                          int E64, float* logits, int n_cu, hipStream_t s) {
-  dim3 grid((unsigned)((n + RW * RT - 1) / (RW * RT)), (unsigned)(E64 / 64));
+  dim3 grid((unsigned)((n + ROUTE_TILE - 1) / ROUTE_TILE), (unsigned)(E64 / 64));
   if ((long)grid.x * grid.y > n_cu)
-    router_kernel<false, RNB_SHALLOW><<<grid, 512, 0, s>>>(x, n, d, wt, bias, E, E64, logits, 0, 0, nullptr,
-                                                           nullptr, nullptr, nullptr);
+    router_kernel<false, 1><<<grid, 512, 0, s>>>(x, n, d, wt, bias, E, E64, logits, 0, 0, nullptr, nullptr,
+                                                 nullptr, nullptr);
   else
-    router_kernel<false, RNB_DEEP><<<grid, 512, 0, s>>>(x, n, d, wt, bias, E, E64, logits, 0, 0, nullptr,
-                                                        nullptr, nullptr, nullptr);
+    router_kernel<false, 2><<<grid, 512, 0, s>>>(x, n, d, wt, bias, E, E64, logits, 0, 0, nullptr, nullptr,
+                                                 nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -622,11 +604,11 @@ hipError_t launch_router_route(const float* x, int n, int d, const float* wt, co
   if (E > 64) return hipErrorInvalidValue;
   dim3 grid((unsigned)((n + ROUTE_TILE - 1) / ROUTE_TILE), 1);
   if ((long)grid.x > n_cu)
-    router_kernel<true, RNB_SHALLOW><<<grid, 512, 0, s>>>(x, n, d, wt, bias, E, 64, nullptr, k, norm, ids, w,
-                                                          rank, hist);
+    router_kernel<true, 1><<<grid, 512, 0, s>>>(x, n, d, wt, bias, E, 64, nullptr, k, norm, ids, w, rank,
+                                                hist);
   else
-    router_kernel<true, RNB_DEEP><<<grid, 512, 0, s>>>(x, n, d, wt, bias, E, 64, nullptr, k, norm, ids, w,
-                                                       rank, hist);
+    router_kernel<true, 2><<<grid, 512, 0, s>>>(x, n, d, wt, bias, E, 64, nullptr, k, norm, ids, w, rank,
+                                                hist);
   return hipGetLastError();
 }
 
