@@ -89,137 +89,104 @@ __device__ __forceinline__ float wave_sum_rows(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
-// Routing of one tile of ROUTE_TILE tokens, TPT threads per token (threads
-// tid < ROUTE_TILE * TPT of the workgroup; every thread of the workgroup
-// calls this, since it meets workgroup barriers; both the fused router and
-// the routing launch for E > 64 give each token a wavefront).  The tile's logits
-// l[token][e] are in LDS.  Top-k by the contract's order (logit descending,
-// id ascending): each expert's 64-bit key orders exactly that way and is
-// unique, the token's TPT threads hold its keys in registers (expert
-// g + TPT c in thread g, NKEY >= E/TPT of them), and slot r takes the largest
-// key left after r rounds of a maximum over the TPT threads, its owner
-// clearing it.  Then
-// softmax over all E, optional renormalisation, and the per-expert rank of
-// each (token, slot) pair among the tile's pairs in (token, slot) order, with
-// the tile's histogram, for the bucketing kernel.
+// Routing of one tile of ROUTE_TILE tokens, one wavefront per token (threads
+// tid < ROUTE_TILE * 64 of the workgroup; every thread of the workgroup calls
+// this, since it meets workgroup barriers).  The tile's logits l[token][e] are
+// in LDS.  Top-k by the contract's order (logit descending, id ascending): each
+// expert's 64-bit key orders exactly that way and is unique; lane g holds the
+// keys of experts g + 64c, and slot r takes the largest key left after r
+// rounds of a wavefront maximum, its owner clearing it.  The maximum is
+// uniform, so lane r keeps slot r's expert and logit (decoded from the key).
+// Then softmax over all E, optional renormalisation, and, for the bucketing
+// kernel, the per-expert rank of each (token, slot) pair among the tile's
+// pairs in (token, slot) order and the tile's histogram.  A token's k experts
+// are distinct, so a pair's rank is the number of earlier tokens of the tile
+// that picked the same expert: both come from per-token ballots of the picked
+// experts.
 struct RouteLds {
   float l[ROUTE_TILE][MAX_EXPERTS];
-  int ids[ROUTE_TILE * MAX_TOPK];
-  float val[ROUTE_TILE][MAX_TOPK];
-  int cnt[MAX_EXPERTS];
+  unsigned long long pick[ROUTE_TILE][MAX_EXPERTS / 64];  // bit g of [t][c]: token t picked expert g + 64c
 };
 
-template <int NKEY, int TPT>
+// The logit a key was made from (-0 comes back as +0).
+__device__ __forceinline__ float key_logit(unsigned long long key) {
+  const uint32_t ord = (uint32_t)(key >> 32);
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord);
+}
+
+template <int NKEY>
 __device__ __forceinline__ void route_tile(RouteLds& R, int tile, int t0, int nt, int E, int k, int norm, int tid,
-                           int nthreads, int32_t* __restrict__ ids, float* __restrict__ wout,
-                           int32_t* __restrict__ rank, int32_t* __restrict__ hist) {
-  static_assert(TPT == 16 || TPT == 64, "a token's threads stay inside one wavefront");
-  for (int e = tid; e < E; e += nthreads) R.cnt[e] = 0;
+                                           int32_t* __restrict__ ids, float* __restrict__ wout,
+                                           int32_t* __restrict__ rank, int32_t* __restrict__ hist) {
   __syncthreads();  // the caller's logit writes are visible to every thread
-  // thread (token tl = tid / TPT, lane g = tid % TPT of the token) owns experts g + TPT c
-  const int tl = tid / TPT, g = tid % TPT;
-  const bool mine = tid < ROUTE_TILE * TPT;
+  const int tl = tid >> 6, g = tid & 63;
+  const bool mine = tid < ROUTE_TILE * 64;  // wavefront-uniform
+  int slot[NKEY];
   if (mine) {
-    // slots >= k and absent tokens keep -1 (the same wavefront's later
-    // stores below land after this one)
-    if (g < MAX_TOPK) R.ids[tl * MAX_TOPK + g] = -1;
     unsigned long long key[NKEY];
 #pragma unroll
     for (int c = 0; c < NKEY; ++c) {
-      const int e = g + TPT * c;
+      const int e = g + 64 * c;
       key[c] = (e < E) ? topk_key(R.l[tl][e], e) : 0ull;  // 0: below every real key
+      slot[c] = -1;
     }
+    int my_id = 0;
+    float my_val = 0.0f;
     for (int r = 0; r < k; ++r) {
       unsigned long long m = 0ull;
 #pragma unroll
       for (int c = 0; c < NKEY; ++c) m = key[c] > m ? key[c] : m;
-      if constexpr (TPT == 64) {
-        m = wave_max_u64(m);
-      } else {
+      m = wave_max_u64(m);
 #pragma unroll
-        for (int off = TPT / 2; off > 0; off >>= 1) {
-          const unsigned long long o = __shfl_xor(m, off, TPT);
-          m = o > m ? o : m;
-        }
+      for (int c = 0; c < NKEY; ++c) {
+        const bool hit = key[c] == m;
+        slot[c] = hit ? r : slot[c];
+        key[c] = hit ? 0ull : key[c];
       }
-#pragma unroll
-      for (int c = 0; c < NKEY; ++c) key[c] = key[c] == m ? 0ull : key[c];
-      if (g == 0 && tl < nt) {
-        const int e = (int)~(uint32_t)m;
-        R.ids[tl * MAX_TOPK + r] = e;
-        R.val[tl][r] = R.l[tl][e];
+      if (g == r) {
+        my_id = (int)~(uint32_t)m;
+        my_val = key_logit(m);
       }
     }
-  }
-  __syncthreads();
-
-  if (mine) {
-    // softmax over all E (the TPT threads of a token share the sum), weights of the k slots
-    const float m = R.val[tl][0];
+    // softmax over all E, weights of the k slots (lane s: slot s)
+    const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val), 0));
     float part = 0.0f;
-    for (int e = g; e < E; e += TPT) part += expf(R.l[tl][e] - m);
-    if constexpr (TPT == 64) {
-      part = wave_sum_rows(part);
-    } else {
 #pragma unroll
-      for (int off = TPT / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, TPT);
+    for (int c = 0; c < NKEY; ++c) {
+      const int e = g + 64 * c;
+      if (e < E) part += expf(R.l[tl][e] - m0);
     }
-    float p = (g < k) ? expf(R.val[tl][min(g, k - 1)] - m) / part : 0.0f;
-    if (norm) {
-      float sum = p;
-      if constexpr (TPT == 64) {
-        sum = wave_sum_rows(sum);
-      } else {
-#pragma unroll
-        for (int off = TPT / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, TPT);
-      }
-      p = p / sum;
-    }
+    part = wave_sum_rows(part);
+    float p = (g < k) ? expf(my_val - m0) / part : 0.0f;
+    if (norm) p = p / wave_sum_rows(p);
     if (tl < nt && g < k) {
-      ids[(size_t)(t0 + tl) * k + g] = R.ids[tl * MAX_TOPK + g];
+      ids[(size_t)(t0 + tl) * k + g] = my_id;
       wout[(size_t)(t0 + tl) * k + g] = p;
     }
-  }
-
-  // rank of pair q = (token, slot) among the tile's earlier pairs of the same expert
-  const int np = nt * k;
-  if (tid < np) {
-    const int q = tid;
-    const int e = R.ids[(q / k) * MAX_TOPK + q % k];
-    int r = 0, later = 0;
-    // pairs of earlier tokens (all their k slots), then this token's earlier
-    // slots; the ids of two tokens are read per pass, all reads issued before
-    // the compares
-    for (int t2 = 0; t2 < nt; t2 += 2) {
-      // unconditional reads (inside R.ids: t2 + 1 < ROUTE_TILE), masked below
-      int4 v[2][MAX_TOPK / 4];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int c4 = 0; c4 < MAX_TOPK / 4; ++c4)
-          v[h][c4] = reinterpret_cast<const int4*>(&R.ids[(t2 + h) * MAX_TOPK])[c4];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int c4 = 0; c4 < MAX_TOPK / 4; ++c4) {
-          const int ev[4] = {v[h][c4].x, v[h][c4].y, v[h][c4].z, v[h][c4].w};
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            // slots past k and absent tokens hold -1; the order tests are
-            // sign bits of differences (no mask operations)
-            const int q2 = (t2 + h) * k + 4 * c4 + u;
-            const int before = (int)((uint32_t)(q2 - q) >> 31), after = (int)((uint32_t)(q - q2) >> 31);
-            const bool same = ev[u] == e;
-            r += same ? before : 0;
-            later |= same ? after : 0;
-          }
-        }
+    for (int c = 0; c < NKEY; ++c) {
+      const unsigned long long b = __ballot(slot[c] >= 0);
+      if (g == 0) R.pick[tl][c] = (tl < nt) ? b : 0ull;  // absent tokens pick nothing
     }
-    rank[(size_t)(t0 + q / k) * k + q % k] = r;
-    if (!later) R.cnt[e] = r + 1;
   }
   __syncthreads();
-  for (int e = tid; e < E; e += nthreads) hist[(size_t)tile * E + e] = R.cnt[e];
+  if (mine) {
+#pragma unroll
+    for (int c = 0; c < NKEY; ++c) {
+      if (tl < nt && slot[c] >= 0) {
+        int rk = 0;
+        for (int t2 = 0; t2 < tl; ++t2) rk += (int)((R.pick[t2][c] >> g) & 1ull);
+        rank[(size_t)(t0 + tl) * k + slot[c]] = rk;
+      }
+      const int e = g + 64 * c;
+      if (tl == 0 && e < E) {
+        int cnt = 0;
+#pragma unroll
+        for (int t2 = 0; t2 < ROUTE_TILE; ++t2) cnt += (int)((R.pick[t2][c] >> g) & 1ull);
+        hist[(size_t)tile * E + e] = cnt;
+      }
+    }
+  }
 }
 
 // Router logits for ROUTE_TILE (8) tokens x 64 experts per workgroup (lane =
@@ -366,8 +333,7 @@ __global__ __launch_bounds__(512, 3 - WB) void router_kernel(
       const float bb = bias ? bias[e] : 0.0f;
       R.l[wave][e] = bias ? total + bb : total;
     }
-    route_tile<1, 64>(R, blockIdx.x, t0, min(ROUTE_TILE, n - t0), E, k, norm, threadIdx.x, 512, ids, wout,
-               rank, hist);
+    route_tile<1>(R, blockIdx.x, t0, min(ROUTE_TILE, n - t0), E, k, norm, threadIdx.x, ids, wout, rank, hist);
   } else {
     if (e < E) {
       const float bb = bias ? bias[e] : 0.0f;
@@ -413,8 +379,7 @@ __global__ __launch_bounds__(ROUTE_WIDE_THREADS) void route_kernel(
   const int t0 = blockIdx.x * ROUTE_TILE;
   const int nt = min(ROUTE_TILE, n - t0);
   route_load_logits(R, logits, t0, nt, E, threadIdx.x);
-  route_tile<MAX_EXPERTS / 64, 64>(R, blockIdx.x, t0, nt, E, k, norm, threadIdx.x, ROUTE_WIDE_THREADS, ids, wout, rank,
-                                   hist);
+  route_tile<MAX_EXPERTS / 64>(R, blockIdx.x, t0, nt, E, k, norm, threadIdx.x, ids, wout, rank, hist);
 }
 
 // ---------------------------------------------------------------- decode
