@@ -286,15 +286,18 @@ __global__ __launch_bounds__(512, 3 - WB) void router_kernel(
   // even and odd rounds), weights per WB
   f4v xA[2], xB[2], wA[16], wB[WB == 2 ? 16 : 1];
   float total = 0.0f;
+  // Round 0's operands first and alone (every CU requests them at once, and
+  // later requests would share the bandwidth they arrive by); the next
+  // rounds' requests follow the barrier and arrive during round 0.
   load_x(0, xA);
   load_w(0, wA);
+  store_x(0, xA);
+  __syncthreads();
   if (NR > 1) {
     load_x(1, xB);
     if constexpr (WB == 2) load_w(1, wB);
   }
-  store_x(0, xA);
   if (NR > 2) load_x(2, xA);
-  __syncthreads();
   // One round: compute it, stage round r+1's values (their buffer was last
   // read in round r-1, before its barrier) and request round r+3's into the
   // freed registers, request the next weights, then (after the barrier) fold
