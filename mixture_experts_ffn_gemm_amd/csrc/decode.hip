@@ -175,19 +175,6 @@ struct GroupList {
   int pairs[MAX_GROUPS][DECODE_MAX_TOKENS];
 };
 
-// Wavefront maximum of an unsigned value: prefix maxima within each row of
-// 16 lanes by DPP shifts, the row maxima carried into rows 1 and 3, then into
-// rows 2 and 3 by DPP row broadcasts; lane 63 ends with the maximum.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true));  // row_shr:1
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true));  // row_shr:2
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true));  // row_shr:4
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true));  // row_shr:8
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
-  return __builtin_amdgcn_readlane(v, 63);
-}
-
 // Inclusive prefix sum over the wavefront (same DPP pattern with additions).
 __device__ __forceinline__ int wave_inclusive_sum(int v) {
   v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);
@@ -233,9 +220,8 @@ __device__ __forceinline__ int decode_route(const DecodeArgs& a, DecRoute& R, Gr
       unsigned long long b = kv[0];
 #pragma unroll
       for (int m = 1; m < 4; ++m) b = kv[m] > b ? kv[m] : b;
-      const uint32_t mh = wave_max_u32((uint32_t)(b >> 32));
-      const uint32_t ml = wave_max_u32((uint32_t)(b >> 32) == mh ? (uint32_t)b : 0u);
-      const unsigned long long mx = ((unsigned long long)mh << 32) | ml;
+      const unsigned long long mx = wave_max_key(b);
+      const uint32_t ml = (uint32_t)mx;
 #pragma unroll
       for (int m = 0; m < 4; ++m)
         if (kv[m] == mx) {  // keys are distinct: one lane, one m

@@ -71,6 +71,29 @@ __device__ __forceinline__ unsigned long long topk_key(float l, int e) {
   return ((unsigned long long)ord << 32) | (uint32_t)~(uint32_t)e;
 }
 
+// Wavefront maximum of an unsigned value: prefix maxima within each row of
+// 16 lanes by DPP shifts, the row maxima carried into rows 1 and 3, then into
+// rows 2 and 3 by DPP row broadcasts; lane 63 ends with the maximum, which is
+// returned to every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true));  // row_shr:1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true));  // row_shr:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true));  // row_shr:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true));  // row_shr:8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Wavefront maximum of 64-bit keys whose values are distinct across lanes (or
+// zero): the maximum of the high words, then of the low words among the lanes
+// that hold that high word.
+__device__ __forceinline__ unsigned long long wave_max_key(unsigned long long v) {
+  const uint32_t mh = wave_max_u32((uint32_t)(v >> 32));
+  const uint32_t ml = wave_max_u32((uint32_t)(v >> 32) == mh ? (uint32_t)v : 0u);
+  return ((unsigned long long)mh << 32) | ml;
+}
+
 // Workgroup barrier that orders LDS accesses only: global loads still in flight
 // (a register prefetch ring) are not drained, unlike __syncthreads().
 __device__ inline void lds_barrier() {

@@ -46,36 +46,14 @@ __device__ __forceinline__ void router_fma16_2(float& acc0, float& acc1, float x
 }
 #undef RFMA2
 
-// Reductions over all 64 lanes of a wavefront (every lane active), without
-// the LDS crossbar: four DPP steps inside each 16-lane row (swap neighbours,
-// swap pairs, mirror the halves of 8, mirror the halves of 16) leave the
-// row's result in all of its lanes, then the four rows' results are read
-// with v_readlane and combined in a fixed order.
+// Sum over all 64 lanes of a wavefront (every lane active), without the LDS
+// crossbar: four DPP steps inside each 16-lane row (swap neighbours, swap
+// pairs, mirror the halves of 8, mirror the halves of 16) leave the row's sum
+// in all of its lanes, then the four rows' sums are read with v_readlane and
+// added in a fixed order.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
-}
-template <int CTRL>
-__device__ __forceinline__ unsigned long long dpp64(unsigned long long v) {
-  const uint32_t lo = dpp32<CTRL>((uint32_t)v), hi = dpp32<CTRL>((uint32_t)(v >> 32));
-  return ((unsigned long long)hi << 32) | lo;
-}
-__device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) {
-  return a > b ? a : b;
-}
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-  v = umax64(v, dpp64<0xB1>(v));   // quad_perm [1,0,3,2]
-  v = umax64(v, dpp64<0x4E>(v));   // quad_perm [2,3,0,1]
-  v = umax64(v, dpp64<0x141>(v));  // row_half_mirror
-  v = umax64(v, dpp64<0x140>(v));  // row_mirror
-  unsigned long long r = 0ull;
-#pragma unroll
-  for (int row = 0; row < 4; ++row) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * row);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * row);
-    r = umax64(r, ((unsigned long long)hi << 32) | lo);
-  }
-  return r;
 }
 __device__ __forceinline__ float wave_sum_rows(float v) {
   v += __uint_as_float(dpp32<0xB1>(__float_as_uint(v)));
@@ -136,7 +114,7 @@ __device__ __forceinline__ void route_tile(RouteLds& R, int tile, int t0, int nt
       unsigned long long m = 0ull;
 #pragma unroll
       for (int c = 0; c < NKEY; ++c) m = key[c] > m ? key[c] : m;
-      m = wave_max_u64(m);
+      m = wave_max_key(m);
 #pragma unroll
       for (int c = 0; c < NKEY; ++c) {
         const bool hit = key[c] == m;
@@ -175,7 +153,8 @@ __device__ __forceinline__ void route_tile(RouteLds& R, int tile, int t0, int nt
     for (int c = 0; c < NKEY; ++c) {
       if (tl < nt && slot[c] >= 0) {
         int rk = 0;
-        for (int t2 = 0; t2 < tl; ++t2) rk += (int)((R.pick[t2][c] >> g) & 1ull);
+#pragma unroll
+        for (int t2 = 0; t2 < ROUTE_TILE; ++t2) rk += (t2 < tl) ? (int)((R.pick[t2][c] >> g) & 1ull) : 0;
         rank[(size_t)(t0 + tl) * k + slot[c]] = rk;
       }
       const int e = g + 64 * c;
