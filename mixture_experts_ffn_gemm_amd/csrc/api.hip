@@ -359,9 +359,15 @@ int run_decode(const moe_ffn_weights* W, const float* x, int32_t n, float* out, 
   a.partial = partial;
   HIP_TRY(launch_decode_gateup(a, s));
   HIP_TRY(mark(2));
-  HIP_TRY(launch_decode_down(a, s));
-  HIP_TRY(mark(3));
-  HIP_TRY(launch_combine(partial, w, dm.has_shared ? gs : nullptr, n, dm.k, kk, dm.d, out, s));
+  if (n == 1 && kk <= DECODE_FUSED_MAX_SLOTS) {
+    // one token: down matvec and combine in one launch (stage 3 is empty)
+    HIP_TRY(launch_decode_down_combine(a, gs, out, s));
+    HIP_TRY(mark(3));
+  } else {
+    HIP_TRY(launch_decode_down(a, s));
+    HIP_TRY(mark(3));
+    HIP_TRY(launch_combine(partial, w, dm.has_shared ? gs : nullptr, n, dm.k, kk, dm.d, out, s));
+  }
   HIP_TRY(mark(4));
 
   HIP_TRY(copy_routing(dm, n, r, ids, w, gs, exp_start, tok_i, tok_k, partial, s));

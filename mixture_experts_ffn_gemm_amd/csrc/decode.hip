@@ -488,6 +488,155 @@ __global__ __launch_bounds__(DW * 64) void decode_gemv_kernel(DecodeArgs a) {
   }
 }
 
+// ---- down matvec + ordered combine for one token ----
+// Decode of a single token (n == 1, kk = k (+1) <= DC_SB slots): the down
+// matvec of its selected experts (and the shared one) and the ordered combine
+// in one launch.  Workgroup u owns output rows 32u .. 32u+31 (tile u%4 of
+// strip u/4 of every down plane) for all kk slots, so the combine needs no
+// other workgroup's results.  Wavefront w takes k-steps w, w+8, ... of every
+// slot, as the gathered down launch does, and requests the pieces of all kk
+// slots before it waits for any: one memory round trip per 8 k-steps for the
+// whole token.  The per-slot sums meet in LDS in wavefront order (the order,
+// and so the bits, of the gathered down launch and its partials), and lanes
+// 0..31 of wavefront 0 then run the combine's chain over the slots (the
+// chain of combine_kernel).  The partials are written as well.
+constexpr int DC_SB = DECODE_FUSED_MAX_SLOTS;  // slots per token this launch serves
+struct Piece1 {
+  v4u w[KSTEP];  // codes of blocks 0..3 (lane: row l%32, half l/32 of each block)
+  v2u s[2];      // scale pair words of blocks 0-1 and 2-3
+};
+
+__device__ __forceinline__ void compute_piece1(const Piece1& p, const int8_t* act, const uint16_t* as, int lane,
+                                               float& acc) {
+  const float sw[KSTEP] = {h2f(p.s[0][0]), h2f(p.s[0][1]), h2f(p.s[1][0]), h2f(p.s[1][1])};
+  const int8_t* arow = act + (lane >> 5) * 16;
+  uint4 av[KSTEP];
+#pragma unroll
+  for (int kbi = 0; kbi < KSTEP; ++kbi) av[kbi] = *reinterpret_cast<const uint4*>(arow + kbi * 32);
+  const uint2 s2 = *reinterpret_cast<const uint2*>(as);
+  const float sa[KSTEP] = {h2f(s2.x), h2f(s2.x >> 16), h2f(s2.y), h2f(s2.y >> 16)};
+#pragma unroll
+  for (int kbi = 0; kbi < KSTEP; ++kbi) {
+    const v4u wv = p.w[kbi];
+    int dot = __builtin_amdgcn_sdot4((int)wv[0], (int)av[kbi].x, 0, false);
+    dot = __builtin_amdgcn_sdot4((int)wv[1], (int)av[kbi].y, dot, false);
+    dot = __builtin_amdgcn_sdot4((int)wv[2], (int)av[kbi].z, dot, false);
+    dot = __builtin_amdgcn_sdot4((int)wv[3], (int)av[kbi].w, dot, false);
+    acc = __builtin_fmaf((float)dot, sw[kbi] * sa[kbi], acc);
+  }
+}
+
+__global__ __launch_bounds__(DW * 64) void decode_down_combine_kernel(DecodeArgs a, const float* __restrict__ gs,
+                                                                      float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) int8_t s_act[DC_SB][DW * 128];      // the pass's h codes per slot
+  __shared__ __attribute__((aligned(16))) uint16_t s_as[DC_SB][DW * KSTEP];   // and their scales
+  __shared__ float red[DW][DC_SB][32];
+  __shared__ float ys[DC_SB][32];
+  __shared__ int s_g[DC_SB], s_ks[DC_SB], s_ex[DC_SB];
+  __shared__ float s_w[DC_SB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kk = a.kk, k = a.k, E = a.E;
+  // slot s: expert ids[s] (s < k) or the shared expert, its k-step count,
+  // scale exponent and combine weight
+  if (tid < kk) {
+    int g = tid < k ? a.ids[tid] : E;
+    g = (g >= 0 && g <= E) ? g : 0;
+    s_g[tid] = g;
+    s_ks[tid] = ((g == E) ? a.Fs_pad : a.F_pad) / (KSTEP * QB);
+    s_ex[tid] = a.dn_exp[g];
+    s_w[tid] = tid < k ? a.w[tid] : gs[0];
+  }
+  __syncthreads();
+  const int KSM = a.kmax_pad / (KSTEP * QB);
+  const int strip = blockIdx.x >> 2, tsel = blockIdx.x & 3;
+  const uint32_t o_code = (uint32_t)lane * 16, o_scale = (uint32_t)(lane & 31) * 8;
+  float acc[DC_SB];
+#pragma unroll
+  for (int i = 0; i < DC_SB; ++i) acc[i] = 0.0f;
+
+  for (int ks0 = 0; ks0 < KSM; ks0 += DW) {
+    const int kq = ks0 + wave;  // this wavefront's k-step of the pass
+    // the pass's h rows (slot s: pair row s), requested first: thread q moves
+    // 16-byte piece q and q + 512 of the DC_SB x 64, thread q < DC_SB * DW the
+    // 4 scales of (slot q / DW, k-step q % DW); pieces past a slot's k-steps
+    // are not moved (and not read)
+    uint4 hv[2];
+    bool hok[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int q = tid + h * DW * 64, i = q >> 6, j = (q >> 3) & 7, c16 = q & 7;
+      const int ic = min(i, kk - 1);
+      hok[h] = i < kk && ks0 + j < s_ks[ic];
+      hv[h] = hok[h] ? *reinterpret_cast<const uint4*>(a.hq + (size_t)ic * a.kmax_pad + (ks0 + j) * 128 + c16 * 16)
+                     : make_uint4(0u, 0u, 0u, 0u);
+    }
+    const int si = min(tid / DW, kk - 1), sj = tid % DW;
+    const bool sok = tid < DC_SB * DW && tid / DW < kk && ks0 + sj < s_ks[si];
+    const uint2 sv = sok ? reinterpret_cast<const uint2*>(a.hs + (size_t)si * (a.kmax_pad / QB))[ks0 + sj]
+                         : make_uint2(0u, 0u);
+    // the pieces of every slot (a k-step past a slot's last re-reads its last
+    // one and is not computed)
+    Piece1 p[DC_SB];
+#pragma unroll
+    for (int i = 0; i < DC_SB; ++i) {
+      const int s = min(i, kk - 1);
+      const int g = __builtin_amdgcn_readfirstlane(s_g[s]);
+      const int KSs = __builtin_amdgcn_readfirstlane(s_ks[s]);
+      const uint8_t* plane = (g == E ? a.sh_dn : a.dn + (size_t)g * a.dn_group) + (size_t)strip * KSs * DN_KSTEP_BYTES;
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(plane), (short)0, -1, BUF_DWORD3);
+      const int step_off = min(kq, KSs - 1) * DN_KSTEP_BYTES;
+#pragma unroll
+      for (int kbi = 0; kbi < KSTEP; ++kbi)
+        p[i].w[kbi] = __builtin_amdgcn_raw_buffer_load_b128(rs, o_code, step_off + (kbi * 4 + tsel) * 1024, 0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        p[i].s[h] = __builtin_amdgcn_raw_buffer_load_b64(rs, o_scale, step_off + 16 * 1024 + tsel * 512 + h * 256, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every request is out before any wait
+    lds_barrier();  // every wavefront is done with the previous pass's LDS
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int q = tid + h * DW * 64, i = q >> 6, r = q & 63;
+      if (hok[h]) reinterpret_cast<uint4*>(s_act[i])[r] = hv[h];
+    }
+    if (sok) reinterpret_cast<uint2*>(s_as[si])[sj] = sv;
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < DC_SB; ++i)
+      if (i < kk && kq < s_ks[i])
+        compute_piece1(p[i], s_act[i] + (kq - ks0) * 128, s_as[i] + (kq - ks0) * KSTEP, lane, acc[i]);
+  }
+
+  // the lane pair (two halves of each block), then the wavefronts in order
+#pragma unroll
+  for (int i = 0; i < DC_SB; ++i) {
+    const float v = acc[i] + __shfl_xor(acc[i], 32, 64);
+    if (i < kk && lane < 32) red[wave][i][lane] = v;
+  }
+  __syncthreads();
+  const int row0 = 32 * (int)blockIdx.x;
+  if (tid < DC_SB * 32) {
+    const int i = tid >> 5, r = tid & 31;
+    if (i < kk) {
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < DW; ++w) v += red[w][i][r];
+      v = ldexpf(v, s_ex[i] - 23);
+      ys[i][r] = v;
+      if (row0 + r < a.d) a.partial[(size_t)i * a.d + row0 + r] = v;
+    }
+  }
+  __syncthreads();
+  if (tid < 32 && row0 + tid < a.d) {
+    float o = 0.0f;
+    for (int s = 0; s < k; ++s) o = __builtin_fmaf(s_w[s], ys[s][tid], o);
+    if (a.has_shared) o = __builtin_fmaf(s_w[k], ys[k][tid], o);
+    out[row0 + tid] = o;
+  }
+}
+
 }  // namespace
 
 // Workgroups per CU that fit at once (registers and LDS), from the runtime's
@@ -511,6 +660,12 @@ hipError_t launch_decode_gateup(const DecodeArgs& a, hipStream_t s) {
   const long units = (long)a.n_bound * (a.kmax_pad / 32);
   const long grid = std::min<long>(units, (long)a.n_cu * resident_per_cu<true>());
   decode_gemv_kernel<true><<<(unsigned)grid, DW * 64, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_down_combine(const DecodeArgs& a, const float* gs, float* out, hipStream_t s) {
+  if (a.n != 1 || a.kk > DC_SB) return hipErrorInvalidValue;
+  decode_down_combine_kernel<<<(unsigned)(a.d_pad / 32), DW * 64, 0, s>>>(a, gs, out);
   return hipGetLastError();
 }
 

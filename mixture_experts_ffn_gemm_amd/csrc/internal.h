@@ -268,6 +268,11 @@ struct DecodeArgs {
 };
 hipError_t launch_decode_gateup(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s);
+// One token (n == 1) with at most 9 slots (k plus the shared expert): the down
+// matvec and the ordered combine in one launch, out [d] and partial as the
+// two launches write them.
+constexpr int DECODE_FUSED_MAX_SLOTS = 9;
+hipError_t launch_decode_down_combine(const DecodeArgs& a, const float* gs, float* out, hipStream_t s);
 
 hipError_t launch_combine(const float* partial, const float* w, const float* gs, int n, int k,
                           int kk, int d, float* out, hipStream_t s);

@@ -812,6 +812,30 @@ def test_decode_repeat_is_bitwise_identical():
         assert np.array_equal(a[key], b[key]), key
 
 
+@pytest.mark.parametrize("case", range(len(DECODE_SHAPES)))
+def test_decode_single_token_out_is_the_combine_of_its_partials(case):
+    """One token with at most 9 slots (k plus the shared expert) runs the down
+    matvec and the ordered combine in one launch.  Its output must equal, bit
+    for bit, the standalone combine stage applied to the partials, weights and
+    shared gate the same call reports (the same fp32 chain over the slots);
+    shapes with more slots take the two-launch path, which must satisfy the
+    same identity."""
+    from mixture_experts_ffn_gemm_amd import binding as B
+    shape, lw = mw.random_shape_case(case, **DECODE_SHAPES[case])
+    s = lw.shape
+    say(f"decode n=1 combine identity case {case}: d={s.d} E={s.n_experts} k={s.top_k} shared={bool(s.shared_ffn)}")
+    x = mw.make_tokens(700 + case, 1, shape.d)
+    g = run_gpu(lw, x, api="decode")
+    check_routing(lw, x, g)
+    check_outputs(lw, x, g)
+    out = torch.full((1, s.d), float("nan"), dtype=torch.float32, device="cuda")
+    B.moe_ffn_combine(torch.from_numpy(g["partial"]).cuda(), torch.from_numpy(g["topk_w"]).cuda(),
+                      torch.from_numpy(g["shared_gate"]).cuda() if s.shared_ffn else None,
+                      1, s.top_k, s.d, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), g["out"])
+
+
 def test_empty_batch_is_a_noop():
     from mixture_experts_ffn_gemm_amd.layer import MoeLayer
     lw = mw.workload_layer("tiny")
