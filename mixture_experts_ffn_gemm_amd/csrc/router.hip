@@ -45,6 +45,21 @@ __device__ __forceinline__ void router_fma16_2(float& acc0, float& acc1, float x
         "v"(w3.z), "v"(w3.w));
 }
 #undef RFMA2
+#define RFMA1(I, W) "v_fmac_f32_dpp %0, %1, " W " row_newbcast:" #I " row_mask:0xf bank_mask:0xf\n\t"
+// One chain of router_fma16_2's form (a batch with an odd token count).
+__device__ __forceinline__ void router_fma16_1(float& acc0, float x0, const f4v& w0, const f4v& w1, const f4v& w2,
+                                               const f4v& w3) {
+  asm volatile("s_nop 1\n\t"
+      RFMA1(0, "%2") RFMA1(1, "%3") RFMA1(2, "%4") RFMA1(3, "%5")
+      RFMA1(4, "%6") RFMA1(5, "%7") RFMA1(6, "%8") RFMA1(7, "%9")
+      RFMA1(8, "%10") RFMA1(9, "%11") RFMA1(10, "%12") RFMA1(11, "%13")
+      RFMA1(12, "%14") RFMA1(13, "%15") RFMA1(14, "%16") RFMA1(15, "%17")
+      : "+v"(acc0)
+      : "v"(x0), "v"(w0.x), "v"(w0.y), "v"(w0.z), "v"(w0.w), "v"(w1.x), "v"(w1.y),
+        "v"(w1.z), "v"(w1.w), "v"(w2.x), "v"(w2.y), "v"(w2.z), "v"(w2.w), "v"(w3.x), "v"(w3.y),
+        "v"(w3.z), "v"(w3.w));
+}
+#undef RFMA1
 
 // Sum over all 64 lanes of a wavefront (every lane active), without the LDS
 // crossbar: four DPP steps inside each 16-lane row (swap neighbours, swap
@@ -516,6 +531,96 @@ __global__ __launch_bounds__(256, 1) void decode_router_kernel(
 }
 
 
+// The same logits for batches of 3..8 tokens, where decode_router_kernel's
+// per-lane token reads bind (each lane reads its block's 16 quads for every
+// token).  One workgroup per 16 experts, 8 wavefronts: in each pass of 2048 j
+// row r of wavefront w (its 16 lanes are the 16 experts) chains block 4w + r
+// for all NT tokens with its lanes' weight quads in registers, and the token
+// values reach the row by DPP row broadcast inside the FMA (lane i of the row
+// reads value i of each 16-j piece), so one LDS read serves 16 steps.  The
+// block sums meet in LDS and thread (expert, token) adds them in block order.
+constexpr int DRP_E = 16;  // experts per workgroup
+template <int NT>
+__global__ __launch_bounds__(512, 1) void decode_router_dpp_kernel(
+    const float* __restrict__ x, int n, int d, int d_pad, const float* __restrict__ wt,
+    const float* __restrict__ bias, int E, int E64, int n_rwg, float* __restrict__ logits,
+    const float* __restrict__ shg, float* __restrict__ gs, int8_t* __restrict__ xq,
+    uint16_t* __restrict__ xs) {
+  __shared__ __attribute__((aligned(16))) float xl[NT][DR_JP];
+  __shared__ __attribute__((aligned(16))) float part[NT][DRP_E][DR_NBP + 4];  // +4: bank offset per expert
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if ((int)blockIdx.x >= n_rwg) {
+    const int t = (int)blockIdx.x - n_rwg;
+    if (wave == 0 && t < n)
+      decode_quantize_row(x + (size_t)t * d, d, d_pad, shg, gs + t, xq + (size_t)t * d_pad,
+                          xs + (size_t)t * (d_pad / QB), lane);
+    return;
+  }
+  const int el = lane & 15, bl = 4 * wave + (lane >> 4);
+  const int e = DRP_E * (int)blockIdx.x + el;  // < E64: the matrix holds zero rows past E
+  const int se = tid % DRP_E, st = tid / DRP_E;
+  float total = 0.0f;
+  for (int j0 = 0; j0 < d; j0 += DR_JP) {
+    // this pass's token values (thread tid: quad tid of every token; quads
+    // past d skipped)
+    f4v xv[NT];
+    const bool xin = j0 + 4 * tid < d;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      if (xin) xv[t] = *reinterpret_cast<const f4v*>(x + (size_t)t * d + j0 + 4 * tid);
+    // this row's block: the lane's 16 weight quads (8 or none past d's last
+    // full block; d % 32 == 0)
+    const int jb = j0 + DR_RB * bl;
+    const int nq = max(0, min(DR_RB, d - jb)) / 4;
+    f4v w[DR_RB / 4];
+#pragma unroll
+    for (int q = 0; q < DR_RB / 4; ++q)
+      if (q < nq) w[q] = *reinterpret_cast<const f4v*>(wt + ((size_t)(jb / 4 + q) * E64 + e) * 4);
+    if (j0 > 0) __syncthreads();  // every lane is done with the previous pass's values and sums
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      if (xin) *reinterpret_cast<f4v*>(&xl[t][4 * tid]) = xv[t];
+    __syncthreads();
+    float acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = 0.0f;
+    const float* xb = &xl[0][DR_RB * bl] + el;
+    auto piece = [&](int s) {  // 16 j: quads 4s .. 4s+3
+#pragma unroll
+      for (int t = 0; t + 1 < NT; t += 2)
+        router_fma16_2(acc[t], acc[t + 1], xb[t * DR_JP + 16 * s], xb[(t + 1) * DR_JP + 16 * s], w[4 * s],
+                       w[4 * s + 1], w[4 * s + 2], w[4 * s + 3]);
+      if constexpr (NT % 2)
+        router_fma16_1(acc[NT - 1], xb[(NT - 1) * DR_JP + 16 * s], w[4 * s], w[4 * s + 1], w[4 * s + 2],
+                       w[4 * s + 3]);
+    };
+    if (nq > 0) {  // row-uniform; the DPP reads stay inside the row
+      piece(0);
+      piece(1);
+      if (nq == DR_RB / 4) {
+        piece(2);
+        piece(3);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) part[t][el][bl] = acc[t];
+    __syncthreads();
+    if (st < NT) {
+      // all of the pass's block sums read at once (past nb: stale, unused)
+      const int nb = min(DR_NBP, (d - j0 + DR_RB - 1) / DR_RB);
+      f4v pv[DR_NBP / 4];
+#pragma unroll
+      for (int b4 = 0; b4 < DR_NBP / 4; ++b4) pv[b4] = *reinterpret_cast<const f4v*>(&part[st][se][4 * b4]);
+#pragma unroll
+      for (int b = 0; b < DR_NBP; ++b)
+        if (b < nb) total += pv[b / 4][b % 4];
+    }
+  }
+  const int eo = DRP_E * (int)blockIdx.x + se;
+  if (st < NT && st < n && eo < E) logits[(size_t)st * E + eo] = bias ? total + bias[eo] : total;
+}
+
 __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ v, int64_t n_values,
                                                        int8_t* __restrict__ q,
                                                        uint16_t* __restrict__ scales) {
@@ -571,17 +676,25 @@ hipError_t launch_decode_router(const float* x, int n, int d, int d_pad, const f
                                 const float* sh_gate_vec, float* gs, int8_t* dxq, uint16_t* dxs,
                                 hipStream_t s) {
   if (n < 1 || n > DECODE_MAX_TOKENS) return hipErrorInvalidValue;
-  const int n_rwg = (E + DR_E - 1) / DR_E;
-#define DR_LAUNCH(NT)                                                                             \
-  case NT:                                                                                         \
-    decode_router_kernel<NT><<<n_rwg + n, 256, 0, s>>>(x, n, d, d_pad, wt, bias, E, E64, n_rwg, logits, \
-                                                       sh_gate_vec, gs, dxq, dxs);                 \
+  // 1-2 tokens: lanes read their own token values (more workgroups stream the
+  // matrix); 3-8: the DPP form (one LDS read per 16 steps)
+  const int n_rwg = (E + DR_E - 1) / DR_E, n_rwg_dpp = (E + DRP_E - 1) / DRP_E;
+#define DR_LAUNCH(NT)                                                                                  \
+  case NT:                                                                                              \
+    decode_router_kernel<NT><<<n_rwg + n, 256, 0, s>>>(x, n, d, d_pad, wt, bias, E, E64, n_rwg, logits,      \
+                                                       sh_gate_vec, gs, dxq, dxs);                      \
+    break;
+#define DRP_LAUNCH(NT)                                                                                 \
+  case NT:                                                                                              \
+    decode_router_dpp_kernel<NT><<<n_rwg_dpp + n, 512, 0, s>>>(x, n, d, d_pad, wt, bias, E, E64, n_rwg_dpp,  \
+                                                               logits, sh_gate_vec, gs, dxq, dxs);      \
     break;
   static_assert(DECODE_MAX_TOKENS == 8, "one instantiation per batch size");
   switch (n) {
-    DR_LAUNCH(1) DR_LAUNCH(2) DR_LAUNCH(3) DR_LAUNCH(4) DR_LAUNCH(5) DR_LAUNCH(6) DR_LAUNCH(7) DR_LAUNCH(8)
+    DR_LAUNCH(1) DR_LAUNCH(2) DRP_LAUNCH(3) DRP_LAUNCH(4) DRP_LAUNCH(5) DRP_LAUNCH(6) DRP_LAUNCH(7) DRP_LAUNCH(8)
   }
 #undef DR_LAUNCH
+#undef DRP_LAUNCH
   return hipGetLastError();
 }
 
