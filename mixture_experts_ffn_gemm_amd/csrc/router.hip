@@ -207,10 +207,11 @@ __device__ __forceinline__ void route_tile(RouteLds& R, int tile, int t0, int nt
 // no logits in global memory and no separate routing launch.
 // WB: weight buffers per wavefront.  2: round r+2's weights are requested
 // during round r (one workgroup per CU); 1: round r+1's after round r is
-// computed, at most 128 VGPRs, so that two workgroups share a CU and each
-// hides the other's waits (grids with more workgroups than CUs).
+// computed, at most 128 VGPRs (four wavefronts per SIMD), so that two
+// workgroups share a CU and each hides the other's waits (grids with more
+// workgroups than CUs).
 template <bool FUSE, int WB>
-__global__ __launch_bounds__(512, 3 - WB) void router_kernel(
+__global__ __launch_bounds__(512, 6 - 2 * WB) void router_kernel(
     const float* __restrict__ x, int n, int d, const float* __restrict__ wt,
     const float* __restrict__ bias, int E, int E64, float* __restrict__ logits, int k, int norm,
     int32_t* __restrict__ ids, float* __restrict__ wout, int32_t* __restrict__ rank,
@@ -261,15 +262,26 @@ __global__ __launch_bounds__(512, 3 - WB) void router_kernel(
     if (b < NB) {  // wavefront-uniform
       const bool full = d - RB * b >= RB;  // else 32 j (d % 32 == 0): sub-chunks 0 and 1
       const float* xb = &xs[bi][0][RB * wave] + (lane & 15);
+      // WB == 2: every token value of the block requested before the first FMA
+      // (one LDS latency per round, not one per 16-step piece; past a half
+      // block the reads are stale and unused).  WB == 1 (128 VGPRs): per pair.
+      constexpr int XR = WB == 2 ? ROUTE_TILE : 2;
+      float xr[XR][4];
+      auto fetch = [&](int t0x, int nt) {
+#pragma unroll
+        for (int t = 0; t < nt; ++t)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) xr[(t0x + t) % XR][s] = xb[(t0x + t) * RJR + 16 * s];
+      };
+      if constexpr (WB == 2) fetch(0, ROUTE_TILE);
 #pragma unroll
       for (int tp = 0; tp < ROUTE_TILE / 2; ++tp) {
-        const float* x0 = xb + (2 * tp) * RJR;
-        const float* x1 = x0 + RJR;
+        if constexpr (WB == 1) fetch(2 * tp, 2);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
           if (s < 2 || full)
-            router_fma16_2(acc[2 * tp], acc[2 * tp + 1], x0[16 * s], x1[16 * s], w[4 * s], w[4 * s + 1],
-                           w[4 * s + 2], w[4 * s + 3]);
+            router_fma16_2(acc[2 * tp], acc[2 * tp + 1], xr[(2 * tp) % XR][s], xr[(2 * tp + 1) % XR][s], w[4 * s],
+                           w[4 * s + 1], w[4 * s + 2], w[4 * s + 3]);
       }
     }
 #pragma unroll
