@@ -96,6 +96,7 @@ struct Lay {
 };
 static_assert(NWAVE * 32 * EPI_STRIDE * 4 <= Lay<true>::STAGE, "epilogue scratch must fit in one buffer");
 static_assert(2 * 2 * Lay<false>::STAGE <= 160 * 1024, "two workgroups per CU must fit in the LDS");
+static_assert(NWAVE * 32 * DN_EPI_STRIDE * 4 <= 2 * Lay<false>::STAGE, "the down epilogue's transpose must fit in the stage buffers");
 
 // This wavefront's copies of k-step j into the buffer at LDS address L, in
 // two halves issued at different points of the k loop, so that the copies of
@@ -585,15 +586,15 @@ __device__ __forceinline__ void tile_work(const GemmArgs& a, char (&lds)[2][Lay<
       if (j + 2 < KS) issue_weights<GATEUP>(src, j + 2, (j & 1) ? lds1 : lds0, wave);
     }
   }
-  // gate/up: every wavefront is out of the k loop, so LDS is free for the
-  // epilogue (the down epilogue uses no LDS).  Split-K: the row group's
-  // partial sums meet in its first wavefront, which alone runs the epilogue.
+  // Every wavefront is out of the k loop, so LDS is free for the epilogue
+  // (both epilogues transpose through it).  Split-K: the row group's partial
+  // sums meet in its first wavefront, which alone runs the epilogue.
   if constexpr (S > 1)
     split_reduce(&lds[0][0], S, rg, si, lane, acc);
-  else if (GATEUP)
+  else
     __syncthreads();
   if (!active || si != 0) return;
-  epilogue<GATEUP>(a, &lds[0][0], lane, wave, t32, cs, g, wrow0, row_end, tok, slt, acc);
+  epilogue<GATEUP, true>(a, &lds[0][0], lane, wave, t32, cs, g, wrow0, row_end, tok, slt, acc);
 }
 
 // The work of a (tile, strip) workgroup whose tile has one 32-row group: the
@@ -651,7 +652,7 @@ __device__ __forceinline__ void tile_work1(const GemmArgs& a, char* lds, int lan
   }
   split_reduce(lds, 4, 0, si, lane, acc);
   if (si != 0) return;
-  epilogue<GATEUP>(a, lds, lane, 0, t32, cs, g, row0, row_end, tok, slt, acc);
+  epilogue<GATEUP, true>(a, lds, lane, 0, t32, cs, g, row0, row_end, tok, slt, acc);
 }
 
 template <bool GATEUP>

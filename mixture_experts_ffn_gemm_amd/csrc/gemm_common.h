@@ -149,6 +149,37 @@ __device__ __forceinline__ void epilogue_down(const GemmArgs& a, int lane, int c
   }
 }
 
+// The down epilogue through LDS: the wavefront's 32 x 128 outputs (scaled by
+// 2^eg) transposed through its own [32][DN_EPI_STRIDE]-float area of the
+// then idle stage buffers, so that each store writes two whole 512-byte rows
+// of partials (16 stores per wavefront instead of 64 of 2 x 128 bytes).
+// Every wavefront of the workgroup must be out of the k loop.  Rows 4 apart
+// (the two lane halves of one accumulator register) start 32 banks apart.
+constexpr int DN_EPI_STRIDE = 136;
+__device__ __forceinline__ void epilogue_down_lds(const GemmArgs& a, char* lds, int lane, int wave, int cs, int g,
+                                                  int ri, v16f (&acc)[4]) {
+  const int eg = __builtin_amdgcn_readfirstlane(a.dn_exp[g]);
+  float* el = reinterpret_cast<float*>(lds) + wave * (32 * DN_EPI_STRIDE);
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      el[out_row(v, lane) * DN_EPI_STRIDE + tt * 32 + (lane & 31)] = ldexpf(acc[tt][v], eg);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  const int c4 = lane & 31, col = cs * DN_COLS + 4 * c4;
+  const bool colok = col < a.d;  // d % 32 == 0: four columns are all inside or all padding
+  int rr[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) rr[i] = __shfl(ri, 2 * i + (lane >> 5), 64);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = 2 * i + (lane >> 5);
+    const float4 v = *reinterpret_cast<const float4*>(el + row * DN_EPI_STRIDE + 4 * c4);
+    if (rr[i] >= 0 && colok) *reinterpret_cast<float4*>(a.partial + (size_t)rr[i] * a.d + col) = v;
+  }
+}
+
 // Grouped GEMM.  GATEUP: A = the int8 token rows of the tile's (token, slot)
 // pairs, which the quantiser wrote in chunk form at their padded rows; B = the
 // [gate;up] strip of 64 SwiGLU columns; epilogue h = silu(gate) * up,
@@ -159,7 +190,9 @@ __device__ __forceinline__ void epilogue_down(const GemmArgs& a, int lane, int c
 // The epilogue of one wavefront's 32 rows (CSR rows wrow0.., 32-row tile
 // t32) against strip cs of group g; tok / slt are this lane's (token, slot)
 // for down.  Gate/up uses this wavefront's area at the start of the LDS.
-template <bool GATEUP>
+// DN_LDS: the down epilogue through LDS (epilogue_down_lds; the caller's LDS
+// must hold NWAVE x 32 x DN_EPI_STRIDE floats), else direct scattered stores.
+template <bool GATEUP, bool DN_LDS = false>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, char* lds, int lane, int wave, int t32, int cs, int g,
                                          int wrow0, int row_end, int tok, int slt, v16f (&acc)[4]) {
   if constexpr (GATEUP) {
@@ -215,6 +248,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, char* lds, int lane,
     *reinterpret_cast<uint4*>(line + (((p0 + 1) ^ (r & 7)) << 4)) =
         make_uint4(packed[4], packed[5], packed[6], packed[7]);
     a.hs[(((size_t)t32 * (a.kbmax / KSTEP) + (kbf >> 2)) * 32 + r) * KSTEP + (kbf & 3)] = s16;
+  } else if constexpr (DN_LDS) {
+    epilogue_down_lds(a, lds, lane, wave, cs, g, partial_row(a, lane, wrow0, row_end, tok, slt), acc);
   } else {
     epilogue_down(a, lane, cs, g, partial_row(a, lane, wrow0, row_end, tok, slt), acc);
   }
