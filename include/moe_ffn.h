@@ -304,7 +304,9 @@ int moe_ffn_decode(const moe_ffn_weights* w, const float* x, int32_t n_tokens, f
  * caller-created hipEvent_t handles; event i is recorded on `stream` before
  * decode stage i and the last one after the final stage: 0 router logits +
  * activation quantiser, 1 routing + gathered gate/up matvec + SwiGLU, 2
- * gathered down matvec, 3 combine.  Same arguments and results as
+ * gathered down matvec, 3 combine (for one token with at most 9 slots, k
+ * plus the shared expert, stage 2 runs the down matvec and the combine in
+ * one launch and stage 3 is empty).  Same arguments and results as
  * moe_ffn_decode otherwise. */
 #define MOE_FFN_N_DECODE_STAGE_EVENTS 5
 int moe_ffn_decode_profiled(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* out,
