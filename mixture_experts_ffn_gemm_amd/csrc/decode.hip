@@ -165,6 +165,7 @@ struct DecRoute {
   int sel[DECODE_MAX_TOKENS][MAX_TOPK];
   float selv[DECODE_MAX_TOKENS][MAX_TOPK];
   int wtot[4];
+  __attribute__((aligned(16))) unsigned long long kl[DECODE_MAX_TOKENS][64];  // E <= 64: each token's keys, for wave_key_rank
 };
 // The active groups in list order (routed experts ascending, then the shared
 // expert): group id, row count and the rows' (token, slot) pairs.
@@ -216,20 +217,30 @@ __device__ __forceinline__ int decode_route(const DecodeArgs& a, DecRoute& R, Gr
       kv[m] = e < E ? topk_key(lv[m], e) : 0ull;  // every real key is > 0
       R.slot[wave][e] = 0xff;
     }
-    for (int s = 0; s < k; ++s) {
-      unsigned long long b = kv[0];
+    if (E <= 64) {
+      // one key per lane: its rank is its slot (keys are distinct)
+      const int rk = wave_key_rank(kv[0], R.kl[wave], lane);
+      if (lane < E && rk < k) {
+        R.slot[wave][lane] = (uint8_t)rk;
+        R.selv[wave][rk] = lv[0];
+        R.sel[wave][rk] = lane;
+      }
+    } else {
+      for (int s = 0; s < k; ++s) {
+        unsigned long long b = kv[0];
 #pragma unroll
-      for (int m = 1; m < 4; ++m) b = kv[m] > b ? kv[m] : b;
-      const unsigned long long mx = wave_max_key(b);
-      const uint32_t ml = (uint32_t)mx;
+        for (int m = 1; m < 4; ++m) b = kv[m] > b ? kv[m] : b;
+        const unsigned long long mx = wave_max_key(b);
+        const uint32_t ml = (uint32_t)mx;
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
-        if (kv[m] == mx) {  // keys are distinct: one lane, one m
-          R.slot[wave][lane + 64 * m] = (uint8_t)s;
-          R.selv[wave][s] = lv[m];
-          kv[m] = 0ull;
-        }
-      if (lane == 0) R.sel[wave][s] = (int)~ml;
+        for (int m = 0; m < 4; ++m)
+          if (kv[m] == mx) {  // keys are distinct: one lane, one m
+            R.slot[wave][lane + 64 * m] = (uint8_t)s;
+            R.selv[wave][s] = lv[m];
+            kv[m] = 0ull;
+          }
+        if (lane == 0) R.sel[wave][s] = (int)~ml;
+      }
     }
     if (wg0) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

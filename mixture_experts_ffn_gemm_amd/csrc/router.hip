@@ -90,6 +90,8 @@ __device__ __forceinline__ float wave_sum_rows(float v) {
 // keys of experts g + 64c, and slot r takes the largest key left after r
 // rounds of a wavefront maximum, its owner clearing it.  The maximum is
 // uniform, so lane r keeps slot r's expert and logit (decoded from the key).
+// With one key per lane (E <= 64) a single pass ranks every key instead
+// (wave_key_rank): the rank of a key is its slot.
 // Then softmax over all E, optional renormalisation, and, for the bucketing
 // kernel, the per-expert rank of each (token, slot) pair among the tile's
 // pairs in (token, slot) order and the tile's histogram.  A token's k experts
@@ -99,6 +101,9 @@ __device__ __forceinline__ float wave_sum_rows(float v) {
 struct RouteLds {
   float l[ROUTE_TILE][MAX_EXPERTS];
   unsigned long long pick[ROUTE_TILE][MAX_EXPERTS / 64];  // bit g of [t][c]: token t picked expert g + 64c
+  __attribute__((aligned(16))) unsigned long long kl[ROUTE_TILE][64];  // E <= 64: each token's keys (wave_key_rank)
+  int sel_id[ROUTE_TILE][MAX_TOPK];                       // E <= 64: slot s's expert and logit
+  float sel_v[ROUTE_TILE][MAX_TOPK];
 };
 
 // The logit a key was made from (-0 comes back as +0).
@@ -125,20 +130,38 @@ __device__ __forceinline__ void route_tile(RouteLds& R, int tile, int t0, int nt
     }
     int my_id = 0;
     float my_val = 0.0f;
-    for (int r = 0; r < k; ++r) {
-      unsigned long long m = 0ull;
-#pragma unroll
-      for (int c = 0; c < NKEY; ++c) m = key[c] > m ? key[c] : m;
-      m = wave_max_key(m);
-#pragma unroll
-      for (int c = 0; c < NKEY; ++c) {
-        const bool hit = key[c] == m;
-        slot[c] = hit ? r : slot[c];
-        key[c] = hit ? 0ull : key[c];
+    if constexpr (NKEY == 1) {
+      // one key per lane: its rank is its slot (keys are distinct); slot r's
+      // expert and logit reach lane r through LDS
+      const int rk = wave_key_rank(key[0], R.kl[tl], g);
+      if (g < E && rk < k) {
+        slot[0] = rk;
+        R.sel_id[tl][rk] = g;
+        R.sel_v[tl][rk] = key_logit(key[0]);
       }
-      if (g == r) {
-        my_id = (int)~(uint32_t)m;
-        my_val = key_logit(m);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (g < k) {
+        my_id = R.sel_id[tl][g];
+        my_val = R.sel_v[tl][g];
+      }
+    } else {
+      for (int r = 0; r < k; ++r) {
+        unsigned long long m = 0ull;
+#pragma unroll
+        for (int c = 0; c < NKEY; ++c) m = key[c] > m ? key[c] : m;
+        m = wave_max_key(m);
+#pragma unroll
+        for (int c = 0; c < NKEY; ++c) {
+          const bool hit = key[c] == m;
+          slot[c] = hit ? r : slot[c];
+          key[c] = hit ? 0ull : key[c];
+        }
+        if (g == r) {
+          my_id = (int)~(uint32_t)m;
+          my_val = key_logit(m);
+        }
       }
     }
     // softmax over all E, weights of the k slots (lane s: slot s)
