@@ -106,7 +106,7 @@ def stage_bytes(shape, n_tokens, counts, fmt="q8_0"):
 KERNEL_SOURCES = {
     "grouped_gemm": ("gemm.hip", "gemm_common.h", "internal.h", "device_util.h"),
     "grouped_gemm_q4k": ("gemm_q4k.hip", "gemm_common.h", "internal.h", "device_util.h"),
-    "decode_gemv": ("decode.hip", "internal.h", "device_util.h"),
+    "decode_gemv": ("decode.hip", "internal.h", "device_util.h", "route_util.h"),
 }
 
 

@@ -35,6 +35,7 @@
 #include <algorithm>
 
 #include "device_util.h"
+#include "route_util.h"
 #include "internal.h"
 
 namespace moe {

@@ -9,6 +9,7 @@
 #include <hip/hip_fp16.h>
 
 #include "device_util.h"
+#include "route_util.h"
 #include "internal.h"
 
 namespace moe {
