@@ -556,10 +556,12 @@ __global__ __launch_bounds__(DW * 64) void decode_down_combine_kernel(DecodeArgs
     g = (g >= 0 && g <= E) ? g : 0;
     s_g[tid] = g;
     s_ks[tid] = ((g == E) ? a.Fs_pad : a.F_pad) / (KSTEP * QB);
-    s_ex[tid] = a.dn_exp[g];
     s_w[tid] = tid < k ? a.w[tid] : gs[0];
   }
   __syncthreads();
+  // the slots' scale exponents are needed only at the end: requested after
+  // the first pass's pieces, so that no round trip precedes the weights
+  int exv = 0;
   const int KSM = a.kmax_pad / (KSTEP * QB);
   const int strip = blockIdx.x >> 2, tsel = blockIdx.x & 3;
   const uint32_t o_code = (uint32_t)lane * 16, o_scale = (uint32_t)(lane & 31) * 8;
@@ -606,6 +608,7 @@ __global__ __launch_bounds__(DW * 64) void decode_down_combine_kernel(DecodeArgs
       for (int h = 0; h < 2; ++h)
         p[i].s[h] = __builtin_amdgcn_raw_buffer_load_b64(rs, o_scale, step_off + 16 * 1024 + tsel * 512 + h * 256, 0);
     }
+    if (ks0 == 0 && tid < kk) exv = a.dn_exp[s_g[tid]];
     __builtin_amdgcn_sched_barrier(0);  // every request is out before any wait
     lds_barrier();  // every wavefront is done with the previous pass's LDS
 #pragma unroll
@@ -627,6 +630,7 @@ __global__ __launch_bounds__(DW * 64) void decode_down_combine_kernel(DecodeArgs
     const float v = acc[i] + __shfl_xor(acc[i], 32, 64);
     if (i < kk && lane < 32) red[wave][i][lane] = v;
   }
+  if (tid < kk) s_ex[tid] = exv;
   __syncthreads();
   const int row0 = 32 * (int)blockIdx.x;
   if (tid < DC_SB * 32) {
