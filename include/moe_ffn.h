@@ -53,7 +53,9 @@
  *   - Supported shapes: d, ffn, shared_ffn multiples of 32 (internally
  *     zero-padded to multiples of 128); 1 <= n_experts <= 256;
  *     1 <= top_k <= min(n_experts, 16); 0 <= n_tokens <= the max_tokens the
- *     workspace was sized for.  n_tokens == 0 is a no-op.
+ *     workspace was sized for, and n_tokens * padded d below 2^32 (the
+ *     activation codes of one call are addressed by 32-bit offsets); other
+ *     counts are MOE_FFN_INVALID_ARG.  n_tokens == 0 is a no-op.
  */
 #ifndef MOE_FFN_H
 #define MOE_FFN_H
@@ -245,8 +247,8 @@ int moe_ffn_prefill_residual(const moe_ffn_weights* w, const float* x, int32_t n
  * A batch whose workspace (moe_ffn_workspace_size(n_tokens)) exceeds the
  * array returns MOE_FFN_SCRATCH_TOO_SMALL before anything is enqueued: at
  * the OLMoE-shaped layer (d 2048, 64 experts, top-8, ffn 1024) that is above
- * 1527 tokens, at the 35B-A3B-shaped layer (256 experts, top-8, ffn 512 +
- * shared 512) above 791.  x, out, routing and stream are those of
+ * 2026 tokens, at the 35B-A3B-shaped layer (256 experts, top-8, ffn 512 +
+ * shared 512) above 1749.  x, out, routing and stream are those of
  * moe_ffn_prefill. */
 #define MOE_FFN_STATIC_SCRATCH_BYTES (160u << 20)
 int moe_ffn_prefill_static(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* out,

@@ -51,12 +51,12 @@ WsLayout ws_layout(const Dims& dm, int max_tokens) {
   L.exp_start = take((size_t)(dm.E + 2) * 4);
   L.tok_i = take(P_total * 4);
   L.tok_k = take(P_total * 4);
-  L.pos = take(Nn * kk * 4);
+  L.row_tok = take((size_t)L.tile_bound * MT_WG * 4);
   L.tiles = take((4 + 3 * (size_t)L.tile_bound) * 4);
   const size_t t32 = (size_t)L.tile_bound * (MT_WG / MT_WAVE);
   const size_t kbd = (size_t)dm.d_pad / QB;
-  L.gq = take(t32 * kbd * 1024);
-  L.gqs = take(t32 * 32 * kbd * 2);
+  L.gq = take(Nn * dm.d_pad);        // token-major codes
+  L.gqs = take(t32 * 32 * kbd * 2);  // their scales per tile row
   L.hq = take(t32 * kbmax * 1024);
   L.hs = take(t32 * 32 * kbmax * 2);
   L.partial = take(Nn * kk * dm.d * 4);
@@ -158,6 +158,7 @@ GemmArgs gemm_args(const moe_ffn_weights* W, const WsLayout& L, char* base, int 
   a.tiles = (const int32_t*)(base + L.tiles);
   a.tok_i = (const int32_t*)(base + L.tok_i);
   a.tok_k = (const int32_t*)(base + L.tok_k);
+  a.row_tok = (const int32_t*)(base + L.row_tok);
   a.E = dm.E;
   a.G = dm.G;
   a.n_tokens = n;
@@ -197,6 +198,8 @@ int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, v
               size_t ws_bytes, const moe_ffn_routing* r, hipStream_t s, hipEvent_t* ev = nullptr,
               const ResidualOut* res = nullptr, int reverse_tiles = 0) {
   if (!W || n < 0 || n > MAX_TOKENS) return MOE_FFN_INVALID_ARG;
+  // gate/up addresses its token-major activation codes by 32-bit offsets
+  if ((uint64_t)n * (uint64_t)W->dm.d_pad > 0xffffff00ull) return MOE_FFN_INVALID_ARG;
   if (n == 0) return current_device_matches(W);  // no-op; buffers may be NULL
   if (!x || !ws || (!res && !out)) return MOE_FFN_INVALID_ARG;
   const Dims& dm = W->dm;
@@ -230,7 +233,6 @@ int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, v
   int32_t* exp_start = (int32_t*)(base + L.exp_start);
   int32_t* tok_i = (int32_t*)(base + L.tok_i);
   int32_t* tok_k = (int32_t*)(base + L.tok_k);
-  int32_t* pos = (int32_t*)(base + L.pos);
   int32_t* tiles = (int32_t*)(base + L.tiles);
   int8_t* gq = (int8_t*)(base + L.gq);
   uint16_t* gqs = (uint16_t*)(base + L.gqs);
@@ -251,7 +253,8 @@ int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, v
     HIP_TRY(launch_route(logits, n, dm.E, dm.k, dm.norm, ids, w, rank, hist, s));
   }
   HIP_TRY(mark(2));
-  HIP_TRY(launch_bucket_quantize(ids, rank, hist, n, dm.E, dm.k, dm.has_shared, exp_start, tok_i, tok_k, pos,
+  HIP_TRY(launch_bucket_quantize(ids, rank, hist, n, dm.E, dm.k, dm.has_shared, exp_start, tok_i, tok_k,
+                                 (int32_t*)(base + L.row_tok),
                                  tiles, L.tile_bound, x, dm.d, dm.d_pad, gq, gqs,
                                  dm.has_shared ? W->sh_gate_vec : nullptr, gs, r ? r->xq : nullptr,
                                  r ? r->xs : nullptr, s));

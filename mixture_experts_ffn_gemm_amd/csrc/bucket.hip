@@ -9,26 +9,24 @@
 //     expStart[e] + (pairs of e in earlier tiles) + rank,
 // which keeps every expert's rows in (token, slot) order -- a stable counting
 // sort with no atomics, so the result is deterministic.  Each group's rows are
-// cut into 128-row GEMM tiles; a pair's padded row (its group's first tile *
-// 128 + its index within the group) is written per (token, slot), so the
-// quantiser can place the token's codes where the GEMM's tile reads them.
-// Workgroup 0 also writes expStart and the tile table that drives the grouped
-// GEMMs.
+// cut into 128-row GEMM tiles, and each pair's token is also written at its
+// tile row (first tile of its group * 128 + its index within the group), so
+// that a GEMM workgroup finds its rows' tokens at an address given by its
+// tile alone.  Workgroup 0 also writes expStart and the tile table that
+// drives the grouped GEMMs.
 //
-// The same workgroup then quantises its tile's token rows and scatters the
-// codes to the rows it has just computed (one launch for both stages: the
-// rows' loads are issued before the histograms are read, so their latency
-// hides under the bucketing).  One wavefront per token: lane pairs quantise
-// 32-blocks (each lane 16 values), and each block's codes and scale are
-// written once per expert slot of the token, straight into the GEMM operand
-// layout at the slot's padded row (t32 = row / 32, r = row % 32): one 4 KiB
-// slab per (t32, k-step) holding [32 rows][128 B], piece p (16 codes: block
-// p/2 of the k-step, half p%2) of row r at 16 * (p ^ (r % 8)), and the scales
-// at [t32][k-step][r][block].  The 8 lanes of one k-step therefore write one
-// whole 128-byte line per slot.  The K-padding blocks past d get zero codes
-// and scales.  With a shared expert the wavefront also computes the gate
-// sigmoid(x . g) (a fixed-order reduction).  Optionally the token-major codes
-// and scales are written out.
+// The same workgroup then quantises its tile's token rows (one launch for
+// both stages: the rows' loads are issued before the histograms are read, so
+// their latency hides under the bucketing).  One wavefront per token: lane
+// pairs quantise 32-blocks (each lane 16 values).  Each block's codes are
+// written once, token-major (gq[token][d_pad]), and the gate/up GEMM gathers
+// its tiles' rows from there; each block's scale is written once per expert
+// slot of the token, in the GEMM's scale layout at the slot's tile row
+// (t32 = row / 32, r = row % 32): gqs[t32][k-step][r][block].  The K-padding
+// blocks past d get zero codes and scales.  With a shared expert
+// the wavefront also computes the gate sigmoid(x . g) (a fixed-order
+// reduction).  Optionally the token-major codes and scales of the unpadded
+// width d are written out as well.
 #include "device_util.h"
 #include "internal.h"
 
@@ -82,7 +80,7 @@ __global__ __launch_bounds__(BQ_THREADS) __attribute__((amdgpu_waves_per_eu(4, 8
     const int32_t* __restrict__ ids, const int32_t* __restrict__ rank,
     const int32_t* __restrict__ hist, int n, int E, int k, int has_shared, int n_tiles,
     int32_t* __restrict__ exp_start, int32_t* __restrict__ tok_i, int32_t* __restrict__ tok_k,
-    int32_t* __restrict__ pos_out, int32_t* __restrict__ tiles, int tile_bound, QuantArgs qa) {
+    int32_t* __restrict__ row_tok, int32_t* __restrict__ tiles, int tile_bound, QuantArgs qa) {
   __shared__ int s_start[2 * 256 + 2];
   __shared__ int s_pre[MAX_EXPERTS];
   __shared__ int s_cnt[MAX_EXPERTS + 1];
@@ -162,6 +160,9 @@ __global__ __launch_bounds__(BQ_THREADS) __attribute__((amdgpu_waves_per_eu(4, 8
   else if (threadIdx.x < 128) wave_exclusive_scan_512(s_nt, G, threadIdx.x - 64);
   __syncthreads();
 
+  // Each pair's CSR row, and its token at its tile row: row i of tile T
+  // (T * 128 + i) is CSR row (first row of T) + i, so a pair at index `local`
+  // within group e sits at tile row (first tile of e) * 128 + local.
   const int pad_rows = tile_bound * MT_WG;
   for (int q = threadIdx.x; q < nt * k; q += BQ_THREADS) {
     const int t = t0 + q / k, s = q % k;
@@ -173,18 +174,16 @@ __global__ __launch_bounds__(BQ_THREADS) __attribute__((amdgpu_waves_per_eu(4, 8
       tok_k[pos] = s;
     }
     const int prow = s_nt[e] * MT_WG + local;
-    const int pv = prow < pad_rows ? prow : -1;
-    pos_out[(size_t)t * kk + s] = pv;
-    s_pos[q / k][s] = pv;
+    if (prow < pad_rows) row_tok[prow] = t;
+    s_pos[q / k][s] = prow < pad_rows ? prow : -1;
   }
   if (has_shared)
     for (int q = threadIdx.x; q < nt; q += BQ_THREADS) {
       tok_i[P + t0 + q] = t0 + q;
       tok_k[P + t0 + q] = k;
       const int prow = s_nt[E] * MT_WG + t0 + q;
-      const int pv = prow < pad_rows ? prow : -1;
-      pos_out[(size_t)(t0 + q) * kk + k] = pv;
-      s_pos[q][k] = pv;
+      if (prow < pad_rows) row_tok[prow] = t0 + q;
+      s_pos[q][k] = prow < pad_rows ? prow : -1;
     }
 
   if (tile == 0) {
@@ -211,12 +210,12 @@ __global__ __launch_bounds__(BQ_THREADS) __attribute__((amdgpu_waves_per_eu(4, 8
   }
   __syncthreads();  // the tile's padded rows are in s_pos
 
-  // Quantise and scatter: wavefront w takes token t0 + w.
+  // Quantise: wavefront w takes token t0 + w.
   if (wave >= nt) return;
   const int t = t0 + wave;
   float gacc = 0.0f;
   // Each pass covers 8 k-steps; the pass after next is requested before this
-  // pass is quantised and scattered.
+  // pass is quantised and stored.
   for (int j0 = 0; j0 < KS; j0 += 8) {
     f4v nn[4] = {};
     if (j0 + 16 < KS) load(j0 + 16, nn);
@@ -235,17 +234,19 @@ __global__ __launch_bounds__(BQ_THREADS) __attribute__((amdgpu_waves_per_eu(4, 8
     uint32_t pk[4];
     uint16_t s16;
     quant_half_block16(v, pk, s16);  // lanes 2i, 2i+1 share a block; all take part
+    // the k-step's 4 scales (held by lanes 0, 2, 4, 6 of its 8) in every lane
+    const int g8 = lane & ~7;
+    const uint32_t sb0 = (uint32_t)__shfl((int)s16, g8, 64), sb1 = (uint32_t)__shfl((int)s16, g8 + 2, 64);
+    const uint32_t sb2 = (uint32_t)__shfl((int)s16, g8 + 4, 64), sb3 = (uint32_t)__shfl((int)s16, g8 + 6, 64);
     if (j < KS) {
       const uint4 codes = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-#pragma unroll
-      for (int s2 = 0; s2 < MAX_TOPK + 1; ++s2) {
-        const int row = (s2 < kk) ? s_pos[wave][s2] : -1;  // read from LDS per store: no 17 live registers
-        if (row >= 0) {
-          const int t32 = row >> 5, r = row & 31;
-          const size_t slab = (size_t)t32 * KS + j;
-          *reinterpret_cast<uint4*>(qa.gq + (slab * 32 + r) * 128 + ((p ^ (r & 7)) << 4)) = codes;
-          if (half == 0) qa.gqs[(slab * 32 + r) * KSTEP + (p >> 1)] = s16;
-        }
+      *reinterpret_cast<uint4*>(qa.gq + (size_t)t * qa.d_pad + c0) = codes;
+      // one 8-byte store per expert slot: lane p of the k-step takes slots p and p + 8
+      const uint2 sc4 = make_uint2(sb0 | (sb1 << 16), sb2 | (sb3 << 16));
+      for (int s2 = p; s2 < kk; s2 += 8) {
+        const int row = s_pos[wave][s2];
+        if (row >= 0)
+          *reinterpret_cast<uint2*>(qa.gqs + (((size_t)(row >> 5) * KS + j) * 32 + (row & 31)) * KSTEP) = sc4;
       }
       if (qa.xq_out && valid) *reinterpret_cast<uint4*>(qa.xq_out + (size_t)t * qa.d + c0) = codes;
       if (qa.xs_out && half == 0 && valid) qa.xs_out[(size_t)t * (qa.d / QB) + kb] = s16;
@@ -271,14 +272,14 @@ __global__ __launch_bounds__(BQ_THREADS) __attribute__((amdgpu_waves_per_eu(4, 8
 
 hipError_t launch_bucket_quantize(const int32_t* ids, const int32_t* rank, const int32_t* hist, int n,
                                   int E, int k, int has_shared, int32_t* exp_start, int32_t* tok_i,
-                                  int32_t* tok_k, int32_t* pos, int32_t* tiles, int tile_bound,
+                                  int32_t* tok_k, int32_t* row_tok, int32_t* tiles, int tile_bound,
                                   const float* x, int d, int d_pad, int8_t* gq, uint16_t* gqs,
                                   const float* sh_gate_vec, float* gs, int8_t* xq_out, uint16_t* xs_out,
                                   hipStream_t s) {
   const int n_tiles = (n + ROUTE_TILE - 1) / ROUTE_TILE;
   const QuantArgs qa{x, d, d_pad, gq, gqs, sh_gate_vec, gs, xq_out, xs_out};
   bucket_quantize_kernel<<<n_tiles, BQ_THREADS, 0, s>>>(ids, rank, hist, n, E, k, has_shared, n_tiles, exp_start,
-                                                        tok_i, tok_k, pos, tiles, tile_bound, qa);
+                                                        tok_i, tok_k, row_tok, tiles, tile_bound, qa);
   return hipGetLastError();
 }
 

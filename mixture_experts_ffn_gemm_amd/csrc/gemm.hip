@@ -47,10 +47,12 @@
 //   pieces of row r XOR-swizzled by r%8 so that the MFMA operand reads are
 //   free of LDS bank conflicts) and their scales (256 B), with direct
 //   global->LDS copies into one of two LDS buffers.  Every copy reads whole
-//   cache lines: the quantiser and the gate/up epilogue store the activations
-//   already in slab form (a gather of 32 scattered rows per copy would hold
-//   one vector-L1 miss slot per row and stall the copies behind the L1's miss
-//   limit).  Every wavefront issues
+//   cache lines: gate/up gathers its rows from the token-major codes, each
+//   copy covering 8 rows' 128-byte k-step pieces (a copy of 32 rows' 32-byte
+//   blocks would hold one vector-L1 miss slot per row), and reads their
+//   scales, which the quantiser stores per expert slot, in slab form; down
+//   reads h and its scales, which the gate/up epilogue stores in slab form.
+//   Every wavefront issues
 //   exactly Lay::DMA copies per k-step, in two halves (weights right after
 //   the barrier, activations one block later) so that the copies of all
 //   wavefronts never queue at once.  The copies are inline assembly, so the
@@ -120,11 +122,10 @@ __device__ __forceinline__ void issue_weights(const Src& s, int j, uint32_t L, i
 }
 template <bool GATEUP>
 __device__ __forceinline__ void issue_acts(const Src& s, int j, uint32_t L, int wave, int lane) {
-  const int8_t* a = s.a + (size_t)j * KSTEP * 1024;
 #pragma unroll
   for (int i = 0; i < KSTEP; ++i)
-    dma16(a + i * 1024, lane * 16, L + Lay<GATEUP>::A_OFF + (wave * KSTEP + i) * 1024);
-  dma4(s.as + (size_t)j * 32 * KSTEP, lane * 4, L + Lay<GATEUP>::AS_OFF + wave * 256);
+    dma_act_chunk<GATEUP>(s, j, i, lane, L + Lay<GATEUP>::A_OFF + (wave * KSTEP + i) * 1024);
+  dma_act_scales<GATEUP>(s, j, lane, L + Lay<GATEUP>::AS_OFF + wave * 256);
 }
 
 // The same copies issued in parts, one part per tile of a block (the hook
@@ -152,13 +153,12 @@ __device__ __forceinline__ void issue_weights_part(const Src& s, int j, uint32_t
 }
 template <bool GATEUP>
 __device__ __forceinline__ void issue_acts_part(const Src& s, int j, uint32_t L, int wave, int lane, int p) {
-  const int8_t* a = s.a + (size_t)j * KSTEP * 1024;
   if (p < 2) {
 #pragma unroll
     for (int i = 2 * p; i < 2 * p + 2; ++i)
-      dma16(a + i * 1024, lane * 16, L + Lay<GATEUP>::A_OFF + (wave * KSTEP + i) * 1024);
+      dma_act_chunk<GATEUP>(s, j, i, lane, L + Lay<GATEUP>::A_OFF + (wave * KSTEP + i) * 1024);
   } else if (p == 2) {
-    dma4(s.as + (size_t)j * 32 * KSTEP, lane * 4, L + Lay<GATEUP>::AS_OFF + wave * 256);
+    dma_act_scales<GATEUP>(s, j, lane, L + Lay<GATEUP>::AS_OFF + wave * 256);
   }
 }
 
@@ -441,8 +441,11 @@ static_assert(Lay1<true>::STAGE % 256 == 0 && Lay1<false>::STAGE % 256 == 0, "st
 template <bool GATEUP>
 __device__ __forceinline__ void issue_kstep1(const Src& s, int j, uint32_t L, int wave, int lane) {
   issue_weights<GATEUP>(s, j, L, wave);
-  dma16(s.a + (size_t)j * KSTEP * 1024 + wave * 1024, lane * 16, L + Lay1<GATEUP>::A_OFF + wave * 1024);
-  dma4(s.as + (size_t)j * 32 * KSTEP, lane * 4, L + Lay1<GATEUP>::AS_OFF);
+  if constexpr (GATEUP)
+    dma_act_chunk<true>(s, j, 0, lane, L + Lay1<GATEUP>::A_OFF + wave * 1024);
+  else
+    dma_act_chunk<false>(s, j, wave, lane, L + Lay1<GATEUP>::A_OFF + wave * 1024);
+  dma_act_scales<GATEUP>(s, j, lane, L + Lay1<GATEUP>::AS_OFF);
 }
 
 // K-step j of a one-row-group tile.  On entry X and sc hold block si of
@@ -517,15 +520,22 @@ __device__ __forceinline__ void tile_work(const GemmArgs& a, char (&lds)[2][Lay<
   const int wrow0 = row0 + MT_WAVE * rg;    // first CSR row of this wavefront's row group
   const bool active = wrow0 < row_end;      // wavefront-uniform (every wavefront when S > 1)
   const int t32 = T * NWAVE + rg;           // 32-row tile index of the A slab and the h chunks
-  // A operand: this wavefront's run of 1 KiB chunks (one per 32-block) and
-  // their scales, per 32-row quarter t32 of the tile.
-  const int a_kb = GATEUP ? a.d_pad / QB : a.kbmax;
+  // A operand: gate/up gathers the 32 rows of its row group from the
+  // token-major codes; down reads the h slab of 32-row quarter t32 of the tile.
   Src src;
   src.w = strip;
   src.o_w = lane * 16;
   src.o_ws = 16 * 1024 + wave * (GATEUP ? 256 : 512) + lane * 4;
-  src.a = (GATEUP ? a.gq : a.hq) + (size_t)t32 * a_kb * 1024;
-  src.as = (GATEUP ? a.gqs : a.hs) + (size_t)t32 * a_kb * 32;
+  if constexpr (GATEUP) {
+    src.a = a.gq;
+    src.as = a.gqs + (size_t)t32 * (a.d_pad / QB) * 32;
+    int t[MT_WAVE];
+    load_row_tokens(a, T, MT_WAVE * rg, t);
+    gather_offsets(a, t, MT_WAVE * rg, row0, row_end, lane, -1, src);
+  } else {
+    src.a = a.hq + (size_t)t32 * a.kbmax * 1024;
+    src.as = a.hs + (size_t)t32 * a.kbmax * 32;
+  }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)&lds[0][0];
   const uint32_t lds1 = (uint32_t)(uintptr_t)(lds_char*)&lds[1][0];
 
@@ -606,13 +616,20 @@ __device__ __forceinline__ void tile_work1(const GemmArgs& a, char* lds, int lan
   using L1 = Lay1<GATEUP>;
   const int si = wave;
   const int t32 = T * NWAVE;
-  const int a_kb = GATEUP ? a.d_pad / QB : a.kbmax;
   Src src;
   src.w = strip;
   src.o_w = lane * 16;
   src.o_ws = 16 * 1024 + wave * (GATEUP ? 256 : 512) + lane * 4;
-  src.a = (GATEUP ? a.gq : a.hq) + (size_t)t32 * a_kb * 1024;
-  src.as = (GATEUP ? a.gqs : a.hs) + (size_t)t32 * a_kb * 32;
+  if constexpr (GATEUP) {
+    src.a = a.gq;
+    src.as = a.gqs + (size_t)t32 * (a.d_pad / QB) * 32;
+    int t[MT_WAVE];
+    load_row_tokens(a, T, 0, t);
+    gather_offsets(a, t, 0, row0, row_end, lane, wave, src);
+  } else {
+    src.a = a.hq + (size_t)t32 * a.kbmax * 1024;
+    src.as = a.hs + (size_t)t32 * a.kbmax * 32;
+  }
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_char*)lds;
 
   // Down: the (token, slot) of this lane's CSR row, loaded before any copy
@@ -678,7 +695,13 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
   const int T = a.reverse ? n_tiles - 1 - Tl : Tl;
   const int32_t* ent = a.tiles + 4 + 3 * T;
   const int g = ent[0], row0 = ent[1], row_end = ent[2];
-  if (g < 0 || g >= a.G || row0 < 0 || row_end <= row0 || row_end > a.p_total) return;
+  // Gate/up: the tile's row tokens are brought into the scalar cache with
+  // the table entry (their addresses need only T; each wavefront touches the
+  // two 64-byte lines of a quarter of the tile), so that the entry and the
+  // tokens cost one memory latency and the loads of the tile body hit.
+  if constexpr (GATEUP) touch_row_tokens(a, T, wave);
+  // (one test of all three fields, so that their loads go out together)
+  if ((g < 0) | (g >= a.G) | (row0 < 0) | (row_end <= row0) | (row_end > a.p_total)) return;
   const bool shared = g >= a.E;
   const int Fg_pad = shared ? a.Fs_pad : a.F_pad;
   if (GATEUP && cs >= Fg_pad / GU_COLS) return;
@@ -743,13 +766,20 @@ __global__ __launch_bounds__(256) void block_sums_kernel(GemmArgs a, int T, int 
                                 : (shared ? a.sh_dn : a.dn + (size_t)g * a.dn_group);
   strip += (size_t)cs * KS * L::W_BYTES;
   const int t32 = T * NWAVE + wave;
-  const int a_kb = GATEUP ? a.d_pad / QB : a.kbmax;
   Src src;
   src.w = strip;
   src.o_w = lane * 16;
   src.o_ws = 16 * 1024 + wave * (GATEUP ? 256 : 512) + lane * 4;
-  src.a = (GATEUP ? a.gq : a.hq) + (size_t)t32 * a_kb * 1024;
-  src.as = (GATEUP ? a.gqs : a.hs) + (size_t)t32 * a_kb * 32;
+  if constexpr (GATEUP) {
+    src.a = a.gq;
+    src.as = a.gqs + (size_t)t32 * (a.d_pad / QB) * 32;
+    int t[MT_WAVE];
+    load_row_tokens(a, T, MT_WAVE * wave, t);
+    gather_offsets(a, t, MT_WAVE * wave, row0, row_end, lane, -1, src);
+  } else {
+    src.a = a.hq + (size_t)t32 * a.kbmax * 1024;
+    src.as = a.hs + (size_t)t32 * a.kbmax * 32;
+  }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)&lds[0];
   const int j = kb / KSTEP, b = kb % KSTEP;
   issue_weights<GATEUP>(src, j, lds0, wave);

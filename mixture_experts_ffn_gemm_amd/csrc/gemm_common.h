@@ -72,15 +72,95 @@ __device__ __forceinline__ void wait_copies_reads_barrier() {
 
 // Copy sources of k-step 0: wavefront-uniform bases and per-lane 32-bit
 // offsets.  K-step j adds j times the format's k-step bytes to the weight
-// base, KSTEP chunks to the activation base and one k-step of scales (32 rows
-// x KSTEP) to the scale base.
+// base.  Down reads h in slab form ([32 rows][128 B] per k-step): k-step j
+// adds KSTEP chunks to the activation base and one k-step of scales (32 rows
+// x KSTEP) to the scale base.  Gate/up gathers its code rows from the
+// token-major codes gq[token][d_pad]: k-step j adds KSTEP blocks (128 bytes)
+// to the base, and the per-lane offsets o_a name the tokens; its scales are
+// in slab form like h's (gqs, per 32-row quarter of a tile).
 struct Src {
   const uint8_t* w;    // the strip's first k-step
-  const int8_t* a;     // this wavefront's activation chunks (gq or hq)
-  const uint16_t* as;  // their scales (gqs or hs)
+  const int8_t* a;     // gate/up: gq; down: this wavefront's h chunks
+  const uint16_t* as;  // this wavefront's scale slab (gqs or hs)
   uint32_t o_w;        // 16 * lane: code chunk piece
   uint32_t o_ws;       // Q8_0: 16 KiB + 4 * lane + this wavefront's share of the weight scales
+  uint32_t o_a[KSTEP]; // gate/up: chunk i's piece of this lane (see gather_offsets)
 };
+
+// The tokens of rows i0..i0+31 of tile T as the bucketing stored them
+// (row_tok[T * 128 + i]; the tile's row i is CSR row row0 + i).  Scalar
+// loads whose addresses depend only on T, so they can go out together with
+// the tile's table entry, and waiting for them never waits for the copies in
+// flight (those count on the vector-memory counter).  Entries past a group's
+// rows were never written: gather_offsets discards them.
+__device__ __forceinline__ void load_row_tokens(const GemmArgs& a, int T, int i0, int (&t)[MT_WAVE]) {
+  typedef const int32_t __attribute__((address_space(4)))* tok_ptr;
+  const tok_ptr p = (tok_ptr)a.row_tok + (size_t)T * MT_WG + i0;
+#pragma unroll
+  for (int m = 0; m < MT_WAVE; ++m) t[m] = p[m];
+}
+
+// Loads rows 32 wave and 32 wave + 16 of tile T's row tokens and waits for
+// them, so that the two 64-byte scalar-cache lines of the wavefront's quarter
+// of the tile are resident when the tile body reads them.
+__device__ __forceinline__ void touch_row_tokens(const GemmArgs& a, int T, int wave) {
+  typedef const int32_t __attribute__((address_space(4)))* tok_ptr;
+  const tok_ptr p = (tok_ptr)a.row_tok + (size_t)T * MT_WG + MT_WAVE * wave;
+  const int v = p[0] ^ p[16];
+  asm volatile("" ::"s"(v));
+}
+
+// Gate/up copy offsets of the 32-row slab of rows i0..i0+31 of a tile whose
+// rows are CSR rows row0..row_end-1, from their raw tokens t (a row past the
+// end, or a token id out of range, reads token 0).  The LDS slab is
+// [row][128 B] per k-step, the 16-byte piece p of row r at slot p ^ (r % 8);
+// copy i of a k-step fills LDS bytes 1024 i + 16 lane, i.e. slot lane % 8 of
+// row 8 i + lane / 8, so lane reads piece (lane % 8) ^ (lane / 8) -- bytes
+// 16 p of the k-step's 128 -- of that row's token.  `chunk0` >= 0 asks for
+// copy `chunk0` alone, in o_a[0] (the one-row-group pipeline, where each
+// wavefront copies one chunk of a shared slab).
+__device__ __forceinline__ void gather_offsets(const GemmArgs& a, const int (&raw)[MT_WAVE], int i0, int row0,
+                                               int row_end, int lane, int chunk0, Src& s) {
+  int t[MT_WAVE];
+#pragma unroll
+  for (int m = 0; m < MT_WAVE; ++m)
+    t[m] = (row0 + i0 + m < row_end && (unsigned)raw[m] < (unsigned)a.n_tokens) ? raw[m] : 0;
+  const int r8 = lane >> 3;
+  const uint32_t piece = (uint32_t)(((lane & 7) ^ r8) << 4);
+  const uint32_t dp = (uint32_t)a.d_pad;
+  if (chunk0 >= 0) {
+    int v = 0;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int u = chunk0 == 0 ? t[m] : chunk0 == 1 ? t[8 + m] : chunk0 == 2 ? t[16 + m] : t[24 + m];
+      v = (r8 == m) ? u : v;
+    }
+    s.o_a[0] = (uint32_t)v * dp + piece;
+  } else {
+#pragma unroll
+    for (int i = 0; i < KSTEP; ++i) {
+      int v = t[8 * i];
+#pragma unroll
+      for (int m = 1; m < 8; ++m) v = (r8 == m) ? t[8 * i + m] : v;
+      s.o_a[i] = (uint32_t)v * dp + piece;
+    }
+  }
+}
+
+// The activation copies of k-step j: chunk i of the slab (four per k-step),
+// from the token-major codes (gate/up) or the h slab (down), and the slab's
+// scales.
+template <bool GATEUP>
+__device__ __forceinline__ void dma_act_chunk(const Src& s, int j, int i, int lane, uint32_t lds) {
+  if constexpr (GATEUP)
+    dma16(s.a + (size_t)j * KSTEP * QB, s.o_a[i], lds);
+  else
+    dma16(s.a + ((size_t)j * KSTEP + i) * 1024, lane * 16, lds);
+}
+template <bool GATEUP>
+__device__ __forceinline__ void dma_act_scales(const Src& s, int j, int lane, uint32_t lds) {
+  dma4(s.as + (size_t)j * 32 * KSTEP, lane * 4, lds);
+}
 
 struct NoHook {
   __device__ void operator()(int) const {}

@@ -86,20 +86,21 @@ __device__ __forceinline__ void issue_weights_part_q4(const Src& s, int j, uint3
   const uint8_t* w = s.w + (size_t)j * Q4K_KSTEP_BYTES;
   if (p < 3) dma16(w + (wave + 4 * p) * 1024, s.o_w, L + (wave + 4 * p) * 1024);
 }
+template <bool GATEUP>
 __device__ __forceinline__ void issue_acts_q4(const Src& s, int j, uint32_t L, int wave, int lane) {
-  const int8_t* a = s.a + (size_t)j * KSTEP * 1024;
 #pragma unroll
-  for (int i = 0; i < KSTEP; ++i) dma16(a + i * 1024, lane * 16, L + LayQ4::A_OFF + (wave * KSTEP + i) * 1024);
-  dma4(s.as + (size_t)j * 32 * KSTEP, lane * 4, L + LayQ4::AS_OFF + wave * 256);
+  for (int i = 0; i < KSTEP; ++i)
+    dma_act_chunk<GATEUP>(s, j, i, lane, L + LayQ4::A_OFF + (wave * KSTEP + i) * 1024);
+  dma_act_scales<GATEUP>(s, j, lane, L + LayQ4::AS_OFF + wave * 256);
 }
+template <bool GATEUP>
 __device__ __forceinline__ void issue_acts_part_q4(const Src& s, int j, uint32_t L, int wave, int lane, int p) {
-  const int8_t* a = s.a + (size_t)j * KSTEP * 1024;
   if (p < 2) {
 #pragma unroll
     for (int i = 2 * p; i < 2 * p + 2; ++i)
-      dma16(a + i * 1024, lane * 16, L + LayQ4::A_OFF + (wave * KSTEP + i) * 1024);
+      dma_act_chunk<GATEUP>(s, j, i, lane, L + LayQ4::A_OFF + (wave * KSTEP + i) * 1024);
   } else if (p == 2) {
-    dma4(s.as + (size_t)j * 32 * KSTEP, lane * 4, L + LayQ4::AS_OFF + wave * 256);
+    dma_act_scales<GATEUP>(s, j, lane, L + LayQ4::AS_OFF + wave * 256);
   }
 }
 
@@ -268,6 +269,7 @@ __device__ __forceinline__ void compute_block_q4(const OpsQ4& o, const ScalesQ4&
 // barrier and operand reads are placed as in the Q8_0 k-step: the
 // activation half of k-step j+1 goes out during block 0, the barrier comes
 // before block 3, and the weights of k-step j+2 go out during block 3.
+template <bool GATEUP>
 __device__ __forceinline__ void kstep_q4(const Src& src, int j, int KS, int wave, int lane, const char* cur,
                                          const char* nxt, uint32_t cur_lds, uint32_t nxt_lds, OpsQ4& X, OpsQ4& Y,
                                          const ScalesQ4& sc, ScalesQ4& sn, const Ctx& cx, uint2& ps,
@@ -275,7 +277,7 @@ __device__ __forceinline__ void kstep_q4(const Src& src, int j, int KS, int wave
   const bool acts = j >= 1 && j + 1 < KS;
   read_block_q4(cur, 1, wave, lane, Y);
   compute_block_q4(X, sc, 0, Y, sc, 1, false, sc.mp, cx, lane, ps, c, cf, s, acc, [&](int t) {
-    if (acts) issue_acts_part_q4(src, j + 1, nxt_lds, wave, lane, t);
+    if (acts) issue_acts_part_q4<GATEUP>(src, j + 1, nxt_lds, wave, lane, t);
   });
   read_block_q4(cur, 2, wave, lane, X);
   compute_block_q4(Y, sc, 1, X, sc, 2, false, sc.mp, cx, lane, ps, c, cf, s, acc);
@@ -296,6 +298,7 @@ __device__ __forceinline__ void kstep_q4(const Src& src, int j, int KS, int wave
 // two blocks only: the code sums of the other two stay at their bias, so
 // their P is zero).  Copies, barrier and their placement are those of
 // kstep_q4; each wavefront copies its row group's slab into its own area.
+template <bool GATEUP>
 __device__ __forceinline__ void kstep_q4_split2(const Src& src, int j, int KS, int wave, int lane, int si,
                                                 const char* cur, const char* nxt, uint32_t cur_lds,
                                                 uint32_t nxt_lds, OpsQ4& X, OpsQ4& Y, const ScalesQ4& sc,
@@ -304,7 +307,7 @@ __device__ __forceinline__ void kstep_q4_split2(const Src& src, int j, int KS, i
   const bool acts = j >= 1 && j + 1 < KS;
   read_block_q4(cur, si + 2, wave, lane, Y);
   compute_block_q4(X, sc, si, Y, sc, si + 2, false, sc.mp, cx, lane, ps, c, cf, s, acc, [&](int t) {
-    if (acts) issue_acts_part_q4(src, j + 1, nxt_lds, wave, lane, t);
+    if (acts) issue_acts_part_q4<GATEUP>(src, j + 1, nxt_lds, wave, lane, t);
   });
   if (j + 1 < KS) wait_copies_barrier_0();
   const bool weights = j + 2 < KS;
@@ -333,21 +336,27 @@ static_assert(3 * Lay1Q4::STAGE <= 2 * LayQ4::STAGE, "three stages must fit in t
 constexpr int T1_PAIR_OFF = 3 * Lay1Q4::STAGE;
 static_assert(T1_PAIR_OFF + 2 * 64 * 4 <= 2 * LayQ4::STAGE, "pair slots must fit in the LDS buffers");
 static_assert(3 * 64 * 64 * 4 <= T1_PAIR_OFF, "the split reduction must not reach the pair slots");
+// Gate/up: each wavefront's gather offset (o_a[0] per lane) in the same place
+// (down's pair slots), read back before each k-step's copies.
+constexpr int T1_GATHER_OFF = T1_PAIR_OFF;
+static_assert(T1_GATHER_OFF + NWAVE * 64 * 4 <= 2 * LayQ4::STAGE, "gather offsets must fit in the LDS buffers");
 static_assert(Lay1Q4::STAGE % 256 == 0, "stage alignment");
 
 // This wavefront's copies of k-step j into the stage at LDS address L: its
 // three weight pieces, chunk `wave` of the slab and the slab's scales (every
 // wavefront copies the same 256 bytes, so that all issue the same number).
+template <bool GATEUP>
 __device__ __forceinline__ void issue_kstep1_q4(const Src& s, int j, uint32_t L, int wave, int lane) {
   issue_weights_q4(s, j, L, wave);
-  dma16(s.a + (size_t)j * KSTEP * 1024 + wave * 1024, lane * 16, L + Lay1Q4::A_OFF + wave * 1024);
-  dma4(s.as + (size_t)j * 32 * KSTEP, lane * 4, L + Lay1Q4::AS_OFF);
+  dma_act_chunk<GATEUP>(s, j, GATEUP ? 0 : wave, lane, L + Lay1Q4::A_OFF + wave * 1024);
+  dma_act_scales<GATEUP>(s, j, lane, L + Lay1Q4::AS_OFF);
 }
 
 // K-step j of a one-row-group tile.  On entry X and sc hold block si of
 // k-step j; k-steps j+1 and j+2 are in flight.  The barrier publishes k-step
 // j+1 and proves that every wavefront has read k-step j, whose stage then
 // receives k-step j+3.  On exit Y and sn hold block si of k-step j+1.
+template <bool GATEUP>
 __device__ __forceinline__ void kstep1_q4(const Src& src, int j, int KS, int wave, int lane, int si, const char* lds,
                                           uint32_t lds_base, const OpsQ4& X, OpsQ4& Y, const ScalesQ4& sc,
                                           ScalesQ4& sn, const Ctx& cx, uint2& ps, v16i& c, v16f& cf, v16f& s,
@@ -365,7 +374,16 @@ __device__ __forceinline__ void kstep1_q4(const Src& src, int j, int KS, int wav
       wait_copies_reads_barrier<Lay1Q4::DMA>();
     else
       wait_copies_reads_barrier<0>();
-    if (j + 3 < KS) issue_kstep1_q4(src, j + 3, lds_base + st * Lay1Q4::STAGE, wave, lane);
+    if (j + 3 < KS) {
+      if constexpr (GATEUP) {
+        // the gather offset waits in LDS between k-steps (no register held)
+        Src s2 = src;
+        s2.o_a[0] = *reinterpret_cast<const uint32_t*>(lds + T1_GATHER_OFF + wave * 256 + lane * 4);
+        issue_kstep1_q4<true>(s2, j + 3, lds_base + st * Lay1Q4::STAGE, wave, lane);
+      } else {
+        issue_kstep1_q4<false>(src, j + 3, lds_base + st * Lay1Q4::STAGE, wave, lane);
+      }
+    }
   }
   const char* nb = lds + sn1 * Lay1Q4::STAGE;
   read_block_q4_at(nb, Lay1Q4::A_OFF, si, lane, Y);
@@ -406,13 +424,20 @@ __device__ __forceinline__ void tile_work_q4(const GemmArgs& a, char (&lds)[2][L
   const int wrow0 = row0 + MT_WAVE * rg;
   const bool active = wrow0 < row_end;  // every wavefront when S > 1
   const int t32 = T * NWAVE + rg;
-  const int a_kb = GATEUP ? a.d_pad / QB : a.kbmax;
   Src src;
   src.w = strip;
   src.o_w = lane * 16;
   src.o_ws = 0;
-  src.a = (GATEUP ? a.gq : a.hq) + (size_t)t32 * a_kb * 1024;
-  src.as = (GATEUP ? a.gqs : a.hs) + (size_t)t32 * a_kb * 32;
+  if constexpr (GATEUP) {
+    src.a = a.gq;
+    src.as = a.gqs + (size_t)t32 * (a.d_pad / QB) * 32;
+    int t[MT_WAVE];
+    load_row_tokens(a, T, MT_WAVE * rg, t);
+    gather_offsets(a, t, MT_WAVE * rg, row0, row_end, lane, -1, src);
+  } else {
+    src.a = a.hq + (size_t)t32 * a.kbmax * 1024;
+    src.as = a.hs + (size_t)t32 * a.kbmax * 32;
+  }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)&lds[0][0];
   const uint32_t lds1 = (uint32_t)(uintptr_t)(lds_char*)&lds[1][0];
 
@@ -420,7 +445,7 @@ __device__ __forceinline__ void tile_work_q4(const GemmArgs& a, char (&lds)[2][L
   // between them (issued by every wavefront, so that the vmcnt count holds
   // for all); wait for k-step 0.
   issue_weights_q4(src, 0, lds0, wave);
-  issue_acts_q4(src, 0, lds0, wave, lane);
+  issue_acts_q4<GATEUP>(src, 0, lds0, wave, lane);
   int tok = -1, slt = -1;
   if (!GATEUP) {
     const int p_lane = min(wrow0 + (lane & 31), a.p_total - 1);
@@ -429,7 +454,7 @@ __device__ __forceinline__ void tile_work_q4(const GemmArgs& a, char (&lds)[2][L
   }
   if (KS > 1) {
     issue_weights_q4(src, 1, lds1, wave);
-    issue_acts_q4(src, 1, lds1, wave, lane);
+    issue_acts_q4<GATEUP>(src, 1, lds1, wave, lane);
     wait_copies_barrier_n<LayQ4::DMA + 2 * !GATEUP>();
   } else {
     wait_copies_barrier_0();
@@ -450,20 +475,20 @@ __device__ __forceinline__ void tile_work_q4(const GemmArgs& a, char (&lds)[2][L
     // Unrolled by two so that each buffer and scale set has a fixed role.
     for (int j = 0; j < KS; j += 2) {
       if constexpr (S == 1) {
-        kstep_q4(src, j, KS, wave, lane, lds[0], lds[1], lds0, lds1, X, Y, s0, s1, cx, ps, c, cf, s, acc);
+        kstep_q4<GATEUP>(src, j, KS, wave, lane, lds[0], lds[1], lds0, lds1, X, Y, s0, s1, cx, ps, c, cf, s, acc);
         if (j + 1 < KS)
-          kstep_q4(src, j + 1, KS, wave, lane, lds[1], lds[0], lds1, lds0, X, Y, s1, s0, cx, ps, c, cf, s, acc);
+          kstep_q4<GATEUP>(src, j + 1, KS, wave, lane, lds[1], lds[0], lds1, lds0, X, Y, s1, s0, cx, ps, c, cf, s, acc);
       } else {
-        kstep_q4_split2(src, j, KS, wave, lane, si, lds[0], lds[1], lds0, lds1, X, Y, s0, s1, cx, ps, c, cf, s,
+        kstep_q4_split2<GATEUP>(src, j, KS, wave, lane, si, lds[0], lds[1], lds0, lds1, X, Y, s0, s1, cx, ps, c, cf, s,
                         acc);
         if (j + 1 < KS)
-          kstep_q4_split2(src, j + 1, KS, wave, lane, si, lds[1], lds[0], lds1, lds0, X, Y, s1, s0, cx, ps, c, cf,
+          kstep_q4_split2<GATEUP>(src, j + 1, KS, wave, lane, si, lds[1], lds[0], lds1, lds0, X, Y, s1, s0, cx, ps, c, cf,
                           s, acc);
       }
     }
   } else if constexpr (S == 1) {
     for (int j = 0; j + 1 < KS; ++j) {
-      if (j >= 1) issue_acts_q4(src, j + 1, (j & 1) ? lds0 : lds1, wave, lane);
+      if (j >= 1) issue_acts_q4<GATEUP>(src, j + 1, (j & 1) ? lds0 : lds1, wave, lane);
       wait_copies_barrier_0();
       if (j + 2 < KS) issue_weights_q4(src, j + 2, (j & 1) ? lds1 : lds0, wave);
     }
@@ -487,13 +512,21 @@ __device__ __forceinline__ void tile_work1_q4(const GemmArgs& a, char* lds, int 
                                               int row0, int row_end, int KS, const uint8_t* strip) {
   const int si = wave;
   const int t32 = T * NWAVE;
-  const int a_kb = GATEUP ? a.d_pad / QB : a.kbmax;
   Src src;
   src.w = strip;
   src.o_w = lane * 16;
   src.o_ws = 0;
-  src.a = (GATEUP ? a.gq : a.hq) + (size_t)t32 * a_kb * 1024;
-  src.as = (GATEUP ? a.gqs : a.hs) + (size_t)t32 * a_kb * 32;
+  if constexpr (GATEUP) {
+    src.a = a.gq;
+    src.as = a.gqs + (size_t)t32 * (a.d_pad / QB) * 32;
+    int t[MT_WAVE];
+    load_row_tokens(a, T, 0, t);
+    gather_offsets(a, t, 0, row0, row_end, lane, wave, src);
+    *reinterpret_cast<uint32_t*>(lds + T1_GATHER_OFF + wave * 256 + lane * 4) = src.o_a[0];
+  } else {
+    src.a = a.hq + (size_t)t32 * a.kbmax * 1024;
+    src.as = a.hs + (size_t)t32 * a.kbmax * 32;
+  }
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_char*)lds;
 
   // Down: the (token, slot) of this lane's CSR row, copied into LDS before
@@ -505,9 +538,9 @@ __device__ __forceinline__ void tile_work1_q4(const GemmArgs& a, char* lds, int 
     dma4(a.tok_k, (uint32_t)p_lane * 4, lds_base + T1_PAIR_OFF + 256);
   }
   // Prologue: k-steps 0, 1 and 2 in flight; wait for k-step 0.
-  issue_kstep1_q4(src, 0, lds_base, wave, lane);
-  if (KS > 1) issue_kstep1_q4(src, 1, lds_base + Lay1Q4::STAGE, wave, lane);
-  if (KS > 2) issue_kstep1_q4(src, 2, lds_base + 2 * Lay1Q4::STAGE, wave, lane);
+  issue_kstep1_q4<GATEUP>(src, 0, lds_base, wave, lane);
+  if (KS > 1) issue_kstep1_q4<GATEUP>(src, 1, lds_base + Lay1Q4::STAGE, wave, lane);
+  if (KS > 2) issue_kstep1_q4<GATEUP>(src, 2, lds_base + 2 * Lay1Q4::STAGE, wave, lane);
   if (KS > 2)
     wait_copies_reads_barrier<2 * Lay1Q4::DMA>();
   else if (KS > 1)
@@ -528,8 +561,8 @@ __device__ __forceinline__ void tile_work1_q4(const GemmArgs& a, char* lds, int 
   pipeline_init_q4(X, s0, si, lane, cx, c, cf, s);
   uint2 ps = make_uint2(PS_ZERO, PS_ZERO);
   for (int j = 0; j < KS; j += 2) {
-    kstep1_q4(src, j, KS, wave, lane, si, lds, lds_base, X, Y, s0, s1, cx, ps, c, cf, s, acc);
-    if (j + 1 < KS) kstep1_q4(src, j + 1, KS, wave, lane, si, lds, lds_base, Y, X, s1, s0, cx, ps, c, cf, s, acc);
+    kstep1_q4<GATEUP>(src, j, KS, wave, lane, si, lds, lds_base, X, Y, s0, s1, cx, ps, c, cf, s, acc);
+    if (j + 1 < KS) kstep1_q4<GATEUP>(src, j + 1, KS, wave, lane, si, lds, lds_base, Y, X, s1, s0, cx, ps, c, cf, s, acc);
   }
   split_reduce(lds, 4, 0, si, lane, acc);
   if (si != 0) return;
@@ -563,7 +596,13 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_q4k_kernel(GemmArgs a) {
   const int T = a.reverse ? n_tiles - 1 - Tl : Tl;
   const int32_t* ent = a.tiles + 4 + 3 * T;
   const int g = ent[0], row0 = ent[1], row_end = ent[2];
-  if (g < 0 || g >= a.G || row0 < 0 || row_end <= row0 || row_end > a.p_total) return;
+  // Gate/up: the tile's row tokens are brought into the scalar cache with
+  // the table entry (their addresses need only T; each wavefront touches the
+  // two 64-byte lines of a quarter of the tile), so that the entry and the
+  // tokens cost one memory latency and the loads of the tile body hit.
+  if constexpr (GATEUP) touch_row_tokens(a, T, wave);
+  // (one test of all three fields, so that their loads go out together)
+  if ((g < 0) | (g >= a.G) | (row0 < 0) | (row_end <= row0) | (row_end > a.p_total)) return;
   const bool shared = g >= a.E;
   const int Fg_pad = shared ? a.Fs_pad : a.F_pad;
   if (GATEUP && cs >= Fg_pad / GU_COLS) return;

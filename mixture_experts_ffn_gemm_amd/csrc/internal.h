@@ -31,20 +31,23 @@
 // Workspace (per call, caller-allocated, carved by ws_layout()):
 //   logits fp32 [N][E]; ids, rank i32 [N][k]; w fp32 [N][k]; gs fp32 [N];
 //   hist i32 [ceil(N/8)][E]; exp_start i32 [E+2]; tok_i, tok_k i32 [N*k + N];
-//   pos i32 [N][k + has_shared]  (padded GEMM row of each (token, slot) pair:
-//                               first tile of its group * 128 + its index in
-//                               the group; -1 if beyond the tile bound);
+//   row_tok i32 [T_bound][128]  (the token of row i of tile T at T*128 + i,
+//                               the tile's rows being CSR rows row0 + i; rows
+//                               past a group's end are not written);
 //   tiles i32 [4 + 3*T_bound]  (tiles[0] = number of 128-row tiles, then
 //                               {group, first CSR row, end CSR row} per tile);
-//   The GEMM A operands, per 32-row quarter t32 of a tile (padded row / 32)
-//   and k-step j (4 blocks = 128 codes):
-//   gq int8 [4*T_bound][d_pad/128][32 rows][128]  (gate/up activations: a 4 KiB
-//                               slab per (t32, j); the 16-code piece p of row r
-//                               (block p/2 of the k-step, half p%2) sits at byte
-//                               16 * (p ^ (r % 8)) of the row's 128-byte line);
-//   gqs fp16 [4*T_bound][d_pad/128][32][4]    (their scales);
-//   hq int8 [4*T_bound][KBMAX/4][32][128], hs fp16 [4*T_bound][KBMAX/4][32][4]
-//                               (the same for h, the down GEMM's A operand);
+//   gq int8 [N][d_pad]          (token-major activation codes, zero past d:
+//                               the gate/up GEMM gathers its rows from here);
+//   gqs fp16 [4*T_bound][d_pad/128][32][4]  (their scales per 32-row quarter
+//                               t32 of a tile (padded row / 32), k-step and
+//                               row, as for hs below);
+//   The down GEMM's A operand h, per 32-row quarter t32 of a tile (padded
+//   row / 32) and k-step j (4 blocks = 128 codes):
+//   hq int8 [4*T_bound][KBMAX/4][32 rows][128]  (a 4 KiB slab per (t32, j);
+//                               the 16-code piece p of row r (block p/2 of the
+//                               k-step, half p%2) sits at byte 16 * (p ^ (r % 8))
+//                               of the row's 128-byte line);
+//   hs fp16 [4*T_bound][KBMAX/4][32][4]         (their scales);
 //   partial fp32 [N][k + has_shared][d].
 // The decode region, always reserved for Nd = min(N, DECODE_MAX_TOKENS) tokens
 // (so the total never shrinks as N grows), used by decode calls only:
@@ -99,7 +102,7 @@ struct Dims {
 inline int round_up(int v, int m) { return (v + m - 1) / m * m; }
 
 struct WsLayout {
-  size_t logits, ids, rank, w, gs, hist, exp_start, tok_i, tok_k, pos, tiles, gq, gqs, hq, hs, partial;
+  size_t logits, ids, rank, w, gs, hist, exp_start, tok_i, tok_k, row_tok, tiles, gq, gqs, hq, hs, partial;
   size_t dlist, dxq, dxs, dhq, dhs;  // decode region (min(N, 8) tokens)
   size_t total;
   int n_route_tiles;
@@ -169,16 +172,16 @@ hipError_t launch_route(const float* logits, int n, int E, int k, int norm, int3
                         int32_t* rank, int32_t* hist, hipStream_t s);
 hipError_t launch_quantize(const float* v, int64_t n_values, int8_t* q, uint16_t* scales,
                            hipStream_t s);
-// The bucketing (expStart, expTokI/expTokK, each pair's padded GEMM row pos,
-// the tile table) and, in the same workgroups, the activation quantiser: every
-// token row quantised per 32-block, its codes and scales written to the
-// padded GEMM rows pos[t][0..kk) in the gq/gqs layout (rows past the tile
-// bound are -1 and skipped); with sh_gate_vec != NULL also
-// gs[t] = sigmoid(x[t] . g); xq_out [N][d] / xs_out [N][d/32] (each optional)
-// receive token-major copies.
+// The bucketing (expStart, expTokI/expTokK, the tile table and its row
+// tokens row_tok [T_bound][128]) and, in the same
+// workgroups, the activation quantiser: every token row quantised per
+// 32-block, codes into gq [N][d_pad], scales into gqs at each of the token's
+// tile rows (zero past d); with
+// sh_gate_vec != NULL also gs[t] = sigmoid(x[t] . g); xq_out [N][d] /
+// xs_out [N][d/32] (each optional) receive copies of the unpadded width.
 hipError_t launch_bucket_quantize(const int32_t* ids, const int32_t* rank, const int32_t* hist, int n,
                                   int E, int k, int has_shared, int32_t* exp_start, int32_t* tok_i,
-                                  int32_t* tok_k, int32_t* pos, int32_t* tiles, int tile_bound,
+                                  int32_t* tok_k, int32_t* row_tok, int32_t* tiles, int tile_bound,
                                   const float* x, int d, int d_pad, int8_t* gq, uint16_t* gqs,
                                   const float* sh_gate_vec, float* gs, int8_t* xq_out, uint16_t* xs_out,
                                   hipStream_t s);
@@ -188,6 +191,7 @@ struct GemmArgs {
   const int32_t* tiles;
   const int32_t* tok_i;
   const int32_t* tok_k;
+  const int32_t* row_tok;  // [T_bound][128]: the token of each tile row
   int E;
   int G;          // groups: E routed (+1 shared)
   int n_tokens;
