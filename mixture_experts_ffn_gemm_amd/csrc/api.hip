@@ -56,6 +56,7 @@ WsLayout ws_layout(const Dims& dm, int max_tokens) {
   const size_t t32 = (size_t)L.tile_bound * (MT_WG / MT_WAVE);
   const size_t kbd = (size_t)dm.d_pad / QB;
   L.gq = take(Nn * dm.d_pad);        // token-major codes
+  L.gxs = take(dm.E > 64 ? Nn * kbd * 2 : 0);  // and their scales, when the routing launch quantises
   L.gqs = take(t32 * 32 * kbd * 2);  // their scales per tile row
   L.hq = take(t32 * kbmax * 1024);
   L.hs = take(t32 * 32 * kbmax * 2);
@@ -250,14 +251,19 @@ int run_layer(const moe_ffn_weights* W, const float* x, int32_t n, float* out, v
   } else {
     HIP_TRY(launch_router(x, n, dm.d, W->router_wt, rbias, dm.E, dm.E64, logits, W->n_cu, s));
     HIP_TRY(mark(1));
-    HIP_TRY(launch_route(logits, n, dm.E, dm.k, dm.norm, ids, w, rank, hist, s));
+    // the routing launch also quantises the tokens (its routing workgroups fill few CUs)
+    const RowQuant rq{x, dm.d, dm.d_pad, dm.has_shared ? W->sh_gate_vec : nullptr, gs, gq,
+                      (uint16_t*)(base + L.gxs), r ? r->xq : nullptr, r ? r->xs : nullptr};
+    HIP_TRY(launch_route(logits, n, dm.E, dm.k, dm.norm, ids, w, rank, hist, rq, s));
   }
   HIP_TRY(mark(2));
+  const bool quantised = dm.E > 64;
   HIP_TRY(launch_bucket_quantize(ids, rank, hist, n, dm.E, dm.k, dm.has_shared, exp_start, tok_i, tok_k,
                                  (int32_t*)(base + L.row_tok),
                                  tiles, L.tile_bound, x, dm.d, dm.d_pad, gq, gqs,
-                                 dm.has_shared ? W->sh_gate_vec : nullptr, gs, r ? r->xq : nullptr,
-                                 r ? r->xs : nullptr, s));
+                                 dm.has_shared ? W->sh_gate_vec : nullptr, gs,
+                                 (r && !quantised) ? r->xq : nullptr, (r && !quantised) ? r->xs : nullptr,
+                                 quantised ? (const uint16_t*)(base + L.gxs) : nullptr, s));
   GemmArgs a = gemm_args(W, L, base, n);
   a.reverse = reverse_tiles;
   HIP_TRY(mark(3));

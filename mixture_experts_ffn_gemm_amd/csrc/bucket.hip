@@ -72,6 +72,7 @@ struct QuantArgs {
   float* gs;
   int8_t* xq_out;    // optional token-major copies
   uint16_t* xs_out;
+  const uint16_t* xs_tok;  // non-NULL: the codes are written, these are their scales
 };
 
 // At most 128 VGPRs (four wavefronts per SIMD), so that two 512-thread
@@ -109,9 +110,11 @@ __global__ __launch_bounds__(BQ_THREADS) __attribute__((amdgpu_waves_per_eu(4, 8
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const f4v*>(src + 4 * i);
   };
-  f4v cur[4], nxt[4] = {};
-  load(0, cur);
-  if (8 < KS) load(8, nxt);
+  f4v cur[4] = {}, nxt[4] = {};
+  if (!qa.xs_tok) {
+    load(0, cur);
+    if (8 < KS) load(8, nxt);
+  }
 
   // Per-expert totals over all tiles and over the tiles before this one; for
   // small E several threads share an expert's column and their sums meet in LDS.
@@ -213,6 +216,24 @@ __global__ __launch_bounds__(BQ_THREADS) __attribute__((amdgpu_waves_per_eu(4, 8
   // Quantise: wavefront w takes token t0 + w.
   if (wave >= nt) return;
   const int t = t0 + wave;
+  // The k-step's 4 scales, once per expert slot at the slot's tile row: lane
+  // p of the k-step's 8 takes slots p and p + 8.
+  auto place_scales = [&](int j, int p, uint2 sc4) {
+    for (int s2 = p; s2 < kk; s2 += 8) {
+      const int row = s_pos[wave][s2];
+      if (row >= 0)
+        *reinterpret_cast<uint2*>(qa.gqs + (((size_t)(row >> 5) * KS + j) * 32 + (row & 31)) * KSTEP) = sc4;
+    }
+  };
+  if (qa.xs_tok) {
+    for (int j0 = 0; j0 < KS; j0 += 8) {
+      const int j = j0 + (lane >> 3);
+      if (j < KS)
+        place_scales(j, lane & 7,
+                     *reinterpret_cast<const uint2*>(qa.xs_tok + (size_t)t * (qa.d_pad / QB) + KSTEP * j));
+    }
+    return;
+  }
   float gacc = 0.0f;
   // Each pass covers 8 k-steps; the pass after next is requested before this
   // pass is quantised and stored.
@@ -241,13 +262,7 @@ __global__ __launch_bounds__(BQ_THREADS) __attribute__((amdgpu_waves_per_eu(4, 8
     if (j < KS) {
       const uint4 codes = make_uint4(pk[0], pk[1], pk[2], pk[3]);
       *reinterpret_cast<uint4*>(qa.gq + (size_t)t * qa.d_pad + c0) = codes;
-      // one 8-byte store per expert slot: lane p of the k-step takes slots p and p + 8
-      const uint2 sc4 = make_uint2(sb0 | (sb1 << 16), sb2 | (sb3 << 16));
-      for (int s2 = p; s2 < kk; s2 += 8) {
-        const int row = s_pos[wave][s2];
-        if (row >= 0)
-          *reinterpret_cast<uint2*>(qa.gqs + (((size_t)(row >> 5) * KS + j) * 32 + (row & 31)) * KSTEP) = sc4;
-      }
+      place_scales(j, p, make_uint2(sb0 | (sb1 << 16), sb2 | (sb3 << 16)));
       if (qa.xq_out && valid) *reinterpret_cast<uint4*>(qa.xq_out + (size_t)t * qa.d + c0) = codes;
       if (qa.xs_out && half == 0 && valid) qa.xs_out[(size_t)t * (qa.d / QB) + kb] = s16;
     }
@@ -275,9 +290,9 @@ hipError_t launch_bucket_quantize(const int32_t* ids, const int32_t* rank, const
                                   int32_t* tok_k, int32_t* row_tok, int32_t* tiles, int tile_bound,
                                   const float* x, int d, int d_pad, int8_t* gq, uint16_t* gqs,
                                   const float* sh_gate_vec, float* gs, int8_t* xq_out, uint16_t* xs_out,
-                                  hipStream_t s) {
+                                  const uint16_t* xs_tok, hipStream_t s) {
   const int n_tiles = (n + ROUTE_TILE - 1) / ROUTE_TILE;
-  const QuantArgs qa{x, d, d_pad, gq, gqs, sh_gate_vec, gs, xq_out, xs_out};
+  const QuantArgs qa{x, d, d_pad, gq, gqs, sh_gate_vec, gs, xq_out, xs_out, xs_tok};
   bucket_quantize_kernel<<<n_tiles, BQ_THREADS, 0, s>>>(ids, rank, hist, n, E, k, has_shared, n_tiles, exp_start,
                                                         tok_i, tok_k, row_tok, tiles, tile_bound, qa);
   return hipGetLastError();

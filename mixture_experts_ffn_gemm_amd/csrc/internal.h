@@ -38,6 +38,8 @@
 //                               {group, first CSR row, end CSR row} per tile);
 //   gq int8 [N][d_pad]          (token-major activation codes, zero past d:
 //                               the gate/up GEMM gathers its rows from here);
+//   gxs fp16 [N][d_pad/32]      (their scales token-major, E > 64 only: the
+//                               routing launch quantises there);
 //   gqs fp16 [4*T_bound][d_pad/128][32][4]  (their scales per 32-row quarter
 //                               t32 of a tile (padded row / 32), k-step and
 //                               row, as for hs below);
@@ -102,7 +104,7 @@ struct Dims {
 inline int round_up(int v, int m) { return (v + m - 1) / m * m; }
 
 struct WsLayout {
-  size_t logits, ids, rank, w, gs, hist, exp_start, tok_i, tok_k, row_tok, tiles, gq, gqs, hq, hs, partial;
+  size_t logits, ids, rank, w, gs, hist, exp_start, tok_i, tok_k, row_tok, tiles, gq, gxs, gqs, hq, hs, partial;
   size_t dlist, dxq, dxs, dhq, dhs;  // decode region (min(N, 8) tokens)
   size_t total;
   int n_route_tiles;
@@ -168,8 +170,24 @@ hipError_t launch_router(const float* x, int n, int d, const float* wt, const fl
 hipError_t launch_router_route(const float* x, int n, int d, const float* wt, const float* bias,
                                int E, int k, int norm, int32_t* ids, float* w, int32_t* rank,
                                int32_t* hist, int n_cu, hipStream_t s);
+// Token-major activation quantiser: every row of x [n][d] quantised per
+// 32-block into xq [n][d_pad] / xs [n][d_pad/32] (zero past d), optionally
+// also into xq_out [n][d] / xs_out [n][d/32]; with shg != NULL also
+// gs[t] = sigmoid(x[t] . shg).
+struct RowQuant {
+  const float* x;
+  int d, d_pad;
+  const float* shg;
+  float* gs;
+  int8_t* xq;
+  uint16_t* xs;
+  int8_t* xq_out;
+  uint16_t* xs_out;
+};
+// Routing from the logits (E > 64), in the same launch as the token-major
+// quantiser rq (its workgroups run beside the routing ones).
 hipError_t launch_route(const float* logits, int n, int E, int k, int norm, int32_t* ids, float* w,
-                        int32_t* rank, int32_t* hist, hipStream_t s);
+                        int32_t* rank, int32_t* hist, const RowQuant& rq, hipStream_t s);
 hipError_t launch_quantize(const float* v, int64_t n_values, int8_t* q, uint16_t* scales,
                            hipStream_t s);
 // The bucketing (expStart, expTokI/expTokK, the tile table and its row
@@ -179,12 +197,15 @@ hipError_t launch_quantize(const float* v, int64_t n_values, int8_t* q, uint16_t
 // tile rows (zero past d); with
 // sh_gate_vec != NULL also gs[t] = sigmoid(x[t] . g); xq_out [N][d] /
 // xs_out [N][d/32] (each optional) receive copies of the unpadded width.
+// With xs_tok != NULL the codes, the gate and the optional copies were
+// written by the routing launch (RowQuant, scales xs_tok [N][d_pad/32]): the
+// workgroups only place the scales at the tile rows, and x is not read.
 hipError_t launch_bucket_quantize(const int32_t* ids, const int32_t* rank, const int32_t* hist, int n,
                                   int E, int k, int has_shared, int32_t* exp_start, int32_t* tok_i,
                                   int32_t* tok_k, int32_t* row_tok, int32_t* tiles, int tile_bound,
                                   const float* x, int d, int d_pad, int8_t* gq, uint16_t* gqs,
                                   const float* sh_gate_vec, float* gs, int8_t* xq_out, uint16_t* xs_out,
-                                  hipStream_t s);
+                                  const uint16_t* xs_tok, hipStream_t s);
 
 struct GemmArgs {
   // common

@@ -403,17 +403,6 @@ __device__ __forceinline__ void route_load_logits(RouteLds& R, const float* __re
   }
 }
 
-// Routing as its own kernel (E > 64: a router workgroup holds only a 64-expert
-// slice of its tokens' logits).  One workgroup per ROUTE_TILE tokens.
-__global__ __launch_bounds__(ROUTE_WIDE_THREADS) void route_kernel(
-    const float* __restrict__ logits, int n, int E, int k, int norm, int32_t* __restrict__ ids,
-    float* __restrict__ wout, int32_t* __restrict__ rank, int32_t* __restrict__ hist) {
-  __shared__ __attribute__((aligned(16))) RouteLds R;
-  const int t0 = blockIdx.x * ROUTE_TILE;
-  const int nt = min(ROUTE_TILE, n - t0);
-  route_load_logits(R, logits, t0, nt, E, threadIdx.x);
-  route_tile<MAX_EXPERTS / 64>(R, blockIdx.x, t0, nt, E, k, norm, threadIdx.x, ids, wout, rank, hist);
-}
 
 // ---------------------------------------------------------------- decode
 // Decode router (1 <= N <= 8).  The same logits as router_kernel (fp32;
@@ -441,11 +430,15 @@ static_assert(DR_E * DR_NBP == 256, "one (expert, block) per lane");
 
 // Quantise token row xr (one wavefront): pass j0 covers values [1024 j0', +1024),
 // lane l the 16 values from 16 l; codes/scales to xq_row/xs_row up to d_pad
-// (zero past d); with shg the shared-gate dot product in the prefill order.
-__device__ __forceinline__ void decode_quantize_row(const float* __restrict__ xr, int d, int d_pad,
-                                                    const float* __restrict__ shg, float* __restrict__ gs_t,
-                                                    int8_t* __restrict__ xq_row,
-                                                    uint16_t* __restrict__ xs_row, int lane) {
+// (zero past d), and to xq_out/xs_out (optional) up to d; with shg the
+// shared-gate dot product.  Pieces, decisions and the gate's order are those
+// of the prefill quantiser in the bucketing launch, so the results are
+// bit-identical.
+__device__ __forceinline__ void quantize_row(const float* __restrict__ xr, int d, int d_pad,
+                                             const float* __restrict__ shg, float* __restrict__ gs_t,
+                                             int8_t* __restrict__ xq_row, uint16_t* __restrict__ xs_row,
+                                             int8_t* __restrict__ xq_out, uint16_t* __restrict__ xs_out,
+                                             int lane) {
   float gacc = 0.0f;
   for (int c00 = 0; c00 < d_pad; c00 += 1024) {
     const int c0 = c00 + lane * 16;
@@ -469,6 +462,8 @@ __device__ __forceinline__ void decode_quantize_row(const float* __restrict__ xr
       *reinterpret_cast<uint4*>(xq_row + c0) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
       if ((lane & 1) == 0) xs_row[c0 / QB] = s16;
     }
+    if (xq_out && valid) *reinterpret_cast<uint4*>(xq_out + c0) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    if (xs_out && valid && (lane & 1) == 0) xs_out[c0 / QB] = s16;
     if (shg && valid) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) gacc = __builtin_fmaf(v[i], shg[c0 + i], gacc);
@@ -479,6 +474,32 @@ __device__ __forceinline__ void decode_quantize_row(const float* __restrict__ xr
     for (int off = 32; off > 0; off >>= 1) gacc += __shfl_xor(gacc, off, 64);
     if (lane == 0) *gs_t = 1.0f / (1.0f + expf(-gacc));
   }
+}
+
+// Routing as its own kernel (E > 64: a router workgroup holds only a 64-expert
+// slice of its tokens' logits).  One workgroup per ROUTE_TILE tokens.  The
+// routing fills few CUs, so the same launch also quantises the tokens: the
+// n_tiles workgroups past the routing ones take ROUTE_TILE tokens each, one
+// wavefront per token, writing the token-major codes and scales (and the
+// shared-expert gate) that the bucketing launch would otherwise produce.
+__global__ __launch_bounds__(ROUTE_WIDE_THREADS) void route_kernel(
+    const float* __restrict__ logits, int n, int E, int k, int norm, int32_t* __restrict__ ids,
+    float* __restrict__ wout, int32_t* __restrict__ rank, int32_t* __restrict__ hist, RowQuant rq) {
+  const int n_tiles = (n + ROUTE_TILE - 1) / ROUTE_TILE;
+  if ((int)blockIdx.x >= n_tiles) {
+    const int lane = threadIdx.x & 63;
+    const int t = ((int)blockIdx.x - n_tiles) * ROUTE_TILE + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (t < n)
+      quantize_row(rq.x + (size_t)t * rq.d, rq.d, rq.d_pad, rq.shg, rq.gs + t, rq.xq + (size_t)t * rq.d_pad,
+                   rq.xs + (size_t)t * (rq.d_pad / QB), rq.xq_out ? rq.xq_out + (size_t)t * rq.d : nullptr,
+                   rq.xs_out ? rq.xs_out + (size_t)t * (rq.d / QB) : nullptr, lane);
+    return;
+  }
+  __shared__ __attribute__((aligned(16))) RouteLds R;
+  const int t0 = blockIdx.x * ROUTE_TILE;
+  const int nt = min(ROUTE_TILE, n - t0);
+  route_load_logits(R, logits, t0, nt, E, threadIdx.x);
+  route_tile<MAX_EXPERTS / 64>(R, blockIdx.x, t0, nt, E, k, norm, threadIdx.x, ids, wout, rank, hist);
 }
 
 template <int NT>
@@ -494,8 +515,8 @@ __global__ __launch_bounds__(256, 1) void decode_router_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int t = (int)blockIdx.x - n_rwg;
     if (wave == 0 && t < n)
-      decode_quantize_row(x + (size_t)t * d, d, d_pad, shg, gs + t, xq + (size_t)t * d_pad,
-                          xs + (size_t)t * (d_pad / QB), lane);
+      quantize_row(x + (size_t)t * d, d, d_pad, shg, gs + t, xq + (size_t)t * d_pad,
+                   xs + (size_t)t * (d_pad / QB), nullptr, nullptr, lane);
     return;
   }
   const int el = tid % DR_E, bl = tid / DR_E;
@@ -589,8 +610,8 @@ __global__ __launch_bounds__(512, 1) void decode_router_dpp_kernel(
   if ((int)blockIdx.x >= n_rwg) {
     const int t = (int)blockIdx.x - n_rwg;
     if (wave == 0 && t < n)
-      decode_quantize_row(x + (size_t)t * d, d, d_pad, shg, gs + t, xq + (size_t)t * d_pad,
-                          xs + (size_t)t * (d_pad / QB), lane);
+      quantize_row(x + (size_t)t * d, d, d_pad, shg, gs + t, xq + (size_t)t * d_pad,
+                   xs + (size_t)t * (d_pad / QB), nullptr, nullptr, lane);
     return;
   }
   const int el = lane & 15, bl = 4 * wave + (lane >> 4);
@@ -701,9 +722,9 @@ hipError_t launch_router_route(const float* x, int n, int d, const float* wt, co
 }
 
 hipError_t launch_route(const float* logits, int n, int E, int k, int norm, int32_t* ids, float* w,
-                        int32_t* rank, int32_t* hist, hipStream_t s) {
+                        int32_t* rank, int32_t* hist, const RowQuant& rq, hipStream_t s) {
   const int tiles = (n + ROUTE_TILE - 1) / ROUTE_TILE;
-  route_kernel<<<tiles, ROUTE_WIDE_THREADS, 0, s>>>(logits, n, E, k, norm, ids, w, rank, hist);
+  route_kernel<<<2 * tiles, ROUTE_WIDE_THREADS, 0, s>>>(logits, n, E, k, norm, ids, w, rank, hist, rq);
   return hipGetLastError();
 }
 
