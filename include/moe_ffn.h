@@ -248,7 +248,7 @@ int moe_ffn_prefill_residual(const moe_ffn_weights* w, const float* x, int32_t n
  * array returns MOE_FFN_SCRATCH_TOO_SMALL before anything is enqueued: at
  * the OLMoE-shaped layer (d 2048, 64 experts, top-8, ffn 1024) that is above
  * 2026 tokens, at the 35B-A3B-shaped layer (256 experts, top-8, ffn 512 +
- * shared 512) above 1749.  x, out, routing and stream are those of
+ * shared 512) above 1748.  x, out, routing and stream are those of
  * moe_ffn_prefill. */
 #define MOE_FFN_STATIC_SCRATCH_BYTES (160u << 20)
 int moe_ffn_prefill_static(const moe_ffn_weights* w, const float* x, int32_t n_tokens, float* out,

@@ -170,3 +170,17 @@ def test_chunked_prefill_validates_on_the_host(B):
     assert L.moe_ffn_prefill_chunked(16, 16, 4, 0, 0, 32, 64, 1 << 20, None) == -1     # chunk 0
     assert L.moe_ffn_prefill_chunked(16, 16, 4, 2, 2, 32, 64, 1 << 20, None) == -1     # unknown flag
     assert L.moe_ffn_prefill_chunked(16, 16, -1, 2, 0, 32, 64, 1 << 20, None) == -1    # negative n
+
+
+@pytest.mark.parametrize("dims, limit", [
+    ((2048, 64, 8, 1024, 0, 0), 2026),      # OLMoE-shaped layer
+    ((2048, 256, 8, 512, 512, 1), 1748),    # 35B-A3B-shaped layer with a shared expert
+])
+def test_static_scratch_token_limits_match_the_header(B, dims, limit):
+    """The header states how many tokens the no-allocation entry point takes
+    at these two shapes: exactly the largest batch whose workspace fits."""
+    dm = B.moe_ffn_dims(*dims)
+    assert B.moe_ffn_workspace_size_for_dims(dm, limit) <= B.STATIC_SCRATCH_BYTES
+    assert B.moe_ffn_workspace_size_for_dims(dm, limit + 1) > B.STATIC_SCRATCH_BYTES
+    header = open(os.path.join(os.path.dirname(__file__), "..", "include", "moe_ffn.h")).read()
+    assert f"{limit} tokens" in header or f"above {limit}" in header
